@@ -1,0 +1,211 @@
+/*
+ * ee.h - C ABI of libee, the KV-shared early-exit decode step on one MI355X (gfx950).
+ *
+ * The method (page titles and sections of the surveyed web pages):
+ *   - "River-LLM 深度解析" section 4.1-4.3: every decoder layer has an int4 (W4A16)
+ *     "exit layer" copy; once a token exits, the copies run its remaining layers
+ *     and write K/V into the same cache slots as the backbone layer would, so no
+ *     KV entry is ever missing (section 8.2, one store per layer).
+ *   - "大语言模型解码加速：自适应层并行机制解析" (AdaDecode explainer) section 2.1:
+ *     the intermediate exit head of layer l is h^(l) T^(l) E^T with T^(l) a d x d
+ *     matrix and E the LM-head matrix; section 2.2: a token exits when the top-1
+ *     probability exceeds gamma (default 0.75).
+ *   - CALM explainer section 2.2: exit decisions are per token and per layer;
+ *     section 3.3: sequences of one batch exit at different layers.
+ *
+ * One decode step, per sequence b: embed the input token; for l = 1..L run layer
+ * l with the backbone bf16 weights while b is on the backbone, else with the
+ * int4 exit copy; write k, v of position pos_b into slot (l, b, pos_b); after
+ * backbone layer l < L evaluate the exit head: z = bf16(T_l bf16(h)),
+ * logits = E z, p = max softmax(logits); exit iff p > gamma_l (strict), or iff
+ * l equals the forced exit layer when one is given.  The emitted token is the
+ * greedy argmax of the final RMSNorm + LM head after layer L (lowest index on
+ * ties).  The exit layer e_b is the layer after which b left the backbone; e_b =
+ * L means b never exited.
+ *
+ * Precision: bf16 weights and GEMV inputs, float32 accumulation, float32
+ * residual stream, bf16 K/V cache, float32 logits and softmax.  int4 codes are
+ * symmetric per group of G inputs of a row with a bf16 scale
+ * s = bf16(max|w| / 7), q = clamp(rint(w / s), -8, 7), w_hat = q * s.
+ *
+ * Conventions
+ *   - Every entry point returns ee_status; EE_OK is 0, errors are negative.
+ *     Output parameters are written only on EE_OK.  ee_last_error() returns a
+ *     thread-local message for the last failure.  No C++ exception crosses the ABI.
+ *   - Arguments are validated on the host before any launch; an invalid call
+ *     changes no state.
+ *   - EE_ERR_HIP is sticky for the model: destroy it and start again.
+ *   - "device" pointers point to GPU memory of the current HIP device; "host"
+ *     pointers to ordinary CPU memory.  A model or cache is used by one host
+ *     thread at a time.
+ *   - Weight matrices are bf16, row-major [out, in] (a linear map y = W x), and
+ *     are borrowed: the caller keeps them alive and unchanged until
+ *     ee_destroy_model.  The library owns everything it derives (int4 copies,
+ *     RoPE table, workspaces).
+ */
+#ifndef EE_H
+#define EE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t ee_status;
+#define EE_OK 0
+#define EE_ERR_INVALID_ARG (-1)   /* a null pointer, a value out of range, a bad shape */
+#define EE_ERR_OUT_OF_MEMORY (-2) /* device or pinned host allocation failed */
+#define EE_ERR_HIP (-3)           /* a HIP runtime call failed (sticky) */
+#define EE_ERR_CACHE_FULL (-4)    /* a sequence would grow beyond the cache's max_seq */
+#define EE_ERR_SHAPE (-5)         /* the model shape is not supported by the kernels */
+#define EE_ERR_NOT_WRITTEN (-6)   /* a KV slot read back was never written (occupancy on) */
+#define EE_ERR_UNSUPPORTED (-7)   /* a feature not available in this build */
+
+#define EE_EXIT_INT4 0 /* exit copies are the int4 group-quantised layers */
+#define EE_EXIT_BF16 1 /* exit copies are the backbone layers themselves (test mode) */
+
+#define EE_KV_TRACK_OCCUPANCY 1u /* count writes per (layer, sequence, position) slot */
+
+typedef struct ee_model ee_model;
+typedef struct ee_kv_cache ee_kv_cache;
+
+/* Model shape.  Supported: n_layers >= 1; d_model, d_ff multiples of group_size;
+ * group_size in {32, 64, 128}; head_dim even, 16 <= head_dim <= 256, multiple of
+ * 16; n_heads a multiple of n_kv_heads with n_heads / n_kv_heads <= 16;
+ * vocab >= 1; 1 <= max_batch <= 64; max_positions >= 1 bounds every position. */
+typedef struct ee_model_config {
+  int32_t n_layers;
+  int32_t d_model;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t d_ff;
+  int32_t vocab;
+  int32_t group_size;
+  float rms_eps;
+  float rope_theta;
+  int32_t exit_mode; /* EE_EXIT_INT4 or EE_EXIT_BF16 */
+  int32_t max_batch;
+  int32_t max_positions;
+} ee_model_config;
+
+/* Device pointers of one layer.  Shapes: attn_norm, ffn_norm [d]; wq [H*hd, d];
+ * wk, wv [Hkv*hd, d]; wo [d, H*hd]; w_gate, w_up [F, d]; w_down [d, F];
+ * head_T [d, d] holds the exit head's projection with z_j = sum_i T[j, i] h_i
+ * (NULL for the last layer, which has no exit head). */
+typedef struct ee_layer_weights {
+  const void *attn_norm, *wq, *wk, *wv, *wo;
+  const void *ffn_norm, *w_gate, *w_up, *w_down;
+  const void *head_T;
+} ee_layer_weights;
+
+/* tok_emb [V, d] embedding rows; lm_head [V, d] is E of both the exit heads and
+ * the final head; final_norm [d].  layers is a HOST array of n_layers entries. */
+typedef struct ee_weights {
+  const void *tok_emb, *lm_head, *final_norm;
+  const ee_layer_weights *layers;
+} ee_weights;
+
+/* Optional per-step diagnostics (host buffers; NULL members are skipped).
+ * Requesting any of them runs the step without graph replay. */
+typedef struct ee_step_debug {
+  float *p_top1; /* [batch][L-1]: exit-head top-1 probability, NaN where no head ran */
+  float *logits; /* [batch][V]: final LM-head logits */
+  float *hidden; /* [batch][L+1][d]: residual after the embedding and after each layer */
+  float *gap;    /* [batch]: top-1 minus top-2 final logit (+inf when V == 1) */
+} ee_step_debug;
+
+/* Creates a model.  cfg, w: host structs describing borrowed device weights.
+ * gamma: host [n_layers - 1] per-layer thresholds, or NULL for 0.75 everywhere.
+ * Builds the int4 exit copies of layers 2..L on the device (synchronously).
+ * Errors: INVALID_ARG (nulls, values), SHAPE (unsupported shape),
+ * OUT_OF_MEMORY, HIP. */
+ee_status ee_create_model(const ee_model_config *cfg, const ee_weights *w,
+                          const float *gamma, ee_model **out);
+
+/* Destroys a model (NULL is allowed).  Caches created from it must be destroyed first. */
+ee_status ee_destroy_model(ee_model *m);
+
+/* Device bytes a KV cache of max_batch sequences and max_seq positions needs:
+ * K and V, each [L][max_batch][Hkv][max_seq][hd] bf16, plus the per-sequence lengths. */
+ee_status ee_kv_cache_bytes(const ee_model *m, int32_t max_batch, int32_t max_seq,
+                            size_t *bytes);
+
+/* Creates an empty cache (all lengths 0).  dev_buf: caller-owned device buffer of
+ * at least ee_kv_cache_bytes bytes (kept alive until destroy), or NULL to let the
+ * library allocate.  max_batch <= model max_batch, max_seq <= max_positions.
+ * flags: EE_KV_TRACK_OCCUPANCY keeps a u8 write counter per slot. */
+ee_status ee_kv_cache_create(ee_model *m, int32_t max_batch, int32_t max_seq,
+                             void *dev_buf, size_t buf_bytes, uint32_t flags,
+                             ee_kv_cache **out);
+
+/* Sets the length of sequence seq (or of all sequences when seq == -1) to 0 and
+ * clears its occupancy counters. */
+ee_status ee_kv_cache_reset(ee_kv_cache *c, int32_t seq);
+
+/* Copies the max_batch sequence lengths to lens_host. */
+ee_status ee_kv_cache_lengths(const ee_kv_cache *c, int32_t *lens_host);
+
+/* Copies K and V of positions [pos0, pos0+n) of one (1-based) layer and sequence
+ * to host buffers, each [n][Hkv][hd] bf16 (uint16 bit patterns).  With occupancy
+ * tracking, returns NOT_WRITTEN if any slot in the range was never written. */
+ee_status ee_kv_cache_read(const ee_kv_cache *c, int32_t layer, int32_t seq, int32_t pos0,
+                           int32_t n, void *k_host, void *v_host);
+
+/* Copies the occupancy counters [L][max_batch][max_seq] (u8) to the host.
+ * UNSUPPORTED if the cache was created without EE_KV_TRACK_OCCUPANCY. */
+ee_status ee_kv_cache_occupancy(const ee_kv_cache *c, uint8_t *counts_host);
+
+ee_status ee_kv_cache_destroy(ee_kv_cache *c);
+
+/* Prefill: runs sequences 0..batch-1 over P prompt tokens each (host [batch][P]
+ * int32, row-major) at full depth with the backbone weights (no exit heads),
+ * writing KV slots at positions len_b .. len_b+P-1, then returns the greedy token
+ * after the last position in out_tokens_host [batch].  That token is also kept
+ * on the device as the next decode input.  hip_stream: a hipStream_t or NULL
+ * (the library's own stream); the call returns after the work has finished.
+ * Errors: INVALID_ARG (token out of [0, V), batch out of range), CACHE_FULL. */
+ee_status ee_prefill(ee_model *m, ee_kv_cache *c, int32_t batch, const int32_t *tokens_host,
+                     int32_t P, void *hip_stream, int32_t *out_tokens_host);
+
+/* One decode step for sequences 0..batch-1.
+ * in_tokens_host: [batch] input tokens, or NULL to use each sequence's last
+ *   output token kept on the device (from ee_prefill or the previous step).
+ * forced_exit_host: [batch] or NULL; 0 lets the exit head decide, 1..L forces
+ *   the exit layer (the heads still run; their decision is overridden).
+ * gamma_host: [L-1] thresholds for this step, or NULL for the model's.
+ * out_tokens_host, out_exit_layers_host: [batch] greedy tokens and exit layers.
+ * dbg: optional diagnostics.  Returns after the outputs are on the host.
+ * With a non-NULL hip_stream and no diagnostics, the step's launches are
+ * captured once into a HIP graph per (cache, batch) and replayed.
+ * Errors: INVALID_ARG, CACHE_FULL (some len_b + 1 > max_seq; nothing runs). */
+ee_status ee_decode_step(ee_model *m, ee_kv_cache *c, int32_t batch,
+                         const int32_t *in_tokens_host, const int32_t *forced_exit_host,
+                         const float *gamma_host, void *hip_stream, int32_t *out_tokens_host,
+                         int32_t *out_exit_layers_host, ee_step_debug *dbg);
+
+/* Copies the int4 exit copy of one linear map of 1-based layer (2..L) back to the
+ * host as int8 codes [nrows][K] and bf16 scales [nrows][K/G] (uint16 bits).
+ * which: 0 wq, 1 wk, 2 wv, 3 wo, 4 w_gate, 5 w_up, 6 w_down.
+ * UNSUPPORTED in EE_EXIT_BF16 mode. */
+ee_status ee_exit_weights_read(const ee_model *m, int32_t layer, int32_t which, int32_t row0,
+                               int32_t nrows, int8_t *codes_host, uint16_t *scales_host);
+
+/* Kernel timing for measurement.  When enabled, every launch of the exit-head
+ * vocabulary GEMV (and the final LM head) is bracketed by HIP events on the
+ * stream it runs on, graph replays included; ee_profile_read returns the number
+ * of such launches and their summed duration in milliseconds since the last
+ * read, then clears the counters.  kind: 0 exit-head vocabulary GEMV. */
+ee_status ee_profile_enable(ee_model *m, int32_t on);
+ee_status ee_profile_read(ee_model *m, int32_t kind, int64_t *launches, double *total_ms);
+
+/* Thread-local message describing the last error ("" if none). */
+const char *ee_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EE_H */

@@ -1,0 +1,888 @@
+// Host side of libee: model and KV-cache management, the per-step launch
+// schedule, argument validation and the C ABI declared in include/ee.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <exception>
+#include <map>
+#include <new>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "ee.h"
+#include "ee_internal.h"
+
+using namespace ee;
+
+namespace {
+
+thread_local std::string g_err;
+
+struct Error {
+  ee_status code;
+  std::string msg;
+};
+
+[[noreturn]] void fail(ee_status code, const std::string& msg) { throw Error{code, msg}; }
+
+#define HIPCHK(expr)                                                                       \
+  do {                                                                                     \
+    hipError_t e_ = (expr);                                                                \
+    if (e_ != hipSuccess)                                                                  \
+      fail(EE_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(e_));                 \
+  } while (0)
+
+template <typename T>
+T* dalloc(size_t n) {
+  void* p = nullptr;
+  if (n == 0) n = 1;
+  if (hipMalloc(&p, n * sizeof(T)) != hipSuccess) {
+    (void)hipGetLastError();
+    fail(EE_ERR_OUT_OF_MEMORY, "hipMalloc of " + std::to_string(n * sizeof(T)) + " bytes failed");
+  }
+  return (T*)p;
+}
+
+struct Q4 {
+  uint32_t* codes = nullptr;
+  uint16_t* scales = nullptr;
+  int N = 0, K = 0;
+};
+
+struct LayerQ {
+  Q4 qkv, o, gate, up, down;
+};
+
+constexpr int kNwg = 512;  // projection workgroups (2 per CU)
+
+}  // namespace
+
+struct ee_model {
+  ee_model_config cfg{};
+  const uint16_t *tok_emb = nullptr, *lm_head = nullptr, *final_norm = nullptr;
+  std::vector<ee_layer_weights> lw;
+  std::vector<LayerQ> lq;  // index l-1; layer 1 has no copy
+  std::vector<float> gamma;
+  float* d_gamma = nullptr;
+  float *d_cos = nullptr, *d_sin = nullptr;
+  // workspaces
+  float* h = nullptr;
+  uint16_t *hb = nullptr, *x = nullptr, *qkv = nullptr, *qrot = nullptr, *attn_o = nullptr;
+  uint16_t *act = nullptr, *z = nullptr;
+  float* head_part = nullptr;
+  float* attn_part = nullptr;
+  int nch_max = 0;
+  StepState* st = nullptr;
+  float* p_rec = nullptr;
+  float* dbg_logits = nullptr;
+  float* dbg_hidden = nullptr;
+  int32_t* d_prompt = nullptr;
+  size_t prompt_cap = 0;
+  // pinned host staging
+  int32_t* h_in = nullptr;   // tok[64], forced[64]
+  float* h_gamma = nullptr;  // [L-1]
+  int32_t* h_out = nullptr;  // out_tok[64], e[64]
+  float* h_gap = nullptr;
+  hipStream_t own = nullptr;
+  bool broken = false;
+  std::string broken_msg;
+  // profiling
+  bool prof = false;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_used = 0;
+  int64_t prof_launches = 0;
+  double prof_ms = 0.0;
+  int ncaches = 0;
+  std::vector<void*> allocs;
+
+  template <typename T>
+  T* alloc(size_t n) {
+    T* p = dalloc<T>(n);
+    allocs.push_back(p);
+    return p;
+  }
+};
+
+struct ee_kv_cache {
+  ee_model* m = nullptr;
+  int Bmax = 0, S = 0;
+  uint16_t *K = nullptr, *V = nullptr;
+  int32_t* lens = nullptr;  // device
+  uint8_t* occ = nullptr;
+  std::vector<int32_t> hlens;
+  void* owned = nullptr;
+};
+
+namespace {
+
+template <typename F>
+ee_status guard(F&& f) {
+  try {
+    f();
+    g_err.clear();
+    return EE_OK;
+  } catch (const Error& e) {
+    g_err = e.msg;
+    return e.code;
+  } catch (const std::bad_alloc&) {
+    g_err = "host allocation failed";
+    return EE_ERR_OUT_OF_MEMORY;
+  } catch (const std::exception& e) {
+    g_err = e.what();
+    return EE_ERR_INVALID_ARG;
+  } catch (...) {
+    g_err = "unknown error";
+    return EE_ERR_INVALID_ARG;
+  }
+}
+
+void check_model(const ee_model* m) {
+  if (!m) fail(EE_ERR_INVALID_ARG, "null model");
+  if (m->broken) fail(EE_ERR_HIP, "model is unusable after an earlier HIP error: " + m->broken_msg);
+}
+
+// Runs f; a HIP failure marks the model unusable (sticky).
+template <typename F>
+void with_sticky(ee_model* m, F&& f) {
+  try {
+    f();
+  } catch (const Error& e) {
+    if (e.code == EE_ERR_HIP) {
+      m->broken = true;
+      m->broken_msg = e.msg;
+    }
+    throw;
+  }
+}
+
+void validate_config(const ee_model_config& c) {
+  auto need = [](bool ok, const char* what) {
+    if (!ok) fail(EE_ERR_INVALID_ARG, what);
+  };
+  auto shape = [](bool ok, const char* what) {
+    if (!ok) fail(EE_ERR_SHAPE, what);
+  };
+  need(c.n_layers >= 1, "n_layers must be >= 1");
+  need(c.d_model >= 1 && c.d_ff >= 1 && c.vocab >= 1, "d_model, d_ff, vocab must be positive");
+  need(c.n_heads >= 1 && c.n_kv_heads >= 1 && c.n_heads % c.n_kv_heads == 0,
+       "n_heads must be a positive multiple of n_kv_heads");
+  need(c.max_batch >= 1 && c.max_batch <= kMaxBatch, "max_batch must be in [1, 64]");
+  need(c.max_positions >= 1, "max_positions must be >= 1");
+  need(c.exit_mode == EE_EXIT_INT4 || c.exit_mode == EE_EXIT_BF16, "bad exit_mode");
+  need(std::isfinite(c.rms_eps) && c.rms_eps > 0 && std::isfinite(c.rope_theta) && c.rope_theta > 0,
+       "rms_eps and rope_theta must be positive");
+  shape(c.group_size == 32 || c.group_size == 64 || c.group_size == 128, "group_size must be 32, 64 or 128");
+  shape(c.head_dim == 32 || c.head_dim == 64 || c.head_dim == 128, "head_dim must be 32, 64 or 128");
+  shape(c.n_heads / c.n_kv_heads <= 16, "at most 16 query heads per kv head");
+  shape(c.d_model % c.group_size == 0 && c.d_ff % c.group_size == 0,
+        "d_model and d_ff must be multiples of group_size");
+  const int qd = c.n_heads * c.head_dim;
+  shape(qd % c.group_size == 0, "n_heads * head_dim must be a multiple of group_size");
+  const int kmax = std::max(std::max(c.d_model, c.d_ff), qd);
+  shape((long long)8 * (kmax / c.group_size) <= kXgElems, "too many int4 groups per row");
+  shape(c.d_model % 8 == 0 && c.d_ff % 8 == 0, "widths must be multiples of 8");
+}
+
+hipStream_t pick_stream(ee_model* m, void* s) { return s ? (hipStream_t)s : m->own; }
+
+void prof_begin(ee_model* m, hipStream_t s, hipEvent_t* e0) {
+  if (!m->prof) return;
+  if (m->ev_used + 2 > m->ev_pool.size()) {
+    for (int i = 0; i < 64; ++i) {
+      hipEvent_t e;
+      HIPCHK(hipEventCreate(&e));
+      m->ev_pool.push_back(e);
+    }
+  }
+  *e0 = m->ev_pool[m->ev_used++];
+  HIPCHK(hipEventRecord(*e0, s));
+}
+
+void prof_end(ee_model* m, hipStream_t s) {
+  if (!m->prof) return;
+  hipEvent_t e1 = m->ev_pool[m->ev_used++];
+  HIPCHK(hipEventRecord(e1, s));
+}
+
+void prof_collect(ee_model* m) {
+  if (!m->prof) return;
+  for (size_t i = 0; i + 1 < m->ev_used; i += 2) {
+    float ms = 0;
+    HIPCHK(hipEventElapsedTime(&ms, m->ev_pool[i], m->ev_pool[i + 1]));
+    m->prof_ms += ms;
+    m->prof_launches += 1;
+  }
+  m->ev_used = 0;
+}
+
+ProjArgs base_args(const ee_model* m) {
+  ProjArgs a{};
+  a.G = m->cfg.group_size;
+  a.nseg = 1;
+  return a;
+}
+
+void set_seg1(ProjArgs& a, const void* w, int N) {
+  a.nseg = 1;
+  a.wb[0] = (const uint16_t*)w;
+  a.wb[1] = a.wb[2] = nullptr;
+  a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = N;
+}
+
+struct Debug {
+  bool hidden = false, logits = false;
+};
+
+// Enqueues one position of all B sequences: layers 1..L, exit heads when
+// heads is set, and the final head when final is set (else the lengths advance).
+void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final,
+                      const int32_t* prompt, int P, int t, const Debug& dbg, hipStream_t s) {
+  const ee_model_config& cf = m->cfg;
+  const int L = cf.n_layers, d = cf.d_model, F = cf.d_ff, H = cf.n_heads, Hkv = cf.n_kv_heads;
+  const int hd = cf.head_dim, qd = H * hd, kvd = Hkv * hd, nqkv = qd + 2 * kvd;
+  StepState* st = m->st;
+  const bool int4 = cf.exit_mode == EE_EXIT_INT4;
+
+  launch_init(st, prompt, P, t, B, L, m->tok_emb, d, cf.vocab, m->h, m->p_rec, s);
+  if (dbg.hidden)
+    HIPCHK(hipMemcpy2DAsync(m->dbg_hidden, (size_t)(L + 1) * d * 4, m->h, (size_t)d * 4,
+                            (size_t)d * 4, B, hipMemcpyDeviceToDevice, s));
+  // row lists: backbone rows run the bf16 weights, exited rows the int4 copy;
+  // with unquantised exit copies every row runs the bf16 weights.
+  const int32_t* list_bf = int4 ? st->act : st->all;
+  const int32_t* cnt_bf = int4 ? &st->n_act : &st->n_all;
+
+  for (int l = 1; l <= L; ++l) {
+    const ee_layer_weights& w = m->lw[l - 1];
+    const LayerQ* q = (int4 && l >= 2) ? &m->lq[l - 1] : nullptr;
+    const size_t kvoff = (size_t)(l - 1) * c->Bmax * Hkv * c->S * hd;
+
+    launch_rmsnorm(m->h, (const uint16_t*)w.attn_norm, m->x, B, d, cf.rms_eps, s);
+    {
+      ProjArgs a = base_args(m);
+      a.N = nqkv;
+      a.K = d;
+      a.nseg = 3;
+      a.wb[0] = (const uint16_t*)w.wq;
+      a.wb[1] = (const uint16_t*)w.wk;
+      a.wb[2] = (const uint16_t*)w.wv;
+      a.seg_end[0] = qd;
+      a.seg_end[1] = qd + kvd;
+      a.seg_end[2] = nqkv;
+      if (q) {
+        a.q4 = q->qkv.codes;
+        a.s4 = q->qkv.scales;
+        a.list_i4 = st->ex;
+        a.cnt_i4 = &st->n_ex;
+      }
+      a.list_bf = list_bf;
+      a.cnt_bf = cnt_bf;
+      a.x = m->x;
+      a.x_stride = d;
+      a.y = m->qkv;
+      a.y_stride = nqkv;
+      launch_proj(EPI_BF16, a, kNwg, s);
+    }
+    launch_rope_kv(m->qkv, m->qrot, c->K + kvoff, c->V + kvoff,
+                   c->occ ? c->occ + (size_t)(l - 1) * c->Bmax * c->S : nullptr, c->lens, m->d_cos,
+                   m->d_sin, B, H, Hkv, hd, c->S, c->Bmax, s);
+    {
+      AttnArgs a{};
+      a.q = m->qrot;
+      a.K = c->K + kvoff;
+      a.V = c->V + kvoff;
+      a.S = c->S;
+      a.Bmax = c->Bmax;
+      a.lens = c->lens;
+      a.H = H;
+      a.Hkv = Hkv;
+      a.hd = hd;
+      a.B = B;
+      a.nch = (c->S + kAttnChunk - 1) / kAttnChunk;
+      a.scale = (float)(1.0 / std::sqrt((double)hd));
+      a.part = m->attn_part;
+      a.out = m->attn_o;
+      launch_attention(a, s);
+    }
+    {
+      ProjArgs a = base_args(m);
+      a.N = d;
+      a.K = qd;
+      set_seg1(a, w.wo, d);
+      if (q) {
+        a.q4 = q->o.codes;
+        a.s4 = q->o.scales;
+        a.list_i4 = st->ex;
+        a.cnt_i4 = &st->n_ex;
+      }
+      a.list_bf = list_bf;
+      a.cnt_bf = cnt_bf;
+      a.x = m->attn_o;
+      a.x_stride = qd;
+      a.y = m->h;
+      a.y_stride = d;
+      launch_proj(EPI_RESID, a, kNwg, s);
+    }
+    launch_rmsnorm(m->h, (const uint16_t*)w.ffn_norm, m->x, B, d, cf.rms_eps, s);
+    {
+      ProjArgs a = base_args(m);
+      a.N = F;
+      a.K = d;
+      set_seg1(a, w.w_gate, F);
+      a.wb2 = (const uint16_t*)w.w_up;
+      if (q) {
+        a.q4 = q->gate.codes;
+        a.s4 = q->gate.scales;
+        a.q4b = q->up.codes;
+        a.s4b = q->up.scales;
+        a.list_i4 = st->ex;
+        a.cnt_i4 = &st->n_ex;
+      }
+      a.list_bf = list_bf;
+      a.cnt_bf = cnt_bf;
+      a.x = m->x;
+      a.x_stride = d;
+      a.y = m->act;
+      a.y_stride = F;
+      launch_proj(EPI_SWIGLU, a, kNwg, s);
+    }
+    const bool head_here = heads && l < L;
+    {
+      ProjArgs a = base_args(m);
+      a.N = d;
+      a.K = F;
+      set_seg1(a, w.w_down, d);
+      if (q) {
+        a.q4 = q->down.codes;
+        a.s4 = q->down.scales;
+        a.list_i4 = st->ex;
+        a.cnt_i4 = &st->n_ex;
+      }
+      a.list_bf = list_bf;
+      a.cnt_bf = cnt_bf;
+      a.x = m->act;
+      a.x_stride = F;
+      a.y = m->h;
+      a.y_stride = d;
+      a.y2 = head_here ? m->hb : nullptr;
+      a.y2_stride = d;
+      launch_proj(EPI_RESID, a, kNwg, s);
+    }
+    if (head_here) {
+      {
+        ProjArgs a = base_args(m);
+        a.N = d;
+        a.K = d;
+        set_seg1(a, w.head_T, d);
+        a.list_bf = st->act;
+        a.cnt_bf = &st->n_act;
+        a.x = m->hb;
+        a.x_stride = d;
+        a.y = m->z;
+        a.y_stride = d;
+        launch_proj(EPI_BF16, a, kNwg, s);
+      }
+      {
+        ProjArgs a = base_args(m);
+        a.N = cf.vocab;
+        a.K = d;
+        set_seg1(a, m->lm_head, cf.vocab);
+        a.list_bf = st->act;
+        a.cnt_bf = &st->n_act;
+        a.x = m->z;
+        a.x_stride = d;
+        a.part = m->head_part;
+        hipEvent_t e0;
+        prof_begin(m, s, &e0);
+        launch_proj(EPI_LSE, a, kNwg, s);
+        prof_end(m, s);
+      }
+      launch_decide(st, m->head_part, kNwg, m->d_gamma, l, L, B, m->p_rec, s);
+    }
+    if (dbg.hidden)
+      HIPCHK(hipMemcpy2DAsync(m->dbg_hidden + (size_t)l * d, (size_t)(L + 1) * d * 4, m->h,
+                              (size_t)d * 4, (size_t)d * 4, B, hipMemcpyDeviceToDevice, s));
+  }
+  if (final) {
+    launch_rmsnorm(m->h, m->final_norm, m->x, B, d, cf.rms_eps, s);
+    ProjArgs a = base_args(m);
+    a.N = cf.vocab;
+    a.K = d;
+    set_seg1(a, m->lm_head, cf.vocab);
+    a.list_bf = st->all;
+    a.cnt_bf = &st->n_all;
+    a.x = m->x;
+    a.x_stride = d;
+    a.part = m->head_part;
+    a.logits = dbg.logits ? m->dbg_logits : nullptr;
+    a.logits_stride = cf.vocab;
+    launch_proj(EPI_ARGMAX, a, kNwg, s);
+    launch_final(st, m->head_part, kNwg, B, cf.vocab, c->lens, 1, s);
+  } else {
+    launch_advance(c->lens, B, s);
+  }
+  HIPCHK(hipGetLastError());
+}
+
+void free_model(ee_model* m) {
+  if (!m) return;
+  for (void* p : m->allocs) (void)hipFree(p);
+  for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
+  if (m->h_in) (void)hipHostFree(m->h_in);
+  if (m->h_gamma) (void)hipHostFree(m->h_gamma);
+  if (m->h_out) (void)hipHostFree(m->h_out);
+  if (m->h_gap) (void)hipHostFree(m->h_gap);
+  if (m->own) (void)hipStreamDestroy(m->own);
+  delete m;
+}
+
+template <typename T>
+T* halloc(size_t n) {
+  void* p = nullptr;
+  if (hipHostMalloc(&p, std::max<size_t>(n, 1) * sizeof(T), hipHostMallocDefault) != hipSuccess) {
+    (void)hipGetLastError();
+    fail(EE_ERR_OUT_OF_MEMORY, "pinned host allocation failed");
+  }
+  return (T*)p;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+const char* ee_last_error(void) { return g_err.c_str(); }
+
+ee_status ee_create_model(const ee_model_config* cfg, const ee_weights* w, const float* gamma,
+                          ee_model** out) {
+  return guard([&] {
+    if (!cfg || !w || !out) fail(EE_ERR_INVALID_ARG, "null argument");
+    validate_config(*cfg);
+    const ee_model_config& c = *cfg;
+    if (!w->tok_emb || !w->lm_head || !w->final_norm || !w->layers)
+      fail(EE_ERR_INVALID_ARG, "null weight pointer");
+    for (int l = 0; l < c.n_layers; ++l) {
+      const ee_layer_weights& lw = w->layers[l];
+      if (!lw.attn_norm || !lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.ffn_norm || !lw.w_gate ||
+          !lw.w_up || !lw.w_down || (l + 1 < c.n_layers && !lw.head_T))
+        fail(EE_ERR_INVALID_ARG, "null weight pointer in layer " + std::to_string(l + 1));
+    }
+    std::vector<float> gam(c.n_layers > 1 ? c.n_layers - 1 : 0, 0.75f);
+    if (gamma)
+      for (size_t i = 0; i < gam.size(); ++i) {
+        if (!std::isfinite(gamma[i])) fail(EE_ERR_INVALID_ARG, "gamma must be finite");
+        gam[i] = gamma[i];
+      }
+    ee_model* m = new ee_model();
+    try {
+      m->cfg = c;
+      m->tok_emb = (const uint16_t*)w->tok_emb;
+      m->lm_head = (const uint16_t*)w->lm_head;
+      m->final_norm = (const uint16_t*)w->final_norm;
+      m->lw.assign(w->layers, w->layers + c.n_layers);
+      m->gamma = gam;
+      HIPCHK(hipStreamCreateWithFlags(&m->own, hipStreamNonBlocking));
+      const int L = c.n_layers, d = c.d_model, F = c.d_ff, G = c.group_size;
+      const int qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+      // int4 exit copies of layers 2..L
+      m->lq.resize(L);
+      if (c.exit_mode == EE_EXIT_INT4) {
+        auto mk = [&](int N, int K) {
+          Q4 q;
+          q.N = N;
+          q.K = K;
+          q.codes = m->alloc<uint32_t>((size_t)N * (K / 8));
+          q.scales = m->alloc<uint16_t>((size_t)N * (K / G));
+          return q;
+        };
+        for (int l = 2; l <= L; ++l) {
+          LayerQ& q = m->lq[l - 1];
+          const ee_layer_weights& lw = m->lw[l - 1];
+          q.qkv = mk(qd + 2 * kvd, d);
+          q.o = mk(d, qd);
+          q.gate = mk(F, d);
+          q.up = mk(F, d);
+          q.down = mk(d, F);
+          launch_quantize((const uint16_t*)lw.wq, qd, d, G, q.qkv.codes, q.qkv.scales, m->own);
+          launch_quantize((const uint16_t*)lw.wk, kvd, d, G, q.qkv.codes + (size_t)qd * (d / 8),
+                          q.qkv.scales + (size_t)qd * (d / G), m->own);
+          launch_quantize((const uint16_t*)lw.wv, kvd, d, G,
+                          q.qkv.codes + (size_t)(qd + kvd) * (d / 8),
+                          q.qkv.scales + (size_t)(qd + kvd) * (d / G), m->own);
+          launch_quantize((const uint16_t*)lw.wo, d, qd, G, q.o.codes, q.o.scales, m->own);
+          launch_quantize((const uint16_t*)lw.w_gate, F, d, G, q.gate.codes, q.gate.scales, m->own);
+          launch_quantize((const uint16_t*)lw.w_up, F, d, G, q.up.codes, q.up.scales, m->own);
+          launch_quantize((const uint16_t*)lw.w_down, d, F, G, q.down.codes, q.down.scales, m->own);
+          HIPCHK(hipGetLastError());
+        }
+      }
+      // RoPE table: cos/sin of pos * theta^(-2i/hd) in double, rounded to float
+      const int half = c.head_dim / 2;
+      std::vector<float> cs((size_t)c.max_positions * half), sn(cs.size());
+      for (int p = 0; p < c.max_positions; ++p)
+        for (int i = 0; i < half; ++i) {
+          const double inv = std::pow((double)c.rope_theta, -(2.0 * i) / c.head_dim);
+          const double ang = (double)p * inv;
+          cs[(size_t)p * half + i] = (float)std::cos(ang);
+          sn[(size_t)p * half + i] = (float)std::sin(ang);
+        }
+      m->d_cos = m->alloc<float>(cs.size());
+      m->d_sin = m->alloc<float>(sn.size());
+      HIPCHK(hipMemcpy(m->d_cos, cs.data(), cs.size() * 4, hipMemcpyHostToDevice));
+      HIPCHK(hipMemcpy(m->d_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice));
+      const int Bm = kMaxBatch;
+      m->h = m->alloc<float>((size_t)Bm * d);
+      m->hb = m->alloc<uint16_t>((size_t)Bm * d);
+      m->x = m->alloc<uint16_t>((size_t)Bm * d);
+      m->qkv = m->alloc<uint16_t>((size_t)Bm * (qd + 2 * kvd));
+      m->qrot = m->alloc<uint16_t>((size_t)Bm * qd);
+      m->attn_o = m->alloc<uint16_t>((size_t)Bm * qd);
+      m->act = m->alloc<uint16_t>((size_t)Bm * F);
+      m->z = m->alloc<uint16_t>((size_t)Bm * d);
+      m->head_part = m->alloc<float>((size_t)kNwg * kMaxBatch * 4);
+      m->nch_max = (c.max_positions + kAttnChunk - 1) / kAttnChunk;
+      m->attn_part = m->alloc<float>((size_t)c.max_batch * c.n_heads * m->nch_max * (c.head_dim + 2));
+      m->st = m->alloc<StepState>(1);
+      m->p_rec = m->alloc<float>((size_t)std::max(L - 1, 1) * kMaxBatch);
+      m->d_gamma = m->alloc<float>(std::max(L - 1, 1));
+      HIPCHK(hipMemset(m->st, 0, sizeof(StepState)));
+      if (L > 1)
+        HIPCHK(hipMemcpy(m->d_gamma, gam.data(), gam.size() * 4, hipMemcpyHostToDevice));
+      m->h_in = halloc<int32_t>(2 * kMaxBatch);
+      m->h_gamma = halloc<float>(std::max(L - 1, 1));
+      m->h_out = halloc<int32_t>(2 * kMaxBatch);
+      m->h_gap = halloc<float>(kMaxBatch);
+      HIPCHK(hipStreamSynchronize(m->own));
+    } catch (...) {
+      free_model(m);
+      throw;
+    }
+    *out = m;
+  });
+}
+
+ee_status ee_destroy_model(ee_model* m) {
+  return guard([&] {
+    if (!m) return;
+    if (m->ncaches > 0) fail(EE_ERR_INVALID_ARG, "destroy the model's caches first");
+    (void)hipStreamSynchronize(m->own);
+    free_model(m);
+  });
+}
+
+ee_status ee_kv_cache_bytes(const ee_model* m, int32_t max_batch, int32_t max_seq, size_t* bytes) {
+  return guard([&] {
+    if (!m || !bytes) fail(EE_ERR_INVALID_ARG, "null argument");
+    if (max_batch < 1 || max_batch > m->cfg.max_batch) fail(EE_ERR_INVALID_ARG, "max_batch out of range");
+    if (max_seq < 1 || max_seq > m->cfg.max_positions) fail(EE_ERR_INVALID_ARG, "max_seq out of range");
+    const size_t kv = (size_t)m->cfg.n_layers * max_batch * m->cfg.n_kv_heads * max_seq *
+                      m->cfg.head_dim * 2;
+    *bytes = 2 * kv + 256;
+  });
+}
+
+ee_status ee_kv_cache_create(ee_model* m, int32_t max_batch, int32_t max_seq, void* dev_buf,
+                             size_t buf_bytes, uint32_t flags, ee_kv_cache** out) {
+  return guard([&] {
+    check_model(m);
+    if (!out) fail(EE_ERR_INVALID_ARG, "null argument");
+    size_t need = 0;
+    ee_status st = ee_kv_cache_bytes(m, max_batch, max_seq, &need);
+    if (st != EE_OK) fail(st, g_err);
+    if (flags & ~EE_KV_TRACK_OCCUPANCY) fail(EE_ERR_INVALID_ARG, "unknown flags");
+    if (dev_buf && buf_bytes < need) fail(EE_ERR_INVALID_ARG, "buffer too small");
+    with_sticky(m, [&] {
+      ee_kv_cache* c = new ee_kv_cache();
+      try {
+        c->m = m;
+        c->Bmax = max_batch;
+        c->S = max_seq;
+        char* base = (char*)dev_buf;
+        if (!base) {
+          base = dalloc<char>(need);
+          c->owned = base;
+        }
+        const size_t kv = (need - 256) / 2;
+        c->K = (uint16_t*)base;
+        c->V = (uint16_t*)(base + kv);
+        c->lens = (int32_t*)(base + 2 * kv);
+        HIPCHK(hipMemsetAsync(c->lens, 0, 256, m->own));
+        if (flags & EE_KV_TRACK_OCCUPANCY) {
+          const size_t n = (size_t)m->cfg.n_layers * max_batch * max_seq;
+          c->occ = dalloc<uint8_t>(n);
+          HIPCHK(hipMemsetAsync(c->occ, 0, n, m->own));
+        }
+        HIPCHK(hipStreamSynchronize(m->own));
+        c->hlens.assign(max_batch, 0);
+      } catch (...) {
+        if (c->owned) (void)hipFree(c->owned);
+        if (c->occ) (void)hipFree(c->occ);
+        delete c;
+        throw;
+      }
+      m->ncaches++;
+      *out = c;
+    });
+  });
+}
+
+ee_status ee_kv_cache_reset(ee_kv_cache* c, int32_t seq) {
+  return guard([&] {
+    if (!c) fail(EE_ERR_INVALID_ARG, "null cache");
+    check_model(c->m);
+    if (seq < -1 || seq >= c->Bmax) fail(EE_ERR_INVALID_ARG, "seq out of range");
+    ee_model* m = c->m;
+    with_sticky(m, [&] {
+      const int lo = seq < 0 ? 0 : seq, hi = seq < 0 ? c->Bmax : seq + 1;
+      for (int b = lo; b < hi; ++b) c->hlens[b] = 0;
+      HIPCHK(hipMemcpyAsync(c->lens, c->hlens.data(), c->Bmax * 4, hipMemcpyHostToDevice, m->own));
+      if (c->occ)
+        for (int l = 0; l < m->cfg.n_layers; ++l)
+          HIPCHK(hipMemsetAsync(c->occ + ((size_t)l * c->Bmax + lo) * c->S, 0,
+                                (size_t)(hi - lo) * c->S, m->own));
+      HIPCHK(hipStreamSynchronize(m->own));
+    });
+  });
+}
+
+ee_status ee_kv_cache_lengths(const ee_kv_cache* c, int32_t* lens_host) {
+  return guard([&] {
+    if (!c || !lens_host) fail(EE_ERR_INVALID_ARG, "null argument");
+    std::memcpy(lens_host, c->hlens.data(), c->Bmax * 4);
+  });
+}
+
+ee_status ee_kv_cache_read(const ee_kv_cache* c, int32_t layer, int32_t seq, int32_t pos0, int32_t n,
+                           void* k_host, void* v_host) {
+  return guard([&] {
+    if (!c || !k_host || !v_host) fail(EE_ERR_INVALID_ARG, "null argument");
+    ee_model* m = c->m;
+    check_model(m);
+    const ee_model_config& cf = m->cfg;
+    if (layer < 1 || layer > cf.n_layers) fail(EE_ERR_INVALID_ARG, "layer out of range");
+    if (seq < 0 || seq >= c->Bmax) fail(EE_ERR_INVALID_ARG, "seq out of range");
+    if (pos0 < 0 || n < 0 || pos0 + n > c->S) fail(EE_ERR_INVALID_ARG, "positions out of range");
+    if (n == 0) return;
+    with_sticky(m, [&] {
+      if (c->occ) {
+        std::vector<uint8_t> occ(n);
+        HIPCHK(hipMemcpy(occ.data(), c->occ + ((size_t)(layer - 1) * c->Bmax + seq) * c->S + pos0, n,
+                         hipMemcpyDeviceToHost));
+        for (int i = 0; i < n; ++i)
+          if (occ[i] == 0) fail(EE_ERR_NOT_WRITTEN, "KV slot never written");
+      }
+      const int Hkv = cf.n_kv_heads, hd = cf.head_dim;
+      for (int kh = 0; kh < Hkv; ++kh) {
+        const size_t off = ((((size_t)(layer - 1) * c->Bmax + seq) * Hkv + kh) * c->S + pos0) * hd;
+        HIPCHK(hipMemcpy2D((uint16_t*)k_host + kh * hd, (size_t)Hkv * hd * 2, c->K + off, (size_t)hd * 2,
+                           (size_t)hd * 2, n, hipMemcpyDeviceToHost));
+        HIPCHK(hipMemcpy2D((uint16_t*)v_host + kh * hd, (size_t)Hkv * hd * 2, c->V + off, (size_t)hd * 2,
+                           (size_t)hd * 2, n, hipMemcpyDeviceToHost));
+      }
+    });
+  });
+}
+
+ee_status ee_kv_cache_occupancy(const ee_kv_cache* c, uint8_t* counts_host) {
+  return guard([&] {
+    if (!c || !counts_host) fail(EE_ERR_INVALID_ARG, "null argument");
+    check_model(c->m);
+    if (!c->occ) fail(EE_ERR_UNSUPPORTED, "cache created without occupancy tracking");
+    with_sticky(c->m, [&] {
+      HIPCHK(hipMemcpy(counts_host, c->occ, (size_t)c->m->cfg.n_layers * c->Bmax * c->S,
+                       hipMemcpyDeviceToHost));
+    });
+  });
+}
+
+ee_status ee_kv_cache_destroy(ee_kv_cache* c) {
+  return guard([&] {
+    if (!c) return;
+    (void)hipStreamSynchronize(c->m->own);
+    if (c->owned) (void)hipFree(c->owned);
+    if (c->occ) (void)hipFree(c->occ);
+    c->m->ncaches--;
+    delete c;
+  });
+}
+
+ee_status ee_prefill(ee_model* m, ee_kv_cache* c, int32_t batch, const int32_t* tokens_host, int32_t P,
+                     void* hip_stream, int32_t* out_tokens_host) {
+  return guard([&] {
+    check_model(m);
+    if (!c || c->m != m) fail(EE_ERR_INVALID_ARG, "cache does not belong to the model");
+    if (!tokens_host || !out_tokens_host) fail(EE_ERR_INVALID_ARG, "null argument");
+    if (batch < 1 || batch > c->Bmax) fail(EE_ERR_INVALID_ARG, "batch out of range");
+    if (P < 1) fail(EE_ERR_INVALID_ARG, "P must be >= 1");
+    const int V = m->cfg.vocab;
+    for (size_t i = 0; i < (size_t)batch * P; ++i)
+      if (tokens_host[i] < 0 || tokens_host[i] >= V) fail(EE_ERR_INVALID_ARG, "token out of range");
+    for (int b = 0; b < batch; ++b)
+      if ((long long)c->hlens[b] + P > c->S) fail(EE_ERR_CACHE_FULL, "prefill exceeds max_seq");
+    with_sticky(m, [&] {
+      hipStream_t s = pick_stream(m, hip_stream);
+      const size_t n = (size_t)batch * P;
+      if (n > m->prompt_cap) {
+        if (m->d_prompt) {
+          (void)hipFree(m->d_prompt);
+          for (auto& p : m->allocs)
+            if (p == m->d_prompt) p = nullptr;
+        }
+        m->d_prompt = m->alloc<int32_t>(n);
+        m->prompt_cap = n;
+      }
+      HIPCHK(hipMemcpyAsync(m->d_prompt, tokens_host, n * 4, hipMemcpyHostToDevice, s));
+      for (int b = 0; b < batch; ++b) m->h_in[kMaxBatch + b] = 0;
+      HIPCHK(hipMemcpyAsync(m->st->forced, m->h_in + kMaxBatch, batch * 4, hipMemcpyHostToDevice, s));
+      Debug dbg;
+      for (int t = 0; t < P; ++t)
+        enqueue_position(m, c, batch, false, t == P - 1, m->d_prompt, P, t, dbg, s);
+      HIPCHK(hipMemcpyAsync(m->h_out, m->st->out_tok, batch * 4, hipMemcpyDeviceToHost, s));
+      HIPCHK(hipStreamSynchronize(s));
+      m->ev_used = 0;
+      std::memcpy(out_tokens_host, m->h_out, batch * 4);
+      for (int b = 0; b < batch; ++b) c->hlens[b] += P;
+    });
+  });
+}
+
+ee_status ee_decode_step(ee_model* m, ee_kv_cache* c, int32_t batch, const int32_t* in_tokens_host,
+                         const int32_t* forced_exit_host, const float* gamma_host, void* hip_stream,
+                         int32_t* out_tokens_host, int32_t* out_exit_layers_host, ee_step_debug* dbg) {
+  return guard([&] {
+    check_model(m);
+    if (!c || c->m != m) fail(EE_ERR_INVALID_ARG, "cache does not belong to the model");
+    if (!out_tokens_host || !out_exit_layers_host) fail(EE_ERR_INVALID_ARG, "null output");
+    if (batch < 1 || batch > c->Bmax) fail(EE_ERR_INVALID_ARG, "batch out of range");
+    const ee_model_config& cf = m->cfg;
+    const int L = cf.n_layers;
+    if (in_tokens_host)
+      for (int b = 0; b < batch; ++b)
+        if (in_tokens_host[b] < 0 || in_tokens_host[b] >= cf.vocab)
+          fail(EE_ERR_INVALID_ARG, "token out of range");
+    if (forced_exit_host)
+      for (int b = 0; b < batch; ++b)
+        if (forced_exit_host[b] < 0 || forced_exit_host[b] > L)
+          fail(EE_ERR_INVALID_ARG, "forced exit layer out of range");
+    if (gamma_host)
+      for (int l = 0; l < L - 1; ++l)
+        if (!std::isfinite(gamma_host[l])) fail(EE_ERR_INVALID_ARG, "gamma must be finite");
+    for (int b = 0; b < batch; ++b)
+      if (c->hlens[b] + 1 > c->S) fail(EE_ERR_CACHE_FULL, "sequence " + std::to_string(b) + " is full");
+    with_sticky(m, [&] {
+      hipStream_t s = pick_stream(m, hip_stream);
+      Debug dd;
+      if (dbg) {
+        dd.hidden = dbg->hidden != nullptr;
+        dd.logits = dbg->logits != nullptr;
+        if (dd.hidden && !m->dbg_hidden)
+          m->dbg_hidden = m->alloc<float>((size_t)kMaxBatch * (L + 1) * cf.d_model);
+        if (dd.logits && !m->dbg_logits) m->dbg_logits = m->alloc<float>((size_t)kMaxBatch * cf.vocab);
+      }
+      // inputs of the step
+      for (int b = 0; b < batch; ++b) {
+        m->h_in[b] = in_tokens_host ? in_tokens_host[b] : 0;
+        m->h_in[kMaxBatch + b] = forced_exit_host ? forced_exit_host[b] : 0;
+      }
+      for (int l = 0; l < L - 1; ++l) m->h_gamma[l] = gamma_host ? gamma_host[l] : m->gamma[l];
+      if (in_tokens_host)
+        HIPCHK(hipMemcpyAsync(m->st->tok, m->h_in, batch * 4, hipMemcpyHostToDevice, s));
+      HIPCHK(hipMemcpyAsync(m->st->forced, m->h_in + kMaxBatch, batch * 4, hipMemcpyHostToDevice, s));
+      if (L > 1)
+        HIPCHK(hipMemcpyAsync(m->d_gamma, m->h_gamma, (L - 1) * 4, hipMemcpyHostToDevice, s));
+      enqueue_position(m, c, batch, true, true, nullptr, 1, 0, dd, s);
+      HIPCHK(hipMemcpyAsync(m->h_out, m->st->out_tok, batch * 4, hipMemcpyDeviceToHost, s));
+      HIPCHK(hipMemcpyAsync(m->h_out + kMaxBatch, m->st->e, batch * 4, hipMemcpyDeviceToHost, s));
+      HIPCHK(hipMemcpyAsync(m->h_gap, m->st->gap, batch * 4, hipMemcpyDeviceToHost, s));
+      std::vector<float> prec;
+      if (dbg && dbg->p_top1 && L > 1) {
+        prec.resize((size_t)(L - 1) * kMaxBatch);
+        HIPCHK(hipMemcpyAsync(prec.data(), m->p_rec, prec.size() * 4, hipMemcpyDeviceToHost, s));
+      }
+      if (dd.logits)
+        HIPCHK(hipMemcpyAsync(dbg->logits, m->dbg_logits, (size_t)batch * cf.vocab * 4,
+                              hipMemcpyDeviceToHost, s));
+      if (dd.hidden)
+        HIPCHK(hipMemcpyAsync(dbg->hidden, m->dbg_hidden, (size_t)batch * (L + 1) * cf.d_model * 4,
+                              hipMemcpyDeviceToHost, s));
+      HIPCHK(hipStreamSynchronize(s));
+      prof_collect(m);
+      std::memcpy(out_tokens_host, m->h_out, batch * 4);
+      std::memcpy(out_exit_layers_host, m->h_out + kMaxBatch, batch * 4);
+      if (dbg && dbg->gap) std::memcpy(dbg->gap, m->h_gap, batch * 4);
+      if (dbg && dbg->p_top1)
+        for (int b = 0; b < batch; ++b)
+          for (int l = 0; l < L - 1; ++l) dbg->p_top1[(size_t)b * (L - 1) + l] = prec[(size_t)l * kMaxBatch + b];
+      for (int b = 0; b < batch; ++b) c->hlens[b] += 1;
+    });
+  });
+}
+
+ee_status ee_exit_weights_read(const ee_model* m, int32_t layer, int32_t which, int32_t row0, int32_t nrows,
+                               int8_t* codes_host, uint16_t* scales_host) {
+  return guard([&] {
+    check_model(m);
+    if (!codes_host || !scales_host) fail(EE_ERR_INVALID_ARG, "null argument");
+    const ee_model_config& cf = m->cfg;
+    if (cf.exit_mode != EE_EXIT_INT4) fail(EE_ERR_UNSUPPORTED, "no int4 copies in EE_EXIT_BF16 mode");
+    if (layer < 2 || layer > cf.n_layers) fail(EE_ERR_INVALID_ARG, "layer must be in [2, L]");
+    const LayerQ& q = m->lq[layer - 1];
+    const int qd = cf.n_heads * cf.head_dim, kvd = cf.n_kv_heads * cf.head_dim;
+    const Q4* src = nullptr;
+    int off = 0, N = 0;
+    switch (which) {
+      case 0: src = &q.qkv; off = 0; N = qd; break;
+      case 1: src = &q.qkv; off = qd; N = kvd; break;
+      case 2: src = &q.qkv; off = qd + kvd; N = kvd; break;
+      case 3: src = &q.o; N = src->N; break;
+      case 4: src = &q.gate; N = src->N; break;
+      case 5: src = &q.up; N = src->N; break;
+      case 6: src = &q.down; N = src->N; break;
+      default: fail(EE_ERR_INVALID_ARG, "which must be in [0, 6]");
+    }
+    if (row0 < 0 || nrows < 0 || row0 + nrows > N) fail(EE_ERR_INVALID_ARG, "rows out of range");
+    if (nrows == 0) return;
+    const int K = src->K, G = cf.group_size;
+    ee_model* mm = const_cast<ee_model*>(m);
+    with_sticky(mm, [&] {
+      int8_t* tmp = dalloc<int8_t>((size_t)nrows * K);
+      launch_unpack_codes(src->codes, src->N, K, off + row0, nrows, tmp, mm->own);
+      hipError_t e1 = hipStreamSynchronize(mm->own);
+      hipError_t e2 = hipMemcpy(codes_host, tmp, (size_t)nrows * K, hipMemcpyDeviceToHost);
+      (void)hipFree(tmp);
+      HIPCHK(e1);
+      HIPCHK(e2);
+      HIPCHK(hipMemcpy(scales_host, src->scales + (size_t)(off + row0) * (K / G), (size_t)nrows * (K / G) * 2,
+                       hipMemcpyDeviceToHost));
+    });
+  });
+}
+
+ee_status ee_profile_enable(ee_model* m, int32_t on) {
+  return guard([&] {
+    check_model(m);
+    m->prof = on != 0;
+    m->prof_launches = 0;
+    m->prof_ms = 0;
+    m->ev_used = 0;
+  });
+}
+
+ee_status ee_profile_read(ee_model* m, int32_t kind, int64_t* launches, double* total_ms) {
+  return guard([&] {
+    check_model(m);
+    if (!launches || !total_ms) fail(EE_ERR_INVALID_ARG, "null argument");
+    if (kind != 0) fail(EE_ERR_INVALID_ARG, "unknown kind");
+    *launches = m->prof_launches;
+    *total_ms = m->prof_ms;
+    m->prof_launches = 0;
+    m->prof_ms = 0;
+  });
+}
+
+}  // extern "C"

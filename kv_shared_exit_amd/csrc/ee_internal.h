@@ -1,0 +1,86 @@
+// Internal interface between the host orchestration (ee_api.hip) and the
+// gfx950 kernels (ee_kernels.hip).  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ee {
+
+constexpr int kMaxBatch = 64;      // rows of one decode step
+constexpr int kProjThreads = 256;  // 4 waves per projection workgroup
+constexpr int kAttnChunk = 256;    // positions per attention workgroup (4 waves x 64)
+constexpr int kXLdsElems = 32768;  // bf16 elements of the staged GEMV input (64 KB)
+constexpr int kXgElems = 4096;     // int4 group sums held in LDS
+constexpr int kNib = 2048;         // elements covered by one 16-byte-per-lane int4 block
+
+enum Epi { EPI_BF16 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LSE = 3, EPI_ARGMAX = 4 };
+
+// Device-resident state of one step.  Every value that changes from step to
+// step lives here, so a captured graph replays unchanged.
+struct StepState {
+  int32_t tok[kMaxBatch];      // input token of the step (next input after it)
+  int32_t forced[kMaxBatch];   // 0: exit head decides; 1..L: forced exit layer
+  int32_t exited[kMaxBatch];
+  int32_t e[kMaxBatch];        // exit layer
+  int32_t act[kMaxBatch];      // rows on the backbone (bf16 weights)
+  int32_t ex[kMaxBatch];       // rows on the exit copies (int4 weights)
+  int32_t all[kMaxBatch];      // 0..B-1
+  int32_t n_act, n_ex, n_all, pad;
+  int32_t out_tok[kMaxBatch];
+  float gap[kMaxBatch];
+};
+
+struct ProjArgs {
+  int N, K, G;
+  int nseg;              // bf16 row segments (QKV: 3)
+  int seg_end[3];        // cumulative end row of each segment
+  const uint16_t* wb[3]; // bf16 segment bases, row-major [rows][K]
+  const uint16_t* wb2;   // SwiGLU: the "up" matrix (gate is wb[0])
+  const uint32_t* q4;    // int4 codes [N][K/8] dwords (permuted blocks, see quantize kernel)
+  const uint16_t* s4;    // bf16 scales [N][K/G]
+  const uint32_t* q4b;   // SwiGLU "up" codes
+  const uint16_t* s4b;
+  const uint16_t* x;     // bf16 input rows, indexed by sequence id
+  int x_stride;
+  const int32_t* list_bf; const int32_t* cnt_bf;  // rows run with bf16 weights
+  const int32_t* list_i4; const int32_t* cnt_i4;  // rows run with int4 weights (may be null)
+  void* y; int y_stride;                          // output rows, indexed by sequence id
+  uint16_t* y2; int y2_stride;                    // EPI_RESID: bf16 copy of the new residual
+  float* part;                                    // EPI_LSE / EPI_ARGMAX partials per workgroup
+  float* logits; int logits_stride;               // EPI_ARGMAX: optional logits out
+  float* prof_dummy;
+};
+
+struct AttnArgs {
+  const uint16_t* q;   // rotated q [b][H*hd]
+  const uint16_t* K;   // layer base of the cache: [Bmax][Hkv][S][hd]
+  const uint16_t* V;
+  int S, Bmax;
+  const int32_t* lens; // position of the current token per sequence
+  int H, Hkv, hd, B, nch;
+  float scale;
+  float* part;         // [B][H][nch][hd + 2]
+  uint16_t* out;       // [b][H*hd]
+};
+
+// launchers (ee_kernels.hip)
+void launch_proj(int epi, const ProjArgs& a, int nwg, hipStream_t s);
+void launch_init(StepState* st, const int32_t* prompt, int P, int t, int B, int L,
+                 const uint16_t* emb, int d, int V, float* h, float* p_rec, hipStream_t s);
+void launch_rmsnorm(const float* h, const uint16_t* g, uint16_t* x, int B, int d, float eps,
+                    hipStream_t s);
+void launch_rope_kv(const uint16_t* qkv, uint16_t* qrot, uint16_t* Kl, uint16_t* Vl,
+                    uint8_t* occ_l, const int32_t* lens, const float* cosT, const float* sinT,
+                    int B, int H, int Hkv, int hd, int S, int Bmax, hipStream_t s);
+void launch_attention(const AttnArgs& a, hipStream_t s);
+void launch_decide(StepState* st, const float* part, int nwg, const float* gamma, int layer,
+                   int L, int B, float* p_rec, hipStream_t s);
+void launch_final(StepState* st, const float* part, int nwg, int B, int V, int32_t* lens, int advance,
+                  hipStream_t s);
+void launch_advance(int32_t* lens, int B, hipStream_t s);
+void launch_quantize(const uint16_t* w, int N, int K, int G, uint32_t* codes, uint16_t* scales,
+                     hipStream_t s);
+void launch_unpack_codes(const uint32_t* codes, int N, int K, int row0, int nrows, int8_t* out,
+                         hipStream_t s);
+
+}  // namespace ee

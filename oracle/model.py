@@ -267,7 +267,8 @@ def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=N
     ``forced``: optional int [B]; 0 lets the exit head decide, 1..L forces the
     exit layer (the heads still run; their decision is overridden).
     Returns ``(tokens [B], exit_layers [B], info)`` where info holds
-    ``p`` [B, L-1] (NaN where no head ran), ``gap`` [B], ``logits`` [B, V] and,
+    ``p`` [B, L-1] (NaN where no head ran), ``head_absmax`` [B, L-1] (largest
+    |logit| of each evaluated exit head), ``gap`` [B], ``logits`` [B, V] and,
     with ``trace``, ``hidden`` [B, L+1, d] (after the embedding and after every
     layer).
     """
@@ -285,6 +286,7 @@ def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=N
     exited = np.zeros(B, dtype=bool)
     e = np.full(B, L, dtype=np.int32)
     p_rec = np.full((B, L - 1), np.nan)
+    head_max = np.full((B, L - 1), np.nan)
     hidden = [h.copy()] if trace else None
     for l in range(1, L + 1):
         bb = np.nonzero(~exited)[0]
@@ -294,8 +296,9 @@ def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=N
         if len(ex):
             _layer_rows(model, cache, l, ex, h, pos, use_exit=True)
         if l < L and len(bb):
-            p, _ = exit_head(model, l, h[bb])
+            p, hl = exit_head(model, l, h[bb])
             p_rec[bb, l - 1] = p
+            head_max[bb, l - 1] = np.abs(hl).max(axis=-1)
             for i, b in enumerate(bb):
                 go = (l == forced[b]) if forced[b] > 0 else (p[i] > gamma[l - 1])
                 if go:
@@ -305,7 +308,7 @@ def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=N
             hidden.append(h.copy())
     tok, gap, logits = final_head(model, h)
     cache.lens[:B] += 1
-    info = {"p": p_rec, "gap": gap, "logits": logits}
+    info = {"p": p_rec, "head_absmax": head_max, "gap": gap, "logits": logits}
     if trace:
         info["hidden"] = np.stack(hidden, axis=1)
     return tok, e, info

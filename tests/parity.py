@@ -1,0 +1,154 @@
+"""GPU-vs-oracle parity protocol shared by the GPU tests.
+
+Both sides get the same seeded weights and prompts.  At every decode step the
+oracle runs first; its token is fed to both sides (teacher forcing), and where
+an exit decision of the oracle lies within 1e-3 of gamma the GPU is forced to
+the oracle's exit layer for that sequence.  Then:
+  * exit layers must match exactly (every row; forced rows trivially),
+  * tokens must match exactly where the oracle's top-2 logit gap exceeds 1e-2,
+  * KV slot occupancy must match exactly,
+  * logits, hidden states (after every layer) and K/V must agree within a max
+    relative error of 2e-2 (max |gpu - oracle| / max |oracle| per tensor),
+  * exit-head probabilities must agree to what the logit tolerance implies:
+    p = 1 / sum_v exp(l_v - max l), so perturbing every logit by at most d
+    moves ln p by at most 2 d; with d = 2e-2 * max|l| of the head,
+    |ln p_gpu - ln p_oracle| <= 4e-2 * max|l|.
+"""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+
+import synth
+from oracle import model as om
+from oracle.numerics import from_bf16_bits
+
+TOL = 2e-2
+GAP_BAND = 1e-2
+P_BAND = 1e-3
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def maxrel(a, r):
+    a = np.asarray(a, np.float64)
+    r = np.asarray(r, np.float64)
+    den = np.abs(r).max()
+    if den == 0:
+        return float(np.abs(a).max())
+    return float(np.abs(a - r).max() / den)
+
+
+class Result:
+    def __init__(self):
+        self.compared_tokens = 0
+        self.tie_tokens = 0
+        self.forced_rows = 0
+        self.exits = []
+        self.worst = {}
+
+    def note(self, key, v):
+        self.worst[key] = max(self.worst.get(key, 0.0), v)
+
+
+def run_parity(shape, weights, batch, P, steps, gamma, exit_mode="int4", forced_fn=None,
+               prompts=None, max_seq=None, check_kv=True, check_hidden=True, label=""):
+    import torch
+    from kv_shared_exit_amd import api, _binding as B
+
+    L = shape.n_layers
+    S = max_seq or (P + steps + 1)
+    mode = B.EE_EXIT_INT4 if exit_mode == "int4" else B.EE_EXIT_BF16
+    t0 = time.time()
+    dev = api.upload_weights(weights)
+    model = api.Model(shape, dev, gamma=gamma, exit_mode=mode, max_batch=batch, max_positions=S)
+    cache = api.KVCache(model, batch, S, track=True)
+    orc = om.OracleModel(shape, weights, exit_mode=exit_mode)
+    ocache = om.KVCache(shape, batch, S)
+    if prompts is None:
+        prompts = np.random.default_rng(123).integers(0, shape.vocab, (batch, P)).astype(np.int32)
+    res = Result()
+    stream = torch.cuda.Stream()
+    try:
+        tg = api.prefill(model, cache, prompts, stream=stream)
+        to, info = om.prefill(orc, ocache, prompts)
+        for b in range(batch):
+            if info["gap"][b] > GAP_BAND:
+                assert tg[b] == to[b], f"{label} prefill token b={b}: gpu {tg[b]} oracle {to[b]}"
+                res.compared_tokens += 1
+            else:
+                res.tie_tokens += 1
+        log(f"[{label}] prefill P={P} B={batch} ok ({time.time() - t0:.1f}s)")
+        tok_in = to.astype(np.int32)
+        gam = np.broadcast_to(np.asarray(gamma, np.float64), (L - 1,))
+        for s in range(steps):
+            forced = np.zeros(batch, np.int32) if forced_fn is None else np.asarray(forced_fn(s), np.int32)
+            to, eo, io = om.decode_step(orc, ocache, tok_in, gamma=gam, forced=forced, trace=check_hidden)
+            fg = forced.copy()
+            for b in range(batch):
+                if forced[b] == 0:
+                    pe = io["p"][b]
+                    ok = np.isfinite(pe)
+                    if np.any(np.abs(pe[ok] - gam[ok]) <= P_BAND):
+                        fg[b] = eo[b]
+                        res.forced_rows += 1
+            dbg = {"p": None, "logits": None, "gap": None}
+            if check_hidden:
+                dbg["hidden"] = None
+            tgpu, egpu = api.decode_step(model, cache, batch, tokens=tok_in, forced=fg, gamma=gam,
+                                         stream=stream, debug=dbg)
+            np.testing.assert_array_equal(egpu, eo, err_msg=f"{label} step {s} exit layers")
+            for b in range(batch):
+                if io["gap"][b] > GAP_BAND:
+                    assert tgpu[b] == to[b], (f"{label} step {s} b={b}: token gpu {tgpu[b]} oracle "
+                                              f"{to[b]} gap {io['gap'][b]:.3g}")
+                    res.compared_tokens += 1
+                else:
+                    res.tie_tokens += 1
+                e = maxrel(dbg["logits"][b], io["logits"][b])
+                res.note("logits", e)
+                assert e <= TOL, f"{label} step {s} b={b} logits maxrel {e:.3g}"
+                if check_hidden:
+                    for l in range(L + 1):
+                        e = maxrel(dbg["hidden"][b, l], io["hidden"][b, l])
+                        res.note("hidden", e)
+                        assert e <= TOL, f"{label} step {s} b={b} hidden after layer {l}: maxrel {e:.3g}"
+                pg, po = dbg["p"][b, :L - 1], io["p"][b]
+                np.testing.assert_array_equal(np.isnan(pg), np.isnan(po),
+                                              err_msg=f"{label} step {s} b={b} heads evaluated")
+                ok = np.isfinite(po)
+                if ok.any():
+                    e = float(np.abs(pg[ok] - po[ok]).max())
+                    res.note("p_abs", e)
+                    dl = np.abs(np.log(pg[ok]) - np.log(po[ok]))
+                    bound = 2 * TOL * io["head_absmax"][b][ok]
+                    res.note("lnp_over_bound", float((dl / bound).max()))
+                    assert np.all(dl <= bound), f"{label} step {s} b={b} ln p err {dl.max():.3g}"
+            res.exits.append(eo.copy())
+            tok_in = to.astype(np.int32)
+        log(f"[{label}] {steps} decode steps ok ({time.time() - t0:.1f}s) worst={res.worst} "
+            f"tokens compared={res.compared_tokens} ties={res.tie_tokens} forced={res.forced_rows}")
+        occ = cache.occupancy()
+        n = P + steps
+        np.testing.assert_array_equal(occ[:, :batch, :n], ocache.occ[:, :batch, :n].astype(np.uint8))
+        assert np.all(occ[:, :batch, n:] == 0)
+        if check_kv:
+            for l in range(1, L + 1):
+                for b in range(batch):
+                    k, v = cache.read(l, b, 0, n)
+                    kr = ocache.K[l - 1, b, :, :n].transpose(1, 0, 2)
+                    vr = ocache.V[l - 1, b, :, :n].transpose(1, 0, 2)
+                    ek = maxrel(from_bf16_bits(k), kr)
+                    ev = maxrel(from_bf16_bits(v), vr)
+                    res.note("kv", max(ek, ev))
+                    assert ek <= TOL and ev <= TOL, f"{label} KV layer {l} seq {b}: {ek:.3g} {ev:.3g}"
+        log(f"[{label}] KV/occupancy ok ({time.time() - t0:.1f}s) worst={res.worst}")
+    finally:
+        cache.close()
+        model.close()
+    return res

@@ -1,0 +1,149 @@
+"""GPU tests of the C ABI: int4 copies bit-exact vs the oracle, error paths, self-consistency."""
+import numpy as np
+import pytest
+
+import synth
+from synth import ModelShape
+from oracle.quant import quantize_int4
+from oracle.numerics import from_bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+ODD = ModelShape(3, 160, 5, 1, 32, 224, 1003, 32, rope_theta=500000.0)
+MID = ModelShape(3, 2048, 16, 4, 128, 5120, 5000, 128, rope_theta=500000.0)
+G64 = ModelShape(2, 4352, 32, 2, 128, 2176, 300, 64)   # K = 4352: two full int4 blocks + a 256 tail
+
+
+@pytest.fixture(scope="module")
+def api():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_shared_exit_amd import api as A
+    return A
+
+
+def _model(api, sh, seed=3, alpha=None, **kw):
+    w = synth.make_weights(sh, seed, alpha=alpha)
+    dev = api.upload_weights(w)
+    return w, api.Model(sh, dev, **kw)
+
+
+@pytest.mark.parametrize("sh", [ODD, MID, G64], ids=["odd", "mid", "g64"])
+def test_int4_copies_bit_exact(api, sh):
+    w, m = _model(api, sh, max_batch=2, max_positions=8)
+    try:
+        for l in range(2, sh.n_layers + 1):
+            for name in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down"):
+                codes, scales = m.exit_weights(l, name)
+                q, s = quantize_int4(from_bf16_bits(w["layers"][l - 1][name]), sh.group)
+                np.testing.assert_array_equal(codes, q, err_msg=f"codes layer {l} {name}")
+                np.testing.assert_array_equal(from_bf16_bits(scales), s, err_msg=f"scales layer {l} {name}")
+    finally:
+        m.close()
+
+
+def test_error_paths_leave_state_unchanged(api):
+    from kv_shared_exit_amd import _binding as B
+    sh = ODD
+    w, m = _model(api, sh, max_batch=2, max_positions=8)
+    c = api.KVCache(m, 2, 6, track=True)
+    try:
+        prompts = np.array([[1, 2, 3], [4, 5, 6]], np.int32)
+        api.prefill(m, c, prompts)
+        assert list(c.lengths()) == [3, 3]
+        with pytest.raises(B.EEError) as e:
+            api.decode_step(m, c, 2, tokens=[1, sh.vocab])
+        assert e.value.status == B.EE_ERR_INVALID_ARG
+        with pytest.raises(B.EEError) as e:
+            api.decode_step(m, c, 2, tokens=[1, 2], forced=[0, sh.n_layers + 1])
+        assert e.value.status == B.EE_ERR_INVALID_ARG
+        with pytest.raises(B.EEError) as e:
+            api.decode_step(m, c, 3, tokens=[1, 2, 3])
+        assert e.value.status == B.EE_ERR_INVALID_ARG
+        with pytest.raises(B.EEError) as e:
+            api.prefill(m, c, np.zeros((2, 4), np.int32))   # 3 + 4 > 6
+        assert e.value.status == B.EE_ERR_CACHE_FULL
+        assert list(c.lengths()) == [3, 3]
+        for _ in range(3):
+            api.decode_step(m, c, 2)
+        assert list(c.lengths()) == [6, 6]
+        with pytest.raises(B.EEError) as e:
+            api.decode_step(m, c, 2)
+        assert e.value.status == B.EE_ERR_CACHE_FULL
+        assert list(c.lengths()) == [6, 6]
+        occ = c.occupancy()
+        assert np.all(occ[:, :, :6] == 1)
+        c.reset(1)
+        assert list(c.lengths()) == [6, 0]
+        with pytest.raises(B.EEError) as e:
+            c.read(1, 1, 0, 1)
+        assert e.value.status == B.EE_ERR_NOT_WRITTEN
+        k, v = c.read(2, 0, 0, 6)
+        assert k.shape == (6, sh.n_kv_heads, sh.head_dim)
+        # a model with live caches cannot be destroyed
+        with pytest.raises(B.EEError):
+            m.close()
+    finally:
+        c.close()
+        m.close()
+
+
+def test_cache_without_tracking_has_no_occupancy(api):
+    from kv_shared_exit_amd import _binding as B
+    w, m = _model(api, ODD, max_batch=1, max_positions=4)
+    c = api.KVCache(m, 1, 4, track=False, torch_buffer=False)
+    try:
+        with pytest.raises(B.EEError) as e:
+            c.occupancy()
+        assert e.value.status == B.EE_ERR_UNSUPPORTED
+    finally:
+        c.close()
+        m.close()
+
+
+def _run(api, sh, w, mode, gamma, B_, P, steps, forced=None, graph=False):
+    import torch
+    dev = api.upload_weights(w)
+    m = api.Model(sh, dev, gamma=gamma, exit_mode=mode, max_batch=B_, max_positions=P + steps + 1)
+    c = api.KVCache(m, B_, P + steps + 1)
+    prompts = np.random.default_rng(7).integers(0, sh.vocab, (B_, P)).astype(np.int32)
+    st = torch.cuda.Stream()
+    out = []
+    try:
+        tok = api.prefill(m, c, prompts, stream=st)
+        for s in range(steps):
+            dbg = {"logits": None, "p": None} if not graph else None
+            t, e = api.decode_step(m, c, B_, forced=None if forced is None else forced(s),
+                                   stream=st, debug=dbg)
+            out.append((t.copy(), e.copy(), None if dbg is None else dbg["logits"].copy()))
+    finally:
+        c.close()
+        m.close()
+    return out
+
+
+def test_no_exit_equals_unquantised_exit_copies_bitwise(api):
+    """gamma > 1 (nobody exits) and unquantised exit copies run the same arithmetic: bitwise equal."""
+    from kv_shared_exit_amd import _binding as B
+    sh = MID
+    w = synth.make_weights(sh, 5, alpha=np.full(sh.n_layers - 1, 1e3))
+    a = _run(api, sh, w, B.EE_EXIT_INT4, 1.5, 3, 6, 4)
+    b = _run(api, sh, w, B.EE_EXIT_BF16, 0.1, 3, 6, 4)
+    for (ta, ea, la), (tb, eb, lb) in zip(a, b):
+        assert np.all(ea == sh.n_layers)
+        np.testing.assert_array_equal(ta, tb)
+        np.testing.assert_array_equal(la, lb)
+
+
+def test_two_runs_are_bitwise_identical(api):
+    from kv_shared_exit_amd import _binding as B
+    sh = ODD
+    w = synth.make_weights(sh, 6, alpha=np.full(sh.n_layers - 1, 3000.0))
+    rng = lambda s: np.random.default_rng(s).integers(0, sh.n_layers + 1, 4).astype(np.int32)
+    a = _run(api, sh, w, B.EE_EXIT_INT4, 0.75, 4, 5, 6, forced=rng)
+    b = _run(api, sh, w, B.EE_EXIT_INT4, 0.75, 4, 5, 6, forced=rng)
+    for (ta, ea, la), (tb, eb, lb) in zip(a, b):
+        np.testing.assert_array_equal(ta, tb)
+        np.testing.assert_array_equal(ea, eb)
+        np.testing.assert_array_equal(la, lb)

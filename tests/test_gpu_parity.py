@@ -1,0 +1,86 @@
+"""GPU parity of the whole decode step against the oracle (runs through the C ABI)."""
+import numpy as np
+import pytest
+
+import synth
+from synth import ModelShape, Workload
+from oracle.calibrate import calibrate
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = {
+    "tiny": synth.TINY,
+    # widths that are not multiples of any tile, one kv head for five q heads,
+    # int4 rows shorter than one 2048-element block, a ragged vocabulary
+    "odd": ModelShape(3, 160, 5, 1, 32, 224, 1003, 32, rope_theta=500000.0),
+    # full int4 blocks plus a tail (5120 = 2*2048 + 1024), an input wider than
+    # the LDS-staged limit (down projection K = 5120), head_dim 128, 4 q per kv head
+    "mid": ModelShape(3, 2048, 16, 4, 128, 5120, 5000, 128, rope_theta=500000.0),
+    # head_dim 64 with 8 kv heads, group 64
+    "hd64": ModelShape(2, 512, 8, 8, 64, 1024, 2048, 64, rope_theta=10000.0),
+}
+
+
+def _weights(name, mean_exit, P, steps, gamma=0.75, seed=5):
+    sh = SHAPES[name]
+    wl = Workload(name, sh, 1, P, steps + 1, gamma, "calibrated", mean_exit, index=seed)
+    cal = calibrate(wl, verbose=False)
+    return sh, synth.make_weights(sh, seed, alpha=np.array(cal["alpha"]))
+
+
+@pytest.fixture(scope="module")
+def gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_shared_exit_amd import _binding
+    _binding.load()
+    return torch
+
+
+def test_tiny_workload_full_generation(gpu):
+    from parity import run_parity
+    wl = synth.workload("tiny")
+    sh = wl.shape
+    alpha = synth.load_alpha(wl)
+    w = synth.make_weights(sh, wl.seed_weights, alpha=alpha)
+    res = run_parity(sh, w, 1, wl.prompt_len, wl.decode_steps, wl.gamma,
+                     prompts=synth.make_prompts(wl), label="tiny")
+    assert res.compared_tokens >= 20
+
+
+@pytest.mark.parametrize("name,batch,P,steps", [("tiny", 3, 9, 8), ("odd", 4, 7, 6),
+                                                ("hd64", 5, 40, 4)])
+def test_small_shapes_batched(gpu, name, batch, P, steps):
+    from parity import run_parity
+    sh, w = _weights(name, 2.0, P, steps)
+    res = run_parity(sh, w, batch, P, steps, 0.75, label=name)
+    ex = np.stack(res.exits)
+    assert ex.min() < sh.n_layers     # some exits happened
+
+
+def test_mid_shape_long_context(gpu):
+    """Contexts over several 256-position attention chunks plus a ragged tail."""
+    from parity import run_parity
+    sh, w = _weights("mid", 2.0, 16, 2)
+    res = run_parity(sh, w, 3, 300, 3, 0.75, label="mid")
+
+
+@pytest.mark.parametrize("name", ["odd", "mid"])
+def test_forced_exit_schedule(gpu, name):
+    """Per-sequence forced exits diverging inside the batch, every layer 1..L."""
+    from parity import run_parity
+    sh = SHAPES[name]
+    w = synth.make_weights(sh, 9)
+    L = sh.n_layers
+    B = 6
+    rng = np.random.default_rng(4)
+    res = run_parity(sh, w, B, 5, 5, 0.75, forced_fn=lambda s: rng.integers(1, L + 1, B),
+                     label=f"{name}-forced")
+
+
+@pytest.mark.parametrize("name", ["odd", "mid"])
+def test_unquantised_exit_copies(gpu, name):
+    from parity import run_parity
+    sh, w = _weights(name, 1.6, 6, 4)
+    run_parity(sh, w, 3, 6, 4, 0.75, exit_mode="bf16", label=f"{name}-bf16")
