@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Decode throughput of the KV-shared early-exit step on one MI355X.
+
+Workload (default "8b"): Llama-3.1-8B-shaped decoder (32 layers, d 4096, 32/8
+heads, head_dim 128, FFN 14336, vocab 128256) with seeded random bf16 weights,
+an exit head T (4096 x 4096) after every layer, int4 group-128 exit copies,
+batch 8, 1024-token uniform-random prompts, gamma 0.75 with per-layer
+calibrated head scales.  The prefill is untimed; ``--warmup`` decode steps run
+untimed, then ``--steps`` decode steps are timed (each step: all layers, exit
+heads, exit copies, final head, tokens and exit layers back on the host).
+
+Prints one JSON line: tokens/s, the roofline of the dominant kernel (the exit
+head's vocabulary GEMV, timed with HIP events on its stream during the timed
+steps), whole-step algorithmic bandwidth, the realised exit layers, and the
+oracle's decode speed on the host cores (a bounded sample).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def step_bytes(sh, exits, ctx, B):
+    """Algorithmic HBM bytes of one decode step given the realised exit layers.
+
+    Per layer l: bf16 weights when some row is still on the backbone (e_b >= l),
+    int4 codes + bf16 scales when some row has exited (e_b < l), the exit head
+    (T and E) when l < L and some row is on the backbone; then the final LM head,
+    K/V reads of every row's context, K/V writes and the embedding rows."""
+    L, d, V, G = sh.n_layers, sh.d_model, sh.vocab, sh.group
+    n = sh.params_per_layer()
+    w_bf, w_i4 = 2 * n, n // 2 + 2 * n // G
+    e = np.asarray(exits)
+    tot = 0
+    heads = 0
+    for l in range(1, L + 1):
+        A = int((e >= l).sum())
+        X = B - A
+        if A:
+            tot += w_bf
+        if X:
+            tot += w_i4
+        if l < L and A:
+            tot += 2 * d * d + 2 * V * d
+            heads += 1
+    tot += 2 * V * d
+    kv_row = 2 * sh.n_kv_heads * sh.head_dim * 2
+    tot += int(np.sum(ctx)) * L * kv_row + B * L * kv_row + B * d * 2
+    return tot, heads
+
+
+def cpu_baseline(wl, weights, exit_layer, ctx):
+    """The oracle's decode speed: one decode step of one sequence at the workload's shape,
+    with a synthetic (seeded) KV context of ``ctx`` positions and a forced exit layer."""
+    from threadpoolctl import threadpool_info
+    from oracle import model as om
+    sh = wl.shape
+    orc = om.OracleModel(sh, weights, cache_f64=False)
+    for l in range(exit_layer + 1, sh.n_layers + 1):
+        for name in om.LINEAR:
+            orc.quantized(l, name)            # model setup, like the GPU's ee_create_model
+    cache = om.KVCache(sh, 1, ctx + 2)
+    rng = np.random.default_rng(4242)
+    kv = rng.standard_normal(cache.K[:, :, :, :ctx].shape, dtype=np.float32)
+    cache.K[:, :, :, :ctx] = kv.astype(np.float32)
+    cache.V[:, :, :, :ctx] = kv[:, :, :, ::-1].astype(np.float32)
+    cache.lens[0] = ctx
+    t0 = time.perf_counter()
+    om.decode_step(orc, cache, [1], gamma=wl.gamma, forced=[exit_layer])
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": round(1.0 / dt, 5), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"1 decode step of 1 sequence, {sh.n_layers}-layer d{sh.d_model} shape, "
+                       f"synthetic {ctx}-position KV context, forced exit after layer {exit_layer}; "
+                       f"{dt:.1f} s, float64 numpy")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="8b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch every kernel eagerly")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the early-exit decode step is data-parallel "
+              "(every sequence is independent) and this build runs on one MI355X only; "
+              f"--gpus {args.gpus} is not supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from kv_shared_exit_amd import api
+
+    wl = synth.workload(args.workload)
+    sh = wl.shape
+    B, P = wl.batch, wl.prompt_len
+    K = args.steps if args.steps is not None else wl.decode_steps - args.warmup
+    W = args.warmup
+    S = P + W + K + 1
+    alpha = synth.load_alpha(wl)
+    if alpha is None and wl.policy == "calibrated":
+        log("no calibration file: exit heads unscaled (alpha = 1)")
+    t0 = time.time()
+    weights = synth.make_weights(sh, wl.seed_weights, alpha=alpha)
+    log(f"weights drawn ({time.time() - t0:.0f}s)")
+    dev = api.upload_weights(weights)
+    model = api.Model(sh, dev, gamma=wl.gamma, max_batch=B, max_positions=S)
+    cache = api.KVCache(model, B, S)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    log(f"model ready ({time.time() - t0:.0f}s)")
+    prompts = synth.make_prompts(wl)
+    api.prefill(model, cache, prompts, stream=stream)
+    log(f"prefill {B}x{P} done ({time.time() - t0:.0f}s)")
+
+    forced = None
+    exits = []
+
+    def step(s):
+        f = synth.make_forced_exits(wl, s) if wl.policy == "forced" else None
+        return api.decode_step(model, cache, B, forced=f, stream=stream)
+
+    for s in range(W):
+        step(s)
+    torch.cuda.synchronize()
+    ctx0 = cache.lengths()[:B].copy()
+    model.profile(True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(K):
+        _, e = step(W + s)
+        exits.append(e.copy())
+    torch.cuda.synchronize()
+    t_el = time.perf_counter() - t_start
+    n_launch, head_ms = model.profile_read(0)
+    model.profile(False)
+    log(f"timed {K} steps in {t_el:.3f}s")
+
+    exits = np.stack(exits)
+    total_bytes = 0
+    head_launches = 0
+    for s in range(K):
+        ctx = ctx0 + s + 1
+        b, h = step_bytes(sh, exits[s], ctx, B)
+        total_bytes += b
+        head_launches += h
+    # dominant kernel: the exit head's vocabulary GEMV (E read once per launch)
+    a_rows = sum(int((exits[s] >= l).sum()) for s in range(K) for l in range(1, sh.n_layers)
+                 if (exits[s] >= l).any())
+    head_bytes = 2 * sh.vocab * sh.d_model + 2 * sh.d_model * (a_rows / max(head_launches, 1))
+    avg_ms = head_ms / max(n_launch, 1)
+    achieved = head_bytes / (avg_ms * 1e-3) / 1e9 if n_launch else 0.0
+
+    copy_probe = None
+    if args.copy_probe:
+        x = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        copy_probe = {"bytes_read": x.numel() * 4, "bytes_written": y.numel() * 4}
+
+    hist = np.bincount(exits.reshape(-1), minlength=sh.n_layers + 1)[1:]
+    mean_exit = float(exits.mean())
+    out = {
+        "metric": "decode tokens/s at 1 MI355X (8B shape, b=8) + achieved HBM GB/s fraction",
+        "value": round(B * K / t_el, 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(1e3 * t_el / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {sh.n_layers} layers d{sh.d_model} "
+                               f"{sh.n_heads}/{sh.n_kv_heads} heads hd{sh.head_dim} F{sh.d_ff} "
+                               f"V{sh.vocab}, int4 G{sh.group} exit copies, batch {B}, "
+                               f"{P}-token prompts, gamma {wl.gamma}",
+                   "global_batch": B, "seq_len": P, "decode_steps": K, "parallelism": "none"},
+        "roofline": {"bound": "hbm", "kernel": "exit-head vocabulary GEMV (proj_kernel<3>)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "launches": n_launch, "avg_us": round(1e3 * avg_ms, 2),
+                     "bytes_per_launch": int(head_bytes)},
+        "step": {"algorithmic_GB": round(total_bytes / K / 1e9, 3),
+                 "GBps": round(total_bytes / t_el / 1e9, 1),
+                 "frac": round(total_bytes / t_el / 1e9 / HBM_PEAK_GBS, 4),
+                 "mean_exit_layer": round(mean_exit, 3),
+                 "exit_hist": hist.tolist(),
+                 "head_launches_per_step": round(head_launches / K, 2)},
+        "cpu_baseline": None,
+    }
+    if copy_probe:
+        out["copy_probe"] = copy_probe
+    cache.close()
+    model.close()
+    del dev
+    if not args.no_cpu_baseline:
+        ex = int(round(mean_exit))
+        out["cpu_baseline"] = cpu_baseline(wl, weights, min(max(ex, 1), sh.n_layers), P)
+        log(f"cpu baseline done ({time.time() - t0:.0f}s)")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,13 +18,16 @@ alpha_l > alpha*.  alpha_l is the h-quantile of the samples' alpha*, so a
 fraction h of them exit.  This is the analogue, for random weights, of CALM's
 threshold tuning on a validation set (CALM explainer, section 4.2).
 
-Samples come from a layer-major prefill of seeded calibration prompts
-(positions in the same range the workload decodes), at full depth with the
-backbone weights.  The unit-scale logits use T drawn at standard deviation
-0.02 without bf16 rounding; the realised exit distribution is therefore close
-to, not exactly, the target.  Parity unpinned: this only chooses inputs.
+Samples are the hidden states after every layer of full-depth greedy decode
+steps (heads off) that follow a prefill of seeded calibration prompts of the
+workload's prompt length, so they cover the positions and the kind of inputs
+(the model's own greedy tokens) the workload decodes.  Matrix products run in
+float32 here (the oracle's float64 path is used for every parity check).  The
+unit-scale logits use T drawn at standard deviation 0.02 without bf16
+rounding; the realised exit distribution is therefore close to, not exactly,
+the target.  Parity unpinned: this only chooses inputs.
 
-Usage: python -m oracle.calibrate <workload> [--samples N]
+Usage: python -m oracle.calibrate <workload> [--steps N] [--batch B]
 writes synth/calibration/<workload>.json.
 """
 from __future__ import annotations
@@ -37,8 +40,8 @@ import time
 import numpy as np
 
 import synth
-from .model import OracleModel, KVCache, prefill
-from .numerics import bf16_round
+from .model import OracleModel, KVCache, prefill, decode_step
+from .numerics import bf16_round, from_bf16_bits
 
 
 def alpha_threshold(logits: np.ndarray, gamma: float, iters: int = 60) -> np.ndarray:
@@ -56,50 +59,65 @@ def alpha_threshold(logits: np.ndarray, gamma: float, iters: int = 60) -> np.nda
     return np.exp(0.5 * (lo + hi))
 
 
-def calibrate(wl, samples: int | None = None, calib_batch: int = 1, verbose: bool = True):
+def calibrate(wl, steps: int | None = None, calib_batch: int = 4, verbose: bool = True,
+              matmul_dtype=np.float32):
+    """Per-layer alpha for workload ``wl`` from full-depth greedy decode states."""
     sh = wl.shape
     L = sh.n_layers
     h = synth.geometric_hazard(wl.mean_exit, L)
-    # positions of the samples: the decode range of the workload
-    P0 = wl.prompt_len
-    n_pos = min(wl.decode_steps + 1, samples or (wl.decode_steps + 1))
-    Pc = P0 + n_pos
+    steps = wl.decode_steps if steps is None else min(steps, wl.decode_steps)
     t0 = time.time()
+
+    def say(msg):
+        if verbose:
+            print(f"[calibrate {wl.name}] {msg} ({time.time() - t0:.0f}s)", flush=True)
+
     w = synth.make_weights(sh, wl.seed_weights)
-    m = OracleModel(sh, w, exit_mode="bf16", cache_f64=False)
-    cache = KVCache(sh, calib_batch, Pc)
-    prompts = synth.make_prompts(wl, batch=calib_batch, length=Pc, seed=wl.seed_calib)
-    _, info = prefill(m, cache, prompts, trace=True)
-    hid = info["hidden"][:, P0:Pc]                            # [Bc, n_pos, L+1, d]
-    if verbose:
-        print(f"[calibrate {wl.name}] prefill of {calib_batch}x{Pc} done in {time.time()-t0:.0f}s",
-              flush=True)
-    E = m.lm_head
+    m = OracleModel(sh, w, exit_mode="bf16", cache_f64=True, matmul_dtype=matmul_dtype)
+    for l in range(1, L + 1):                     # widen once, then drop the bf16 copies
+        for name in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "attn_norm", "ffn_norm"):
+            m.w(l, name)
+        keep = {"head_T": w["layers"][l - 1].get("head_T")}
+        w["layers"][l - 1] = keep
+    say("weights ready")
+    P0 = wl.prompt_len
+    cache = KVCache(sh, calib_batch, P0 + steps + 1)
+    prompts = synth.make_prompts(wl, batch=calib_batch, length=P0, seed=wl.seed_calib)
+    tok, _ = prefill(m, cache, prompts)
+    say(f"prefill {calib_batch}x{P0}")
+    states = []
+    for s in range(steps):
+        tok, _, info = decode_step(m, cache, tok, gamma=2.0, trace=True, heads=False)
+        states.append(info["hidden"])              # [Bc, L+1, d]
+        if s % 32 == 0:
+            say(f"decode step {s}")
+    hid = np.stack(states, axis=1)                 # [Bc, steps, L+1, d]
+    del m._f64
+    E = from_bf16_bits(w["lm_head"]).astype(matmul_dtype)
     alphas = []
     for l in range(1, L):
         hl = hid[:, :, l].reshape(-1, sh.d_model)
-        T = synth.draw_unit_normal(wl.seed_weights, "head_T", l, (sh.d_model, sh.d_model))
-        T = T.astype(np.float64) * 0.02
-        z = bf16_round(hl) @ T.T
-        logits = z @ E.T
+        T = synth.draw_unit_normal(wl.seed_weights, "head_T", l, (sh.d_model, sh.d_model)) * 0.02
+        z = bf16_round(hl).astype(matmul_dtype) @ T.astype(matmul_dtype).T
+        logits = (z @ E.T).astype(np.float64)
         astar = alpha_threshold(logits, wl.gamma)
         a = float(np.quantile(astar, h))
         alphas.append(a)
-        if verbose:
-            print(f"[calibrate {wl.name}] layer {l}: alpha={a:.4g} ({time.time()-t0:.0f}s)", flush=True)
+        say(f"layer {l}: alpha={a:.4g}")
     return {"workload": wl.name, "gamma": wl.gamma, "mean_exit": wl.mean_exit, "hazard": h,
             "samples_per_layer": int(hid.shape[0] * hid.shape[1]),
-            "positions": [P0, Pc], "alpha": alphas}
+            "source": f"full-depth greedy decode, {calib_batch} prompts of {P0} tokens, {steps} steps",
+            "alpha": alphas}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("workload")
-    ap.add_argument("--samples", type=int, default=None)
-    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--batch", type=int, default=4)
     args = ap.parse_args()
     wl = synth.workload(args.workload)
-    res = calibrate(wl, args.samples, args.batch)
+    res = calibrate(wl, args.steps, args.batch)
     os.makedirs(synth.CALIB_DIR, exist_ok=True)
     path = os.path.join(synth.CALIB_DIR, f"{wl.name}.json")
     with open(path, "w") as f:

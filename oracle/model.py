@@ -109,6 +109,13 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, n_kv_heads: int) -> np.n
     return bf16_round(out.reshape(-1))
 
 
+def lin(x: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """x @ W^T for a linear map stored [out, in], in W's precision, returned as float64."""
+    if W.dtype == np.float64:
+        return x @ W.T
+    return (x.astype(W.dtype) @ W.T).astype(np.float64)
+
+
 # ----------------------------------------------------------------------------
 # model and shared KV cache
 # ----------------------------------------------------------------------------
@@ -118,17 +125,21 @@ class OracleModel:
     ``weights`` is the dict produced by ``synth.make_weights`` (bf16 bit
     patterns).  ``exit_mode`` is "int4" (exit copies are the quantised layers)
     or "bf16" (exit copies are the backbone layers themselves).  ``cache_f64``
-    keeps float64 copies of every matrix (fast, memory hungry); otherwise each
-    matrix is widened when used.
+    keeps widened copies of every matrix (fast, memory hungry); otherwise each
+    matrix is widened when used.  ``matmul_dtype`` is float64 for every
+    comparison made by the tests; the exit-head calibration, which only picks
+    inputs, may ask for float32 matrix products to reach the 8B shape.
     """
 
-    def __init__(self, shape, weights, exit_mode: str = "int4", cache_f64: bool = True):
+    def __init__(self, shape, weights, exit_mode: str = "int4", cache_f64: bool = True,
+                 matmul_dtype=np.float64):
         if exit_mode not in ("int4", "bf16"):
             raise ValueError(exit_mode)
         self.shape = shape
         self.raw = weights
         self.exit_mode = exit_mode
         self.cache_f64 = cache_f64
+        self.mdt = np.dtype(matmul_dtype)
         self._f64 = {}
         self._q = {}
         self.tok_emb = from_bf16_bits(weights["tok_emb"])
@@ -143,6 +154,8 @@ class OracleModel:
         if key in self._f64:
             return self._f64[key]
         t = from_bf16_bits(self.raw["layers"][layer - 1][name])
+        if t.ndim == 2 and self.mdt != np.float64:
+            t = t.astype(self.mdt)
         if self.cache_f64:
             self._f64[key] = t
         return t
@@ -151,8 +164,7 @@ class OracleModel:
         """(codes int8 [N, K], scales float64 [N, K/G]) of the exit copy of a linear map."""
         key = (layer, name)
         if key not in self._q:
-            self._q[key] = quantize_int4(self.w(layer, name) if self.cache_f64 else
-                                         from_bf16_bits(self.raw["layers"][layer - 1][name]),
+            self._q[key] = quantize_int4(from_bf16_bits(self.raw["layers"][layer - 1][name]),
                                          self.shape.group)
         return self._q[key]
 
@@ -164,7 +176,7 @@ class OracleModel:
         if key in self._f64:
             return self._f64[key]
         q, s = self.quantized(layer, name)
-        t = dequantize_int4(q, s, self.shape.group)
+        t = dequantize_int4(q, s, self.shape.group).astype(self.mdt)
         if self.cache_f64:
             self._f64[key] = t
         return t
@@ -213,9 +225,9 @@ def _layer_rows(model: OracleModel, cache: KVCache, layer: int, rows, h, pos, us
     W = model.w_exit if use_exit else model.w
     hr = h[rows]
     x = rmsnorm(hr, model.w(layer, "attn_norm"), sh.rms_eps)
-    q = bf16_round(x @ W(layer, "wq").T).reshape(len(rows), H, hd)
-    k = bf16_round(x @ W(layer, "wk").T).reshape(len(rows), Hkv, hd)
-    v = bf16_round(x @ W(layer, "wv").T).reshape(len(rows), Hkv, hd)
+    q = bf16_round(lin(x, W(layer, "wq"))).reshape(len(rows), H, hd)
+    k = bf16_round(lin(x, W(layer, "wk"))).reshape(len(rows), Hkv, hd)
+    v = bf16_round(lin(x, W(layer, "wv"))).reshape(len(rows), Hkv, hd)
     cos, sin = model.rope(int(max(pos[rows])) + 1)
     o = np.empty((len(rows), H * hd))
     for i, b in enumerate(rows):
@@ -225,10 +237,10 @@ def _layer_rows(model: OracleModel, cache: KVCache, layer: int, rows, h, pos, us
         cache.store(layer, b, p, kr, v[i])
         Kb, Vb = cache.keys(layer, b, p + 1)
         o[i] = attend(qr, Kb, Vb, Hkv)
-    hr = hr + o @ W(layer, "wo").T
+    hr = hr + lin(o, W(layer, "wo"))
     x = rmsnorm(hr, model.w(layer, "ffn_norm"), sh.rms_eps)
-    a = bf16_round(silu(x @ W(layer, "w_gate").T) * (x @ W(layer, "w_up").T))
-    hr = hr + a @ W(layer, "w_down").T
+    a = bf16_round(silu(lin(x, W(layer, "w_gate"))) * lin(x, W(layer, "w_up")))
+    hr = hr + lin(a, W(layer, "w_down"))
     h[rows] = hr
 
 
@@ -238,7 +250,7 @@ def exit_head(model: OracleModel, layer: int, h: np.ndarray):
     z = bf16(T_l bf16(h)); logits = E z with E the LM-head matrix
     (AdaDecode explainer section 2.1, head weight E T^(l)); p = max softmax.
     """
-    z = bf16_round(bf16_round(h) @ model.w(layer, "head_T").T)
+    z = bf16_round(lin(bf16_round(h), model.w(layer, "head_T")))
     logits = z @ model.lm_head.T
     return softmax_top1(logits), logits
 
@@ -260,7 +272,7 @@ def final_head(model: OracleModel, h: np.ndarray):
 # decode step, prefill, generation
 # ----------------------------------------------------------------------------
 def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=None,
-                trace: bool = False):
+                trace: bool = False, heads: bool = True):
     """One decode step for sequences 0..B-1 of ``cache`` (B = len(tokens)).
 
     ``gamma``: per-layer thresholds gamma_1..gamma_{L-1} (scalar broadcasts).
@@ -270,7 +282,8 @@ def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=N
     ``p`` [B, L-1] (NaN where no head ran), ``head_absmax`` [B, L-1] (largest
     |logit| of each evaluated exit head), ``gap`` [B], ``logits`` [B, V] and,
     with ``trace``, ``hidden`` [B, L+1, d] (after the embedding and after every
-    layer).
+    layer).  ``heads=False`` skips the exit heads (no sequence exits); it is
+    used to sample full-depth states.
     """
     sh = model.shape
     L = sh.n_layers
@@ -295,7 +308,7 @@ def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=N
             _layer_rows(model, cache, l, bb, h, pos, use_exit=False)
         if len(ex):
             _layer_rows(model, cache, l, ex, h, pos, use_exit=True)
-        if l < L and len(bb):
+        if heads and l < L and len(bb):
             p, hl = exit_head(model, l, h[bb])
             p_rec[bb, l - 1] = p
             head_max[bb, l - 1] = np.abs(hl).max(axis=-1)
@@ -335,9 +348,9 @@ def prefill(model: OracleModel, cache: KVCache, prompts, trace: bool = False):
     scale = 1.0 / np.sqrt(hd)
     for l in range(1, L + 1):
         x = rmsnorm(h, model.w(l, "attn_norm"), sh.rms_eps)
-        q = bf16_round(x @ model.w(l, "wq").T).reshape(B, P, H, hd)
-        k = bf16_round(x @ model.w(l, "wk").T).reshape(B, P, Hkv, hd)
-        v = bf16_round(x @ model.w(l, "wv").T).reshape(B, P, Hkv, hd)
+        q = bf16_round(lin(x, model.w(l, "wq"))).reshape(B, P, H, hd)
+        k = bf16_round(lin(x, model.w(l, "wk"))).reshape(B, P, Hkv, hd)
+        v = bf16_round(lin(x, model.w(l, "wv"))).reshape(B, P, Hkv, hd)
         o = np.empty((B, P, H, hd))
         for b in range(B):
             ap = pos0[b] + np.arange(P)
@@ -357,10 +370,10 @@ def prefill(model: OracleModel, cache: KVCache, prompts, trace: bool = False):
                 pi /= pi.sum(axis=1, keepdims=True)
                 o[b, :, i] = pi @ Vb[j]
         o = bf16_round(o.reshape(B, P, H * hd))
-        h = h + o @ model.w(l, "wo").T
+        h = h + lin(o, model.w(l, "wo"))
         x = rmsnorm(h, model.w(l, "ffn_norm"), sh.rms_eps)
-        a = bf16_round(silu(x @ model.w(l, "w_gate").T) * (x @ model.w(l, "w_up").T))
-        h = h + a @ model.w(l, "w_down").T
+        a = bf16_round(silu(lin(x, model.w(l, "w_gate"))) * lin(x, model.w(l, "w_up")))
+        h = h + lin(a, model.w(l, "w_down"))
         if trace:
             hidden.append(h.copy())
     tok, gap, logits = final_head(model, h[:, -1])
