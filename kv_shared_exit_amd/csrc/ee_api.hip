@@ -181,9 +181,10 @@ void validate_config(const ee_model_config& c) {
         "d_model and d_ff must be multiples of group_size");
   const int qd = c.n_heads * c.head_dim;
   shape(qd % c.group_size == 0, "n_heads * head_dim must be a multiple of group_size");
-  const int kmax = std::max(std::max(c.d_model, c.d_ff), qd);
-  shape((long long)8 * (kmax / c.group_size) <= kXgElems, "too many int4 groups per row");
   shape(c.d_model % 8 == 0 && c.d_ff % 8 == 0, "widths must be multiples of 8");
+  shape(c.d_model <= kXLdsElems / std::min(8, c.max_batch),
+        "d_model too wide for the vocabulary GEMV's staged input at this max_batch");
+  shape(c.d_model % 32 == 0 && c.d_ff % 32 == 0, "widths must be multiples of 32");
 }
 
 hipStream_t pick_stream(ee_model* m, void* s) { return s ? (hipStream_t)s : m->own; }
@@ -383,7 +384,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
         a.x_stride = d;
         a.y = m->z;
         a.y_stride = d;
-        launch_proj(EPI_BF16, a, kNwg, s);
+          launch_proj(EPI_BF16, a, kNwg, s);
       }
       {
         ProjArgs a = base_args(m);
@@ -397,7 +398,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
         a.part = m->head_part;
         hipEvent_t e0;
         prof_begin(m, s, &e0);
-        launch_proj(EPI_LSE, a, kNwg, s);
+          launch_proj(EPI_LSE, a, kNwg, s);
         prof_end(m, s);
       }
       launch_decide(st, m->head_part, kNwg, m->d_gamma, l, L, B, m->p_rec, s);
@@ -496,8 +497,11 @@ ee_status ee_create_model(const ee_model_config* cfg, const ee_weights* w, const
           Q4 q;
           q.N = N;
           q.K = K;
-          q.codes = m->alloc<uint32_t>((size_t)N * (K / 8));
-          q.scales = m->alloc<uint16_t>((size_t)N * (K / G));
+          const size_t n16 = (size_t)(N + 15) / 16 * 16;
+          q.codes = m->alloc<uint32_t>(n16 * (K / 8));
+          q.scales = m->alloc<uint16_t>(n16 * (K / G));
+          HIPCHK(hipMemsetAsync(q.codes, 0x88, n16 * (K / 8) * 4, m->own));
+          HIPCHK(hipMemsetAsync(q.scales, 0, n16 * (K / G) * 2, m->own));
           return q;
         };
         for (int l = 2; l <= L; ++l) {
@@ -508,16 +512,13 @@ ee_status ee_create_model(const ee_model_config* cfg, const ee_weights* w, const
           q.gate = mk(F, d);
           q.up = mk(F, d);
           q.down = mk(d, F);
-          launch_quantize((const uint16_t*)lw.wq, qd, d, G, q.qkv.codes, q.qkv.scales, m->own);
-          launch_quantize((const uint16_t*)lw.wk, kvd, d, G, q.qkv.codes + (size_t)qd * (d / 8),
-                          q.qkv.scales + (size_t)qd * (d / G), m->own);
-          launch_quantize((const uint16_t*)lw.wv, kvd, d, G,
-                          q.qkv.codes + (size_t)(qd + kvd) * (d / 8),
-                          q.qkv.scales + (size_t)(qd + kvd) * (d / G), m->own);
-          launch_quantize((const uint16_t*)lw.wo, d, qd, G, q.o.codes, q.o.scales, m->own);
-          launch_quantize((const uint16_t*)lw.w_gate, F, d, G, q.gate.codes, q.gate.scales, m->own);
-          launch_quantize((const uint16_t*)lw.w_up, F, d, G, q.up.codes, q.up.scales, m->own);
-          launch_quantize((const uint16_t*)lw.w_down, d, F, G, q.down.codes, q.down.scales, m->own);
+          launch_quantize((const uint16_t*)lw.wq, qd, d, G, 0, q.qkv.codes, q.qkv.scales, m->own);
+          launch_quantize((const uint16_t*)lw.wk, kvd, d, G, qd, q.qkv.codes, q.qkv.scales, m->own);
+          launch_quantize((const uint16_t*)lw.wv, kvd, d, G, qd + kvd, q.qkv.codes, q.qkv.scales, m->own);
+          launch_quantize((const uint16_t*)lw.wo, d, qd, G, 0, q.o.codes, q.o.scales, m->own);
+          launch_quantize((const uint16_t*)lw.w_gate, F, d, G, 0, q.gate.codes, q.gate.scales, m->own);
+          launch_quantize((const uint16_t*)lw.w_up, F, d, G, 0, q.up.codes, q.up.scales, m->own);
+          launch_quantize((const uint16_t*)lw.w_down, d, F, G, 0, q.down.codes, q.down.scales, m->own);
           HIPCHK(hipGetLastError());
         }
       }
@@ -851,14 +852,21 @@ ee_status ee_exit_weights_read(const ee_model* m, int32_t layer, int32_t which, 
     ee_model* mm = const_cast<ee_model*>(m);
     with_sticky(mm, [&] {
       int8_t* tmp = dalloc<int8_t>((size_t)nrows * K);
-      launch_unpack_codes(src->codes, src->N, K, off + row0, nrows, tmp, mm->own);
+      uint16_t* stmp = nullptr;
+      hipError_t e0 = hipMalloc((void**)&stmp, (size_t)nrows * (K / G) * 2);
+      if (e0 != hipSuccess) {
+        (void)hipFree(tmp);
+        HIPCHK(e0);
+      }
+      launch_unpack(src->codes, src->scales, K, G, off + row0, nrows, tmp, stmp, mm->own);
       hipError_t e1 = hipStreamSynchronize(mm->own);
       hipError_t e2 = hipMemcpy(codes_host, tmp, (size_t)nrows * K, hipMemcpyDeviceToHost);
+      hipError_t e3 = hipMemcpy(scales_host, stmp, (size_t)nrows * (K / G) * 2, hipMemcpyDeviceToHost);
       (void)hipFree(tmp);
+      (void)hipFree(stmp);
       HIPCHK(e1);
       HIPCHK(e2);
-      HIPCHK(hipMemcpy(scales_host, src->scales + (size_t)(off + row0) * (K / G), (size_t)nrows * (K / G) * 2,
-                       hipMemcpyDeviceToHost));
+      HIPCHK(e3);
     });
   });
 }

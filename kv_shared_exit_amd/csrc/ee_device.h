@@ -1,0 +1,95 @@
+// Device helpers shared by the gfx950 kernels: bf16 conversions, the bf16 dot
+// product, the cross-lane transpose-reduce and the (max, sum exp) / top-2
+// merges used by the vocabulary reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+namespace ee {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Streaming 16-byte load that does not allocate in the caches (weights are
+// read once per launch).
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load((const u32x4_t*)p));
+}
+
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float32 -> bf16 bits, round to nearest, ties to even (inputs are finite)
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane "transpose-reduce": V partial sums per lane, summed over the 64
+// lanes of the wave.  Each halving stage keeps half of the values and trades
+// the other half with the partner lane, so the total work is ~2V exchanges
+// instead of 6V.  Afterwards lane l holds the sum for value index xidx<V>(l)
+// (lanes >= V hold copies).
+// ---------------------------------------------------------------------------
+template <int V, int S>
+struct XRed {
+  __device__ __forceinline__ static void run(float* v, int lane) {
+    if constexpr ((1 << S) < V) {
+      constexpr int half = V >> (S + 1);
+      const bool hi = (lane >> S) & 1;
+#pragma unroll
+      for (int i = 0; i < half; ++i) {
+        const float keep = hi ? v[half + i] : v[i];
+        const float send = hi ? v[i] : v[half + i];
+        v[i] = keep + __shfl_xor(send, 1 << S);
+      }
+      XRed<V, S + 1>::run(v, lane);
+    } else if constexpr (S < 6) {
+      v[0] += __shfl_xor(v[0], 1 << S);
+      XRed<V, S + 1>::run(v, lane);
+    }
+  }
+};
+
+template <int V>
+__device__ __forceinline__ int xidx(int lane) {
+  int idx = 0;
+#pragma unroll
+  for (int s = 0; (1 << s) < V; ++s)
+    if ((lane >> s) & 1) idx += V >> (s + 1);
+  return idx;
+}
+
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;
+  s = s * __expf(m - M) + s2 * __expf(m2 - M);
+  m = M;
+}
+
+struct Top2 {
+  float v1;
+  int i1;
+  float v2;
+};
+
+__device__ __forceinline__ void top2_merge(Top2& a, const Top2& o) {
+  if (o.v1 > a.v1 || (o.v1 == a.v1 && o.i1 < a.i1)) {
+    a.v2 = fmaxf(o.v2, a.v1);
+    a.v1 = o.v1;
+    a.i1 = o.i1;
+  } else {
+    a.v2 = fmaxf(a.v2, o.v1);
+  }
+}
+
+}  // namespace ee

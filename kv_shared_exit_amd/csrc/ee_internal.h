@@ -7,11 +7,10 @@
 namespace ee {
 
 constexpr int kMaxBatch = 64;      // rows of one decode step
-constexpr int kProjThreads = 256;  // 4 waves per projection workgroup
+constexpr int kProjThreads = 512;  // 8 waves per projection workgroup
 constexpr int kAttnChunk = 256;    // positions per attention workgroup (4 waves x 64)
 constexpr int kXLdsElems = 32768;  // bf16 elements of the staged GEMV input (64 KB)
-constexpr int kXgElems = 4096;     // int4 group sums held in LDS
-constexpr int kNib = 2048;         // elements covered by one 16-byte-per-lane int4 block
+constexpr int kNwgMax = 512;       // projection grid cap (size of the per-workgroup partial buffers)
 
 enum Epi { EPI_BF16 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LSE = 3, EPI_ARGMAX = 4 };
 
@@ -36,8 +35,8 @@ struct ProjArgs {
   int seg_end[3];        // cumulative end row of each segment
   const uint16_t* wb[3]; // bf16 segment bases, row-major [rows][K]
   const uint16_t* wb2;   // SwiGLU: the "up" matrix (gate is wb[0])
-  const uint32_t* q4;    // int4 codes [N][K/8] dwords (permuted blocks, see quantize kernel)
-  const uint16_t* s4;    // bf16 scales [N][K/G]
+  const uint32_t* q4;    // int4 codes [N16][K/8] dwords (layout: ee_proj.hip)
+  const uint16_t* s4;    // bf16 scales [N16/16][K/G][16]
   const uint32_t* q4b;   // SwiGLU "up" codes
   const uint16_t* s4b;
   const uint16_t* x;     // bf16 input rows, indexed by sequence id
@@ -48,7 +47,6 @@ struct ProjArgs {
   uint16_t* y2; int y2_stride;                    // EPI_RESID: bf16 copy of the new residual
   float* part;                                    // EPI_LSE / EPI_ARGMAX partials per workgroup
   float* logits; int logits_stride;               // EPI_ARGMAX: optional logits out
-  float* prof_dummy;
 };
 
 struct AttnArgs {
@@ -78,9 +76,9 @@ void launch_decide(StepState* st, const float* part, int nwg, const float* gamma
 void launch_final(StepState* st, const float* part, int nwg, int B, int V, int32_t* lens, int advance,
                   hipStream_t s);
 void launch_advance(int32_t* lens, int B, hipStream_t s);
-void launch_quantize(const uint16_t* w, int N, int K, int G, uint32_t* codes, uint16_t* scales,
-                     hipStream_t s);
-void launch_unpack_codes(const uint32_t* codes, int N, int K, int row0, int nrows, int8_t* out,
-                         hipStream_t s);
+void launch_quantize(const uint16_t* w, int N, int K, int G, int row0, uint32_t* codes,
+                     uint16_t* scales, hipStream_t s);
+void launch_unpack(const uint32_t* codes, const uint16_t* scales, int K, int G, int row0, int nrows,
+                   int8_t* out, uint16_t* sout, hipStream_t s);
 
 }  // namespace ee

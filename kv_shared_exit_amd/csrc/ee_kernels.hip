@@ -5,11 +5,8 @@
 //   init       embed the input tokens into the float32 residual, reset the
 //              per-step exit state and the row lists
 //   rmsnorm    bf16(h * rsqrt(mean(h^2) + eps) * g)
-//   proj       the projections: one launch serves the rows still on the
-//              backbone (bf16 weights) and the rows that exited (int4 exit
-//              copy of the same layer); fused epilogues store bf16, add into
-//              the residual, apply SwiGLU, or reduce vocabulary logits to
-//              per-workgroup (max, sum exp) or (argmax, top-2) partials
+//   proj       (ee_proj.hip) the projections over both weight copies, and
+//              the int4 packer
 //   rope_kv    rotate q and k, write k and v into the shared cache slot of the
 //              position (the same slot for either weight copy)
 //   attention  grouped-query decode attention, split over 256-position chunks;
@@ -19,418 +16,13 @@
 //              gamma or apply a forced exit, rebuild the backbone/exit row lists
 //              with a wave ballot (active-sequence compaction)
 //   final      argmax of the LM head, top-2 gap, next input token
-//   quantize   build the int4 exit copies (setup)
 #include "ee_internal.h"
+#include "ee_device.h"
 
 #include <math.h>
 
 namespace ee {
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
-
-// float32 -> bf16 bits, round to nearest, ties to even (inputs are finite)
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-// ---------------------------------------------------------------------------
-// Cross-lane "transpose-reduce": V partial sums per lane, summed over the 64
-// lanes of the wave.  Each halving stage keeps half of the values and trades
-// the other half with the partner lane, so the total work is ~2V exchanges
-// instead of 6V.  Afterwards lane l holds the sum for value index xidx<V>(l)
-// (lanes >= V hold copies).
-// ---------------------------------------------------------------------------
-template <int V, int S>
-struct XRed {
-  __device__ __forceinline__ static void run(float* v, int lane) {
-    if constexpr ((1 << S) < V) {
-      constexpr int half = V >> (S + 1);
-      const bool hi = (lane >> S) & 1;
-#pragma unroll
-      for (int i = 0; i < half; ++i) {
-        const float keep = hi ? v[half + i] : v[i];
-        const float send = hi ? v[i] : v[half + i];
-        v[i] = keep + __shfl_xor(send, 1 << S);
-      }
-      XRed<V, S + 1>::run(v, lane);
-    } else if constexpr (S < 6) {
-      v[0] += __shfl_xor(v[0], 1 << S);
-      XRed<V, S + 1>::run(v, lane);
-    }
-  }
-};
-
-template <int V>
-__device__ __forceinline__ int xidx(int lane) {
-  int idx = 0;
-#pragma unroll
-  for (int s = 0; (1 << s) < V; ++s)
-    if ((lane >> s) & 1) idx += V >> (s + 1);
-  return idx;
-}
-
-// ---------------------------------------------------------------------------
-// Projection GEMV
-// ---------------------------------------------------------------------------
-template <int EPI>
-struct EpiTraits {
-  static constexpr int R = (EPI == EPI_LSE || EPI == EPI_ARGMAX) ? 8 : 2;  // rows per wave tile
-  static constexpr int P = (EPI == EPI_SWIGLU) ? 2 : 1;                     // matrices per tile
-};
-
-__device__ __forceinline__ const uint16_t* bf_row(const ProjArgs& a, int n) {
-  int s = 0, start = 0;
-  if (n >= a.seg_end[0]) {
-    s = (n >= a.seg_end[1]) ? 2 : 1;
-    start = a.seg_end[s - 1];
-  }
-  return a.wb[s] + (size_t)(n - start) * a.K;
-}
-
-// acc[r * NB + b] += sum_k W_r[k] x_b[k]; lanes own 8-element slices, 512 per step.
-template <int RP, int NB>
-__device__ __forceinline__ void dot_bf16(const uint16_t* const (&w)[RP], const uint16_t* const (&x)[NB],
-                                         int K, int lane, float (&acc)[RP * NB]) {
-  for (int k = lane * 8; k < K; k += 512) {
-    uint4 wv[RP];
-#pragma unroll
-    for (int r = 0; r < RP; ++r) wv[r] = *(const uint4*)(w[r] + k);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const uint4 xv = *(const uint4*)(x[b] + k);
-#pragma unroll
-      for (int r = 0; r < RP; ++r) {
-        float t = acc[r * NB + b];
-        t = dot2(wv[r].x, xv.x, t);
-        t = dot2(wv[r].y, xv.y, t);
-        t = dot2(wv[r].z, xv.z, t);
-        t = dot2(wv[r].w, xv.w, t);
-        acc[r * NB + b] = t;
-      }
-    }
-  }
-}
-
-// One int4 dword (8 codes) times 8 inputs of each batch row.  The codes are
-// offset binary (u = q + 8); OR-ing a nibble into bf16 0x4300 gives 128 + u =
-// 136 + q exactly, so the products below are (136 + q) x.  The 136 * sum(x)
-// part is removed per group afterwards (i4_correct), leaving sum q x; the
-// group's scale multiplies the dword's partial sum.
-template <int RP, int NB>
-__device__ __forceinline__ void i4_word(const uint32_t (&word)[RP], const float (&sc)[RP],
-                                        const uint16_t* const (&x)[NB], int e0,
-                                        float (&acc)[RP * NB]) {
-  uint32_t pr[RP][4];
-#pragma unroll
-  for (int r = 0; r < RP; ++r) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pr[r][i] = ((word[r] >> (4 * i)) & 0x000F000Fu) | 0x43004300u;
-  }
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const uint4 xv = *(const uint4*)(x[b] + e0);
-#pragma unroll
-    for (int r = 0; r < RP; ++r) {
-      float t = dot2(pr[r][0], xv.x, 0.0f);
-      t = dot2(pr[r][1], xv.y, t);
-      t = dot2(pr[r][2], xv.z, t);
-      t = dot2(pr[r][3], xv.w, t);
-      acc[r * NB + b] = fmaf(sc[r], t, acc[r * NB + b]);
-    }
-  }
-}
-
-// Codes of a row: K/8 dwords.  Within each full 2048-element block the dword
-// holding elements [8t, 8t+8) (t = blk*256 + j*64 + lane) is stored at
-// blk*256 + lane*4 + j, so one 16-byte load per lane fetches its four dwords;
-// the tail (K mod 2048) keeps natural order.
-template <int RP, int NB>
-__device__ __forceinline__ void dot_i4(const uint32_t* const (&q)[RP], const uint16_t* const (&s)[RP],
-                                       const uint16_t* const (&x)[NB], int K, int G, int lane,
-                                       float (&acc)[RP * NB]) {
-  const int words = K >> 3;
-  const int nblk = K / kNib;
-  for (int blk = 0; blk < nblk; ++blk) {
-    uint4 cw[RP];
-#pragma unroll
-    for (int r = 0; r < RP; ++r) cw[r] = *(const uint4*)(q[r] + blk * 256 + lane * 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e0 = (blk * 256 + j * 64 + lane) * 8;
-      uint32_t word[RP];
-      float sc[RP];
-#pragma unroll
-      for (int r = 0; r < RP; ++r) {
-        word[r] = j == 0 ? cw[r].x : j == 1 ? cw[r].y : j == 2 ? cw[r].z : cw[r].w;
-        sc[r] = bf2f(s[r][e0 / G]);
-      }
-      i4_word<RP, NB>(word, sc, x, e0, acc);
-    }
-  }
-  for (int t = nblk * 256 + lane; t < words; t += 64) {
-    uint32_t word[RP];
-    float sc[RP];
-#pragma unroll
-    for (int r = 0; r < RP; ++r) {
-      word[r] = q[r][t];
-      sc[r] = bf2f(s[r][(t * 8) / G]);
-    }
-    i4_word<RP, NB>(word, sc, x, t * 8, acc);
-  }
-}
-
-// acc -= 136 * s_g * sum_{k in g} x_k for the groups this lane owns.
-template <int RP, int NB>
-__device__ __forceinline__ void i4_correct(const uint16_t* const (&s)[RP], const float* xg, int ngr,
-                                           int lane, float (&acc)[RP * NB]) {
-  for (int g = lane; g < ngr; g += 64) {
-#pragma unroll
-    for (int r = 0; r < RP; ++r) {
-      const float c = -136.0f * bf2f(s[r][g]);
-#pragma unroll
-      for (int b = 0; b < NB; ++b) acc[r * NB + b] = fmaf(c, xg[b * ngr + g], acc[r * NB + b]);
-    }
-  }
-}
-
-__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
-  const float M = fmaxf(m, m2);
-  if (M == -INFINITY) return;
-  s = s * __expf(m - M) + s2 * __expf(m2 - M);
-  m = M;
-}
-
-struct Top2 {
-  float v1;
-  int i1;
-  float v2;
-};
-
-__device__ __forceinline__ void top2_merge(Top2& a, const Top2& o) {
-  if (o.v1 > a.v1 || (o.v1 == a.v1 && o.i1 < a.i1)) {
-    a.v2 = fmaxf(o.v2, a.v1);
-    a.v1 = o.v1;
-    a.i1 = o.i1;
-  } else {
-    a.v2 = fmaxf(a.v2, o.v1);
-  }
-}
-
-template <int EPI, bool XL, int NB>
-__device__ __forceinline__ void proj_chunk(const ProjArgs& a, int fmt, int nb, const int32_t* list,
-                                           int c0, const uint16_t* xs, const float* xg, float* red) {
-  constexpr int R = EpiTraits<EPI>::R;
-  constexpr int P = EpiTraits<EPI>::P;
-  constexpr int RP = R * P;
-  constexpr int V = RP * NB;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int gw = blockIdx.x * 4 + wave;
-  const int nw = gridDim.x * 4;
-  const int N = a.N, K = a.K;
-  const int ntiles = (N + R - 1) / R;
-
-  const uint16_t* x[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int bb = b < nb ? b : nb - 1;
-    x[b] = XL ? xs + bb * K : a.x + (size_t)list[c0 + bb] * a.x_stride;
-  }
-  const int idx = xidx<V>(lane);
-  const int rr = idx / NB;
-  const int bsel = idx - rr * NB;
-  const bool lane_ok = lane < V && bsel < nb;
-  const int ngr = K / a.G;
-
-  // running reduction state of this lane (vocabulary epilogues)
-  float lm = -INFINITY, ls = 0.0f;
-  Top2 tp{-INFINITY, 0x7fffffff, -INFINITY};
-
-  for (int t = gw; t < ntiles; t += nw) {
-    const int n0 = t * R;
-    float acc[V];
-#pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = 0.0f;
-    if (fmt == 0) {
-      const uint16_t* w[RP];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int n = min(n0 + r, N - 1);
-        w[r] = bf_row(a, n);
-        if constexpr (P == 2) w[R + r] = a.wb2 + (size_t)n * K;
-      }
-      dot_bf16<RP, NB>(w, x, K, lane, acc);
-    } else {
-      const uint32_t* q[RP];
-      const uint16_t* s[RP];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int n = min(n0 + r, N - 1);
-        q[r] = a.q4 + (size_t)n * (K >> 3);
-        s[r] = a.s4 + (size_t)n * ngr;
-        if constexpr (P == 2) {
-          q[R + r] = a.q4b + (size_t)n * (K >> 3);
-          s[R + r] = a.s4b + (size_t)n * ngr;
-        }
-      }
-      dot_i4<RP, NB>(q, s, x, K, a.G, lane, acc);
-      i4_correct<RP, NB>(s, xg, ngr, lane, acc);
-    }
-    XRed<V, 0>::run(acc, lane);
-    const float v = acc[0];
-
-    if constexpr (EPI == EPI_SWIGLU) {
-      const float u = __shfl_xor(v, 1);
-      const int n = n0 + rr;  // bit 0 clear: gate half
-      if (lane_ok && (lane & 1) == 0 && n < N) {
-        const int seq = list[c0 + bsel];
-        const float g = v;
-        const float act = g / (1.0f + __expf(-g)) * u;
-        ((uint16_t*)a.y)[(size_t)seq * a.y_stride + n] = (uint16_t)f2bf(act);
-      }
-    } else {
-      const int n = n0 + rr;
-      if (lane_ok && n < N) {
-        if constexpr (EPI == EPI_BF16) {
-          const int seq = list[c0 + bsel];
-          ((uint16_t*)a.y)[(size_t)seq * a.y_stride + n] = (uint16_t)f2bf(v);
-        } else if constexpr (EPI == EPI_RESID) {
-          const int seq = list[c0 + bsel];
-          float* yp = (float*)a.y + (size_t)seq * a.y_stride + n;
-          const float nv = *yp + v;
-          *yp = nv;
-          if (a.y2) a.y2[(size_t)seq * a.y2_stride + n] = (uint16_t)f2bf(nv);
-        } else if constexpr (EPI == EPI_LSE) {
-          lse_merge(lm, ls, v, 1.0f);
-        } else if constexpr (EPI == EPI_ARGMAX) {
-          if (a.logits) a.logits[(size_t)list[c0 + bsel] * a.logits_stride + n] = v;
-          if (v > tp.v1) {
-            tp.v2 = tp.v1;
-            tp.v1 = v;
-            tp.i1 = n;
-          } else if (v > tp.v2) {
-            tp.v2 = v;
-          }
-        }
-      }
-    }
-  }
-
-  if constexpr (EPI == EPI_LSE || EPI == EPI_ARGMAX) {
-    float* rw = red + (wave * 64 + lane) * 4;
-    if constexpr (EPI == EPI_LSE) {
-      rw[0] = lm;
-      rw[1] = ls;
-    } else {
-      rw[0] = tp.v1;
-      rw[1] = __int_as_float(tp.i1);
-      rw[2] = tp.v2;
-    }
-    __syncthreads();
-    const int tid = threadIdx.x;
-    if (tid < nb) {
-      float* out = a.part + ((size_t)blockIdx.x * kMaxBatch + (c0 + tid)) * 4;
-      if constexpr (EPI == EPI_LSE) {
-        float m = -INFINITY, s = 0.0f;
-        for (int w = 0; w < 4; ++w)
-          for (int l = 0; l < V; ++l)
-            if (xidx<V>(l) % NB == tid) {
-              const float* src = red + (w * 64 + l) * 4;
-              lse_merge(m, s, src[0], src[1]);
-            }
-        out[0] = m;
-        out[1] = s;
-      } else {
-        Top2 best{-INFINITY, 0x7fffffff, -INFINITY};
-        for (int w = 0; w < 4; ++w)
-          for (int l = 0; l < V; ++l)
-            if (xidx<V>(l) % NB == tid) {
-              const float* src = red + (w * 64 + l) * 4;
-              top2_merge(best, Top2{src[0], __float_as_int(src[1]), src[2]});
-            }
-        out[0] = best.v1;
-        out[1] = __int_as_float(best.i1);
-        out[2] = best.v2;
-      }
-    }
-  }
-}
-
-template <int EPI, bool XL>
-__global__ __launch_bounds__(kProjThreads) void proj_kernel(const ProjArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[XL ? kXLdsElems : 8];
-  __shared__ float xg[kXgElems];
-  __shared__ float red[4 * 64 * 4];
-  const int K = a.K;
-  for (int fmt = 0; fmt < 2; ++fmt) {
-    const int32_t* cntp = fmt ? a.cnt_i4 : a.cnt_bf;
-    const int n = cntp ? min(max(*cntp, 0), kMaxBatch) : 0;
-    const int32_t* list = fmt ? a.list_i4 : a.list_bf;
-    for (int c0 = 0; c0 < n; c0 += 8) {
-      const int nb = min(8, n - c0);
-      __syncthreads();
-      if constexpr (XL) {
-        const int k8 = K >> 3;
-        for (int i = threadIdx.x; i < nb * k8; i += kProjThreads) {
-          const int b = i / k8;
-          const int kk = i - b * k8;
-          *(uint4*)&xs[b * K + kk * 8] =
-              *(const uint4*)(a.x + (size_t)list[c0 + b] * a.x_stride + kk * 8);
-        }
-      }
-      if (fmt == 1) {
-        __syncthreads();
-        const int ngr = K / a.G;
-        for (int i = threadIdx.x; i < nb * ngr; i += kProjThreads) {
-          const int b = i / ngr;
-          const int g = i - b * ngr;
-          const uint16_t* src = XL ? xs + b * K + g * a.G
-                                   : a.x + (size_t)list[c0 + b] * a.x_stride + g * a.G;
-          float sum = 0.0f;
-          for (int e = 0; e < a.G; ++e) sum += bf2f(src[e]);
-          xg[b * ngr + g] = sum;
-        }
-      }
-      __syncthreads();
-      if (nb == 1)
-        proj_chunk<EPI, XL, 1>(a, fmt, nb, list, c0, xs, xg, red);
-      else if (nb == 2)
-        proj_chunk<EPI, XL, 2>(a, fmt, nb, list, c0, xs, xg, red);
-      else if (nb <= 4)
-        proj_chunk<EPI, XL, 4>(a, fmt, nb, list, c0, xs, xg, red);
-      else
-        proj_chunk<EPI, XL, 8>(a, fmt, nb, list, c0, xs, xg, red);
-    }
-  }
-}
-
-template <int EPI>
-static void launch_proj_t(const ProjArgs& a, int nwg, hipStream_t s) {
-  if (a.K * 8 <= kXLdsElems)
-    hipLaunchKernelGGL((proj_kernel<EPI, true>), dim3(nwg), dim3(kProjThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((proj_kernel<EPI, false>), dim3(nwg), dim3(kProjThreads), 0, s, a);
-}
-
-void launch_proj(int epi, const ProjArgs& a, int nwg, hipStream_t s) {
-  switch (epi) {
-    case EPI_BF16: launch_proj_t<EPI_BF16>(a, nwg, s); break;
-    case EPI_RESID: launch_proj_t<EPI_RESID>(a, nwg, s); break;
-    case EPI_SWIGLU: launch_proj_t<EPI_SWIGLU>(a, nwg, s); break;
-    case EPI_LSE: launch_proj_t<EPI_LSE>(a, nwg, s); break;
-    case EPI_ARGMAX: launch_proj_t<EPI_ARGMAX>(a, nwg, s); break;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Step setup: embedding rows into the residual, exit state, row lists.
@@ -829,73 +421,6 @@ __global__ void advance_kernel(int32_t* lens, int B) {
 
 void launch_advance(int32_t* lens, int B, hipStream_t s) {
   hipLaunchKernelGGL(advance_kernel, dim3(1), dim3(64), 0, s, lens, B);
-}
-
-// ---------------------------------------------------------------------------
-// int4 exit copies: one thread per (row, group).
-//   s = bf16(max|w| / 7) (IEEE float32 division, then round to bf16)
-//   q = clamp(rint(w / s), -8, 7), or 0 when s == 0; stored as q + 8.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int stored_word(int t, int nblk) {
-  if (t < nblk * 256) return (t & ~255) + (t & 63) * 4 + ((t & 255) >> 6);
-  return t;
-}
-
-__global__ void quantize_kernel(const uint16_t* w, int N, int K, int G, uint32_t* codes,
-                                uint16_t* scales) {
-  const int ngr = K / G;
-  const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (long long)N * ngr) return;
-  const int n = (int)(gid / ngr);
-  const int g = (int)(gid - (long long)n * ngr);
-  const uint16_t* src = w + (size_t)n * K + (size_t)g * G;
-  float amax = 0.0f;
-  for (int e = 0; e < G; ++e) amax = fmaxf(amax, fabsf(bf2f(src[e])));
-  const uint32_t sb = f2bf(amax / 7.0f);
-  const float s = bf2f(sb);
-  const int words = K >> 3, nblk = K / kNib;
-  for (int dw = 0; dw < G / 8; ++dw) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      int q = 0;
-      if (s != 0.0f) {
-        q = (int)rintf(bf2f(src[dw * 8 + e]) / s);
-        q = min(7, max(-8, q));
-      }
-      word |= (uint32_t)(q + 8) << (4 * (e >> 1) + 16 * (e & 1));
-    }
-    const int t = (g * G) / 8 + dw;
-    codes[(size_t)n * words + stored_word(t, nblk)] = word;
-  }
-  scales[(size_t)n * ngr + g] = (uint16_t)sb;
-}
-
-void launch_quantize(const uint16_t* w, int N, int K, int G, uint32_t* codes, uint16_t* scales,
-                     hipStream_t s) {
-  const long long n = (long long)N * (K / G);
-  const int threads = 256;
-  const long long blocks = (n + threads - 1) / threads;
-  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)blocks), dim3(threads), 0, s, w, N, K, G, codes, scales);
-}
-
-__global__ void unpack_kernel(const uint32_t* codes, int K, int row0, int nrows, int8_t* out) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long long)nrows * K) return;
-  const int r = (int)(i / K);
-  const int k = (int)(i - (long long)r * K);
-  const int t = k >> 3, e = k & 7;
-  const uint32_t word = codes[(size_t)(row0 + r) * (K >> 3) + stored_word(t, K / kNib)];
-  const int u = (word >> (4 * (e >> 1) + 16 * (e & 1))) & 15;
-  out[i] = (int8_t)(u - 8);
-}
-
-void launch_unpack_codes(const uint32_t* codes, int N, int K, int row0, int nrows, int8_t* out,
-                         hipStream_t s) {
-  (void)N;
-  const long long n = (long long)nrows * K;
-  hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, codes, K, row0,
-                     nrows, out);
 }
 
 }  // namespace ee

@@ -53,7 +53,8 @@ def test_tiny_workload_full_generation(gpu):
                                                 ("hd64", 5, 40, 4)])
 def test_small_shapes_batched(gpu, name, batch, P, steps):
     from parity import run_parity
-    sh, w = _weights(name, 2.0, P, steps)
+    sh = SHAPES[name]
+    sh, w = _weights(name, min(2.0, sh.n_layers - 0.5), P, steps)
     res = run_parity(sh, w, batch, P, steps, 0.75, label=name)
     ex = np.stack(res.exits)
     assert ex.min() < sh.n_layers     # some exits happened
