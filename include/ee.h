@@ -71,10 +71,12 @@ typedef int32_t ee_status;
 typedef struct ee_model ee_model;
 typedef struct ee_kv_cache ee_kv_cache;
 
-/* Model shape.  Supported: n_layers >= 1; d_model, d_ff multiples of group_size;
- * group_size in {32, 64, 128}; head_dim even, 16 <= head_dim <= 256, multiple of
- * 16; n_heads a multiple of n_kv_heads with n_heads / n_kv_heads <= 16;
- * vocab >= 1; 1 <= max_batch <= 64; max_positions >= 1 bounds every position. */
+/* Model shape.  Supported (else EE_ERR_SHAPE): group_size in {32, 64, 128};
+ * d_model, d_ff and n_heads * head_dim multiples of group_size and of 32;
+ * head_dim in {32, 64, 128}; n_heads a multiple of n_kv_heads with at most 16
+ * query heads per kv head; d_model <= 32768 / min(8, max_batch) (the vocabulary
+ * GEMV stages its input rows in 64 KB of LDS).  Also n_layers >= 1, vocab >= 1,
+ * 1 <= max_batch <= 64 and max_positions >= 1 (bounds every position). */
 typedef struct ee_model_config {
   int32_t n_layers;
   int32_t d_model;
@@ -145,6 +147,14 @@ ee_status ee_kv_cache_create(ee_model *m, int32_t max_batch, int32_t max_seq,
  * clears its occupancy counters. */
 ee_status ee_kv_cache_reset(ee_kv_cache *c, int32_t seq);
 
+/* Discards the last n positions of sequence seq (all sequences when seq == -1):
+ * the length drops by n and, with occupancy tracking, the dropped slots' write
+ * counters are cleared, so the positions can be written again.  This is the
+ * rollback of a rejected token ("大语言模型解码加速：自适应层并行机制解析",
+ * section 3.1: on a failed verification the KV entries after the last valid
+ * token are discarded).  INVALID_ARG if n < 0 or n exceeds a length. */
+ee_status ee_kv_cache_rollback(ee_kv_cache *c, int32_t seq, int32_t n);
+
 /* Copies the max_batch sequence lengths to lens_host. */
 ee_status ee_kv_cache_lengths(const ee_kv_cache *c, int32_t *lens_host);
 
@@ -164,11 +174,14 @@ ee_status ee_kv_cache_destroy(ee_kv_cache *c);
  * int32, row-major) at full depth with the backbone weights (no exit heads),
  * writing KV slots at positions len_b .. len_b+P-1, then returns the greedy token
  * after the last position in out_tokens_host [batch].  That token is also kept
- * on the device as the next decode input.  hip_stream: a hipStream_t or NULL
- * (the library's own stream); the call returns after the work has finished.
+ * on the device as the next decode input.  last_logits_host: optional host
+ * [batch][V] float32 LM-head logits of the last position (NULL: not copied).
+ * hip_stream: a hipStream_t or NULL (the library's own stream); the call
+ * returns after the work has finished.
  * Errors: INVALID_ARG (token out of [0, V), batch out of range), CACHE_FULL. */
 ee_status ee_prefill(ee_model *m, ee_kv_cache *c, int32_t batch, const int32_t *tokens_host,
-                     int32_t P, void *hip_stream, int32_t *out_tokens_host);
+                     int32_t P, void *hip_stream, int32_t *out_tokens_host,
+                     float *last_logits_host);
 
 /* One decode step for sequences 0..batch-1.
  * in_tokens_host: [batch] input tokens, or NULL to use each sequence's last

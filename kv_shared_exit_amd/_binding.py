@@ -29,7 +29,7 @@ EE_KV_TRACK_OCCUPANCY = 1
 
 EXPORTS = [
     "ee_create_model", "ee_destroy_model", "ee_kv_cache_bytes", "ee_kv_cache_create",
-    "ee_kv_cache_reset", "ee_kv_cache_lengths", "ee_kv_cache_read", "ee_kv_cache_occupancy",
+    "ee_kv_cache_reset", "ee_kv_cache_rollback", "ee_kv_cache_lengths", "ee_kv_cache_read", "ee_kv_cache_occupancy",
     "ee_kv_cache_destroy", "ee_prefill", "ee_decode_step", "ee_exit_weights_read",
     "ee_profile_enable", "ee_profile_read", "ee_last_error",
 ]
@@ -82,11 +82,12 @@ def load() -> C.CDLL:
         "ee_kv_cache_bytes": [P, I32, I32, C.POINTER(SZ)],
         "ee_kv_cache_create": [P, I32, I32, P, SZ, U32, C.POINTER(P)],
         "ee_kv_cache_reset": [P, I32],
+        "ee_kv_cache_rollback": [P, I32, I32],
         "ee_kv_cache_lengths": [P, P],
         "ee_kv_cache_read": [P, I32, I32, I32, I32, P, P],
         "ee_kv_cache_occupancy": [P, P],
         "ee_kv_cache_destroy": [P],
-        "ee_prefill": [P, P, I32, P, I32, P, P],
+        "ee_prefill": [P, P, I32, P, I32, P, P, P],
         "ee_decode_step": [P, P, I32, P, P, P, P, P, P, P],
         "ee_exit_weights_read": [P, I32, I32, I32, I32, P, P],
         "ee_profile_enable": [P, I32],

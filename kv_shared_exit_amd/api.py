@@ -124,6 +124,9 @@ class KVCache:
     def reset(self, seq: int = -1):
         B.check(self.lib.ee_kv_cache_reset(self.h, seq))
 
+    def rollback(self, seq: int = -1, n: int = 1):
+        B.check(self.lib.ee_kv_cache_rollback(self.h, seq, n))
+
     def lengths(self) -> np.ndarray:
         out = np.empty(self.max_batch, np.int32)
         B.check(self.lib.ee_kv_cache_lengths(self.h, B._ptr(out)))
@@ -150,13 +153,15 @@ def _stream_ptr(stream):
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def prefill(model: Model, cache: KVCache, prompts, stream=None) -> np.ndarray:
+def prefill(model: Model, cache: KVCache, prompts, stream=None, logits: bool = False):
+    """Prefill; returns the first tokens, or (tokens, last-position logits) with ``logits``."""
     prompts = np.ascontiguousarray(prompts, dtype=np.int32)
     batch, P = prompts.shape
     out = np.empty(batch, np.int32)
+    lg = np.empty((batch, model.shape.vocab), np.float32) if logits else None
     B.check(model.lib.ee_prefill(model.h, cache.h, batch, B._ptr(prompts), P,
-                                 _stream_ptr(stream), B._ptr(out)))
-    return out
+                                 _stream_ptr(stream), B._ptr(out), B._ptr(lg)))
+    return (out, lg) if logits else out
 
 
 def decode_step(model: Model, cache: KVCache, batch: int, tokens=None, forced=None, gamma=None,

@@ -70,7 +70,7 @@ struct ee_model {
   float *d_cos = nullptr, *d_sin = nullptr;
   // workspaces
   float* h = nullptr;
-  uint16_t *hb = nullptr, *x = nullptr, *qkv = nullptr, *qrot = nullptr, *attn_o = nullptr;
+  uint16_t *qrot = nullptr, *attn_o = nullptr;
   uint16_t *act = nullptr, *z = nullptr;
   float* head_part = nullptr;
   float* attn_part = nullptr;
@@ -183,7 +183,7 @@ void validate_config(const ee_model_config& c) {
   shape(qd % c.group_size == 0, "n_heads * head_dim must be a multiple of group_size");
   shape(c.d_model % 8 == 0 && c.d_ff % 8 == 0, "widths must be multiples of 8");
   shape(c.d_model <= kXLdsElems / std::min(8, c.max_batch),
-        "d_model too wide for the vocabulary GEMV's staged input at this max_batch");
+        "d_model too wide for the projections' staged inputs at this max_batch");
   shape(c.d_model % 32 == 0 && c.d_ff % 32 == 0, "widths must be multiples of 32");
 }
 
@@ -233,6 +233,26 @@ void set_seg1(ProjArgs& a, const void* w, int N) {
   a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = N;
 }
 
+// Attention work split: one wave per run of `tpw` 64-position tiles of a
+// (sequence, kv head); tpw grows with the context so that the launch keeps
+// about 2048 waves (and its partials stay a few percent of the K/V bytes).
+void attn_split(int S, int B, int Hkv, int* tpw, int* nch) {
+  const int tiles = (S + 63) / 64;
+  int t = 1;
+  while (t < tiles && (long long)B * Hkv * ((tiles + t - 1) / t) > 2048) t *= 2;
+  *tpw = t;
+  *nch = (tiles + t - 1) / t;
+}
+
+// Input of a projection that reads bf16(rmsnorm(h) * g): the projection
+// normalises the residual rows while staging them.
+void norm_input(ee_model* m, ProjArgs& a, const void* gain) {
+  a.eps = m->cfg.rms_eps;
+  a.xmode = 1;
+  a.h = m->h;
+  a.gain = (const uint16_t*)gain;
+}
+
 struct Debug {
   bool hidden = false, logits = false;
 };
@@ -261,7 +281,6 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
     const LayerQ* q = (int4 && l >= 2) ? &m->lq[l - 1] : nullptr;
     const size_t kvoff = (size_t)(l - 1) * c->Bmax * Hkv * c->S * hd;
 
-    launch_rmsnorm(m->h, (const uint16_t*)w.attn_norm, m->x, B, d, cf.rms_eps, s);
     {
       ProjArgs a = base_args(m);
       a.N = nqkv;
@@ -281,15 +300,21 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       }
       a.list_bf = list_bf;
       a.cnt_bf = cnt_bf;
-      a.x = m->x;
-      a.x_stride = d;
-      a.y = m->qkv;
-      a.y_stride = nqkv;
-      launch_proj(EPI_BF16, a, kNwg, s);
+      norm_input(m, a, w.attn_norm);
+      // epilogue: RoPE on q and k, k and v into this position's shared cache slot
+      a.cosT = m->d_cos;
+      a.sinT = m->d_sin;
+      a.lens = c->lens;
+      a.qrot = m->qrot;
+      a.Kl = c->K + kvoff;
+      a.Vl = c->V + kvoff;
+      a.occ_l = c->occ ? c->occ + (size_t)(l - 1) * c->Bmax * c->S : nullptr;
+      a.H = H;
+      a.Hkv = Hkv;
+      a.hd = hd;
+      a.S = c->S;
+      launch_proj(EPI_QKV, a, kNwg, B, s);
     }
-    launch_rope_kv(m->qkv, m->qrot, c->K + kvoff, c->V + kvoff,
-                   c->occ ? c->occ + (size_t)(l - 1) * c->Bmax * c->S : nullptr, c->lens, m->d_cos,
-                   m->d_sin, B, H, Hkv, hd, c->S, c->Bmax, s);
     {
       AttnArgs a{};
       a.q = m->qrot;
@@ -302,7 +327,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       a.Hkv = Hkv;
       a.hd = hd;
       a.B = B;
-      a.nch = (c->S + kAttnChunk - 1) / kAttnChunk;
+      attn_split(c->S, B, Hkv, &a.tpw, &a.nch);
       a.scale = (float)(1.0 / std::sqrt((double)hd));
       a.part = m->attn_part;
       a.out = m->attn_o;
@@ -325,9 +350,8 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       a.x_stride = qd;
       a.y = m->h;
       a.y_stride = d;
-      launch_proj(EPI_RESID, a, kNwg, s);
+      launch_proj(EPI_RESID, a, kNwg, B, s);
     }
-    launch_rmsnorm(m->h, (const uint16_t*)w.ffn_norm, m->x, B, d, cf.rms_eps, s);
     {
       ProjArgs a = base_args(m);
       a.N = F;
@@ -344,11 +368,10 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       }
       a.list_bf = list_bf;
       a.cnt_bf = cnt_bf;
-      a.x = m->x;
-      a.x_stride = d;
+      norm_input(m, a, w.ffn_norm);
       a.y = m->act;
       a.y_stride = F;
-      launch_proj(EPI_SWIGLU, a, kNwg, s);
+      launch_proj(EPI_SWIGLU, a, kNwg, B, s);
     }
     const bool head_here = heads && l < L;
     {
@@ -368,9 +391,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       a.x_stride = F;
       a.y = m->h;
       a.y_stride = d;
-      a.y2 = head_here ? m->hb : nullptr;
-      a.y2_stride = d;
-      launch_proj(EPI_RESID, a, kNwg, s);
+      launch_proj(EPI_RESID, a, kNwg, B, s);
     }
     if (head_here) {
       {
@@ -380,11 +401,11 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
         set_seg1(a, w.head_T, d);
         a.list_bf = st->act;
         a.cnt_bf = &st->n_act;
-        a.x = m->hb;
-        a.x_stride = d;
+        a.xmode = 2;  // bf16(h), staged from the residual
+        a.h = m->h;
         a.y = m->z;
         a.y_stride = d;
-          launch_proj(EPI_BF16, a, kNwg, s);
+        launch_proj(EPI_BF16, a, kNwg, B, s);
       }
       {
         ProjArgs a = base_args(m);
@@ -398,7 +419,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
         a.part = m->head_part;
         hipEvent_t e0;
         prof_begin(m, s, &e0);
-          launch_proj(EPI_LSE, a, kNwg, s);
+        launch_proj(EPI_LSE, a, kNwg, B, s);
         prof_end(m, s);
       }
       launch_decide(st, m->head_part, kNwg, m->d_gamma, l, L, B, m->p_rec, s);
@@ -408,19 +429,17 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
                               (size_t)d * 4, (size_t)d * 4, B, hipMemcpyDeviceToDevice, s));
   }
   if (final) {
-    launch_rmsnorm(m->h, m->final_norm, m->x, B, d, cf.rms_eps, s);
     ProjArgs a = base_args(m);
     a.N = cf.vocab;
     a.K = d;
     set_seg1(a, m->lm_head, cf.vocab);
     a.list_bf = st->all;
     a.cnt_bf = &st->n_all;
-    a.x = m->x;
-    a.x_stride = d;
+    norm_input(m, a, m->final_norm);
     a.part = m->head_part;
     a.logits = dbg.logits ? m->dbg_logits : nullptr;
     a.logits_stride = cf.vocab;
-    launch_proj(EPI_ARGMAX, a, kNwg, s);
+    launch_proj(EPI_ARGMAX, a, kNwg, B, s);
     launch_final(st, m->head_part, kNwg, B, cf.vocab, c->lens, 1, s);
   } else {
     launch_advance(c->lens, B, s);
@@ -538,15 +557,20 @@ ee_status ee_create_model(const ee_model_config* cfg, const ee_weights* w, const
       HIPCHK(hipMemcpy(m->d_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice));
       const int Bm = kMaxBatch;
       m->h = m->alloc<float>((size_t)Bm * d);
-      m->hb = m->alloc<uint16_t>((size_t)Bm * d);
-      m->x = m->alloc<uint16_t>((size_t)Bm * d);
-      m->qkv = m->alloc<uint16_t>((size_t)Bm * (qd + 2 * kvd));
       m->qrot = m->alloc<uint16_t>((size_t)Bm * qd);
       m->attn_o = m->alloc<uint16_t>((size_t)Bm * qd);
       m->act = m->alloc<uint16_t>((size_t)Bm * F);
       m->z = m->alloc<uint16_t>((size_t)Bm * d);
       m->head_part = m->alloc<float>((size_t)kNwg * kMaxBatch * 4);
-      m->nch_max = (c.max_positions + kAttnChunk - 1) / kAttnChunk;
+      // the most partials any cache (S <= max_positions, B >= 1) can need: the
+      // split is not monotone in S, so take the maximum over every tile count
+      m->nch_max = 1;
+      for (int tiles = 1; tiles <= (c.max_positions + 63) / 64; ++tiles) {
+        int tpw = 0, nch = 0;
+        attn_split(tiles * 64, 1, c.n_kv_heads, &tpw, &nch);
+        m->nch_max = std::max(m->nch_max, nch);
+      }
+      if (m->nch_max > 2048) fail(EE_ERR_SHAPE, "too many attention partials");
       m->attn_part = m->alloc<float>((size_t)c.max_batch * c.n_heads * m->nch_max * (c.head_dim + 2));
       m->st = m->alloc<StepState>(1);
       m->p_rec = m->alloc<float>((size_t)std::max(L - 1, 1) * kMaxBatch);
@@ -651,6 +675,30 @@ ee_status ee_kv_cache_reset(ee_kv_cache* c, int32_t seq) {
   });
 }
 
+ee_status ee_kv_cache_rollback(ee_kv_cache* c, int32_t seq, int32_t n) {
+  return guard([&] {
+    if (!c) fail(EE_ERR_INVALID_ARG, "null cache");
+    check_model(c->m);
+    if (seq < -1 || seq >= c->Bmax) fail(EE_ERR_INVALID_ARG, "seq out of range");
+    if (n < 0) fail(EE_ERR_INVALID_ARG, "n must be >= 0");
+    const int lo = seq < 0 ? 0 : seq, hi = seq < 0 ? c->Bmax : seq + 1;
+    for (int b = lo; b < hi; ++b)
+      if (c->hlens[b] < n) fail(EE_ERR_INVALID_ARG, "rollback beyond the start of a sequence");
+    if (n == 0) return;
+    ee_model* m = c->m;
+    with_sticky(m, [&] {
+      for (int b = lo; b < hi; ++b) {
+        c->hlens[b] -= n;
+        if (c->occ)
+          for (int l = 0; l < m->cfg.n_layers; ++l)
+            HIPCHK(hipMemsetAsync(c->occ + ((size_t)l * c->Bmax + b) * c->S + c->hlens[b], 0, n, m->own));
+      }
+      HIPCHK(hipMemcpyAsync(c->lens, c->hlens.data(), c->Bmax * 4, hipMemcpyHostToDevice, m->own));
+      HIPCHK(hipStreamSynchronize(m->own));
+    });
+  });
+}
+
 ee_status ee_kv_cache_lengths(const ee_kv_cache* c, int32_t* lens_host) {
   return guard([&] {
     if (!c || !lens_host) fail(EE_ERR_INVALID_ARG, "null argument");
@@ -713,7 +761,7 @@ ee_status ee_kv_cache_destroy(ee_kv_cache* c) {
 }
 
 ee_status ee_prefill(ee_model* m, ee_kv_cache* c, int32_t batch, const int32_t* tokens_host, int32_t P,
-                     void* hip_stream, int32_t* out_tokens_host) {
+                     void* hip_stream, int32_t* out_tokens_host, float* last_logits_host) {
   return guard([&] {
     check_model(m);
     if (!c || c->m != m) fail(EE_ERR_INVALID_ARG, "cache does not belong to the model");
@@ -741,9 +789,15 @@ ee_status ee_prefill(ee_model* m, ee_kv_cache* c, int32_t batch, const int32_t* 
       for (int b = 0; b < batch; ++b) m->h_in[kMaxBatch + b] = 0;
       HIPCHK(hipMemcpyAsync(m->st->forced, m->h_in + kMaxBatch, batch * 4, hipMemcpyHostToDevice, s));
       Debug dbg;
+      Debug last;
+      last.logits = last_logits_host != nullptr;
+      if (last.logits && !m->dbg_logits) m->dbg_logits = m->alloc<float>((size_t)kMaxBatch * m->cfg.vocab);
       for (int t = 0; t < P; ++t)
-        enqueue_position(m, c, batch, false, t == P - 1, m->d_prompt, P, t, dbg, s);
+        enqueue_position(m, c, batch, false, t == P - 1, m->d_prompt, P, t, t == P - 1 ? last : dbg, s);
       HIPCHK(hipMemcpyAsync(m->h_out, m->st->out_tok, batch * 4, hipMemcpyDeviceToHost, s));
+      if (last.logits)
+        HIPCHK(hipMemcpyAsync(last_logits_host, m->dbg_logits, (size_t)batch * m->cfg.vocab * 4,
+                              hipMemcpyDeviceToHost, s));
       HIPCHK(hipStreamSynchronize(s));
       m->ev_used = 0;
       std::memcpy(out_tokens_host, m->h_out, batch * 4);

@@ -8,11 +8,10 @@ namespace ee {
 
 constexpr int kMaxBatch = 64;      // rows of one decode step
 constexpr int kProjThreads = 512;  // 8 waves per projection workgroup
-constexpr int kAttnChunk = 256;    // positions per attention workgroup (4 waves x 64)
 constexpr int kXLdsElems = 32768;  // bf16 elements of the staged GEMV input (64 KB)
 constexpr int kNwgMax = 512;       // projection grid cap (size of the per-workgroup partial buffers)
 
-enum Epi { EPI_BF16 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LSE = 3, EPI_ARGMAX = 4 };
+enum Epi { EPI_BF16 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LSE = 3, EPI_ARGMAX = 4, EPI_QKV = 5 };
 
 // Device-resident state of one step.  Every value that changes from step to
 // step lives here, so a captured graph replays unchanged.
@@ -31,22 +30,33 @@ struct StepState {
 
 struct ProjArgs {
   int N, K, G;
+  int ldw, k0;           // weight row length and first column of this launch's K range
   int nseg;              // bf16 row segments (QKV: 3)
   int seg_end[3];        // cumulative end row of each segment
-  const uint16_t* wb[3]; // bf16 segment bases, row-major [rows][K]
+  const uint16_t* wb[3]; // bf16 segment bases, row-major [rows][ldw]
   const uint16_t* wb2;   // SwiGLU: the "up" matrix (gate is wb[0])
-  const uint32_t* q4;    // int4 codes [N16][K/8] dwords (layout: ee_proj.hip)
-  const uint16_t* s4;    // bf16 scales [N16/16][K/G][16]
+  const uint32_t* q4;    // int4 codes [N16][ldw/8] dwords (layout: ee_proj.hip)
+  const uint16_t* s4;    // bf16 scales [N16/16][ldw/G][16]
   const uint32_t* q4b;   // SwiGLU "up" codes
   const uint16_t* s4b;
-  const uint16_t* x;     // bf16 input rows, indexed by sequence id
+  const uint16_t* x;     // bf16 input rows, indexed by sequence id (xmode 0)
   int x_stride;
+  int xmode;             // 0: x; 1: bf16(rmsnorm(h) * gain); 2: bf16(h)   (staged inputs only)
+  const float* h;        // float32 residual rows [b][K] (xmode 1, 2)
+  const uint16_t* gain;  // RMSNorm gains [K] (xmode 1)
+  float eps;
   const int32_t* list_bf; const int32_t* cnt_bf;  // rows run with bf16 weights
   const int32_t* list_i4; const int32_t* cnt_i4;  // rows run with int4 weights (may be null)
   void* y; int y_stride;                          // output rows, indexed by sequence id
-  uint16_t* y2; int y2_stride;                    // EPI_RESID: bf16 copy of the new residual
   float* part;                                    // EPI_LSE / EPI_ARGMAX partials per workgroup
   float* logits; int logits_stride;               // EPI_ARGMAX: optional logits out
+  // EPI_QKV: RoPE on q and k, q to qrot, k and v into the cache slot of the position
+  const float* cosT; const float* sinT;           // [pos][hd/2]
+  const int32_t* lens;                            // position of the current token
+  uint16_t* qrot;                                 // [b][H*hd]
+  uint16_t* Kl; uint16_t* Vl;                     // layer base [Bmax][Hkv][S][hd]
+  uint8_t* occ_l;                                 // [Bmax][S] write counters, or null
+  int H, Hkv, hd, S;
 };
 
 struct AttnArgs {
@@ -55,21 +65,21 @@ struct AttnArgs {
   const uint16_t* V;
   int S, Bmax;
   const int32_t* lens; // position of the current token per sequence
-  int H, Hkv, hd, B, nch;
+  int H, Hkv, hd, B;
+  int tpw, nch;        // 64-position tiles per wave; waves (partials) per (sequence, kv head)
   float scale;
   float* part;         // [B][H][nch][hd + 2]
   uint16_t* out;       // [b][H*hd]
 };
 
 // launchers (ee_kernels.hip)
-void launch_proj(int epi, const ProjArgs& a, int nwg, hipStream_t s);
+// Whether min(8, batch) input rows of width K fit the projection's LDS stage.
+// launch_proj splits a wider EPI_RESID projection (xmode 0) into launches over
+// column ranges of W that do fit; other projections must fit.
+bool proj_fits(int K, int batch);
+void launch_proj(int epi, const ProjArgs& a, int nwg, int batch, hipStream_t s);
 void launch_init(StepState* st, const int32_t* prompt, int P, int t, int B, int L,
                  const uint16_t* emb, int d, int V, float* h, float* p_rec, hipStream_t s);
-void launch_rmsnorm(const float* h, const uint16_t* g, uint16_t* x, int B, int d, float eps,
-                    hipStream_t s);
-void launch_rope_kv(const uint16_t* qkv, uint16_t* qrot, uint16_t* Kl, uint16_t* Vl,
-                    uint8_t* occ_l, const int32_t* lens, const float* cosT, const float* sinT,
-                    int B, int H, int Hkv, int hd, int S, int Bmax, hipStream_t s);
 void launch_attention(const AttnArgs& a, hipStream_t s);
 void launch_decide(StepState* st, const float* part, int nwg, const float* gamma, int layer,
                    int L, int B, float* p_rec, hipStream_t s);

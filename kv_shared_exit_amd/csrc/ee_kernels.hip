@@ -4,14 +4,13 @@
 // 2.1-2.2; CALM explainer sections 2.2 and 3.3) is built from these kernels:
 //   init       embed the input tokens into the float32 residual, reset the
 //              per-step exit state and the row lists
-//   rmsnorm    bf16(h * rsqrt(mean(h^2) + eps) * g)
-//   proj       (ee_proj.hip) the projections over both weight copies, and
-//              the int4 packer
-//   rope_kv    rotate q and k, write k and v into the shared cache slot of the
-//              position (the same slot for either weight copy)
-//   attention  grouped-query decode attention, split over 256-position chunks;
-//              K/V tiles staged in LDS, scores on MFMA, softmax per wave, and a
-//              combine kernel merging the chunks
+//   proj       (ee_proj.hip) the projections over both weight copies, with the
+//              RMSNorm in their input staging and RoPE plus the write of k and
+//              v into the shared cache slot of the position (the same slot for
+//              either weight copy) in the QKV epilogue; the int4 packer
+//   attention  grouped-query decode attention: one wave per run of 64-position
+//              tiles of a (sequence, kv head), scores on MFMA, online softmax,
+//              and a combine kernel merging the runs
 //   decide     finish the exit head (p = 1 / sum exp(l - max)), compare with
 //              gamma or apply a forced exit, rebuild the backbone/exit row lists
 //              with a wave ballot (active-sequence compaction)
@@ -22,7 +21,6 @@
 #include <math.h>
 
 namespace ee {
-
 
 // ---------------------------------------------------------------------------
 // Step setup: embedding rows into the residual, exit state, row lists.
@@ -57,249 +55,205 @@ void launch_init(StepState* st, const int32_t* prompt, int P, int t, int B, int 
 }
 
 // ---------------------------------------------------------------------------
-// RMSNorm: one workgroup per row, fixed reduction order.
+// Grouped-query decode attention over the shared cache (River-LLM explainer,
+// section 3.1: softmax(q K^T / sqrt(d)) V over every cached position).
+//
+// One wave per (sequence b, kv head j, run of `tpw` 64-position tiles).  For
+// each tile the wave reads K straight from HBM into MFMA A operands (16
+// positions x 32 head dims per lane group, 16-byte loads) and computes the
+// scores of all q heads of the group with v_mfma_f32_16x16x32_bf16 (q heads
+// padded to 16 as the B operand, held in registers).  Softmax statistics are
+// per q head (online across the wave's tiles); the probabilities go through
+// LDS (1 KB) to the PV product, which runs on the vector ALUs with V rows read
+// as 16-byte chunks (16 lanes per position row for head_dim 128).  Each wave
+// writes one (m, l, o) partial; attn_combine merges a sequence's partials in
+// order.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, const uint16_t* g, uint16_t* x,
-                                                      int d, float eps) {
-  __shared__ float wsum[4];
-  const int b = blockIdx.x;
-  const float* hr = h + (size_t)b * d;
-  float ss = 0.0f;
-  for (int i = threadIdx.x; i < d; i += 256) ss = fmaf(hr[i], hr[i], ss);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
-  const float r = 1.0f / sqrtf(tot / (float)d + eps);
-  uint16_t* xr = x + (size_t)b * d;
-  for (int i = threadIdx.x; i < d; i += 256) xr[i] = (uint16_t)f2bf(hr[i] * r * bf2f(g[i]));
-}
-
-void launch_rmsnorm(const float* h, const uint16_t* g, uint16_t* x, int B, int d, float eps,
-                    hipStream_t s) {
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(B), dim3(256), 0, s, h, g, x, d, eps);
-}
-
-// ---------------------------------------------------------------------------
-// RoPE on q and k, and the shared-slot K/V write of the current position.
-// ---------------------------------------------------------------------------
-__global__ void rope_kv_kernel(const uint16_t* qkv, uint16_t* qrot, uint16_t* Kl, uint16_t* Vl,
-                               uint8_t* occ_l, const int32_t* lens, const float* cosT,
-                               const float* sinT, int H, int Hkv, int hd, int S) {
-  const int b = blockIdx.x;
-  const int pos = lens[b];
-  const int half = hd >> 1;
-  const uint16_t* row = qkv + (size_t)b * (H + 2 * Hkv) * hd;
-  const float* cr = cosT + (size_t)pos * half;
-  const float* sr = sinT + (size_t)pos * half;
-  for (int i = threadIdx.x; i < (H + Hkv) * half; i += blockDim.x) {
-    const int head = i / half;
-    const int e = i - head * half;
-    const uint16_t* src = row + head * hd;
-    const float x1 = bf2f(src[e]);
-    const float x2 = bf2f(src[e + half]);
-    const float c = cr[e], sn = sr[e];
-    const uint16_t o1 = (uint16_t)f2bf(x1 * c - x2 * sn);
-    const uint16_t o2 = (uint16_t)f2bf(x2 * c + x1 * sn);
-    uint16_t* dst;
-    if (head < H)
-      dst = qrot + ((size_t)b * H + head) * hd;
-    else
-      dst = Kl + (((size_t)b * Hkv + (head - H)) * S + pos) * hd;
-    dst[e] = o1;
-    dst[e + half] = o2;
-  }
-  const uint16_t* vsrc = row + (size_t)(H + Hkv) * hd;
-  for (int i = threadIdx.x; i < Hkv * hd; i += blockDim.x) {
-    const int kh = i / hd;
-    const int e = i - kh * hd;
-    Vl[(((size_t)b * Hkv + kh) * S + pos) * hd + e] = vsrc[i];
-  }
-  if (occ_l && threadIdx.x == 0) occ_l[(size_t)b * S + pos] += 1;
-}
-
-void launch_rope_kv(const uint16_t* qkv, uint16_t* qrot, uint16_t* Kl, uint16_t* Vl, uint8_t* occ_l,
-                    const int32_t* lens, const float* cosT, const float* sinT, int B, int H, int Hkv,
-                    int hd, int S, int Bmax, hipStream_t s) {
-  (void)Bmax;
-  hipLaunchKernelGGL(rope_kv_kernel, dim3(B), dim3(256), 0, s, qkv, qrot, Kl, Vl, occ_l, lens, cosT,
-                     sinT, H, Hkv, hd, S);
-}
-
-// ---------------------------------------------------------------------------
-// Grouped-query decode attention over the shared cache.
-// Block (chunk c, kv head j, sequence b): positions [256c, 256c+256) of the
-// sequence's context; wave w owns 64 of them.  Per wave: stage the K tile in
-// LDS (rows padded by 16 bytes), scores S[t][i] = K[t] . q_i on MFMA
-// (16 positions x 16 padded q heads x 32 head dims per instruction), softmax
-// statistics per q head, stage the V tile into the same LDS, accumulate
-// o_i = sum_t p[t][i] V[t] on the vector ALUs, merge the four waves, and write
-// the chunk's (m, l, o) partial.  attn_combine merges the chunks in order.
-// ---------------------------------------------------------------------------
-template <int HD>
-__device__ __forceinline__ void stage_tile(uint16_t* tile, const uint16_t* src, int nval, int lane) {
-  constexpr int CPR = HD / 8;  // 16-byte chunks per row
-  constexpr int LD = HD + 8;
-  for (int i = lane; i < 64 * CPR; i += 64) {
-    const int row = i / CPR;
-    const int ch = i - row * CPR;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row < nval) v = *(const uint4*)(src + (size_t)row * HD + ch * 8);
-    *(uint4*)(tile + row * LD + ch * 8) = v;
-  }
-}
-
 template <int HD, int GQ>
-__global__ __launch_bounds__(256) void attn_kernel(const AttnArgs a) {
-  constexpr int LD = HD + 8;
-  constexpr int KK = HD / 32;
-  constexpr int DPL = 2;             // head dims per lane in the PV pass
-  constexpr int LPR = HD / DPL;      // lanes per position row
-  constexpr int NPG = 64 / LPR;      // position groups per wave
-  __shared__ __attribute__((aligned(16))) uint16_t tile[4][64 * LD];
-  __shared__ float pb[4][64][GQ];
-  __shared__ float mw[4][GQ], lw[4][GQ];
-  __shared__ float ow[4][GQ][HD];
+__global__ __launch_bounds__(64) void attn_kernel(const AttnArgs a) {
+  constexpr int KK = HD / 32;          // MFMA steps over the head dim
+  constexpr int CPR = HD / 8;          // 16-byte chunks per K/V row
+  constexpr int RPI = 64 / CPR;        // rows per V load instruction
+  constexpr int NVL = 64 / RPI;        // V loads per 64-row tile
+  __shared__ float pb[64][GQ];
+  __shared__ float cr[GQ];
 
   const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
   const int ctx = a.lens[b] + 1;
-  const int start = c * kAttnChunk;
-  if (start >= ctx) return;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tpw = a.tpw;
+  const int tstart = c * tpw * 64;
+  if (tstart >= ctx) return;
+  const int lane = threadIdx.x;
   const int g = a.H / a.Hkv;
-  const int t0 = start + w * 64;
-  const int nval = max(0, min(64, ctx - t0));
-  const size_t rowbase = (((size_t)b * a.Hkv + j) * a.S + t0) * HD;
-  uint16_t* tw = tile[w];
+  const int hh = lane & 15;            // q head in the MFMA B / C layouts
+  const int qc = lane >> 4;
+  const size_t base = ((size_t)b * a.Hkv + j) * a.S;   // row of position 0
+  const uint16_t* Kb = a.K + base * HD;
+  const uint16_t* Vb = a.V + base * HD;
 
-  const int hh = lane & 15;
   uint4 qv[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     qv[kk] = make_uint4(0, 0, 0, 0);
-    if (hh < g)
-      qv[kk] = *(const uint4*)(a.q + ((size_t)b * a.H + j * g + hh) * HD + (lane >> 4) * 8 + 32 * kk);
+    if (hh < g) qv[kk] = *(const uint4*)(a.q + ((size_t)b * a.H + j * g + hh) * HD + qc * 8 + 32 * kk);
   }
+  const int vr = lane / CPR, vc = lane - vr * CPR;   // V: row within load, 16-byte chunk
 
-  stage_tile<HD>(tw, a.K + rowbase, nval, lane);
-  __syncthreads();
+  float m = -INFINITY, l = 0.0f;   // per q head hh (replicated over qc)
+  float o[GQ][8];
+#pragma unroll
+  for (int i = 0; i < GQ; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[i][e] = 0.0f;
 
-  float m = -INFINITY, l = 0.0f;
-  if (nval > 0) {
+  const int tend = min(ctx, tstart + tpw * 64);
+  for (int t0 = tstart; t0 < tend; t0 += 64) {
+    const int nval = min(64, ctx - t0);
+    // scores S[t][i] for 64 positions
     float sc[4][4];
+    float mt = -INFINITY;
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
+      const int row = t0 + min(pt * 16 + (lane & 15), nval - 1);
+      uint4 kv[KK];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) kv[kk] = ld_stream(Kb + (size_t)row * HD + qc * 8 + 32 * kk);
       f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const uint4 av = *(const uint4*)(tw + (pt * 16 + (lane & 15)) * LD + (lane >> 4) * 8 + 32 * kk);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+      for (int kk = 0; kk < KK; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv[kk]),
                                                       __builtin_bit_cast(bf16x8_t, qv[kk]), acc, 0, 0, 0);
-      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int p = pt * 16 + (lane >> 4) * 4 + r;
+        const int p = pt * 16 + qc * 4 + r;
         sc[pt][r] = p < nval ? acc[r] * a.scale : -INFINITY;
-        m = fmaxf(m, sc[pt][r]);
+        mt = fmaxf(mt, sc[pt][r]);
       }
     }
-    m = fmaxf(m, __shfl_xor(m, 16));
-    m = fmaxf(m, __shfl_xor(m, 32));
+    // V rows of this tile: lane reads chunk vc of rows vr, vr + RPI, ...
+    uint4 vv[NVL];
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+      const int row = t0 + min(vr + i * RPI, nval - 1);
+      vv[i] = ld_stream(Vb + (size_t)row * HD + vc * 8);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m, mt);
+    const float corr = __expf(m - mn);   // 0 on the first tile (m = -inf)
+    float ls = 0.0f;
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = __expf(sc[pt][r] - m);
-        l += p;
-        if (hh < GQ) pb[w][pt * 16 + (lane >> 4) * 4 + r][hh] = p;
+        const float p = __expf(sc[pt][r] - mn);
+        ls += p;
+        if (hh < GQ) pb[pt * 16 + qc * 4 + r][hh] = p;
       }
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-  }
-  if (lane < GQ) {
-    mw[w][lane] = m;
-    lw[w][lane] = l;
-  }
-  __syncthreads();
-  stage_tile<HD>(tw, a.V + rowbase, nval, lane);
-  __syncthreads();
-
-  float o[GQ][DPL];
-#pragma unroll
-  for (int i = 0; i < GQ; ++i)
-#pragma unroll
-    for (int d = 0; d < DPL; ++d) o[i][d] = 0.0f;
-  const int pg = lane / LPR, dl = lane - pg * LPR;
-  for (int t = pg; t < nval; t += NPG) {
-    const uint32_t vv = *(const uint32_t*)(tw + t * LD + dl * DPL);
-    const float v0 = bf2f(vv & 0xffffu), v1 = bf2f(vv >> 16);
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+    l = l * corr + ls;
+    m = mn;
+    if (lane < GQ) cr[lane] = corr;
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < GQ; ++i) {
-      const float p = pb[w][t][i];
-      o[i][0] = fmaf(p, v0, o[i][0]);
-      o[i][1] = fmaf(p, v1, o[i][1]);
-    }
-  }
+      const float f = cr[i];
 #pragma unroll
-  for (int sft = LPR; sft < 64; sft <<= 1)
+      for (int e = 0; e < 8; ++e) o[i][e] *= f;
+    }
+#pragma unroll
+    for (int ii = 0; ii < NVL; ++ii) {
+      const int t = vr + ii * RPI;
+      if (t < nval) {
+        const uint4 v4 = vv[ii];
+        const float ve[8] = {bf2f(v4.x & 0xffffu), bf2f(v4.x >> 16), bf2f(v4.y & 0xffffu), bf2f(v4.y >> 16),
+                             bf2f(v4.z & 0xffffu), bf2f(v4.z >> 16), bf2f(v4.w & 0xffffu), bf2f(v4.w >> 16)};
+#pragma unroll
+        for (int i = 0; i < GQ; ++i) {
+          const float p = pb[t][i];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[i][e] = fmaf(p, ve[e], o[i][e]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // sum over the row groups of a V load (lanes with equal vc)
+#pragma unroll
+  for (int sft = CPR; sft < 64; sft <<= 1)
+#pragma unroll
+    for (int i = 0; i < GQ; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[i][e] += __shfl_xor(o[i][e], sft);
+  const int nw = a.nch;
+  if (vr == 0) {
 #pragma unroll
     for (int i = 0; i < GQ; ++i) {
-      o[i][0] += __shfl_xor(o[i][0], sft);
-      o[i][1] += __shfl_xor(o[i][1], sft);
-    }
-  if (pg == 0) {
+      if (i >= g) break;
+      float* out = a.part + ((((size_t)b * a.H + j * g + i) * nw) + c) * (HD + 2);
 #pragma unroll
-    for (int i = 0; i < GQ; ++i) {
-      ow[w][i][dl * DPL] = o[i][0];
-      ow[w][i][dl * DPL + 1] = o[i][1];
+      for (int e = 0; e < 8; ++e) out[vc * 8 + e] = o[i][e];
     }
   }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < g * HD; idx += 256) {
-    const int i = idx / HD;
-    const int dd = idx - i * HD;
-    float M = -INFINITY;
-    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, mw[ww][i]);
-    float L = 0.0f, O = 0.0f;
-    for (int ww = 0; ww < 4; ++ww) {
-      if (mw[ww][i] == -INFINITY) continue;
-      const float f = __expf(mw[ww][i] - M);
-      L = fmaf(lw[ww][i], f, L);
-      O = fmaf(ow[ww][i][dd], f, O);
-    }
-    float* out = a.part + ((((size_t)b * a.H + j * g + i) * a.nch) + c) * (HD + 2);
-    out[dd] = O;
-    if (dd == 0) {
-      out[HD] = M;
-      out[HD + 1] = L;
-    }
+  if (lane < g) {
+    float* out = a.part + ((((size_t)b * a.H + j * g + lane) * nw) + c) * (HD + 2);
+    out[HD] = m;
+    out[HD + 1] = l;
   }
 }
 
-__global__ void attn_combine_kernel(const AttnArgs a) {
+// Merges the (m, l, o) partials of one (sequence, q head) in partial order:
+// weights f_c = exp(m_c - max m) and L = sum f_c l_c in parallel, then
+// o = sum_c f_c o_c / L per head dimension.
+__global__ __launch_bounds__(128) void attn_combine_kernel(const AttnArgs a) {
+  constexpr int kMaxParts = 2048;
+  __shared__ float fw[kMaxParts];
+  __shared__ float red[2];
   const int h = blockIdx.x, b = blockIdx.y;
   const int hd = a.hd;
+  const int tid = threadIdx.x;
   const int ctx = a.lens[b] + 1;
-  const int nc = (ctx + kAttnChunk - 1) / kAttnChunk;
+  const int span = a.tpw * 64;
+  const int nc = min((ctx + span - 1) / span, kMaxParts);
   const float* base = a.part + (((size_t)b * a.H + h) * a.nch) * (hd + 2);
   float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, base[c * (hd + 2) + hd]);
-  for (int d = threadIdx.x; d < hd; d += blockDim.x) {
-    float L = 0.0f, O = 0.0f;
-    for (int c = 0; c < nc; ++c) {
-      const float* p = base + c * (hd + 2);
-      const float f = __expf(p[hd] - M);
-      L = fmaf(p[hd + 1], f, L);
-      O = fmaf(p[d], f, O);
+  for (int c = tid; c < nc; c += 128) M = fmaxf(M, base[(size_t)c * (hd + 2) + hd]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if ((tid & 63) == 0) red[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(red[0], red[1]);
+  float L = 0.0f;
+  for (int c = tid; c < nc; c += 128) {
+    const float* p = base + (size_t)c * (hd + 2);
+    const float f = __expf(p[hd] - M);
+    fw[c] = f;
+    L = fmaf(p[hd + 1], f, L);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
+  __syncthreads();
+  if ((tid & 63) == 0) red[tid >> 6] = L;
+  __syncthreads();
+  L = red[0] + red[1];
+  for (int d = tid; d < hd; d += 128) {
+    float O0 = 0.0f, O1 = 0.0f, O2 = 0.0f, O3 = 0.0f;
+    int c = 0;
+    for (; c + 4 <= nc; c += 4) {
+      O0 = fmaf(base[(size_t)c * (hd + 2) + d], fw[c], O0);
+      O1 = fmaf(base[(size_t)(c + 1) * (hd + 2) + d], fw[c + 1], O1);
+      O2 = fmaf(base[(size_t)(c + 2) * (hd + 2) + d], fw[c + 2], O2);
+      O3 = fmaf(base[(size_t)(c + 3) * (hd + 2) + d], fw[c + 3], O3);
     }
-    a.out[((size_t)b * a.H + h) * hd + d] = (uint16_t)f2bf(O / L);
+    for (; c < nc; ++c) O0 = fmaf(base[(size_t)c * (hd + 2) + d], fw[c], O0);
+    a.out[((size_t)b * a.H + h) * hd + d] = (uint16_t)f2bf(((O0 + O1) + (O2 + O3)) / L);
   }
 }
 
 template <int HD, int GQ>
 static void launch_attn_t(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((attn_kernel<HD, GQ>), dim3(a.nch, a.Hkv, a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_kernel<HD, GQ>), dim3(a.nch, a.Hkv, a.B), dim3(64), 0, s, a);
 }
 
 template <int HD>

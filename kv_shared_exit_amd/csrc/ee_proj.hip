@@ -29,6 +29,7 @@
 #include "ee_device.h"
 
 #include <algorithm>
+#include <stdexcept>
 
 namespace ee {
 
@@ -36,9 +37,47 @@ constexpr int kWaves = kProjThreads / 64;
 
 template <int EPI>
 struct Ep {
-  static constexpr int P = EPI == EPI_SWIGLU ? 2 : 1;                     // matrices per tile
-  static constexpr int R = EPI == EPI_SWIGLU ? 1 : 2;
+  static constexpr int P = EPI == EPI_SWIGLU ? 2 : 1;  // matrices per tile
+  static constexpr int R = EPI == EPI_SWIGLU ? 1 : 2;  // bf16 rows per wave tile
 };
+
+// Rows of a QKV tile: each tile pairs rotation rows c and c + hd/2 of one head
+// (RoPE rotates element i with element i + hd/2), so both halves of every pair
+// finish in the same wave.  A tile of 2*half rows covers c0 .. c0+half-1 and
+// their partners.
+__device__ __forceinline__ int qkv_row(const ProjArgs& a, int t, int m, int half) {
+  const int per_head = a.hd / (2 * half);
+  const int head = t / per_head;
+  const int c0 = (t - head * per_head) * half;
+  return head * a.hd + (m >= half ? a.hd / 2 : 0) + c0 + (m % half);
+}
+
+// QKV epilogue for row n of sequence seq: v is this row's value, u its RoPE
+// partner's (row n -/+ hd/2).  q and k are rounded to bf16, rotated in float32
+// and rounded again; k and v go to the shared cache slot of the position.
+__device__ __forceinline__ void qkv_out(const ProjArgs& a, int seq, int n, float v, float u) {
+  const int hd = a.hd, half = hd >> 1;
+  const int head = n / hd;
+  const int e = n - head * hd;
+  const int pos = a.lens[seq];
+  if (head < a.H + a.Hkv) {
+    const int i = e < half ? e : e - half;
+    const float c = a.cosT[(size_t)pos * half + i], sn = a.sinT[(size_t)pos * half + i];
+    const float x = bf2f(f2bf(v)), y = bf2f(f2bf(u));
+    const float r = e < half ? x * c - y * sn : x * c + y * sn;  // (x1 c - x2 s, x2 c + x1 s)
+    const uint16_t o = (uint16_t)f2bf(r);
+    if (head < a.H) {
+      a.qrot[((size_t)seq * a.H + head) * hd + e] = o;
+    } else {
+      const int kh = head - a.H;
+      a.Kl[(((size_t)seq * a.Hkv + kh) * a.S + pos) * hd + e] = o;
+      if (a.occ_l && kh == 0 && e == 0) a.occ_l[(size_t)seq * a.S + pos] += 1;
+    }
+  } else {
+    const int vh = head - a.H - a.Hkv;
+    a.Vl[(((size_t)seq * a.Hkv + vh) * a.S + pos) * hd + e] = (uint16_t)f2bf(v);
+  }
+}
 
 __device__ __forceinline__ const uint16_t* bf_row(const ProjArgs& a, int n) {
   int s = 0, start = 0;
@@ -46,10 +85,10 @@ __device__ __forceinline__ const uint16_t* bf_row(const ProjArgs& a, int n) {
     s = (n >= a.seg_end[1]) ? 2 : 1;
     start = a.seg_end[s - 1];
   }
-  return a.wb[s] + (size_t)(n - start) * a.K;
+  return a.wb[s] + (size_t)(n - start) * a.ldw + a.k0;
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 // Epilogue of one finished output value v (row n, sequence seq).
 template <int EPI>
@@ -58,37 +97,128 @@ __device__ __forceinline__ void store_out(const ProjArgs& a, int seq, int n, flo
     ((uint16_t*)a.y)[(size_t)seq * a.y_stride + n] = (uint16_t)f2bf(v);
   } else if constexpr (EPI == EPI_RESID) {
     float* yp = (float*)a.y + (size_t)seq * a.y_stride + n;
-    const float nv = *yp + v;
-    *yp = nv;
-    if (a.y2) a.y2[(size_t)seq * a.y2_stride + n] = (uint16_t)f2bf(nv);
+    *yp = *yp + v;
   }
 }
 
-// Stages input rows list[c0 .. c0+nb) into LDS (row stride K).
+// Stages input rows list[c0 .. c0+nb) into LDS (row stride K).  xmode 0 copies
+// columns k0 .. k0+K of x.  With xmode 1 the rows are the RMSNorm of the
+// residual, x = bf16(h / sqrt(mean(h^2) + eps) * g), computed here; with xmode
+// 2 they are bf16(h).
+//
+// A thread handles at most kItems items of 8 elements and issues the loads of
+// a round of them before using any, so each round costs one memory latency
+// (float32 rows take two rounds, and the RMSNorm reads them twice: once for
+// the statistics, once to normalise).  The squares are summed per item, then
+// per row by one wave in a fixed order, so every workgroup derives identical
+// statistics.
+constexpr int kItems = kXLdsElems / 8 / kProjThreads;
+constexpr int kRound = kItems / 2;
+
 __device__ __forceinline__ void stage_x(const ProjArgs& a, const int32_t* list, int c0, int nb, uint16_t* xs) {
-  const int k8 = a.K >> 3;
-  for (int i = threadIdx.x; i < nb * k8; i += kProjThreads) {
-    const int b = i / k8;
-    const int kk = i - b * k8;
-    *(uint4*)&xs[b * a.K + kk * 8] = *(const uint4*)(a.x + (size_t)list[c0 + b] * a.x_stride + kk * 8);
+  const int K = a.K;
+  const int k8 = K >> 3;
+  const int n = nb * k8;  // items; item i = (row b, column group kk) sits at xs[b*K + kk*8] = xs[i*8]
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));  // keeps the per-item index math here (not hoisted and held live)
+  __shared__ int seq[8];  // sequence id of each staged row
+  if (tid < 8) seq[tid] = list[c0 + min(tid, nb - 1)];
+  __syncthreads();
+  auto row_of = [&](int b) { return seq[b]; };
+  if (a.xmode == 0) {
+    uint4 v[kItems];
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+      const int i = min(tid + j * kProjThreads, n - 1);
+      const int b = i / k8;
+      v[j] = *(const uint4*)(a.x + (size_t)row_of(b) * a.x_stride + a.k0 + (i - b * k8) * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+      const int i = tid + j * kProjThreads;
+      if (i < n) *(uint4*)&xs[i * 8] = v[j];
+    }
+    return;
   }
+  // one round of float32 items: loads first, then f(j, i, lo, hi) per valid item
+  auto round = [&](int r, auto&& f) {
+    float4 v0[kRound], v1[kRound];
+#pragma unroll
+    for (int j = 0; j < kRound; ++j) {
+      const int i = min(tid + (r * kRound + j) * kProjThreads, n - 1);
+      const int b = i / k8;
+      const float* hr = a.h + (size_t)row_of(b) * K + (i - b * k8) * 8;
+      v0[j] = *(const float4*)hr;
+      v1[j] = *(const float4*)(hr + 4);
+    }
+#pragma unroll
+    for (int j = 0; j < kRound; ++j) {
+      const int i = tid + (r * kRound + j) * kProjThreads;
+      if (i < n) f(i, v0[j], v1[j]);
+    }
+  };
+  __shared__ float rs[8];
+  if (a.xmode == 1) {
+    float* ssi = (float*)xs;  // per-item sums of squares (xs is written after they are used)
+    for (int r = 0; r < 2; ++r)
+      round(r, [&](int i, const float4& lo, const float4& hi) {
+        float ss = lo.x * lo.x;
+        ss = fmaf(lo.y, lo.y, ss);
+        ss = fmaf(lo.z, lo.z, ss);
+        ss = fmaf(lo.w, lo.w, ss);
+        ss = fmaf(hi.x, hi.x, ss);
+        ss = fmaf(hi.y, hi.y, ss);
+        ss = fmaf(hi.z, hi.z, ss);
+        ss = fmaf(hi.w, hi.w, ss);
+        ssi[i] = ss;
+      });
+    __syncthreads();
+    const int lane = tid & 63, wave = tid >> 6;
+    if (wave < nb) {  // wave b sums row b: lane-strided, then a fixed butterfly
+      float t = 0.0f;
+      for (int k = lane; k < k8; k += 64) t += ssi[wave * k8 + k];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o);
+      if (lane == 0) rs[wave] = 1.0f / sqrtf(t / (float)K + a.eps);
+    }
+    __syncthreads();  // rs is ready and ssi is no longer read
+  }
+  for (int r = 0; r < 2; ++r)
+    round(r, [&](int i, const float4& lo, const float4& hi) {
+      const int b = i / k8;
+      const int kk = i - b * k8;
+      float f[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      if (a.xmode == 1) {
+        const float rr = rs[b];
+        const uint4 g = *(const uint4*)(a.gain + kk * 8);
+        const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = f[e] * rr * bf2f((gw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+      }
+      uint4 o;
+      o.x = f2bf(f[0]) | (f2bf(f[1]) << 16);
+      o.y = f2bf(f[2]) | (f2bf(f[3]) << 16);
+      o.z = f2bf(f[4]) | (f2bf(f[5]) << 16);
+      o.w = f2bf(f[6]) | (f2bf(f[7]) << 16);
+      *(uint4*)&xs[i * 8] = o;
+    });
 }
 
 // ---------------------------------------------------------------------------
 // bf16 rows (vector ALU, dot2)
 // ---------------------------------------------------------------------------
 // One 512-element step of a bf16 wave tile: acc[r*NB+b] += W_r . x_b over this
-// lane's 8 elements.  Inputs are read in groups of four to bound registers.
-template <int RP, int NB, bool XL>
-__device__ __forceinline__ void bf16_step(const uint4 (&wv)[RP], const uint16_t* xs, const uint16_t* xg,
-                                          const int (&xo)[NB], int k, float (&acc)[RP * NB]) {
+// lane's 8 elements.  Inputs are read from LDS in groups of four to bound
+// registers.
+template <int RP, int NB>
+__device__ __forceinline__ void bf16_step(const uint4 (&wv)[RP], const uint16_t* xs, const int (&xo)[NB], int k,
+                                          float (&acc)[RP * NB]) {
   constexpr int BG = NB < 4 ? NB : 4;
 #pragma unroll
   for (int b0 = 0; b0 < NB; b0 += BG) {
     uint4 xv[BG];
 #pragma unroll
-    for (int b = 0; b < BG; ++b)
-      xv[b] = XL ? *(const uint4*)(xs + xo[b0 + b] + k) : *(const uint4*)(xg + (size_t)xo[b0 + b] + k);
+    for (int b = 0; b < BG; ++b) xv[b] = *(const uint4*)(xs + xo[b0 + b] + k);
 #pragma unroll
     for (int b = 0; b < BG; ++b)
 #pragma unroll
@@ -103,14 +233,16 @@ __device__ __forceinline__ void bf16_step(const uint4 (&wv)[RP], const uint16_t*
   }
 }
 
-template <int EPI, bool XL, int NB>
+template <int EPI, int NB>
 __device__ __forceinline__ void bf16_pass(const ProjArgs& a, int nb, const int32_t* list, int c0,
                                           uint16_t* xs, float* red) {
   constexpr int P = Ep<EPI>::P;
   constexpr int R = Ep<EPI>::R;
   constexpr int RP = R * P;
   constexpr int V = RP * NB;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));  // lane-derived values are computed per pass, not held across passes
+  const int wave = threadIdx.x >> 6;
   const int wid = blockIdx.x * kWaves + wave;
   const int nwc = gridDim.x * kWaves;
   const int N = a.N, K = a.K;
@@ -120,12 +252,9 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, int nb, const int32
   const int bsel = idx - rr * NB;
   const bool lane_ok = lane < V && bsel < nb;
 
-  int xo[NB];  // element offset of each input row (LDS or global)
+  int xo[NB];  // LDS element offset of each input row
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    const int bb = b < nb ? b : nb - 1;
-    xo[b] = XL ? bb * K : list[c0 + bb] * a.x_stride;
-  }
+  for (int b = 0; b < NB; ++b) xo[b] = (b < nb ? b : nb - 1) * K;
 
   float lm = -INFINITY, ls = 0.0f;
   Top2 tp{-INFINITY, 0x7fffffff, -INFINITY};
@@ -139,9 +268,9 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, int nb, const int32
   auto set_rows = [&](int tt) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int n = min(tt * R + r, N - 1);
+      const int n = EPI == EPI_QKV ? qkv_row(a, tt, r, R / 2) : min(tt * R + r, N - 1);
       w[r] = bf_row(a, n) + lane * 8;
-      if constexpr (P == 2) w[R + r] = a.wb2 + (size_t)n * K + lane * 8;
+      if constexpr (P == 2) w[R + r] = a.wb2 + (size_t)n * a.ldw + a.k0 + lane * 8;
     }
   };
   if (t < ntiles && nfull > 0) {
@@ -149,7 +278,7 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, int nb, const int32
 #pragma unroll
     for (int r = 0; r < RP; ++r) cur[r] = ld_stream(w[r]);
   }
-  if constexpr (XL) stage_x(a, list, c0, nb, xs);
+  stage_x(a, list, c0, nb, xs);
   __syncthreads();
 
   for (; t < ntiles; t += nwc) {
@@ -171,29 +300,32 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, int nb, const int32
     for (; st + 2 < nfull; st += 2) {
 #pragma unroll
       for (int r = 0; r < RP; ++r) alt[r] = ld_stream(w[r] + (st + 1) * 512);
-      bf16_step<RP, NB, XL>(cur, xs, a.x, xo, lane * 8 + st * 512, acc);
+      bf16_step<RP, NB>(cur, xs, xo, lane * 8 + st * 512, acc);
 #pragma unroll
       for (int r = 0; r < RP; ++r) cur[r] = ld_stream(w[r] + (st + 2) * 512);
-      bf16_step<RP, NB, XL>(alt, xs, a.x, xo, lane * 8 + (st + 1) * 512, acc);
+      bf16_step<RP, NB>(alt, xs, xo, lane * 8 + (st + 1) * 512, acc);
     }
     if (st + 1 < nfull) {
 #pragma unroll
       for (int r = 0; r < RP; ++r) alt[r] = ld_stream(w[r] + (st + 1) * 512);
-      bf16_step<RP, NB, XL>(cur, xs, a.x, xo, lane * 8 + st * 512, acc);
-      bf16_step<RP, NB, XL>(alt, xs, a.x, xo, lane * 8 + (st + 1) * 512, acc);
+      bf16_step<RP, NB>(cur, xs, xo, lane * 8 + st * 512, acc);
+      bf16_step<RP, NB>(alt, xs, xo, lane * 8 + (st + 1) * 512, acc);
     } else if (st < nfull) {
-      bf16_step<RP, NB, XL>(cur, xs, a.x, xo, lane * 8 + st * 512, acc);
+      bf16_step<RP, NB>(cur, xs, xo, lane * 8 + st * 512, acc);
     }
     if (kt < K) {  // ragged tail (K not a multiple of 512)
       uint4 tw[RP];
 #pragma unroll
       for (int r = 0; r < RP; ++r) tw[r] = ld_stream(w[r] + nfull * 512);
-      bf16_step<RP, NB, XL>(tw, xs, a.x, xo, kt, acc);
+      bf16_step<RP, NB>(tw, xs, xo, kt, acc);
     }
     XRed<V, 0>::run(acc, lane);
     const float v = acc[0];
-    const int n = n0 + (rr % R);
-    if constexpr (EPI == EPI_SWIGLU) {
+    const int n = EPI == EPI_QKV ? qkv_row(a, t, rr, R / 2) : n0 + (rr % R);
+    if constexpr (EPI == EPI_QKV) {
+      const float u = __shfl_xor(v, 1);  // the RoPE partner row sits in the partner lane
+      if (lane_ok) qkv_out(a, list[c0 + bsel], n, v, u);
+    } else if constexpr (EPI == EPI_SWIGLU) {
       const float u = __shfl_xor(v, 1);  // the up row sits in the partner lane
       if (lane_ok && (lane & 1) == 0 && n < N)
         ((uint16_t*)a.y)[(size_t)list[c0 + bsel] * a.y_stride + n] = (uint16_t)f2bf(silu_mul(v, u));
@@ -258,13 +390,21 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, int nb, const int32
 // ---------------------------------------------------------------------------
 // int4 rows (MFMA)
 //
-// Codes of a row: K/8 dwords, dword t holding elements [8t, 8t+8) with element
-// 8t+2i in bits [4i, 4i+4) and 8t+2i+1 in bits [16+4i, 16+4i+4), value q + 8.
-// Within each full 128-element block the four dwords a lane needs for the
-// block's four MFMA steps are adjacent: logical dword 16u + 4j + c (step j,
-// lane quarter c) is stored at 16u + 4c + j.  A tail (K mod 128 > 0) keeps
+// Codes of a row: ldw/8 dwords, dword t holding elements [8t, 8t+8) with
+// element 8t+2i in bits [4i, 4i+4) and 8t+2i+1 in bits [16+4i, 16+4i+4), value
+// q + 8.  Within each full 128-element block the four dwords a lane needs for
+// the block's four MFMA steps are adjacent: logical dword 16u + 4j + c (step j,
+// lane quarter c) is stored at 16u + 4c + j.  A tail (ldw mod 128 > 0) keeps
 // natural order.  Rows are padded to a multiple of 16 with zero codes.
-// Scales: [N16/16][K/G][16] bf16 (16 rows of one tile and one group adjacent).
+// Scales: [N16/16][ldw/G][16] bf16 (16 rows of one tile and one group adjacent).
+//
+// Work split: a 16-row tile is shared by WPT waves (1, 2, 4 or 8, chosen so
+// each wave owns about D blocks of 128 columns); a workgroup works on 8/WPT
+// tiles at a time.  Each wave keeps D blocks of codes and their scales in
+// flight in a register ring, refilled as blocks are consumed; the refills run
+// on into the workgroup's next tiles, so one tile's reduction overlaps the
+// next tile's loads.  A ring slot past the wave's work is pointed at a small
+// always-valid address (the scale array's start) and its compute is skipped.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bf16x8_t unpack8(uint32_t w) {
   uint4 o;
@@ -279,14 +419,19 @@ __device__ __forceinline__ uint32_t pick(const uint4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
 
-// tot += s_row * (C - C136) for the 4 rows of this lane
-__device__ __forceinline__ void i4_group_scale(const uint16_t* stile, int g, int q, const f32x4_t& cg,
-                                               const f32x4_t& c136, f32x4_t& tot) {
-  const uint2 sv = *(const uint2*)(stile + g * 16 + 4 * q);
-  tot[0] = fmaf(bf2f(sv.x & 0xffffu), cg[0] - c136[0], tot[0]);
-  tot[1] = fmaf(bf2f(sv.x >> 16), cg[1] - c136[1], tot[1]);
-  tot[2] = fmaf(bf2f(sv.y & 0xffffu), cg[2] - c136[2], tot[2]);
-  tot[3] = fmaf(bf2f(sv.y >> 16), cg[3] - c136[3], tot[3]);
+// tot += (sl * s_row) * (C - C136) for the 4 rows of this lane (sv: their 4
+// scales; sl is 1, or 0 for a slot without work)
+__device__ __forceinline__ void i4_group_scale(const uint2& sv, float sl, const f32x4_t& cg, const f32x4_t& c136,
+                                               f32x4_t& tot) {
+  tot[0] = fmaf(sl * bf2f(sv.x & 0xffffu), cg[0] - c136[0], tot[0]);
+  tot[1] = fmaf(sl * bf2f(sv.x >> 16), cg[1] - c136[1], tot[1]);
+  tot[2] = fmaf(sl * bf2f(sv.y & 0xffffu), cg[2] - c136[2], tot[2]);
+  tot[3] = fmaf(sl * bf2f(sv.y >> 16), cg[3] - c136[3], tot[3]);
+}
+
+__device__ __forceinline__ bf16x8_t k136_operand() {
+  const uint4 k136 = make_uint4(0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u);  // bf16 136.0
+  return __builtin_bit_cast(bf16x8_t, k136);
 }
 
 template <int P>
@@ -299,102 +444,168 @@ __device__ __forceinline__ void i4_step(const uint32_t (&word)[P], const uint4& 
   for (int p = 0; p < P; ++p) cg[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack8(word[p]), b8, cg[p], 0, 0, 0);
 }
 
-template <int EPI, bool XL>
+// Ring depth (blocks of 128 columns in flight per wave) for P matrices and NG
+// scale groups per block: about 4 KB of codes per wave, within 128 VGPRs.
+template <int P, int NG>
+struct I4Ring {
+  static constexpr int D = (P == 2 || NG == 4) ? 2 : 4;
+};
+
+// Waves per 16-row tile for a launch of K columns.
+__host__ __device__ inline int i4_wpt(int K, int D) {
+  const int nfull = K >> 7;
+  int w = 1;
+  while (w < kWaves && nfull > w * D) w *= 2;
+  return w;
+}
+
+template <int EPI, int NG>
 __device__ __forceinline__ void i4_pass(const ProjArgs& a, int nb, const int32_t* list, int c0,
                                         uint16_t* xs, float* red) {
   constexpr int P = Ep<EPI>::P;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int D = I4Ring<P, NG>::D;
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));  // lane-derived values are computed per pass, not held across passes
+  const int wave = threadIdx.x >> 6;
   const int m = lane & 15, q = lane >> 4;
   const int N = a.N, K = a.K, G = a.G;
-  const int ntiles = (N + 15) / 16;
-  const int ngr = K / G;
-  const int mpg = G / 32;             // MFMA steps per group
+  const int ntiles = (N + 15) >> 4;
+  const int ldc = a.ldw >> 3;           // dwords per code row
+  const int ngr = a.ldw / G;            // scale groups per row of the whole matrix
+  const int gk0 = a.k0 / G;             // first group of this launch's columns
   const int nfull = K >> 7;
-  const int ntail = (K & 127) >> 5;   // MFMA steps in the tail
-  const int b0 = wave * nfull / kWaves, b1 = (wave + 1) * nfull / kWaves;
+  const int ntail = (K & 127) >> 5;     // MFMA steps in the tail
+  const int mpg = G >> 5;               // MFMA steps per group
+  const int wpt = i4_wpt(K, D);
+  const int tpi = kWaves / wpt;         // tiles per workgroup iteration
+  const int ws = wave % wpt;            // this wave's K slice of its tile
+  const int b0 = ws * nfull / wpt;
+  const int nbw = (ws + 1) * nfull / wpt - b0;
+  const int nbp = ((nfull + wpt - 1) / wpt + D - 1) / D * D;  // ring rounds per tile, same for all waves
+  const int nit = (ntiles + tpi - 1) / tpi;                    // workgroup iterations in the grid
+  const int ntl = (int)blockIdx.x < nit ? (nit - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
   const bool bok = m < nb;
-  const bool tail_here = wave == kWaves - 1 && ntail > 0;
-  const uint16_t* xrow = XL ? xs + (bok ? m : 0) * K : a.x + (size_t)list[c0 + (bok ? m : 0)] * a.x_stride;
+  const bool tail_here = ws == wpt - 1 && ntail > 0;
+  const uint16_t* xrow = xs + (bok ? m : 0) * K;
 
-  // request the first tile's first codes before the inputs are staged
-  int t = blockIdx.x;
-  uint4 cw0[P];
-  if (t < ntiles && b0 < b1) {
-#pragma unroll
-    for (int p = 0; p < P; ++p)
-      cw0[p] = ld_stream((p == 0 ? a.q4 : a.q4b) + (size_t)(t * 16 + m) * (K >> 3) + b0 * 16 + q * 4);
-  }
-  if constexpr (XL) stage_x(a, list, c0, nb, xs);
-  __syncthreads();
+  // weight row of MFMA A row mm of tile tt (the QKV epilogue pairs RoPE rows)
+  auto arow = [&](int tt, int mm) { return EPI == EPI_QKV ? qkv_row(a, tt, mm, 8) : tt * 16 + mm; };
+  auto tile_of = [&](int j) { return ((int)blockIdx.x + j * (int)gridDim.x) * tpi + wave / wpt; };
+  // where a tile's loads start: code dword offset of this lane's first block
+  // and scale offset of this lane's rows at the first group (-1: no tile)
+  struct TileAt {
+    int code, scale;
+  };
+  auto tile_at = [&](int j) {
+    const int t = tile_of(j);
+    if (j >= ntl || t >= ntiles) return TileAt{-1, -1};
+    const int r0 = arow(t, 4 * q);
+    return TileAt{arow(t, m) * ldc + (a.k0 >> 3) + b0 * 16 + q * 4, ((r0 >> 4) * ngr + gk0 + b0 * NG) * 16 + (r0 & 15)};
+  };
 
-  for (; t < ntiles; t += gridDim.x) {
-    const uint32_t* crow[P];
-    const uint16_t* stile[P];
+  uint4 cw[P][D];
+  uint2 sc[P][D][NG];
+  // issue the loads of block kk of the wave's slice of tile `at` into ring slot i
+  auto issue = [&](const TileAt& at, int kk, int i) {
+    const bool real = at.code >= 0 && kk < nbw;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      crow[p] = (p == 0 ? a.q4 : a.q4b) + (size_t)(t * 16 + m) * (K >> 3);
-      stile[p] = (p == 0 ? a.s4 : a.s4b) + (size_t)t * ngr * 16;
+      const uint32_t* cb = p == 0 ? a.q4 : a.q4b;
+      const uint16_t* sb = p == 0 ? a.s4 : a.s4b;
+      const uint32_t* cp = real ? cb + at.code + kk * 16 : (const uint32_t*)a.s4;
+      cw[p][i] = ld_stream(cp);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) sc[p][i][g] = *(const uint2*)(real ? sb + at.scale + (kk * NG + g) * 16 : a.s4);
     }
+  };
+  TileAt at_cur = tile_at(0);
+  if (nfull > 0) {
+#pragma unroll
+    for (int i = 0; i < D; ++i) issue(at_cur, i, i);
+  }
+  stage_x(a, list, c0, nb, xs);
+  __syncthreads();
+
+  for (int j = 0; j < ntl; ++j) {
+    const int t = tile_of(j);
+    const int r0 = arow(t, 4 * q);
+    const TileAt at_nxt = tile_at(j + 1);
     f32x4_t tot[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) tot[p] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int u = b0; u < b1; ++u) {
-      uint4 cw[P];
-      if (u == b0 && t == (int)blockIdx.x) {
+    for (int kk = 0; kk < nbp; kk += D) {
 #pragma unroll
-        for (int p = 0; p < P; ++p) cw[p] = cw0[p];
-      } else {
+      for (int i = 0; i < D; ++i) {
+        // straight-line ring body (a branch around it would make the
+        // compiler wait for every load in flight): a slot past this wave's
+        // blocks computes on in-bounds data with its scales multiplied by 0
+        const bool live = kk + i < nbw && t < ntiles;
+        const float sl = live ? 1.0f : 0.0f;
+        const int u = min(b0 + kk + i, max(nfull - 1, 0));
+        constexpr int MPG = 4 / NG;  // MFMA steps per scale group
+        // one matrix at a time (fewer live operands); the 136 * sum(x)
+        // correction of each group is computed with the first
+        f32x4_t c136g[NG];
 #pragma unroll
-        for (int p = 0; p < P; ++p) cw[p] = ld_stream(crow[p] + u * 16 + q * 4);
+        for (int p = 0; p < P; ++p) {
+          f32x4_t cg = {0.0f, 0.0f, 0.0f, 0.0f};
+          f32x4_t c136 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            uint4 bv = *(const uint4*)(xrow + u * 128 + 32 * st + 8 * q);
+            if (!bok) bv = make_uint4(0, 0, 0, 0);
+            const bf16x8_t b8 = __builtin_bit_cast(bf16x8_t, bv);
+            if (p == 0) c136 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k136_operand(), b8, c136, 0, 0, 0);
+            cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack8(pick(cw[p][i], st)), b8, cg, 0, 0, 0);
+            if (st % MPG == MPG - 1) {
+              if (p == 0) {
+                c136g[st / MPG] = c136;
+                c136 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+              }
+              i4_group_scale(sc[p][i][st / MPG], sl, cg, c136g[st / MPG], tot[p]);
+              cg = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+          }
+        }
+        // refill with the block D ahead, in this tile or the next (a select,
+        // not a branch, so the loads stay unconditional)
+        const bool here = kk + i + D < nbp;
+        issue(here ? at_cur : at_nxt, here ? kk + i + D : kk + i + D - nbp, i);
       }
+    }
+    if (tail_here && t < ntiles) {
       f32x4_t cg[P];
       f32x4_t c136 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int p = 0; p < P; ++p) cg[p] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ka = u * 128 + 32 * j;
+      for (int st = 0; st < ntail; ++st) {
+        const int ka = nfull * 128 + 32 * st;
         uint4 bv = *(const uint4*)(xrow + ka + 8 * q);
         if (!bok) bv = make_uint4(0, 0, 0, 0);
         uint32_t word[P];
 #pragma unroll
-        for (int p = 0; p < P; ++p) word[p] = pick(cw[p], j);
+        for (int p = 0; p < P; ++p) {
+          const uint32_t* cb = p == 0 ? a.q4 : a.q4b;
+          word[p] = cb[(size_t)arow(t, m) * ldc + ((a.k0 + ka) >> 3) + q];
+        }
         i4_step<P>(word, bv, cg, c136);
-        if (j % mpg == mpg - 1) {
+        if (st % mpg == mpg - 1) {
 #pragma unroll
           for (int p = 0; p < P; ++p) {
-            i4_group_scale(stile[p], ka / G, q, cg[p], c136, tot[p]);
+            const uint16_t* sb = p == 0 ? a.s4 : a.s4b;
+            const uint2 sv = *(const uint2*)(sb + ((size_t)(r0 >> 4) * ngr + gk0 + ka / G) * 16 + (r0 & 15));
+            i4_group_scale(sv, 1.0f, cg[p], c136, tot[p]);
             cg[p] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
           }
           c136 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
         }
       }
     }
-    if (tail_here) {
-      f32x4_t cg[P];
-      f32x4_t c136 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int p = 0; p < P; ++p) cg[p] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-      for (int j = 0; j < ntail; ++j) {
-        const int ka = nfull * 128 + 32 * j;
-        uint4 bv = *(const uint4*)(xrow + ka + 8 * q);
-        if (!bok) bv = make_uint4(0, 0, 0, 0);
-        uint32_t word[P];
-#pragma unroll
-        for (int p = 0; p < P; ++p) word[p] = crow[p][nfull * 16 + 4 * j + q];
-        i4_step<P>(word, bv, cg, c136);
-        if (j % mpg == mpg - 1) {
-#pragma unroll
-          for (int p = 0; p < P; ++p) {
-            i4_group_scale(stile[p], ka / G, q, cg[p], c136, tot[p]);
-            cg[p] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-          }
-          c136 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        }
-      }
-    }
-    // sum the waves' K slices in wave order
+    at_cur = at_nxt;
+    // sum the K slices of each tile in slice order; wave (tile index) tt of
+    // the iteration finishes tile tt
     float vals[P][4];
+    const bool fin = wave < tpi;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       float* rw = red + (wave * 64 + lane) * 4;
@@ -403,22 +614,36 @@ __device__ __forceinline__ void i4_pass(const ProjArgs& a, int nb, const int32_t
       rw[2] = tot[p][2];
       rw[3] = tot[p][3];
       __syncthreads();
-      if (wave == 0) {
+      if (fin) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float s = 0.0f;
-          for (int ww = 0; ww < kWaves; ++ww) s += red[(ww * 64 + lane) * 4 + i];
+          for (int ww = 0; ww < wpt; ++ww) s += red[((wave * wpt + ww) * 64 + lane) * 4 + i];
           vals[p][i] = s;
         }
       }
       __syncthreads();
     }
-    if (wave != 0 || !bok) continue;
-    // lane (q, m) holds rows t*16 + 4q + i of batch column m
+    if (!fin) continue;
+    const int tf = ((int)blockIdx.x + j * (int)gridDim.x) * tpi + wave;  // the tile this wave finishes
+    if (tf >= ntiles) continue;
+    if constexpr (EPI == EPI_QKV) {
+      // lane (q, m) holds rows arow(tf, 4q + i); the RoPE partners sit in lane ^ 32
+      float u[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) u[i] = __shfl_xor(vals[0][i], 32);
+      if (!bok) continue;
+      const int seq = list[c0 + m];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qkv_out(a, seq, arow(tf, 4 * q + i), vals[0][i], u[i]);
+      continue;
+    }
+    if (!bok) continue;
+    // lane (q, m) holds rows tf*16 + 4q + i of batch column m
     const int seq = list[c0 + m];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int n = t * 16 + 4 * q + i;
+      const int n = tf * 16 + 4 * q + i;
       if (n >= N) continue;
       if constexpr (EPI == EPI_SWIGLU)
         ((uint16_t*)a.y)[(size_t)seq * a.y_stride + n] = (uint16_t)f2bf(silu_mul(vals[0][i], vals[P - 1][i]));
@@ -428,13 +653,13 @@ __device__ __forceinline__ void i4_pass(const ProjArgs& a, int nb, const int32_t
   }
 }
 
-template <int EPI, bool XL>
+template <int EPI, int NG>
 __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[XL ? kXLdsElems : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kXLdsElems];
   __shared__ __attribute__((aligned(16))) float red[kWaves * 64 * 4];
   for (int fmt = 0; fmt < 2; ++fmt) {
-    if constexpr (EPI == EPI_LSE || EPI == EPI_ARGMAX) {
-      if (fmt == 1) break;
+    if constexpr (EPI == EPI_LSE || EPI == EPI_ARGMAX || EPI == EPI_BF16) {
+      if (fmt == 1) break;  // these run on backbone rows only
     }
     const int32_t* cntp = fmt ? a.cnt_i4 : a.cnt_bf;
     const int n = cntp ? min(max(*cntp, 0), kMaxBatch) : 0;
@@ -444,37 +669,72 @@ __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a)
       __syncthreads();  // the previous pass is done with xs and red
       if (fmt == 0) {
         if (nb == 1)
-          bf16_pass<EPI, XL, 1>(a, nb, list, c0, xs, red);
+          bf16_pass<EPI, 1>(a, nb, list, c0, xs, red);
         else if (nb == 2)
-          bf16_pass<EPI, XL, 2>(a, nb, list, c0, xs, red);
+          bf16_pass<EPI, 2>(a, nb, list, c0, xs, red);
         else if (nb <= 4)
-          bf16_pass<EPI, XL, 4>(a, nb, list, c0, xs, red);
+          bf16_pass<EPI, 4>(a, nb, list, c0, xs, red);
         else
-          bf16_pass<EPI, XL, 8>(a, nb, list, c0, xs, red);
+          bf16_pass<EPI, 8>(a, nb, list, c0, xs, red);
       } else {
-        if constexpr (EPI != EPI_LSE && EPI != EPI_ARGMAX) i4_pass<EPI, XL>(a, nb, list, c0, xs, red);
+        if constexpr (EPI == EPI_RESID || EPI == EPI_SWIGLU || EPI == EPI_QKV) i4_pass<EPI, NG>(a, nb, list, c0, xs, red);
       }
     }
   }
 }
 
+bool proj_fits(int K, int batch) { return (long long)std::min(8, batch) * K <= kXLdsElems; }
+
 template <int EPI>
-static void launch_epi(const ProjArgs& a, int g, hipStream_t s) {
-  if ((long long)8 * a.K <= kXLdsElems)
-    hipLaunchKernelGGL((proj_kernel<EPI, true>), dim3(g), dim3(kProjThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((proj_kernel<EPI, false>), dim3(g), dim3(kProjThreads), 0, s, a);
+static void launch_ng(const ProjArgs& a, int g, hipStream_t s) {
+  if constexpr (EPI == EPI_RESID || EPI == EPI_SWIGLU || EPI == EPI_QKV) {
+    if (a.G == 32) {
+      hipLaunchKernelGGL((proj_kernel<EPI, 4>), dim3(g), dim3(kProjThreads), 0, s, a);
+      return;
+    }
+    if (a.G == 64) {
+      hipLaunchKernelGGL((proj_kernel<EPI, 2>), dim3(g), dim3(kProjThreads), 0, s, a);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((proj_kernel<EPI, 1>), dim3(g), dim3(kProjThreads), 0, s, a);
 }
 
-void launch_proj(int epi, const ProjArgs& a, int nwg, hipStream_t s) {
+static void launch_one(int epi, const ProjArgs& a, int g, hipStream_t s) {
+  switch (epi) {
+    case EPI_BF16: launch_ng<EPI_BF16>(a, g, s); break;
+    case EPI_RESID: launch_ng<EPI_RESID>(a, g, s); break;
+    case EPI_SWIGLU: launch_ng<EPI_SWIGLU>(a, g, s); break;
+    case EPI_LSE: launch_ng<EPI_LSE>(a, g, s); break;
+    case EPI_ARGMAX: launch_ng<EPI_ARGMAX>(a, g, s); break;
+    case EPI_QKV: launch_ng<EPI_QKV>(a, g, s); break;
+  }
+}
+
+void launch_proj(int epi, const ProjArgs& a0, int nwg, int batch, hipStream_t s) {
+  ProjArgs a = a0;
+  if (a.ldw == 0) a.ldw = a.K;
   // the vocabulary epilogues write one partial per workgroup (kNwgMax of them)
   const int g = std::max(1, std::min(nwg, kNwgMax));
-  switch (epi) {
-    case EPI_BF16: launch_epi<EPI_BF16>(a, g, s); break;
-    case EPI_RESID: launch_epi<EPI_RESID>(a, g, s); break;
-    case EPI_SWIGLU: launch_epi<EPI_SWIGLU>(a, g, s); break;
-    case EPI_LSE: launch_epi<EPI_LSE>(a, g, s); break;
-    case EPI_ARGMAX: launch_epi<EPI_ARGMAX>(a, g, s); break;
+  const int rows = std::min(8, batch);
+  if (proj_fits(a.K, batch)) {
+    launch_one(epi, a, g, s);
+    return;
+  }
+  // y += W x over column ranges of W whose inputs fit the stage: the ranges
+  // are whole 128-column blocks of near-equal size (group boundaries too)
+  if (epi != EPI_RESID || a.xmode != 0 || a.k0 != 0) throw std::logic_error("projection input too wide");
+  const int cmax = (kXLdsElems / rows) / 128 * 128;
+  const int nch = (a.K + cmax - 1) / cmax;
+  const int blocks = (a.K + 127) / 128;
+  int k0 = 0;
+  for (int c = 0; c < nch; ++c) {
+    const int kb = (c + 1) * blocks / nch * 128;
+    ProjArgs b = a;
+    b.k0 = k0;
+    b.K = std::min(a.K, kb) - k0;
+    launch_one(epi, b, g, s);
+    k0 += b.K;
   }
 }
 

@@ -147,3 +147,33 @@ def test_two_runs_are_bitwise_identical(api):
         np.testing.assert_array_equal(ta, tb)
         np.testing.assert_array_equal(ea, eb)
         np.testing.assert_array_equal(la, lb)
+
+
+def test_rollback_then_replay_is_identical(api):
+    from kv_shared_exit_amd import _binding as B
+    sh = ODD
+    w, m = _model(api, sh, alpha=np.full(sh.n_layers - 1, 3000.0), max_batch=3, max_positions=16)
+    c = api.KVCache(m, 3, 16, track=True)
+    try:
+        api.prefill(m, c, np.array([[5, 6, 7], [8, 9, 10], [11, 12, 13]], np.int32))
+        toks = np.array([1, 2, 3], np.int32)
+        d1 = {"logits": None}
+        t1, e1 = api.decode_step(m, c, 3, tokens=toks, debug=d1)
+        k1, v1 = c.read(2, 1, 0, 4)
+        c.rollback(-1, 1)
+        assert list(c.lengths()) == [3, 3, 3]
+        assert np.all(c.occupancy()[:, :, 3] == 0)
+        d2 = {"logits": None}
+        t2, e2 = api.decode_step(m, c, 3, tokens=toks, debug=d2)
+        np.testing.assert_array_equal(t1, t2)
+        np.testing.assert_array_equal(e1, e2)
+        np.testing.assert_array_equal(d1["logits"], d2["logits"])
+        k2, v2 = c.read(2, 1, 0, 4)
+        np.testing.assert_array_equal(k1, k2)
+        assert np.all(c.occupancy()[:, :, :4] == 1)
+        with pytest.raises(B.EEError) as e:
+            c.rollback(0, 5)
+        assert e.value.status == B.EE_ERR_INVALID_ARG
+    finally:
+        c.close()
+        m.close()

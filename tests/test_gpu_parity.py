@@ -85,3 +85,13 @@ def test_unquantised_exit_copies(gpu, name):
     from parity import run_parity
     sh, w = _weights(name, 1.6, 6, 4)
     run_parity(sh, w, 3, 6, 4, 0.75, exit_mode="bf16", label=f"{name}-bf16")
+
+
+def test_long_context_several_tiles_per_wave(gpu):
+    """8 sequences x 8 kv heads x 2100 positions: each attention wave owns several
+    64-position tiles (online softmax across tiles), plus a ragged last tile."""
+    from parity import run_parity
+    sh = SHAPES["hd64"]
+    w = synth.make_weights(sh, 12)
+    run_parity(sh, w, 8, 2100, 2, 0.75, forced_fn=lambda s: np.array([1, 2, 2, 1, 2, 2, 1, 2]),
+               label="hd64-long", check_kv=False)
