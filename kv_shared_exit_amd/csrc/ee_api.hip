@@ -69,7 +69,11 @@ struct ee_model {
   float* d_gamma = nullptr;
   float *d_cos = nullptr, *d_sin = nullptr;
   // workspaces
-  float* h = nullptr;
+  float* h = nullptr;      // float32 residual [b][d]
+  float* parts = nullptr;  // partial sums of the column ranges of O / down [range][b][d]
+  int nkc_max = 1;
+  uint16_t *xn = nullptr;  // bf16 RMSNorm of the residual, the next projection's input [b][d]
+  uint16_t *hb = nullptr;  // bf16(h), the exit head's input [b][d]
   uint16_t *qrot = nullptr, *attn_o = nullptr;
   uint16_t *act = nullptr, *z = nullptr;
   float* head_part = nullptr;
@@ -244,15 +248,6 @@ void attn_split(int S, int B, int Hkv, int* tpw, int* nch) {
   *nch = (tiles + t - 1) / t;
 }
 
-// Input of a projection that reads bf16(rmsnorm(h) * g): the projection
-// normalises the residual rows while staging them.
-void norm_input(ee_model* m, ProjArgs& a, const void* gain) {
-  a.eps = m->cfg.rms_eps;
-  a.xmode = 1;
-  a.h = m->h;
-  a.gain = (const uint16_t*)gain;
-}
-
 struct Debug {
   bool hidden = false, logits = false;
 };
@@ -267,7 +262,9 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
   StepState* st = m->st;
   const bool int4 = cf.exit_mode == EE_EXIT_INT4;
 
+  const size_t pstride = (size_t)kMaxBatch * d;  // elements between partial-sum ranges
   launch_init(st, prompt, P, t, B, L, m->tok_emb, d, cf.vocab, m->h, m->p_rec, s);
+  launch_finish(m->h, nullptr, 0, pstride, B, d, (const uint16_t*)m->lw[0].attn_norm, cf.rms_eps, m->xn, nullptr, s);
   if (dbg.hidden)
     HIPCHK(hipMemcpy2DAsync(m->dbg_hidden, (size_t)(L + 1) * d * 4, m->h, (size_t)d * 4,
                             (size_t)d * 4, B, hipMemcpyDeviceToDevice, s));
@@ -300,7 +297,8 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       }
       a.list_bf = list_bf;
       a.cnt_bf = cnt_bf;
-      norm_input(m, a, w.attn_norm);
+      a.x = m->xn;  // bf16(rmsnorm(h) * attn_norm)
+      a.x_stride = d;
       // epilogue: RoPE on q and k, k and v into this position's shared cache slot
       a.cosT = m->d_cos;
       a.sinT = m->d_sin;
@@ -348,9 +346,11 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       a.cnt_bf = cnt_bf;
       a.x = m->attn_o;
       a.x_stride = qd;
-      a.y = m->h;
+      a.y = m->parts;
       a.y_stride = d;
-      launch_proj(EPI_RESID, a, kNwg, B, s);
+      a.y_cstride = (int)pstride;
+      const int nkc = launch_proj(EPI_PART, a, kNwg, B, s);
+      launch_finish(m->h, m->parts, nkc, pstride, B, d, (const uint16_t*)w.ffn_norm, cf.rms_eps, m->xn, nullptr, s);
     }
     {
       ProjArgs a = base_args(m);
@@ -368,7 +368,8 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       }
       a.list_bf = list_bf;
       a.cnt_bf = cnt_bf;
-      norm_input(m, a, w.ffn_norm);
+      a.x = m->xn;  // bf16(rmsnorm(h) * ffn_norm)
+      a.x_stride = d;
       a.y = m->act;
       a.y_stride = F;
       launch_proj(EPI_SWIGLU, a, kNwg, B, s);
@@ -389,9 +390,15 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       a.cnt_bf = cnt_bf;
       a.x = m->act;
       a.x_stride = F;
-      a.y = m->h;
+      a.y = m->parts;
       a.y_stride = d;
-      launch_proj(EPI_RESID, a, kNwg, B, s);
+      a.y_cstride = (int)pstride;
+      const int nkc = launch_proj(EPI_PART, a, kNwg, B, s);
+      // the next projection's input: the next layer's attention norm, or the
+      // final norm before the LM head; bf16(h) for this layer's exit head
+      const void* g_next = l < L ? m->lw[l].attn_norm : (const void*)m->final_norm;
+      launch_finish(m->h, m->parts, nkc, pstride, B, d, (const uint16_t*)g_next, cf.rms_eps, m->xn,
+                    head_here ? m->hb : nullptr, s);
     }
     if (head_here) {
       {
@@ -401,8 +408,8 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
         set_seg1(a, w.head_T, d);
         a.list_bf = st->act;
         a.cnt_bf = &st->n_act;
-        a.xmode = 2;  // bf16(h), staged from the residual
-        a.h = m->h;
+        a.x = m->hb;  // bf16(h)
+        a.x_stride = d;
         a.y = m->z;
         a.y_stride = d;
         launch_proj(EPI_BF16, a, kNwg, B, s);
@@ -435,7 +442,8 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
     set_seg1(a, m->lm_head, cf.vocab);
     a.list_bf = st->all;
     a.cnt_bf = &st->n_all;
-    norm_input(m, a, m->final_norm);
+    a.x = m->xn;  // bf16(rmsnorm(h) * final_norm)
+    a.x_stride = d;
     a.part = m->head_part;
     a.logits = dbg.logits ? m->dbg_logits : nullptr;
     a.logits_stride = cf.vocab;
@@ -557,6 +565,11 @@ ee_status ee_create_model(const ee_model_config* cfg, const ee_weights* w, const
       HIPCHK(hipMemcpy(m->d_sin, sn.data(), sn.size() * 4, hipMemcpyHostToDevice));
       const int Bm = kMaxBatch;
       m->h = m->alloc<float>((size_t)Bm * d);
+      const int rows = std::min(8, c.max_batch);
+      m->nkc_max = std::max(proj_ranges(qd, d, kNwg, rows, nullptr), proj_ranges(F, d, kNwg, rows, nullptr));
+      m->parts = m->alloc<float>((size_t)m->nkc_max * Bm * d);
+      m->xn = m->alloc<uint16_t>((size_t)Bm * d);
+      m->hb = m->alloc<uint16_t>((size_t)Bm * d);
       m->qrot = m->alloc<uint16_t>((size_t)Bm * qd);
       m->attn_o = m->alloc<uint16_t>((size_t)Bm * qd);
       m->act = m->alloc<uint16_t>((size_t)Bm * F);

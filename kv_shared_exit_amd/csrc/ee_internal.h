@@ -11,7 +11,11 @@ constexpr int kProjThreads = 512;  // 8 waves per projection workgroup
 constexpr int kXLdsElems = 32768;  // bf16 elements of the staged GEMV input (64 KB)
 constexpr int kNwgMax = 512;       // projection grid cap (size of the per-workgroup partial buffers)
 
-enum Epi { EPI_BF16 = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_LSE = 3, EPI_ARGMAX = 4, EPI_QKV = 5 };
+// Projection epilogues: bf16 output; float32 partial sums of a column range
+// (summed into the residual by the finish kernel); SwiGLU; the exit head's
+// (max, sum exp) per workgroup; the LM head's top-2 per workgroup; RoPE and the
+// shared-slot K/V write.
+enum Epi { EPI_BF16 = 0, EPI_PART = 1, EPI_SWIGLU = 2, EPI_LSE = 3, EPI_ARGMAX = 4, EPI_QKV = 5 };
 
 // Device-resident state of one step.  Every value that changes from step to
 // step lives here, so a captured graph replays unchanged.
@@ -29,25 +33,22 @@ struct StepState {
 };
 
 struct ProjArgs {
-  int N, K, G;
-  int ldw, k0;           // weight row length and first column of this launch's K range
+  int N, K, G;           // rows, columns (whole matrix), int4 group size
+  int nkc, kc;           // column ranges of a launch (EPI_PART only; else 1, K) and their width
   int nseg;              // bf16 row segments (QKV: 3)
   int seg_end[3];        // cumulative end row of each segment
-  const uint16_t* wb[3]; // bf16 segment bases, row-major [rows][ldw]
+  const uint16_t* wb[3]; // bf16 segment bases, row-major [rows][K]
   const uint16_t* wb2;   // SwiGLU: the "up" matrix (gate is wb[0])
-  const uint32_t* q4;    // int4 codes [N16][ldw/8] dwords (layout: ee_proj.hip)
-  const uint16_t* s4;    // bf16 scales [N16/16][ldw/G][16]
+  const uint32_t* q4;    // int4 codes [N16][K/8] dwords (layout: ee_proj.hip)
+  const uint16_t* s4;    // bf16 scales [N16/16][K/G][16]
   const uint32_t* q4b;   // SwiGLU "up" codes
   const uint16_t* s4b;
-  const uint16_t* x;     // bf16 input rows, indexed by sequence id (xmode 0)
+  const uint16_t* x;     // bf16 input rows [seq][x_stride]
   int x_stride;
-  int xmode;             // 0: x; 1: bf16(rmsnorm(h) * gain); 2: bf16(h)   (staged inputs only)
-  const float* h;        // float32 residual rows [b][K] (xmode 1, 2)
-  const uint16_t* gain;  // RMSNorm gains [K] (xmode 1)
-  float eps;
   const int32_t* list_bf; const int32_t* cnt_bf;  // rows run with bf16 weights
   const int32_t* list_i4; const int32_t* cnt_i4;  // rows run with int4 weights (may be null)
   void* y; int y_stride;                          // output rows, indexed by sequence id
+  int y_cstride;                                  // EPI_PART: elements between column ranges
   float* part;                                    // EPI_LSE / EPI_ARGMAX partials per workgroup
   float* logits; int logits_stride;               // EPI_ARGMAX: optional logits out
   // EPI_QKV: RoPE on q and k, q to qrot, k and v into the cache slot of the position
@@ -74,10 +75,17 @@ struct AttnArgs {
 
 // launchers (ee_kernels.hip)
 // Whether min(8, batch) input rows of width K fit the projection's LDS stage.
-// launch_proj splits a wider EPI_RESID projection (xmode 0) into launches over
-// column ranges of W that do fit; other projections must fit.
 bool proj_fits(int K, int batch);
-void launch_proj(int epi, const ProjArgs& a, int nwg, int batch, hipStream_t s);
+// Launches a projection over `batch` rows.  EPI_PART picks its column ranges
+// (a.nkc, a.kc) and returns their count; the other epilogues need
+// proj_fits(K, batch).
+int launch_proj(int epi, const ProjArgs& a, int nwg, int batch, hipStream_t s);
+// The column ranges EPI_PART uses for K columns, N rows (and their width).
+int proj_ranges(int K, int N, int nwg, int batch, int* kc);
+// h[b] += sum_c parts[c][b] for b < B (nparts may be 0); then, when gain is
+// set, x[b] = bf16(rmsnorm(h[b]) * gain), and when hb is set, hb[b] = bf16(h[b]).
+void launch_finish(float* h, const float* parts, int nparts, size_t cstride, int B, int d,
+                   const uint16_t* gain, float eps, uint16_t* x, uint16_t* hb, hipStream_t s);
 void launch_init(StepState* st, const int32_t* prompt, int P, int t, int B, int L,
                  const uint16_t* emb, int d, int V, float* h, float* p_rec, hipStream_t s);
 void launch_attention(const AttnArgs& a, hipStream_t s);

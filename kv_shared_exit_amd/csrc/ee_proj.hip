@@ -8,10 +8,11 @@
 // each layer serves both kinds of rows; the row lists remove the divergence).
 //
 // Layout of the work
-//   * The input rows (at most 8 per pass) are staged in LDS (64 KB) when they
-//     fit; wider inputs (the down projection) are read from L2 directly.  There
-//     is no split-K: a cross-workgroup reduction needs device-scope fences,
-//     which on gfx950 write back and invalidate the L2.
+//   * The input rows (at most 8 per pass) are staged in LDS (64 KB).  A launch
+//     with the partial-sum epilogue splits the columns into ranges that each
+//     fit the stage; every workgroup works on one range and writes float32
+//     partial sums, which the finish kernel adds to the residual in a fixed
+//     order (no cross-workgroup synchronisation, bitwise reproducible).
 //   * bf16 rows: each wave owns R weight rows; a lane reads 16 contiguous bytes
 //     per row per step (a wave reads 1 KB contiguous per row), double-buffered,
 //     and accumulates bf16 pairs with v_dot2_f32_bf16 against the inputs; a
@@ -19,12 +20,13 @@
 //     The first weights are requested before the inputs are staged.
 //   * int4 rows: the dequantise-and-multiply is ALU-heavy on the vector unit
 //     (8 products per 4 bytes per batch row), so it runs on MFMA
-//     (v_mfma_f32_16x16x32_bf16): a workgroup owns 16 weight rows, its 8 waves
-//     split K, each lane unpacks one dword of codes (8 weights) into the A
-//     operand in registers (nibble | 0x4300 is the bf16 value 136 + q), the
-//     inputs are the B operand (batch rows padded to 16 with zeros), and a
-//     second MFMA with A = 136 everywhere yields 136 * sum(x) per step, which is
-//     removed before each group of G inputs is scaled by its bf16 scale.
+//     (v_mfma_f32_16x16x32_bf16): a 16-row tile is shared by up to 8 waves
+//     that split its columns, each lane unpacks one dword of codes (8 weights)
+//     into the A operand in registers (nibble | 0x4300 is the bf16 value
+//     136 + q), the inputs are the B operand (batch rows padded to 16 with
+//     zeros), and a second MFMA with A = 136 everywhere yields 136 * sum(x) per
+//     step, which is removed before each group of G inputs is scaled by its
+//     bf16 scale.
 #include "ee_internal.h"
 #include "ee_device.h"
 
@@ -39,6 +41,14 @@ template <int EPI>
 struct Ep {
   static constexpr int P = EPI == EPI_SWIGLU ? 2 : 1;  // matrices per tile
   static constexpr int R = EPI == EPI_SWIGLU ? 1 : 2;  // bf16 rows per wave tile
+};
+
+// The share of a launch one workgroup works on: its column range and its
+// index among the workgroups of that range.
+struct Work {
+  int K, k0;    // columns of the range and the first of them
+  int wg, nwg;  // workgroup index within the range, workgroups per range
+  int chunk;    // range index
 };
 
 // Rows of a QKV tile: each tile pairs rotation rows c and c + hd/2 of one head
@@ -79,129 +89,57 @@ __device__ __forceinline__ void qkv_out(const ProjArgs& a, int seq, int n, float
   }
 }
 
-__device__ __forceinline__ const uint16_t* bf_row(const ProjArgs& a, int n) {
+__device__ __forceinline__ const uint16_t* bf_row(const ProjArgs& a, const Work& w, int n) {
   int s = 0, start = 0;
   if (n >= a.seg_end[0]) {
     s = (n >= a.seg_end[1]) ? 2 : 1;
     start = a.seg_end[s - 1];
   }
-  return a.wb[s] + (size_t)(n - start) * a.ldw + a.k0;
+  return a.wb[s] + (size_t)(n - start) * a.K + w.k0;
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 // Epilogue of one finished output value v (row n, sequence seq).
 template <int EPI>
-__device__ __forceinline__ void store_out(const ProjArgs& a, int seq, int n, float v) {
+__device__ __forceinline__ void store_out(const ProjArgs& a, const Work& w, int seq, int n, float v) {
   if constexpr (EPI == EPI_BF16) {
     ((uint16_t*)a.y)[(size_t)seq * a.y_stride + n] = (uint16_t)f2bf(v);
-  } else if constexpr (EPI == EPI_RESID) {
-    float* yp = (float*)a.y + (size_t)seq * a.y_stride + n;
-    *yp = *yp + v;
+  } else if constexpr (EPI == EPI_PART) {
+    ((float*)a.y)[(size_t)w.chunk * a.y_cstride + (size_t)seq * a.y_stride + n] = v;
   }
 }
 
-// Stages input rows list[c0 .. c0+nb) into LDS (row stride K).  xmode 0 copies
-// columns k0 .. k0+K of x.  With xmode 1 the rows are the RMSNorm of the
-// residual, x = bf16(h / sqrt(mean(h^2) + eps) * g), computed here; with xmode
-// 2 they are bf16(h).
-//
-// A thread handles at most kItems items of 8 elements and issues the loads of
-// a round of them before using any, so each round costs one memory latency
-// (float32 rows take two rounds, and the RMSNorm reads them twice: once for
-// the statistics, once to normalise).  The squares are summed per item, then
-// per row by one wave in a fixed order, so every workgroup derives identical
-// statistics.
+// Staging of the input rows list[c0 .. c0+nb) of this workgroup's column range
+// into LDS (row stride w.K).  stage_rows puts the rows' sequence ids in LDS and
+// is called before the first weights are requested, so that its load is not
+// queued behind them; stage_x then copies the rows.  Every thread issues all
+// of its loads (at most kItems items of 8 elements) before storing any, so the
+// copy costs one memory latency.
 constexpr int kItems = kXLdsElems / 8 / kProjThreads;
-constexpr int kRound = kItems / 2;
 
-__device__ __forceinline__ void stage_x(const ProjArgs& a, const int32_t* list, int c0, int nb, uint16_t* xs) {
-  const int K = a.K;
-  const int k8 = K >> 3;
+__device__ __forceinline__ void stage_rows(const int32_t* list, int c0, int nb, int* seq) {
+  if (threadIdx.x < 8) seq[threadIdx.x] = list[c0 + min((int)threadIdx.x, nb - 1)];
+}
+
+__device__ __forceinline__ void stage_x(const ProjArgs& a, const Work& w, int nb, const int* seq, uint16_t* xs) {
+  __syncthreads();  // seq is in LDS
+  const int k8 = w.K >> 3;
   const int n = nb * k8;  // items; item i = (row b, column group kk) sits at xs[b*K + kk*8] = xs[i*8]
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));  // keeps the per-item index math here (not hoisted and held live)
-  __shared__ int seq[8];  // sequence id of each staged row
-  if (tid < 8) seq[tid] = list[c0 + min(tid, nb - 1)];
-  __syncthreads();
-  auto row_of = [&](int b) { return seq[b]; };
-  if (a.xmode == 0) {
-    uint4 v[kItems];
+  uint4 v[kItems];
 #pragma unroll
-    for (int j = 0; j < kItems; ++j) {
-      const int i = min(tid + j * kProjThreads, n - 1);
-      const int b = i / k8;
-      v[j] = *(const uint4*)(a.x + (size_t)row_of(b) * a.x_stride + a.k0 + (i - b * k8) * 8);
-    }
-#pragma unroll
-    for (int j = 0; j < kItems; ++j) {
-      const int i = tid + j * kProjThreads;
-      if (i < n) *(uint4*)&xs[i * 8] = v[j];
-    }
-    return;
+  for (int j = 0; j < kItems; ++j) {
+    const int i = min(tid + j * kProjThreads, n - 1);
+    const int b = i / k8;
+    v[j] = *(const uint4*)(a.x + (size_t)seq[b] * a.x_stride + w.k0 + (i - b * k8) * 8);
   }
-  // one round of float32 items: loads first, then f(j, i, lo, hi) per valid item
-  auto round = [&](int r, auto&& f) {
-    float4 v0[kRound], v1[kRound];
 #pragma unroll
-    for (int j = 0; j < kRound; ++j) {
-      const int i = min(tid + (r * kRound + j) * kProjThreads, n - 1);
-      const int b = i / k8;
-      const float* hr = a.h + (size_t)row_of(b) * K + (i - b * k8) * 8;
-      v0[j] = *(const float4*)hr;
-      v1[j] = *(const float4*)(hr + 4);
-    }
-#pragma unroll
-    for (int j = 0; j < kRound; ++j) {
-      const int i = tid + (r * kRound + j) * kProjThreads;
-      if (i < n) f(i, v0[j], v1[j]);
-    }
-  };
-  __shared__ float rs[8];
-  if (a.xmode == 1) {
-    float* ssi = (float*)xs;  // per-item sums of squares (xs is written after they are used)
-    for (int r = 0; r < 2; ++r)
-      round(r, [&](int i, const float4& lo, const float4& hi) {
-        float ss = lo.x * lo.x;
-        ss = fmaf(lo.y, lo.y, ss);
-        ss = fmaf(lo.z, lo.z, ss);
-        ss = fmaf(lo.w, lo.w, ss);
-        ss = fmaf(hi.x, hi.x, ss);
-        ss = fmaf(hi.y, hi.y, ss);
-        ss = fmaf(hi.z, hi.z, ss);
-        ss = fmaf(hi.w, hi.w, ss);
-        ssi[i] = ss;
-      });
-    __syncthreads();
-    const int lane = tid & 63, wave = tid >> 6;
-    if (wave < nb) {  // wave b sums row b: lane-strided, then a fixed butterfly
-      float t = 0.0f;
-      for (int k = lane; k < k8; k += 64) t += ssi[wave * k8 + k];
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o);
-      if (lane == 0) rs[wave] = 1.0f / sqrtf(t / (float)K + a.eps);
-    }
-    __syncthreads();  // rs is ready and ssi is no longer read
+  for (int j = 0; j < kItems; ++j) {
+    const int i = tid + j * kProjThreads;
+    if (i < n) *(uint4*)&xs[i * 8] = v[j];
   }
-  for (int r = 0; r < 2; ++r)
-    round(r, [&](int i, const float4& lo, const float4& hi) {
-      const int b = i / k8;
-      const int kk = i - b * k8;
-      float f[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      if (a.xmode == 1) {
-        const float rr = rs[b];
-        const uint4 g = *(const uint4*)(a.gain + kk * 8);
-        const uint32_t gw[4] = {g.x, g.y, g.z, g.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = f[e] * rr * bf2f((gw[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-      }
-      uint4 o;
-      o.x = f2bf(f[0]) | (f2bf(f[1]) << 16);
-      o.y = f2bf(f[2]) | (f2bf(f[3]) << 16);
-      o.z = f2bf(f[4]) | (f2bf(f[5]) << 16);
-      o.w = f2bf(f[6]) | (f2bf(f[7]) << 16);
-      *(uint4*)&xs[i * 8] = o;
-    });
 }
 
 // ---------------------------------------------------------------------------
@@ -234,8 +172,8 @@ __device__ __forceinline__ void bf16_step(const uint4 (&wv)[RP], const uint16_t*
 }
 
 template <int EPI, int NB>
-__device__ __forceinline__ void bf16_pass(const ProjArgs& a, int nb, const int32_t* list, int c0,
-                                          uint16_t* xs, float* red) {
+__device__ __forceinline__ void bf16_pass(const ProjArgs& a, const Work& wk, int nb, const int32_t* list, int c0,
+                                          int* seq, uint16_t* xs, float* red) {
   constexpr int P = Ep<EPI>::P;
   constexpr int R = Ep<EPI>::R;
   constexpr int RP = R * P;
@@ -243,9 +181,9 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, int nb, const int32
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));  // lane-derived values are computed per pass, not held across passes
   const int wave = threadIdx.x >> 6;
-  const int wid = blockIdx.x * kWaves + wave;
-  const int nwc = gridDim.x * kWaves;
-  const int N = a.N, K = a.K;
+  const int wid = wk.wg * kWaves + wave;
+  const int nwc = wk.nwg * kWaves;
+  const int N = a.N, K = wk.K;
   const int ntiles = (N + R - 1) / R;
   const int idx = xidx<V>(lane);
   const int rr = idx / NB;
@@ -259,6 +197,7 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, int nb, const int32
   float lm = -INFINITY, ls = 0.0f;
   Top2 tp{-INFINITY, 0x7fffffff, -INFINITY};
 
+  stage_rows(list, c0, nb, seq);
   // request the first tile's first weights before the inputs are staged
   const int nfull = K >> 9;                  // full 512-element steps (every lane active)
   const int kt = nfull * 512 + lane * 8;     // this lane's element in the ragged tail
@@ -269,8 +208,8 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, int nb, const int32
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int n = EPI == EPI_QKV ? qkv_row(a, tt, r, R / 2) : min(tt * R + r, N - 1);
-      w[r] = bf_row(a, n) + lane * 8;
-      if constexpr (P == 2) w[R + r] = a.wb2 + (size_t)n * a.ldw + a.k0 + lane * 8;
+      w[r] = bf_row(a, wk, n) + lane * 8;
+      if constexpr (P == 2) w[R + r] = a.wb2 + (size_t)n * a.K + wk.k0 + lane * 8;
     }
   };
   if (t < ntiles && nfull > 0) {
@@ -278,7 +217,7 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, int nb, const int32
 #pragma unroll
     for (int r = 0; r < RP; ++r) cur[r] = ld_stream(w[r]);
   }
-  stage_x(a, list, c0, nb, xs);
+  stage_x(a, wk, nb, seq, xs);
   __syncthreads();
 
   for (; t < ntiles; t += nwc) {
@@ -324,16 +263,16 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, int nb, const int32
     const int n = EPI == EPI_QKV ? qkv_row(a, t, rr, R / 2) : n0 + (rr % R);
     if constexpr (EPI == EPI_QKV) {
       const float u = __shfl_xor(v, 1);  // the RoPE partner row sits in the partner lane
-      if (lane_ok) qkv_out(a, list[c0 + bsel], n, v, u);
+      if (lane_ok) qkv_out(a, seq[bsel], n, v, u);
     } else if constexpr (EPI == EPI_SWIGLU) {
       const float u = __shfl_xor(v, 1);  // the up row sits in the partner lane
       if (lane_ok && (lane & 1) == 0 && n < N)
-        ((uint16_t*)a.y)[(size_t)list[c0 + bsel] * a.y_stride + n] = (uint16_t)f2bf(silu_mul(v, u));
+        ((uint16_t*)a.y)[(size_t)seq[bsel] * a.y_stride + n] = (uint16_t)f2bf(silu_mul(v, u));
     } else if constexpr (EPI == EPI_LSE) {
       if (lane_ok && n < N) lse_merge(lm, ls, v, 1.0f);
     } else if constexpr (EPI == EPI_ARGMAX) {
       if (lane_ok && n < N) {
-        if (a.logits) a.logits[(size_t)list[c0 + bsel] * a.logits_stride + n] = v;
+        if (a.logits) a.logits[(size_t)seq[bsel] * a.logits_stride + n] = v;
         if (v > tp.v1) {
           tp.v2 = tp.v1;
           tp.v1 = v;
@@ -343,7 +282,7 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, int nb, const int32
         }
       }
     } else {
-      if (lane_ok && n < N) store_out<EPI>(a, list[c0 + bsel], n, v);
+      if (lane_ok && n < N) store_out<EPI>(a, wk, seq[bsel], n, v);
     }
   }
 
@@ -390,21 +329,21 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, int nb, const int32
 // ---------------------------------------------------------------------------
 // int4 rows (MFMA)
 //
-// Codes of a row: ldw/8 dwords, dword t holding elements [8t, 8t+8) with
-// element 8t+2i in bits [4i, 4i+4) and 8t+2i+1 in bits [16+4i, 16+4i+4), value
-// q + 8.  Within each full 128-element block the four dwords a lane needs for
-// the block's four MFMA steps are adjacent: logical dword 16u + 4j + c (step j,
-// lane quarter c) is stored at 16u + 4c + j.  A tail (ldw mod 128 > 0) keeps
+// Codes of a row: K/8 dwords, dword t holding elements [8t, 8t+8) with element
+// 8t+2i in bits [4i, 4i+4) and 8t+2i+1 in bits [16+4i, 16+4i+4), value q + 8.
+// Within each full 128-element block the four dwords a lane needs for the
+// block's four MFMA steps are adjacent: logical dword 16u + 4j + c (step j,
+// lane quarter c) is stored at 16u + 4c + j.  A tail (K mod 128 > 0) keeps
 // natural order.  Rows are padded to a multiple of 16 with zero codes.
-// Scales: [N16/16][ldw/G][16] bf16 (16 rows of one tile and one group adjacent).
+// Scales: [N16/16][K/G][16] bf16 (16 rows of one tile and one group adjacent).
 //
 // Work split: a 16-row tile is shared by WPT waves (1, 2, 4 or 8, chosen so
 // each wave owns about D blocks of 128 columns); a workgroup works on 8/WPT
 // tiles at a time.  Each wave keeps D blocks of codes and their scales in
 // flight in a register ring, refilled as blocks are consumed; the refills run
 // on into the workgroup's next tiles, so one tile's reduction overlaps the
-// next tile's loads.  A ring slot past the wave's work is pointed at a small
-// always-valid address (the scale array's start) and its compute is skipped.
+// next tile's loads.  A ring slot past the wave's work loads from the scale
+// array (always valid) and contributes zero.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bf16x8_t unpack8(uint32_t w) {
   uint4 o;
@@ -438,8 +377,7 @@ template <int P>
 __device__ __forceinline__ void i4_step(const uint32_t (&word)[P], const uint4& bv, f32x4_t (&cg)[P],
                                         f32x4_t& c136) {
   const bf16x8_t b8 = __builtin_bit_cast(bf16x8_t, bv);
-  const uint4 k136 = make_uint4(0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u);
-  c136 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k136), b8, c136, 0, 0, 0);
+  c136 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k136_operand(), b8, c136, 0, 0, 0);
 #pragma unroll
   for (int p = 0; p < P; ++p) cg[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack8(word[p]), b8, cg[p], 0, 0, 0);
 }
@@ -451,7 +389,7 @@ struct I4Ring {
   static constexpr int D = (P == 2 || NG == 4) ? 2 : 4;
 };
 
-// Waves per 16-row tile for a launch of K columns.
+// Waves per 16-row tile for a range of K columns.
 __host__ __device__ inline int i4_wpt(int K, int D) {
   const int nfull = K >> 7;
   int w = 1;
@@ -460,19 +398,19 @@ __host__ __device__ inline int i4_wpt(int K, int D) {
 }
 
 template <int EPI, int NG>
-__device__ __forceinline__ void i4_pass(const ProjArgs& a, int nb, const int32_t* list, int c0,
-                                        uint16_t* xs, float* red) {
+__device__ __forceinline__ void i4_pass(const ProjArgs& a, const Work& wk, int nb, const int32_t* list, int c0,
+                                        int* seq, uint16_t* xs, float* red) {
   constexpr int P = Ep<EPI>::P;
   constexpr int D = I4Ring<P, NG>::D;
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));  // lane-derived values are computed per pass, not held across passes
   const int wave = threadIdx.x >> 6;
   const int m = lane & 15, q = lane >> 4;
-  const int N = a.N, K = a.K, G = a.G;
+  const int N = a.N, K = wk.K, G = a.G;
   const int ntiles = (N + 15) >> 4;
-  const int ldc = a.ldw >> 3;           // dwords per code row
-  const int ngr = a.ldw / G;            // scale groups per row of the whole matrix
-  const int gk0 = a.k0 / G;             // first group of this launch's columns
+  const int ldc = a.K >> 3;             // dwords per code row
+  const int ngr = a.K / G;              // scale groups per row of the whole matrix
+  const int gk0 = wk.k0 / G;            // first group of this range
   const int nfull = K >> 7;
   const int ntail = (K & 127) >> 5;     // MFMA steps in the tail
   const int mpg = G >> 5;               // MFMA steps per group
@@ -482,15 +420,15 @@ __device__ __forceinline__ void i4_pass(const ProjArgs& a, int nb, const int32_t
   const int b0 = ws * nfull / wpt;
   const int nbw = (ws + 1) * nfull / wpt - b0;
   const int nbp = ((nfull + wpt - 1) / wpt + D - 1) / D * D;  // ring rounds per tile, same for all waves
-  const int nit = (ntiles + tpi - 1) / tpi;                    // workgroup iterations in the grid
-  const int ntl = (int)blockIdx.x < nit ? (nit - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  const int nit = (ntiles + tpi - 1) / tpi;                    // workgroup iterations in the range
+  const int ntl = wk.wg < nit ? (nit - 1 - wk.wg) / wk.nwg + 1 : 0;
   const bool bok = m < nb;
   const bool tail_here = ws == wpt - 1 && ntail > 0;
   const uint16_t* xrow = xs + (bok ? m : 0) * K;
 
   // weight row of MFMA A row mm of tile tt (the QKV epilogue pairs RoPE rows)
   auto arow = [&](int tt, int mm) { return EPI == EPI_QKV ? qkv_row(a, tt, mm, 8) : tt * 16 + mm; };
-  auto tile_of = [&](int j) { return ((int)blockIdx.x + j * (int)gridDim.x) * tpi + wave / wpt; };
+  auto tile_of = [&](int j) { return (wk.wg + j * wk.nwg) * tpi + wave / wpt; };
   // where a tile's loads start: code dword offset of this lane's first block
   // and scale offset of this lane's rows at the first group (-1: no tile)
   struct TileAt {
@@ -500,11 +438,15 @@ __device__ __forceinline__ void i4_pass(const ProjArgs& a, int nb, const int32_t
     const int t = tile_of(j);
     if (j >= ntl || t >= ntiles) return TileAt{-1, -1};
     const int r0 = arow(t, 4 * q);
-    return TileAt{arow(t, m) * ldc + (a.k0 >> 3) + b0 * 16 + q * 4, ((r0 >> 4) * ngr + gk0 + b0 * NG) * 16 + (r0 & 15)};
+    return TileAt{arow(t, m) * ldc + (wk.k0 >> 3) + b0 * 16 + q * 4, ((r0 >> 4) * ngr + gk0 + b0 * NG) * 16 + (r0 & 15)};
   };
 
   uint4 cw[P][D];
   uint2 sc[P][D][NG];
+  // a slot without work loads 64 bytes of the scale array at a place of its
+  // own (one line per wave, spread over the array, so the idle loads of all
+  // waves do not queue on one L2 channel)
+  const uint16_t* idle = a.s4 + (size_t)(((wk.chunk * wk.nwg + wk.wg) * kWaves + wave) * 32 % (ntiles * 16 * ngr));
   // issue the loads of block kk of the wave's slice of tile `at` into ring slot i
   auto issue = [&](const TileAt& at, int kk, int i) {
     const bool real = at.code >= 0 && kk < nbw;
@@ -512,18 +454,19 @@ __device__ __forceinline__ void i4_pass(const ProjArgs& a, int nb, const int32_t
     for (int p = 0; p < P; ++p) {
       const uint32_t* cb = p == 0 ? a.q4 : a.q4b;
       const uint16_t* sb = p == 0 ? a.s4 : a.s4b;
-      const uint32_t* cp = real ? cb + at.code + kk * 16 : (const uint32_t*)a.s4;
+      const uint32_t* cp = real ? cb + at.code + kk * 16 : (const uint32_t*)idle;
       cw[p][i] = ld_stream(cp);
 #pragma unroll
-      for (int g = 0; g < NG; ++g) sc[p][i][g] = *(const uint2*)(real ? sb + at.scale + (kk * NG + g) * 16 : a.s4);
+      for (int g = 0; g < NG; ++g) sc[p][i][g] = *(const uint2*)(real ? sb + at.scale + (kk * NG + g) * 16 : idle);
     }
   };
+  stage_rows(list, c0, nb, seq);
   TileAt at_cur = tile_at(0);
   if (nfull > 0) {
 #pragma unroll
     for (int i = 0; i < D; ++i) issue(at_cur, i, i);
   }
-  stage_x(a, list, c0, nb, xs);
+  stage_x(a, wk, nb, seq, xs);
   __syncthreads();
 
   for (int j = 0; j < ntl; ++j) {
@@ -586,7 +529,7 @@ __device__ __forceinline__ void i4_pass(const ProjArgs& a, int nb, const int32_t
 #pragma unroll
         for (int p = 0; p < P; ++p) {
           const uint32_t* cb = p == 0 ? a.q4 : a.q4b;
-          word[p] = cb[(size_t)arow(t, m) * ldc + ((a.k0 + ka) >> 3) + q];
+          word[p] = cb[(size_t)arow(t, m) * ldc + ((wk.k0 + ka) >> 3) + q];
         }
         i4_step<P>(word, bv, cg, c136);
         if (st % mpg == mpg - 1) {
@@ -625,7 +568,7 @@ __device__ __forceinline__ void i4_pass(const ProjArgs& a, int nb, const int32_t
       __syncthreads();
     }
     if (!fin) continue;
-    const int tf = ((int)blockIdx.x + j * (int)gridDim.x) * tpi + wave;  // the tile this wave finishes
+    const int tf = (wk.wg + j * wk.nwg) * tpi + wave;  // the tile this wave finishes
     if (tf >= ntiles) continue;
     if constexpr (EPI == EPI_QKV) {
       // lane (q, m) holds rows arow(tf, 4q + i); the RoPE partners sit in lane ^ 32
@@ -633,22 +576,20 @@ __device__ __forceinline__ void i4_pass(const ProjArgs& a, int nb, const int32_t
 #pragma unroll
       for (int i = 0; i < 4; ++i) u[i] = __shfl_xor(vals[0][i], 32);
       if (!bok) continue;
-      const int seq = list[c0 + m];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qkv_out(a, seq, arow(tf, 4 * q + i), vals[0][i], u[i]);
+      for (int i = 0; i < 4; ++i) qkv_out(a, seq[m], arow(tf, 4 * q + i), vals[0][i], u[i]);
       continue;
     }
     if (!bok) continue;
     // lane (q, m) holds rows tf*16 + 4q + i of batch column m
-    const int seq = list[c0 + m];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int n = tf * 16 + 4 * q + i;
       if (n >= N) continue;
       if constexpr (EPI == EPI_SWIGLU)
-        ((uint16_t*)a.y)[(size_t)seq * a.y_stride + n] = (uint16_t)f2bf(silu_mul(vals[0][i], vals[P - 1][i]));
+        ((uint16_t*)a.y)[(size_t)seq[m] * a.y_stride + n] = (uint16_t)f2bf(silu_mul(vals[0][i], vals[P - 1][i]));
       else
-        store_out<EPI>(a, seq, n, vals[0][i]);
+        store_out<EPI>(a, wk, seq[m], n, vals[0][i]);
     }
   }
 }
@@ -657,6 +598,13 @@ template <int EPI, int NG>
 __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[kXLdsElems];
   __shared__ __attribute__((aligned(16))) float red[kWaves * 64 * 4];
+  __shared__ int seq[8];  // sequence ids of the staged rows
+  Work wk;
+  wk.nwg = gridDim.x / a.nkc;
+  wk.chunk = blockIdx.x / wk.nwg;
+  wk.wg = blockIdx.x - wk.chunk * wk.nwg;
+  wk.k0 = wk.chunk * a.kc;
+  wk.K = min(a.kc, a.K - wk.k0);
   for (int fmt = 0; fmt < 2; ++fmt) {
     if constexpr (EPI == EPI_LSE || EPI == EPI_ARGMAX || EPI == EPI_BF16) {
       if (fmt == 1) break;  // these run on backbone rows only
@@ -666,18 +614,19 @@ __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a)
     const int32_t* list = fmt ? a.list_i4 : a.list_bf;
     for (int c0 = 0; c0 < n; c0 += 8) {
       const int nb = min(8, n - c0);
-      __syncthreads();  // the previous pass is done with xs and red
+      __syncthreads();  // the previous pass is done with xs, red and seq
       if (fmt == 0) {
         if (nb == 1)
-          bf16_pass<EPI, 1>(a, nb, list, c0, xs, red);
+          bf16_pass<EPI, 1>(a, wk, nb, list, c0, seq, xs, red);
         else if (nb == 2)
-          bf16_pass<EPI, 2>(a, nb, list, c0, xs, red);
+          bf16_pass<EPI, 2>(a, wk, nb, list, c0, seq, xs, red);
         else if (nb <= 4)
-          bf16_pass<EPI, 4>(a, nb, list, c0, xs, red);
+          bf16_pass<EPI, 4>(a, wk, nb, list, c0, seq, xs, red);
         else
-          bf16_pass<EPI, 8>(a, nb, list, c0, xs, red);
+          bf16_pass<EPI, 8>(a, wk, nb, list, c0, seq, xs, red);
       } else {
-        if constexpr (EPI == EPI_RESID || EPI == EPI_SWIGLU || EPI == EPI_QKV) i4_pass<EPI, NG>(a, nb, list, c0, xs, red);
+        if constexpr (EPI == EPI_PART || EPI == EPI_SWIGLU || EPI == EPI_QKV)
+          i4_pass<EPI, NG>(a, wk, nb, list, c0, seq, xs, red);
       }
     }
   }
@@ -687,7 +636,7 @@ bool proj_fits(int K, int batch) { return (long long)std::min(8, batch) * K <= k
 
 template <int EPI>
 static void launch_ng(const ProjArgs& a, int g, hipStream_t s) {
-  if constexpr (EPI == EPI_RESID || EPI == EPI_SWIGLU || EPI == EPI_QKV) {
+  if constexpr (EPI == EPI_PART || EPI == EPI_SWIGLU || EPI == EPI_QKV) {
     if (a.G == 32) {
       hipLaunchKernelGGL((proj_kernel<EPI, 4>), dim3(g), dim3(kProjThreads), 0, s, a);
       return;
@@ -700,42 +649,156 @@ static void launch_ng(const ProjArgs& a, int g, hipStream_t s) {
   hipLaunchKernelGGL((proj_kernel<EPI, 1>), dim3(g), dim3(kProjThreads), 0, s, a);
 }
 
-static void launch_one(int epi, const ProjArgs& a, int g, hipStream_t s) {
+int proj_ranges(int K, int N, int nwg, int batch, int* kc) {
+  // whole 128-column blocks that fit the stage, and enough ranges that the
+  // 16-row int4 tiles of all ranges cover the grid (ranges of >= 8 blocks)
+  const int rows = std::min(8, batch);
+  const int g = std::max(1, std::min(nwg, kNwgMax));
+  const int blocks = (K + 127) / 128;
+  const int cmax = (kXLdsElems / rows) / 128;  // blocks per range at most
+  const int nmin = (blocks + cmax - 1) / cmax;
+  const int want = std::min(4, g * 16 / std::max(N, 1));
+  const int n = std::max(1, std::max(nmin, std::min(want, blocks / 8)));
+  const int kcb = (blocks + n - 1) / n;
+  if (kc) *kc = kcb * 128;
+  return (blocks + kcb - 1) / kcb;
+}
+
+int launch_proj(int epi, const ProjArgs& a0, int nwg, int batch, hipStream_t s) {
+  ProjArgs a = a0;
+  // the vocabulary epilogues write one partial per workgroup (kNwgMax of them)
+  int g = std::max(1, std::min(nwg, kNwgMax));
+  a.nkc = 1;
+  a.kc = a.K;
+  if (epi == EPI_PART) {
+    a.nkc = proj_ranges(a.K, a.N, nwg, batch, &a.kc);
+    g = std::max(1, g / a.nkc) * a.nkc;
+  } else if (!proj_fits(a.K, batch)) {
+    throw std::logic_error("projection input too wide for the stage");
+  }
   switch (epi) {
     case EPI_BF16: launch_ng<EPI_BF16>(a, g, s); break;
-    case EPI_RESID: launch_ng<EPI_RESID>(a, g, s); break;
+    case EPI_PART: launch_ng<EPI_PART>(a, g, s); break;
     case EPI_SWIGLU: launch_ng<EPI_SWIGLU>(a, g, s); break;
     case EPI_LSE: launch_ng<EPI_LSE>(a, g, s); break;
     case EPI_ARGMAX: launch_ng<EPI_ARGMAX>(a, g, s); break;
     case EPI_QKV: launch_ng<EPI_QKV>(a, g, s); break;
   }
+  return a.nkc;
 }
 
-void launch_proj(int epi, const ProjArgs& a0, int nwg, int batch, hipStream_t s) {
-  ProjArgs a = a0;
-  if (a.ldw == 0) a.ldw = a.K;
-  // the vocabulary epilogues write one partial per workgroup (kNwgMax of them)
-  const int g = std::max(1, std::min(nwg, kNwgMax));
-  const int rows = std::min(8, batch);
-  if (proj_fits(a.K, batch)) {
-    launch_one(epi, a, g, s);
-    return;
+// ---------------------------------------------------------------------------
+// Residual finish: h += sum of the partial sums of the column ranges (fixed
+// order), then the RMSNorm of the new residual for the next projection
+// (bf16(h * rsqrt(mean(h^2) + eps) * g)) and optionally bf16(h).  One
+// workgroup per row.
+// ---------------------------------------------------------------------------
+constexpr int kFinThreads = 256;
+constexpr int kFinVec = 4;    // float4 per thread per row chunk
+constexpr int kFinParts = 8;  // column ranges summed with all loads in flight
+
+// One workgroup per (row, chunk of kFinThreads * kFinVec * 4 columns) would
+// need a second pass for the norm; instead a workgroup owns a row and loops
+// over its chunks, issuing every load of a chunk (residual, partial sums,
+// gains) before using any.
+__global__ __launch_bounds__(kFinThreads) void finish_kernel(float* h, const float* parts, int nparts, size_t cstride,
+                                                             int d, const uint16_t* gain, float eps, uint16_t* x,
+                                                             uint16_t* hb) {
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int d4 = d >> 2;
+  float* hr = h + (size_t)b * d;
+  const int per = kFinThreads * kFinVec;  // float4 per chunk
+  float ss = 0.0f;
+  for (int c0 = 0; c0 < d4; c0 += per) {
+    float4 v[kFinVec];
+    float4 pv[kFinParts][kFinVec];
+#pragma unroll
+    for (int j = 0; j < kFinVec; ++j) {
+      const int i = min(c0 + tid + j * kFinThreads, d4 - 1);
+      v[j] = *(const float4*)(hr + 4 * i);
+#pragma unroll
+      for (int c = 0; c < kFinParts; ++c) {
+        // ranges past nparts reload the last one (or, with none, the residual
+        // row itself: parts may be null then) and are not added
+        const float* src = nparts > 0 ? parts + min(c, nparts - 1) * cstride + (size_t)b * d : hr;
+        pv[c][j] = *(const float4*)(src + 4 * i);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kFinVec; ++j) {
+#pragma unroll
+      for (int c = 0; c < kFinParts; ++c) {
+        if (c < nparts) {
+          v[j].x += pv[c][j].x;
+          v[j].y += pv[c][j].y;
+          v[j].z += pv[c][j].z;
+          v[j].w += pv[c][j].w;
+        }
+      }
+      for (int c = kFinParts; c < nparts; ++c) {  // more ranges than kFinParts (very wide inputs)
+        const int i = min(c0 + tid + j * kFinThreads, d4 - 1);
+        const float4 p = *(const float4*)(parts + c * cstride + (size_t)b * d + 4 * i);
+        v[j].x += p.x;
+        v[j].y += p.y;
+        v[j].z += p.z;
+        v[j].w += p.w;
+      }
+      const int i = c0 + tid + j * kFinThreads;
+      if (i >= d4) continue;
+      if (nparts > 0) *(float4*)(hr + 4 * i) = v[j];
+      ss = fmaf(v[j].x, v[j].x, ss);
+      ss = fmaf(v[j].y, v[j].y, ss);
+      ss = fmaf(v[j].z, v[j].z, ss);
+      ss = fmaf(v[j].w, v[j].w, ss);
+      if (hb) {
+        uint2 o;
+        o.x = f2bf(v[j].x) | (f2bf(v[j].y) << 16);
+        o.y = f2bf(v[j].z) | (f2bf(v[j].w) << 16);
+        *(uint2*)(hb + (size_t)b * d + 4 * i) = o;
+      }
+    }
   }
-  // y += W x over column ranges of W whose inputs fit the stage: the ranges
-  // are whole 128-column blocks of near-equal size (group boundaries too)
-  if (epi != EPI_RESID || a.xmode != 0 || a.k0 != 0) throw std::logic_error("projection input too wide");
-  const int cmax = (kXLdsElems / rows) / 128 * 128;
-  const int nch = (a.K + cmax - 1) / cmax;
-  const int blocks = (a.K + 127) / 128;
-  int k0 = 0;
-  for (int c = 0; c < nch; ++c) {
-    const int kb = (c + 1) * blocks / nch * 128;
-    ProjArgs b = a;
-    b.k0 = k0;
-    b.K = std::min(a.K, kb) - k0;
-    launch_one(epi, b, g, s);
-    k0 += b.K;
+  if (!gain) return;
+  __shared__ float wsum[kFinThreads / 64];
+  __shared__ float rs;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+  __syncthreads();
+  if (tid == 0) {
+    float t = 0.0f;
+    for (int w = 0; w < kFinThreads / 64; ++w) t += wsum[w];
+    rs = 1.0f / sqrtf(t / (float)d + eps);
   }
+  __syncthreads();
+  const float r = rs;
+  // the normalised row: the residual is re-read (this workgroup just wrote it)
+  for (int c0 = 0; c0 < d4; c0 += per) {
+    float4 v[kFinVec];
+    uint2 g[kFinVec];
+#pragma unroll
+    for (int j = 0; j < kFinVec; ++j) {
+      const int i = min(c0 + tid + j * kFinThreads, d4 - 1);
+      v[j] = *(const float4*)(hr + 4 * i);
+      g[j] = *(const uint2*)(gain + 4 * i);
+    }
+#pragma unroll
+    for (int j = 0; j < kFinVec; ++j) {
+      const int i = c0 + tid + j * kFinThreads;
+      if (i >= d4) continue;
+      uint2 o;
+      o.x = f2bf(v[j].x * r * bf2f(g[j].x & 0xffffu)) | (f2bf(v[j].y * r * bf2f(g[j].x >> 16)) << 16);
+      o.y = f2bf(v[j].z * r * bf2f(g[j].y & 0xffffu)) | (f2bf(v[j].w * r * bf2f(g[j].y >> 16)) << 16);
+      *(uint2*)(x + (size_t)b * d + 4 * i) = o;
+    }
+  }
+}
+
+void launch_finish(float* h, const float* parts, int nparts, size_t cstride, int B, int d, const uint16_t* gain,
+                   float eps, uint16_t* x, uint16_t* hb, hipStream_t s) {
+  hipLaunchKernelGGL(finish_kernel, dim3(B), dim3(kFinThreads), 0, s, h, parts, nparts, cstride, d, gain, eps, x,
+                     hb);
 }
 
 // ---------------------------------------------------------------------------
