@@ -27,9 +27,28 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 
+# HBM traffic of one exit-head launch with rows on the backbone (8B shape, 8
+# staged rows), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of
+# kv_shared_exit_amd/ee_probe (profiles/exit_head_lse_8b_traffic.md), each
+# scaled by what the same counter reads for a 1 GiB device copy.  Valid only
+# for the kernel sources it was measured on (their sha256); otherwise null.
+TRAFFIC = {"workload": "8b", "fetch_kib": 513391.9479, "write_kib": 64.0,
+           "fetch_scale": 1.9999337, "write_scale": 1.0,
+           "sources_sha256": "94e1a111fd5ad4ccf054ab4d6728fdf0b781cbbf7cb9f144d86c4ec123c2e266"}
+KERNEL_SOURCES = ("ee_proj.hip", "ee_device.h", "ee_internal.h")
+
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "kv_shared_exit_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def step_bytes(sh, exits, ctx, B):
@@ -176,6 +195,13 @@ def main():
     avg_ms = head_ms / max(n_launch, 1)
     head_bytes = head_bytes_total / max(n_launch, 1)
     achieved = head_bytes_total / (head_ms * 1e-3) / 1e9 if n_launch else 0.0
+    # measured HBM traffic per launch, averaged like the algorithmic bytes (a
+    # launch without rows reads nothing)
+    traffic = None
+    if wl.name == TRAFFIC["workload"] and kernel_sources_sha256() == TRAFFIC["sources_sha256"] and n_launch:
+        per_work = (TRAFFIC["fetch_kib"] * TRAFFIC["fetch_scale"] + TRAFFIC["write_kib"] * TRAFFIC["write_scale"]) * 1024
+        n_work = sum(1 for s_ in range(K) for l in range(1, sh.n_layers) if (exits[s_] >= l).any())
+        traffic = round(per_work * n_work / n_launch)
 
     copy_probe = None
     if args.copy_probe:
@@ -207,7 +233,7 @@ def main():
                    "global_batch": B, "seq_len": P, "decode_steps": K, "parallelism": "none"},
         "roofline": {"bound": "hbm", "kernel": "exit-head vocabulary GEMV (proj_kernel<3, 1>)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "launches": n_launch, "launches_with_work": head_launches,
                      "avg_us": round(1e3 * avg_ms, 2), "bytes_per_launch": int(head_bytes)},
         "step": {"algorithmic_GB": round(total_bytes / K / 1e9, 3),

@@ -207,10 +207,11 @@ ee_status ee_exit_weights_read(const ee_model *m, int32_t layer, int32_t which, 
                                int32_t nrows, int8_t *codes_host, uint16_t *scales_host);
 
 /* Kernel timing for measurement.  When enabled, every launch of the exit-head
- * vocabulary GEMV (and the final LM head) is bracketed by HIP events on the
- * stream it runs on, graph replays included; ee_profile_read returns the number
- * of such launches and their summed duration in milliseconds since the last
- * read, then clears the counters.  kind: 0 exit-head vocabulary GEMV. */
+ * vocabulary GEMV records its own start and end into a pair of HIP events on
+ * the stream it runs on (hipExtLaunchKernel), so the pair times the kernel
+ * alone; ee_profile_read returns the number of such launches and their summed
+ * duration in milliseconds since the last read, then clears the counters.
+ * kind: 0 exit-head vocabulary GEMV. */
 ee_status ee_profile_enable(ee_model *m, int32_t on);
 ee_status ee_profile_read(ee_model *m, int32_t kind, int64_t *launches, double *total_ms);
 

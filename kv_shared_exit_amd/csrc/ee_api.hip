@@ -193,7 +193,10 @@ void validate_config(const ee_model_config& c) {
 
 hipStream_t pick_stream(ee_model* m, void* s) { return s ? (hipStream_t)s : m->own; }
 
-void prof_begin(ee_model* m, hipStream_t s, hipEvent_t* e0) {
+// Events for the profiled launches: the launch itself records its start and
+// end into them (hipExtLaunchKernel), so they time the kernel alone.
+void prof_events(ee_model* m, hipEvent_t* e0, hipEvent_t* e1) {
+  *e0 = *e1 = nullptr;
   if (!m->prof) return;
   if (m->ev_used + 2 > m->ev_pool.size()) {
     for (int i = 0; i < 64; ++i) {
@@ -203,13 +206,7 @@ void prof_begin(ee_model* m, hipStream_t s, hipEvent_t* e0) {
     }
   }
   *e0 = m->ev_pool[m->ev_used++];
-  HIPCHK(hipEventRecord(*e0, s));
-}
-
-void prof_end(ee_model* m, hipStream_t s) {
-  if (!m->prof) return;
-  hipEvent_t e1 = m->ev_pool[m->ev_used++];
-  HIPCHK(hipEventRecord(e1, s));
+  *e1 = m->ev_pool[m->ev_used++];
 }
 
 void prof_collect(ee_model* m) {
@@ -424,10 +421,9 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
         a.x = m->z;
         a.x_stride = d;
         a.part = m->head_part;
-        hipEvent_t e0;
-        prof_begin(m, s, &e0);
-        launch_proj(EPI_LSE, a, kNwg, B, s);
-        prof_end(m, s);
+        hipEvent_t e0, e1;
+        prof_events(m, &e0, &e1);
+        launch_proj(EPI_LSE, a, kNwg, B, s, e0, e1);
       }
       launch_decide(st, m->head_part, kNwg, m->d_gamma, l, L, B, m->p_rec, s);
     }

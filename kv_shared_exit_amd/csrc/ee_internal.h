@@ -79,7 +79,9 @@ bool proj_fits(int K, int batch);
 // Launches a projection over `batch` rows.  EPI_PART picks its column ranges
 // (a.nkc, a.kc) and returns their count; the other epilogues need
 // proj_fits(K, batch).
-int launch_proj(int epi, const ProjArgs& a, int nwg, int batch, hipStream_t s);
+// With ev0/ev1 set, the launch records its own start and end into them.
+int launch_proj(int epi, const ProjArgs& a, int nwg, int batch, hipStream_t s, hipEvent_t ev0 = nullptr,
+                hipEvent_t ev1 = nullptr);
 // The column ranges EPI_PART uses for K columns, N rows (and their width).
 int proj_ranges(int K, int N, int nwg, int batch, int* kc);
 // h[b] += sum_c parts[c][b] for b < B (nparts may be 0); then, when gain is

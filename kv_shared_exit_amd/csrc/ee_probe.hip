@@ -1,0 +1,110 @@
+// ee_probe: launches one of the library's kernels on synthetic operands, for
+// hardware-counter runs of a single kernel (rocprofv3 --pmc) outside a Python
+// process, and a plain device copy of known size that calibrates the byte
+// counters.
+//
+//   ee_probe lse V d rows reps   exit-head vocabulary GEMV (proj_kernel<EPI_LSE>)
+//                                over a V x d bf16 matrix and `rows` staged rows
+//   ee_probe copy MiB            one copy kernel reading and writing MiB each
+//
+// Prints the mean launch time (HIP events on the launch stream).
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "ee_internal.h"
+
+using namespace ee;
+
+#define CK(x)                                                                        \
+  do {                                                                               \
+    hipError_t e_ = (x);                                                             \
+    if (e_ != hipSuccess) {                                                          \
+      std::fprintf(stderr, "HIP error %s at line %d\n", hipGetErrorString(e_), __LINE__); \
+      std::exit(1);                                                                  \
+    }                                                                                \
+  } while (0)
+
+__global__ void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ dst, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+static int usage() {
+  std::fprintf(stderr, "usage: ee_probe lse V d rows reps | ee_probe copy MiB\n");
+  return 2;
+}
+
+int main(int argc, char** argv) {
+  if (argc < 2) return usage();
+  hipStream_t s;
+  CK(hipStreamCreate(&s));
+  hipEvent_t e0, e1;
+  CK(hipEventCreate(&e0));
+  CK(hipEventCreate(&e1));
+  if (!std::strcmp(argv[1], "copy")) {
+    if (argc < 3) return usage();
+    const size_t mib = std::strtoull(argv[2], nullptr, 10);
+    if (mib == 0 || mib > 16384) return usage();
+    const size_t n = mib << 16;  // uint4 elements
+    uint4 *src, *dst;
+    CK(hipMalloc(&src, n * 16));
+    CK(hipMalloc(&dst, n * 16));
+    CK(hipMemsetAsync(src, 1, n * 16, s));
+    CK(hipStreamSynchronize(s));
+    CK(hipEventRecord(e0, s));
+    hipLaunchKernelGGL(copy_kernel, dim3(4096), dim3(256), 0, s, src, dst, n);
+    CK(hipEventRecord(e1, s));
+    CK(hipEventSynchronize(e1));
+    float ms = 0;
+    CK(hipEventElapsedTime(&ms, e0, e1));
+    std::printf("copy %zu MiB: %.2f us, %.1f GB/s (read + write)\n", mib, 1e3 * ms, 2.0 * n * 16 / (ms * 1e6));
+    return 0;
+  }
+  if (!std::strcmp(argv[1], "lse")) {
+    if (argc < 6) return usage();
+    const int V = std::atoi(argv[2]), d = std::atoi(argv[3]), rows = std::atoi(argv[4]), reps = std::atoi(argv[5]);
+    if (V < 1 || d < 32 || d % 32 || rows < 1 || rows > 8 || reps < 1 || !proj_fits(d, rows)) return usage();
+    uint16_t *E, *x;
+    float* part;
+    int32_t* lists;
+    CK(hipMalloc(&E, (size_t)V * d * 2));
+    CK(hipMalloc(&x, (size_t)kMaxBatch * d * 2));
+    CK(hipMalloc(&part, (size_t)kNwgMax * kMaxBatch * 4 * 4));
+    CK(hipMalloc(&lists, 2 * kMaxBatch * 4));
+    CK(hipMemsetAsync(E, 0x3c, (size_t)V * d * 2, s));  // bf16 ~0.0115
+    CK(hipMemsetAsync(x, 0x3c, (size_t)kMaxBatch * d * 2, s));
+    std::vector<int32_t> hl(2 * kMaxBatch, 0);
+    for (int i = 0; i < kMaxBatch; ++i) hl[i] = i;
+    hl[kMaxBatch] = rows;
+    CK(hipMemcpyAsync(lists, hl.data(), hl.size() * 4, hipMemcpyHostToDevice, s));
+    ProjArgs a{};
+    a.N = V;
+    a.K = d;
+    a.G = 128;
+    a.nseg = 1;
+    a.wb[0] = E;
+    a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = V;
+    a.x = x;
+    a.x_stride = d;
+    a.list_bf = lists;
+    a.cnt_bf = lists + kMaxBatch;
+    a.part = part;
+    launch_proj(EPI_LSE, a, kNwgMax, rows, s);  // warm-up
+    CK(hipStreamSynchronize(s));
+    CK(hipEventRecord(e0, s));
+    for (int r = 0; r < reps; ++r) launch_proj(EPI_LSE, a, kNwgMax, rows, s);
+    CK(hipEventRecord(e1, s));
+    CK(hipEventSynchronize(e1));
+    float ms = 0;
+    CK(hipEventElapsedTime(&ms, e0, e1));
+    const double us = 1e3 * ms / reps;
+    const double bytes = 2.0 * V * d + 2.0 * d * rows;
+    std::printf("lse V=%d d=%d rows=%d: %.2f us per launch, %.1f GB/s algorithmic\n", V, d, rows, us, bytes / us / 1e3);
+    return 0;
+  }
+  return usage();
+}

@@ -30,6 +30,8 @@
 #include "ee_internal.h"
 #include "ee_device.h"
 
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 #include <stdexcept>
 
@@ -634,19 +636,21 @@ __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a)
 
 bool proj_fits(int K, int batch) { return (long long)std::min(8, batch) * K <= kXLdsElems; }
 
+template <int EPI, int NG>
+static void launch_k(const ProjArgs& a, int g, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  if (ev0)
+    hipExtLaunchKernelGGL((proj_kernel<EPI, NG>), dim3(g), dim3(kProjThreads), 0, s, ev0, ev1, 0, a);
+  else
+    hipLaunchKernelGGL((proj_kernel<EPI, NG>), dim3(g), dim3(kProjThreads), 0, s, a);
+}
+
 template <int EPI>
-static void launch_ng(const ProjArgs& a, int g, hipStream_t s) {
+static void launch_ng(const ProjArgs& a, int g, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   if constexpr (EPI == EPI_PART || EPI == EPI_SWIGLU || EPI == EPI_QKV) {
-    if (a.G == 32) {
-      hipLaunchKernelGGL((proj_kernel<EPI, 4>), dim3(g), dim3(kProjThreads), 0, s, a);
-      return;
-    }
-    if (a.G == 64) {
-      hipLaunchKernelGGL((proj_kernel<EPI, 2>), dim3(g), dim3(kProjThreads), 0, s, a);
-      return;
-    }
+    if (a.G == 32) return launch_k<EPI, 4>(a, g, s, ev0, ev1);
+    if (a.G == 64) return launch_k<EPI, 2>(a, g, s, ev0, ev1);
   }
-  hipLaunchKernelGGL((proj_kernel<EPI, 1>), dim3(g), dim3(kProjThreads), 0, s, a);
+  launch_k<EPI, 1>(a, g, s, ev0, ev1);
 }
 
 int proj_ranges(int K, int N, int nwg, int batch, int* kc) {
@@ -664,7 +668,7 @@ int proj_ranges(int K, int N, int nwg, int batch, int* kc) {
   return (blocks + kcb - 1) / kcb;
 }
 
-int launch_proj(int epi, const ProjArgs& a0, int nwg, int batch, hipStream_t s) {
+int launch_proj(int epi, const ProjArgs& a0, int nwg, int batch, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   ProjArgs a = a0;
   // the vocabulary epilogues write one partial per workgroup (kNwgMax of them)
   int g = std::max(1, std::min(nwg, kNwgMax));
@@ -677,12 +681,12 @@ int launch_proj(int epi, const ProjArgs& a0, int nwg, int batch, hipStream_t s) 
     throw std::logic_error("projection input too wide for the stage");
   }
   switch (epi) {
-    case EPI_BF16: launch_ng<EPI_BF16>(a, g, s); break;
-    case EPI_PART: launch_ng<EPI_PART>(a, g, s); break;
-    case EPI_SWIGLU: launch_ng<EPI_SWIGLU>(a, g, s); break;
-    case EPI_LSE: launch_ng<EPI_LSE>(a, g, s); break;
-    case EPI_ARGMAX: launch_ng<EPI_ARGMAX>(a, g, s); break;
-    case EPI_QKV: launch_ng<EPI_QKV>(a, g, s); break;
+    case EPI_BF16: launch_ng<EPI_BF16>(a, g, s, ev0, ev1); break;
+    case EPI_PART: launch_ng<EPI_PART>(a, g, s, ev0, ev1); break;
+    case EPI_SWIGLU: launch_ng<EPI_SWIGLU>(a, g, s, ev0, ev1); break;
+    case EPI_LSE: launch_ng<EPI_LSE>(a, g, s, ev0, ev1); break;
+    case EPI_ARGMAX: launch_ng<EPI_ARGMAX>(a, g, s, ev0, ev1); break;
+    case EPI_QKV: launch_ng<EPI_QKV>(a, g, s, ev0, ev1); break;
   }
   return a.nkc;
 }
