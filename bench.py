@@ -113,7 +113,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true", help="launch every kernel eagerly")
+    ap.add_argument("--no-profile", action="store_true",
+                    help="do not time the exit-head launches (no roofline figure)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -150,28 +151,46 @@ def main():
     api.prefill(model, cache, prompts, stream=stream)
     log(f"prefill {B}x{P} done ({time.time() - t0:.0f}s)")
 
-    forced = None
-    exits = []
+    exits, toks = [], []
 
-    def step(s):
+    def step(s, tokens=None):
         f = synth.make_forced_exits(wl, s) if wl.policy == "forced" else None
-        return api.decode_step(model, cache, B, forced=f, stream=stream)
+        return api.decode_step(model, cache, B, tokens=tokens, forced=f, stream=stream)
 
+    last = None
     for s in range(W):
-        step(s)
+        last, _ = step(s)
     torch.cuda.synchronize()
     ctx0 = cache.lengths()[:B].copy()
-    model.profile(True)
+    tok_in0 = last.copy()
+    # timed region: the production path (each step replays its captured graph)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(K):
-        _, e = step(W + s)
+        t, e = step(W + s)
+        toks.append(t.copy())
         exits.append(e.copy())
     torch.cuda.synchronize()
     t_el = time.perf_counter() - t_start
-    n_launch, head_ms = model.profile_read(0)
-    model.profile(False)
     log(f"timed {K} steps in {t_el:.3f}s")
+
+    # the same K steps once more, rolled back and re-run with the same inputs,
+    # each exit-head launch timed by events it records itself (profiled steps
+    # launch their kernels one by one); the decisions must repeat exactly
+    n_launch, head_ms = 0, 0.0
+    if not args.no_profile:
+        cache.rollback(-1, K)
+        model.profile(True)
+        tin = tok_in0
+        for s in range(K):
+            t, e = step(W + s, tokens=tin)
+            if not (np.array_equal(t, toks[s]) and np.array_equal(e, exits[s])):
+                raise RuntimeError(f"profiled re-run of step {s} differs from the timed run")
+            tin = t
+        torch.cuda.synchronize()
+        n_launch, head_ms = model.profile_read(0)
+        model.profile(False)
+        log(f"profiled re-run: {n_launch} exit-head launches, {head_ms:.2f} ms")
 
     exits = np.stack(exits)
     total_bytes = 0
@@ -193,7 +212,7 @@ def main():
             if a_rows:
                 head_bytes_total += 2 * sh.vocab * sh.d_model + 2 * sh.d_model * a_rows
     avg_ms = head_ms / max(n_launch, 1)
-    head_bytes = head_bytes_total / max(n_launch, 1)
+    head_bytes = head_bytes_total / n_launch if n_launch else 0.0
     achieved = head_bytes_total / (head_ms * 1e-3) / 1e9 if n_launch else 0.0
     # measured HBM traffic per launch, averaged like the algorithmic bytes (a
     # launch without rows reads nothing)

@@ -191,8 +191,11 @@ ee_status ee_prefill(ee_model *m, ee_kv_cache *c, int32_t batch, const int32_t *
  * gamma_host: [L-1] thresholds for this step, or NULL for the model's.
  * out_tokens_host, out_exit_layers_host: [batch] greedy tokens and exit layers.
  * dbg: optional diagnostics.  Returns after the outputs are on the host.
- * With a non-NULL hip_stream and no diagnostics, the step's launches are
- * captured once into a HIP graph per (cache, batch) and replayed.
+ * Without diagnostics and without profiling (ee_profile_enable), the step's
+ * kernels are captured into a HIP graph on the first such call for this cache
+ * and batch and replayed by later calls (the graph is released with the cache
+ * or the model); otherwise they are launched one by one.  Both give the same
+ * results bit for bit.
  * Errors: INVALID_ARG, CACHE_FULL (some len_b + 1 > max_seq; nothing runs). */
 ee_status ee_decode_step(ee_model *m, ee_kv_cache *c, int32_t batch,
                          const int32_t *in_tokens_host, const int32_t *forced_exit_host,

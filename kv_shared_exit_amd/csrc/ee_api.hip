@@ -100,6 +100,14 @@ struct ee_model {
   int64_t prof_launches = 0;
   double prof_ms = 0.0;
   int ncaches = 0;
+  // decode steps captured once per (cache, batch) and replayed
+  struct StepGraph {
+    const ee_kv_cache* c;
+    int B;
+    hipGraphExec_t exec;
+  };
+  std::vector<StepGraph> graphs;
+
   std::vector<void*> allocs;
 
   template <typename T>
@@ -451,8 +459,56 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
   HIPCHK(hipGetLastError());
 }
 
+// The kernels of one decode step (no debug outputs) as a HIP graph, captured on
+// first use for this cache and batch, then replayed: the launches' arguments
+// depend only on those (every per-step value lives in device memory), so a
+// replay equals the eager launches.  Profiled steps launch eagerly (the
+// kernel-recorded events of the exit head are not captured into graphs).
+void replay_step(ee_model* m, ee_kv_cache* c, int B, hipStream_t s) {
+  if (m->prof) {
+    enqueue_position(m, c, B, true, true, nullptr, 1, 0, Debug{}, s);
+    return;
+  }
+
+  ee_model::StepGraph* g = nullptr;
+  for (auto& e : m->graphs)
+    if (e.c == c && e.B == B) g = &e;
+  if (!g) {
+    hipGraph_t graph = nullptr;
+    HIPCHK(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+    bool ok = true;
+    try {
+      enqueue_position(m, c, B, true, true, nullptr, 1, 0, Debug{}, s);
+    } catch (const Error&) {
+      ok = false;
+    }
+    const hipError_t ec = hipStreamEndCapture(s, &graph);
+    hipGraphExec_t exec = nullptr;
+    if (ok && ec == hipSuccess && graph) ok = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) == hipSuccess;
+    else ok = false;
+    if (graph) (void)hipGraphDestroy(graph);
+    (void)hipGetLastError();
+    if (!ok) fail(EE_ERR_HIP, "capturing the decode step failed");
+    m->graphs.push_back({c, B, exec});
+    g = &m->graphs.back();
+  }
+  HIPCHK(hipGraphLaunch(g->exec, s));
+}
+
+void drop_graphs(ee_model* m, const ee_kv_cache* c) {
+  for (size_t i = 0; i < m->graphs.size();) {
+    if (!c || m->graphs[i].c == c) {
+      (void)hipGraphExecDestroy(m->graphs[i].exec);
+      m->graphs.erase(m->graphs.begin() + i);
+    } else {
+      ++i;
+    }
+  }
+}
+
 void free_model(ee_model* m) {
   if (!m) return;
+  drop_graphs(m, nullptr);
   for (void* p : m->allocs) (void)hipFree(p);
   for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
   if (m->h_in) (void)hipHostFree(m->h_in);
@@ -762,6 +818,7 @@ ee_status ee_kv_cache_destroy(ee_kv_cache* c) {
   return guard([&] {
     if (!c) return;
     (void)hipStreamSynchronize(c->m->own);
+    drop_graphs(c->m, c);
     if (c->owned) (void)hipFree(c->owned);
     if (c->occ) (void)hipFree(c->occ);
     c->m->ncaches--;
@@ -859,7 +916,11 @@ ee_status ee_decode_step(ee_model* m, ee_kv_cache* c, int32_t batch, const int32
       HIPCHK(hipMemcpyAsync(m->st->forced, m->h_in + kMaxBatch, batch * 4, hipMemcpyHostToDevice, s));
       if (L > 1)
         HIPCHK(hipMemcpyAsync(m->d_gamma, m->h_gamma, (L - 1) * 4, hipMemcpyHostToDevice, s));
-      enqueue_position(m, c, batch, true, true, nullptr, 1, 0, dd, s);
+      if (dbg) {
+        enqueue_position(m, c, batch, true, true, nullptr, 1, 0, dd, s);
+      } else {
+        replay_step(m, c, batch, s);
+      }
       HIPCHK(hipMemcpyAsync(m->h_out, m->st->out_tok, batch * 4, hipMemcpyDeviceToHost, s));
       HIPCHK(hipMemcpyAsync(m->h_out + kMaxBatch, m->st->e, batch * 4, hipMemcpyDeviceToHost, s));
       HIPCHK(hipMemcpyAsync(m->h_gap, m->st->gap, batch * 4, hipMemcpyDeviceToHost, s));

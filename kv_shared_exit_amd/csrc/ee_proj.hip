@@ -38,6 +38,8 @@
 namespace ee {
 
 constexpr int kWaves = kProjThreads / 64;
+// bf16 rows on MFMA (true) or on the vector ALU with dot2 (false)
+constexpr bool kBf16Mfma = false;
 
 template <int EPI>
 struct Ep {
@@ -120,14 +122,21 @@ __device__ __forceinline__ void store_out(const ProjArgs& a, const Work& w, int 
 // copy costs one memory latency.
 constexpr int kItems = kXLdsElems / 8 / kProjThreads;
 
+// LDS row stride of the staged inputs: K plus 16 bytes, so that the MFMA B
+// operand reads (16 rows, 16 bytes each, in groups of 8 lanes) fall in
+// different banks.
+__device__ __forceinline__ int xstride(int K) { return K + 8; }
+
+// The first chunk's ids were put in LDS at kernel start (read with scalar
+// loads, before anything is stored); later chunks read the list here.
 __device__ __forceinline__ void stage_rows(const int32_t* list, int c0, int nb, int* seq) {
-  if (threadIdx.x < 8) seq[threadIdx.x] = list[c0 + min((int)threadIdx.x, nb - 1)];
+  if (c0 > 0 && threadIdx.x < 8) seq[threadIdx.x] = list[c0 + min((int)threadIdx.x, nb - 1)];
 }
 
 __device__ __forceinline__ void stage_x(const ProjArgs& a, const Work& w, int nb, const int* seq, uint16_t* xs) {
   __syncthreads();  // seq is in LDS
   const int k8 = w.K >> 3;
-  const int n = nb * k8;  // items; item i = (row b, column group kk) sits at xs[b*K + kk*8] = xs[i*8]
+  const int n = nb * k8;  // items; item i = (row b, column group kk) goes to xs[b * xstride(K) + kk*8]
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));  // keeps the per-item index math here (not hoisted and held live)
   uint4 v[kItems];
@@ -140,7 +149,10 @@ __device__ __forceinline__ void stage_x(const ProjArgs& a, const Work& w, int nb
 #pragma unroll
   for (int j = 0; j < kItems; ++j) {
     const int i = tid + j * kProjThreads;
-    if (i < n) *(uint4*)&xs[i * 8] = v[j];
+    if (i < n) {
+      const int b = i / k8;
+      *(uint4*)&xs[b * xstride(w.K) + (i - b * k8) * 8] = v[j];
+    }
   }
 }
 
@@ -194,7 +206,7 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, const Work& wk, int
 
   int xo[NB];  // LDS element offset of each input row
 #pragma unroll
-  for (int b = 0; b < NB; ++b) xo[b] = (b < nb ? b : nb - 1) * K;
+  for (int b = 0; b < NB; ++b) xo[b] = (b < nb ? b : nb - 1) * xstride(K);
 
   float lm = -INFINITY, ls = 0.0f;
   Top2 tp{-INFINITY, 0x7fffffff, -INFINITY};
@@ -384,26 +396,32 @@ __device__ __forceinline__ void i4_step(const uint32_t (&word)[P], const uint4& 
   for (int p = 0; p < P; ++p) cg[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack8(word[p]), b8, cg[p], 0, 0, 0);
 }
 
-// Ring depth (blocks of 128 columns in flight per wave) for P matrices and NG
-// scale groups per block: about 4 KB of codes per wave, within 128 VGPRs.
-template <int P, int NG>
-struct I4Ring {
-  static constexpr int D = (P == 2 || NG == 4) ? 2 : 4;
+// Ring depth (blocks of 128 columns in flight per wave): bf16 blocks are 64
+// bytes per lane (four MFMA A operands), int4 blocks 16 bytes of codes plus
+// the scales; within 128 VGPRs.
+template <bool BF, int P, int NG>
+struct MmaRing {
+  static constexpr int D = BF ? (P == 2 ? 1 : 2) : (P == 2 ? 1 : NG == 4 ? 2 : 4);
 };
 
-// Waves per 16-row tile for a range of K columns.
-__host__ __device__ inline int i4_wpt(int K, int D) {
-  const int nfull = K >> 7;
+// Waves sharing a 16-row tile (splitting its 128-column blocks): enough that
+// the tiles of a column range occupy its waves, at most one block per wave.
+__host__ __device__ inline int mma_wpt(int nfull, int ntiles, int nwaves) {
   int w = 1;
-  while (w < kWaves && nfull > w * D) w *= 2;
+  while (w < kWaves && 2 * w <= nfull && (long long)ntiles * w < nwaves) w *= 2;
   return w;
 }
 
-template <int EPI, int NG>
-__device__ __forceinline__ void i4_pass(const ProjArgs& a, const Work& wk, int nb, const int32_t* list, int c0,
-                                        int* seq, uint16_t* xs, float* red) {
+// MFMA pass over 16-row tiles for one weight format: BF true reads the bf16
+// rows straight into the A operands (lane (m, q) holds row m, columns
+// 8q..8q+7 of each 32-column step); BF false unpacks int4 codes (see above).
+// The inputs are the B operand (batch rows padded to 16 with zeros).
+template <int EPI, int NG, bool BF>
+__device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int nb, const int32_t* list, int c0,
+                                         int* seq, uint16_t* xs, float* red) {
   constexpr int P = Ep<EPI>::P;
-  constexpr int D = I4Ring<P, NG>::D;
+  constexpr int D = MmaRing<BF, P, NG>::D;
+  constexpr int SL = BF ? 4 : 1;  // 16-byte loads per block and matrix
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));  // lane-derived values are computed per pass, not held across passes
   const int wave = threadIdx.x >> 6;
@@ -415,8 +433,7 @@ __device__ __forceinline__ void i4_pass(const ProjArgs& a, const Work& wk, int n
   const int gk0 = wk.k0 / G;            // first group of this range
   const int nfull = K >> 7;
   const int ntail = (K & 127) >> 5;     // MFMA steps in the tail
-  const int mpg = G >> 5;               // MFMA steps per group
-  const int wpt = i4_wpt(K, D);
+  const int wpt = mma_wpt(nfull, ntiles, wk.nwg * kWaves);
   const int tpi = kWaves / wpt;         // tiles per workgroup iteration
   const int ws = wave % wpt;            // this wave's K slice of its tile
   const int b0 = ws * nfull / wpt;
@@ -426,51 +443,79 @@ __device__ __forceinline__ void i4_pass(const ProjArgs& a, const Work& wk, int n
   const int ntl = wk.wg < nit ? (nit - 1 - wk.wg) / wk.nwg + 1 : 0;
   const bool bok = m < nb;
   const bool tail_here = ws == wpt - 1 && ntail > 0;
-  const uint16_t* xrow = xs + (bok ? m : 0) * K;
+  const uint16_t* xrow = xs + (bok ? m : 0) * xstride(K);
 
   // weight row of MFMA A row mm of tile tt (the QKV epilogue pairs RoPE rows)
-  auto arow = [&](int tt, int mm) { return EPI == EPI_QKV ? qkv_row(a, tt, mm, 8) : tt * 16 + mm; };
+  // (bf16 rows past N read row N-1; int4 rows are padded to a multiple of 16)
+  auto arow = [&](int tt, int mm) {
+    return EPI == EPI_QKV ? qkv_row(a, tt, mm, 8) : BF ? min(tt * 16 + mm, N - 1) : tt * 16 + mm;
+  };
   auto tile_of = [&](int j) { return (wk.wg + j * wk.nwg) * tpi + wave / wpt; };
-  // where a tile's loads start: code dword offset of this lane's first block
-  // and scale offset of this lane's rows at the first group (-1: no tile)
+  // where a tile's loads start for this lane: bf16 row pointers (first
+  // block of the slice), or int4 code and scale offsets; ok false: no tile
   struct TileAt {
+    const uint16_t* w0;
+    const uint16_t* w1;
     int code, scale;
+    bool ok;
   };
   auto tile_at = [&](int j) {
+    TileAt r{a.wb[0], a.wb[0], 0, 0, false};
     const int t = tile_of(j);
-    if (j >= ntl || t >= ntiles) return TileAt{-1, -1};
-    const int r0 = arow(t, 4 * q);
-    return TileAt{arow(t, m) * ldc + (wk.k0 >> 3) + b0 * 16 + q * 4, ((r0 >> 4) * ngr + gk0 + b0 * NG) * 16 + (r0 & 15)};
+    if (j >= ntl || t >= ntiles) return r;
+    r.ok = true;
+    const int n = arow(t, m);
+    if constexpr (BF) {
+      r.w0 = bf_row(a, wk, n) + b0 * 128 + q * 8;
+      if constexpr (P == 2) r.w1 = a.wb2 + (size_t)n * a.K + wk.k0 + b0 * 128 + q * 8;
+    } else {
+      const int r0 = arow(t, 4 * q);
+      r.code = n * ldc + (wk.k0 >> 3) + b0 * 16 + q * 4;
+      r.scale = ((r0 >> 4) * ngr + gk0 + b0 * NG) * 16 + (r0 & 15);
+    }
+    return r;
   };
 
-  uint4 cw[P][D];
+  uint4 ra[P][D][SL];
   uint2 sc[P][D][NG];
-  // a slot without work loads 64 bytes of the scale array at a place of its
-  // own (one line per wave, spread over the array, so the idle loads of all
-  // waves do not queue on one L2 channel)
-  const uint16_t* idle = a.s4 + (size_t)(((wk.chunk * wk.nwg + wk.wg) * kWaves + wave) * 32 % (ntiles * 16 * ngr));
-  // issue the loads of block kk of the wave's slice of tile `at` into ring slot i
-  auto issue = [&](const TileAt& at, int kk, int i) {
-    const bool real = at.code >= 0 && kk < nbw;
+  // a slot without work loads a line of its own (spread, so the idle loads
+  // of all waves do not queue on one L2 channel) and contributes zero
+  const uint16_t* idle = BF ? a.wb[0] + (size_t)(((wk.chunk * wk.nwg + wk.wg) * kWaves + wave) * 64 % ((size_t)ntiles * 16))
+                            : a.s4 + (size_t)(((wk.chunk * wk.nwg + wk.wg) * kWaves + wave) * 32 % (ntiles * 16 * ngr));
+  // issue the loads of block kk of the wave's slice of tile c (here) or n
+  // into ring slot i (member-wise selects keep everything in registers)
+  auto issue = [&](const TileAt& c, const TileAt& nx, bool here, int kk, int i) {
+    const bool ok = here ? c.ok : nx.ok;
+    const bool real = ok && kk < nbw;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-      const uint32_t* cb = p == 0 ? a.q4 : a.q4b;
-      const uint16_t* sb = p == 0 ? a.s4 : a.s4b;
-      const uint32_t* cp = real ? cb + at.code + kk * 16 : (const uint32_t*)idle;
-      cw[p][i] = ld_stream(cp);
+      if constexpr (BF) {
+        const uint16_t* base = p == 0 ? (here ? c.w0 : nx.w0) : (here ? c.w1 : nx.w1);
+        const uint16_t* src = real ? base + kk * 128 : idle;
 #pragma unroll
-      for (int g = 0; g < NG; ++g) sc[p][i][g] = *(const uint2*)(real ? sb + at.scale + (kk * NG + g) * 16 : idle);
+        for (int st = 0; st < 4; ++st) ra[p][i][st] = ld_stream(src + (real ? st * 32 : 0));
+      } else {
+        const uint32_t* cb = p == 0 ? a.q4 : a.q4b;
+        const uint16_t* sb = p == 0 ? a.s4 : a.s4b;
+        const int code = here ? c.code : nx.code;
+        const int scale = here ? c.scale : nx.scale;
+        ra[p][i][0] = ld_stream(real ? (const void*)(cb + code + kk * 16) : (const void*)idle);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) sc[p][i][g] = *(const uint2*)(real ? sb + scale + (kk * NG + g) * 16 : idle);
+      }
     }
   };
   stage_rows(list, c0, nb, seq);
   TileAt at_cur = tile_at(0);
   if (nfull > 0) {
 #pragma unroll
-    for (int i = 0; i < D; ++i) issue(at_cur, i, i);
+    for (int i = 0; i < D; ++i) issue(at_cur, at_cur, true, i, i);
   }
   stage_x(a, wk, nb, seq, xs);
   __syncthreads();
 
+  float lm = -INFINITY, ls = 0.0f;            // EPI_LSE: running (max, sum exp) of column m
+  Top2 tp{-INFINITY, 0x7fffffff, -INFINITY};  // EPI_ARGMAX
   for (int j = 0; j < ntl; ++j) {
     const int t = tile_of(j);
     const int r0 = arow(t, 4 * q);
@@ -483,91 +528,116 @@ __device__ __forceinline__ void i4_pass(const ProjArgs& a, const Work& wk, int n
       for (int i = 0; i < D; ++i) {
         // straight-line ring body (a branch around it would make the
         // compiler wait for every load in flight): a slot past this wave's
-        // blocks computes on in-bounds data with its scales multiplied by 0
+        // blocks computes on in-bounds data and is multiplied by 0
         const bool live = kk + i < nbw && t < ntiles;
         const float sl = live ? 1.0f : 0.0f;
         const int u = min(b0 + kk + i, max(nfull - 1, 0));
-        constexpr int MPG = 4 / NG;  // MFMA steps per scale group
-        // one matrix at a time (fewer live operands); the 136 * sum(x)
-        // correction of each group is computed with the first
-        f32x4_t c136g[NG];
+        if constexpr (BF) {
 #pragma unroll
-        for (int p = 0; p < P; ++p) {
-          f32x4_t cg = {0.0f, 0.0f, 0.0f, 0.0f};
-          f32x4_t c136 = {0.0f, 0.0f, 0.0f, 0.0f};
+          for (int p = 0; p < P; ++p) {
+            f32x4_t cg = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-          for (int st = 0; st < 4; ++st) {
-            uint4 bv = *(const uint4*)(xrow + u * 128 + 32 * st + 8 * q);
-            if (!bok) bv = make_uint4(0, 0, 0, 0);
-            const bf16x8_t b8 = __builtin_bit_cast(bf16x8_t, bv);
-            if (p == 0) c136 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k136_operand(), b8, c136, 0, 0, 0);
-            cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack8(pick(cw[p][i], st)), b8, cg, 0, 0, 0);
-            if (st % MPG == MPG - 1) {
-              if (p == 0) {
-                c136g[st / MPG] = c136;
-                c136 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int st = 0; st < 4; ++st) {
+              uint4 bv = *(const uint4*)(xrow + u * 128 + 32 * st + 8 * q);
+              if (!bok) bv = make_uint4(0, 0, 0, 0);
+              cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ra[p][i][st]),
+                                                           __builtin_bit_cast(bf16x8_t, bv), cg, 0, 0, 0);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tot[p][e] = fmaf(sl, cg[e], tot[p][e]);
+          }
+        } else {
+          constexpr int MPG = 4 / NG;  // MFMA steps per scale group
+          // one matrix at a time (fewer live operands); the 136 * sum(x)
+          // correction of each group is computed with the first
+          f32x4_t c136g[NG];
+#pragma unroll
+          for (int p = 0; p < P; ++p) {
+            f32x4_t cg = {0.0f, 0.0f, 0.0f, 0.0f};
+            f32x4_t c136 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+              uint4 bv = *(const uint4*)(xrow + u * 128 + 32 * st + 8 * q);
+              if (!bok) bv = make_uint4(0, 0, 0, 0);
+              const bf16x8_t b8 = __builtin_bit_cast(bf16x8_t, bv);
+              if (p == 0) c136 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k136_operand(), b8, c136, 0, 0, 0);
+              cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack8(pick(ra[p][i][0], st)), b8, cg, 0, 0, 0);
+              if (st % MPG == MPG - 1) {
+                if (p == 0) {
+                  c136g[st / MPG] = c136;
+                  c136 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                }
+                i4_group_scale(sc[p][i][st / MPG], sl, cg, c136g[st / MPG], tot[p]);
+                cg = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
               }
-              i4_group_scale(sc[p][i][st / MPG], sl, cg, c136g[st / MPG], tot[p]);
-              cg = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
             }
           }
         }
         // refill with the block D ahead, in this tile or the next (a select,
         // not a branch, so the loads stay unconditional)
         const bool here = kk + i + D < nbp;
-        issue(here ? at_cur : at_nxt, here ? kk + i + D : kk + i + D - nbp, i);
+        issue(at_cur, at_nxt, here, here ? kk + i + D : kk + i + D - nbp, i);
       }
     }
-    if (tail_here && t < ntiles) {
-      f32x4_t cg[P];
-      f32x4_t c136 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int p = 0; p < P; ++p) cg[p] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    if (tail_here && t < ntiles) {  // K mod 128: steps of 32 columns, last wave of the tile
       for (int st = 0; st < ntail; ++st) {
         const int ka = nfull * 128 + 32 * st;
         uint4 bv = *(const uint4*)(xrow + ka + 8 * q);
         if (!bok) bv = make_uint4(0, 0, 0, 0);
-        uint32_t word[P];
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-          const uint32_t* cb = p == 0 ? a.q4 : a.q4b;
-          word[p] = cb[(size_t)arow(t, m) * ldc + ((wk.k0 + ka) >> 3) + q];
-        }
-        i4_step<P>(word, bv, cg, c136);
-        if (st % mpg == mpg - 1) {
+        const bf16x8_t b8 = __builtin_bit_cast(bf16x8_t, bv);
+        if constexpr (BF) {
 #pragma unroll
           for (int p = 0; p < P; ++p) {
-            const uint16_t* sb = p == 0 ? a.s4 : a.s4b;
-            const uint2 sv = *(const uint2*)(sb + ((size_t)(r0 >> 4) * ngr + gk0 + ka / G) * 16 + (r0 & 15));
-            i4_group_scale(sv, 1.0f, cg[p], c136, tot[p]);
-            cg[p] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            const int n = arow(t, m);
+            const uint16_t* wr = p == 0 ? bf_row(a, wk, n) : a.wb2 + (size_t)n * a.K + wk.k0;
+            const uint4 av = *(const uint4*)(wr + ka + 8 * q);
+            tot[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), b8, tot[p], 0, 0, 0);
           }
-          c136 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        } else {
+          f32x4_t c136 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k136_operand(), b8, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                 0, 0, 0);
+#pragma unroll
+          for (int p = 0; p < P; ++p) {
+            const uint32_t* cb = p == 0 ? a.q4 : a.q4b;
+            const uint16_t* sb = p == 0 ? a.s4 : a.s4b;
+            const uint32_t word = cb[(size_t)arow(t, m) * ldc + ((wk.k0 + ka) >> 3) + q];
+            const f32x4_t cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack8(word), b8,
+                                                                       f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+            // scaled per 32-column step (every step lies in one group)
+            const uint2 sv = *(const uint2*)(sb + ((size_t)(r0 >> 4) * ngr + gk0 + ka / G) * 16 + (r0 & 15));
+            i4_group_scale(sv, 1.0f, cg, c136, tot[p]);
+          }
         }
       }
     }
     at_cur = at_nxt;
-    // sum the K slices of each tile in slice order; wave (tile index) tt of
-    // the iteration finishes tile tt
+    // with several waves per tile, sum their K slices in slice order; wave
+    // (tile index) tt of the iteration finishes tile tt
     float vals[P][4];
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vals[p][i] = tot[p][i];
     const bool fin = wave < tpi;
+    if (wpt > 1) {
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      float* rw = red + (wave * 64 + lane) * 4;
-      rw[0] = tot[p][0];
-      rw[1] = tot[p][1];
-      rw[2] = tot[p][2];
-      rw[3] = tot[p][3];
-      __syncthreads();
-      if (fin) {
+      for (int p = 0; p < P; ++p) {
+        float* rw = red + (wave * 64 + lane) * 4;
+        rw[0] = tot[p][0];
+        rw[1] = tot[p][1];
+        rw[2] = tot[p][2];
+        rw[3] = tot[p][3];
+        __syncthreads();
+        if (fin) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float s = 0.0f;
-          for (int ww = 0; ww < wpt; ++ww) s += red[((wave * wpt + ww) * 64 + lane) * 4 + i];
-          vals[p][i] = s;
+          for (int i = 0; i < 4; ++i) {
+            float s = 0.0f;
+            for (int ww = 0; ww < wpt; ++ww) s += red[((wave * wpt + ww) * 64 + lane) * 4 + i];
+            vals[p][i] = s;
+          }
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
     if (!fin) continue;
     const int tf = (wk.wg + j * wk.nwg) * tpi + wave;  // the tile this wave finishes
@@ -588,47 +658,117 @@ __device__ __forceinline__ void i4_pass(const ProjArgs& a, const Work& wk, int n
     for (int i = 0; i < 4; ++i) {
       const int n = tf * 16 + 4 * q + i;
       if (n >= N) continue;
-      if constexpr (EPI == EPI_SWIGLU)
-        ((uint16_t*)a.y)[(size_t)seq[m] * a.y_stride + n] = (uint16_t)f2bf(silu_mul(vals[0][i], vals[P - 1][i]));
-      else
-        store_out<EPI>(a, wk, seq[m], n, vals[0][i]);
+      const float v = vals[0][i];
+      if constexpr (EPI == EPI_SWIGLU) {
+        ((uint16_t*)a.y)[(size_t)seq[m] * a.y_stride + n] = (uint16_t)f2bf(silu_mul(v, vals[P - 1][i]));
+      } else if constexpr (EPI == EPI_LSE) {
+        lse_merge(lm, ls, v, 1.0f);
+      } else if constexpr (EPI == EPI_ARGMAX) {
+        if (a.logits) a.logits[(size_t)seq[m] * a.logits_stride + n] = v;
+        if (v > tp.v1) {  // rows arrive in increasing order within a lane: ties keep the lowest
+          tp.v2 = tp.v1;
+          tp.v1 = v;
+          tp.i1 = n;
+        } else if (v > tp.v2) {
+          tp.v2 = v;
+        }
+      } else {
+        store_out<EPI>(a, wk, seq[m], n, v);
+      }
+    }
+  }
+
+  if constexpr (EPI == EPI_LSE || EPI == EPI_ARGMAX) {
+    // per column m: merge the 4 lanes (q) of every wave, waves in order
+    __syncthreads();  // the tile reductions are done with red
+    float* rw = red + (wave * 64 + lane) * 4;
+    if constexpr (EPI == EPI_LSE) {
+      rw[0] = lm;
+      rw[1] = ls;
+    } else {
+      rw[0] = tp.v1;
+      rw[1] = __int_as_float(tp.i1);
+      rw[2] = tp.v2;
+    }
+    __syncthreads();
+    const int tid = threadIdx.x;
+    if (tid < nb) {
+      float* out = a.part + ((size_t)blockIdx.x * kMaxBatch + (c0 + tid)) * 4;
+      if constexpr (EPI == EPI_LSE) {
+        float mm = -INFINITY, s = 0.0f;
+        for (int ww = 0; ww < kWaves; ++ww)
+          for (int qq = 0; qq < 4; ++qq) {
+            const float* src = red + (ww * 64 + qq * 16 + tid) * 4;
+            lse_merge(mm, s, src[0], src[1]);
+          }
+        out[0] = mm;
+        out[1] = s;
+      } else {
+        Top2 best{-INFINITY, 0x7fffffff, -INFINITY};
+        for (int ww = 0; ww < kWaves; ++ww)
+          for (int qq = 0; qq < 4; ++qq) {
+            const float* src = red + (ww * 64 + qq * 16 + tid) * 4;
+            top2_merge(best, Top2{src[0], __float_as_int(src[1]), src[2]});
+          }
+        out[0] = best.v1;
+        out[1] = __int_as_float(best.i1);
+        out[2] = best.v2;
+      }
     }
   }
 }
 
 template <int EPI, int NG>
 __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[kXLdsElems];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kXLdsElems + 8 * 8];
   __shared__ __attribute__((aligned(16))) float red[kWaves * 64 * 4];
-  __shared__ int seq[8];  // sequence ids of the staged rows
+  __shared__ int seqc[8];  // sequence ids of the staged rows of a later chunk
   Work wk;
   wk.nwg = gridDim.x / a.nkc;
   wk.chunk = blockIdx.x / wk.nwg;
   wk.wg = blockIdx.x - wk.chunk * wk.nwg;
   wk.k0 = wk.chunk * a.kc;
   wk.K = min(a.kc, a.K - wk.k0);
+  // row counts and the first 8 ids of both lists, read before anything is
+  // stored (so the compiler uses scalar loads); a chunk's ids must be padded
+  // with its last id, which the passes' staging relies on
+  __shared__ int seq0[2][8];
+  const int n_bf = a.cnt_bf ? min(max(*a.cnt_bf, 0), kMaxBatch) : 0;
+  const int n_i4 = a.cnt_i4 ? min(max(*a.cnt_i4, 0), kMaxBatch) : 0;
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      seq0[0][e] = n_bf > 0 ? a.list_bf[min(e, n_bf - 1)] : 0;
+      seq0[1][e] = n_i4 > 0 ? a.list_i4[min(e, n_i4 - 1)] : 0;
+    }
+  }
   for (int fmt = 0; fmt < 2; ++fmt) {
     if constexpr (EPI == EPI_LSE || EPI == EPI_ARGMAX || EPI == EPI_BF16) {
       if (fmt == 1) break;  // these run on backbone rows only
     }
-    const int32_t* cntp = fmt ? a.cnt_i4 : a.cnt_bf;
-    const int n = cntp ? min(max(*cntp, 0), kMaxBatch) : 0;
+    const int n = fmt ? n_i4 : n_bf;
     const int32_t* list = fmt ? a.list_i4 : a.list_bf;
+
     for (int c0 = 0; c0 < n; c0 += 8) {
       const int nb = min(8, n - c0);
       __syncthreads();  // the previous pass is done with xs, red and seq
+      int* seq = c0 == 0 ? seq0[fmt] : seqc;
       if (fmt == 0) {
-        if (nb == 1)
-          bf16_pass<EPI, 1>(a, wk, nb, list, c0, seq, xs, red);
-        else if (nb == 2)
-          bf16_pass<EPI, 2>(a, wk, nb, list, c0, seq, xs, red);
-        else if (nb <= 4)
-          bf16_pass<EPI, 4>(a, wk, nb, list, c0, seq, xs, red);
-        else
-          bf16_pass<EPI, 8>(a, wk, nb, list, c0, seq, xs, red);
+        if constexpr (kBf16Mfma) {
+          mma_pass<EPI, NG, true>(a, wk, nb, list, c0, seq, xs, red);
+        } else {
+          if (nb == 1)
+            bf16_pass<EPI, 1>(a, wk, nb, list, c0, seq, xs, red);
+          else if (nb == 2)
+            bf16_pass<EPI, 2>(a, wk, nb, list, c0, seq, xs, red);
+          else if (nb <= 4)
+            bf16_pass<EPI, 4>(a, wk, nb, list, c0, seq, xs, red);
+          else
+            bf16_pass<EPI, 8>(a, wk, nb, list, c0, seq, xs, red);
+        }
       } else {
         if constexpr (EPI == EPI_PART || EPI == EPI_SWIGLU || EPI == EPI_QKV)
-          i4_pass<EPI, NG>(a, wk, nb, list, c0, seq, xs, red);
+          mma_pass<EPI, NG, false>(a, wk, nb, list, c0, seq, xs, red);
       }
     }
   }

@@ -102,7 +102,7 @@ def test_cache_without_tracking_has_no_occupancy(api):
         m.close()
 
 
-def _run(api, sh, w, mode, gamma, B_, P, steps, forced=None, graph=False):
+def _run(api, sh, w, mode, gamma, B_, P, steps, forced=None, graph=False, kv=None):
     import torch
     dev = api.upload_weights(w)
     m = api.Model(sh, dev, gamma=gamma, exit_mode=mode, max_batch=B_, max_positions=P + steps + 1)
@@ -117,6 +117,10 @@ def _run(api, sh, w, mode, gamma, B_, P, steps, forced=None, graph=False):
             t, e = api.decode_step(m, c, B_, forced=None if forced is None else forced(s),
                                    stream=st, debug=dbg)
             out.append((t.copy(), e.copy(), None if dbg is None else dbg["logits"].copy()))
+        if kv is not None:
+            for l in range(1, sh.n_layers + 1):
+                for b in range(B_):
+                    kv.append(c.read(l, b, 0, P + steps))
     finally:
         c.close()
         m.close()
@@ -177,3 +181,21 @@ def test_rollback_then_replay_is_identical(api):
     finally:
         c.close()
         m.close()
+
+
+def test_graph_replay_equals_eager(api):
+    """Steps without debug outputs replay a captured graph; with them the kernels
+    are launched one by one.  Both must give the same tokens, exits and K/V."""
+    from kv_shared_exit_amd import _binding as B
+    sh = MID
+    w = synth.make_weights(sh, 8, alpha=np.full(sh.n_layers - 1, 3000.0))
+    forced = lambda s: np.random.default_rng(100 + s).integers(0, sh.n_layers + 1, 5).astype(np.int32)
+    kva, kvb = [], []
+    a = _run(api, sh, w, B.EE_EXIT_INT4, 0.75, 5, 6, 5, forced=forced, graph=False, kv=kva)
+    b = _run(api, sh, w, B.EE_EXIT_INT4, 0.75, 5, 6, 5, forced=forced, graph=True, kv=kvb)
+    for (ta, ea, _), (tb, eb, _) in zip(a, b):
+        np.testing.assert_array_equal(ta, tb)
+        np.testing.assert_array_equal(ea, eb)
+    for (ka, va), (kb, vb) in zip(kva, kvb):
+        np.testing.assert_array_equal(ka, kb)
+        np.testing.assert_array_equal(va, vb)
