@@ -315,6 +315,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       a.H = H;
       a.Hkv = Hkv;
       a.hd = hd;
+      a.hd_log2 = __builtin_ctz(hd);
       a.S = c->S;
       launch_proj(EPI_QKV, a, kNwg, B, s);
     }

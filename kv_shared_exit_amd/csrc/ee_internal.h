@@ -58,6 +58,8 @@ struct ProjArgs {
   uint16_t* Kl; uint16_t* Vl;                     // layer base [Bmax][Hkv][S][hd]
   uint8_t* occ_l;                                 // [Bmax][S] write counters, or null
   int H, Hkv, hd, S;
+  int hd_log2;                                    // log2(hd)
+  int nwg_r;                                      // workgroups per column range (set by launch_proj)
 };
 
 struct AttnArgs {

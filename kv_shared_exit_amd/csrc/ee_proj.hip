@@ -59,11 +59,13 @@ struct Work {
 // (RoPE rotates element i with element i + hd/2), so both halves of every pair
 // finish in the same wave.  A tile of 2*half rows covers c0 .. c0+half-1 and
 // their partners.
-__device__ __forceinline__ int qkv_row(const ProjArgs& a, int t, int m, int half) {
-  const int per_head = a.hd / (2 * half);
-  const int head = t / per_head;
-  const int c0 = (t - head * per_head) * half;
-  return head * a.hd + (m >= half ? a.hd / 2 : 0) + c0 + (m % half);
+template <int HALF>
+__device__ __forceinline__ int qkv_row(const ProjArgs& a, int t, int m) {
+  constexpr int L2 = HALF == 1 ? 1 : HALF == 2 ? 2 : HALF == 4 ? 3 : 4;  // log2(2 * HALF)
+  const int sh = a.hd_log2 - L2;  // log2(tiles per head)
+  const int head = t >> sh;
+  const int c0 = (t & ((1 << sh) - 1)) * HALF;
+  return (head << a.hd_log2) + (m >= HALF ? a.hd / 2 : 0) + c0 + (m % HALF);
 }
 
 // QKV epilogue for row n of sequence seq: v is this row's value, u its RoPE
@@ -71,8 +73,8 @@ __device__ __forceinline__ int qkv_row(const ProjArgs& a, int t, int m, int half
 // and rounded again; k and v go to the shared cache slot of the position.
 __device__ __forceinline__ void qkv_out(const ProjArgs& a, int seq, int n, float v, float u) {
   const int hd = a.hd, half = hd >> 1;
-  const int head = n / hd;
-  const int e = n - head * hd;
+  const int head = n >> a.hd_log2;
+  const int e = n & (hd - 1);
   const int pos = a.lens[seq];
   if (head < a.H + a.Hkv) {
     const int i = e < half ? e : e - half;
@@ -139,18 +141,26 @@ __device__ __forceinline__ void stage_x(const ProjArgs& a, const Work& w, int nb
   const int n = nb * k8;  // items; item i = (row b, column group kk) goes to xs[b * xstride(K) + kk*8]
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));  // keeps the per-item index math here (not hoisted and held live)
+  // row of item i: i / k8 from a float reciprocal, corrected to the exact quotient
+  const float inv = 1.0f / (float)k8;
+  auto row_of = [&](int i) {
+    int b = (int)((float)i * inv);
+    b += (b + 1) * k8 <= i;
+    b -= b * k8 > i;
+    return b;
+  };
   uint4 v[kItems];
 #pragma unroll
   for (int j = 0; j < kItems; ++j) {
     const int i = min(tid + j * kProjThreads, n - 1);
-    const int b = i / k8;
+    const int b = row_of(i);
     v[j] = *(const uint4*)(a.x + (size_t)seq[b] * a.x_stride + w.k0 + (i - b * k8) * 8);
   }
 #pragma unroll
   for (int j = 0; j < kItems; ++j) {
     const int i = tid + j * kProjThreads;
     if (i < n) {
-      const int b = i / k8;
+      const int b = row_of(i);
       *(uint4*)&xs[b * xstride(w.K) + (i - b * k8) * 8] = v[j];
     }
   }
@@ -221,7 +231,7 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, const Work& wk, int
   auto set_rows = [&](int tt) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int n = EPI == EPI_QKV ? qkv_row(a, tt, r, R / 2) : min(tt * R + r, N - 1);
+      const int n = EPI == EPI_QKV ? qkv_row<R / 2>(a, tt, r) : min(tt * R + r, N - 1);
       w[r] = bf_row(a, wk, n) + lane * 8;
       if constexpr (P == 2) w[R + r] = a.wb2 + (size_t)n * a.K + wk.k0 + lane * 8;
     }
@@ -274,7 +284,7 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, const Work& wk, int
     }
     XRed<V, 0>::run(acc, lane);
     const float v = acc[0];
-    const int n = EPI == EPI_QKV ? qkv_row(a, t, rr, R / 2) : n0 + (rr % R);
+    const int n = EPI == EPI_QKV ? qkv_row<R / 2>(a, t, rr) : n0 + (rr % R);
     if constexpr (EPI == EPI_QKV) {
       const float u = __shfl_xor(v, 1);  // the RoPE partner row sits in the partner lane
       if (lane_ok) qkv_out(a, seq[bsel], n, v, u);
@@ -426,7 +436,10 @@ __device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int 
   asm volatile("" : "+v"(lane));  // lane-derived values are computed per pass, not held across passes
   const int wave = threadIdx.x >> 6;
   const int m = lane & 15, q = lane >> 4;
-  const int N = a.N, K = wk.K, G = a.G;
+  // (no integer division below: the group size follows from NG, the wave
+  // split is a power of two; each wave repeats this setup)
+  constexpr int G = 128 / NG;
+  const int N = a.N, K = wk.K;
   const int ntiles = (N + 15) >> 4;
   const int ldc = a.K >> 3;             // dwords per code row
   const int ngr = a.K / G;              // scale groups per row of the whole matrix
@@ -434,13 +447,13 @@ __device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int 
   const int nfull = K >> 7;
   const int ntail = (K & 127) >> 5;     // MFMA steps in the tail
   const int wpt = mma_wpt(nfull, ntiles, wk.nwg * kWaves);
-  const int tpi = kWaves / wpt;         // tiles per workgroup iteration
-  const int ws = wave % wpt;            // this wave's K slice of its tile
-  const int b0 = ws * nfull / wpt;
-  const int nbw = (ws + 1) * nfull / wpt - b0;
-  const int nbp = ((nfull + wpt - 1) / wpt + D - 1) / D * D;  // ring rounds per tile, same for all waves
-  const int nit = (ntiles + tpi - 1) / tpi;                    // workgroup iterations in the range
-  const int ntl = wk.wg < nit ? (nit - 1 - wk.wg) / wk.nwg + 1 : 0;
+  const int lw = __builtin_ctz(wpt);
+  const int tpi = kWaves >> lw;         // tiles per workgroup iteration
+  const int ws = wave & (wpt - 1);      // this wave's K slice of its tile
+  const int b0 = (ws * nfull) >> lw;
+  const int nbw = (((ws + 1) * nfull) >> lw) - b0;
+  const int nbp = (((nfull + wpt - 1) >> lw) + D - 1) / D * D;  // ring rounds per tile, same for all waves
+  const int nit = (ntiles + tpi - 1) >> (3 - lw);              // workgroup iterations in the range
   const bool bok = m < nb;
   const bool tail_here = ws == wpt - 1 && ntail > 0;
   const uint16_t* xrow = xs + (bok ? m : 0) * xstride(K);
@@ -448,9 +461,10 @@ __device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int 
   // weight row of MFMA A row mm of tile tt (the QKV epilogue pairs RoPE rows)
   // (bf16 rows past N read row N-1; int4 rows are padded to a multiple of 16)
   auto arow = [&](int tt, int mm) {
-    return EPI == EPI_QKV ? qkv_row(a, tt, mm, 8) : BF ? min(tt * 16 + mm, N - 1) : tt * 16 + mm;
+    return EPI == EPI_QKV ? qkv_row<8>(a, tt, mm) : BF ? min(tt * 16 + mm, N - 1) : tt * 16 + mm;
   };
-  auto tile_of = [&](int j) { return (wk.wg + j * wk.nwg) * tpi + wave / wpt; };
+  auto tile_of = [&](int j) { return (wk.wg + j * wk.nwg) * tpi + (wave >> lw); };
+  auto has_iter = [&](int j) { return wk.wg + j * wk.nwg < nit; };
   // where a tile's loads start for this lane: bf16 row pointers (first
   // block of the slice), or int4 code and scale offsets; ok false: no tile
   struct TileAt {
@@ -462,7 +476,7 @@ __device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int 
   auto tile_at = [&](int j) {
     TileAt r{a.wb[0], a.wb[0], 0, 0, false};
     const int t = tile_of(j);
-    if (j >= ntl || t >= ntiles) return r;
+    if (!has_iter(j) || t >= ntiles) return r;
     r.ok = true;
     const int n = arow(t, m);
     if constexpr (BF) {
@@ -480,8 +494,10 @@ __device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int 
   uint2 sc[P][D][NG];
   // a slot without work loads a line of its own (spread, so the idle loads
   // of all waves do not queue on one L2 channel) and contributes zero
-  const uint16_t* idle = BF ? a.wb[0] + (size_t)(((wk.chunk * wk.nwg + wk.wg) * kWaves + wave) * 64 % ((size_t)ntiles * 16))
-                            : a.s4 + (size_t)(((wk.chunk * wk.nwg + wk.wg) * kWaves + wave) * 32 % (ntiles * 16 * ngr));
+  const int gwave = (wk.chunk * wk.nwg + wk.wg) * kWaves + wave;
+  const int ispan = BF ? min(ntiles * 16, N * a.K) : ntiles * 16 * ngr;  // elements that may be read
+  const int imask = (1 << (31 - __builtin_clz(ispan))) - 1;              // power of two <= ispan, minus 1
+  const uint16_t* idle = (BF ? a.wb[0] : a.s4) + ((gwave * (BF ? 64 : 32)) & imask);
   // issue the loads of block kk of the wave's slice of tile c (here) or n
   // into ring slot i (member-wise selects keep everything in registers)
   auto issue = [&](const TileAt& c, const TileAt& nx, bool here, int kk, int i) {
@@ -516,7 +532,7 @@ __device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int 
 
   float lm = -INFINITY, ls = 0.0f;            // EPI_LSE: running (max, sum exp) of column m
   Top2 tp{-INFINITY, 0x7fffffff, -INFINITY};  // EPI_ARGMAX
-  for (int j = 0; j < ntl; ++j) {
+  for (int j = 0; has_iter(j); ++j) {
     const int t = tile_of(j);
     const int r0 = arow(t, 4 * q);
     const TileAt at_nxt = tile_at(j + 1);
@@ -724,24 +740,39 @@ __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a)
   __shared__ __attribute__((aligned(16))) float red[kWaves * 64 * 4];
   __shared__ int seqc[8];  // sequence ids of the staged rows of a later chunk
   Work wk;
-  wk.nwg = gridDim.x / a.nkc;
-  wk.chunk = blockIdx.x / wk.nwg;
+  wk.nwg = a.nwg_r;
+  wk.chunk = 0;
+  while ((wk.chunk + 1) * wk.nwg <= (int)blockIdx.x) ++wk.chunk;
   wk.wg = blockIdx.x - wk.chunk * wk.nwg;
   wk.k0 = wk.chunk * a.kc;
   wk.K = min(a.kc, a.K - wk.k0);
-  // row counts and the first 8 ids of both lists, read before anything is
-  // stored (so the compiler uses scalar loads); a chunk's ids must be padded
-  // with its last id, which the passes' staging relies on
+  // Row counts and the first 8 ids of both lists, all read at once before
+  // anything is stored (scalar loads that depend only on the arguments: no
+  // chain of dependent loads before the first weights are requested).  A
+  // chunk's ids are padded with its last id, which the staging relies on.
   __shared__ int seq0[2][8];
   const int n_bf = a.cnt_bf ? min(max(*a.cnt_bf, 0), kMaxBatch) : 0;
   const int n_i4 = a.cnt_i4 ? min(max(*a.cnt_i4, 0), kMaxBatch) : 0;
+  int lb[8], li[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    lb[e] = a.list_bf ? a.list_bf[e] : 0;
+    li[e] = a.list_i4 ? a.list_i4[e] : 0;
+  }
   if (threadIdx.x == 0) {
+    int pb = lb[0], pi = li[0];  // the last id of each list's first chunk
+#pragma unroll
+    for (int e = 1; e < 8; ++e) {
+      pb = e < n_bf ? lb[e] : pb;
+      pi = e < n_i4 ? li[e] : pi;
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      seq0[0][e] = n_bf > 0 ? a.list_bf[min(e, n_bf - 1)] : 0;
-      seq0[1][e] = n_i4 > 0 ? a.list_i4[min(e, n_i4 - 1)] : 0;
+      seq0[0][e] = e < n_bf ? lb[e] : pb;
+      seq0[1][e] = e < n_i4 ? li[e] : pi;
     }
   }
+  bool first = true;  // the first pass needs no barrier: its staging waits for seq0
   for (int fmt = 0; fmt < 2; ++fmt) {
     if constexpr (EPI == EPI_LSE || EPI == EPI_ARGMAX || EPI == EPI_BF16) {
       if (fmt == 1) break;  // these run on backbone rows only
@@ -751,7 +782,8 @@ __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a)
 
     for (int c0 = 0; c0 < n; c0 += 8) {
       const int nb = min(8, n - c0);
-      __syncthreads();  // the previous pass is done with xs, red and seq
+      if (!first) __syncthreads();  // the previous pass is done with xs, red and seq
+      first = false;
       int* seq = c0 == 0 ? seq0[fmt] : seqc;
       if (fmt == 0) {
         if constexpr (kBf16Mfma) {
@@ -820,6 +852,9 @@ int launch_proj(int epi, const ProjArgs& a0, int nwg, int batch, hipStream_t s, 
   } else if (!proj_fits(a.K, batch)) {
     throw std::logic_error("projection input too wide for the stage");
   }
+  a.nwg_r = g / a.nkc;
+  if (epi == EPI_QKV && (a.hd < 32 || (a.hd & (a.hd - 1)) || (1 << a.hd_log2) != a.hd))
+    throw std::logic_error("QKV epilogue needs a power-of-two head_dim >= 32 and its log2");
   switch (epi) {
     case EPI_BF16: launch_ng<EPI_BF16>(a, g, s, ev0, ev1); break;
     case EPI_PART: launch_ng<EPI_PART>(a, g, s, ev0, ev1); break;
