@@ -1,0 +1,182 @@
+"""GPU checks at the benchmark's full size: the 8B decoder shape (32 layers,
+d 4096, 32/8 heads, F 14336, V 128256, int4 G128 copies) with batch 8, the
+launch configuration bench.py times.
+
+The oracle cannot run whole generations at this size, so the comparisons are
+sampled (one sequence, a few positions; by batch independence a sequence run
+alone by the oracle equals the same sequence inside the GPU's batch), and the
+rest are properties that hold at any size:
+  * full depth (gamma > 1, nobody exits): sequence 0's prefill logits, its
+    decode step's hidden state after every layer, logits, token and its K/V
+    against the oracle run without exit heads (heads cannot change a step in
+    which nobody exits);
+  * exit after layer 1 (every row runs layers 2..L on the int4 copies): the
+    hidden states after layers 1 and 2 against the oracle's first two layers
+    (the later layers do not influence them);
+  * int4 copies bit-exact for sampled rows of sampled layers;
+  * at the benchmark's prompt length: graph replay equals launching the
+    kernels one by one (tokens, exit layers, K/V), and every written KV slot
+    was written exactly once.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import model as om
+from oracle.numerics import from_bf16_bits
+from oracle.quant import quantize_int4
+
+pytestmark = pytest.mark.gpu
+
+SH = synth.LLAMA8B
+B = 8
+TOL = 2e-2
+
+
+def maxrel(a, r):
+    a = np.asarray(a, np.float64)
+    r = np.asarray(r, np.float64)
+    return float(np.abs(a - r).max() / max(np.abs(r).max(), 1e-30))
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_shared_exit_amd import api
+    wl = synth.workload("8b")
+    w = synth.make_weights(SH, wl.seed_weights, alpha=synth.load_alpha(wl))
+    dev = api.upload_weights(w)
+    torch.cuda.synchronize()
+    yield api, w, dev
+    del dev
+
+
+def _prompts(P):
+    return np.random.default_rng(77).integers(0, SH.vocab, (B, P)).astype(np.int32)
+
+
+def test_full_depth_sequence_matches_oracle(env):
+    api, w, dev = env
+    P = 3
+    prompts = _prompts(P)
+    model = api.Model(SH, dev, gamma=2.0, max_batch=B, max_positions=P + 2)
+    cache = api.KVCache(model, B, P + 2, track=True)
+    try:
+        tg, lg = api.prefill(model, cache, prompts, logits=True)
+        dbg = {"logits": None, "hidden": None, "p": None}
+        tok_in = tg.copy()
+        t1, e1 = api.decode_step(model, cache, B, tokens=tok_in, debug=dbg)
+        assert np.all(e1 == SH.n_layers)
+        k_gpu = {l: cache.read(l, 0, 0, P + 1) for l in (1, 16, 32)}
+    finally:
+        cache.close()
+        model.close()
+
+    orc = om.OracleModel(SH, w, cache_f64=True)   # widened once, used by both passes
+    oc = om.KVCache(SH, 1, P + 2)
+    to, info = om.prefill(orc, oc, prompts[:1])
+    e = maxrel(lg[0], info["logits"][0])
+    assert e <= TOL, f"prefill logits maxrel {e:.3g}"
+    band = max(1e-2, 2 * float(np.abs(lg[0].astype(np.float64) - info["logits"][0]).max()))
+    if info["gap"][0] > band:
+        assert tg[0] == to[0]
+    t2, e2, io = om.decode_step(orc, oc, tok_in[:1], trace=True, heads=False)
+    for l in range(SH.n_layers + 1):
+        e = maxrel(dbg["hidden"][0, l], io["hidden"][0, l])
+        assert e <= TOL, f"hidden after layer {l}: maxrel {e:.3g}"
+    e = maxrel(dbg["logits"][0], io["logits"][0])
+    assert e <= TOL, f"decode logits maxrel {e:.3g}"
+    band = max(1e-2, 2 * float(np.abs(dbg["logits"][0].astype(np.float64) - io["logits"][0]).max()))
+    if io["gap"][0] > band:
+        assert t1[0] == t2[0]
+    for l, (k, v) in k_gpu.items():
+        kr = oc.K[l - 1, 0, :, :P + 1].transpose(1, 0, 2)
+        vr = oc.V[l - 1, 0, :, :P + 1].transpose(1, 0, 2)
+        assert maxrel(from_bf16_bits(k), kr) <= TOL and maxrel(from_bf16_bits(v), vr) <= TOL, f"KV layer {l}"
+
+
+def test_exit_after_layer_one_runs_int4_copies(env):
+    api, w, dev = env
+    P = 2
+    prompts = _prompts(P)
+    model = api.Model(SH, dev, gamma=0.75, max_batch=B, max_positions=P + 2)
+    cache = api.KVCache(model, B, P + 2, track=True)
+    try:
+        tg = api.prefill(model, cache, prompts)
+        dbg = {"hidden": None, "p": None}
+        t1, e1 = api.decode_step(model, cache, B, tokens=tg, forced=np.ones(B, np.int32), debug=dbg)
+        np.testing.assert_array_equal(e1, np.ones(B, np.int32))
+        assert np.all(np.isnan(dbg["p"][:, 1:])), "heads after the exit layer must not run"
+    finally:
+        cache.close()
+        model.close()
+    # the oracle's first two layers: layer 1 on the backbone, layer 2 on its int4 copy
+    sh2 = dataclasses.replace(SH, n_layers=2)
+    w2 = {"tok_emb": w["tok_emb"], "lm_head": w["lm_head"], "final_norm": w["final_norm"],
+          "layers": w["layers"][:2]}
+    orc = om.OracleModel(sh2, w2, cache_f64=False)
+    oc = om.KVCache(sh2, 1, P + 2)
+    om.prefill(orc, oc, prompts[:1])
+    _, eo, io = om.decode_step(orc, oc, tg[:1], forced=[1], trace=True)
+    assert eo[0] == 1
+    for l in range(3):
+        e = maxrel(dbg["hidden"][0, l], io["hidden"][0, l])
+        assert e <= TOL, f"hidden after layer {l}: maxrel {e:.3g}"
+
+
+def test_int4_copies_sampled_rows_bit_exact(env):
+    api, w, dev = env
+    model = api.Model(SH, dev, max_batch=B, max_positions=4)
+    try:
+        rng = np.random.default_rng(5)
+        for l in (2, 17, 32):
+            for name in ("wq", "wv", "wo", "w_gate", "w_down"):
+                N, K = SH.linear_shapes()[name]
+                for row0 in sorted(set(rng.integers(0, N - 16, 3).tolist() + [N - 16])):
+                    codes, scales = model.exit_weights(l, name, row0, 16)
+                    ref = from_bf16_bits(w["layers"][l - 1][name][row0:row0 + 16])
+                    q, s = quantize_int4(ref, SH.group)
+                    np.testing.assert_array_equal(codes, q, err_msg=f"layer {l} {name} rows {row0}..")
+                    np.testing.assert_array_equal(from_bf16_bits(scales), s)
+    finally:
+        model.close()
+
+
+def test_bench_configuration_graph_equals_eager_and_slots_written_once(env):
+    import torch
+    api, w, dev = env
+    wl = synth.workload("8b")
+    P, steps = wl.prompt_len, 3
+    prompts = synth.make_prompts(wl)
+    model = api.Model(SH, dev, gamma=wl.gamma, max_batch=B, max_positions=P + steps + 1)
+    cache = api.KVCache(model, B, P + steps + 1, track=True)
+    stream = torch.cuda.Stream()
+    try:
+        tok = api.prefill(model, cache, prompts, stream=stream)
+        graph_out, tin = [], tok.copy()
+        for s in range(steps):          # no debug outputs: the captured graph is replayed
+            t, e = api.decode_step(model, cache, B, tokens=tin, stream=stream)
+            graph_out.append((t.copy(), e.copy()))
+            tin = t
+        kv_graph = [cache.read(l, b, P, steps) for l in (1, 8, 32) for b in (0, 7)]
+        occ = cache.occupancy()
+        assert np.all(occ[:, :B, :P + steps] == 1) and np.all(occ[:, :B, P + steps:] == 0)
+        cache.rollback(-1, steps)
+        tin = tok.copy()
+        for s in range(steps):          # with debug outputs: kernels launched one by one
+            t, e = api.decode_step(model, cache, B, tokens=tin, stream=stream, debug={"p": None})
+            np.testing.assert_array_equal(t, graph_out[s][0])
+            np.testing.assert_array_equal(e, graph_out[s][1])
+            tin = t
+        kv_eager = [cache.read(l, b, P, steps) for l in (1, 8, 32) for b in (0, 7)]
+        for (kg, vg), (ke, ve) in zip(kv_graph, kv_eager):
+            np.testing.assert_array_equal(kg, ke)
+            np.testing.assert_array_equal(vg, ve)
+        assert np.all(cache.occupancy()[:, :B, :P + steps] == 1)
+    finally:
+        cache.close()
+        model.close()
