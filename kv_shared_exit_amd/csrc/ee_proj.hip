@@ -40,6 +40,9 @@ namespace ee {
 constexpr int kWaves = kProjThreads / 64;
 // bf16 rows on MFMA (true) or on the vector ALU with dot2 (false)
 constexpr bool kBf16Mfma = false;
+// share of a range's workgroups given to the bf16 rows when both formats have
+// rows, in 1/256 (bf16 streams ~4x the bytes of its int4 copy)
+constexpr int kBfShare = 176;
 
 template <int EPI>
 struct Ep {
@@ -772,8 +775,28 @@ __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a)
       seq0[1][e] = e < n_i4 ? li[e] : pi;
     }
   }
+  // When both weight formats have rows, the workgroups of each column range
+  // split between them (the int4 share above its share of the bytes, since
+  // that pass is latency-bound) and the two passes run side by side instead
+  // of one after the other.  Measured to pay for the QKV and O projections
+  // only: with more ranges (down) or two matrices per tile (gate/up) the
+  // int4 pass needs the whole grid.
+  int fmt_lo = 0, fmt_hi = 1;
+  if constexpr (EPI == EPI_PART || EPI == EPI_QKV) {
+    if (n_bf > 0 && n_i4 > 0 && wk.nwg >= 2 && a.nkc <= 2) {
+      const int nbf = min(wk.nwg - 1, max(1, (wk.nwg * kBfShare) >> 8));
+      if (wk.wg < nbf) {
+        fmt_hi = 0;
+        wk.nwg = nbf;
+      } else {
+        fmt_lo = 1;
+        wk.wg -= nbf;
+        wk.nwg -= nbf;
+      }
+    }
+  }
   bool first = true;  // the first pass needs no barrier: its staging waits for seq0
-  for (int fmt = 0; fmt < 2; ++fmt) {
+  for (int fmt = fmt_lo; fmt <= fmt_hi; ++fmt) {
     if constexpr (EPI == EPI_LSE || EPI == EPI_ARGMAX || EPI == EPI_BF16) {
       if (fmt == 1) break;  // these run on backbone rows only
     }
