@@ -899,10 +899,10 @@ constexpr int kFinThreads = 256;
 constexpr int kFinVec = 4;    // float4 per thread per row chunk
 constexpr int kFinParts = 8;  // column ranges summed with all loads in flight
 
-// One workgroup per (row, chunk of kFinThreads * kFinVec * 4 columns) would
-// need a second pass for the norm; instead a workgroup owns a row and loops
-// over its chunks, issuing every load of a chunk (residual, partial sums,
-// gains) before using any.
+// A workgroup owns a row.  Rows up to kFinThreads * kFinVec * 4 columns are
+// held in registers between the sum of squares and the normalisation; wider
+// rows are processed in chunks and re-read (this workgroup wrote them).  Every
+// load of a chunk (residual, partial sums, gains) is issued before any is used.
 __global__ __launch_bounds__(kFinThreads) void finish_kernel(float* h, const float* parts, int nparts, size_t cstride,
                                                              int d, const uint16_t* gain, float eps, uint16_t* x,
                                                              uint16_t* hb) {
@@ -911,14 +911,17 @@ __global__ __launch_bounds__(kFinThreads) void finish_kernel(float* h, const flo
   const int d4 = d >> 2;
   float* hr = h + (size_t)b * d;
   const int per = kFinThreads * kFinVec;  // float4 per chunk
+  const bool one = d4 <= per;
   float ss = 0.0f;
+  float4 v[kFinVec];
+  uint2 g[kFinVec];
   for (int c0 = 0; c0 < d4; c0 += per) {
-    float4 v[kFinVec];
     float4 pv[kFinParts][kFinVec];
 #pragma unroll
     for (int j = 0; j < kFinVec; ++j) {
       const int i = min(c0 + tid + j * kFinThreads, d4 - 1);
       v[j] = *(const float4*)(hr + 4 * i);
+      if (gain) g[j] = *(const uint2*)(gain + 4 * i);
 #pragma unroll
       for (int c = 0; c < kFinParts; ++c) {
         // ranges past nparts reload the last one (or, with none, the residual
@@ -975,10 +978,21 @@ __global__ __launch_bounds__(kFinThreads) void finish_kernel(float* h, const flo
   }
   __syncthreads();
   const float r = rs;
-  // the normalised row: the residual is re-read (this workgroup just wrote it)
+  auto put = [&](int i, const float4& vv, const uint2& gg) {
+    uint2 o;
+    o.x = f2bf(vv.x * r * bf2f(gg.x & 0xffffu)) | (f2bf(vv.y * r * bf2f(gg.x >> 16)) << 16);
+    o.y = f2bf(vv.z * r * bf2f(gg.y & 0xffffu)) | (f2bf(vv.w * r * bf2f(gg.y >> 16)) << 16);
+    *(uint2*)(x + (size_t)b * d + 4 * i) = o;
+  };
+  if (one) {  // the row is still in registers
+#pragma unroll
+    for (int j = 0; j < kFinVec; ++j) {
+      const int i = tid + j * kFinThreads;
+      if (i < d4) put(i, v[j], g[j]);
+    }
+    return;
+  }
   for (int c0 = 0; c0 < d4; c0 += per) {
-    float4 v[kFinVec];
-    uint2 g[kFinVec];
 #pragma unroll
     for (int j = 0; j < kFinVec; ++j) {
       const int i = min(c0 + tid + j * kFinThreads, d4 - 1);
@@ -988,11 +1002,7 @@ __global__ __launch_bounds__(kFinThreads) void finish_kernel(float* h, const flo
 #pragma unroll
     for (int j = 0; j < kFinVec; ++j) {
       const int i = c0 + tid + j * kFinThreads;
-      if (i >= d4) continue;
-      uint2 o;
-      o.x = f2bf(v[j].x * r * bf2f(g[j].x & 0xffffu)) | (f2bf(v[j].y * r * bf2f(g[j].x >> 16)) << 16);
-      o.y = f2bf(v[j].z * r * bf2f(g[j].y & 0xffffu)) | (f2bf(v[j].w * r * bf2f(g[j].y >> 16)) << 16);
-      *(uint2*)(x + (size_t)b * d + 4 * i) = o;
+      if (i < d4) put(i, v[j], g[j]);
     }
   }
 }

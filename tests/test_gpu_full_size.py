@@ -16,7 +16,8 @@ rest are properties that hold at any size:
   * int4 copies bit-exact for sampled rows of sampled layers;
   * at the benchmark's prompt length: graph replay equals launching the
     kernels one by one (tokens, exit layers, K/V), and every written KV slot
-    was written exactly once.
+    was written exactly once;
+  * two layers at the exact widths of the 1B and 34B workloads (batch 1 and 4).
 """
 import dataclasses
 
@@ -180,3 +181,54 @@ def test_bench_configuration_graph_equals_eager_and_slots_written_once(env):
     finally:
         cache.close()
         model.close()
+
+
+@pytest.mark.parametrize("name,batch", [("1b", 1), ("34b", 4)])
+def test_layer_widths_of_other_workloads(name, batch):
+    """Two layers with the exact widths of the 1B (d 2048, 32/8 heads of 64,
+    F 8192, V 128256) and 34B (d 8192, 64/8 heads of 128, F 22016, V 32000)
+    workloads at their batch sizes: the kernels see the same shapes as in the
+    full models (depth does not change any launch).  Full depth against the
+    oracle for sequence 0, int4 copies bit-exact on sampled rows."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_shared_exit_amd import api
+    wl = synth.workload(name)
+    sh = dataclasses.replace(wl.shape, n_layers=2)
+    w = synth.make_weights(sh, wl.seed_weights)
+    P = 3
+    prompts = np.random.default_rng(78).integers(0, sh.vocab, (batch, P)).astype(np.int32)
+    dev = api.upload_weights(w)
+    model = api.Model(sh, dev, gamma=2.0, max_batch=batch, max_positions=P + 2)
+    cache = api.KVCache(model, batch, P + 2, track=True)
+    try:
+        tg, lg = api.prefill(model, cache, prompts, logits=True)
+        dbg = {"logits": None, "hidden": None}
+        t1, e1 = api.decode_step(model, cache, batch, tokens=tg, debug=dbg)
+        assert np.all(e1 == sh.n_layers)
+        k_gpu = {l: cache.read(l, 0, 0, P + 1) for l in (1, 2)}
+        codes, scales = model.exit_weights(2, "w_down", 64, 16)
+    finally:
+        cache.close()
+        model.close()
+    q, s_ = quantize_int4(from_bf16_bits(w["layers"][1]["w_down"][64:80]), sh.group)
+    np.testing.assert_array_equal(codes, q)
+    np.testing.assert_array_equal(from_bf16_bits(scales), s_)
+    orc = om.OracleModel(sh, w, cache_f64=True)
+    oc = om.KVCache(sh, 1, P + 2)
+    to, info = om.prefill(orc, oc, prompts[:1])
+    assert maxrel(lg[0], info["logits"][0]) <= TOL
+    t2, _, io = om.decode_step(orc, oc, tg[:1], trace=True, heads=False)
+    for l in range(sh.n_layers + 1):
+        e = maxrel(dbg["hidden"][0, l], io["hidden"][0, l])
+        assert e <= TOL, f"{name}: hidden after layer {l}: maxrel {e:.3g}"
+    e = maxrel(dbg["logits"][0], io["logits"][0])
+    assert e <= TOL, f"{name}: logits maxrel {e:.3g}"
+    band = max(1e-2, 2 * float(np.abs(dbg["logits"][0].astype(np.float64) - io["logits"][0]).max()))
+    if io["gap"][0] > band:
+        assert t1[0] == t2[0]
+    for l, (k, v) in k_gpu.items():
+        kr = oc.K[l - 1, 0, :, :P + 1].transpose(1, 0, 2)
+        vr = oc.V[l - 1, 0, :, :P + 1].transpose(1, 0, 2)
+        assert maxrel(from_bf16_bits(k), kr) <= TOL and maxrel(from_bf16_bits(v), vr) <= TOL

@@ -18,6 +18,8 @@ SHAPES = {
     "mid": ModelShape(3, 2048, 16, 4, 128, 5120, 5000, 128, rope_theta=500000.0),
     # head_dim 64 with 8 kv heads, group 64
     "hd64": ModelShape(2, 512, 8, 8, 64, 1024, 2048, 64, rope_theta=10000.0),
+    # head_dim 64 with 4 q heads per kv head (the 1B attention), group 128
+    "gqa4": ModelShape(3, 1024, 16, 4, 64, 2048, 2000, 128, rope_theta=500000.0),
 }
 
 
@@ -95,3 +97,25 @@ def test_long_context_several_tiles_per_wave(gpu):
     w = synth.make_weights(sh, 12)
     run_parity(sh, w, 8, 2100, 2, 0.75, forced_fn=lambda s: np.array([1, 2, 2, 1, 2, 2, 1, 2]),
                label="hd64-long", check_kv=False)
+
+
+@pytest.mark.parametrize("name,batch", [("odd", 11), ("mid", 10)])
+def test_more_than_eight_rows(gpu, name, batch):
+    """More rows than one 8-row pass: the projections run the rows in chunks of 8
+    (the later chunks read their ids from the lists), with forced exits so both
+    weight formats have rows in every chunk."""
+    from parity import run_parity
+    sh = SHAPES[name]
+    w = synth.make_weights(sh, 13)
+    L = sh.n_layers
+    rng = np.random.default_rng(8)
+    res = run_parity(sh, w, batch, 4, 3, 0.75, forced_fn=lambda s: rng.integers(1, L + 1, batch),
+                     label=f"{name}-b{batch}")
+    ex = np.stack(res.exits)
+    assert ex.min() < L and ex.max() == L
+
+
+def test_gqa4_head_dim_64(gpu):
+    from parity import run_parity
+    sh, w = _weights("gqa4", 2.0, 20, 3)
+    run_parity(sh, w, 4, 20, 3, 0.75, label="gqa4")
