@@ -268,8 +268,8 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
   const bool int4 = cf.exit_mode == EE_EXIT_INT4;
 
   const size_t pstride = (size_t)kMaxBatch * d;  // elements between partial-sum ranges
-  launch_init(st, prompt, P, t, B, L, m->tok_emb, d, cf.vocab, m->h, m->p_rec, s);
-  launch_finish(m->h, nullptr, 0, pstride, B, d, (const uint16_t*)m->lw[0].attn_norm, cf.rms_eps, m->xn, nullptr, s);
+  launch_init(st, prompt, P, t, B, L, m->tok_emb, d, cf.vocab, m->h, m->p_rec,
+              (const uint16_t*)m->lw[0].attn_norm, cf.rms_eps, m->xn, s);
   if (dbg.hidden)
     HIPCHK(hipMemcpy2DAsync(m->dbg_hidden, (size_t)(L + 1) * d * 4, m->h, (size_t)d * 4,
                             (size_t)d * 4, B, hipMemcpyDeviceToDevice, s));
@@ -568,6 +568,7 @@ ee_status ee_create_model(const ee_model_config* cfg, const ee_weights* w, const
       m->lw.assign(w->layers, w->layers + c.n_layers);
       m->gamma = gam;
       HIPCHK(hipStreamCreateWithFlags(&m->own, hipStreamNonBlocking));
+      no_rows();  // resolved on this device here, before any graph capture
       const int L = c.n_layers, d = c.d_model, F = c.d_ff, G = c.group_size;
       const int qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
       // int4 exit copies of layers 2..L

@@ -84,14 +84,20 @@ bool proj_fits(int K, int batch);
 // With ev0/ev1 set, the launch records its own start and end into them.
 int launch_proj(int epi, const ProjArgs& a, int nwg, int batch, hipStream_t s, hipEvent_t ev0 = nullptr,
                 hipEvent_t ev1 = nullptr);
+// Device address of an all-zero row list on the current device (stands in for
+// an absent list); resolved on first call per device, before any capture.
+const int32_t* no_rows();
 // The column ranges EPI_PART uses for K columns, N rows (and their width).
 int proj_ranges(int K, int N, int nwg, int batch, int* kc);
-// h[b] += sum_c parts[c][b] for b < B (nparts may be 0); then, when gain is
-// set, x[b] = bf16(rmsnorm(h[b]) * gain), and when hb is set, hb[b] = bf16(h[b]).
+// h[b] += sum_c parts[c][b] for b < B (nparts may be 0); then x[b] =
+// bf16(rmsnorm(h[b]) * gain), and when hb is set, hb[b] = bf16(h[b]).
 void launch_finish(float* h, const float* parts, int nparts, size_t cstride, int B, int d,
                    const uint16_t* gain, float eps, uint16_t* x, uint16_t* hb, hipStream_t s);
+// Step setup: h[b] = embedding of the input token, x[b] = bf16(rmsnorm(h[b]) *
+// gain) (the first layer's attention input), exit state and row lists reset.
 void launch_init(StepState* st, const int32_t* prompt, int P, int t, int B, int L,
-                 const uint16_t* emb, int d, int V, float* h, float* p_rec, hipStream_t s);
+                 const uint16_t* emb, int d, int V, float* h, float* p_rec, const uint16_t* gain,
+                 float eps, uint16_t* x, hipStream_t s);
 void launch_attention(const AttnArgs& a, hipStream_t s);
 void launch_decide(StepState* st, const float* part, int nwg, const float* gamma, int layer,
                    int L, int B, float* p_rec, hipStream_t s);

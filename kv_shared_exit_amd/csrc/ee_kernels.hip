@@ -2,12 +2,14 @@
 //
 // The step (River-LLM explainer sections 4.1-4.3; AdaDecode explainer sections
 // 2.1-2.2; CALM explainer sections 2.2 and 3.3) is built from these kernels:
-//   init       embed the input tokens into the float32 residual, reset the
-//              per-step exit state and the row lists
-//   proj       (ee_proj.hip) the projections over both weight copies, with the
-//              RMSNorm in their input staging and RoPE plus the write of k and
-//              v into the shared cache slot of the position (the same slot for
-//              either weight copy) in the QKV epilogue; the int4 packer
+//   init       embed the input tokens into the float32 residual and normalise
+//              them for the first layer, reset the per-step exit state and the
+//              row lists
+//   proj       (ee_proj.hip) the projections over both weight copies, RoPE plus
+//              the write of k and v into the shared cache slot of the position
+//              (the same slot for either weight copy) in the QKV epilogue, the
+//              residual finish with the RMSNorm of the next input; the int4
+//              packer
 //   attention  grouped-query decode attention: one wave per run of 64-position
 //              tiles of a (sequence, kv head), scores on MFMA, online softmax,
 //              and a combine kernel merging the runs
@@ -20,28 +22,68 @@
 
 #include <math.h>
 
+#include <stdexcept>
+
 namespace ee {
 
 // ---------------------------------------------------------------------------
 // Step setup: embedding rows into the residual, exit state, row lists.
 // ---------------------------------------------------------------------------
-__global__ void init_kernel(StepState* st, const int32_t* prompt, int P, int t, int B, int L,
-                            const uint16_t* emb, int d, int V, float* h, float* p_rec) {
+constexpr int kInitThreads = 256;
+
+__global__ __launch_bounds__(kInitThreads) void init_kernel(StepState* st, const int32_t* prompt, int P, int t,
+                                                            int B, int L, const uint16_t* emb, int d, int V,
+                                                            float* h, float* p_rec, const uint16_t* gain, float eps,
+                                                            uint16_t* x) {
   const int b = blockIdx.x;
+  const int tid = threadIdx.x;
   int tok = prompt ? prompt[(size_t)b * P + t] : st->tok[b];
   tok = min(max(tok, 0), V - 1);  // host-validated; a device-produced token is always < V
   const uint16_t* src = emb + (size_t)tok * d;
-  for (int i = threadIdx.x; i < d; i += blockDim.x) h[(size_t)b * d + i] = bf2f(src[i]);
+  // h = embedding row (4 columns per item; d is a multiple of 32), then the
+  // RMSNorm of the row (same formula as the residual finish) into x
+  const int d4 = d >> 2;
+  float ss = 0.0f;
+  for (int i = tid; i < d4; i += kInitThreads) {
+    const uint2 e = *(const uint2*)(src + 4 * i);
+    const float4 v = make_float4(bf2f(e.x & 0xffffu), bf2f(e.x >> 16), bf2f(e.y & 0xffffu), bf2f(e.y >> 16));
+    *(float4*)(h + (size_t)b * d + 4 * i) = v;
+    ss = fmaf(v.x, v.x, ss);
+    ss = fmaf(v.y, v.y, ss);
+    ss = fmaf(v.z, v.z, ss);
+    ss = fmaf(v.w, v.w, ss);
+  }
+  __shared__ float wsum[kInitThreads / 64];
+  __shared__ float rs;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+  __syncthreads();
+  if (tid == 0) {
+    float tt = 0.0f;
+    for (int w = 0; w < kInitThreads / 64; ++w) tt += wsum[w];
+    rs = 1.0f / sqrtf(tt / (float)d + eps);
+  }
+  __syncthreads();
+  const float r = rs;
+  for (int i = tid; i < d4; i += kInitThreads) {
+    const uint2 e = *(const uint2*)(src + 4 * i);
+    const uint2 g = *(const uint2*)(gain + 4 * i);
+    uint2 o;
+    o.x = f2bf(bf2f(e.x & 0xffffu) * r * bf2f(g.x & 0xffffu)) | (f2bf(bf2f(e.x >> 16) * r * bf2f(g.x >> 16)) << 16);
+    o.y = f2bf(bf2f(e.y & 0xffffu) * r * bf2f(g.y & 0xffffu)) | (f2bf(bf2f(e.y >> 16) * r * bf2f(g.y >> 16)) << 16);
+    *(uint2*)(x + (size_t)b * d + 4 * i) = o;
+  }
   if (p_rec)
-    for (int l = threadIdx.x; l < L - 1; l += blockDim.x) p_rec[l * kMaxBatch + b] = __int_as_float(0x7fc00000);
+    for (int l = tid; l < L - 1; l += kInitThreads) p_rec[l * kMaxBatch + b] = __int_as_float(0x7fc00000);
   if (b == 0) {
-    for (int i = threadIdx.x; i < B; i += blockDim.x) {
+    for (int i = tid; i < B; i += kInitThreads) {
       st->exited[i] = 0;
       st->e[i] = L;
       st->act[i] = i;
       st->all[i] = i;
     }
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
       st->n_act = B;
       st->n_ex = 0;
       st->n_all = B;
@@ -50,8 +92,10 @@ __global__ void init_kernel(StepState* st, const int32_t* prompt, int P, int t, 
 }
 
 void launch_init(StepState* st, const int32_t* prompt, int P, int t, int B, int L,
-                 const uint16_t* emb, int d, int V, float* h, float* p_rec, hipStream_t s) {
-  hipLaunchKernelGGL(init_kernel, dim3(B), dim3(256), 0, s, st, prompt, P, t, B, L, emb, d, V, h, p_rec);
+                 const uint16_t* emb, int d, int V, float* h, float* p_rec, const uint16_t* gain,
+                 float eps, uint16_t* x, hipStream_t s) {
+  hipLaunchKernelGGL(init_kernel, dim3(B), dim3(kInitThreads), 0, s, st, prompt, P, t, B, L, emb, d, V, h, p_rec,
+                     gain, eps, x);
 }
 
 // ---------------------------------------------------------------------------
@@ -278,23 +322,41 @@ void launch_attention(const AttnArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Exit decision and active-sequence compaction.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void decide_kernel(StepState* st, const float* part, int nwg,
-                                                     const float* gamma, int layer, int L, int B,
-                                                     float* p_rec) {
+constexpr int kHeadThreads = 512;              // decide / final: one wave per row
+constexpr int kHeadWaves = kHeadThreads / 64;
+constexpr int kPartPerLane = kNwgMax / 64;    // partials a lane merges (nwg <= kNwgMax)
+
+// Loads the (max, sum exp) partials k = lane + 64j of list position i, all
+// requested before any is used (absent ones: (-inf, 0), which merge as no-ops).
+__device__ __forceinline__ void load_lse_parts(const float* part, int nwg, int i, int lane,
+                                               float2 (&v)[kPartPerLane]) {
+#pragma unroll
+  for (int j = 0; j < kPartPerLane; ++j) {
+    const int k = lane + 64 * j;
+    v[j] = k < nwg ? *(const float2*)(part + ((size_t)k * kMaxBatch + i) * 4) : make_float2(-INFINITY, 0.0f);
+  }
+}
+
+__global__ __launch_bounds__(kHeadThreads) void decide_kernel(StepState* st, const float* part, int nwg,
+                                                              const float* gamma, int layer, int L, int B,
+                                                              float* p_rec) {
   __shared__ int sx[kMaxBatch];
   __shared__ int sn;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if (threadIdx.x < B) sx[threadIdx.x] = st->exited[threadIdx.x];
+  // the first row of each wave is requested before the row count is known
+  // (list positions below kMaxBatch are always in bounds)
+  float2 v[kPartPerLane];
+  load_lse_parts(part, nwg, w, lane, v);
+  if ((int)threadIdx.x < B) sx[threadIdx.x] = st->exited[threadIdx.x];
   if (threadIdx.x == 0) sn = min(max(st->n_act, 0), B);
   __syncthreads();
   const int n = sn;
-  for (int i = w; i < n; i += 4) {
+  for (int i = w; i < n; i += kHeadWaves) {
+    if (i != w) load_lse_parts(part, nwg, i, lane, v);
     const int b = st->act[i];
     float m = -INFINITY, s = 0.0f;
-    for (int k = lane; k < nwg; k += 64) {
-      const float* p = part + ((size_t)k * kMaxBatch + i) * 4;
-      lse_merge(m, s, p[0], p[1]);
-    }
+#pragma unroll
+    for (int j = 0; j < kPartPerLane; ++j) lse_merge(m, s, v[j].x, v[j].y);
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
@@ -334,21 +396,24 @@ __global__ __launch_bounds__(256) void decide_kernel(StepState* st, const float*
 
 void launch_decide(StepState* st, const float* part, int nwg, const float* gamma, int layer, int L,
                    int B, float* p_rec, hipStream_t s) {
-  hipLaunchKernelGGL(decide_kernel, dim3(1), dim3(256), 0, s, st, part, nwg, gamma, layer, L, B, p_rec);
+  if (nwg < 1 || nwg > kNwgMax) throw std::logic_error("decide: partial count out of range");
+  hipLaunchKernelGGL(decide_kernel, dim3(1), dim3(kHeadThreads), 0, s, st, part, nwg, gamma, layer, L, B, p_rec);
 }
 
-// ---------------------------------------------------------------------------
-// Final LM head: merge argmax partials, emit the token, advance the sequence.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void final_kernel(StepState* st, const float* part, int nwg, int B,
-                                                    int V, int32_t* lens, int advance) {
+__global__ __launch_bounds__(kHeadThreads) void final_kernel(StepState* st, const float* part, int nwg, int B,
+                                                             int V, int32_t* lens, int advance) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int b = w; b < B; b += 4) {
-    Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
-    for (int k = lane; k < nwg; k += 64) {
-      const float* p = part + ((size_t)k * kMaxBatch + b) * 4;
-      top2_merge(t, Top2{p[0], __float_as_int(p[1]), p[2]});
+  for (int b = w; b < B; b += kHeadWaves) {
+    float4 v[kPartPerLane];
+#pragma unroll
+    for (int j = 0; j < kPartPerLane; ++j) {
+      const int k = lane + 64 * j;
+      v[j] = k < nwg ? *(const float4*)(part + ((size_t)k * kMaxBatch + b) * 4)
+                     : make_float4(-INFINITY, __int_as_float(0x7fffffff), -INFINITY, 0.0f);
     }
+    Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
+#pragma unroll
+    for (int j = 0; j < kPartPerLane; ++j) top2_merge(t, Top2{v[j].x, __float_as_int(v[j].y), v[j].z});
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       Top2 u{__shfl_xor(t.v1, o), __shfl_xor(t.i1, o), __shfl_xor(t.v2, o)};
@@ -366,7 +431,8 @@ __global__ __launch_bounds__(256) void final_kernel(StepState* st, const float* 
 
 void launch_final(StepState* st, const float* part, int nwg, int B, int V, int32_t* lens, int advance,
                   hipStream_t s) {
-  hipLaunchKernelGGL(final_kernel, dim3(1), dim3(256), 0, s, st, part, nwg, B, V, lens, advance);
+  if (nwg < 1 || nwg > kNwgMax) throw std::logic_error("final: partial count out of range");
+  hipLaunchKernelGGL(final_kernel, dim3(1), dim3(kHeadThreads), 0, s, st, part, nwg, B, V, lens, advance);
 }
 
 __global__ void advance_kernel(int32_t* lens, int B) {

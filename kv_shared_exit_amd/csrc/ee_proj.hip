@@ -737,6 +737,10 @@ __device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int 
   }
 }
 
+// Zero rows: stands in for an absent row list or count (its address on each
+// device is resolved by no_rows()).
+__device__ int32_t kNoRows[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+
 template <int EPI, int NG>
 __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[kXLdsElems + 8 * 8];
@@ -749,30 +753,29 @@ __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a)
   wk.wg = blockIdx.x - wk.chunk * wk.nwg;
   wk.k0 = wk.chunk * a.kc;
   wk.K = min(a.kc, a.K - wk.k0);
-  // Row counts and the first 8 ids of both lists, all read at once before
-  // anything is stored (scalar loads that depend only on the arguments: no
-  // chain of dependent loads before the first weights are requested).  A
-  // chunk's ids are padded with its last id, which the staging relies on.
+  // Row counts and the first 8 ids of both lists, read before anything is
+  // stored (no chain of dependent loads before the first weights are
+  // requested); the staging relies on the padding below.  launch_proj points an absent list or count at kNoRows, so nothing here
+  // branches on a pointer (a branch per pointer serialised the loads: one
+  // memory latency each).  The list pointers are pinned to the first argument
+  // loads; lanes 0..7 of wave 0 read the first 8 ids of both lists and store
+  // them, a chunk's ids padded with its last id.
   __shared__ int seq0[2][8];
-  const int n_bf = a.cnt_bf ? min(max(*a.cnt_bf, 0), kMaxBatch) : 0;
-  const int n_i4 = a.cnt_i4 ? min(max(*a.cnt_i4, 0), kMaxBatch) : 0;
-  int lb[8], li[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    lb[e] = a.list_bf ? a.list_bf[e] : 0;
-    li[e] = a.list_i4 ? a.list_i4[e] : 0;
+  {
+    const int32_t* lbp = a.list_bf;
+    const int32_t* lip = a.list_i4;
+    asm volatile("" ::"s"(lbp), "s"(lip));
   }
-  if (threadIdx.x == 0) {
-    int pb = lb[0], pi = li[0];  // the last id of each list's first chunk
-#pragma unroll
-    for (int e = 1; e < 8; ++e) {
-      pb = e < n_bf ? lb[e] : pb;
-      pi = e < n_i4 ? li[e] : pi;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      seq0[0][e] = e < n_bf ? lb[e] : pb;
-      seq0[1][e] = e < n_i4 ? li[e] : pi;
+  const int n_bf = min(max(*a.cnt_bf, 0), kMaxBatch);
+  const int n_i4 = min(max(*a.cnt_i4, 0), kMaxBatch);
+  if (threadIdx.x < 64) {
+    const int e = threadIdx.x & 7;
+    const int lb = a.list_bf[e], li = a.list_i4[e];
+    const int pb = __shfl(lb, max(min(n_bf, 8) - 1, 0));
+    const int pi = __shfl(li, max(min(n_i4, 8) - 1, 0));
+    if (threadIdx.x < 8) {
+      seq0[0][e] = e < n_bf ? lb : pb;
+      seq0[1][e] = e < n_i4 ? li : pi;
     }
   }
   // When both weight formats have rows, the workgroups of each column range
@@ -863,8 +866,25 @@ int proj_ranges(int K, int N, int nwg, int batch, int* kc) {
   return (blocks + kcb - 1) / kcb;
 }
 
+const int32_t* no_rows() {
+  constexpr int kMaxDevices = 64;
+  static const int32_t* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    throw std::runtime_error("no_rows: no current HIP device");
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(kNoRows)) != hipSuccess || !p)
+      throw std::runtime_error("no_rows: hipGetSymbolAddress failed");
+    addr[dev] = (const int32_t*)p;
+  }
+  return addr[dev];
+}
+
 int launch_proj(int epi, const ProjArgs& a0, int nwg, int batch, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   ProjArgs a = a0;
+  if (!a.cnt_bf || !a.list_bf) a.cnt_bf = a.list_bf = no_rows();
+  if (!a.cnt_i4 || !a.list_i4) a.cnt_i4 = a.list_i4 = no_rows();
   // the vocabulary epilogues write one partial per workgroup (kNwgMax of them)
   int g = std::max(1, std::min(nwg, kNwgMax));
   a.nkc = 1;
@@ -915,20 +935,22 @@ __global__ __launch_bounds__(kFinThreads) void finish_kernel(float* h, const flo
   float ss = 0.0f;
   float4 v[kFinVec];
   uint2 g[kFinVec];
+  // ranges past nparts reload the last one (or, with none, the residual row
+  // itself: parts may be null then) and are not added; every load of a chunk
+  // is unconditional (a branch around a load makes the compiler wait for the
+  // loads before it)
+  const float* pbase = nparts > 0 ? parts + (size_t)b * d : hr;
+  const size_t pcs = nparts > 0 ? cstride : 0;
+  const int plast = max(nparts - 1, 0);
   for (int c0 = 0; c0 < d4; c0 += per) {
     float4 pv[kFinParts][kFinVec];
 #pragma unroll
     for (int j = 0; j < kFinVec; ++j) {
       const int i = min(c0 + tid + j * kFinThreads, d4 - 1);
       v[j] = *(const float4*)(hr + 4 * i);
-      if (gain) g[j] = *(const uint2*)(gain + 4 * i);
+      g[j] = *(const uint2*)(gain + 4 * i);
 #pragma unroll
-      for (int c = 0; c < kFinParts; ++c) {
-        // ranges past nparts reload the last one (or, with none, the residual
-        // row itself: parts may be null then) and are not added
-        const float* src = nparts > 0 ? parts + min(c, nparts - 1) * cstride + (size_t)b * d : hr;
-        pv[c][j] = *(const float4*)(src + 4 * i);
-      }
+      for (int c = 0; c < kFinParts; ++c) pv[c][j] = *(const float4*)(pbase + min(c, plast) * pcs + 4 * i);
     }
 #pragma unroll
     for (int j = 0; j < kFinVec; ++j) {
@@ -964,7 +986,6 @@ __global__ __launch_bounds__(kFinThreads) void finish_kernel(float* h, const flo
       }
     }
   }
-  if (!gain) return;
   __shared__ float wsum[kFinThreads / 64];
   __shared__ float rs;
 #pragma unroll
@@ -1009,6 +1030,7 @@ __global__ __launch_bounds__(kFinThreads) void finish_kernel(float* h, const flo
 
 void launch_finish(float* h, const float* parts, int nparts, size_t cstride, int B, int d, const uint16_t* gain,
                    float eps, uint16_t* x, uint16_t* hb, hipStream_t s) {
+  if (!gain || !x || (nparts > 0 && !parts) || d % 4) throw std::logic_error("finish: bad arguments");
   hipLaunchKernelGGL(finish_kernel, dim3(B), dim3(kFinThreads), 0, s, h, parts, nparts, cstride, d, gain, eps, x,
                      hb);
 }
