@@ -109,9 +109,13 @@ void launch_init(StepState* st, const int32_t* prompt, int P, int t, int B, int 
 // padded to 16 as the B operand, held in registers).  Softmax statistics are
 // per q head (online across the wave's tiles); the probabilities go through
 // LDS (1 KB) to the PV product, which runs on the vector ALUs with V rows read
-// as 16-byte chunks (16 lanes per position row for head_dim 128).  Each wave
-// writes one (m, l, o) partial; attn_combine merges a sequence's partials in
-// order.
+// as 16-byte chunks (16 lanes per position row for head_dim 128).
+//
+// A tile's K and V loads are all issued together (rows are clamped to the
+// cache capacity; positions at or past the length are masked: score -inf,
+// never multiplied).  Each wave writes one (m, l, o) partial; a wave whose run
+// starts at or past the length writes the empty partial (m = -inf, l = 0),
+// which the combine kernel skips, so the combine needs no length.
 // ---------------------------------------------------------------------------
 template <int HD, int GQ>
 __global__ __launch_bounds__(64) void attn_kernel(const AttnArgs a) {
@@ -123,25 +127,49 @@ __global__ __launch_bounds__(64) void attn_kernel(const AttnArgs a) {
   __shared__ float cr[GQ];
 
   const int c = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-  const int ctx = a.lens[b] + 1;
   const int tpw = a.tpw;
   const int tstart = c * tpw * 64;
-  if (tstart >= ctx) return;
   const int lane = threadIdx.x;
   const int g = a.H / a.Hkv;
   const int hh = lane & 15;            // q head in the MFMA B / C layouts
   const int qc = lane >> 4;
+  const int smax = a.S - 1;            // last row of the cache
   const size_t base = ((size_t)b * a.Hkv + j) * a.S;   // row of position 0
   const uint16_t* Kb = a.K + base * HD;
   const uint16_t* Vb = a.V + base * HD;
+  const int vr = lane / CPR, vc = lane - vr * CPR;   // V: row within load, 16-byte chunk
 
+  uint4 kv[4][KK];   // K rows t0 + pt*16 + (lane & 15), head dims qc*8 + 32*kk
+  uint4 vv[NVL];     // V rows t0 + vr + i*RPI, chunk vc
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+      const int row = min(t0 + pt * 16 + (lane & 15), smax);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) kv[pt][kk] = ld_stream(Kb + (size_t)row * HD + qc * 8 + 32 * kk);
+    }
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+      const int row = min(t0 + vr + i * RPI, smax);
+      vv[i] = ld_stream(Vb + (size_t)row * HD + vc * 8);
+    }
+  };
   uint4 qv[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) {
     qv[kk] = make_uint4(0, 0, 0, 0);
     if (hh < g) qv[kk] = *(const uint4*)(a.q + ((size_t)b * a.H + j * g + hh) * HD + qc * 8 + 32 * kk);
   }
-  const int vr = lane / CPR, vc = lane - vr * CPR;   // V: row within load, 16-byte chunk
+  const int ctx = a.lens[b] + 1;
+  const int nw = a.nch;
+  if (tstart >= ctx) {  // no position in this run
+    if (lane < g) {
+      float* out = a.part + ((((size_t)b * a.H + j * g + lane) * nw) + c) * (HD + 2);
+      out[HD] = -INFINITY;
+      out[HD + 1] = 0.0f;
+    }
+    return;
+  }
 
   float m = -INFINITY, l = 0.0f;   // per q head hh (replicated over qc)
   float o[GQ][8];
@@ -152,20 +180,17 @@ __global__ __launch_bounds__(64) void attn_kernel(const AttnArgs a) {
 
   const int tend = min(ctx, tstart + tpw * 64);
   for (int t0 = tstart; t0 < tend; t0 += 64) {
+    load_tile(t0);
     const int nval = min(64, ctx - t0);
     // scores S[t][i] for 64 positions
     float sc[4][4];
     float mt = -INFINITY;
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {
-      const int row = t0 + min(pt * 16 + (lane & 15), nval - 1);
-      uint4 kv[KK];
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kv[kk] = ld_stream(Kb + (size_t)row * HD + qc * 8 + 32 * kk);
       f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv[kk]),
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv[pt][kk]),
                                                       __builtin_bit_cast(bf16x8_t, qv[kk]), acc, 0, 0, 0);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -173,13 +198,6 @@ __global__ __launch_bounds__(64) void attn_kernel(const AttnArgs a) {
         sc[pt][r] = p < nval ? acc[r] * a.scale : -INFINITY;
         mt = fmaxf(mt, sc[pt][r]);
       }
-    }
-    // V rows of this tile: lane reads chunk vc of rows vr, vr + RPI, ...
-    uint4 vv[NVL];
-#pragma unroll
-    for (int i = 0; i < NVL; ++i) {
-      const int row = t0 + min(vr + i * RPI, nval - 1);
-      vv[i] = ld_stream(Vb + (size_t)row * HD + vc * 8);
     }
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
@@ -230,7 +248,6 @@ __global__ __launch_bounds__(64) void attn_kernel(const AttnArgs a) {
     for (int i = 0; i < GQ; ++i)
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[i][e] += __shfl_xor(o[i][e], sft);
-  const int nw = a.nch;
   if (vr == 0) {
 #pragma unroll
     for (int i = 0; i < GQ; ++i) {
@@ -248,51 +265,47 @@ __global__ __launch_bounds__(64) void attn_kernel(const AttnArgs a) {
 }
 
 // Merges the (m, l, o) partials of one (sequence, q head) in partial order:
-// weights f_c = exp(m_c - max m) and L = sum f_c l_c in parallel, then
-// o = sum_c f_c o_c / L per head dimension.
+// weights f_c = exp(m_c - max m) and L = sum f_c l_c, then o = sum_c f_c o_c
+// / L per head dimension.  Empty partials (m = -inf) have weight 0 and their
+// o is not read into the sum.  The partials are taken in batches of kCombBatch
+// whose loads are all issued at once, merged online (running max) across
+// batches.
+constexpr int kCombBatch = 32;
+
 __global__ __launch_bounds__(128) void attn_combine_kernel(const AttnArgs a) {
-  constexpr int kMaxParts = 2048;
-  __shared__ float fw[kMaxParts];
-  __shared__ float red[2];
   const int h = blockIdx.x, b = blockIdx.y;
   const int hd = a.hd;
   const int tid = threadIdx.x;
-  const int ctx = a.lens[b] + 1;
-  const int span = a.tpw * 64;
-  const int nc = min((ctx + span - 1) / span, kMaxParts);
-  const float* base = a.part + (((size_t)b * a.H + h) * a.nch) * (hd + 2);
-  float M = -INFINITY;
-  for (int c = tid; c < nc; c += 128) M = fmaxf(M, base[(size_t)c * (hd + 2) + hd]);
+  const int nc = a.nch;
+  const float* base = a.part + (((size_t)b * a.H + h) * nc) * (hd + 2);
+  const int d = min(tid, hd - 1);   // this thread's head dimension (threads past hd repeat the last)
+  float M = -INFINITY, L = 0.0f, O = 0.0f;
+  for (int c0 = 0; c0 < nc; c0 += kCombBatch) {
+    float mv[kCombBatch], lv[kCombBatch], ov[kCombBatch];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  if ((tid & 63) == 0) red[tid >> 6] = M;
-  __syncthreads();
-  M = fmaxf(red[0], red[1]);
-  float L = 0.0f;
-  for (int c = tid; c < nc; c += 128) {
-    const float* p = base + (size_t)c * (hd + 2);
-    const float f = __expf(p[hd] - M);
-    fw[c] = f;
-    L = fmaf(p[hd + 1], f, L);
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o);
-  __syncthreads();
-  if ((tid & 63) == 0) red[tid >> 6] = L;
-  __syncthreads();
-  L = red[0] + red[1];
-  for (int d = tid; d < hd; d += 128) {
-    float O0 = 0.0f, O1 = 0.0f, O2 = 0.0f, O3 = 0.0f;
-    int c = 0;
-    for (; c + 4 <= nc; c += 4) {
-      O0 = fmaf(base[(size_t)c * (hd + 2) + d], fw[c], O0);
-      O1 = fmaf(base[(size_t)(c + 1) * (hd + 2) + d], fw[c + 1], O1);
-      O2 = fmaf(base[(size_t)(c + 2) * (hd + 2) + d], fw[c + 2], O2);
-      O3 = fmaf(base[(size_t)(c + 3) * (hd + 2) + d], fw[c + 3], O3);
+    for (int i = 0; i < kCombBatch; ++i) {
+      const int cc = min(c0 + i, nc - 1);
+      const float* p = base + (size_t)cc * (hd + 2);
+      mv[i] = c0 + i < nc ? p[hd] : -INFINITY;
+      lv[i] = p[hd + 1];
+      ov[i] = p[d];
     }
-    for (; c < nc; ++c) O0 = fmaf(base[(size_t)c * (hd + 2) + d], fw[c], O0);
-    a.out[((size_t)b * a.H + h) * hd + d] = (uint16_t)f2bf(((O0 + O1) + (O2 + O3)) / L);
+    float Mb = M;
+#pragma unroll
+    for (int i = 0; i < kCombBatch; ++i) Mb = fmaxf(Mb, mv[i]);
+    if (Mb == -INFINITY) continue;   // nothing yet
+    const float rs = __expf(M - Mb);  // 0 when M = -inf
+    L *= rs;
+    O *= rs;
+#pragma unroll
+    for (int i = 0; i < kCombBatch; ++i) {
+      const float f = __expf(mv[i] - Mb);   // 0 for empty partials
+      L = fmaf(lv[i], f, L);
+      O = f > 0.0f ? fmaf(ov[i], f, O) : O;
+    }
+    M = Mb;
   }
+  if (tid < hd) a.out[((size_t)b * a.H + h) * hd + tid] = (uint16_t)f2bf(O / L);
 }
 
 template <int HD, int GQ>
