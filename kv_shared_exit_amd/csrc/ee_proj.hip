@@ -41,8 +41,9 @@ constexpr int kWaves = kProjThreads / 64;
 // bf16 rows on MFMA (true) or on the vector ALU with dot2 (false)
 constexpr bool kBf16Mfma = false;
 // share of a range's workgroups given to the bf16 rows when both formats have
-// rows, in 1/256 (bf16 streams ~4x the bytes of its int4 copy)
-constexpr int kBfShare = 176;
+// rows, in 1/256 (bf16 streams ~4x the bytes of its int4 copy; measured)
+constexpr int kBfShare = 176;     // QKV, O
+constexpr int kBfShareFfn = 128;  // gate/up, down
 
 template <int EPI>
 struct Ep {
@@ -781,13 +782,14 @@ __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a)
   // When both weight formats have rows, the workgroups of each column range
   // split between them (the int4 share above its share of the bytes, since
   // that pass is latency-bound) and the two passes run side by side instead
-  // of one after the other.  Measured to pay for the QKV and O projections
-  // only: with more ranges (down) or two matrices per tile (gate/up) the
-  // int4 pass needs the whole grid.
+  // of one after the other.  The bf16 share (of 256) was measured per
+  // projection kind: QKV and O (at most 2 ranges) 176, the FFN (gate/up,
+  // down) 128.
   int fmt_lo = 0, fmt_hi = 1;
-  if constexpr (EPI == EPI_PART || EPI == EPI_QKV) {
-    if (n_bf > 0 && n_i4 > 0 && wk.nwg >= 2 && a.nkc <= 2) {
-      const int nbf = min(wk.nwg - 1, max(1, (wk.nwg * kBfShare) >> 8));
+  if constexpr (EPI == EPI_PART || EPI == EPI_QKV || EPI == EPI_SWIGLU) {
+    if (n_bf > 0 && n_i4 > 0 && wk.nwg >= 2) {
+      const int share = (EPI == EPI_SWIGLU || a.nkc > 2) ? kBfShareFfn : kBfShare;
+      const int nbf = min(wk.nwg - 1, max(1, (wk.nwg * share) >> 8));
       if (wk.wg < nbf) {
         fmt_hi = 0;
         wk.nwg = nbf;
