@@ -32,9 +32,9 @@ HBM_PEAK_GBS = 8000.0
 # kv_shared_exit_amd/ee_probe (profiles/exit_head_lse_8b_traffic.md), each
 # scaled by what the same counter reads for a 1 GiB device copy.  Valid only
 # for the kernel sources it was measured on (their sha256); otherwise null.
-TRAFFIC = {"workload": "8b", "fetch_kib": 513391.9479, "write_kib": 64.0,
-           "fetch_scale": 1.9999337, "write_scale": 1.0,
-           "sources_sha256": "94e1a111fd5ad4ccf054ab4d6728fdf0b781cbbf7cb9f144d86c4ec123c2e266"}
+TRAFFIC = {"workload": "8b", "fetch_kib": 513404.6354, "write_kib": 64.0,
+           "fetch_scale": 1.9999340, "write_scale": 1.0,
+           "sources_sha256": "ecc91d042734f9c3c41a1e944dc9be00b9a55956f7639a78b5962c2d1cd69f16"}
 KERNEL_SOURCES = ("ee_proj.hip", "ee_device.h", "ee_internal.h")
 
 
