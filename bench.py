@@ -10,9 +10,11 @@ untimed, then ``--steps`` decode steps are timed (each step: all layers, exit
 heads, exit copies, final head, tokens and exit layers back on the host).
 
 Prints one JSON line: tokens/s, the roofline of the dominant kernel (the exit
-head's vocabulary GEMV, timed with HIP events on its stream during the timed
-steps), whole-step algorithmic bandwidth, the realised exit layers, and the
-oracle's decode speed on the host cores (a bounded sample).
+head's vocabulary GEMV, timed with HIP events it records on its stream during a
+rolled-back re-run of the timed steps), whole-step algorithmic bandwidth, the
+realised exit layers, the speedup over the plain full-depth decoder and over
+exit heads with unquantised exit copies (same exit layers), and the oracle's
+decode speed on the host cores (a bounded sample).
 """
 import argparse
 import json
@@ -106,6 +108,42 @@ def cpu_baseline(wl, weights, exit_layer, ctx):
                        f"{dt:.1f} s, float64 numpy")}
 
 
+def baselines(api, wl, weights, dev, stream, exits, W, K2, ms_main):
+    """The method against the decoders it replaces, on the same prompts and
+    weights, each timed over K2 graph-replayed steps after W warm-up steps:
+    (i) the plain decoder at full depth without exit heads (EE_EXIT_NONE);
+    (ii) exit heads with unquantised exit copies (EE_EXIT_BF16) and the exit
+    layers the timed run took, step by step (forced).  speedup = baseline time
+    per step / the method's time per step."""
+    import torch
+    from kv_shared_exit_amd import _binding as Bd
+    sh, B, P = wl.shape, wl.batch, wl.prompt_len
+    S = P + W + K2 + 1
+    import synth
+    prompts = synth.make_prompts(wl)
+    res = {}
+    for name, mode in (("full_depth_no_heads", Bd.EE_EXIT_NONE), ("bf16_exit_copies_same_exits", Bd.EE_EXIT_BF16)):
+        m = api.Model(sh, dev, gamma=wl.gamma, exit_mode=mode, max_batch=B, max_positions=S)
+        c = api.KVCache(m, B, S)
+        try:
+            api.prefill(m, c, prompts, stream=stream)
+            forced = (lambda s_: exits[s_ % len(exits)]) if mode == Bd.EE_EXIT_BF16 else (lambda s_: None)
+            for s_ in range(W):
+                api.decode_step(m, c, B, forced=forced(s_), stream=stream)
+            torch.cuda.synchronize()
+            t_start = time.perf_counter()
+            for s_ in range(K2):
+                api.decode_step(m, c, B, forced=forced(s_), stream=stream)
+            torch.cuda.synchronize()
+            res[name + "_ms_per_step"] = round(1e3 * (time.perf_counter() - t_start) / K2, 4)
+        finally:
+            c.close()
+            m.close()
+    return {"steps": K2, "method_ms_per_step": round(ms_main, 4), **res,
+            "vs_full_depth_no_heads": round(res["full_depth_no_heads_ms_per_step"] / ms_main, 4),
+            "vs_bf16_exit_copies_same_exits": round(res["bf16_exit_copies_same_exits_ms_per_step"] / ms_main, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +153,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true",
                     help="do not time the exit-head launches (no roofline figure)")
+    ap.add_argument("--no-baselines", action="store_true",
+                    help="skip the full-depth and bf16-exit-copy comparison runs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -267,6 +307,9 @@ def main():
         out["copy_probe"] = copy_probe
     cache.close()
     model.close()
+    if not args.no_baselines:
+        out["speedup"] = baselines(api, wl, weights, dev, stream, exits, W, min(K, 40), 1e3 * t_el / K)
+        log(f"baselines done ({time.time() - t0:.0f}s)")
     del dev
     if not args.no_cpu_baseline:
         ex = int(round(mean_exit))

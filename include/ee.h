@@ -65,6 +65,9 @@ typedef int32_t ee_status;
 
 #define EE_EXIT_INT4 0 /* exit copies are the int4 group-quantised layers */
 #define EE_EXIT_BF16 1 /* exit copies are the backbone layers themselves (test mode) */
+#define EE_EXIT_NONE 2 /* no exit heads: the plain decoder at full depth, the baseline
+                          the method is compared with (every exit layer is n_layers;
+                          head_T may be NULL; forced exits and gamma are ignored) */
 
 #define EE_KV_TRACK_OCCUPANCY 1u /* count writes per (layer, sequence, position) slot */
 
@@ -88,7 +91,7 @@ typedef struct ee_model_config {
   int32_t group_size;
   float rms_eps;
   float rope_theta;
-  int32_t exit_mode; /* EE_EXIT_INT4 or EE_EXIT_BF16 */
+  int32_t exit_mode; /* EE_EXIT_INT4, EE_EXIT_BF16 or EE_EXIT_NONE */
   int32_t max_batch;
   int32_t max_positions;
 } ee_model_config;
@@ -205,7 +208,7 @@ ee_status ee_decode_step(ee_model *m, ee_kv_cache *c, int32_t batch,
 /* Copies the int4 exit copy of one linear map of 1-based layer (2..L) back to the
  * host as int8 codes [nrows][K] and bf16 scales [nrows][K/G] (uint16 bits).
  * which: 0 wq, 1 wk, 2 wv, 3 wo, 4 w_gate, 5 w_up, 6 w_down.
- * UNSUPPORTED in EE_EXIT_BF16 mode. */
+ * UNSUPPORTED in EE_EXIT_BF16 and EE_EXIT_NONE modes. */
 ee_status ee_exit_weights_read(const ee_model *m, int32_t layer, int32_t which, int32_t row0,
                                int32_t nrows, int8_t *codes_host, uint16_t *scales_host);
 

@@ -25,6 +25,7 @@ EE_ERR_NOT_WRITTEN = -6
 EE_ERR_UNSUPPORTED = -7
 EE_EXIT_INT4 = 0
 EE_EXIT_BF16 = 1
+EE_EXIT_NONE = 2
 EE_KV_TRACK_OCCUPANCY = 1
 
 EXPORTS = [

@@ -183,7 +183,8 @@ void validate_config(const ee_model_config& c) {
        "n_heads must be a positive multiple of n_kv_heads");
   need(c.max_batch >= 1 && c.max_batch <= kMaxBatch, "max_batch must be in [1, 64]");
   need(c.max_positions >= 1, "max_positions must be >= 1");
-  need(c.exit_mode == EE_EXIT_INT4 || c.exit_mode == EE_EXIT_BF16, "bad exit_mode");
+  need(c.exit_mode == EE_EXIT_INT4 || c.exit_mode == EE_EXIT_BF16 || c.exit_mode == EE_EXIT_NONE,
+       "bad exit_mode");
   need(std::isfinite(c.rms_eps) && c.rms_eps > 0 && std::isfinite(c.rope_theta) && c.rope_theta > 0,
        "rms_eps and rope_theta must be positive");
   shape(c.group_size == 32 || c.group_size == 64 || c.group_size == 128, "group_size must be 32, 64 or 128");
@@ -266,6 +267,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
   const int hd = cf.head_dim, qd = H * hd, kvd = Hkv * hd, nqkv = qd + 2 * kvd;
   StepState* st = m->st;
   const bool int4 = cf.exit_mode == EE_EXIT_INT4;
+  heads = heads && cf.exit_mode != EE_EXIT_NONE;  // the plain decoder has no exit heads
 
   const size_t pstride = (size_t)kMaxBatch * d;  // elements between partial-sum ranges
   launch_init(st, prompt, P, t, B, L, m->tok_emb, d, cf.vocab, m->h, m->p_rec,
@@ -550,7 +552,7 @@ ee_status ee_create_model(const ee_model_config* cfg, const ee_weights* w, const
     for (int l = 0; l < c.n_layers; ++l) {
       const ee_layer_weights& lw = w->layers[l];
       if (!lw.attn_norm || !lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.ffn_norm || !lw.w_gate ||
-          !lw.w_up || !lw.w_down || (l + 1 < c.n_layers && !lw.head_T))
+          !lw.w_up || !lw.w_down || (l + 1 < c.n_layers && !lw.head_T && c.exit_mode != EE_EXIT_NONE))
         fail(EE_ERR_INVALID_ARG, "null weight pointer in layer " + std::to_string(l + 1));
     }
     std::vector<float> gam(c.n_layers > 1 ? c.n_layers - 1 : 0, 0.75f);
@@ -956,7 +958,7 @@ ee_status ee_exit_weights_read(const ee_model* m, int32_t layer, int32_t which, 
     check_model(m);
     if (!codes_host || !scales_host) fail(EE_ERR_INVALID_ARG, "null argument");
     const ee_model_config& cf = m->cfg;
-    if (cf.exit_mode != EE_EXIT_INT4) fail(EE_ERR_UNSUPPORTED, "no int4 copies in EE_EXIT_BF16 mode");
+    if (cf.exit_mode != EE_EXIT_INT4) fail(EE_ERR_UNSUPPORTED, "no int4 copies in this exit mode");
     if (layer < 2 || layer > cf.n_layers) fail(EE_ERR_INVALID_ARG, "layer must be in [2, L]");
     const LayerQ& q = m->lq[layer - 1];
     const int qd = cf.n_heads * cf.head_dim, kvd = cf.n_kv_heads * cf.head_dim;

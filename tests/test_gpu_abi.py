@@ -140,6 +140,37 @@ def test_no_exit_equals_unquantised_exit_copies_bitwise(api):
         np.testing.assert_array_equal(la, lb)
 
 
+def test_plain_decoder_mode_equals_no_exit_bitwise(api):
+    """EE_EXIT_NONE (the baseline: no exit heads, full depth) runs the same layer
+    arithmetic as the exit-head model when nobody exits (gamma > 1): tokens and
+    final logits bitwise equal, every exit layer = L; it needs no head weights,
+    and the graph-replayed step gives the same tokens."""
+    from kv_shared_exit_amd import _binding as B
+    sh = MID
+    w = synth.make_weights(sh, 5, alpha=np.full(sh.n_layers - 1, 1e3))
+    a = _run(api, sh, w, B.EE_EXIT_INT4, 1.5, 3, 6, 4)
+    w_nohead = {k: v for k, v in w.items() if k != "layers"}
+    w_nohead["layers"] = [{k: v for k, v in lw.items() if k != "head_T"} for lw in w["layers"]]
+    b = _run(api, sh, w_nohead, B.EE_EXIT_NONE, None, 3, 6, 4)
+    g = _run(api, sh, w_nohead, B.EE_EXIT_NONE, None, 3, 6, 4, graph=True)
+    for (ta, ea, la), (tb, eb, lb), (tg, eg, _) in zip(a, b, g):
+        assert np.all(ea == sh.n_layers) and np.all(eb == sh.n_layers) and np.all(eg == sh.n_layers)
+        np.testing.assert_array_equal(ta, tb)
+        np.testing.assert_array_equal(la, lb)
+        np.testing.assert_array_equal(tb, tg)
+
+
+def test_plain_decoder_mode_has_no_exit_copies(api):
+    from kv_shared_exit_amd import _binding as B
+    w, m = _model(api, ODD, exit_mode=B.EE_EXIT_NONE, max_batch=1, max_positions=4)
+    try:
+        with pytest.raises(B.EEError) as e:
+            m.exit_weights(2, "wq")
+        assert e.value.status == B.EE_ERR_UNSUPPORTED
+    finally:
+        m.close()
+
+
 def test_two_runs_are_bitwise_identical(api):
     from kv_shared_exit_amd import _binding as B
     sh = ODD
