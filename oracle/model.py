@@ -24,6 +24,14 @@ layers numbered l = 1..L and exit layer e in 1..L (e = L: no exit):
           exit iff p > gamma_l  (strict; AdaDecode section 2.2)  -> e = l
   token = argmax(E_out bf16(rmsnorm(h) * g_final)), lowest index on ties
 
+With criterion "sts" the exit head is replaced by River-LLM's state
+transition similarity (River-LLM explainer, sections 5.1-5.2): after layer l
+the cosine between the row's hidden state entering the layer and leaving it
+(each normalised to unit length, then the dot product, float64), and the row
+exits iff that similarity > tau_l (the per-layer thresholds take gamma's
+place).  The pages apply the threshold to the batch minimum; here, as for the
+exit head, each sequence decides for itself.
+
 The token of a step is the greedy argmax of the final LM head after the exit
 river has finished the remaining layers; the exit head only decides which
 copy runs the remaining layers (the reading under which "unquantised exit
@@ -255,6 +263,17 @@ def exit_head(model: OracleModel, layer: int, h: np.ndarray):
     return softmax_top1(logits), logits
 
 
+def state_transition_similarity(h_in: np.ndarray, h_out: np.ndarray) -> np.ndarray:
+    """Cosine similarity of a layer's input and output hidden states per row
+    (River-LLM explainer, section 5.1): each row scaled to unit length (norm
+    floored at 1e-12), then the dot product; float64."""
+    a = np.asarray(h_in, dtype=np.float64)
+    b = np.asarray(h_out, dtype=np.float64)
+    na = np.maximum(np.sqrt((a * a).sum(axis=-1)), 1e-12)
+    nb = np.maximum(np.sqrt((b * b).sum(axis=-1)), 1e-12)
+    return ((a / na[..., None]) * (b / nb[..., None])).sum(axis=-1)
+
+
 def final_head(model: OracleModel, h: np.ndarray):
     """Greedy token, top-2 logit gap and logits of the final LM head on rows h [n, d]."""
     y = rmsnorm(h, model.final_norm, model.shape.rms_eps)
@@ -272,19 +291,23 @@ def final_head(model: OracleModel, h: np.ndarray):
 # decode step, prefill, generation
 # ----------------------------------------------------------------------------
 def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=None,
-                trace: bool = False, heads: bool = True):
+                trace: bool = False, heads: bool = True, criterion: str = "head"):
     """One decode step for sequences 0..B-1 of ``cache`` (B = len(tokens)).
 
-    ``gamma``: per-layer thresholds gamma_1..gamma_{L-1} (scalar broadcasts).
-    ``forced``: optional int [B]; 0 lets the exit head decide, 1..L forces the
-    exit layer (the heads still run; their decision is overridden).
+    ``gamma``: per-layer thresholds gamma_1..gamma_{L-1} (scalar broadcasts);
+    with ``criterion="sts"`` they are the similarity thresholds tau_l.
+    ``forced``: optional int [B]; 0 lets the criterion decide, 1..L forces the
+    exit layer (the criterion is still evaluated; its decision is overridden).
     Returns ``(tokens [B], exit_layers [B], info)`` where info holds
-    ``p`` [B, L-1] (NaN where no head ran), ``head_absmax`` [B, L-1] (largest
-    |logit| of each evaluated exit head), ``gap`` [B], ``logits`` [B, V] and,
-    with ``trace``, ``hidden`` [B, L+1, d] (after the embedding and after every
-    layer).  ``heads=False`` skips the exit heads (no sequence exits); it is
-    used to sample full-depth states.
+    ``p`` [B, L-1] (the criterion's value: top-1 probability of the exit head,
+    or the state transition similarity; NaN where not evaluated),
+    ``head_absmax`` [B, L-1] (largest |logit| of each evaluated exit head),
+    ``gap`` [B], ``logits`` [B, V] and, with ``trace``, ``hidden`` [B, L+1, d]
+    (after the embedding and after every layer).  ``heads=False`` evaluates no
+    criterion (no sequence exits); it is used to sample full-depth states.
     """
+    if criterion not in ("head", "sts"):
+        raise ValueError(f"unknown criterion {criterion!r}")
     sh = model.shape
     L = sh.n_layers
     tokens = np.asarray(tokens, dtype=np.int64)
@@ -304,14 +327,19 @@ def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=N
     for l in range(1, L + 1):
         bb = np.nonzero(~exited)[0]
         ex = np.nonzero(exited)[0]
+        decide = heads and l < L and len(bb) > 0
+        h_in = h[bb].copy() if decide and criterion == "sts" else None
         if len(bb):
             _layer_rows(model, cache, l, bb, h, pos, use_exit=False)
         if len(ex):
             _layer_rows(model, cache, l, ex, h, pos, use_exit=True)
-        if heads and l < L and len(bb):
-            p, hl = exit_head(model, l, h[bb])
+        if decide:
+            if criterion == "head":
+                p, hl = exit_head(model, l, h[bb])
+                head_max[bb, l - 1] = np.abs(hl).max(axis=-1)
+            else:
+                p = state_transition_similarity(h_in, h[bb])
             p_rec[bb, l - 1] = p
-            head_max[bb, l - 1] = np.abs(hl).max(axis=-1)
             for i, b in enumerate(bb):
                 go = (l == forced[b]) if forced[b] > 0 else (p[i] > gamma[l - 1])
                 if go:
@@ -385,7 +413,7 @@ def prefill(model: OracleModel, cache: KVCache, prompts, trace: bool = False):
 
 
 def generate(model: OracleModel, cache: KVCache, prompts, steps: int, gamma=None,
-             forced_fn=None):
+             forced_fn=None, criterion: str = "head"):
     """Prefill, then ``steps`` decode steps feeding back each greedy token.
 
     ``forced_fn(step)`` may return a forced-exit array for a step.  Returns
@@ -395,7 +423,7 @@ def generate(model: OracleModel, cache: KVCache, prompts, steps: int, gamma=None
     toks, exits = [tok], []
     for s in range(steps):
         f = forced_fn(s) if forced_fn is not None else None
-        tok, e, _ = decode_step(model, cache, tok, gamma=gamma, forced=f)
+        tok, e, _ = decode_step(model, cache, tok, gamma=gamma, forced=f, criterion=criterion)
         toks.append(tok)
         exits.append(e)
     return np.stack(toks, axis=1), (np.stack(exits, axis=1) if exits else
