@@ -69,6 +69,19 @@ typedef int32_t ee_status;
                           the method is compared with (every exit layer is n_layers;
                           head_T may be NULL; forced exits and gamma are ignored) */
 
+/* Exit criterion evaluated after layers 1..L-1 for the sequences still on the
+ * backbone (not used with EE_EXIT_NONE):
+ *   EE_CRIT_HEAD  the exit head's top-1 probability p = max softmax(h T_l E^T)
+ *                 compared with gamma_l (AdaDecode explainer, sections 2.1-2.2);
+ *   EE_CRIT_STS   River-LLM's state transition similarity: the cosine between
+ *                 the sequence's hidden state entering layer l and leaving it,
+ *                 compared with tau_l (River-LLM explainer, sections 5.1-5.2),
+ *                 per sequence; the model's thresholds (and a step's gamma_host)
+ *                 are the tau_l, the exit heads do not run and head_T may be NULL.
+ * Either way a sequence exits iff its value > the layer's threshold. */
+#define EE_CRIT_HEAD 0
+#define EE_CRIT_STS 1
+
 #define EE_KV_TRACK_OCCUPANCY 1u /* count writes per (layer, sequence, position) slot */
 
 typedef struct ee_model ee_model;
@@ -94,6 +107,7 @@ typedef struct ee_model_config {
   int32_t exit_mode; /* EE_EXIT_INT4, EE_EXIT_BF16 or EE_EXIT_NONE */
   int32_t max_batch;
   int32_t max_positions;
+  int32_t criterion; /* EE_CRIT_HEAD or EE_CRIT_STS */
 } ee_model_config;
 
 /* Device pointers of one layer.  Shapes: attn_norm, ffn_norm [d]; wq [H*hd, d];
@@ -116,14 +130,16 @@ typedef struct ee_weights {
 /* Optional per-step diagnostics (host buffers; NULL members are skipped).
  * Requesting any of them runs the step without graph replay. */
 typedef struct ee_step_debug {
-  float *p_top1; /* [batch][L-1]: exit-head top-1 probability, NaN where no head ran */
+  float *p_top1; /* [batch][L-1]: the criterion's value (exit-head top-1 probability, or
+                    the state transition similarity), NaN where it was not evaluated */
   float *logits; /* [batch][V]: final LM-head logits */
   float *hidden; /* [batch][L+1][d]: residual after the embedding and after each layer */
   float *gap;    /* [batch]: top-1 minus top-2 final logit (+inf when V == 1) */
 } ee_step_debug;
 
 /* Creates a model.  cfg, w: host structs describing borrowed device weights.
- * gamma: host [n_layers - 1] per-layer thresholds, or NULL for 0.75 everywhere.
+ * gamma: host [n_layers - 1] per-layer thresholds (gamma_l, or tau_l with
+ * EE_CRIT_STS), or NULL for 0.75 everywhere.
  * Builds the int4 exit copies of layers 2..L on the device (synchronously).
  * Errors: INVALID_ARG (nulls, values), SHAPE (unsupported shape),
  * OUT_OF_MEMORY, HIP. */

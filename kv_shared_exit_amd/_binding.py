@@ -26,6 +26,8 @@ EE_ERR_UNSUPPORTED = -7
 EE_EXIT_INT4 = 0
 EE_EXIT_BF16 = 1
 EE_EXIT_NONE = 2
+EE_CRIT_HEAD = 0
+EE_CRIT_STS = 1
 EE_KV_TRACK_OCCUPANCY = 1
 
 EXPORTS = [
@@ -47,7 +49,7 @@ class ModelConfig(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("d_ff", C.c_int32),
                 ("vocab", C.c_int32), ("group_size", C.c_int32), ("rms_eps", C.c_float),
                 ("rope_theta", C.c_float), ("exit_mode", C.c_int32), ("max_batch", C.c_int32),
-                ("max_positions", C.c_int32)]
+                ("max_positions", C.c_int32), ("criterion", C.c_int32)]
 
 
 class LayerWeights(C.Structure):

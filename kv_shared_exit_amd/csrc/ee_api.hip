@@ -77,6 +77,8 @@ struct ee_model {
   uint16_t *qrot = nullptr, *attn_o = nullptr;
   uint16_t *act = nullptr, *z = nullptr;
   float* head_part = nullptr;
+  float* h2 = nullptr;   // residual after attention while the layer's input is kept in h (EE_CRIT_STS) [b][d]
+  float* sts = nullptr;  // state transition similarity per sequence [64]
   float* attn_part = nullptr;
   int nch_max = 0;
   StepState* st = nullptr;
@@ -185,6 +187,7 @@ void validate_config(const ee_model_config& c) {
   need(c.max_positions >= 1, "max_positions must be >= 1");
   need(c.exit_mode == EE_EXIT_INT4 || c.exit_mode == EE_EXIT_BF16 || c.exit_mode == EE_EXIT_NONE,
        "bad exit_mode");
+  need(c.criterion == EE_CRIT_HEAD || c.criterion == EE_CRIT_STS, "bad criterion");
   need(std::isfinite(c.rms_eps) && c.rms_eps > 0 && std::isfinite(c.rope_theta) && c.rope_theta > 0,
        "rms_eps and rope_theta must be positive");
   shape(c.group_size == 32 || c.group_size == 64 || c.group_size == 128, "group_size must be 32, 64 or 128");
@@ -267,7 +270,8 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
   const int hd = cf.head_dim, qd = H * hd, kvd = Hkv * hd, nqkv = qd + 2 * kvd;
   StepState* st = m->st;
   const bool int4 = cf.exit_mode == EE_EXIT_INT4;
-  heads = heads && cf.exit_mode != EE_EXIT_NONE;  // the plain decoder has no exit heads
+  heads = heads && cf.exit_mode != EE_EXIT_NONE;  // the plain decoder evaluates no criterion
+  const bool sts_crit = cf.criterion == EE_CRIT_STS;
 
   const size_t pstride = (size_t)kMaxBatch * d;  // elements between partial-sum ranges
   launch_init(st, prompt, P, t, B, L, m->tok_emb, d, cf.vocab, m->h, m->p_rec,
@@ -358,7 +362,11 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       a.y_stride = d;
       a.y_cstride = (int)pstride;
       const int nkc = launch_proj(EPI_PART, a, kNwg, B, s);
-      launch_finish(m->h, m->parts, nkc, pstride, B, d, (const uint16_t*)w.ffn_norm, cf.rms_eps, m->xn, nullptr, s);
+      // with the similarity criterion the layer's input stays in h (the
+      // residual after attention goes to h2) until the layer's end
+      float* h_mid = heads && sts_crit && l < L ? m->h2 : m->h;
+      launch_finish(h_mid, m->h, m->parts, nkc, pstride, B, d, (const uint16_t*)w.ffn_norm, cf.rms_eps, m->xn,
+                    nullptr, nullptr, nullptr, s);
     }
     {
       ProjArgs a = base_args(m);
@@ -382,7 +390,8 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       a.y_stride = F;
       launch_proj(EPI_SWIGLU, a, kNwg, B, s);
     }
-    const bool head_here = heads && l < L;
+    const bool head_here = heads && l < L;          // the criterion is evaluated after this layer
+    const bool sts_here = head_here && sts_crit;
     {
       ProjArgs a = base_args(m);
       a.N = d;
@@ -405,10 +414,15 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       // the next projection's input: the next layer's attention norm, or the
       // final norm before the LM head; bf16(h) for this layer's exit head
       const void* g_next = l < L ? m->lw[l].attn_norm : (const void*)m->final_norm;
-      launch_finish(m->h, m->parts, nkc, pstride, B, d, (const uint16_t*)g_next, cf.rms_eps, m->xn,
-                    head_here ? m->hb : nullptr, s);
+      if (sts_here)  // h = h2 + partials; sts = cos(layer input in h, new h)
+        launch_finish(m->h, m->h2, m->parts, nkc, pstride, B, d, (const uint16_t*)g_next, cf.rms_eps, m->xn,
+                      nullptr, m->h, m->sts, s);
+      else
+        launch_finish(m->h, m->h, m->parts, nkc, pstride, B, d, (const uint16_t*)g_next, cf.rms_eps, m->xn,
+                      head_here ? m->hb : nullptr, nullptr, nullptr, s);
     }
-    if (head_here) {
+    if (sts_here) launch_decide(st, nullptr, 0, m->d_gamma, l, L, B, m->p_rec, m->sts, s);
+    if (head_here && !sts_crit) {
       {
         ProjArgs a = base_args(m);
         a.N = d;
@@ -436,7 +450,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
         prof_events(m, &e0, &e1);
         launch_proj(EPI_LSE, a, kNwg, B, s, e0, e1);
       }
-      launch_decide(st, m->head_part, kNwg, m->d_gamma, l, L, B, m->p_rec, s);
+      launch_decide(st, m->head_part, kNwg, m->d_gamma, l, L, B, m->p_rec, nullptr, s);
     }
     if (dbg.hidden)
       HIPCHK(hipMemcpy2DAsync(m->dbg_hidden + (size_t)l * d, (size_t)(L + 1) * d * 4, m->h,
@@ -552,7 +566,8 @@ ee_status ee_create_model(const ee_model_config* cfg, const ee_weights* w, const
     for (int l = 0; l < c.n_layers; ++l) {
       const ee_layer_weights& lw = w->layers[l];
       if (!lw.attn_norm || !lw.wq || !lw.wk || !lw.wv || !lw.wo || !lw.ffn_norm || !lw.w_gate ||
-          !lw.w_up || !lw.w_down || (l + 1 < c.n_layers && !lw.head_T && c.exit_mode != EE_EXIT_NONE))
+          !lw.w_up || !lw.w_down ||
+          (l + 1 < c.n_layers && !lw.head_T && c.exit_mode != EE_EXIT_NONE && c.criterion == EE_CRIT_HEAD))
         fail(EE_ERR_INVALID_ARG, "null weight pointer in layer " + std::to_string(l + 1));
     }
     std::vector<float> gam(c.n_layers > 1 ? c.n_layers - 1 : 0, 0.75f);
@@ -631,6 +646,8 @@ ee_status ee_create_model(const ee_model_config* cfg, const ee_weights* w, const
       m->act = m->alloc<uint16_t>((size_t)Bm * F);
       m->z = m->alloc<uint16_t>((size_t)Bm * d);
       m->head_part = m->alloc<float>((size_t)kNwg * kMaxBatch * 4);
+      m->h2 = m->alloc<float>((size_t)Bm * d);
+      m->sts = m->alloc<float>(kMaxBatch);
       // the most partials any cache (S <= max_positions, B >= 1) can need: the
       // split is not monotone in S, so take the maximum over every tile count
       m->nch_max = 1;

@@ -89,18 +89,24 @@ int launch_proj(int epi, const ProjArgs& a, int nwg, int batch, hipStream_t s, h
 const int32_t* no_rows();
 // The column ranges EPI_PART uses for K columns, N rows (and their width).
 int proj_ranges(int K, int N, int nwg, int batch, int* kc);
-// h[b] += sum_c parts[c][b] for b < B (nparts may be 0); then x[b] =
-// bf16(rmsnorm(h[b]) * gain), and when hb is set, hb[b] = bf16(h[b]).
-void launch_finish(float* h, const float* parts, int nparts, size_t cstride, int B, int d,
-                   const uint16_t* gain, float eps, uint16_t* x, uint16_t* hb, hipStream_t s);
+// h[b] = hsrc[b] + sum_c parts[c][b] for b < B (hsrc may be h; nparts may be
+// 0); then x[b] = bf16(rmsnorm(h[b]) * gain), and when hb is set,
+// hb[b] = bf16(h[b]).  With hin and sts both set, sts[b] = cos(hin[b], h[b])
+// (hin may be h: each element is read before it is overwritten).
+void launch_finish(float* h, const float* hsrc, const float* parts, int nparts, size_t cstride, int B, int d,
+                   const uint16_t* gain, float eps, uint16_t* x, uint16_t* hb, const float* hin, float* sts,
+                   hipStream_t s);
 // Step setup: h[b] = embedding of the input token, x[b] = bf16(rmsnorm(h[b]) *
 // gain) (the first layer's attention input), exit state and row lists reset.
 void launch_init(StepState* st, const int32_t* prompt, int P, int t, int B, int L,
                  const uint16_t* emb, int d, int V, float* h, float* p_rec, const uint16_t* gain,
                  float eps, uint16_t* x, hipStream_t s);
 void launch_attention(const AttnArgs& a, hipStream_t s);
+// Exit decision after layer `layer` for the rows on the backbone: from the exit
+// head's nwg (max, sum exp) partials, or, when sts is set, from the state
+// transition similarity per sequence (nwg and part unused).
 void launch_decide(StepState* st, const float* part, int nwg, const float* gamma, int layer,
-                   int L, int B, float* p_rec, hipStream_t s);
+                   int L, int B, float* p_rec, const float* sts, hipStream_t s);
 void launch_final(StepState* st, const float* part, int nwg, int B, int V, int32_t* lens, int advance,
                   hipStream_t s);
 void launch_advance(int32_t* lens, int B, hipStream_t s);

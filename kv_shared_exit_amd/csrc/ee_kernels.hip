@@ -350,33 +350,41 @@ __device__ __forceinline__ void load_lse_parts(const float* part, int nwg, int i
   }
 }
 
+// STS: the value of a row is its state transition similarity sts[b] (read by
+// lane 0 of the row's wave) instead of the exit head's p.
+template <bool STS>
 __global__ __launch_bounds__(kHeadThreads) void decide_kernel(StepState* st, const float* part, int nwg,
                                                               const float* gamma, int layer, int L, int B,
-                                                              float* p_rec) {
+                                                              float* p_rec, const float* sts) {
   __shared__ int sx[kMaxBatch];
   __shared__ int sn;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   // the first row of each wave is requested before the row count is known
   // (list positions below kMaxBatch are always in bounds)
   float2 v[kPartPerLane];
-  load_lse_parts(part, nwg, w, lane, v);
+  if constexpr (!STS) load_lse_parts(part, nwg, w, lane, v);
   if ((int)threadIdx.x < B) sx[threadIdx.x] = st->exited[threadIdx.x];
   if (threadIdx.x == 0) sn = min(max(st->n_act, 0), B);
   __syncthreads();
   const int n = sn;
   for (int i = w; i < n; i += kHeadWaves) {
-    if (i != w) load_lse_parts(part, nwg, i, lane, v);
     const int b = st->act[i];
-    float m = -INFINITY, s = 0.0f;
+    float p = 0.0f;
+    if constexpr (STS) {
+      p = sts[b];
+    } else {
+      if (i != w) load_lse_parts(part, nwg, i, lane, v);
+      float m = -INFINITY, s = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kPartPerLane; ++j) lse_merge(m, s, v[j].x, v[j].y);
+      for (int j = 0; j < kPartPerLane; ++j) lse_merge(m, s, v[j].x, v[j].y);
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
-      lse_merge(m, s, m2, s2);
+      for (int o = 1; o < 64; o <<= 1) {
+        const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
+        lse_merge(m, s, m2, s2);
+      }
+      p = 1.0f / s;
     }
     if (lane == 0) {
-      const float p = 1.0f / s;
       const int f = st->forced[b];
       const bool ex = f > 0 ? (layer == f) : (p > gamma[layer - 1]);
       if (p_rec) p_rec[(layer - 1) * kMaxBatch + b] = p;
@@ -408,9 +416,15 @@ __global__ __launch_bounds__(kHeadThreads) void decide_kernel(StepState* st, con
 }
 
 void launch_decide(StepState* st, const float* part, int nwg, const float* gamma, int layer, int L,
-                   int B, float* p_rec, hipStream_t s) {
+                   int B, float* p_rec, const float* sts, hipStream_t s) {
+  if (sts) {
+    hipLaunchKernelGGL(decide_kernel<true>, dim3(1), dim3(kHeadThreads), 0, s, st, part, nwg, gamma, layer, L, B,
+                       p_rec, sts);
+    return;
+  }
   if (nwg < 1 || nwg > kNwgMax) throw std::logic_error("decide: partial count out of range");
-  hipLaunchKernelGGL(decide_kernel, dim3(1), dim3(kHeadThreads), 0, s, st, part, nwg, gamma, layer, L, B, p_rec);
+  hipLaunchKernelGGL(decide_kernel<false>, dim3(1), dim3(kHeadThreads), 0, s, st, part, nwg, gamma, layer, L, B,
+                     p_rec, sts);
 }
 
 __global__ __launch_bounds__(kHeadThreads) void final_kernel(StepState* st, const float* part, int nwg, int B,

@@ -912,10 +912,13 @@ int launch_proj(int epi, const ProjArgs& a0, int nwg, int batch, hipStream_t s, 
 }
 
 // ---------------------------------------------------------------------------
-// Residual finish: h += sum of the partial sums of the column ranges (fixed
-// order), then the RMSNorm of the new residual for the next projection
-// (bf16(h * rsqrt(mean(h^2) + eps) * g)) and optionally bf16(h).  One
-// workgroup per row.
+// Residual finish: h = hsrc + the partial sums of the column ranges (fixed
+// order; hsrc may be h itself), then the RMSNorm of the new residual for the
+// next projection (bf16(h * rsqrt(mean(h^2) + eps) * g)) and optionally
+// bf16(h).  With STS, also the state transition similarity of the row
+// (River-LLM explainer, section 5.1): the cosine between the layer's input
+// hin and the new residual, dot / (|hin| |h|) with each norm floored at 1e-12
+// (hin is read before h is written, so it may be h).  One workgroup per row.
 // ---------------------------------------------------------------------------
 constexpr int kFinThreads = 256;
 constexpr int kFinVec = 4;    // float4 per thread per row chunk
@@ -925,31 +928,37 @@ constexpr int kFinParts = 8;  // column ranges summed with all loads in flight
 // held in registers between the sum of squares and the normalisation; wider
 // rows are processed in chunks and re-read (this workgroup wrote them).  Every
 // load of a chunk (residual, partial sums, gains) is issued before any is used.
-__global__ __launch_bounds__(kFinThreads) void finish_kernel(float* h, const float* parts, int nparts, size_t cstride,
-                                                             int d, const uint16_t* gain, float eps, uint16_t* x,
-                                                             uint16_t* hb) {
+template <bool STS>
+__global__ __launch_bounds__(kFinThreads) void finish_kernel(float* h, const float* hsrc, const float* parts,
+                                                             int nparts, size_t cstride, int d, const uint16_t* gain,
+                                                             float eps, uint16_t* x, uint16_t* hb, const float* hin,
+                                                             float* sts) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int d4 = d >> 2;
   float* hr = h + (size_t)b * d;
+  const float* hs = hsrc + (size_t)b * d;
+  const float* hi = STS ? hin + (size_t)b * d : hs;
   const int per = kFinThreads * kFinVec;  // float4 per chunk
   const bool one = d4 <= per;
-  float ss = 0.0f;
+  float ss = 0.0f, si = 0.0f, sd = 0.0f;
   float4 v[kFinVec];
   uint2 g[kFinVec];
-  // ranges past nparts reload the last one (or, with none, the residual row
+  // ranges past nparts reload the last one (or, with none, the source row
   // itself: parts may be null then) and are not added; every load of a chunk
   // is unconditional (a branch around a load makes the compiler wait for the
   // loads before it)
-  const float* pbase = nparts > 0 ? parts + (size_t)b * d : hr;
+  const float* pbase = nparts > 0 ? parts + (size_t)b * d : hs;
   const size_t pcs = nparts > 0 ? cstride : 0;
   const int plast = max(nparts - 1, 0);
   for (int c0 = 0; c0 < d4; c0 += per) {
     float4 pv[kFinParts][kFinVec];
+    float4 vi[kFinVec];
 #pragma unroll
     for (int j = 0; j < kFinVec; ++j) {
       const int i = min(c0 + tid + j * kFinThreads, d4 - 1);
-      v[j] = *(const float4*)(hr + 4 * i);
+      v[j] = *(const float4*)(hs + 4 * i);
+      if constexpr (STS) vi[j] = *(const float4*)(hi + 4 * i);
       g[j] = *(const uint2*)(gain + 4 * i);
 #pragma unroll
       for (int c = 0; c < kFinParts; ++c) pv[c][j] = *(const float4*)(pbase + min(c, plast) * pcs + 4 * i);
@@ -975,11 +984,21 @@ __global__ __launch_bounds__(kFinThreads) void finish_kernel(float* h, const flo
       }
       const int i = c0 + tid + j * kFinThreads;
       if (i >= d4) continue;
-      if (nparts > 0) *(float4*)(hr + 4 * i) = v[j];
+      *(float4*)(hr + 4 * i) = v[j];
       ss = fmaf(v[j].x, v[j].x, ss);
       ss = fmaf(v[j].y, v[j].y, ss);
       ss = fmaf(v[j].z, v[j].z, ss);
       ss = fmaf(v[j].w, v[j].w, ss);
+      if constexpr (STS) {
+        si = fmaf(vi[j].x, vi[j].x, si);
+        si = fmaf(vi[j].y, vi[j].y, si);
+        si = fmaf(vi[j].z, vi[j].z, si);
+        si = fmaf(vi[j].w, vi[j].w, si);
+        sd = fmaf(vi[j].x, v[j].x, sd);
+        sd = fmaf(vi[j].y, v[j].y, sd);
+        sd = fmaf(vi[j].z, v[j].z, sd);
+        sd = fmaf(vi[j].w, v[j].w, sd);
+      }
       if (hb) {
         uint2 o;
         o.x = f2bf(v[j].x) | (f2bf(v[j].y) << 16);
@@ -988,16 +1007,32 @@ __global__ __launch_bounds__(kFinThreads) void finish_kernel(float* h, const flo
       }
     }
   }
-  __shared__ float wsum[kFinThreads / 64];
+  constexpr int kW = kFinThreads / 64;
+  __shared__ float wsum[3][kW];
   __shared__ float rs;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
-  if ((tid & 63) == 0) wsum[tid >> 6] = ss;
+  for (int o = 32; o >= 1; o >>= 1) {
+    ss += __shfl_xor(ss, o);
+    if constexpr (STS) {
+      si += __shfl_xor(si, o);
+      sd += __shfl_xor(sd, o);
+    }
+  }
+  if ((tid & 63) == 0) {
+    wsum[0][tid >> 6] = ss;
+    wsum[1][tid >> 6] = si;
+    wsum[2][tid >> 6] = sd;
+  }
   __syncthreads();
   if (tid == 0) {
-    float t = 0.0f;
-    for (int w = 0; w < kFinThreads / 64; ++w) t += wsum[w];
+    float t = 0.0f, ti = 0.0f, td = 0.0f;
+    for (int w = 0; w < kW; ++w) {
+      t += wsum[0][w];
+      ti += wsum[1][w];
+      td += wsum[2][w];
+    }
     rs = 1.0f / sqrtf(t / (float)d + eps);
+    if constexpr (STS) sts[b] = td / (fmaxf(sqrtf(ti), 1e-12f) * fmaxf(sqrtf(t), 1e-12f));
   }
   __syncthreads();
   const float r = rs;
@@ -1030,11 +1065,17 @@ __global__ __launch_bounds__(kFinThreads) void finish_kernel(float* h, const flo
   }
 }
 
-void launch_finish(float* h, const float* parts, int nparts, size_t cstride, int B, int d, const uint16_t* gain,
-                   float eps, uint16_t* x, uint16_t* hb, hipStream_t s) {
-  if (!gain || !x || (nparts > 0 && !parts) || d % 4) throw std::logic_error("finish: bad arguments");
-  hipLaunchKernelGGL(finish_kernel, dim3(B), dim3(kFinThreads), 0, s, h, parts, nparts, cstride, d, gain, eps, x,
-                     hb);
+void launch_finish(float* h, const float* hsrc, const float* parts, int nparts, size_t cstride, int B, int d,
+                   const uint16_t* gain, float eps, uint16_t* x, uint16_t* hb, const float* hin, float* sts,
+                   hipStream_t s) {
+  if (!h || !hsrc || !gain || !x || (nparts > 0 && !parts) || d % 4 || (!hin != !sts))
+    throw std::logic_error("finish: bad arguments");
+  if (sts)
+    hipLaunchKernelGGL(finish_kernel<true>, dim3(B), dim3(kFinThreads), 0, s, h, hsrc, parts, nparts, cstride, d,
+                       gain, eps, x, hb, hin, sts);
+  else
+    hipLaunchKernelGGL(finish_kernel<false>, dim3(B), dim3(kFinThreads), 0, s, h, hsrc, parts, nparts, cstride, d,
+                       gain, eps, x, hb, hin, sts);
 }
 
 // ---------------------------------------------------------------------------

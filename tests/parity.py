@@ -24,7 +24,13 @@ same step (which itself must stay within the tolerances):
   * exit-head probabilities must agree to what the logit tolerance implies:
     p = 1 / sum_v exp(l_v - max l), so perturbing every logit by at most d
     moves ln p by at most 2 d; with d = 2e-2 * max|l| of the head,
-    |ln p_gpu - ln p_oracle| <= 4e-2 * max|l|.
+    |ln p_gpu - ln p_oracle| <= 4e-2 * max|l|;
+  * with the state-transition-similarity criterion, the similarity after
+    layer l must agree to what the hidden states' agreement implies: moving
+    a by da changes cos(a, b) by at most 2 |da| / |a|, so
+    |s_gpu - s_oracle| <= 2 (r_{l-1} + r_l) + 1e-6 with r the norm-relative
+    error of the GPU's hidden state before and after the layer (the same
+    bound decides whether a differing exit is a near tie).
 """
 from __future__ import annotations
 
@@ -70,17 +76,26 @@ class Result:
         self.worst[key] = max(self.worst.get(key, 0.0), v)
 
 
+def _normrel(a, r):
+    a = np.asarray(a, np.float64)
+    r = np.asarray(r, np.float64)
+    return float(np.linalg.norm(a - r) / max(np.linalg.norm(r), 1e-30))
+
+
 def run_parity(shape, weights, batch, P, steps, gamma, exit_mode="int4", forced_fn=None,
-               prompts=None, max_seq=None, check_kv=True, check_hidden=True, label=""):
+               prompts=None, max_seq=None, check_kv=True, check_hidden=True, label="", criterion="head"):
     import torch
     from kv_shared_exit_amd import api, _binding as B
 
     L = shape.n_layers
     S = max_seq or (P + steps + 1)
     mode = B.EE_EXIT_INT4 if exit_mode == "int4" else B.EE_EXIT_BF16
+    sts = criterion == "sts"
+    assert not sts or check_hidden, "the similarity bound needs the hidden states"
     t0 = time.time()
     dev = api.upload_weights(weights)
-    model = api.Model(shape, dev, gamma=gamma, exit_mode=mode, max_batch=batch, max_positions=S)
+    model = api.Model(shape, dev, gamma=gamma, exit_mode=mode, max_batch=batch, max_positions=S,
+                      criterion=B.EE_CRIT_STS if sts else B.EE_CRIT_HEAD)
     cache = api.KVCache(model, batch, S, track=True)
     orc = om.OracleModel(shape, weights, exit_mode=exit_mode)
     ocache = om.KVCache(shape, batch, S)
@@ -108,7 +123,8 @@ def run_parity(shape, weights, batch, P, steps, gamma, exit_mode="int4", forced_
         gam = np.broadcast_to(np.asarray(gamma, np.float64), (L - 1,))
         for s in range(steps):
             forced = np.zeros(batch, np.int32) if forced_fn is None else np.asarray(forced_fn(s), np.int32)
-            to, eo, io = om.decode_step(orc, ocache, tok_in, gamma=gam, forced=forced, trace=check_hidden)
+            to, eo, io = om.decode_step(orc, ocache, tok_in, gamma=gam, forced=forced, trace=check_hidden,
+                                        criterion=criterion)
             fg = forced.copy()
             for b in range(batch):
                 if forced[b] == 0:
@@ -130,8 +146,14 @@ def run_parity(shape, weights, batch, P, steps, gamma, exit_mode="int4", forced_
                 for b in bad:
                     l = int(min(egpu[b], eo[b]))          # first decision that differs
                     pg, po = float(dbg["p"][b, l - 1]), float(io["p"][b, l - 1])
-                    bound = 2 * TOL * float(io["head_absmax"][b, l - 1])
-                    assert (pg - gam[l - 1]) * (po - gam[l - 1]) <= 0 and abs(np.log(pg) - np.log(po)) <= bound, (
+                    if sts:
+                        bound = 2 * (_normrel(dbg["hidden"][b, l - 1], io["hidden"][b, l - 1]) +
+                                     _normrel(dbg["hidden"][b, l], io["hidden"][b, l])) + 1e-6
+                        near = abs(pg - po) <= bound
+                    else:
+                        bound = 2 * TOL * float(io["head_absmax"][b, l - 1])
+                        near = abs(np.log(pg) - np.log(po)) <= bound
+                    assert (pg - gam[l - 1]) * (po - gam[l - 1]) <= 0 and near, (
                         f"{label} step {s} b={b}: exit gpu {egpu[b]} oracle {eo[b]} not a near tie "
                         f"(p gpu {pg:.6f} oracle {po:.6f} gamma {gam[l - 1]})")
                     fg[b] = eo[b]
@@ -161,7 +183,15 @@ def run_parity(shape, weights, batch, P, steps, gamma, exit_mode="int4", forced_
                 np.testing.assert_array_equal(np.isnan(pg), np.isnan(po),
                                               err_msg=f"{label} step {s} b={b} heads evaluated")
                 ok = np.isfinite(po)
-                if ok.any():
+                if ok.any() and sts:
+                    for l in np.nonzero(ok)[0] + 1:
+                        bound = 2 * (_normrel(dbg["hidden"][b, l - 1], io["hidden"][b, l - 1]) +
+                                     _normrel(dbg["hidden"][b, l], io["hidden"][b, l])) + 1e-6
+                        e = abs(float(pg[l - 1]) - float(po[l - 1]))
+                        res.note("sts_abs", e)
+                        res.note("sts_over_bound", e / bound)
+                        assert e <= bound, f"{label} step {s} b={b} layer {l}: similarity err {e:.3g} > {bound:.3g}"
+                elif ok.any():
                     e = float(np.abs(pg[ok] - po[ok]).max())
                     res.note("p_abs", e)
                     dl = np.abs(np.log(pg[ok]) - np.log(po[ok]))

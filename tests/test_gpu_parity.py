@@ -119,3 +119,66 @@ def test_gqa4_head_dim_64(gpu):
     from parity import run_parity
     sh, w = _weights("gqa4", 2.0, 20, 3)
     run_parity(sh, w, 4, 20, 3, 0.75, label="gqa4")
+
+
+# ---------------------------------------------------------------------------
+# River-LLM's state transition similarity as the exit criterion
+# ---------------------------------------------------------------------------
+def _median_similarity(sh, w, B, P, steps, seed):
+    """Per-layer median of the oracle's similarity values at full depth (tau = 1:
+    nobody exits) on prompts of another seed: thresholds that split the rows."""
+    from oracle import model as om
+    m = om.OracleModel(sh, w)
+    c = om.KVCache(sh, B, P + steps + 1)
+    tok, _ = om.prefill(m, c, np.random.default_rng(seed).integers(0, sh.vocab, (B, P)))
+    vals = []
+    for _ in range(steps):
+        tok, _, info = om.decode_step(m, c, tok, gamma=1.0, criterion="sts")
+        vals.append(info["p"])
+    return np.median(np.concatenate(vals, axis=0), axis=0)
+
+
+@pytest.mark.parametrize("name,batch,P,steps", [("tiny", 3, 9, 8), ("odd", 4, 7, 6), ("gqa4", 4, 12, 5)])
+def test_similarity_criterion_against_oracle(gpu, name, batch, P, steps):
+    from parity import run_parity
+    sh = SHAPES[name]
+    w = synth.make_weights(sh, 31)
+    tau = _median_similarity(sh, w, batch, P, steps, seed=99)
+    res = run_parity(sh, w, batch, P, steps, tau, criterion="sts", label=f"{name}-sts")
+    exits = np.concatenate(res.exits)
+    assert (exits < sh.n_layers).any() and (exits > 1).any(), "thresholds should split the rows"
+    assert res.compared_tokens >= batch * steps // 2
+
+
+def test_similarity_extremes_equal_the_head_extremes_bitwise(gpu):
+    """tau = 1 (nobody exits) runs what the exit-head model runs at gamma = 2,
+    and tau = -1.5 (everybody exits after layer 1) what it runs at gamma = -1:
+    tokens, exit layers and K/V bitwise equal (the criterion only decides)."""
+    from kv_shared_exit_amd import api, _binding as B
+    sh = SHAPES["odd"]
+    w = synth.make_weights(sh, 31)
+    dev = api.upload_weights(w)
+    P, steps, batch = 6, 5, 3
+    prompts = np.random.default_rng(4).integers(0, sh.vocab, (batch, P)).astype(np.int32)
+
+    def run(crit, g):
+        m = api.Model(sh, dev, gamma=g, criterion=crit, max_batch=batch, max_positions=P + steps + 1)
+        c = api.KVCache(m, batch, P + steps + 1)
+        try:
+            api.prefill(m, c, prompts)
+            out = [api.decode_step(m, c, batch) for _ in range(steps)]
+            kv = [c.read(l, b, 0, P + steps) for l in range(1, sh.n_layers + 1) for b in range(batch)]
+        finally:
+            c.close()
+            m.close()
+        return out, kv
+
+    for (g_sts, g_head, e_all) in ((1.0, 2.0, sh.n_layers), (-1.5, -1.0, 1)):
+        a, ka = run(B.EE_CRIT_STS, g_sts)
+        b, kb = run(B.EE_CRIT_HEAD, g_head)
+        for (ta, ea), (tb, eb) in zip(a, b):
+            assert np.all(ea == e_all) and np.all(eb == e_all)
+            np.testing.assert_array_equal(ta, tb)
+        for (k1, v1), (k2, v2) in zip(ka, kb):
+            np.testing.assert_array_equal(k1, k2)
+            np.testing.assert_array_equal(v1, v2)
