@@ -53,12 +53,13 @@ def kernel_sources_sha256():
     return h.hexdigest()
 
 
-def step_bytes(sh, exits, ctx, B):
+def step_bytes(sh, exits, ctx, B, head_bytes=True):
     """Algorithmic HBM bytes of one decode step given the realised exit layers.
 
     Per layer l: bf16 weights when some row is still on the backbone (e_b >= l),
     int4 codes + bf16 scales when some row has exited (e_b < l), the exit head
-    (T and E) when l < L and some row is on the backbone; then the final LM head,
+    (T and E) when l < L and some row is on the backbone (not with the
+    similarity criterion, which reads no weights); then the final LM head,
     K/V reads of every row's context, K/V writes and the embedding rows."""
     L, d, V, G = sh.n_layers, sh.d_model, sh.vocab, sh.group
     n = sh.params_per_layer()
@@ -74,7 +75,7 @@ def step_bytes(sh, exits, ctx, B):
         if X:
             tot += w_i4
         if l < L and A:
-            tot += 2 * d * d + 2 * V * d
+            tot += (2 * d * d + 2 * V * d) if head_bytes else 0
             heads += 1
     tot += 2 * V * d
     kv_row = 2 * sh.n_kv_heads * sh.head_dim * 2
@@ -82,7 +83,7 @@ def step_bytes(sh, exits, ctx, B):
     return tot, heads
 
 
-def cpu_baseline(wl, weights, exit_layer, ctx):
+def cpu_baseline(wl, weights, exit_layer, ctx, criterion="head"):
     """The oracle's decode speed: one decode step of one sequence at the workload's shape,
     with a synthetic (seeded) KV context of ``ctx`` positions and a forced exit layer."""
     from threadpoolctl import threadpool_info
@@ -99,16 +100,17 @@ def cpu_baseline(wl, weights, exit_layer, ctx):
     cache.V[:, :, :, :ctx] = kv[:, :, :, ::-1].astype(np.float32)
     cache.lens[0] = ctx
     t0 = time.perf_counter()
-    om.decode_step(orc, cache, [1], gamma=wl.gamma, forced=[exit_layer])
+    om.decode_step(orc, cache, [1], gamma=wl.gamma, forced=[exit_layer], criterion=criterion)
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     return {"value": round(1.0 / dt, 5), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"1 decode step of 1 sequence, {sh.n_layers}-layer d{sh.d_model} shape, "
-                       f"synthetic {ctx}-position KV context, forced exit after layer {exit_layer}; "
+                       f"synthetic {ctx}-position KV context, forced exit after layer {exit_layer}, "
+                       f"{'similarity' if criterion == 'sts' else 'exit-head'} criterion evaluated; "
                        f"{dt:.1f} s, float64 numpy")}
 
 
-def baselines(api, wl, weights, dev, stream, exits, W, K2, ms_main):
+def baselines(api, wl, weights, dev, stream, exits, W, K2, ms_main, criterion=0, thresholds=None):
     """The method against the decoders it replaces, on the same prompts and
     weights, each timed over K2 graph-replayed steps after W warm-up steps:
     (i) the plain decoder at full depth without exit heads (EE_EXIT_NONE);
@@ -123,7 +125,8 @@ def baselines(api, wl, weights, dev, stream, exits, W, K2, ms_main):
     prompts = synth.make_prompts(wl)
     res = {}
     for name, mode in (("full_depth_no_heads", Bd.EE_EXIT_NONE), ("bf16_exit_copies_same_exits", Bd.EE_EXIT_BF16)):
-        m = api.Model(sh, dev, gamma=wl.gamma, exit_mode=mode, max_batch=B, max_positions=S)
+        m = api.Model(sh, dev, gamma=wl.gamma if thresholds is None else thresholds, exit_mode=mode,
+                      max_batch=B, max_positions=S, criterion=criterion)
         c = api.KVCache(m, B, S)
         try:
             api.prefill(m, c, prompts, stream=stream)
@@ -153,6 +156,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true",
                     help="do not time the exit-head launches (no roofline figure)")
+    ap.add_argument("--criterion", choices=("head", "sts"), default="head",
+                    help="exit criterion: the exit head (default) or River-LLM's state transition "
+                         "similarity with the workload's calibrated thresholds (secondary line)")
     ap.add_argument("--no-baselines", action="store_true",
                     help="skip the full-depth and bf16-exit-copy comparison runs")
     ap.add_argument("--copy-probe", action="store_true",
@@ -175,14 +181,26 @@ def main():
     K = args.steps if args.steps is not None else wl.decode_steps - args.warmup
     W = args.warmup
     S = P + W + K + 1
+    from kv_shared_exit_amd import _binding as Bd
+    sts = args.criterion == "sts"
+    crit = Bd.EE_CRIT_STS if sts else Bd.EE_CRIT_HEAD
+    thresholds = wl.gamma
+    if sts:
+        thresholds = synth.load_tau(wl)
+        if thresholds is None:
+            print(f"no similarity thresholds for {wl.name} (synth/calibration/{wl.name}_sts.json)", file=sys.stderr)
+            sys.exit(2)
     alpha = synth.load_alpha(wl)
-    if alpha is None and wl.policy == "calibrated":
+    if alpha is None and wl.policy == "calibrated" and not sts:
         log("no calibration file: exit heads unscaled (alpha = 1)")
     t0 = time.time()
     weights = synth.make_weights(sh, wl.seed_weights, alpha=alpha)
+    if sts:  # the similarity criterion reads no head weights
+        for lw in weights["layers"]:
+            lw.pop("head_T", None)
     log(f"weights drawn ({time.time() - t0:.0f}s)")
     dev = api.upload_weights(weights)
-    model = api.Model(sh, dev, gamma=wl.gamma, max_batch=B, max_positions=S)
+    model = api.Model(sh, dev, gamma=thresholds, max_batch=B, max_positions=S, criterion=crit)
     cache = api.KVCache(model, B, S)
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
@@ -218,7 +236,7 @@ def main():
     # each exit-head launch timed by events it records itself (profiled steps
     # launch their kernels one by one); the decisions must repeat exactly
     n_launch, head_ms = 0, 0.0
-    if not args.no_profile:
+    if not args.no_profile and not sts:
         cache.rollback(-1, K)
         model.profile(True)
         tin = tok_in0
@@ -237,7 +255,7 @@ def main():
     head_launches = 0
     for s in range(K):
         ctx = ctx0 + s + 1
-        b, h = step_bytes(sh, exits[s], ctx, B)
+        b, h = step_bytes(sh, exits[s], ctx, B, head_bytes=not sts)
         total_bytes += b
         head_launches += h
     # dominant kernel: the exit head's vocabulary GEMV.  It is launched after
@@ -307,13 +325,23 @@ def main():
         out["copy_probe"] = copy_probe
     cache.close()
     model.close()
+    if sts:  # no exit-head GEMV runs: the whole step is the measured unit
+        step_gbs = total_bytes / t_el / 1e9
+        out["metric"] = ("decode tokens/s at 1 MI355X (8B shape, b=8), state-transition-similarity exits "
+                         "+ achieved HBM GB/s fraction")
+        out["config"]["workload"] += ", exit criterion: state transition similarity (calibrated tau)"
+        out["roofline"] = {"bound": "hbm", "kernel": "whole decode step (no exit-head GEMV under this criterion)",
+                           "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(step_gbs / HBM_PEAK_GBS, 4), "traffic": None}
     if not args.no_baselines:
-        out["speedup"] = baselines(api, wl, weights, dev, stream, exits, W, min(K, 40), 1e3 * t_el / K)
+        out["speedup"] = baselines(api, wl, weights, dev, stream, exits, W, min(K, 40), 1e3 * t_el / K,
+                                   criterion=crit, thresholds=thresholds)
         log(f"baselines done ({time.time() - t0:.0f}s)")
     del dev
     if not args.no_cpu_baseline:
         ex = int(round(mean_exit))
-        out["cpu_baseline"] = cpu_baseline(wl, weights, min(max(ex, 1), sh.n_layers), P)
+        out["cpu_baseline"] = cpu_baseline(wl, weights, min(max(ex, 1), sh.n_layers), P,
+                                           criterion=args.criterion)
         log(f"cpu baseline done ({time.time() - t0:.0f}s)")
     print(json.dumps(out), flush=True)
 

@@ -40,7 +40,7 @@ import time
 import numpy as np
 
 import synth
-from .model import OracleModel, KVCache, prefill, decode_step
+from .model import OracleModel, KVCache, prefill, decode_step, state_transition_similarity
 from .numerics import bf16_round, from_bf16_bits
 
 
@@ -59,6 +59,65 @@ def alpha_threshold(logits: np.ndarray, gamma: float, iters: int = 60) -> np.nda
     return np.exp(0.5 * (lo + hi))
 
 
+def _full_depth_states(wl, steps, calib_batch, prompt_len, say, matmul_dtype):
+    """Hidden states [Bc, steps, L+1, d] of full-depth greedy decode steps after a
+    prefill of seeded calibration prompts, and the weights with only the heads kept."""
+    sh = wl.shape
+    L = sh.n_layers
+    w = synth.make_weights(sh, wl.seed_weights)
+    m = OracleModel(sh, w, exit_mode="bf16", cache_f64=True, matmul_dtype=matmul_dtype)
+    for l in range(1, L + 1):                     # widen once, then drop the bf16 copies
+        for name in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "attn_norm", "ffn_norm"):
+            m.w(l, name)
+        keep = {"head_T": w["layers"][l - 1].get("head_T")}
+        w["layers"][l - 1] = keep
+    say("weights ready")
+    cache = KVCache(sh, calib_batch, prompt_len + steps + 1)
+    prompts = synth.make_prompts(wl, batch=calib_batch, length=prompt_len, seed=wl.seed_calib)
+    tok, _ = prefill(m, cache, prompts)
+    say(f"prefill {calib_batch}x{prompt_len}")
+    states = []
+    for s in range(steps):
+        tok, _, info = decode_step(m, cache, tok, gamma=2.0, trace=True, heads=False)
+        states.append(info["hidden"])              # [Bc, L+1, d]
+        if s % 32 == 0:
+            say(f"decode step {s}")
+    del m._f64
+    return np.stack(states, axis=1), w
+
+
+def calibrate_sts(wl, steps: int, calib_batch: int = 4, prompt_len: int | None = None, verbose: bool = True,
+                  matmul_dtype=np.float32):
+    """Per-layer thresholds tau_l of the state-transition-similarity criterion
+    (River-LLM explainer, section 5.2) for workload ``wl``: the row exits after
+    layer l iff its similarity > tau_l, so tau_l is the (1 - h) quantile of the
+    similarities after layer l of full-depth decode states, and a fraction h
+    of them exits (the truncated-geometric hazard of the workload's mean exit
+    layer, as for the exit heads).  Parity unpinned: this only chooses inputs."""
+    sh = wl.shape
+    L = sh.n_layers
+    h = synth.geometric_hazard(wl.mean_exit, L)
+    P0 = wl.prompt_len if prompt_len is None else prompt_len
+    t0 = time.time()
+
+    def say(msg):
+        if verbose:
+            print(f"[calibrate-sts {wl.name}] {msg} ({time.time() - t0:.0f}s)", flush=True)
+
+    hid, _ = _full_depth_states(wl, steps, calib_batch, P0, say, matmul_dtype)
+    taus = []
+    for l in range(1, L):
+        sts = state_transition_similarity(hid[:, :, l - 1].reshape(-1, sh.d_model),
+                                          hid[:, :, l].reshape(-1, sh.d_model))
+        t = float(np.quantile(sts, 1.0 - h))
+        taus.append(t)
+        say(f"layer {l}: tau={t:.6f} (similarity {sts.min():.4f}..{sts.max():.4f})")
+    return {"workload": wl.name, "criterion": "sts", "mean_exit": wl.mean_exit, "hazard": h,
+            "samples_per_layer": int(hid.shape[0] * hid.shape[1]),
+            "source": f"full-depth greedy decode, {calib_batch} prompts of {P0} tokens, {steps} steps",
+            "tau": taus}
+
+
 def calibrate(wl, steps: int | None = None, calib_batch: int = 4, verbose: bool = True,
               matmul_dtype=np.float32):
     """Per-layer alpha for workload ``wl`` from full-depth greedy decode states."""
@@ -72,27 +131,8 @@ def calibrate(wl, steps: int | None = None, calib_batch: int = 4, verbose: bool 
         if verbose:
             print(f"[calibrate {wl.name}] {msg} ({time.time() - t0:.0f}s)", flush=True)
 
-    w = synth.make_weights(sh, wl.seed_weights)
-    m = OracleModel(sh, w, exit_mode="bf16", cache_f64=True, matmul_dtype=matmul_dtype)
-    for l in range(1, L + 1):                     # widen once, then drop the bf16 copies
-        for name in ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down", "attn_norm", "ffn_norm"):
-            m.w(l, name)
-        keep = {"head_T": w["layers"][l - 1].get("head_T")}
-        w["layers"][l - 1] = keep
-    say("weights ready")
     P0 = wl.prompt_len
-    cache = KVCache(sh, calib_batch, P0 + steps + 1)
-    prompts = synth.make_prompts(wl, batch=calib_batch, length=P0, seed=wl.seed_calib)
-    tok, _ = prefill(m, cache, prompts)
-    say(f"prefill {calib_batch}x{P0}")
-    states = []
-    for s in range(steps):
-        tok, _, info = decode_step(m, cache, tok, gamma=2.0, trace=True, heads=False)
-        states.append(info["hidden"])              # [Bc, L+1, d]
-        if s % 32 == 0:
-            say(f"decode step {s}")
-    hid = np.stack(states, axis=1)                 # [Bc, steps, L+1, d]
-    del m._f64
+    hid, w = _full_depth_states(wl, steps, calib_batch, P0, say, matmul_dtype)
     E = from_bf16_bits(w["lm_head"]).astype(matmul_dtype)
     alphas = []
     for l in range(1, L):
@@ -115,11 +155,19 @@ def main():
     ap.add_argument("workload")
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--batch", type=int, default=4)
+    ap.add_argument("--criterion", choices=("head", "sts"), default="head")
+    ap.add_argument("--prompt-len", type=int, default=None, help="sts only: calibration prompt length")
     args = ap.parse_args()
     wl = synth.workload(args.workload)
-    res = calibrate(wl, args.steps, args.batch)
+    if args.criterion == "sts":
+        steps = wl.decode_steps if args.steps is None else min(args.steps, wl.decode_steps)
+        res = calibrate_sts(wl, steps, args.batch, args.prompt_len)
+        name = f"{wl.name}_sts"
+    else:
+        res = calibrate(wl, args.steps, args.batch)
+        name = wl.name
     os.makedirs(synth.CALIB_DIR, exist_ok=True)
-    path = os.path.join(synth.CALIB_DIR, f"{wl.name}.json")
+    path = os.path.join(synth.CALIB_DIR, f"{name}.json")
     with open(path, "w") as f:
         json.dump(res, f, indent=1)
     print(path)

@@ -33,7 +33,7 @@ import numpy as np
 __all__ = [
     "ModelShape", "Workload", "WORKLOADS", "workload", "make_weights",
     "make_prompts", "make_forced_exits", "geometric_hazard", "exit_pmf",
-    "load_alpha", "layer_names", "bf16_bits_to_f32",
+    "load_alpha", "load_tau", "layer_names", "bf16_bits_to_f32",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -206,6 +206,19 @@ def load_alpha(wl: Workload) -> np.ndarray | None:
     alpha = np.asarray(data["alpha"], dtype=np.float64)
     assert alpha.shape == (wl.shape.n_layers - 1,)
     return alpha
+
+
+def load_tau(wl: Workload) -> np.ndarray | None:
+    """Per-layer similarity thresholds tau_l (l = 1..L-1) of a workload's state
+    transition similarity criterion, or None."""
+    path = os.path.join(CALIB_DIR, f"{wl.name}_sts.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    tau = np.asarray(data["tau"], dtype=np.float64)
+    assert tau.shape == (wl.shape.n_layers - 1,)
+    return tau
 
 
 def make_weights(shape: ModelShape, seed: int, alpha=None, threads: int | None = None,
