@@ -32,6 +32,10 @@ exits iff that similarity > tau_l (the per-layer thresholds take gamma's
 place).  The pages apply the threshold to the batch minimum; here, as for the
 exit head, each sequence decides for itself.
 
+With check_every = N > 1 the criterion is evaluated only after layers N, 2N,
+... (CALM explainer's check every N layers; AdaDecode's layer subsets); after
+the other layers no sequence exits unless its exit is forced there.
+
 The token of a step is the greedy argmax of the final LM head after the exit
 river has finished the remaining layers; the exit head only decides which
 copy runs the remaining layers (the reading under which "unquantised exit
@@ -291,7 +295,7 @@ def final_head(model: OracleModel, h: np.ndarray):
 # decode step, prefill, generation
 # ----------------------------------------------------------------------------
 def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=None,
-                trace: bool = False, heads: bool = True, criterion: str = "head"):
+                trace: bool = False, heads: bool = True, criterion: str = "head", check_every: int = 1):
     """One decode step for sequences 0..B-1 of ``cache`` (B = len(tokens)).
 
     ``gamma``: per-layer thresholds gamma_1..gamma_{L-1} (scalar broadcasts);
@@ -305,9 +309,13 @@ def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=N
     ``gap`` [B], ``logits`` [B, V] and, with ``trace``, ``hidden`` [B, L+1, d]
     (after the embedding and after every layer).  ``heads=False`` evaluates no
     criterion (no sequence exits); it is used to sample full-depth states.
+    ``check_every``: the criterion runs after layers that are multiples of it;
+    forced exits apply after any layer.
     """
     if criterion not in ("head", "sts"):
         raise ValueError(f"unknown criterion {criterion!r}")
+    if check_every < 1:
+        raise ValueError("check_every must be >= 1")
     sh = model.shape
     L = sh.n_layers
     tokens = np.asarray(tokens, dtype=np.int64)
@@ -327,7 +335,7 @@ def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=N
     for l in range(1, L + 1):
         bb = np.nonzero(~exited)[0]
         ex = np.nonzero(exited)[0]
-        decide = heads and l < L and len(bb) > 0
+        decide = heads and l < L and len(bb) > 0 and l % check_every == 0
         h_in = h[bb].copy() if decide and criterion == "sts" else None
         if len(bb):
             _layer_rows(model, cache, l, bb, h, pos, use_exit=False)
@@ -343,6 +351,11 @@ def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=N
             for i, b in enumerate(bb):
                 go = (l == forced[b]) if forced[b] > 0 else (p[i] > gamma[l - 1])
                 if go:
+                    exited[b] = True
+                    e[b] = l
+        elif heads and l < L:   # not a check layer: only forced exits
+            for b in bb:
+                if forced[b] == l:
                     exited[b] = True
                     e[b] = l
         if trace:
@@ -413,7 +426,7 @@ def prefill(model: OracleModel, cache: KVCache, prompts, trace: bool = False):
 
 
 def generate(model: OracleModel, cache: KVCache, prompts, steps: int, gamma=None,
-             forced_fn=None, criterion: str = "head"):
+             forced_fn=None, criterion: str = "head", check_every: int = 1):
     """Prefill, then ``steps`` decode steps feeding back each greedy token.
 
     ``forced_fn(step)`` may return a forced-exit array for a step.  Returns
@@ -423,7 +436,8 @@ def generate(model: OracleModel, cache: KVCache, prompts, steps: int, gamma=None
     toks, exits = [tok], []
     for s in range(steps):
         f = forced_fn(s) if forced_fn is not None else None
-        tok, e, _ = decode_step(model, cache, tok, gamma=gamma, forced=f, criterion=criterion)
+        tok, e, _ = decode_step(model, cache, tok, gamma=gamma, forced=f, criterion=criterion,
+                                check_every=check_every)
         toks.append(tok)
         exits.append(e)
     return np.stack(toks, axis=1), (np.stack(exits, axis=1) if exits else
