@@ -108,6 +108,9 @@ typedef struct ee_model_config {
   int32_t max_batch;
   int32_t max_positions;
   int32_t criterion; /* EE_CRIT_HEAD or EE_CRIT_STS */
+  int32_t check_every; /* evaluate the criterion only after layers that are multiples of it
+                          (CALM explainer: check every N layers); 0 or 1: every layer.
+                          A forced exit applies after any layer. */
 } ee_model_config;
 
 /* Device pointers of one layer.  Shapes: attn_norm, ffn_norm [d]; wq [H*hd, d];

@@ -49,7 +49,7 @@ class ModelConfig(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("d_ff", C.c_int32),
                 ("vocab", C.c_int32), ("group_size", C.c_int32), ("rms_eps", C.c_float),
                 ("rope_theta", C.c_float), ("exit_mode", C.c_int32), ("max_batch", C.c_int32),
-                ("max_positions", C.c_int32), ("criterion", C.c_int32)]
+                ("max_positions", C.c_int32), ("criterion", C.c_int32), ("check_every", C.c_int32)]
 
 
 class LayerWeights(C.Structure):

@@ -188,6 +188,7 @@ void validate_config(const ee_model_config& c) {
   need(c.exit_mode == EE_EXIT_INT4 || c.exit_mode == EE_EXIT_BF16 || c.exit_mode == EE_EXIT_NONE,
        "bad exit_mode");
   need(c.criterion == EE_CRIT_HEAD || c.criterion == EE_CRIT_STS, "bad criterion");
+  need(c.check_every >= 0, "check_every must be >= 0");
   need(std::isfinite(c.rms_eps) && c.rms_eps > 0 && std::isfinite(c.rope_theta) && c.rope_theta > 0,
        "rms_eps and rope_theta must be positive");
   shape(c.group_size == 32 || c.group_size == 64 || c.group_size == 128, "group_size must be 32, 64 or 128");
@@ -272,6 +273,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
   const bool int4 = cf.exit_mode == EE_EXIT_INT4;
   heads = heads && cf.exit_mode != EE_EXIT_NONE;  // the plain decoder evaluates no criterion
   const bool sts_crit = cf.criterion == EE_CRIT_STS;
+  const int every = std::max(1, cf.check_every);
 
   const size_t pstride = (size_t)kMaxBatch * d;  // elements between partial-sum ranges
   launch_init(st, prompt, P, t, B, L, m->tok_emb, d, cf.vocab, m->h, m->p_rec,
@@ -364,7 +366,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       const int nkc = launch_proj(EPI_PART, a, kNwg, B, s);
       // with the similarity criterion the layer's input stays in h (the
       // residual after attention goes to h2) until the layer's end
-      float* h_mid = heads && sts_crit && l < L ? m->h2 : m->h;
+      float* h_mid = heads && sts_crit && l < L && l % every == 0 ? m->h2 : m->h;
       launch_finish(h_mid, m->h, m->parts, nkc, pstride, B, d, (const uint16_t*)w.ffn_norm, cf.rms_eps, m->xn,
                     nullptr, nullptr, nullptr, s);
     }
@@ -390,7 +392,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       a.y_stride = F;
       launch_proj(EPI_SWIGLU, a, kNwg, B, s);
     }
-    const bool head_here = heads && l < L;          // the criterion is evaluated after this layer
+    const bool head_here = heads && l < L && l % every == 0;  // the criterion is evaluated after this layer
     const bool sts_here = head_here && sts_crit;
     {
       ProjArgs a = base_args(m);
@@ -421,7 +423,9 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
         launch_finish(m->h, m->h, m->parts, nkc, pstride, B, d, (const uint16_t*)g_next, cf.rms_eps, m->xn,
                       head_here ? m->hb : nullptr, nullptr, nullptr, s);
     }
-    if (sts_here) launch_decide(st, nullptr, 0, m->d_gamma, l, L, B, m->p_rec, m->sts, s);
+    if (sts_here) launch_decide(DECIDE_STS, st, nullptr, 0, m->d_gamma, l, L, B, m->p_rec, m->sts, s);
+    if (heads && l < L && !head_here)  // between checks only forced exits apply
+      launch_decide(DECIDE_FORCED, st, nullptr, 0, m->d_gamma, l, L, B, m->p_rec, nullptr, s);
     if (head_here && !sts_crit) {
       {
         ProjArgs a = base_args(m);
@@ -450,7 +454,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
         prof_events(m, &e0, &e1);
         launch_proj(EPI_LSE, a, kNwg, B, s, e0, e1);
       }
-      launch_decide(st, m->head_part, kNwg, m->d_gamma, l, L, B, m->p_rec, nullptr, s);
+      launch_decide(DECIDE_HEAD, st, m->head_part, kNwg, m->d_gamma, l, L, B, m->p_rec, nullptr, s);
     }
     if (dbg.hidden)
       HIPCHK(hipMemcpy2DAsync(m->dbg_hidden + (size_t)l * d, (size_t)(L + 1) * d * 4, m->h,

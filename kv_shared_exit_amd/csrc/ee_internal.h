@@ -103,9 +103,11 @@ void launch_init(StepState* st, const int32_t* prompt, int P, int t, int B, int 
                  float eps, uint16_t* x, hipStream_t s);
 void launch_attention(const AttnArgs& a, hipStream_t s);
 // Exit decision after layer `layer` for the rows on the backbone: from the exit
-// head's nwg (max, sum exp) partials, or, when sts is set, from the state
-// transition similarity per sequence (nwg and part unused).
-void launch_decide(StepState* st, const float* part, int nwg, const float* gamma, int layer,
+// head's nwg (max, sum exp) partials (DECIDE_HEAD), from the state transition
+// similarity per sequence in sts (DECIDE_STS), or forced exits only, no
+// criterion (DECIDE_FORCED, between check layers).
+enum DecideMode { DECIDE_HEAD = 0, DECIDE_STS = 1, DECIDE_FORCED = 2 };
+void launch_decide(int mode, StepState* st, const float* part, int nwg, const float* gamma, int layer,
                    int L, int B, float* p_rec, const float* sts, hipStream_t s);
 void launch_final(StepState* st, const float* part, int nwg, int B, int V, int32_t* lens, int advance,
                   hipStream_t s);

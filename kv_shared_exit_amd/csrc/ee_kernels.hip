@@ -350,19 +350,21 @@ __device__ __forceinline__ void load_lse_parts(const float* part, int nwg, int i
   }
 }
 
-// STS: the value of a row is its state transition similarity sts[b] (read by
-// lane 0 of the row's wave) instead of the exit head's p.
-template <bool STS>
+// MODE DECIDE_STS: the value of a row is its state transition similarity
+// sts[b] instead of the exit head's p; DECIDE_FORCED: no value, only forced
+// exits (p_rec is left as it is).
+template <int MODE>
 __global__ __launch_bounds__(kHeadThreads) void decide_kernel(StepState* st, const float* part, int nwg,
                                                               const float* gamma, int layer, int L, int B,
                                                               float* p_rec, const float* sts) {
+  constexpr bool STS = MODE == DECIDE_STS;
   __shared__ int sx[kMaxBatch];
   __shared__ int sn;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   // the first row of each wave is requested before the row count is known
   // (list positions below kMaxBatch are always in bounds)
   float2 v[kPartPerLane];
-  if constexpr (!STS) load_lse_parts(part, nwg, w, lane, v);
+  if constexpr (MODE == DECIDE_HEAD) load_lse_parts(part, nwg, w, lane, v);
   if ((int)threadIdx.x < B) sx[threadIdx.x] = st->exited[threadIdx.x];
   if (threadIdx.x == 0) sn = min(max(st->n_act, 0), B);
   __syncthreads();
@@ -370,7 +372,9 @@ __global__ __launch_bounds__(kHeadThreads) void decide_kernel(StepState* st, con
   for (int i = w; i < n; i += kHeadWaves) {
     const int b = st->act[i];
     float p = 0.0f;
-    if constexpr (STS) {
+    if constexpr (MODE == DECIDE_FORCED) {
+      p = 0.0f;
+    } else if constexpr (STS) {
       p = sts[b];
     } else {
       if (i != w) load_lse_parts(part, nwg, i, lane, v);
@@ -386,8 +390,8 @@ __global__ __launch_bounds__(kHeadThreads) void decide_kernel(StepState* st, con
     }
     if (lane == 0) {
       const int f = st->forced[b];
-      const bool ex = f > 0 ? (layer == f) : (p > gamma[layer - 1]);
-      if (p_rec) p_rec[(layer - 1) * kMaxBatch + b] = p;
+      const bool ex = f > 0 ? (layer == f) : (MODE != DECIDE_FORCED && p > gamma[layer - 1]);
+      if (p_rec && MODE != DECIDE_FORCED) p_rec[(layer - 1) * kMaxBatch + b] = p;
       if (ex) {
         sx[b] = 1;
         st->e[b] = layer;
@@ -415,16 +419,23 @@ __global__ __launch_bounds__(kHeadThreads) void decide_kernel(StepState* st, con
   }
 }
 
-void launch_decide(StepState* st, const float* part, int nwg, const float* gamma, int layer, int L,
+void launch_decide(int mode, StepState* st, const float* part, int nwg, const float* gamma, int layer, int L,
                    int B, float* p_rec, const float* sts, hipStream_t s) {
-  if (sts) {
-    hipLaunchKernelGGL(decide_kernel<true>, dim3(1), dim3(kHeadThreads), 0, s, st, part, nwg, gamma, layer, L, B,
-                       p_rec, sts);
-    return;
+  switch (mode) {
+    case DECIDE_STS:
+      if (!sts) throw std::logic_error("decide: no similarities");
+      hipLaunchKernelGGL(decide_kernel<DECIDE_STS>, dim3(1), dim3(kHeadThreads), 0, s, st, part, nwg, gamma, layer,
+                         L, B, p_rec, sts);
+      return;
+    case DECIDE_FORCED:
+      hipLaunchKernelGGL(decide_kernel<DECIDE_FORCED>, dim3(1), dim3(kHeadThreads), 0, s, st, part, nwg, gamma,
+                         layer, L, B, p_rec, sts);
+      return;
+    default:
+      if (nwg < 1 || nwg > kNwgMax) throw std::logic_error("decide: partial count out of range");
+      hipLaunchKernelGGL(decide_kernel<DECIDE_HEAD>, dim3(1), dim3(kHeadThreads), 0, s, st, part, nwg, gamma,
+                         layer, L, B, p_rec, sts);
   }
-  if (nwg < 1 || nwg > kNwgMax) throw std::logic_error("decide: partial count out of range");
-  hipLaunchKernelGGL(decide_kernel<false>, dim3(1), dim3(kHeadThreads), 0, s, st, part, nwg, gamma, layer, L, B,
-                     p_rec, sts);
 }
 
 __global__ __launch_bounds__(kHeadThreads) void final_kernel(StepState* st, const float* part, int nwg, int B,

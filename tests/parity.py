@@ -83,7 +83,8 @@ def _normrel(a, r):
 
 
 def run_parity(shape, weights, batch, P, steps, gamma, exit_mode="int4", forced_fn=None,
-               prompts=None, max_seq=None, check_kv=True, check_hidden=True, label="", criterion="head"):
+               prompts=None, max_seq=None, check_kv=True, check_hidden=True, label="", criterion="head",
+               check_every=1):
     import torch
     from kv_shared_exit_amd import api, _binding as B
 
@@ -95,7 +96,7 @@ def run_parity(shape, weights, batch, P, steps, gamma, exit_mode="int4", forced_
     t0 = time.time()
     dev = api.upload_weights(weights)
     model = api.Model(shape, dev, gamma=gamma, exit_mode=mode, max_batch=batch, max_positions=S,
-                      criterion=B.EE_CRIT_STS if sts else B.EE_CRIT_HEAD)
+                      criterion=B.EE_CRIT_STS if sts else B.EE_CRIT_HEAD, check_every=check_every)
     cache = api.KVCache(model, batch, S, track=True)
     orc = om.OracleModel(shape, weights, exit_mode=exit_mode)
     ocache = om.KVCache(shape, batch, S)
@@ -124,7 +125,7 @@ def run_parity(shape, weights, batch, P, steps, gamma, exit_mode="int4", forced_
         for s in range(steps):
             forced = np.zeros(batch, np.int32) if forced_fn is None else np.asarray(forced_fn(s), np.int32)
             to, eo, io = om.decode_step(orc, ocache, tok_in, gamma=gam, forced=forced, trace=check_hidden,
-                                        criterion=criterion)
+                                        criterion=criterion, check_every=check_every)
             fg = forced.copy()
             for b in range(batch):
                 if forced[b] == 0:

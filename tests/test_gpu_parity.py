@@ -182,3 +182,60 @@ def test_similarity_extremes_equal_the_head_extremes_bitwise(gpu):
         for (k1, v1), (k2, v2) in zip(ka, kb):
             np.testing.assert_array_equal(k1, k2)
             np.testing.assert_array_equal(v1, v2)
+
+
+# ---------------------------------------------------------------------------
+# The criterion evaluated only every N layers
+# ---------------------------------------------------------------------------
+FIVE = ModelShape(5, 256, 8, 2, 32, 512, 1500, 32, rope_theta=500000.0)
+
+
+def test_check_every_two_layers_against_oracle(gpu):
+    from parity import run_parity
+    sh = FIVE
+    w = synth.make_weights(sh, 41)
+    tau = _median_similarity(sh, w, 3, 8, 5, seed=98)
+    res = run_parity(sh, w, 3, 8, 5, tau, criterion="sts", check_every=2, label="five-sts-every2")
+    exits = np.concatenate(res.exits)
+    assert set(exits.tolist()) <= {2, 4, 5}
+    assert (exits < sh.n_layers).any()
+
+
+def test_check_every_equals_raised_thresholds_bitwise(gpu):
+    """Checking every N layers decides like checking every layer with the
+    thresholds of the layers in between raised to 2 (unreachable): tokens,
+    exit layers and K/V bitwise equal, head criterion with forced exits mixed in."""
+    from kv_shared_exit_amd import api, _binding as B
+    sh = FIVE
+    wl = Workload("five", sh, 1, 8, 6, 0.75, "calibrated", 2.5, index=7)
+    cal = calibrate(wl, verbose=False)
+    w = synth.make_weights(sh, 7, alpha=np.array(cal["alpha"]))
+    dev = api.upload_weights(w)
+    P, steps, batch, n = 8, 5, 4, 2
+    prompts = np.random.default_rng(6).integers(0, sh.vocab, (batch, P)).astype(np.int32)
+    g = np.full(sh.n_layers - 1, 0.75)
+    g_raised = g.copy()
+    g_raised[[l - 1 for l in range(1, sh.n_layers) if l % n]] = 2.0
+    forced = np.array([0, 3, 0, 0], np.int32)
+
+    def run(gamma, every):
+        m = api.Model(sh, dev, gamma=gamma, check_every=every, max_batch=batch, max_positions=P + steps + 1)
+        c = api.KVCache(m, batch, P + steps + 1)
+        try:
+            api.prefill(m, c, prompts)
+            out = [api.decode_step(m, c, batch, forced=forced) for _ in range(steps)]
+            kv = [c.read(l, b, 0, P + steps) for l in range(1, sh.n_layers + 1) for b in range(batch)]
+        finally:
+            c.close()
+            m.close()
+        return out, kv
+
+    a, ka = run(g, n)
+    b, kb = run(g_raised, 1)
+    for (ta, ea), (tb, eb) in zip(a, b):
+        np.testing.assert_array_equal(ea, eb)
+        np.testing.assert_array_equal(ta, tb)
+        assert ea[1] == 3   # forced between checks
+    for (k1, v1), (k2, v2) in zip(ka, kb):
+        np.testing.assert_array_equal(k1, k2)
+        np.testing.assert_array_equal(v1, v2)
