@@ -239,3 +239,31 @@ def test_check_every_equals_raised_thresholds_bitwise(gpu):
     for (k1, v1), (k2, v2) in zip(ka, kb):
         np.testing.assert_array_equal(k1, k2)
         np.testing.assert_array_equal(v1, v2)
+
+
+# ---------------------------------------------------------------------------
+# Degenerate and maximal shapes
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,sh,batch,gamma", [
+    # one layer: no exit head anywhere, every exit layer is 1 = L
+    ("one-layer", ModelShape(1, 64, 2, 1, 32, 96, 50, 32), 2, 0.75),
+    # a vocabulary of one token: p = 1 > gamma after layer 1, token always 0, gap +inf
+    ("one-token-vocab", ModelShape(2, 64, 2, 2, 32, 96, 1, 32), 3, 0.75),
+])
+def test_degenerate_shapes(gpu, name, sh, batch, gamma):
+    from parity import run_parity
+    w = synth.make_weights(sh, 3)
+    res = run_parity(sh, w, batch, 4, 3, gamma, label=name)
+    exits = np.concatenate(res.exits)
+    assert np.all(exits == 1)
+    assert res.compared_tokens == batch * 4
+
+
+def test_largest_batch(gpu):
+    """64 sequences (the largest batch): every kernel runs its rows in chunks of 8."""
+    from parity import run_parity
+    sh, w = _weights("tiny", 2.0, 6, 3)
+    res = run_parity(sh, w, 64, 6, 3, 0.75, label="tiny-b64")
+    exits = np.concatenate(res.exits)
+    assert len(set(exits.tolist())) >= 2
+    assert res.compared_tokens >= 64 * 3
