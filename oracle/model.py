@@ -32,6 +32,11 @@ exits iff that similarity > tau_l (the per-layer thresholds take gamma's
 place).  The pages apply the threshold to the batch minimum; here, as for the
 exit head, each sequence decides for itself.
 
+With exit_rule "batch_min" (River-LLM explainer, section 5.2: the exit fires
+when the minimum over the batch's tokens exceeds the threshold) the sequences
+on the backbone whose exit is not forced leave together after the first
+evaluated layer at which the smallest of their values > the threshold.
+
 With check_every = N > 1 the criterion is evaluated only after layers N, 2N,
 ... (CALM explainer's check every N layers; AdaDecode's layer subsets); after
 the other layers no sequence exits unless its exit is forced there.
@@ -295,7 +300,8 @@ def final_head(model: OracleModel, h: np.ndarray):
 # decode step, prefill, generation
 # ----------------------------------------------------------------------------
 def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=None,
-                trace: bool = False, heads: bool = True, criterion: str = "head", check_every: int = 1):
+                trace: bool = False, heads: bool = True, criterion: str = "head", check_every: int = 1,
+                exit_rule: str = "sequence"):
     """One decode step for sequences 0..B-1 of ``cache`` (B = len(tokens)).
 
     ``gamma``: per-layer thresholds gamma_1..gamma_{L-1} (scalar broadcasts);
@@ -310,10 +316,14 @@ def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=N
     (after the embedding and after every layer).  ``heads=False`` evaluates no
     criterion (no sequence exits); it is used to sample full-depth states.
     ``check_every``: the criterion runs after layers that are multiples of it;
-    forced exits apply after any layer.
+    forced exits apply after any layer.  ``exit_rule``: "sequence" (each
+    sequence decides for itself) or "batch_min" (the unforced sequences on the
+    backbone exit together when the smallest of their values > the threshold).
     """
     if criterion not in ("head", "sts"):
         raise ValueError(f"unknown criterion {criterion!r}")
+    if exit_rule not in ("sequence", "batch_min"):
+        raise ValueError(f"unknown exit rule {exit_rule!r}")
     if check_every < 1:
         raise ValueError("check_every must be >= 1")
     sh = model.shape
@@ -348,8 +358,15 @@ def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=N
             else:
                 p = state_transition_similarity(h_in, h[bb])
             p_rec[bb, l - 1] = p
+            free = [i for i, b in enumerate(bb) if forced[b] == 0]
+            batch_go = bool(free) and min(p[i] for i in free) > gamma[l - 1]
             for i, b in enumerate(bb):
-                go = (l == forced[b]) if forced[b] > 0 else (p[i] > gamma[l - 1])
+                if forced[b] > 0:
+                    go = l == forced[b]
+                elif exit_rule == "batch_min":
+                    go = batch_go
+                else:
+                    go = p[i] > gamma[l - 1]
                 if go:
                     exited[b] = True
                     e[b] = l
@@ -426,7 +443,7 @@ def prefill(model: OracleModel, cache: KVCache, prompts, trace: bool = False):
 
 
 def generate(model: OracleModel, cache: KVCache, prompts, steps: int, gamma=None,
-             forced_fn=None, criterion: str = "head", check_every: int = 1):
+             forced_fn=None, criterion: str = "head", check_every: int = 1, exit_rule: str = "sequence"):
     """Prefill, then ``steps`` decode steps feeding back each greedy token.
 
     ``forced_fn(step)`` may return a forced-exit array for a step.  Returns
@@ -437,7 +454,7 @@ def generate(model: OracleModel, cache: KVCache, prompts, steps: int, gamma=None
     for s in range(steps):
         f = forced_fn(s) if forced_fn is not None else None
         tok, e, _ = decode_step(model, cache, tok, gamma=gamma, forced=f, criterion=criterion,
-                                check_every=check_every)
+                                check_every=check_every, exit_rule=exit_rule)
         toks.append(tok)
         exits.append(e)
     return np.stack(toks, axis=1), (np.stack(exits, axis=1) if exits else
