@@ -82,6 +82,14 @@ typedef int32_t ee_status;
 #define EE_CRIT_HEAD 0
 #define EE_CRIT_STS 1
 
+/* Who decides an exit after an evaluated layer:
+ *   EE_RULE_SEQUENCE   each sequence on the backbone, from its own value;
+ *   EE_RULE_BATCH_MIN  the sequences on the backbone whose exit is not forced
+ *                      leave together when the smallest of their values exceeds
+ *                      the layer's threshold (River-LLM explainer, section 5.2). */
+#define EE_RULE_SEQUENCE 0
+#define EE_RULE_BATCH_MIN 1
+
 #define EE_KV_TRACK_OCCUPANCY 1u /* count writes per (layer, sequence, position) slot */
 
 typedef struct ee_model ee_model;
@@ -111,6 +119,7 @@ typedef struct ee_model_config {
   int32_t check_every; /* evaluate the criterion only after layers that are multiples of it
                           (CALM explainer: check every N layers); 0 or 1: every layer.
                           A forced exit applies after any layer. */
+  int32_t exit_rule;   /* EE_RULE_SEQUENCE or EE_RULE_BATCH_MIN */
 } ee_model_config;
 
 /* Device pointers of one layer.  Shapes: attn_norm, ffn_norm [d]; wq [H*hd, d];

@@ -28,6 +28,8 @@ EE_EXIT_BF16 = 1
 EE_EXIT_NONE = 2
 EE_CRIT_HEAD = 0
 EE_CRIT_STS = 1
+EE_RULE_SEQUENCE = 0
+EE_RULE_BATCH_MIN = 1
 EE_KV_TRACK_OCCUPANCY = 1
 
 EXPORTS = [
@@ -49,7 +51,8 @@ class ModelConfig(C.Structure):
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("d_ff", C.c_int32),
                 ("vocab", C.c_int32), ("group_size", C.c_int32), ("rms_eps", C.c_float),
                 ("rope_theta", C.c_float), ("exit_mode", C.c_int32), ("max_batch", C.c_int32),
-                ("max_positions", C.c_int32), ("criterion", C.c_int32), ("check_every", C.c_int32)]
+                ("max_positions", C.c_int32), ("criterion", C.c_int32), ("check_every", C.c_int32),
+                ("exit_rule", C.c_int32)]
 
 
 class LayerWeights(C.Structure):

@@ -189,6 +189,7 @@ void validate_config(const ee_model_config& c) {
        "bad exit_mode");
   need(c.criterion == EE_CRIT_HEAD || c.criterion == EE_CRIT_STS, "bad criterion");
   need(c.check_every >= 0, "check_every must be >= 0");
+  need(c.exit_rule == EE_RULE_SEQUENCE || c.exit_rule == EE_RULE_BATCH_MIN, "bad exit_rule");
   need(std::isfinite(c.rms_eps) && c.rms_eps > 0 && std::isfinite(c.rope_theta) && c.rope_theta > 0,
        "rms_eps and rope_theta must be positive");
   shape(c.group_size == 32 || c.group_size == 64 || c.group_size == 128, "group_size must be 32, 64 or 128");
@@ -423,9 +424,10 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
         launch_finish(m->h, m->h, m->parts, nkc, pstride, B, d, (const uint16_t*)g_next, cf.rms_eps, m->xn,
                       head_here ? m->hb : nullptr, nullptr, nullptr, s);
     }
-    if (sts_here) launch_decide(DECIDE_STS, st, nullptr, 0, m->d_gamma, l, L, B, m->p_rec, m->sts, s);
+    const bool bmin = cf.exit_rule == EE_RULE_BATCH_MIN;
+    if (sts_here) launch_decide(DECIDE_STS, bmin, st, nullptr, 0, m->d_gamma, l, L, B, m->p_rec, m->sts, s);
     if (heads && l < L && !head_here)  // between checks only forced exits apply
-      launch_decide(DECIDE_FORCED, st, nullptr, 0, m->d_gamma, l, L, B, m->p_rec, nullptr, s);
+      launch_decide(DECIDE_FORCED, false, st, nullptr, 0, m->d_gamma, l, L, B, m->p_rec, nullptr, s);
     if (head_here && !sts_crit) {
       {
         ProjArgs a = base_args(m);
@@ -454,7 +456,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
         prof_events(m, &e0, &e1);
         launch_proj(EPI_LSE, a, kNwg, B, s, e0, e1);
       }
-      launch_decide(DECIDE_HEAD, st, m->head_part, kNwg, m->d_gamma, l, L, B, m->p_rec, nullptr, s);
+      launch_decide(DECIDE_HEAD, bmin, st, m->head_part, kNwg, m->d_gamma, l, L, B, m->p_rec, nullptr, s);
     }
     if (dbg.hidden)
       HIPCHK(hipMemcpy2DAsync(m->dbg_hidden + (size_t)l * d, (size_t)(L + 1) * d * 4, m->h,

@@ -105,10 +105,11 @@ void launch_attention(const AttnArgs& a, hipStream_t s);
 // Exit decision after layer `layer` for the rows on the backbone: from the exit
 // head's nwg (max, sum exp) partials (DECIDE_HEAD), from the state transition
 // similarity per sequence in sts (DECIDE_STS), or forced exits only, no
-// criterion (DECIDE_FORCED, between check layers).
+// criterion (DECIDE_FORCED, between check layers).  batch_min: the unforced
+// rows leave together when the smallest of their values exceeds the threshold.
 enum DecideMode { DECIDE_HEAD = 0, DECIDE_STS = 1, DECIDE_FORCED = 2 };
-void launch_decide(int mode, StepState* st, const float* part, int nwg, const float* gamma, int layer,
-                   int L, int B, float* p_rec, const float* sts, hipStream_t s);
+void launch_decide(int mode, bool batch_min, StepState* st, const float* part, int nwg, const float* gamma,
+                   int layer, int L, int B, float* p_rec, const float* sts, hipStream_t s);
 void launch_final(StepState* st, const float* part, int nwg, int B, int V, int32_t* lens, int advance,
                   hipStream_t s);
 void launch_advance(int32_t* lens, int B, hipStream_t s);

@@ -353,12 +353,16 @@ __device__ __forceinline__ void load_lse_parts(const float* part, int nwg, int i
 // MODE DECIDE_STS: the value of a row is its state transition similarity
 // sts[b] instead of the exit head's p; DECIDE_FORCED: no value, only forced
 // exits (p_rec is left as it is).
+// batch_min: the unforced rows leave together when the smallest of their
+// values exceeds the threshold (River-LLM explainer, section 5.2), decided
+// by thread 0 over the values in list order.
 template <int MODE>
 __global__ __launch_bounds__(kHeadThreads) void decide_kernel(StepState* st, const float* part, int nwg,
                                                               const float* gamma, int layer, int L, int B,
-                                                              float* p_rec, const float* sts) {
+                                                              float* p_rec, const float* sts, int batch_min) {
   constexpr bool STS = MODE == DECIDE_STS;
   __shared__ int sx[kMaxBatch];
+  __shared__ float pv[kMaxBatch];
   __shared__ int sn;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   // the first row of each wave is requested before the row count is known
@@ -390,12 +394,34 @@ __global__ __launch_bounds__(kHeadThreads) void decide_kernel(StepState* st, con
     }
     if (lane == 0) {
       const int f = st->forced[b];
-      const bool ex = f > 0 ? (layer == f) : (MODE != DECIDE_FORCED && p > gamma[layer - 1]);
+      const bool own = MODE != DECIDE_FORCED && !batch_min && p > gamma[layer - 1];
+      const bool ex = f > 0 ? (layer == f) : own;
       if (p_rec && MODE != DECIDE_FORCED) p_rec[(layer - 1) * kMaxBatch + b] = p;
+      pv[i] = p;
       if (ex) {
         sx[b] = 1;
         st->e[b] = layer;
       }
+    }
+  }
+  if (MODE != DECIDE_FORCED && batch_min) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float mn = INFINITY;
+      bool any = false;
+      for (int i = 0; i < n; ++i)
+        if (st->forced[st->act[i]] == 0) {
+          mn = fminf(mn, pv[i]);
+          any = true;
+        }
+      if (any && mn > gamma[layer - 1])
+        for (int i = 0; i < n; ++i) {
+          const int b = st->act[i];
+          if (st->forced[b] == 0) {
+            sx[b] = 1;
+            st->e[b] = layer;
+          }
+        }
     }
   }
   __syncthreads();
@@ -419,22 +445,23 @@ __global__ __launch_bounds__(kHeadThreads) void decide_kernel(StepState* st, con
   }
 }
 
-void launch_decide(int mode, StepState* st, const float* part, int nwg, const float* gamma, int layer, int L,
-                   int B, float* p_rec, const float* sts, hipStream_t s) {
+void launch_decide(int mode, bool batch_min, StepState* st, const float* part, int nwg, const float* gamma,
+                   int layer, int L, int B, float* p_rec, const float* sts, hipStream_t s) {
+  const int bm = batch_min ? 1 : 0;
   switch (mode) {
     case DECIDE_STS:
       if (!sts) throw std::logic_error("decide: no similarities");
       hipLaunchKernelGGL(decide_kernel<DECIDE_STS>, dim3(1), dim3(kHeadThreads), 0, s, st, part, nwg, gamma, layer,
-                         L, B, p_rec, sts);
+                         L, B, p_rec, sts, bm);
       return;
     case DECIDE_FORCED:
       hipLaunchKernelGGL(decide_kernel<DECIDE_FORCED>, dim3(1), dim3(kHeadThreads), 0, s, st, part, nwg, gamma,
-                         layer, L, B, p_rec, sts);
+                         layer, L, B, p_rec, sts, 0);
       return;
     default:
       if (nwg < 1 || nwg > kNwgMax) throw std::logic_error("decide: partial count out of range");
       hipLaunchKernelGGL(decide_kernel<DECIDE_HEAD>, dim3(1), dim3(kHeadThreads), 0, s, st, part, nwg, gamma,
-                         layer, L, B, p_rec, sts);
+                         layer, L, B, p_rec, sts, bm);
   }
 }
 

@@ -84,7 +84,7 @@ def _normrel(a, r):
 
 def run_parity(shape, weights, batch, P, steps, gamma, exit_mode="int4", forced_fn=None,
                prompts=None, max_seq=None, check_kv=True, check_hidden=True, label="", criterion="head",
-               check_every=1):
+               check_every=1, exit_rule="sequence"):
     import torch
     from kv_shared_exit_amd import api, _binding as B
 
@@ -96,7 +96,9 @@ def run_parity(shape, weights, batch, P, steps, gamma, exit_mode="int4", forced_
     t0 = time.time()
     dev = api.upload_weights(weights)
     model = api.Model(shape, dev, gamma=gamma, exit_mode=mode, max_batch=batch, max_positions=S,
-                      criterion=B.EE_CRIT_STS if sts else B.EE_CRIT_HEAD, check_every=check_every)
+                      criterion=B.EE_CRIT_STS if sts else B.EE_CRIT_HEAD, check_every=check_every,
+                      exit_rule=B.EE_RULE_BATCH_MIN if exit_rule == "batch_min" else B.EE_RULE_SEQUENCE)
+    bmin = exit_rule == "batch_min"
     cache = api.KVCache(model, batch, S, track=True)
     orc = om.OracleModel(shape, weights, exit_mode=exit_mode)
     ocache = om.KVCache(shape, batch, S)
@@ -125,7 +127,7 @@ def run_parity(shape, weights, batch, P, steps, gamma, exit_mode="int4", forced_
         for s in range(steps):
             forced = np.zeros(batch, np.int32) if forced_fn is None else np.asarray(forced_fn(s), np.int32)
             to, eo, io = om.decode_step(orc, ocache, tok_in, gamma=gam, forced=forced, trace=check_hidden,
-                                        criterion=criterion, check_every=check_every)
+                                        criterion=criterion, check_every=check_every, exit_rule=exit_rule)
             fg = forced.copy()
             for b in range(batch):
                 if forced[b] == 0:
@@ -134,6 +136,8 @@ def run_parity(shape, weights, batch, P, steps, gamma, exit_mode="int4", forced_
                     if np.any(np.abs(pe[ok] - gam[ok]) <= P_BAND):
                         fg[b] = eo[b]
                         res.forced_rows += 1
+            if bmin and np.any(fg != forced):   # one row's near tie decides the whole batch
+                fg = np.where(forced > 0, forced, eo).astype(np.int32)
             for attempt in range(2):
                 dbg = {"p": None, "logits": None, "gap": None}
                 if check_hidden:
@@ -144,6 +148,18 @@ def run_parity(shape, weights, batch, P, steps, gamma, exit_mode="int4", forced_
                 if len(bad) == 0:
                     break
                 assert attempt == 0, f"{label} step {s}: exit layers differ under forcing"
+                if bmin:   # the batch minimum decided: compare the minima, then force every row
+                    l = int(min(egpu[bad].min(), eo[bad].min()))
+                    rows = [b for b in range(batch) if forced[b] == 0 and np.isfinite(io["p"][b, l - 1])]
+                    bm_g = min(float(dbg["p"][b, l - 1]) for b in rows)
+                    bm_o = min(float(io["p"][b, l - 1]) for b in rows)
+                    assert (bm_g - gam[l - 1]) * (bm_o - gam[l - 1]) <= 0 and abs(bm_g - bm_o) <= 2e-3, (
+                        f"{label} step {s}: batch exit gpu {egpu} oracle {eo} not a near tie "
+                        f"(min gpu {bm_g:.6f} oracle {bm_o:.6f} threshold {gam[l - 1]})")
+                    fg = np.where(forced > 0, forced, eo).astype(np.int32)
+                    res.widened_exits += 1
+                    cache.rollback(-1, 1)
+                    continue
                 for b in bad:
                     l = int(min(egpu[b], eo[b]))          # first decision that differs
                     pg, po = float(dbg["p"][b, l - 1]), float(io["p"][b, l - 1])

@@ -267,3 +267,49 @@ def test_largest_batch(gpu):
     exits = np.concatenate(res.exits)
     assert len(set(exits.tolist())) >= 2
     assert res.compared_tokens >= 64 * 3
+
+
+# ---------------------------------------------------------------------------
+# The batch-minimum exit rule
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("criterion", ["sts", "head"])
+def test_batch_minimum_rule_against_oracle(gpu, criterion):
+    from parity import run_parity
+    sh = FIVE
+    if criterion == "sts":
+        w = synth.make_weights(sh, 41)
+        # thresholds a little under the medians: the batch minimum crosses them now and then
+        thr = _median_similarity(sh, w, 4, 8, 5, seed=98) - 0.05
+    else:
+        wl = Workload("five", sh, 1, 8, 6, 0.75, "calibrated", 1.5, index=7)
+        w = synth.make_weights(sh, 7, alpha=np.array(calibrate(wl, verbose=False)["alpha"]))
+        thr = 0.75
+    res = run_parity(sh, w, 4, 8, 6, thr, criterion=criterion, exit_rule="batch_min",
+                     label=f"five-{criterion}-batchmin")
+    for e in res.exits:
+        assert len(set(e.tolist())) == 1, f"one exit layer per step: {e}"
+    assert any(e[0] < sh.n_layers for e in res.exits), "the batch should exit early in some step"
+
+
+def test_batch_minimum_of_one_sequence_is_the_per_sequence_rule(gpu):
+    from kv_shared_exit_amd import api, _binding as B
+    sh = FIVE
+    w = synth.make_weights(sh, 41)
+    tau = _median_similarity(sh, w, 1, 8, 5, seed=97)
+    dev = api.upload_weights(w)
+    prompts = np.random.default_rng(8).integers(0, sh.vocab, (1, 8)).astype(np.int32)
+
+    def run(rule):
+        m = api.Model(sh, dev, gamma=tau, criterion=B.EE_CRIT_STS, exit_rule=rule, max_batch=1,
+                      max_positions=16)
+        c = api.KVCache(m, 1, 16)
+        try:
+            api.prefill(m, c, prompts)
+            return [api.decode_step(m, c, 1) for _ in range(6)]
+        finally:
+            c.close()
+            m.close()
+
+    for (ta, ea), (tb, eb) in zip(run(B.EE_RULE_SEQUENCE), run(B.EE_RULE_BATCH_MIN)):
+        np.testing.assert_array_equal(ea, eb)
+        np.testing.assert_array_equal(ta, tb)
