@@ -111,7 +111,8 @@ def cpu_baseline(wl, weights, exit_layer, ctx, criterion="head", every=1):
                        f"{dt:.1f} s, float64 numpy")}
 
 
-def baselines(api, wl, weights, dev, stream, exits, W, K2, ms_main, criterion=0, thresholds=None, every=1):
+def baselines(api, wl, weights, dev, stream, exits, W, K2, ms_main, criterion=0, thresholds=None, every=1,
+              rule=0):
     """The method against the decoders it replaces, on the same prompts and
     weights, each timed over K2 graph-replayed steps after W warm-up steps:
     (i) the plain decoder at full depth without exit heads (EE_EXIT_NONE);
@@ -127,7 +128,7 @@ def baselines(api, wl, weights, dev, stream, exits, W, K2, ms_main, criterion=0,
     res = {}
     for name, mode in (("full_depth_no_heads", Bd.EE_EXIT_NONE), ("bf16_exit_copies_same_exits", Bd.EE_EXIT_BF16)):
         m = api.Model(sh, dev, gamma=wl.gamma if thresholds is None else thresholds, exit_mode=mode,
-                      max_batch=B, max_positions=S, criterion=criterion, check_every=every)
+                      max_batch=B, max_positions=S, criterion=criterion, check_every=every, exit_rule=rule)
         c = api.KVCache(m, B, S)
         try:
             api.prefill(m, c, prompts, stream=stream)
@@ -160,6 +161,8 @@ def main():
     ap.add_argument("--criterion", choices=("head", "sts"), default="head",
                     help="exit criterion: the exit head (default) or River-LLM's state transition "
                          "similarity with the workload's calibrated thresholds (secondary line)")
+    ap.add_argument("--exit-rule", choices=("sequence", "batch-min"), default="sequence",
+                    help="per-sequence exits (default) or River-LLM's batch minimum (secondary line)")
     ap.add_argument("--check-every", type=int, default=1,
                     help="evaluate the exit criterion only after every N-th layer (secondary line)")
     ap.add_argument("--no-baselines", action="store_true",
@@ -204,7 +207,9 @@ def main():
     log(f"weights drawn ({time.time() - t0:.0f}s)")
     dev = api.upload_weights(weights)
     every = max(1, args.check_every)
-    model = api.Model(sh, dev, gamma=thresholds, max_batch=B, max_positions=S, criterion=crit, check_every=every)
+    rule = Bd.EE_RULE_BATCH_MIN if args.exit_rule == "batch-min" else Bd.EE_RULE_SEQUENCE
+    model = api.Model(sh, dev, gamma=thresholds, max_batch=B, max_positions=S, criterion=crit, check_every=every,
+                      exit_rule=rule)
     cache = api.KVCache(model, B, S)
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
@@ -329,6 +334,9 @@ def main():
         out["copy_probe"] = copy_probe
     cache.close()
     model.close()
+    if rule == Bd.EE_RULE_BATCH_MIN:
+        out["metric"] += ", batch-minimum exits"
+        out["config"]["workload"] += ", batch-minimum exit rule"
     if every > 1:
         out["metric"] += f", criterion every {every} layers"
         out["config"]["workload"] += f", criterion evaluated after every {every}th layer"
@@ -341,7 +349,7 @@ def main():
                            "frac": round(step_gbs / HBM_PEAK_GBS, 4), "traffic": None}
     if not args.no_baselines:
         out["speedup"] = baselines(api, wl, weights, dev, stream, exits, W, min(K, 40), 1e3 * t_el / K,
-                                   criterion=crit, thresholds=thresholds, every=every)
+                                   criterion=crit, thresholds=thresholds, every=every, rule=rule)
         log(f"baselines done ({time.time() - t0:.0f}s)")
     del dev
     if not args.no_cpu_baseline:
