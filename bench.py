@@ -192,7 +192,7 @@ def main():
     crit = Bd.EE_CRIT_STS if sts else Bd.EE_CRIT_HEAD
     thresholds = wl.gamma
     if sts:
-        thresholds = synth.load_tau(wl)
+        thresholds = synth.load_tau(wl, batch_min=args.exit_rule == "batch-min")
         if thresholds is None:
             print(f"no similarity thresholds for {wl.name} (synth/calibration/{wl.name}_sts.json)", file=sys.stderr)
             sys.exit(2)

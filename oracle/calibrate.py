@@ -105,17 +105,24 @@ def calibrate_sts(wl, steps: int, calib_batch: int = 4, prompt_len: int | None =
             print(f"[calibrate-sts {wl.name}] {msg} ({time.time() - t0:.0f}s)", flush=True)
 
     hid, _ = _full_depth_states(wl, steps, calib_batch, P0, say, matmul_dtype)
-    taus = []
+    # batch-minimum rule: the batch of wl.batch sequences leaves when its
+    # smallest similarity > tau; with independent sequences that happens with
+    # probability P(s > tau)^B, so the batch hazard is h when each sequence
+    # exceeds tau with probability h^(1/B)
+    hb = h ** (1.0 / wl.batch)
+    taus, taus_b = [], []
     for l in range(1, L):
         sts = state_transition_similarity(hid[:, :, l - 1].reshape(-1, sh.d_model),
                                           hid[:, :, l].reshape(-1, sh.d_model))
         t = float(np.quantile(sts, 1.0 - h))
+        tb = float(np.quantile(sts, 1.0 - hb))
         taus.append(t)
-        say(f"layer {l}: tau={t:.6f} (similarity {sts.min():.4f}..{sts.max():.4f})")
+        taus_b.append(tb)
+        say(f"layer {l}: tau={t:.6f} batch-min tau={tb:.6f} (similarity {sts.min():.4f}..{sts.max():.4f})")
     return {"workload": wl.name, "criterion": "sts", "mean_exit": wl.mean_exit, "hazard": h,
             "samples_per_layer": int(hid.shape[0] * hid.shape[1]),
             "source": f"full-depth greedy decode, {calib_batch} prompts of {P0} tokens, {steps} steps",
-            "tau": taus}
+            "tau": taus, "batch": wl.batch, "tau_batch_min": taus_b}
 
 
 def calibrate(wl, steps: int | None = None, calib_batch: int = 4, verbose: bool = True,

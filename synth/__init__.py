@@ -208,15 +208,19 @@ def load_alpha(wl: Workload) -> np.ndarray | None:
     return alpha
 
 
-def load_tau(wl: Workload) -> np.ndarray | None:
+def load_tau(wl: Workload, batch_min: bool = False) -> np.ndarray | None:
     """Per-layer similarity thresholds tau_l (l = 1..L-1) of a workload's state
-    transition similarity criterion, or None."""
+    transition similarity criterion (for the batch-minimum rule with
+    ``batch_min``), or None."""
     path = os.path.join(CALIB_DIR, f"{wl.name}_sts.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         data = json.load(f)
-    tau = np.asarray(data["tau"], dtype=np.float64)
+    key = "tau_batch_min" if batch_min else "tau"
+    if key not in data:
+        return None
+    tau = np.asarray(data[key], dtype=np.float64)
     assert tau.shape == (wl.shape.n_layers - 1,)
     return tau
 
