@@ -21,7 +21,10 @@
  * l equals the forced exit layer when one is given.  The emitted token is the
  * greedy argmax of the final RMSNorm + LM head after layer L (lowest index on
  * ties).  The exit layer e_b is the layer after which b left the backbone; e_b =
- * L means b never exited.
+ * L means b never exited.  Model options replace the exit head by River-LLM's
+ * state transition similarity (section 5.1-5.2), let the batch minimum decide
+ * (section 5.2), evaluate the criterion only every N layers (CALM explainer,
+ * checking every N layers), or drop the criterion (the plain decoder).
  *
  * Precision: bf16 weights and GEMV inputs, float32 accumulation, float32
  * residual stream, bf16 K/V cache, float32 logits and softmax.  int4 codes are
@@ -217,9 +220,10 @@ ee_status ee_prefill(ee_model *m, ee_kv_cache *c, int32_t batch, const int32_t *
 /* One decode step for sequences 0..batch-1.
  * in_tokens_host: [batch] input tokens, or NULL to use each sequence's last
  *   output token kept on the device (from ee_prefill or the previous step).
- * forced_exit_host: [batch] or NULL; 0 lets the exit head decide, 1..L forces
- *   the exit layer (the heads still run; their decision is overridden).
- * gamma_host: [L-1] thresholds for this step, or NULL for the model's.
+ * forced_exit_host: [batch] or NULL; 0 lets the criterion decide, 1..L forces
+ *   the exit layer (the criterion still runs; its decision is overridden).
+ * gamma_host: [L-1] thresholds for this step (gamma_l or tau_l), or NULL for
+ *   the model's.
  * out_tokens_host, out_exit_layers_host: [batch] greedy tokens and exit layers.
  * dbg: optional diagnostics.  Returns after the outputs are on the host.
  * Without diagnostics and without profiling (ee_profile_enable), the step's
