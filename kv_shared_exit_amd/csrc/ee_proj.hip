@@ -38,7 +38,10 @@
 namespace ee {
 
 constexpr int kWaves = kProjThreads / 64;
-// bf16 rows on MFMA (true) or on the vector ALU with dot2 (false)
+// bf16 rows on MFMA (true) or on the vector ALU with dot2 (false).  With the
+// row-major weights a 16-row MFMA operand load touches 16 rows x 64 bytes, and
+// the vocabulary GEMV measured 219 us against 159-178 us on the vector ALU, so
+// the MFMA path is kept only as the measured alternative.
 constexpr bool kBf16Mfma = false;
 // share of a range's workgroups given to the bf16 rows when both formats have
 // rows, in 1/256 (bf16 streams ~4x the bytes of its int4 copy; measured)
