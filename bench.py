@@ -111,6 +111,16 @@ def cpu_baseline(wl, weights, exit_layer, ctx, criterion="head", every=1):
                        f"{dt:.1f} s, float64 numpy")}
 
 
+def prefill(api, model, cache, prompts, stream, t0, chunk=512):
+    """Prefill in chunks of positions (the library appends each chunk after the
+    cached positions), logging progress on long prompts."""
+    P = prompts.shape[1]
+    for p0 in range(0, P, chunk):
+        api.prefill(model, cache, prompts[:, p0:p0 + chunk], stream=stream)
+        if P > chunk:
+            log(f"prefill positions {min(p0 + chunk, P)}/{P} ({time.time() - t0:.0f}s)")
+
+
 def baselines(api, wl, weights, dev, stream, exits, W, K2, ms_main, criterion=0, thresholds=None, every=1,
               rule=0):
     """The method against the decoders it replaces, on the same prompts and
@@ -131,7 +141,7 @@ def baselines(api, wl, weights, dev, stream, exits, W, K2, ms_main, criterion=0,
                       max_batch=B, max_positions=S, criterion=criterion, check_every=every, exit_rule=rule)
         c = api.KVCache(m, B, S)
         try:
-            api.prefill(m, c, prompts, stream=stream)
+            prefill(api, m, c, prompts, stream, time.time())
             forced = (lambda s_: exits[s_ % len(exits)]) if mode == Bd.EE_EXIT_BF16 else (lambda s_: None)
             for s_ in range(W):
                 api.decode_step(m, c, B, forced=forced(s_), stream=stream)
@@ -197,8 +207,12 @@ def main():
             print(f"no similarity thresholds for {wl.name} (synth/calibration/{wl.name}_sts.json)", file=sys.stderr)
             sys.exit(2)
     alpha = synth.load_alpha(wl)
-    if alpha is None and wl.policy == "calibrated" and not sts:
-        log("no calibration file: exit heads unscaled (alpha = 1)")
+    # a calibrated workload without calibrated exit-head scales (the 34B shape:
+    # its float64 oracle does not fit host memory) runs the exit layers of its
+    # target distribution as forced exits; the heads are still computed
+    target = alpha is None and wl.policy == "calibrated" and not sts
+    if target:
+        log("no calibration file: exit layers drawn from the target distribution (forced), heads computed")
     t0 = time.time()
     weights = synth.make_weights(sh, wl.seed_weights, alpha=alpha)
     if sts:  # the similarity criterion reads no head weights
@@ -215,13 +229,14 @@ def main():
     torch.cuda.synchronize()
     log(f"model ready ({time.time() - t0:.0f}s)")
     prompts = synth.make_prompts(wl)
-    api.prefill(model, cache, prompts, stream=stream)
+    prefill(api, model, cache, prompts, stream, t0)
     log(f"prefill {B}x{P} done ({time.time() - t0:.0f}s)")
 
     exits, toks = [], []
 
     def step(s, tokens=None):
-        f = synth.make_forced_exits(wl, s) if wl.policy == "forced" else None
+        f = (synth.make_forced_exits(wl, s) if wl.policy == "forced" else
+             synth.make_target_exits(wl, s) if target else None)
         return api.decode_step(model, cache, B, tokens=tokens, forced=f, stream=stream)
 
     last = None
@@ -330,6 +345,14 @@ def main():
                  "head_launches_per_step": round(head_launches / K, 2)},
         "cpu_baseline": None,
     }
+    if wl.name != "8b":
+        out["metric"] = out["metric"].replace("(8B shape, b=8)", f"({wl.name} shape, b={B})")
+    if wl.policy == "forced":
+        out["config"]["workload"] += (f", exit layers forced uniform in [{wl.forced_lo}, {wl.forced_hi}] "
+                                      f"per sequence and step (heads computed)")
+    elif target:
+        out["config"]["workload"] += (f", exit layers forced from the target distribution (truncated geometric, "
+                                      f"mean {wl.mean_exit}; heads computed, no calibrated scales)")
     if copy_probe:
         out["copy_probe"] = copy_probe
     cache.close()

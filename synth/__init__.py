@@ -32,7 +32,7 @@ import numpy as np
 
 __all__ = [
     "ModelShape", "Workload", "WORKLOADS", "workload", "make_weights",
-    "make_prompts", "make_forced_exits", "geometric_hazard", "exit_pmf",
+    "make_prompts", "make_forced_exits", "make_target_exits", "geometric_hazard", "exit_pmf",
     "load_alpha", "load_tau", "layer_names", "bf16_bits_to_f32",
 ]
 
@@ -277,6 +277,20 @@ def make_forced_exits(wl: Workload, step: int, batch: int | None = None,
     hi = wl.forced_hi if hi is None else hi
     rng = np.random.default_rng([wl.seed_forced, step])
     return rng.integers(lo, hi + 1, size=batch, dtype=np.int64).astype(np.int32)
+
+
+def make_target_exits(wl: Workload, step: int, batch: int | None = None) -> np.ndarray:
+    """Exit layers for one decode step drawn from a calibrated workload's
+    target distribution (truncated geometric with the workload's mean exit
+    layer), int32 [batch].  Used as forced exits where no calibrated exit-head
+    scales exist, so that the step runs the exit layers the calibration aims
+    at; seeded like the forced schedules (a second stream of the same seed)."""
+    assert wl.mean_exit is not None
+    batch = wl.batch if batch is None else batch
+    L = wl.shape.n_layers
+    cdf = np.cumsum(exit_pmf(geometric_hazard(wl.mean_exit, L), L))
+    u = np.random.default_rng([wl.seed_forced, 1, step]).random(batch)
+    return (np.searchsorted(cdf, u * cdf[-1], side="right") + 1).clip(1, L).astype(np.int32)
 
 
 def exit_pmf(h: float, L: int) -> np.ndarray:

@@ -42,3 +42,25 @@ def test_exit_potential_and_target_distribution():
 
 def test_default_gamma():
     assert synth.workload("8b").gamma == GOLD["gamma_default"]["gamma"]
+
+
+def test_target_exit_draws_follow_the_target_distribution():
+    # the 1B page's mean exit layer (4.81 of 16); draws stand in for calibrated
+    # heads where none exist, so their histogram must match the pmf
+    wl = synth.workload("1b")
+    L = wl.shape.n_layers
+    e = np.concatenate([synth.make_target_exits(wl, s, batch=64) for s in range(500)])
+    assert e.min() >= 1 and e.max() <= L
+    pmf = synth.exit_pmf(synth.geometric_hazard(wl.mean_exit, L), L)
+    freq = np.bincount(e, minlength=L + 1)[1:] / e.size
+    # 32000 draws: every cell within 5 standard errors
+    se = np.sqrt(pmf * (1 - pmf) / e.size)
+    assert np.all(np.abs(freq - pmf) <= 5 * se + 1e-12)
+    assert abs(e.mean() - g_mean(wl)) < 0.1
+    # seeded: the same step gives the same draw, another step another
+    np.testing.assert_array_equal(synth.make_target_exits(wl, 7, batch=8), synth.make_target_exits(wl, 7, batch=8))
+    assert not np.array_equal(synth.make_target_exits(wl, 7, batch=64), synth.make_target_exits(wl, 8, batch=64))
+
+
+def g_mean(wl):
+    return GOLD["exit_potential"]["mean_exit"] if wl.name == "1b" else wl.mean_exit
