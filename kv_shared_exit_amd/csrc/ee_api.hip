@@ -77,6 +77,7 @@ struct ee_model {
   uint16_t *qrot = nullptr, *attn_o = nullptr;
   uint16_t *act = nullptr, *z = nullptr;
   float* head_part = nullptr;
+  uint16_t* lm_head_t = nullptr;  // E in the wide vocabulary pass's tiled order (max_batch > 8), else null
   float* h2 = nullptr;   // residual after attention while the layer's input is kept in h (EE_CRIT_STS) [b][d]
   float* sts = nullptr;  // state transition similarity per sequence [64]
   float* attn_part = nullptr;
@@ -454,7 +455,15 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
         a.part = m->head_part;
         hipEvent_t e0, e1;
         prof_events(m, &e0, &e1);
-        launch_proj(EPI_LSE, a, kNwg, B, s, e0, e1);
+        // more than 8 rows go to the wide pass (one read of E for all rows);
+        // the row count is on the device, so both are launched and one returns
+        const bool wide = m->lm_head_t && B > 8;
+        if (wide) a.max_rows = 8;
+        launch_proj(EPI_LSE, a, kNwg, B, s, e0, wide ? nullptr : e1);
+        if (wide) {
+          a.wb[0] = m->lm_head_t;
+          launch_wide_vocab(EPI_LSE, a, kNwg, s, e1);
+        }
       }
       launch_decide(DECIDE_HEAD, bmin, st, m->head_part, kNwg, m->d_gamma, l, L, B, m->p_rec, nullptr, s);
     }
@@ -474,7 +483,12 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
     a.part = m->head_part;
     a.logits = dbg.logits ? m->dbg_logits : nullptr;
     a.logits_stride = cf.vocab;
-    launch_proj(EPI_ARGMAX, a, kNwg, B, s);
+    if (m->lm_head_t && B > 8) {  // every row of the batch: the wide pass alone
+      a.wb[0] = m->lm_head_t;
+      launch_wide_vocab(EPI_ARGMAX, a, kNwg, s);
+    } else {
+      launch_proj(EPI_ARGMAX, a, kNwg, B, s);
+    }
     launch_final(st, m->head_part, kNwg, B, cf.vocab, c->lens, 1, s);
   } else {
     launch_advance(c->lens, B, s);
@@ -625,6 +639,13 @@ ee_status ee_create_model(const ee_model_config* cfg, const ee_weights* w, const
           launch_quantize((const uint16_t*)lw.w_down, d, F, G, 0, q.down.codes, q.down.scales, m->own);
           HIPCHK(hipGetLastError());
         }
+      }
+      // E once more in the tiled order of the wide vocabulary pass, for batches
+      // of more than 8 rows (E is read once per launch for up to 64 rows)
+      if (c.max_batch > 8 && wide_vocab_supported(d)) {
+        m->lm_head_t = m->alloc<uint16_t>(wide_vocab_elems(c.vocab, d));
+        launch_tile_vocab(m->lm_head, c.vocab, d, m->lm_head_t, m->own);
+        HIPCHK(hipGetLastError());
       }
       // RoPE table: cos/sin of pos * theta^(-2i/hd) in double, rounded to float
       const int half = c.head_dim / 2;

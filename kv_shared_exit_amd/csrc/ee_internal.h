@@ -60,6 +60,8 @@ struct ProjArgs {
   int H, Hkv, hd, S;
   int hd_log2;                                    // log2(hd)
   int nwg_r;                                      // workgroups per column range (set by launch_proj)
+  int max_rows;                                   // EPI_LSE / EPI_ARGMAX: do nothing above this many rows
+                                                  // (the wide pass has them); 0 = no limit
 };
 
 struct AttnArgs {
@@ -102,6 +104,15 @@ void launch_init(StepState* st, const int32_t* prompt, int P, int t, int B, int 
                  const uint16_t* emb, int d, int V, float* h, float* p_rec, const uint16_t* gain,
                  float eps, uint16_t* x, hipStream_t s);
 void launch_attention(const AttnArgs& a, hipStream_t s);
+// Vocabulary GEMVs (EPI_LSE / EPI_ARGMAX) for more than 8 rows on MFMA
+// (ee_wide.hip): E read once for up to 64 rows from a tiled copy made by
+// launch_tile_vocab (wide_vocab_elems(V, d) bf16).  The kernel does nothing
+// when the device-side row count is 8 or less.  Writes nwg partials per row
+// like launch_proj; with ev_end set, the launch records its end into it.
+bool wide_vocab_supported(int d);
+size_t wide_vocab_elems(int V, int d);
+void launch_tile_vocab(const uint16_t* E, int V, int d, uint16_t* Et, hipStream_t s);
+void launch_wide_vocab(int epi, const ProjArgs& a, int nwg, hipStream_t s, hipEvent_t ev_end = nullptr);
 // Exit decision after layer `layer` for the rows on the backbone: from the exit
 // head's nwg (max, sum exp) partials (DECIDE_HEAD), from the state transition
 // similarity per sequence in sts (DECIDE_STS), or forced exits only, no

@@ -772,6 +772,9 @@ __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a)
   }
   const int n_bf = min(max(*a.cnt_bf, 0), kMaxBatch);
   const int n_i4 = min(max(*a.cnt_i4, 0), kMaxBatch);
+  if constexpr (EPI == EPI_LSE || EPI == EPI_ARGMAX) {
+    if (n_bf > a.max_rows) return;  // the wide (MFMA) vocabulary pass has these rows
+  }
   if (threadIdx.x < 64) {
     const int e = threadIdx.x & 7;
     const int lb = a.list_bf[e], li = a.list_i4[e];
@@ -890,6 +893,7 @@ int launch_proj(int epi, const ProjArgs& a0, int nwg, int batch, hipStream_t s, 
   ProjArgs a = a0;
   if (!a.cnt_bf || !a.list_bf) a.cnt_bf = a.list_bf = no_rows();
   if (!a.cnt_i4 || !a.list_i4) a.cnt_i4 = a.list_i4 = no_rows();
+  if (a.max_rows <= 0) a.max_rows = kMaxBatch;
   // the vocabulary epilogues write one partial per workgroup (kNwgMax of them)
   int g = std::max(1, std::min(nwg, kNwgMax));
   a.nkc = 1;

@@ -269,6 +269,30 @@ def test_largest_batch(gpu):
     assert res.compared_tokens >= 64 * 3
 
 
+@pytest.mark.parametrize("label,sh,batch", [
+    # 2 batch blocks of 16 (ragged), head_dim 64, group 64
+    ("wide-hd64", SHAPES["hd64"], 24),
+    # a vocabulary that ends inside a 16-row tile (1003), 3 batch blocks
+    ("wide-odd-vocab", ModelShape(3, 256, 4, 2, 64, 512, 1003, 32, rope_theta=500000.0), 40),
+    # every row of the largest batch (4 blocks of 16)
+    ("wide-b64", ModelShape(2, 256, 4, 2, 64, 384, 700, 32, rope_theta=10000.0), 64),
+])
+def test_wide_batch_vocabulary_pass(gpu, label, sh, batch):
+    """Batches of more than 8 rows: the exit head's vocabulary pass and the LM
+    head run on the matrix-core pass over the tiled copy of E whenever more than
+    8 rows are on the backbone (the final LM head always, since every row takes
+    it), and on the vector-ALU pass otherwise; exits are spread so that layers
+    see both."""
+    from parity import run_parity
+    wl = Workload(label, sh, 1, 6, 4, 0.75, "calibrated", max(1.2, sh.n_layers / 2), index=9)
+    cal = calibrate(wl, verbose=False)
+    w = synth.make_weights(sh, 9, alpha=np.array(cal["alpha"]))
+    res = run_parity(sh, w, batch, 6, 3, 0.75, label=label)
+    exits = np.concatenate(res.exits)
+    assert len(set(exits.tolist())) >= 2
+    assert res.compared_tokens >= batch * 2
+
+
 # ---------------------------------------------------------------------------
 # The batch-minimum exit rule
 # ---------------------------------------------------------------------------
