@@ -78,6 +78,14 @@ struct ee_model {
   uint16_t *act = nullptr, *z = nullptr;
   float* head_part = nullptr;
   uint16_t* lm_head_t = nullptr;  // E in the wide vocabulary pass's tiled order (max_batch > 8), else null
+  // projections for more than 8 rows on matrix cores: each layer's bf16
+  // weights in the tiled order (QKV, O, gate then up, down, the head's T)
+  struct WideW {
+    uint16_t *qkv = nullptr, *o = nullptr, *gu = nullptr, *down = nullptr, *T = nullptr;
+  };
+  bool wide = false;
+  std::vector<WideW> ww;
+  float* wide_y = nullptr;  // partial sums of the wide QKV, gate/up and T projections
   float* h2 = nullptr;   // residual after attention while the layer's input is kept in h (EE_CRIT_STS) [b][d]
   float* sts = nullptr;  // state transition similarity per sequence [64]
   float* attn_part = nullptr;
@@ -287,6 +295,32 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
   // with unquantised exit copies every row runs the bf16 weights.
   const int32_t* list_bf = int4 ? st->act : st->all;
   const int32_t* cnt_bf = int4 ? &st->n_act : &st->n_all;
+  // more than 8 rows: every projection on matrix cores (weights read once for
+  // all rows), float32 partial sums over column ranges summed by an epilogue
+  const bool wide = m->wide && B > 8;
+  auto wide_args = [&](int N, int K, const uint16_t* wt, const uint16_t* x, int x_stride, float* y, int ystride) {
+    WideArgs wa{};
+    wa.N = N;
+    wa.K = K;
+    wa.nr = wide_ranges(N, K, &wa.kr);
+    wa.wt = wt;
+    wa.x = x;
+    wa.x_stride = x_stride;
+    wa.list_bf = list_bf;
+    wa.cnt_bf = cnt_bf;
+    wa.y = y;
+    wa.y_stride = ystride;
+    wa.y_cstride = (size_t)kMaxBatch * ystride;
+    wa.G = cf.group_size;
+    wa.n0 = N;
+    return wa;
+  };
+  auto wide_i4 = [&](WideArgs& wa, const Q4& q0) {
+    wa.q4[0] = q0.codes;
+    wa.s4[0] = q0.scales;
+    wa.list_i4 = st->ex;
+    wa.cnt_i4 = &st->n_ex;
+  };
 
   for (int l = 1; l <= L; ++l) {
     const ee_layer_weights& w = m->lw[l - 1];
@@ -327,7 +361,14 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       a.hd = hd;
       a.hd_log2 = __builtin_ctz(hd);
       a.S = c->S;
-      launch_proj(EPI_QKV, a, kNwg, B, s);
+      if (wide) {
+        WideArgs wa = wide_args(nqkv, d, m->ww[l - 1].qkv, m->xn, d, m->wide_y, nqkv);
+        if (q) wide_i4(wa, q->qkv);
+        launch_wide_proj(wa, s);
+        launch_wide_qkv(m->wide_y, wa.nr, wa.y_cstride, nqkv, st->all, &st->n_all, B, a, s);
+      } else {
+        launch_proj(EPI_QKV, a, kNwg, B, s);
+      }
     }
     {
       AttnArgs a{};
@@ -365,7 +406,15 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       a.y = m->parts;
       a.y_stride = d;
       a.y_cstride = (int)pstride;
-      const int nkc = launch_proj(EPI_PART, a, kNwg, B, s);
+      int nkc;
+      if (wide) {
+        WideArgs wa = wide_args(d, qd, m->ww[l - 1].o, m->attn_o, qd, m->parts, d);
+        if (q) wide_i4(wa, q->o);
+        launch_wide_proj(wa, s);
+        nkc = wa.nr;
+      } else {
+        nkc = launch_proj(EPI_PART, a, kNwg, B, s);
+      }
       // with the similarity criterion the layer's input stays in h (the
       // residual after attention goes to h2) until the layer's end
       float* h_mid = heads && sts_crit && l < L && l % every == 0 ? m->h2 : m->h;
@@ -392,7 +441,19 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       a.x_stride = d;
       a.y = m->act;
       a.y_stride = F;
-      launch_proj(EPI_SWIGLU, a, kNwg, B, s);
+      if (wide) {  // gate rows 0..F-1, up rows F..2F-1
+        WideArgs wa = wide_args(2 * F, d, m->ww[l - 1].gu, m->xn, d, m->wide_y, 2 * F);
+        if (q) {
+          wide_i4(wa, q->gate);
+          wa.q4[1] = q->up.codes;
+          wa.s4[1] = q->up.scales;
+          wa.n0 = F;
+        }
+        launch_wide_proj(wa, s);
+        launch_wide_swiglu(m->wide_y, wa.nr, wa.y_cstride, 2 * F, st->all, &st->n_all, B, F, m->act, s);
+      } else {
+        launch_proj(EPI_SWIGLU, a, kNwg, B, s);
+      }
     }
     const bool head_here = heads && l < L && l % every == 0;  // the criterion is evaluated after this layer
     const bool sts_here = head_here && sts_crit;
@@ -414,7 +475,15 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       a.y = m->parts;
       a.y_stride = d;
       a.y_cstride = (int)pstride;
-      const int nkc = launch_proj(EPI_PART, a, kNwg, B, s);
+      int nkc;
+      if (wide) {
+        WideArgs wa = wide_args(d, F, m->ww[l - 1].down, m->act, F, m->parts, d);
+        if (q) wide_i4(wa, q->down);
+        launch_wide_proj(wa, s);
+        nkc = wa.nr;
+      } else {
+        nkc = launch_proj(EPI_PART, a, kNwg, B, s);
+      }
       // the next projection's input: the next layer's attention norm, or the
       // final norm before the LM head; bf16(h) for this layer's exit head
       const void* g_next = l < L ? m->lw[l].attn_norm : (const void*)m->final_norm;
@@ -441,7 +510,15 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
         a.x_stride = d;
         a.y = m->z;
         a.y_stride = d;
-        launch_proj(EPI_BF16, a, kNwg, B, s);
+        if (wide && m->ww[l - 1].T) {
+          WideArgs wa = wide_args(d, d, m->ww[l - 1].T, m->hb, d, m->wide_y, d);
+          wa.list_bf = st->act;
+          wa.cnt_bf = &st->n_act;
+          launch_wide_proj(wa, s);
+          launch_wide_bf16(m->wide_y, wa.nr, wa.y_cstride, d, st->act, &st->n_act, B, d, m->z, d, s);
+        } else {
+          launch_proj(EPI_BF16, a, kNwg, B, s);
+        }
       }
       {
         ProjArgs a = base_args(m);
@@ -647,6 +724,35 @@ ee_status ee_create_model(const ee_model_config* cfg, const ee_weights* w, const
         launch_tile_vocab(m->lm_head, c.vocab, d, m->lm_head_t, m->own);
         HIPCHK(hipGetLastError());
       }
+      // and the layers' bf16 weights, for the wide projections
+      m->wide = c.max_batch > 8 && wide_vocab_supported(d) && wide_vocab_supported(qd) && wide_vocab_supported(F);
+      if (m->wide) {
+        m->ww.resize(L);
+        for (int l = 1; l <= L; ++l) {
+          const ee_layer_weights& lw = m->lw[l - 1];
+          ee_model::WideW& t = m->ww[l - 1];
+          t.qkv = m->alloc<uint16_t>((size_t)(qd + 2 * kvd) * d);
+          launch_tile_rows((const uint16_t*)lw.wq, qd, d, t.qkv, m->own);
+          launch_tile_rows((const uint16_t*)lw.wk, kvd, d, t.qkv + (size_t)qd * d, m->own);
+          launch_tile_rows((const uint16_t*)lw.wv, kvd, d, t.qkv + (size_t)(qd + kvd) * d, m->own);
+          t.o = m->alloc<uint16_t>((size_t)d * qd);
+          launch_tile_rows((const uint16_t*)lw.wo, d, qd, t.o, m->own);
+          t.gu = m->alloc<uint16_t>((size_t)2 * F * d);
+          launch_tile_rows((const uint16_t*)lw.w_gate, F, d, t.gu, m->own);
+          launch_tile_rows((const uint16_t*)lw.w_up, F, d, t.gu + (size_t)F * d, m->own);
+          t.down = m->alloc<uint16_t>((size_t)d * F);
+          launch_tile_rows((const uint16_t*)lw.w_down, d, F, t.down, m->own);
+          if (l < L && lw.head_T) {
+            t.T = m->alloc<uint16_t>((size_t)d * d);
+            launch_tile_rows((const uint16_t*)lw.head_T, d, d, t.T, m->own);
+          }
+          HIPCHK(hipGetLastError());
+        }
+        const size_t yq = (size_t)wide_ranges(qd + 2 * kvd, d, nullptr) * kMaxBatch * (qd + 2 * kvd);
+        const size_t yg = (size_t)wide_ranges(2 * F, d, nullptr) * kMaxBatch * 2 * F;
+        const size_t yt = (size_t)wide_ranges(d, d, nullptr) * kMaxBatch * d;
+        m->wide_y = m->alloc<float>(std::max(yq, std::max(yg, yt)));
+      }
       // RoPE table: cos/sin of pos * theta^(-2i/hd) in double, rounded to float
       const int half = c.head_dim / 2;
       std::vector<float> cs((size_t)c.max_positions * half), sn(cs.size());
@@ -665,6 +771,8 @@ ee_status ee_create_model(const ee_model_config* cfg, const ee_weights* w, const
       m->h = m->alloc<float>((size_t)Bm * d);
       const int rows = std::min(8, c.max_batch);
       m->nkc_max = std::max(proj_ranges(qd, d, kNwg, rows, nullptr), proj_ranges(F, d, kNwg, rows, nullptr));
+      if (m->wide)
+        m->nkc_max = std::max(m->nkc_max, std::max(wide_ranges(d, qd, nullptr), wide_ranges(d, F, nullptr)));
       m->parts = m->alloc<float>((size_t)m->nkc_max * Bm * d);
       m->xn = m->alloc<uint16_t>((size_t)Bm * d);
       m->hb = m->alloc<uint16_t>((size_t)Bm * d);

@@ -64,6 +64,25 @@ struct ProjArgs {
                                                   // (the wide pass has them); 0 = no limit
 };
 
+// A projection for more than 8 rows on matrix cores (ee_wide.hip): float32
+// partial sums y[r][seq][n] over column ranges r, for the rows of both lists
+// (bf16 rows from the tiled copy of the weights, exited rows from the int4
+// copy); an epilogue kernel (or the finish kernel) sums the ranges.
+struct WideArgs {
+  int N, K;              // output rows (all segments), input columns (multiple of 256)
+  int nr, kr;            // column ranges and their width (multiple of 256)
+  int nrb;               // 128-row blocks
+  int g_bf;              // workgroups of the bf16 pass (nrb * nr); the rest run the int4 pass
+  const uint16_t* wt;    // bf16 weights in the tiled order (launch_tile_rows)
+  const uint32_t* q4[2]; // int4 codes / scales of rows [0, n0) and [n0, N) (layout: ee_proj.hip)
+  const uint16_t* s4[2];
+  int n0, G;
+  const uint16_t* x; int x_stride;                // bf16 input rows [seq][x_stride]
+  const int32_t* list_bf; const int32_t* cnt_bf;  // rows run with bf16 weights
+  const int32_t* list_i4; const int32_t* cnt_i4;  // rows run with int4 weights (may be null)
+  float* y; size_t y_cstride; int y_stride;       // y[r * y_cstride + seq * y_stride + n]
+};
+
 struct AttnArgs {
   const uint16_t* q;   // rotated q [b][H*hd]
   const uint16_t* K;   // layer base of the cache: [Bmax][Hkv][S][hd]
@@ -113,6 +132,25 @@ bool wide_vocab_supported(int d);
 size_t wide_vocab_elems(int V, int d);
 void launch_tile_vocab(const uint16_t* E, int V, int d, uint16_t* Et, hipStream_t s);
 void launch_wide_vocab(int epi, const ProjArgs& a, int nwg, hipStream_t s, hipEvent_t ev_end = nullptr);
+// The tiled order of a bf16 matrix [N][K] (K a multiple of 256; rows padded to
+// 16 with zeros): the 1 KB A operand of each 16-row tile and 32-column step
+// contiguous.  Segments of a multi-part matrix (QKV, gate/up) are tiled one
+// after the other (each a multiple of 16 rows): dst is the segment's first row.
+void launch_tile_rows(const uint16_t* W, int N, int K, uint16_t* dst, hipStream_t s);
+// Column ranges of a wide projection (N rows, K columns): count and width.
+int wide_ranges(int N, int K, int* kr);
+// Partial sums of a wide projection over a.nr ranges (set a.nr, a.kr with
+// wide_ranges); int4 pass only when a.q4[0] is set.
+void launch_wide_proj(WideArgs a, hipStream_t s);
+// Epilogues of a wide projection over the rows of list/cnt: the sum of the
+// ranges, then RoPE and the shared-slot K/V write (QKV, ProjArgs as for
+// EPI_QKV), SwiGLU of rows n and F + n into out [seq][F], or bf16 into out.
+void launch_wide_qkv(const float* y, int nr, size_t cstride, int ystride, const int32_t* list,
+                     const int32_t* cnt, int B, const ProjArgs& qa, hipStream_t s);
+void launch_wide_swiglu(const float* y, int nr, size_t cstride, int ystride, const int32_t* list,
+                        const int32_t* cnt, int B, int F, uint16_t* out, hipStream_t s);
+void launch_wide_bf16(const float* y, int nr, size_t cstride, int ystride, const int32_t* list,
+                      const int32_t* cnt, int B, int N, uint16_t* out, int out_stride, hipStream_t s);
 // Exit decision after layer `layer` for the rows on the backbone: from the exit
 // head's nwg (max, sum exp) partials (DECIDE_HEAD), from the state transition
 // similarity per sequence in sts (DECIDE_STS), or forced exits only, no

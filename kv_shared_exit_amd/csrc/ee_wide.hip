@@ -25,9 +25,11 @@
 // pass.
 #include "ee_internal.h"
 #include "ee_device.h"
+#include "ee_epi.h"
 
 #include <hip/hip_ext.h>
 
+#include <algorithm>
 #include <stdexcept>
 
 namespace ee {
@@ -44,19 +46,47 @@ constexpr int kRing = 8;                  // 32-column steps in flight per tile
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// int4 A operand: 8 codes of a dword (q + 8 in each nibble, elements 2i and
+// 2i+1 in bits 4i and 16+4i) as the bf16 values 136 + q
+__device__ __forceinline__ bf16x8_t unpack8(uint32_t w) {
+  uint4 o;
+  o.x = (w & 0x000F000Fu) | 0x43004300u;
+  o.y = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+  o.z = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
+  o.w = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  return __builtin_bit_cast(bf16x8_t, o);
+}
+
+__device__ __forceinline__ uint32_t pick(const uint4& v, int j) {
+  return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
+// Sum of one staged 16-byte piece (8 bf16 inputs) over the PPG pieces of its
+// scale group (adjacent lanes of the row's 32), stored by the group's first lane
+template <int PPG>
+__device__ __forceinline__ void wide_group_sum(const uint4& v, float* row_sums, int tid) {
+  float t = 0.0f;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t += bf2f(w[i] & 0xffffu) + bf2f(w[i] >> 16);
+#pragma unroll
+  for (int off = 1; off < PPG; off <<= 1) t += __shfl_xor(t, off);
+  if ((tid & (PPG - 1)) == 0) row_sums[(tid & 31) / PPG] = t;
+}
+
 }  // namespace
 
 bool wide_vocab_supported(int d) { return d > 0 && d % kWideCols == 0; }
 
 size_t wide_vocab_elems(int V, int d) { return (size_t)((V + 15) / 16) * 16 * d; }
 
-// Et[((t * nks + k) * 64 + l) * 8 + j] = E[16 t + l % 16][32 k + 8 (l / 16) + j]
-// (zero for rows >= V).  One thread per 16 bytes.
-__global__ void tile_vocab_kernel(const uint16_t* __restrict__ E, int V, int d, uint16_t* __restrict__ Et,
-                                  size_t pieces) {
+// Wt[((t * nks + k) * 64 + l) * 8 + j] = W[16 t + l % 16][32 k + 8 (l / 16) + j]
+// (zero for rows >= N).  One thread per 16 bytes.
+__global__ void tile_rows_kernel(const uint16_t* __restrict__ W, int N, int K, uint16_t* __restrict__ Wt,
+                                 size_t pieces) {
   const size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (g >= pieces) return;
-  const int nks = d / 32;
+  const int nks = K / 32;
   const int lane = (int)(g & 63);
   const size_t blk = g >> 6;
   const int t = (int)(blk / nks);
@@ -64,16 +94,20 @@ __global__ void tile_vocab_kernel(const uint16_t* __restrict__ E, int V, int d, 
   const int row = t * 16 + (lane & 15);
   const int col = k * 32 + (lane >> 4) * 8;
   uint4 v = make_uint4(0, 0, 0, 0);
-  if (row < V) v = *(const uint4*)(E + (size_t)row * d + col);
-  *(uint4*)(Et + g * 8) = v;
+  if (row < N) v = *(const uint4*)(W + (size_t)row * K + col);
+  *(uint4*)(Wt + g * 8) = v;
+}
+
+void launch_tile_rows(const uint16_t* W, int N, int K, uint16_t* dst, hipStream_t s) {
+  if (!wide_vocab_supported(K) || N < 1 || !W || !dst) throw std::logic_error("tiled copy: unsupported shape");
+  const size_t pieces = wide_vocab_elems(N, K) / 8;
+  const int threads = 256;
+  hipLaunchKernelGGL(tile_rows_kernel, dim3((unsigned)((pieces + threads - 1) / threads)), dim3(threads), 0, s, W,
+                     N, K, dst, pieces);
 }
 
 void launch_tile_vocab(const uint16_t* E, int V, int d, uint16_t* Et, hipStream_t s) {
-  if (!wide_vocab_supported(d) || V < 1) throw std::logic_error("tiled vocabulary copy: unsupported shape");
-  const size_t pieces = wide_vocab_elems(V, d) / 8;
-  const int threads = 256;
-  hipLaunchKernelGGL(tile_vocab_kernel, dim3((unsigned)((pieces + threads - 1) / threads)), dim3(threads), 0, s,
-                     E, V, d, Et, pieces);
+  launch_tile_rows(E, V, d, Et, s);
 }
 
 // a.wb[0]: the tiled E; a.N = V; a.K = d; rows: list_bf / cnt_bf (runs only
@@ -274,6 +308,302 @@ void launch_wide_vocab(int epi, const ProjArgs& a0, int nwg, hipStream_t s, hipE
     hipExtLaunchKernelGGL(kern, dim3(g), dim3(kProjThreads), 0, s, nullptr, ev_end, 0, a);
   else
     hipLaunchKernelGGL(kern, dim3(g), dim3(kProjThreads), 0, s, a);
+}
+
+// ---------------------------------------------------------------------------
+// Projections for more than 8 rows (QKV, O, gate/up, down, the head
+// projection T): y[r][seq][n] = sum over the columns of range r of W[n][k]
+// x[seq][k], on matrix cores for up to 64 rows at once, so every weight is
+// read once per launch (River-LLM explainer, section 4: a layer serves its
+// backbone rows with the bf16 weights and its exited rows with the int4 copy;
+// both run in the same launch, the workgroups split between the two).
+//   * A workgroup owns 128 rows (a 16-row tile per wave) and one column range;
+//     the input rows of the range are staged in LDS 256 columns at a time,
+//     double-buffered (as in the vocabulary pass).
+//   * bf16 rows read the tiled copy (8 steps of 1 KB in flight per wave).
+//   * int4 rows: a lane unpacks a dword of codes (8 weights) into the A
+//     operand (nibble | 0x4300 is the bf16 value 136 + q); the 136 * sum(x)
+//     of each scale group is computed once per staged row when the inputs are
+//     staged (not by a second MFMA per wave) and removed before the group's
+//     scale is applied.
+//   * The ranges are summed by the epilogue kernels below (or by the finish
+//     kernel for O and down), in range order.
+// ---------------------------------------------------------------------------
+int wide_ranges(int N, int K, int* kr) {
+  const int nrb = (N + 127) / 128;
+  const int steps = K / kWideCols;
+  int nr = std::max(1, std::min(std::min(8, steps), (512 + nrb - 1) / nrb));
+  const int w = (steps + nr - 1) / nr;
+  if (kr) *kr = w * kWideCols;
+  return (steps + w - 1) / w;
+}
+
+template <int NG>
+__global__ __launch_bounds__(kProjThreads, 4) void wide_proj_kernel(const WideArgs a) {
+  constexpr int G = 128 / NG;   // int4 scale group
+  constexpr int PPG = G / 8;    // 16-byte pieces per group
+  constexpr int SPG = 4 / NG;   // 32-column steps per group
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2 * kWideBuf];
+  __shared__ float xsum[2][kWideRows][2 * NG];  // sum of each staged row over each scale group of the chunk
+  const bool i4 = (int)blockIdx.x >= a.g_bf;
+  const int wg = i4 ? (int)blockIdx.x - a.g_bf : (int)blockIdx.x;
+  const int32_t* list = i4 ? a.list_i4 : a.list_bf;
+  const int n = min(max(*(i4 ? a.cnt_i4 : a.cnt_bf), 0), kWideRows);
+  if (n == 0) return;  // uniform: no rows in this format
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int r = wg % a.nr, rb = wg / a.nr;
+  const int k0 = r * a.kr;
+  const int kw = min(a.kr, a.K - k0);
+  const int nch = kw / kWideCols;
+  const int nbb = (n + 15) >> 4;
+  const int ntiles = a.N >> 4;
+  const int tile = rb * kWideWaves + wave;
+  const int tc = min(tile, ntiles - 1);  // a wave past the last tile computes on it and stores nothing
+
+  const int srow = tid >> 5, scol = (tid & 31) * 8;
+  const uint16_t* sx[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sx[j] = a.x + (size_t)list[min(srow + 16 * j, n - 1)] * a.x_stride + k0 + scol;
+  uint4 s0, s1, s2, s3;
+#define EE_STAGE_LOAD(c)                \
+  do {                                  \
+    const int co_ = (c) * kWideCols;    \
+    s0 = *(const uint4*)(sx[0] + co_);  \
+    s1 = *(const uint4*)(sx[1] + co_);  \
+    s2 = *(const uint4*)(sx[2] + co_);  \
+    s3 = *(const uint4*)(sx[3] + co_);  \
+  } while (0)
+#define EE_STAGE_STORE(buf)                                           \
+  do {                                                                \
+    uint16_t* d_ = xs + (buf) * kWideBuf + srow * kWideStride + scol; \
+    *(uint4*)(d_) = s0;                                               \
+    *(uint4*)(d_ + 16 * kWideStride) = s1;                            \
+    *(uint4*)(d_ + 32 * kWideStride) = s2;                            \
+    *(uint4*)(d_ + 48 * kWideStride) = s3;                            \
+    if (i4) {                                                         \
+      wide_group_sum<PPG>(s0, xsum[buf][srow], tid);                  \
+      wide_group_sum<PPG>(s1, xsum[buf][srow + 16], tid);             \
+      wide_group_sum<PPG>(s2, xsum[buf][srow + 32], tid);             \
+      wide_group_sum<PPG>(s3, xsum[buf][srow + 48], tid);             \
+    }                                                                 \
+  } while (0)
+
+  f32x4_t acc[4];
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) acc[bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  if (!i4) {
+    const int nks = a.K >> 5;
+    const int st0 = k0 >> 5, ns = kw >> 5;  // first step of the range, steps in it
+    const uint16_t* at = a.wt + ((size_t)tc * nks * 64 + lane) * 8;
+    uint4 ra[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ra[i] = ld_stream(at + (size_t)(st0 + min(i, ns - 1)) * 512);
+    EE_STAGE_LOAD(0);
+    EE_STAGE_STORE(0);
+    EE_STAGE_LOAD(min(1, nch - 1));
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+      const uint16_t* xb = xs + (c & 1) * kWideBuf + (lane & 15) * kWideStride + (lane >> 4) * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bf16x8_t aop = as_bf16x8(ra[i]);
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb)
+          if (bb < nbb)
+            acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                aop, as_bf16x8(*(const uint4*)(xb + bb * 16 * kWideStride + i * 32)), acc[bb], 0, 0, 0);
+        ra[i] = ld_stream(at + (size_t)(st0 + min(c * 8 + i + 8, ns - 1)) * 512);  // past the end: reload (unused)
+      }
+      if (c + 1 < nch) EE_STAGE_STORE((c + 1) & 1);
+      __syncthreads();
+      EE_STAGE_LOAD(min(c + 2, nch - 1));
+    }
+  } else {
+    const int seg = tc * 16 >= a.n0 ? 1 : 0;
+    const int ts = tc - (seg ? a.n0 >> 4 : 0);  // tile within its segment
+    const int ngr = a.K / G;
+    const uint32_t* cp = a.q4[seg] + (size_t)(ts * 16 + (lane & 15)) * (a.K >> 3) + (k0 >> 3) + (lane >> 4) * 4;
+    const uint16_t* sp = a.s4[seg] + ((size_t)ts * ngr + k0 / G) * 16 + 4 * (lane >> 4);
+    const int nbk = kw >> 7;  // 128-column blocks of the range
+    uint4 rc[2];
+    uint2 rs[2][NG];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int u = min(i, nbk - 1);
+      rc[i] = ld_stream(cp + u * 16);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) rs[i][g] = *(const uint2*)(sp + (u * NG + g) * 16);
+    }
+    EE_STAGE_LOAD(0);
+    EE_STAGE_STORE(0);
+    EE_STAGE_LOAD(min(1, nch - 1));
+    __syncthreads();
+    f32x4_t cg[4];
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) cg[bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c = 0; c < nch; ++c) {
+      const uint16_t* xb = xs + (c & 1) * kWideBuf + (lane & 15) * kWideStride + (lane >> 4) * 8;
+      const float* xsr = &xsum[c & 1][lane & 15][0];
+#pragma unroll
+      for (int ub = 0; ub < 2; ++ub) {
+        const uint4 cw = rc[ub];
+        uint2 sv[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) sv[g] = rs[ub][g];
+        const int un = min(c * 2 + ub + 2, nbk - 1);  // past the end: reload (unused)
+        rc[ub] = ld_stream(cp + un * 16);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) rs[ub][g] = *(const uint2*)(sp + (un * NG + g) * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8_t aop = unpack8(pick(cw, j));
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb)
+            if (bb < nbb)
+              cg[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  aop, as_bf16x8(*(const uint4*)(xb + bb * 16 * kWideStride + (ub * 4 + j) * 32)), cg[bb], 0, 0, 0);
+          if ((j + 1) % SPG == 0) {  // end of a scale group
+            const int gi = j / SPG;
+            const uint2 sc = sv[gi];
+            const float q0 = bf2f(sc.x & 0xffffu), q1 = bf2f(sc.x >> 16);
+            const float q2 = bf2f(sc.y & 0xffffu), q3 = bf2f(sc.y >> 16);
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+              if (bb < nbb) {
+                const float corr = 136.0f * xsr[bb * 16 * 2 * NG + ub * NG + gi];
+                acc[bb][0] = fmaf(q0, cg[bb][0] - corr, acc[bb][0]);
+                acc[bb][1] = fmaf(q1, cg[bb][1] - corr, acc[bb][1]);
+                acc[bb][2] = fmaf(q2, cg[bb][2] - corr, acc[bb][2]);
+                acc[bb][3] = fmaf(q3, cg[bb][3] - corr, acc[bb][3]);
+              }
+              cg[bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+          }
+        }
+      }
+      if (c + 1 < nch) EE_STAGE_STORE((c + 1) & 1);
+      __syncthreads();
+      EE_STAGE_LOAD(min(c + 2, nch - 1));
+    }
+  }
+#undef EE_STAGE_LOAD
+#undef EE_STAGE_STORE
+
+  // lane l holds rows 16 tile + 4 (l / 16) .. +3 of batch column l % 16 of block bb
+  if (tile < ntiles) {
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) {
+      const int col = bb * 16 + (lane & 15);
+      if (bb < nbb && col < n) {
+        float* dst = a.y + (size_t)r * a.y_cstride + (size_t)list[col] * a.y_stride + tile * 16 + 4 * (lane >> 4);
+        *(float4*)dst = make_float4(acc[bb][0], acc[bb][1], acc[bb][2], acc[bb][3]);
+      }
+    }
+  }
+}
+
+void launch_wide_proj(WideArgs a, hipStream_t s) {
+  if (!a.cnt_bf || !a.list_bf) a.cnt_bf = a.list_bf = no_rows();
+  const bool i4 = a.q4[0] != nullptr;
+  if (!i4 || !a.cnt_i4 || !a.list_i4) a.cnt_i4 = a.list_i4 = no_rows();
+  if (!wide_vocab_supported(a.K) || a.N < 16 || a.N % 16 || !a.wt || !a.x || !a.y || a.nr < 1 ||
+      a.kr % kWideCols || (long long)a.nr * a.kr < a.K || (long long)(a.nr - 1) * a.kr >= a.K)
+    throw std::logic_error("wide projection: unsupported arguments");
+  if (i4 && (a.n0 % 16 || a.n0 <= 0 || !a.s4[0] || (a.n0 < a.N && (!a.q4[1] || !a.s4[1])) ||
+             (a.G != 32 && a.G != 64 && a.G != 128)))
+    throw std::logic_error("wide projection: unsupported int4 arguments");
+  a.nrb = (a.N + 127) / 128;
+  a.g_bf = a.nrb * a.nr;
+  const int g = a.g_bf * (i4 ? 2 : 1);
+  if (!i4 || a.G == 128)
+    hipLaunchKernelGGL(wide_proj_kernel<1>, dim3(g), dim3(kProjThreads), 0, s, a);
+  else if (a.G == 64)
+    hipLaunchKernelGGL(wide_proj_kernel<2>, dim3(g), dim3(kProjThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(wide_proj_kernel<4>, dim3(g), dim3(kProjThreads), 0, s, a);
+}
+
+// ---------------------------------------------------------------------------
+// Epilogues: one thread per (row of the list, output), the ranges summed in
+// order with all loads in flight.
+// ---------------------------------------------------------------------------
+constexpr int kEpiThreads = 256;
+
+__device__ __forceinline__ float wide_sum(const float* y, int nr, size_t cs) {
+  float v[8];
+#pragma unroll
+  for (int r = 0; r < 8; ++r) v[r] = y[(size_t)min(r, nr - 1) * cs];
+  float t = v[0];
+#pragma unroll
+  for (int r = 1; r < 8; ++r)
+    if (r < nr) t += v[r];
+  for (int r = 8; r < nr; ++r) t += y[(size_t)r * cs];
+  return t;
+}
+
+__global__ void wide_qkv_kernel(const float* y, int nr, size_t cs, int ys, const int32_t* list, const int32_t* cnt,
+                                const ProjArgs qa) {
+  const int p = blockIdx.y;
+  if (p >= min(max(*cnt, 0), kMaxBatch)) return;
+  const int nout = (qa.H + 2 * qa.Hkv) * qa.hd;
+  const int nn = blockIdx.x * kEpiThreads + threadIdx.x;
+  if (nn >= nout) return;
+  const int seq = list[p];
+  const int half = qa.hd >> 1;
+  const int e = nn & (qa.hd - 1);
+  const int partner = e < half ? nn + half : nn - half;
+  const float* yr = y + (size_t)seq * ys;
+  qkv_out(qa, seq, nn, wide_sum(yr + nn, nr, cs), wide_sum(yr + partner, nr, cs));
+}
+
+__global__ void wide_swiglu_kernel(const float* y, int nr, size_t cs, int ys, const int32_t* list, const int32_t* cnt,
+                                   int F, uint16_t* out) {
+  const int p = blockIdx.y;
+  if (p >= min(max(*cnt, 0), kMaxBatch)) return;
+  const int nn = blockIdx.x * kEpiThreads + threadIdx.x;
+  if (nn >= F) return;
+  const int seq = list[p];
+  const float* yr = y + (size_t)seq * ys;
+  out[(size_t)seq * F + nn] = (uint16_t)f2bf(silu_mul(wide_sum(yr + nn, nr, cs), wide_sum(yr + F + nn, nr, cs)));
+}
+
+__global__ void wide_bf16_kernel(const float* y, int nr, size_t cs, int ys, const int32_t* list, const int32_t* cnt,
+                                 int N, uint16_t* out, int out_stride) {
+  const int p = blockIdx.y;
+  if (p >= min(max(*cnt, 0), kMaxBatch)) return;
+  const int nn = blockIdx.x * kEpiThreads + threadIdx.x;
+  if (nn >= N) return;
+  const int seq = list[p];
+  out[(size_t)seq * out_stride + nn] = (uint16_t)f2bf(wide_sum(y + (size_t)seq * ys + nn, nr, cs));
+}
+
+void launch_wide_qkv(const float* y, int nr, size_t cstride, int ystride, const int32_t* list, const int32_t* cnt,
+                     int B, const ProjArgs& qa, hipStream_t s) {
+  const int nout = (qa.H + 2 * qa.Hkv) * qa.hd;
+  if (!y || !list || !cnt || nr < 1 || B < 1 || B > kMaxBatch || ystride < nout || qa.hd < 2 ||
+      (qa.hd & (qa.hd - 1)))
+    throw std::logic_error("wide QKV epilogue: bad arguments");
+  hipLaunchKernelGGL(wide_qkv_kernel, dim3((nout + kEpiThreads - 1) / kEpiThreads, B), dim3(kEpiThreads), 0, s, y,
+                     nr, cstride, ystride, list, cnt, qa);
+}
+
+void launch_wide_swiglu(const float* y, int nr, size_t cstride, int ystride, const int32_t* list, const int32_t* cnt,
+                        int B, int F, uint16_t* out, hipStream_t s) {
+  if (!y || !list || !cnt || !out || nr < 1 || B < 1 || B > kMaxBatch || ystride < 2 * F)
+    throw std::logic_error("wide SwiGLU epilogue: bad arguments");
+  hipLaunchKernelGGL(wide_swiglu_kernel, dim3((F + kEpiThreads - 1) / kEpiThreads, B), dim3(kEpiThreads), 0, s, y,
+                     nr, cstride, ystride, list, cnt, F, out);
+}
+
+void launch_wide_bf16(const float* y, int nr, size_t cstride, int ystride, const int32_t* list, const int32_t* cnt,
+                      int B, int N, uint16_t* out, int out_stride, hipStream_t s) {
+  if (!y || !list || !cnt || !out || nr < 1 || B < 1 || B > kMaxBatch || ystride < N || out_stride < N)
+    throw std::logic_error("wide bf16 epilogue: bad arguments");
+  hipLaunchKernelGGL(wide_bf16_kernel, dim3((N + kEpiThreads - 1) / kEpiThreads, B), dim3(kEpiThreads), 0, s, y, nr,
+                     cstride, ystride, list, cnt, N, out, out_stride);
 }
 
 }  // namespace ee

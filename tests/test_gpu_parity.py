@@ -274,15 +274,19 @@ def test_largest_batch(gpu):
     ("wide-hd64", SHAPES["hd64"], 24),
     # a vocabulary that ends inside a 16-row tile (1003), 3 batch blocks
     ("wide-odd-vocab", ModelShape(3, 256, 4, 2, 64, 512, 1003, 32, rope_theta=500000.0), 40),
-    # every row of the largest batch (4 blocks of 16)
+    # every row of the largest batch (4 blocks of 16); F = 384 is not a multiple
+    # of 256, so the projections keep the 8-row passes (vocabulary pass only)
     ("wide-b64", ModelShape(2, 256, 4, 2, 64, 384, 700, 32, rope_theta=10000.0), 64),
+    # group 128, head_dim 128, one batch block plus one row
+    ("wide-g128", ModelShape(3, 512, 4, 2, 128, 768, 500, 128, rope_theta=500000.0), 17),
 ])
 def test_wide_batch_vocabulary_pass(gpu, label, sh, batch):
-    """Batches of more than 8 rows: the exit head's vocabulary pass and the LM
-    head run on the matrix-core pass over the tiled copy of E whenever more than
-    8 rows are on the backbone (the final LM head always, since every row takes
-    it), and on the vector-ALU pass otherwise; exits are spread so that layers
-    see both."""
+    """Batches of more than 8 rows: the projections run on the matrix-core pass
+    (both weight formats, column ranges summed by the epilogues) when the widths
+    are multiples of 256; the exit head's vocabulary pass and the LM head run on
+    the matrix-core pass over the tiled copy of E whenever more than 8 rows are
+    on the backbone (the final LM head always, since every row takes it), and on
+    the vector-ALU pass otherwise; exits are spread so that layers see both."""
     from parity import run_parity
     wl = Workload(label, sh, 1, 6, 4, 0.75, "calibrated", max(1.2, sh.n_layers / 2), index=9)
     cal = calibrate(wl, verbose=False)
