@@ -28,16 +28,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 
 # HBM traffic of one exit-head launch with rows on the backbone (8B shape, 8
 # staged rows), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of
 # kv_shared_exit_amd/ee_probe (profiles/exit_head_lse_8b_traffic.md), each
 # scaled by what the same counter reads for a 1 GiB device copy.  Valid only
 # for the kernel sources it was measured on (their sha256); otherwise null.
-TRAFFIC = {"workload": "8b", "fetch_kib": 513404.6354, "write_kib": 64.0,
-           "fetch_scale": 1.9999340, "write_scale": 1.0,
-           "sources_sha256": "ecc91d042734f9c3c41a1e944dc9be00b9a55956f7639a78b5962c2d1cd69f16"}
-KERNEL_SOURCES = ("ee_proj.hip", "ee_device.h", "ee_internal.h")
+TRAFFIC = {"workload": "8b", "fetch_kib": 513407.1146, "write_kib": 64.0,
+           "fetch_scale": 1.9999328, "write_scale": 1.0,
+           "sources_sha256": "5d501ea503dc16ae418b2fa8cacc42ac44d58418e09c3e686b7ff94d7c7817c0"}
+KERNEL_SOURCES = ("ee_proj.hip", "ee_device.h", "ee_internal.h", "ee_epi.h")
 
 
 def log(msg):
@@ -288,11 +289,13 @@ def main():
     # roofline figure is the launches' algorithmic bytes over their summed
     # duration (= mean bytes per launch / mean launch time).
     head_bytes_total = 0
+    head_flops_total = 0
     for s_ in range(K):
         for l in range(every, sh.n_layers, every):
             a_rows = int((exits[s_] >= l).sum())
             if a_rows:
                 head_bytes_total += 2 * sh.vocab * sh.d_model + 2 * sh.d_model * a_rows
+                head_flops_total += 2 * sh.vocab * sh.d_model * a_rows
     avg_ms = head_ms / max(n_launch, 1)
     head_bytes = head_bytes_total / n_launch if n_launch else 0.0
     achieved = head_bytes_total / (head_ms * 1e-3) / 1e9 if n_launch else 0.0
@@ -347,6 +350,14 @@ def main():
     }
     if wl.name != "8b":
         out["metric"] = out["metric"].replace("(8B shape, b=8)", f"({wl.name} shape, b={B})")
+    if B > 8 and n_launch:
+        # more than 8 rows run the exit head's vocabulary GEMV on matrix cores
+        # (bf16 MFMA): its algorithmic flops (2 V d per row on the backbone)
+        # over the same launch times as the roofline
+        tf = head_flops_total / (head_ms * 1e-3) / 1e12
+        out["mfma"] = {"kernel": "wide exit-head vocabulary pass (wide_vocab_kernel<3>)", "dtype": "bf16",
+                       "achieved": round(tf, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                       "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
     if wl.policy == "forced":
         out["config"]["workload"] += (f", exit layers forced uniform in [{wl.forced_lo}, {wl.forced_hi}] "
                                       f"per sequence and step (heads computed)")
