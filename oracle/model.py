@@ -69,6 +69,7 @@ import numpy as np
 
 from .numerics import bf16_round, from_bf16_bits, f32_round
 from .quant import quantize_int4, dequantize_int4
+from .sampling import sample_token
 
 LINEAR = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 
@@ -301,7 +302,7 @@ def final_head(model: OracleModel, h: np.ndarray):
 # ----------------------------------------------------------------------------
 def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=None,
                 trace: bool = False, heads: bool = True, criterion: str = "head", check_every: int = 1,
-                exit_rule: str = "sequence"):
+                exit_rule: str = "sequence", temperature: float = 0.0, seed: int = 0):
     """One decode step for sequences 0..B-1 of ``cache`` (B = len(tokens)).
 
     ``gamma``: per-layer thresholds gamma_1..gamma_{L-1} (scalar broadcasts);
@@ -319,6 +320,11 @@ def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=N
     forced exits apply after any layer.  ``exit_rule``: "sequence" (each
     sequence decides for itself) or "batch_min" (the unforced sequences on the
     backbone exit together when the smallest of their values > the threshold).
+    ``temperature`` > 0: sampled decoding with AdaDecode's verification
+    (``oracle.sampling.sample_token``; the draft comes from the exit head's
+    logits at the exit layer; needs the exit-head criterion checked after every
+    layer); ``seed`` keys its counter-based generator.  info["sample"] then
+    holds each row's decisions and their margins.
     """
     if criterion not in ("head", "sts"):
         raise ValueError(f"unknown criterion {criterion!r}")
@@ -326,6 +332,9 @@ def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=N
         raise ValueError(f"unknown exit rule {exit_rule!r}")
     if check_every < 1:
         raise ValueError("check_every must be >= 1")
+    sampled = temperature > 0
+    if sampled and (criterion != "head" or check_every != 1):
+        raise ValueError("sampled decoding drafts from the exit head checked after every layer")
     sh = model.shape
     L = sh.n_layers
     tokens = np.asarray(tokens, dtype=np.int64)
@@ -342,6 +351,7 @@ def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=N
     p_rec = np.full((B, L - 1), np.nan)
     head_max = np.full((B, L - 1), np.nan)
     hidden = [h.copy()] if trace else None
+    exit_logits = {}   # sampled decoding: the exit head's logits of each row at its exit layer
     for l in range(1, L + 1):
         bb = np.nonzero(~exited)[0]
         ex = np.nonzero(exited)[0]
@@ -352,6 +362,7 @@ def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=N
         if len(ex):
             _layer_rows(model, cache, l, ex, h, pos, use_exit=True)
         if decide:
+            hl = None
             if criterion == "head":
                 p, hl = exit_head(model, l, h[bb])
                 head_max[bb, l - 1] = np.abs(hl).max(axis=-1)
@@ -370,6 +381,8 @@ def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=N
                 if go:
                     exited[b] = True
                     e[b] = l
+                    if sampled:
+                        exit_logits[b] = hl[i]
         elif heads and l < L:   # not a check layer: only forced exits
             for b in bb:
                 if forced[b] == l:
@@ -378,8 +391,14 @@ def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=N
         if trace:
             hidden.append(h.copy())
     tok, gap, logits = final_head(model, h)
-    cache.lens[:B] += 1
     info = {"p": p_rec, "head_absmax": head_max, "gap": gap, "logits": logits}
+    if sampled:
+        info["sample"] = []
+        for b in range(B):
+            t, si = sample_token(logits[b], exit_logits.get(b), temperature, seed, int(pos[b]), b)
+            tok[b] = t
+            info["sample"].append(si)
+    cache.lens[:B] += 1
     if trace:
         info["hidden"] = np.stack(hidden, axis=1)
     return tok, e, info
@@ -443,7 +462,8 @@ def prefill(model: OracleModel, cache: KVCache, prompts, trace: bool = False):
 
 
 def generate(model: OracleModel, cache: KVCache, prompts, steps: int, gamma=None,
-             forced_fn=None, criterion: str = "head", check_every: int = 1, exit_rule: str = "sequence"):
+             forced_fn=None, criterion: str = "head", check_every: int = 1, exit_rule: str = "sequence",
+             temperature: float = 0.0, seed: int = 0):
     """Prefill, then ``steps`` decode steps feeding back each greedy token.
 
     ``forced_fn(step)`` may return a forced-exit array for a step.  Returns
@@ -454,7 +474,7 @@ def generate(model: OracleModel, cache: KVCache, prompts, steps: int, gamma=None
     for s in range(steps):
         f = forced_fn(s) if forced_fn is not None else None
         tok, e, _ = decode_step(model, cache, tok, gamma=gamma, forced=f, criterion=criterion,
-                                check_every=check_every, exit_rule=exit_rule)
+                                check_every=check_every, exit_rule=exit_rule, temperature=temperature, seed=seed)
         toks.append(tok)
         exits.append(e)
     return np.stack(toks, axis=1), (np.stack(exits, axis=1) if exits else
