@@ -123,6 +123,20 @@ typedef struct ee_model_config {
                           (CALM explainer: check every N layers); 0 or 1: every layer.
                           A forced exit applies after any layer. */
   int32_t exit_rule;   /* EE_RULE_SEQUENCE or EE_RULE_BATCH_MIN */
+  float temperature;   /* 0: greedy decoding.  > 0: sampled decoding with AdaDecode's
+                          verification (AdaDecode explainer, section 3.1): a sequence that
+                          exits at layer l drafts a token from softmax(exit-head logits / T)
+                          there; after the remaining layers the draft is accepted with
+                          probability min(1, p_final / p_draft) (p_final = softmax(final
+                          logits / T)), otherwise the token is drawn from the normalised
+                          relu(p_final - p_draft); a sequence that runs every layer draws
+                          from p_final.  Draws: Gumbel-max over Philox4x64-10 noise with key
+                          (sample_seed, 0) and counter (v / 4, sequence, position, stream)
+                          (streams: 1 draft, 2 final, 3 resample, 4 acceptance uniform, word
+                          0 of block 0); u = ((x >> 41) + 0.5) / 2^23.  Needs EE_CRIT_HEAD,
+                          check_every <= 1, exit copies (not EE_EXIT_NONE) and max_batch
+                          <= 8 (else EE_ERR_UNSUPPORTED).  The prefill's token stays greedy. */
+  uint32_t sample_seed;
 } ee_model_config;
 
 /* Device pointers of one layer.  Shapes: attn_norm, ffn_norm [d]; wq [H*hd, d];

@@ -52,7 +52,7 @@ class ModelConfig(C.Structure):
                 ("vocab", C.c_int32), ("group_size", C.c_int32), ("rms_eps", C.c_float),
                 ("rope_theta", C.c_float), ("exit_mode", C.c_int32), ("max_batch", C.c_int32),
                 ("max_positions", C.c_int32), ("criterion", C.c_int32), ("check_every", C.c_int32),
-                ("exit_rule", C.c_int32)]
+                ("exit_rule", C.c_int32), ("temperature", C.c_float), ("sample_seed", C.c_uint32)]
 
 
 class LayerWeights(C.Structure):

@@ -43,14 +43,16 @@ class Model:
 
     def __init__(self, shape, dev_weights: dict, gamma=None, exit_mode: int = B.EE_EXIT_INT4,
                  max_batch: int = 8, max_positions: int = 4096, criterion: int = B.EE_CRIT_HEAD,
-                 check_every: int = 1, exit_rule: int = B.EE_RULE_SEQUENCE):
+                 check_every: int = 1, exit_rule: int = B.EE_RULE_SEQUENCE, temperature: float = 0.0,
+                 sample_seed: int = 0):
         self.lib = B.load()
         self.shape = shape
         self.w = dev_weights
         L = shape.n_layers
         cfg = B.ModelConfig(L, shape.d_model, shape.n_heads, shape.n_kv_heads, shape.head_dim,
                             shape.d_ff, shape.vocab, shape.group, shape.rms_eps, shape.rope_theta,
-                            exit_mode, max_batch, max_positions, criterion, check_every, exit_rule)
+                            exit_mode, max_batch, max_positions, criterion, check_every, exit_rule,
+                            float(temperature), int(sample_seed))
         layers = (B.LayerWeights * L)()
         for i, lw in enumerate(dev_weights["layers"]):
             for name in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down"):

@@ -77,6 +77,7 @@ struct ee_model {
   uint16_t *qrot = nullptr, *attn_o = nullptr;
   uint16_t *act = nullptr, *z = nullptr;
   float* head_part = nullptr;
+  float* part_s = nullptr;  // sampled decoding: partials by sequence [kNwg][64][kPartS]
   uint16_t* lm_head_t = nullptr;  // E in the wide vocabulary pass's tiled order (max_batch > 8), else null
   // projections for more than 8 rows on matrix cores: each layer's bf16
   // weights in the tiled order (QKV, O, gate then up, down, the head's T)
@@ -199,6 +200,12 @@ void validate_config(const ee_model_config& c) {
   need(c.criterion == EE_CRIT_HEAD || c.criterion == EE_CRIT_STS, "bad criterion");
   need(c.check_every >= 0, "check_every must be >= 0");
   need(c.exit_rule == EE_RULE_SEQUENCE || c.exit_rule == EE_RULE_BATCH_MIN, "bad exit_rule");
+  need(std::isfinite(c.temperature) && c.temperature >= 0.0f, "temperature must be finite and >= 0");
+  if (c.temperature > 0.0f) {
+    need(c.exit_mode != EE_EXIT_NONE && c.criterion == EE_CRIT_HEAD && c.check_every <= 1,
+         "sampled decoding drafts from the exit head evaluated after every layer");
+    if (c.max_batch > 8) fail(EE_ERR_UNSUPPORTED, "sampled decoding supports max_batch <= 8");
+  }
   need(std::isfinite(c.rms_eps) && c.rms_eps > 0 && std::isfinite(c.rope_theta) && c.rope_theta > 0,
        "rms_eps and rope_theta must be positive");
   shape(c.group_size == 32 || c.group_size == 64 || c.group_size == 128, "group_size must be 32, 64 or 128");
@@ -284,6 +291,16 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
   heads = heads && cf.exit_mode != EE_EXIT_NONE;  // the plain decoder evaluates no criterion
   const bool sts_crit = cf.criterion == EE_CRIT_STS;
   const int every = std::max(1, cf.check_every);
+  // sampled decoding (decode steps only; the prefill's token stays greedy)
+  const bool sampled = heads && cf.temperature > 0.0f;
+  const float itau = sampled ? 1.0f / cf.temperature : 0.0f;
+  auto sampled_args = [&](ProjArgs& a) {
+    a.part_s = m->part_s;
+    a.itau = itau;
+    a.seed = cf.sample_seed;
+    a.lens = c->lens;
+    a.st = st;
+  };
 
   const size_t pstride = (size_t)kMaxBatch * d;  // elements between partial-sum ranges
   launch_init(st, prompt, P, t, B, L, m->tok_emb, d, cf.vocab, m->h, m->p_rec,
@@ -535,14 +552,20 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
         // more than 8 rows go to the wide pass (one read of E for all rows);
         // the row count is on the device, so both are launched and one returns
         const bool wide = m->lm_head_t && B > 8;
-        if (wide) a.max_rows = 8;
-        launch_proj(EPI_LSE, a, kNwg, B, s, e0, wide ? nullptr : e1);
-        if (wide) {
-          a.wb[0] = m->lm_head_t;
-          launch_wide_vocab(EPI_LSE, a, kNwg, s, e1);
+        if (sampled) {  // also the draft's Gumbel-max and the tau statistics
+          sampled_args(a);
+          launch_proj(EPI_LSE_S, a, kNwg, B, s, e0, e1);
+        } else {
+          if (wide) a.max_rows = 8;
+          launch_proj(EPI_LSE, a, kNwg, B, s, e0, wide ? nullptr : e1);
+          if (wide) {
+            a.wb[0] = m->lm_head_t;
+            launch_wide_vocab(EPI_LSE, a, kNwg, s, e1);
+          }
         }
       }
       launch_decide(DECIDE_HEAD, bmin, st, m->head_part, kNwg, m->d_gamma, l, L, B, m->p_rec, nullptr, s);
+      if (sampled) launch_sample_draft(st, m->part_s, kNwg, l, B, m->z, m->xn + (size_t)kMaxBatch * d, d, s);
     }
     if (dbg.hidden)
       HIPCHK(hipMemcpy2DAsync(m->dbg_hidden + (size_t)l * d, (size_t)(L + 1) * d * 4, m->h,
@@ -560,13 +583,34 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
     a.part = m->head_part;
     a.logits = dbg.logits ? m->dbg_logits : nullptr;
     a.logits_stride = cf.vocab;
-    if (m->lm_head_t && B > 8) {  // every row of the batch: the wide pass alone
-      a.wb[0] = m->lm_head_t;
-      launch_wide_vocab(EPI_ARGMAX, a, kNwg, s);
+    if (sampled) {
+      // the final distribution's statistics and draw, the greedy top-2 (gap),
+      // the verification, then the resampling of the rejected drafts
+      sampled_args(a);
+      launch_proj(EPI_ARGMAX_S, a, kNwg, B, s);
+      launch_final(st, m->head_part, kNwg, B, cf.vocab, c->lens, 0, s);
+      launch_sample_final(st, m->part_s, kNwg, B, L, cf.vocab, c->lens, itau, cf.sample_seed, s);
+      ProjArgs r = base_args(m);
+      r.N = cf.vocab;
+      r.K = d;
+      set_seg1(r, m->lm_head, cf.vocab);
+      r.list_bf = st->rej;  // pairs (b, 64 + b): the final input and the exit layer's z
+      r.cnt_bf = &st->n_rej;
+      r.x = m->xn;
+      r.x_stride = d;
+      r.part = m->head_part;
+      sampled_args(r);
+      launch_proj(EPI_RESAMPLE, r, kNwg, 2 * B, s);
+      launch_resample_final(st, m->part_s, kNwg, B, cf.vocab, c->lens, s);
     } else {
-      launch_proj(EPI_ARGMAX, a, kNwg, B, s);
+      if (m->lm_head_t && B > 8) {  // every row of the batch: the wide pass alone
+        a.wb[0] = m->lm_head_t;
+        launch_wide_vocab(EPI_ARGMAX, a, kNwg, s);
+      } else {
+        launch_proj(EPI_ARGMAX, a, kNwg, B, s);
+      }
+      launch_final(st, m->head_part, kNwg, B, cf.vocab, c->lens, 1, s);
     }
-    launch_final(st, m->head_part, kNwg, B, cf.vocab, c->lens, 1, s);
   } else {
     launch_advance(c->lens, B, s);
   }
@@ -774,13 +818,15 @@ ee_status ee_create_model(const ee_model_config* cfg, const ee_weights* w, const
       if (m->wide)
         m->nkc_max = std::max(m->nkc_max, std::max(wide_ranges(d, qd, nullptr), wide_ranges(d, F, nullptr)));
       m->parts = m->alloc<float>((size_t)m->nkc_max * Bm * d);
-      m->xn = m->alloc<uint16_t>((size_t)Bm * d);
+      // rows 64.. hold each sequence's z at its exit layer (sampled decoding)
+      m->xn = m->alloc<uint16_t>((size_t)2 * Bm * d);
       m->hb = m->alloc<uint16_t>((size_t)Bm * d);
       m->qrot = m->alloc<uint16_t>((size_t)Bm * qd);
       m->attn_o = m->alloc<uint16_t>((size_t)Bm * qd);
       m->act = m->alloc<uint16_t>((size_t)Bm * F);
       m->z = m->alloc<uint16_t>((size_t)Bm * d);
       m->head_part = m->alloc<float>((size_t)kNwg * kMaxBatch * 4);
+      if (c.temperature > 0.0f) m->part_s = m->alloc<float>((size_t)kNwg * kMaxBatch * kPartS);
       m->h2 = m->alloc<float>((size_t)Bm * d);
       m->sts = m->alloc<float>(kMaxBatch);
       // the most partials any cache (S <= max_positions, B >= 1) can need: the

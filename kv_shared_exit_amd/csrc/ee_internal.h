@@ -15,7 +15,19 @@ constexpr int kNwgMax = 512;       // projection grid cap (size of the per-workg
 // (summed into the residual by the finish kernel); SwiGLU; the exit head's
 // (max, sum exp) per workgroup; the LM head's top-2 per workgroup; RoPE and the
 // shared-slot K/V write.
-enum Epi { EPI_BF16 = 0, EPI_PART = 1, EPI_SWIGLU = 2, EPI_LSE = 3, EPI_ARGMAX = 4, EPI_QKV = 5 };
+// Sampled decoding (AdaDecode's verification) adds: the exit head's pass with
+// the draft's Gumbel-max and the temperature's (max, sum exp) (EPI_LSE_S), the
+// LM head's pass with the final distribution's statistics (EPI_ARGMAX_S), and
+// the resampling pass over relu(p_final - p_draft) (EPI_RESAMPLE).
+enum Epi {
+  EPI_BF16 = 0, EPI_PART = 1, EPI_SWIGLU = 2, EPI_LSE = 3, EPI_ARGMAX = 4, EPI_QKV = 5,
+  EPI_LSE_S = 6, EPI_ARGMAX_S = 7, EPI_RESAMPLE = 8
+};
+
+// Streams of the counter-based draws (the counter is (v / 4, sequence,
+// position, stream)); the same numbering as the oracle's.
+enum SampleStream { STREAM_DRAFT = 1, STREAM_FINAL = 2, STREAM_RESAMPLE = 3, STREAM_ACCEPT = 4 };
+constexpr int kPartS = 8;  // floats per (workgroup, sequence) of the sampled partials
 
 // Device-resident state of one step.  Every value that changes from step to
 // step lives here, so a captured graph replays unchanged.
@@ -30,6 +42,16 @@ struct StepState {
   int32_t n_act, n_ex, n_all, pad;
   int32_t out_tok[kMaxBatch];
   float gap[kMaxBatch];
+  // sampled decoding: the draft of each sequence that exited (token, its exit
+  // logit, log sum exp of the exit logits / tau; draft_tok -1: no draft), the
+  // final distribution's log sum exp, and the rejected sequences as (b, 64 + b)
+  // row pairs for the resampling pass
+  int32_t draft_tok[kMaxBatch];
+  float draft_logit[kMaxBatch];
+  float draft_lse[kMaxBatch];
+  float lse_f[kMaxBatch];
+  int32_t rej[kMaxBatch];
+  int32_t n_rej, pad2;
 };
 
 struct ProjArgs {
@@ -62,6 +84,12 @@ struct ProjArgs {
   int nwg_r;                                      // workgroups per column range (set by launch_proj)
   int max_rows;                                   // EPI_LSE / EPI_ARGMAX: do nothing above this many rows
                                                   // (the wide pass has them); 0 = no limit
+  // sampled epilogues: 1 / temperature, the generator's seed, partials by
+  // sequence [nwg][kMaxBatch][kPartS], and the step state
+  float itau;
+  uint32_t seed;
+  float* part_s;
+  const StepState* st;
 };
 
 // A projection for more than 8 rows on matrix cores (ee_wide.hip): float32
@@ -161,6 +189,19 @@ void launch_decide(int mode, bool batch_min, StepState* st, const float* part, i
                    int layer, int L, int B, float* p_rec, const float* sts, hipStream_t s);
 void launch_final(StepState* st, const float* part, int nwg, int B, int V, int32_t* lens, int advance,
                   hipStream_t s);
+// Sampled decoding (ee_sample.hip).  After the decision at an exit-head layer:
+// the draft of every sequence that exited at this layer (merged from the
+// EPI_LSE_S partials) and its z row copied to zx [b][d].  After the LM head's
+// EPI_ARGMAX_S pass: the emitted token of each sequence (the final
+// distribution's draw without a draft; the draft if accepted) and the list of
+// rejected ones.  After the EPI_RESAMPLE pass: their tokens; then every
+// length advances.
+void launch_sample_draft(StepState* st, const float* part_s, int nwg, int layer, int B, const uint16_t* z,
+                         uint16_t* zx, int d, hipStream_t s);
+void launch_sample_final(StepState* st, const float* part_s, int nwg, int B, int L, int V, const int32_t* lens,
+                         float itau, uint32_t seed, hipStream_t s);
+void launch_resample_final(StepState* st, const float* part_s, int nwg, int B, int V, int32_t* lens,
+                           hipStream_t s);
 void launch_advance(int32_t* lens, int B, hipStream_t s);
 void launch_quantize(const uint16_t* w, int N, int K, int G, int row0, uint32_t* codes,
                      uint16_t* scales, hipStream_t s);

@@ -82,6 +82,7 @@ __global__ __launch_bounds__(kInitThreads) void init_kernel(StepState* st, const
       st->e[i] = L;
       st->act[i] = i;
       st->all[i] = i;
+      st->draft_tok[i] = -1;
     }
     if (tid == 0) {
       st->n_act = B;

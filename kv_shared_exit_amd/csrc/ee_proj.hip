@@ -30,6 +30,7 @@
 #include "ee_internal.h"
 #include "ee_device.h"
 #include "ee_epi.h"
+#include "ee_rng.h"
 
 #include <hip/hip_ext.h>
 
@@ -53,6 +54,11 @@ template <int EPI>
 struct Ep {
   static constexpr int P = EPI == EPI_SWIGLU ? 2 : 1;  // matrices per tile
   static constexpr int R = EPI == EPI_SWIGLU ? 1 : 2;  // bf16 rows per wave tile
+  // the vocabulary passes (one partial per workgroup and row)
+  static constexpr bool VOCAB = EPI == EPI_LSE || EPI == EPI_ARGMAX || EPI == EPI_LSE_S || EPI == EPI_ARGMAX_S ||
+                                EPI == EPI_RESAMPLE;
+  static constexpr bool SAMPLED = EPI == EPI_LSE_S || EPI == EPI_ARGMAX_S || EPI == EPI_RESAMPLE;
+  static constexpr int RW = SAMPLED ? 8 : 4;  // floats per lane in the cross-wave reduction
 };
 
 // The share of a launch one workgroup works on: its column range and its
@@ -199,6 +205,11 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, const Work& wk, int
 
   float lm = -INFINITY, ls = 0.0f;
   Top2 tp{-INFINITY, 0x7fffffff, -INFINITY};
+  // sampled passes: (max, sum exp) of logit / tau, the best Gumbel-perturbed
+  // score with its index, and one logit (the draft's, or the final logit at
+  // the draft's index)
+  float lmt = -INFINITY, lst = 0.0f, pb = -INFINITY, pl = -INFINITY;
+  int pi = 0x7fffffff;
 
   stage_rows(list, c0, nb, seq);
   // request the first tile's first weights before the inputs are staged
@@ -273,6 +284,54 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, const Work& wk, int
         ((uint16_t*)a.y)[(size_t)seq[bsel] * a.y_stride + n] = (uint16_t)f2bf(silu_mul(v, u));
     } else if constexpr (EPI == EPI_LSE) {
       if (lane_ok && n < N) lse_merge(lm, ls, v, 1.0f);
+    } else if constexpr (EPI == EPI_LSE_S) {
+      if (lane_ok && n < N) {
+        const int sq = seq[bsel];
+        lse_merge(lm, ls, v, 1.0f);
+        const float sv = v * a.itau;
+        lse_merge(lmt, lst, sv, 1.0f);
+        const float sc = sv + gumbel_noise(a.seed, a.lens[sq], sq, STREAM_DRAFT, n);
+        if (sc > pb) {  // rows ascend per lane: the lowest index wins ties
+          pb = sc;
+          pi = n;
+          pl = v;
+        }
+      }
+    } else if constexpr (EPI == EPI_ARGMAX_S) {
+      if (lane_ok && n < N) {
+        const int sq = seq[bsel];
+        if (a.logits) a.logits[(size_t)sq * a.logits_stride + n] = v;
+        if (v > tp.v1) {
+          tp.v2 = tp.v1;
+          tp.v1 = v;
+          tp.i1 = n;
+        } else if (v > tp.v2) {
+          tp.v2 = v;
+        }
+        const float sv = v * a.itau;
+        lse_merge(lmt, lst, sv, 1.0f);
+        const float sc = sv + gumbel_noise(a.seed, a.lens[sq], sq, STREAM_FINAL, n);
+        if (sc > pb) {
+          pb = sc;
+          pi = n;
+        }
+        if (n == a.st->draft_tok[sq]) pl = v;
+      }
+    } else if constexpr (EPI == EPI_RESAMPLE) {
+      // rows come in pairs (final input of sequence b, its exit layer's z at
+      // row 64 + b): the pair's two values sit in lanes l and l ^ (V / 2)
+      const float u = __shfl_xor(v, V / 2);
+      if (lane_ok && (bsel & 1) == 0 && n < N) {
+        const int sq = seq[bsel];
+        const float r = __expf(v * a.itau - a.st->lse_f[sq]) - __expf(u * a.itau - a.st->draft_lse[sq]);
+        if (r > 0.0f) {
+          const float sc = __logf(r) + gumbel_noise(a.seed, a.lens[sq], sq, STREAM_RESAMPLE, n);
+          if (sc > pb) {
+            pb = sc;
+            pi = n;
+          }
+        }
+      }
     } else if constexpr (EPI == EPI_ARGMAX) {
       if (lane_ok && n < N) {
         if (a.logits) a.logits[(size_t)seq[bsel] * a.logits_stride + n] = v;
@@ -289,6 +348,63 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, const Work& wk, int
     }
   }
 
+  if constexpr (Ep<EPI>::SAMPLED) {
+    float* rw = red + (wave * 64 + lane) * 8;
+    rw[0] = lm;
+    rw[1] = ls;
+    rw[2] = tp.v1;
+    rw[3] = __int_as_float(tp.i1);
+    rw[4] = tp.v2;
+    rw[5] = lmt;
+    rw[6] = lst;
+    rw[7] = pl;
+    float* rp = red + kWaves * 64 * 8 + (wave * 64 + lane) * 2;  // the perturbed best and its index
+    rp[0] = pb;
+    rp[1] = __int_as_float(pi);
+    __syncthreads();
+    const int tid = threadIdx.x;
+    if (tid < nb && (EPI != EPI_RESAMPLE || (tid & 1) == 0)) {
+      float m = -INFINITY, sm = 0.0f, mt = -INFINITY, st = 0.0f, lg = -INFINITY, best = -INFINITY;
+      int bi = 0x7fffffff;
+      Top2 g2{-INFINITY, 0x7fffffff, -INFINITY};
+      for (int ww = 0; ww < kWaves; ++ww)
+        for (int l = 0; l < V; ++l)
+          if (xidx<V>(l) % NB == tid) {
+            const float* src = red + (ww * 64 + l) * 8;
+            const float* sp = red + kWaves * 64 * 8 + (ww * 64 + l) * 2;
+            lse_merge(m, sm, src[0], src[1]);
+            top2_merge(g2, Top2{src[2], __float_as_int(src[3]), src[4]});
+            lse_merge(mt, st, src[5], src[6]);
+            lg = fmaxf(lg, src[7]);
+            const int si = __float_as_int(sp[1]);
+            if (sp[0] > best || (sp[0] == best && si < bi)) {
+              best = sp[0];
+              bi = si;
+            }
+          }
+      // by list position (what decide and final merge), and by sequence
+      float* out = a.part + ((size_t)blockIdx.x * kMaxBatch + (c0 + tid)) * 4;
+      float* os = a.part_s + ((size_t)blockIdx.x * kMaxBatch + seq[tid]) * kPartS;
+      if constexpr (EPI == EPI_LSE_S) {
+        out[0] = m;
+        out[1] = sm;
+      } else if constexpr (EPI == EPI_ARGMAX_S) {
+        out[0] = g2.v1;
+        out[1] = __int_as_float(g2.i1);
+        out[2] = g2.v2;
+      }
+      if constexpr (EPI == EPI_RESAMPLE) {
+        os[0] = best;
+        os[1] = __int_as_float(bi);
+      } else {
+        os[0] = mt;
+        os[1] = st;
+        os[2] = best;
+        os[3] = __int_as_float(bi);
+        os[4] = lg;
+      }
+    }
+  }
   if constexpr (EPI == EPI_LSE || EPI == EPI_ARGMAX) {
     float* rw = red + (wave * 64 + lane) * 4;
     if constexpr (EPI == EPI_LSE) {
@@ -720,7 +836,7 @@ __device__ int32_t kNoRows[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 template <int EPI, int NG>
 __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[kXLdsElems + 8 * 8];
-  __shared__ __attribute__((aligned(16))) float red[kWaves * 64 * 4];
+  __shared__ __attribute__((aligned(16))) float red[kWaves * 64 * (Ep<EPI>::SAMPLED ? 10 : 4)];
   __shared__ int seqc[8];  // sequence ids of the staged rows of a later chunk
   Work wk;
   wk.nwg = a.nwg_r;
@@ -746,6 +862,9 @@ __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a)
   const int n_i4 = min(max(*a.cnt_i4, 0), kMaxBatch);
   if constexpr (EPI == EPI_LSE || EPI == EPI_ARGMAX) {
     if (n_bf > a.max_rows) return;  // the wide (MFMA) vocabulary pass has these rows
+  }
+  if constexpr (EPI == EPI_RESAMPLE) {
+    if (n_bf == 0) return;  // nothing rejected
   }
   if (threadIdx.x < 64) {
     const int e = threadIdx.x & 7;
@@ -780,7 +899,7 @@ __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a)
   }
   bool first = true;  // the first pass needs no barrier: its staging waits for seq0
   for (int fmt = fmt_lo; fmt <= fmt_hi; ++fmt) {
-    if constexpr (EPI == EPI_LSE || EPI == EPI_ARGMAX || EPI == EPI_BF16) {
+    if constexpr (Ep<EPI>::VOCAB || EPI == EPI_BF16) {
       if (fmt == 1) break;  // these run on backbone rows only
     }
     const int n = fmt ? n_i4 : n_bf;
@@ -886,6 +1005,10 @@ int launch_proj(int epi, const ProjArgs& a0, int nwg, int batch, hipStream_t s, 
     case EPI_LSE: launch_ng<EPI_LSE>(a, g, s, ev0, ev1); break;
     case EPI_ARGMAX: launch_ng<EPI_ARGMAX>(a, g, s, ev0, ev1); break;
     case EPI_QKV: launch_ng<EPI_QKV>(a, g, s, ev0, ev1); break;
+    case EPI_LSE_S: launch_ng<EPI_LSE_S>(a, g, s, ev0, ev1); break;
+    case EPI_ARGMAX_S: launch_ng<EPI_ARGMAX_S>(a, g, s, ev0, ev1); break;
+    case EPI_RESAMPLE: launch_ng<EPI_RESAMPLE>(a, g, s, ev0, ev1); break;
+    default: throw std::logic_error("projection: unknown epilogue");
   }
   return a.nkc;
 }

@@ -46,6 +46,12 @@ from oracle.numerics import from_bf16_bits
 TOL = 2e-2
 GAP_BAND = 1e-2
 P_BAND = 1e-3
+# sampled decoding: a draw's perturbed top-2 gap (score units: logit / tau plus
+# Gumbel noise, float32 on the GPU) and the acceptance test's relative margin
+# |u p_draft - p_final| / max(p_draft, p_final) below which the decision is a
+# near tie (the logit error is added to the gap band by the caller)
+SAMPLE_BAND = 2e-3
+ACCEPT_BAND = 1e-3
 
 
 def log(*a):
@@ -71,6 +77,7 @@ class Result:
         self.widened_tokens = 0
         self.exits = []
         self.worst = {}
+        self.sample_outcomes = []   # sampled decoding: "none" / "accepted" / "rejected" per compared token
 
     def note(self, key, v):
         self.worst[key] = max(self.worst.get(key, 0.0), v)
@@ -84,7 +91,7 @@ def _normrel(a, r):
 
 def run_parity(shape, weights, batch, P, steps, gamma, exit_mode="int4", forced_fn=None,
                prompts=None, max_seq=None, check_kv=True, check_hidden=True, label="", criterion="head",
-               check_every=1, exit_rule="sequence"):
+               check_every=1, exit_rule="sequence", temperature=0.0, seed=0):
     import torch
     from kv_shared_exit_amd import api, _binding as B
 
@@ -97,7 +104,9 @@ def run_parity(shape, weights, batch, P, steps, gamma, exit_mode="int4", forced_
     dev = api.upload_weights(weights)
     model = api.Model(shape, dev, gamma=gamma, exit_mode=mode, max_batch=batch, max_positions=S,
                       criterion=B.EE_CRIT_STS if sts else B.EE_CRIT_HEAD, check_every=check_every,
-                      exit_rule=B.EE_RULE_BATCH_MIN if exit_rule == "batch_min" else B.EE_RULE_SEQUENCE)
+                      exit_rule=B.EE_RULE_BATCH_MIN if exit_rule == "batch_min" else B.EE_RULE_SEQUENCE,
+                      temperature=temperature, sample_seed=seed)
+    sampled = temperature > 0
     bmin = exit_rule == "batch_min"
     cache = api.KVCache(model, batch, S, track=True)
     orc = om.OracleModel(shape, weights, exit_mode=exit_mode)
@@ -127,7 +136,8 @@ def run_parity(shape, weights, batch, P, steps, gamma, exit_mode="int4", forced_
         for s in range(steps):
             forced = np.zeros(batch, np.int32) if forced_fn is None else np.asarray(forced_fn(s), np.int32)
             to, eo, io = om.decode_step(orc, ocache, tok_in, gamma=gam, forced=forced, trace=check_hidden,
-                                        criterion=criterion, check_every=check_every, exit_rule=exit_rule)
+                                        criterion=criterion, check_every=check_every, exit_rule=exit_rule,
+                                        temperature=temperature, seed=seed)
             fg = forced.copy()
             for b in range(batch):
                 if forced[b] == 0:
@@ -180,7 +190,23 @@ def run_parity(shape, weights, batch, P, steps, gamma, exit_mode="int4", forced_
             for b in range(batch):
                 eps = float(np.abs(dbg["logits"][b].astype(np.float64) - io["logits"][b]).max())
                 band = max(GAP_BAND, 2 * eps)
-                if io["gap"][b] > band:
+                if sampled:
+                    # every decision of the draw (perturbed top-2 gaps; the
+                    # acceptance test's relative margin) clear of rounding
+                    si = io["sample"][b]
+                    mg = si["margins"]
+                    gaps = [mg[0]] + mg[2:] if si["draft"] is not None else mg
+                    safe = min(gaps) > SAMPLE_BAND + 2 * eps / temperature and (
+                        si["draft"] is None or mg[1] > ACCEPT_BAND)
+                    if safe:
+                        assert tgpu[b] == to[b], (f"{label} step {s} b={b}: sampled token gpu {tgpu[b]} oracle "
+                                                  f"{to[b]} ({si})")
+                        res.compared_tokens += 1
+                        res.sample_outcomes.append("none" if si["draft"] is None else
+                                                   "accepted" if si["accepted"] else "rejected")
+                    else:
+                        res.tie_tokens += 1
+                elif io["gap"][b] > band:
                     assert tgpu[b] == to[b], (f"{label} step {s} b={b}: token gpu {tgpu[b]} oracle "
                                               f"{to[b]} gap {io['gap'][b]:.3g} band {band:.3g}")
                     res.compared_tokens += 1

@@ -230,3 +230,45 @@ def test_graph_replay_equals_eager(api):
     for (ka, va), (kb, vb) in zip(kva, kvb):
         np.testing.assert_array_equal(ka, kb)
         np.testing.assert_array_equal(va, vb)
+
+
+def test_sampled_decoding_configuration_errors(api):
+    """Sampled decoding drafts from the exit head after every layer, on batches
+    of at most 8 rows; other configurations are refused at creation."""
+    from kv_shared_exit_amd import _binding as B
+    w = synth.make_weights(ODD, 3)
+    dev = api.upload_weights(w)
+    cases = [(dict(temperature=1.0, criterion=B.EE_CRIT_STS), B.EE_ERR_INVALID_ARG),
+             (dict(temperature=1.0, check_every=2), B.EE_ERR_INVALID_ARG),
+             (dict(temperature=1.0, exit_mode=B.EE_EXIT_NONE), B.EE_ERR_INVALID_ARG),
+             (dict(temperature=-1.0), B.EE_ERR_INVALID_ARG),
+             (dict(temperature=float("nan")), B.EE_ERR_INVALID_ARG),
+             (dict(temperature=1.0, max_batch=9), B.EE_ERR_UNSUPPORTED)]
+    for kw, status in cases:
+        with pytest.raises(B.EEError) as e:
+            api.Model(ODD, dev, max_positions=8, **{"max_batch": 2, **kw})
+        assert e.value.status == status, kw
+
+
+def test_sampled_graph_replay_equals_eager_and_repeats(api):
+    """Sampled steps replay their captured graph (the resampling pass included)
+    with the same tokens as eager launches, and a rolled-back step draws the
+    same tokens again (the draws are keyed by sequence and position)."""
+    sh = ODD
+    w, m = _model(api, sh, alpha=np.full(sh.n_layers - 1, 40.0), max_batch=4, max_positions=16,
+                  gamma=0.3, temperature=1.0, sample_seed=7)
+    c = api.KVCache(m, 4, 16)
+    try:
+        api.prefill(m, c, np.arange(20, dtype=np.int32).reshape(4, 5))
+        toks = np.array([1, 2, 3, 4], np.int32)
+        runs = []
+        for debug in (None, {"gap": None}, None):
+            t, e = api.decode_step(m, c, 4, tokens=toks, debug=debug)
+            runs.append((t.copy(), e.copy()))
+            c.rollback(-1, 1)
+        for t, e in runs[1:]:
+            np.testing.assert_array_equal(t, runs[0][0])
+            np.testing.assert_array_equal(e, runs[0][1])
+    finally:
+        c.close()
+        m.close()

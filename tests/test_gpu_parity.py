@@ -341,3 +341,71 @@ def test_batch_minimum_of_one_sequence_is_the_per_sequence_rule(gpu):
     for (ta, ea), (tb, eb) in zip(run(B.EE_RULE_SEQUENCE), run(B.EE_RULE_BATCH_MIN)):
         np.testing.assert_array_equal(ea, eb)
         np.testing.assert_array_equal(ta, tb)
+
+
+# ---------------------------------------------------------------------------
+# Sampled decoding with AdaDecode's verification
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,batch,temperature", [("tiny", 4, 1.0), ("odd", 5, 0.7), ("hd64", 3, 1.5)])
+def test_sampled_decoding_against_oracle(gpu, name, batch, temperature):
+    """Draft at the exit layer (Gumbel-max of the exit head's logits / tau over
+    Philox noise), acceptance with min(1, p_final / p_draft), resampling from
+    relu(p_final - p_draft), and undrafted rows from p_final: tokens equal the
+    oracle's wherever every draw and the acceptance test are clear of rounding.
+    Forced exits spread the drafts over every layer (and leave some rows at
+    full depth, which draw from the final distribution)."""
+    from parity import run_parity
+    sh, w = _weights(name, min(2.0, SHAPES[name].n_layers - 0.5), 7, 6)
+    L = sh.n_layers
+    forced = lambda s: np.array([1 + (b + s) % L for b in range(batch)], np.int32)
+    res = run_parity(sh, w, batch, 7, 6, 0.75, forced_fn=forced, label=f"{name}-sampled",
+                     temperature=temperature, seed=1234)
+    outcomes = set(res.sample_outcomes)
+    assert res.compared_tokens >= batch * 4
+    assert "none" in outcomes and outcomes & {"accepted", "rejected"}, outcomes
+
+
+def test_sampled_decoding_rejections_are_resampled(gpu):
+    """Exit heads scaled up (alpha 3000: nearly one-hot exit distributions, so
+    every row exits after layer 1 on its own criterion and the draft's
+    probability is ~1): a draft is accepted only with the final distribution's
+    probability of it, so most are rejected and the resampling pass decides
+    most tokens."""
+    from parity import run_parity
+    sh = SHAPES["odd"]
+    w = synth.make_weights(sh, 5, alpha=np.full(sh.n_layers - 1, 3000.0))
+    res = run_parity(sh, w, 4, 6, 6, 0.75, label="odd-sampled-rejections", temperature=1.0, seed=99)
+    assert res.sample_outcomes.count("rejected") >= 3, res.sample_outcomes
+
+
+def test_sampled_low_temperature_equals_greedy(gpu):
+    """tau -> 0: the verified draw is the greedy token (the draft is the exit
+    head's argmax, accepted iff it is the final argmax, else the residual's
+    mass sits on the final argmax)."""
+    from kv_shared_exit_amd import api
+    sh, w = _weights("tiny", 2.0, 8, 5)
+    dev = api.upload_weights(w)
+    prompts = np.random.default_rng(8).integers(0, sh.vocab, (4, 8)).astype(np.int32)
+    toks = {}
+    for tau in (0.0, 1e-5):
+        m = api.Model(sh, dev, gamma=0.75, max_batch=4, max_positions=16, temperature=tau, sample_seed=3)
+        c = api.KVCache(m, 4, 16)
+        t = api.prefill(m, c, prompts)
+        seq = []
+        for s in range(5):
+            forced = np.array([1 + (b + s) % sh.n_layers for b in range(4)], np.int32)
+            dbg = {"gap": None}
+            t, e = api.decode_step(m, c, 4, tokens=t, forced=forced, debug=dbg)
+            seq.append((t.copy(), dbg["gap"].copy()))
+        toks[tau] = seq
+        c.close()
+        m.close()
+    checked = 0
+    for (tg, gap), (tc, _) in zip(toks[0.0], toks[1e-5]):
+        for b in range(4):
+            if gap[b] > 1e-3:
+                assert tc[b] == tg[b]
+                checked += 1
+        if not np.array_equal(tg, tc):
+            break
+    assert checked >= 4
