@@ -30,25 +30,27 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 
-# HBM traffic of one exit-head launch with rows on the backbone (8B shape, 8
-# staged rows), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of
-# kv_shared_exit_amd/ee_probe (profiles/exit_head_lse_8b_traffic.md), each
+# HBM traffic of one exit-head launch with rows on the backbone, per workload:
+# the 8B shape with 8 staged rows (proj_kernel<3, 1>) and with 64 rows (the
+# wide pass, wide_vocab_kernel<3>), from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE runs of kv_shared_exit_amd/ee_probe (profiles/*_traffic.md), each
 # scaled by what the same counter reads for a 1 GiB device copy.  Valid only
 # for the kernel sources it was measured on (their sha256); otherwise null.
-TRAFFIC = {"workload": "8b", "fetch_kib": 513407.1146, "write_kib": 64.0,
-           "fetch_scale": 1.9999328, "write_scale": 1.0,
-           "sources_sha256": "5d501ea503dc16ae418b2fa8cacc42ac44d58418e09c3e686b7ff94d7c7817c0"}
-KERNEL_SOURCES = ("ee_proj.hip", "ee_device.h", "ee_internal.h", "ee_epi.h")
+TRAFFIC = {
+    "8b": {"fetch_kib": 513407.1146, "write_kib": 64.0, "fetch_scale": 1.9999328, "write_scale": 1.0,
+           "sources": ("ee_proj.hip", "ee_device.h", "ee_internal.h", "ee_epi.h"),
+           "sources_sha256": "5d501ea503dc16ae418b2fa8cacc42ac44d58418e09c3e686b7ff94d7c7817c0"},
+}
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_sources_sha256():
+def kernel_sources_sha256(sources=("ee_proj.hip", "ee_device.h", "ee_internal.h", "ee_epi.h")):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "kv_shared_exit_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -176,6 +178,9 @@ def main():
                     help="per-sequence exits (default) or River-LLM's batch minimum (secondary line)")
     ap.add_argument("--check-every", type=int, default=1,
                     help="evaluate the exit criterion only after every N-th layer (secondary line)")
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="sampled decoding with AdaDecode's verification at this temperature (secondary "
+                         "line; 0: greedy)")
     ap.add_argument("--no-baselines", action="store_true",
                     help="skip the full-depth and bf16-exit-copy comparison runs")
     ap.add_argument("--copy-probe", action="store_true",
@@ -224,7 +229,7 @@ def main():
     every = max(1, args.check_every)
     rule = Bd.EE_RULE_BATCH_MIN if args.exit_rule == "batch-min" else Bd.EE_RULE_SEQUENCE
     model = api.Model(sh, dev, gamma=thresholds, max_batch=B, max_positions=S, criterion=crit, check_every=every,
-                      exit_rule=rule)
+                      exit_rule=rule, temperature=args.temperature, sample_seed=wl.seed_prompts)
     cache = api.KVCache(model, B, S)
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
@@ -302,8 +307,10 @@ def main():
     # measured HBM traffic per launch, averaged like the algorithmic bytes (a
     # launch without rows reads nothing)
     traffic = None
-    if wl.name == TRAFFIC["workload"] and kernel_sources_sha256() == TRAFFIC["sources_sha256"] and n_launch:
-        per_work = (TRAFFIC["fetch_kib"] * TRAFFIC["fetch_scale"] + TRAFFIC["write_kib"] * TRAFFIC["write_scale"]) * 1024
+    tr = TRAFFIC.get(wl.name)
+    if (tr and not sts and args.temperature == 0 and kernel_sources_sha256(tr["sources"]) == tr["sources_sha256"]
+            and n_launch):
+        per_work = (tr["fetch_kib"] * tr["fetch_scale"] + tr["write_kib"] * tr["write_scale"]) * 1024
         n_work = sum(1 for s_ in range(K) for l in range(every, sh.n_layers, every) if (exits[s_] >= l).any())
         traffic = round(per_work * n_work / n_launch)
 
@@ -315,6 +322,13 @@ def main():
         torch.cuda.synchronize()
         copy_probe = {"bytes_read": x.numel() * 4, "bytes_written": y.numel() * 4}
 
+    if args.temperature > 0:
+        head_kernel = "exit-head vocabulary GEMV with the draft's draw (proj_kernel<6, 1>)"
+    elif B > 8:
+        head_kernel = ("exit-head vocabulary GEMV: wide_vocab_kernel<3> above 8 rows on the backbone, "
+                       "proj_kernel<3, 1> otherwise (one launch each, the other returns at once)")
+    else:
+        head_kernel = "exit-head vocabulary GEMV (proj_kernel<3, 1>)"
     hist = np.bincount(exits.reshape(-1), minlength=sh.n_layers + 1)[1:]
     mean_exit = float(exits.mean())
     out = {
@@ -335,7 +349,7 @@ def main():
                                f"V{sh.vocab}, int4 G{sh.group} exit copies, batch {B}, "
                                f"{P}-token prompts, gamma {wl.gamma}",
                    "global_batch": B, "seq_len": P, "decode_steps": K, "parallelism": "none"},
-        "roofline": {"bound": "hbm", "kernel": "exit-head vocabulary GEMV (proj_kernel<3, 1>)",
+        "roofline": {"bound": "hbm", "kernel": head_kernel,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "launches": n_launch, "launches_with_work": head_launches,
@@ -371,6 +385,10 @@ def main():
     if rule == Bd.EE_RULE_BATCH_MIN:
         out["metric"] += ", batch-minimum exits"
         out["config"]["workload"] += ", batch-minimum exit rule"
+    if args.temperature > 0:
+        out["metric"] += f", sampled (temperature {args.temperature}, verified drafts)"
+        out["config"]["workload"] += (f", sampled decoding at temperature {args.temperature} with AdaDecode's "
+                                      f"verification of the exit-layer drafts")
     if every > 1:
         out["metric"] += f", criterion every {every} layers"
         out["config"]["workload"] += f", criterion evaluated after every {every}th layer"

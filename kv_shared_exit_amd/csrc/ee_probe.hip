@@ -5,6 +5,8 @@
 //
 //   ee_probe lse V d rows reps   exit-head vocabulary GEMV (proj_kernel<EPI_LSE>)
 //                                over a V x d bf16 matrix and `rows` staged rows
+//   ee_probe wide V d rows reps  the same GEMV for 9..64 rows on matrix cores
+//                                (wide_vocab_kernel<EPI_LSE> over the tiled copy)
 //   ee_probe copy MiB            one copy kernel reading and writing MiB each
 //
 // Prints the mean launch time (HIP events on the launch stream).
@@ -34,7 +36,7 @@ __global__ void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ d
 }
 
 static int usage() {
-  std::fprintf(stderr, "usage: ee_probe lse V d rows reps | ee_probe copy MiB\n");
+  std::fprintf(stderr, "usage: ee_probe lse V d rows reps | ee_probe wide V d rows reps | ee_probe copy MiB\n");
   return 2;
 }
 
@@ -64,10 +66,13 @@ int main(int argc, char** argv) {
     std::printf("copy %zu MiB: %.2f us, %.1f GB/s (read + write)\n", mib, 1e3 * ms, 2.0 * n * 16 / (ms * 1e6));
     return 0;
   }
-  if (!std::strcmp(argv[1], "lse")) {
+  const bool wide = !std::strcmp(argv[1], "wide");
+  if (!std::strcmp(argv[1], "lse") || wide) {
     if (argc < 6) return usage();
     const int V = std::atoi(argv[2]), d = std::atoi(argv[3]), rows = std::atoi(argv[4]), reps = std::atoi(argv[5]);
-    if (V < 1 || d < 32 || d % 32 || rows < 1 || rows > 8 || reps < 1 || !proj_fits(d, rows)) return usage();
+    if (V < 1 || d < 32 || d % 32 || rows < 1 || reps < 1) return usage();
+    if (!wide && (rows > 8 || !proj_fits(d, rows))) return usage();
+    if (wide && (rows <= 8 || rows > kMaxBatch || !wide_vocab_supported(d))) return usage();
     uint16_t *E, *x;
     float* part;
     int32_t* lists;
@@ -93,17 +98,30 @@ int main(int argc, char** argv) {
     a.list_bf = lists;
     a.cnt_bf = lists + kMaxBatch;
     a.part = part;
-    launch_proj(EPI_LSE, a, kNwgMax, rows, s);  // warm-up
+    uint16_t* Et = nullptr;
+    if (wide) {
+      CK(hipMalloc(&Et, wide_vocab_elems(V, d) * 2));
+      launch_tile_vocab(E, V, d, Et, s);
+      a.wb[0] = Et;
+    }
+    auto launch = [&] {
+      if (wide)
+        launch_wide_vocab(EPI_LSE, a, kNwgMax, s);
+      else
+        launch_proj(EPI_LSE, a, kNwgMax, rows, s);
+    };
+    launch();  // warm-up
     CK(hipStreamSynchronize(s));
     CK(hipEventRecord(e0, s));
-    for (int r = 0; r < reps; ++r) launch_proj(EPI_LSE, a, kNwgMax, rows, s);
+    for (int r = 0; r < reps; ++r) launch();
     CK(hipEventRecord(e1, s));
     CK(hipEventSynchronize(e1));
     float ms = 0;
     CK(hipEventElapsedTime(&ms, e0, e1));
     const double us = 1e3 * ms / reps;
     const double bytes = 2.0 * V * d + 2.0 * d * rows;
-    std::printf("lse V=%d d=%d rows=%d: %.2f us per launch, %.1f GB/s algorithmic\n", V, d, rows, us, bytes / us / 1e3);
+    std::printf("%s V=%d d=%d rows=%d: %.2f us per launch, %.1f GB/s algorithmic\n", wide ? "wide" : "lse", V, d,
+                rows, us, bytes / us / 1e3);
     return 0;
   }
   return usage();

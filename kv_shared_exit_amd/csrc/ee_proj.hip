@@ -290,11 +290,13 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, const Work& wk, int
         lse_merge(lm, ls, v, 1.0f);
         const float sv = v * a.itau;
         lse_merge(lmt, lst, sv, 1.0f);
-        const float sc = sv + gumbel_noise(a.seed, a.lens[sq], sq, STREAM_DRAFT, n);
-        if (sc > pb) {  // rows ascend per lane: the lowest index wins ties
-          pb = sc;
-          pi = n;
-          pl = v;
+        if (sv + kGumbelMax >= pb) {  // else no noise value can lift it above the best
+          const float sc = sv + gumbel_noise(a.seed, a.lens[sq], sq, STREAM_DRAFT, n);
+          if (sc > pb) {  // rows ascend per lane: the lowest index wins ties
+            pb = sc;
+            pi = n;
+            pl = v;
+          }
         }
       }
     } else if constexpr (EPI == EPI_ARGMAX_S) {
@@ -310,10 +312,12 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, const Work& wk, int
         }
         const float sv = v * a.itau;
         lse_merge(lmt, lst, sv, 1.0f);
-        const float sc = sv + gumbel_noise(a.seed, a.lens[sq], sq, STREAM_FINAL, n);
-        if (sc > pb) {
-          pb = sc;
-          pi = n;
+        if (sv + kGumbelMax >= pb) {
+          const float sc = sv + gumbel_noise(a.seed, a.lens[sq], sq, STREAM_FINAL, n);
+          if (sc > pb) {
+            pb = sc;
+            pi = n;
+          }
         }
         if (n == a.st->draft_tok[sq]) pl = v;
       }
@@ -324,7 +328,7 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, const Work& wk, int
       if (lane_ok && (bsel & 1) == 0 && n < N) {
         const int sq = seq[bsel];
         const float r = __expf(v * a.itau - a.st->lse_f[sq]) - __expf(u * a.itau - a.st->draft_lse[sq]);
-        if (r > 0.0f) {
+        if (r > 0.0f && __logf(r) + kGumbelMax >= pb) {
           const float sc = __logf(r) + gumbel_noise(a.seed, a.lens[sq], sq, STREAM_RESAMPLE, n);
           if (sc > pb) {
             pb = sc;
@@ -349,7 +353,13 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, const Work& wk, int
   }
 
   if constexpr (Ep<EPI>::SAMPLED) {
-    float* rw = red + (wave * 64 + lane) * 8;
+    // 10 floats per lane: reduced through the input stage's LDS (every wave is
+    // done with the inputs after this barrier), which keeps the kernel's LDS
+    // at two workgroups per CU
+    static_assert(kXLdsElems * 2 >= kWaves * 64 * 10 * 4, "the input stage holds the sampled reduction");
+    __syncthreads();
+    float* rd = reinterpret_cast<float*>(xs);
+    float* rw = rd + (wave * 64 + lane) * 8;
     rw[0] = lm;
     rw[1] = ls;
     rw[2] = tp.v1;
@@ -358,7 +368,7 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, const Work& wk, int
     rw[5] = lmt;
     rw[6] = lst;
     rw[7] = pl;
-    float* rp = red + kWaves * 64 * 8 + (wave * 64 + lane) * 2;  // the perturbed best and its index
+    float* rp = rd + kWaves * 64 * 8 + (wave * 64 + lane) * 2;  // the perturbed best and its index
     rp[0] = pb;
     rp[1] = __int_as_float(pi);
     __syncthreads();
@@ -370,8 +380,8 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, const Work& wk, int
       for (int ww = 0; ww < kWaves; ++ww)
         for (int l = 0; l < V; ++l)
           if (xidx<V>(l) % NB == tid) {
-            const float* src = red + (ww * 64 + l) * 8;
-            const float* sp = red + kWaves * 64 * 8 + (ww * 64 + l) * 2;
+            const float* src = rd + (ww * 64 + l) * 8;
+            const float* sp = rd + kWaves * 64 * 8 + (ww * 64 + l) * 2;
             lse_merge(m, sm, src[0], src[1]);
             top2_merge(g2, Top2{src[2], __float_as_int(src[3]), src[4]});
             lse_merge(mt, st, src[5], src[6]);
@@ -836,7 +846,7 @@ __device__ int32_t kNoRows[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 template <int EPI, int NG>
 __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[kXLdsElems + 8 * 8];
-  __shared__ __attribute__((aligned(16))) float red[kWaves * 64 * (Ep<EPI>::SAMPLED ? 10 : 4)];
+  __shared__ __attribute__((aligned(16))) float red[kWaves * 64 * 4];
   __shared__ int seqc[8];  // sequence ids of the staged rows of a later chunk
   Work wk;
   wk.nwg = a.nwg_r;

@@ -37,6 +37,11 @@ __device__ __forceinline__ uint64_t philox_word(uint64_t seed, uint64_t pos, uin
 
 __device__ __forceinline__ float philox_uniform(uint64_t x) { return ((float)(x >> 41) + 0.5f) * 0x1p-23f; }
 
+// Above every Gumbel value these uniforms give (the largest, 1 - 2^-24, gives
+// -log(-log u) = 16.64): an entry whose score is more than this below the best
+// perturbed score so far cannot win a draw, so its noise is not computed.
+constexpr float kGumbelMax = 16.7f;
+
 __device__ __forceinline__ float gumbel_noise(uint32_t seed, int pos, int seq, int stream, int v) {
   const float u = philox_uniform(philox_word(seed, (uint64_t)pos, (uint64_t)seq, (uint64_t)stream, (uint64_t)v));
   return -logf(-logf(u));

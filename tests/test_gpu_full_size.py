@@ -232,3 +232,63 @@ def test_layer_widths_of_other_workloads(name, batch):
         kr = oc.K[l - 1, 0, :, :P + 1].transpose(1, 0, 2)
         vr = oc.V[l - 1, 0, :, :P + 1].transpose(1, 0, 2)
         assert maxrel(from_bf16_bits(k), kr) <= TOL and maxrel(from_bf16_bits(v), vr) <= TOL
+
+
+def test_wide_passes_at_the_8b_widths_batch_64():
+    """The batch-64 configuration's matrix-core (wide) passes at the 8B widths
+    (d 4096, 32/8 heads of 128, F 14336, V 128256, int4 G128) on two layers:
+    every projection and both vocabulary GEMVs see the full-size shapes.
+    Sequences 0 and 63 against the oracle: at full depth (hidden states,
+    logits, token, K/V), and with every row forced out after layer 1 (layer 2
+    on the int4 copy through the wide int4 pass; the exit head's wide pass runs
+    after layer 1 for all 64 rows)."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kv_shared_exit_amd import api
+    wl = synth.workload("8b_b64")
+    sh = dataclasses.replace(wl.shape, n_layers=2)
+    w = synth.make_weights(sh, wl.seed_weights)
+    Bw, P = 64, 3
+    prompts = np.random.default_rng(79).integers(0, sh.vocab, (Bw, P)).astype(np.int32)
+    dev = api.upload_weights(w)
+    out = {}
+    for label, gamma, forced in (("full", 2.0, None), ("exit1", 0.75, np.ones(Bw, np.int32))):
+        model = api.Model(sh, dev, gamma=gamma, max_batch=Bw, max_positions=P + 2)
+        cache = api.KVCache(model, Bw, P + 2, track=True)
+        try:
+            tg, lg = api.prefill(model, cache, prompts, logits=True)
+            dbg = {"logits": None, "hidden": None, "p": None}
+            t1, e1 = api.decode_step(model, cache, Bw, tokens=tg, forced=forced, debug=dbg)
+            kv = {b: cache.read(2, b, 0, P + 1) for b in (0, 63)}
+            assert np.all(cache.occupancy()[:, :Bw, :P + 1] == 1)
+            out[label] = (tg, lg, t1, e1, dbg, kv)
+        finally:
+            cache.close()
+            model.close()
+    orc = om.OracleModel(sh, w, cache_f64=True)
+    for b in (0, 63):
+        for label in ("full", "exit1"):
+            tg, lg, t1, e1, dbg, kv = out[label]
+            oc = om.KVCache(sh, 1, P + 2)
+            to, info = om.prefill(orc, oc, prompts[b:b + 1])
+            assert maxrel(lg[b], info["logits"][0]) <= TOL, f"{label} b={b} prefill logits"
+            forced = None if label == "full" else [1]
+            t2, e2, io = om.decode_step(orc, oc, tg[b:b + 1], forced=forced, trace=True,
+                                        heads=label != "full")
+            assert e1[b] == e2[0]
+            for l in range(sh.n_layers + 1):
+                e = maxrel(dbg["hidden"][b, l], io["hidden"][0, l])
+                assert e <= TOL, f"{label} b={b}: hidden after layer {l}: maxrel {e:.3g}"
+            e = maxrel(dbg["logits"][b], io["logits"][0])
+            assert e <= TOL, f"{label} b={b}: logits maxrel {e:.3g}"
+            band = max(1e-2, 2 * float(np.abs(dbg["logits"][b].astype(np.float64) - io["logits"][0]).max()))
+            if io["gap"][0] > band:
+                assert t1[b] == t2[0], f"{label} b={b}: token"
+            if label == "exit1":   # the exit head ran after layer 1 for every row (wide pass)
+                pe = float(io["p"][0, 0])
+                assert abs(np.log(float(dbg["p"][b, 0])) - np.log(pe)) <= 2 * TOL * float(io["head_absmax"][0, 0])
+            k, v = kv[b]
+            kr = oc.K[1, 0, :, :P + 1].transpose(1, 0, 2)
+            vr = oc.V[1, 0, :, :P + 1].transpose(1, 0, 2)
+            assert maxrel(from_bf16_bits(k), kr) <= TOL and maxrel(from_bf16_bits(v), vr) <= TOL, f"{label} KV"
