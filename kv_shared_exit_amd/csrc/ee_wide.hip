@@ -11,12 +11,15 @@
 //     load as the A operand of v_mfma_f32_16x16x32_bf16 are contiguous (lane l
 //     holds row l % 16, columns 8 (l / 16) .. +8 of the step), so a wave reads
 //     whole cache lines.  Rows past V are zero.
-//   * A workgroup (8 waves) owns 16 tiles (256 rows), two per wave.  The input
-//     rows are staged in LDS 256 columns at a time, double-buffered: the next
-//     columns are fetched while the current ones are multiplied.
-//   * Each wave keeps 8 steps of its two tiles' E blocks in flight in a
-//     register ring, refilled as they are consumed (one workgroup per CU:
-//     256 registers per lane; 128 KB of E in flight per CU).
+//   * A workgroup (8 waves) owns 8 tiles (128 rows) at a time, one per wave,
+//     and takes its next 8 tiles a grid later.  The input rows are staged in
+//     LDS 256 columns at a time, double-buffered: the next columns are fetched
+//     while the current ones are multiplied.
+//   * Each wave keeps 8 steps of its tile's E blocks in flight in a register
+//     ring, refilled as they are consumed (two workgroups per CU within 128
+//     registers per lane: 128 KB of E in flight per CU).  Measured against
+//     two tiles per wave at one workgroup per CU: 175.6 against 182.5 us for
+//     64 rows at the 8B shape.
 //   * Epilogue as the vector-ALU pass: per row of the batch, the workgroup's
 //     (max, sum exp) of its logits, or its top-2 (lowest index on ties); the
 //     logits never reach memory (except on request for diagnostics).
@@ -41,7 +44,7 @@ constexpr int kWideCols = 256;            // input columns staged per chunk
 constexpr int kWideStride = kWideCols + 8;  // LDS row stride (16 bytes of padding)
 constexpr int kWideBuf = kWideRows * kWideStride;
 constexpr int kWideWaves = kProjThreads / 64;
-constexpr int kWideTiles = 2;             // 16-row tiles per wave
+constexpr int kWideTiles = 1;             // 16-row tiles per wave
 constexpr int kRing = 8;                  // 32-column steps in flight per tile
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8_t, v); }
@@ -113,7 +116,7 @@ void launch_tile_vocab(const uint16_t* E, int V, int d, uint16_t* Et, hipStream_
 // a.wb[0]: the tiled E; a.N = V; a.K = d; rows: list_bf / cnt_bf (runs only
 // when the count exceeds 8: the vector-ALU pass takes smaller counts).
 template <int EPI>
-__global__ __launch_bounds__(kProjThreads, 2) void wide_vocab_kernel(const ProjArgs a) {
+__global__ __launch_bounds__(kProjThreads, 4) void wide_vocab_kernel(const ProjArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[2 * kWideBuf];
   __shared__ float red[kWideWaves * kWideRows * 4];
   const int n = min(max(*a.cnt_bf, 0), kWideRows);
