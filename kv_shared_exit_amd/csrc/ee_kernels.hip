@@ -367,14 +367,25 @@ __global__ __launch_bounds__(kHeadThreads) void decide_kernel(StepState* st, con
   __shared__ int sn;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   // the first row of each wave is requested before the row count is known
-  // (list positions below kMaxBatch are always in bounds)
-  float2 v[kPartPerLane];
-  if constexpr (MODE == DECIDE_HEAD) load_lse_parts(part, nwg, w, lane, v);
+  // (list positions below kMaxBatch are always in bounds); the wave's other
+  // rows (batches above 8) are requested together once the count is known
+  constexpr int kRowsPerWave = kMaxBatch / kHeadWaves;
+  float2 v[kRowsPerWave][kPartPerLane];
+  if constexpr (MODE == DECIDE_HEAD) load_lse_parts(part, nwg, w, lane, v[0]);
   if ((int)threadIdx.x < B) sx[threadIdx.x] = st->exited[threadIdx.x];
   if (threadIdx.x == 0) sn = min(max(st->n_act, 0), B);
   __syncthreads();
   const int n = sn;
-  for (int i = w; i < n; i += kHeadWaves) {
+  if constexpr (MODE == DECIDE_HEAD) {
+    if (n > kHeadWaves) {
+#pragma unroll
+      for (int r = 1; r < kRowsPerWave; ++r) load_lse_parts(part, nwg, min(w + r * kHeadWaves, n - 1), lane, v[r]);
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r) {
+    const int i = w + r * kHeadWaves;
+    if (i >= n) break;  // uniform over the wave
     const int b = st->act[i];
     float p = 0.0f;
     if constexpr (MODE == DECIDE_FORCED) {
@@ -382,10 +393,9 @@ __global__ __launch_bounds__(kHeadThreads) void decide_kernel(StepState* st, con
     } else if constexpr (STS) {
       p = sts[b];
     } else {
-      if (i != w) load_lse_parts(part, nwg, i, lane, v);
       float m = -INFINITY, s = 0.0f;
 #pragma unroll
-      for (int j = 0; j < kPartPerLane; ++j) lse_merge(m, s, v[j].x, v[j].y);
+      for (int j = 0; j < kPartPerLane; ++j) lse_merge(m, s, v[r][j].x, v[r][j].y);
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
@@ -466,10 +476,12 @@ void launch_decide(int mode, bool batch_min, StepState* st, const float* part, i
   }
 }
 
-__global__ __launch_bounds__(kHeadThreads) void final_kernel(StepState* st, const float* part, int nwg, int B,
-                                                             int V, int32_t* lens, int advance) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int b = w; b < B; b += kHeadWaves) {
+// One wave per row (a workgroup each: the rows are independent).
+__global__ __launch_bounds__(64) void final_kernel(StepState* st, const float* part, int nwg, int B, int V,
+                                                   int32_t* lens, int advance) {
+  const int lane = threadIdx.x & 63;
+  {
+    const int b = blockIdx.x;
     float4 v[kPartPerLane];
 #pragma unroll
     for (int j = 0; j < kPartPerLane; ++j) {
@@ -498,7 +510,8 @@ __global__ __launch_bounds__(kHeadThreads) void final_kernel(StepState* st, cons
 void launch_final(StepState* st, const float* part, int nwg, int B, int V, int32_t* lens, int advance,
                   hipStream_t s) {
   if (nwg < 1 || nwg > kNwgMax) throw std::logic_error("final: partial count out of range");
-  hipLaunchKernelGGL(final_kernel, dim3(1), dim3(kHeadThreads), 0, s, st, part, nwg, B, V, lens, advance);
+  if (B < 1 || B > kMaxBatch) throw std::logic_error("final: batch out of range");
+  hipLaunchKernelGGL(final_kernel, dim3(B), dim3(64), 0, s, st, part, nwg, B, V, lens, advance);
 }
 
 __global__ void advance_kernel(int32_t* lens, int B) {
