@@ -292,3 +292,44 @@ def test_wide_passes_at_the_8b_widths_batch_64():
             kr = oc.K[1, 0, :, :P + 1].transpose(1, 0, 2)
             vr = oc.V[1, 0, :, :P + 1].transpose(1, 0, 2)
             assert maxrel(from_bf16_bits(k), kr) <= TOL and maxrel(from_bf16_bits(v), vr) <= TOL, f"{label} KV"
+
+
+def test_sampled_step_at_full_size(env):
+    """Sampled decoding with AdaDecode's verification at the benchmark's shape
+    (8B, batch 8, calibrated heads): sequence 0 forced out after layer 8 (its
+    draft comes from the exit head there and is verified after the int4
+    layers), sequence 1 at full depth (drawn from the final distribution);
+    both tokens equal the oracle's wherever the draws are clear of rounding."""
+    from parity import SAMPLE_BAND, ACCEPT_BAND
+    api, w, dev = env
+    P, tau = 2, 1.0
+    prompts = _prompts(P)
+    forced = np.array([8, SH.n_layers] + [12] * (B - 2), np.int32)
+    model = api.Model(SH, dev, gamma=0.75, max_batch=B, max_positions=P + 2, temperature=tau, sample_seed=31)
+    cache = api.KVCache(model, B, P + 2)
+    try:
+        tg = api.prefill(model, cache, prompts)
+        dbg = {"logits": None, "p": None}
+        t1, e1 = api.decode_step(model, cache, B, tokens=tg, forced=forced, debug=dbg)
+        np.testing.assert_array_equal(e1, forced)
+    finally:
+        cache.close()
+        model.close()
+    # sequences 0 and 1 as a batch of two (a sequence's step does not depend on
+    # the others in its batch)
+    orc = om.OracleModel(SH, w, cache_f64=False)
+    oc = om.KVCache(SH, 2, P + 2)
+    om.prefill(orc, oc, prompts[:2])
+    to, eo, io = om.decode_step(orc, oc, tg[:2], forced=forced[:2], temperature=tau, seed=31)
+    compared = 0
+    for b in (0, 1):
+        assert eo[b] == forced[b]
+        eps = float(np.abs(dbg["logits"][b].astype(np.float64) - io["logits"][b]).max())
+        si = io["sample"][b]
+        mg = si["margins"]
+        gaps = [mg[0]] + mg[2:] if si["draft"] is not None else mg
+        assert (si["draft"] is not None) == (b == 0)
+        if min(gaps) > SAMPLE_BAND + 2 * eps / tau and (si["draft"] is None or mg[1] > ACCEPT_BAND):
+            assert t1[b] == to[b], f"b={b}: sampled token gpu {t1[b]} oracle {to[b]} ({si})"
+            compared += 1
+    assert compared >= 1
