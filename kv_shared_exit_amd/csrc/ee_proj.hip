@@ -896,7 +896,12 @@ __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a)
   if constexpr (EPI == EPI_PART || EPI == EPI_QKV || EPI == EPI_SWIGLU) {
     if (n_bf > 0 && n_i4 > 0 && wk.nwg >= 2) {
       const int share = (EPI == EPI_SWIGLU || a.nkc > 2) ? kBfShareFfn : kBfShare;
-      const int nbf = min(wk.nwg - 1, max(1, (wk.nwg * share) >> 8));
+      int nbf = min(wk.nwg - 1, max(1, (wk.nwg * share) >> 8));
+      // the bf16 waves take whole rounds of tiles: keep the rounds this share
+      // gives and hand the workgroups they do not need to the int4 rows
+      const int tb = (a.N + Ep<EPI>::R - 1) / Ep<EPI>::R;
+      const int rounds = (tb + nbf * kWaves - 1) / (nbf * kWaves);
+      nbf = min(nbf, max(1, (tb + rounds * kWaves - 1) / (rounds * kWaves)));
       if (wk.wg < nbf) {
         fmt_hi = 0;
         wk.nwg = nbf;
