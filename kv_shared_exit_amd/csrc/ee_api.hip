@@ -58,6 +58,16 @@ struct LayerQ {
 
 constexpr int kNwg = 512;  // projection workgroups (2 per CU)
 
+// Workgroups of an 8-row vocabulary pass over V rows: the fewest that keep
+// the rounds of 2-row wave tiles the full grid would take, so that every wave
+// takes the same number of tiles (V = 128256: 501 workgroups, 16 tiles each).
+int vocab_nwg(int V) {
+  constexpr int waves = kProjThreads / 64;
+  const int tiles = (V + 1) / 2;
+  const int rounds = (tiles + kNwg * waves - 1) / (kNwg * waves);
+  return std::max(1, std::min(kNwg, (tiles + rounds * waves - 1) / (rounds * waves)));
+}
+
 }  // namespace
 
 struct ee_model {
@@ -293,6 +303,10 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
   const int every = std::max(1, cf.check_every);
   // sampled decoding (decode steps only; the prefill's token stays greedy)
   const bool sampled = heads && cf.temperature > 0.0f;
+  // vocabulary passes: batches above 8 run the wide pass (a full grid of
+  // partials); otherwise the 8-row pass on a grid of equal rounds
+  const bool wide_vocab = m->lm_head_t && B > 8;
+  const int nv = wide_vocab ? kNwg : vocab_nwg(cf.vocab);
   const float itau = sampled ? 1.0f / cf.temperature : 0.0f;
   auto sampled_args = [&](ProjArgs& a) {
     a.part_s = m->part_s;
@@ -551,21 +565,20 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
         prof_events(m, &e0, &e1);
         // more than 8 rows go to the wide pass (one read of E for all rows);
         // the row count is on the device, so both are launched and one returns
-        const bool wide = m->lm_head_t && B > 8;
         if (sampled) {  // also the draft's Gumbel-max and the tau statistics
           sampled_args(a);
-          launch_proj(EPI_LSE_S, a, kNwg, B, s, e0, e1);
+          launch_proj(EPI_LSE_S, a, nv, B, s, e0, e1);
         } else {
-          if (wide) a.max_rows = 8;
-          launch_proj(EPI_LSE, a, kNwg, B, s, e0, wide ? nullptr : e1);
-          if (wide) {
+          if (wide_vocab) a.max_rows = 8;
+          launch_proj(EPI_LSE, a, nv, B, s, e0, wide_vocab ? nullptr : e1);
+          if (wide_vocab) {
             a.wb[0] = m->lm_head_t;
-            launch_wide_vocab(EPI_LSE, a, kNwg, s, e1);
+            launch_wide_vocab(EPI_LSE, a, nv, s, e1);
           }
         }
       }
-      launch_decide(DECIDE_HEAD, bmin, st, m->head_part, kNwg, m->d_gamma, l, L, B, m->p_rec, nullptr, s);
-      if (sampled) launch_sample_draft(st, m->part_s, kNwg, l, B, m->z, m->xn + (size_t)kMaxBatch * d, d, s);
+      launch_decide(DECIDE_HEAD, bmin, st, m->head_part, nv, m->d_gamma, l, L, B, m->p_rec, nullptr, s);
+      if (sampled) launch_sample_draft(st, m->part_s, nv, l, B, m->z, m->xn + (size_t)kMaxBatch * d, d, s);
     }
     if (dbg.hidden)
       HIPCHK(hipMemcpy2DAsync(m->dbg_hidden + (size_t)l * d, (size_t)(L + 1) * d * 4, m->h,
@@ -587,9 +600,9 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       // the final distribution's statistics and draw, the greedy top-2 (gap),
       // the verification, then the resampling of the rejected drafts
       sampled_args(a);
-      launch_proj(EPI_ARGMAX_S, a, kNwg, B, s);
-      launch_final(st, m->head_part, kNwg, B, cf.vocab, c->lens, 0, s);
-      launch_sample_final(st, m->part_s, kNwg, B, L, cf.vocab, c->lens, itau, cf.sample_seed, s);
+      launch_proj(EPI_ARGMAX_S, a, nv, B, s);
+      launch_final(st, m->head_part, nv, B, cf.vocab, c->lens, 0, s);
+      launch_sample_final(st, m->part_s, nv, B, L, cf.vocab, c->lens, itau, cf.sample_seed, s);
       ProjArgs r = base_args(m);
       r.N = cf.vocab;
       r.K = d;
@@ -600,16 +613,16 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       r.x_stride = d;
       r.part = m->head_part;
       sampled_args(r);
-      launch_proj(EPI_RESAMPLE, r, kNwg, 2 * B, s);
-      launch_resample_final(st, m->part_s, kNwg, B, cf.vocab, c->lens, s);
+      launch_proj(EPI_RESAMPLE, r, nv, 2 * B, s);
+      launch_resample_final(st, m->part_s, nv, B, cf.vocab, c->lens, s);
     } else {
-      if (m->lm_head_t && B > 8) {  // every row of the batch: the wide pass alone
+      if (wide_vocab) {  // every row of the batch: the wide pass alone
         a.wb[0] = m->lm_head_t;
-        launch_wide_vocab(EPI_ARGMAX, a, kNwg, s);
+        launch_wide_vocab(EPI_ARGMAX, a, nv, s);
       } else {
-        launch_proj(EPI_ARGMAX, a, kNwg, B, s);
+        launch_proj(EPI_ARGMAX, a, nv, B, s);
       }
-      launch_final(st, m->head_part, kNwg, B, cf.vocab, c->lens, 1, s);
+      launch_final(st, m->head_part, nv, B, cf.vocab, c->lens, 1, s);
     }
   } else {
     launch_advance(c->lens, B, s);

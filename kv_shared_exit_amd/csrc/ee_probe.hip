@@ -12,6 +12,7 @@
 // Prints the mean launch time (HIP events on the launch stream).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -104,11 +105,16 @@ int main(int argc, char** argv) {
       launch_tile_vocab(E, V, d, Et, s);
       a.wb[0] = Et;
     }
+    // the 8-row pass runs on the grid the decode step gives it: the fewest
+    // workgroups that keep the full grid's rounds of 2-row wave tiles
+    const int tiles = (V + 1) / 2, waves = kProjThreads / 64;
+    const int rounds = (tiles + kNwgMax * waves - 1) / (kNwgMax * waves);
+    const int nv = std::max(1, std::min(kNwgMax, (tiles + rounds * waves - 1) / (rounds * waves)));
     auto launch = [&] {
       if (wide)
         launch_wide_vocab(EPI_LSE, a, kNwgMax, s);
       else
-        launch_proj(EPI_LSE, a, kNwgMax, rows, s);
+        launch_proj(EPI_LSE, a, nv, rows, s);
     };
     launch();  // warm-up
     CK(hipStreamSynchronize(s));
