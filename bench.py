@@ -37,9 +37,9 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 # scaled by what the same counter reads for a 1 GiB device copy.  Valid only
 # for the kernel sources it was measured on (their sha256); otherwise null.
 TRAFFIC = {
-    "lse": {"fetch_kib": 513396.125, "write_kib": 64.0, "fetch_scale": 1.9999328, "write_scale": 0.9999998,
+    "lse": {"fetch_kib": 513411.2708, "write_kib": 62.6, "fetch_scale": 1.9999342, "write_scale": 0.9999998,
             "sources": ("ee_proj.hip", "ee_device.h", "ee_internal.h", "ee_epi.h"),
-            "sources_sha256": "92f12699fb7077630feeff02fc5818108e7305c067c12d7670967c8721bb965c"},
+            "sources_sha256": "3f6229e5409dd6858b5e0cfaa7572dc8fef849afa1db2f2f06ea32710193d6d7"},
     "wide": {"fetch_kib": 519640.3333, "write_kib": 512.0, "fetch_scale": 1.9999323, "write_scale": 0.9999999,
              "sources": ("ee_wide.hip", "ee_device.h", "ee_internal.h", "ee_epi.h"),
              "sources_sha256": "0c9d53adb7eb2fcd9cbd8ab52e174fb9c3a6bff1017896d510f7017188834da3"},
