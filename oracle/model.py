@@ -404,12 +404,22 @@ def decode_step(model: OracleModel, cache: KVCache, tokens, gamma=None, forced=N
     return tok, e, info
 
 
-def prefill(model: OracleModel, cache: KVCache, prompts, trace: bool = False):
-    """Full-depth backbone pass over every prompt position of sequences 0..B-1.
+def prefill(model: OracleModel, cache: KVCache, prompts, trace: bool = False, exit_tau=None):
+    """Backbone pass over every prompt position of sequences 0..B-1.
 
     Layer-major: each layer runs on all positions, with causal attention over
     the cached keys.  Returns ``(first_tokens [B], info)`` with ``gap`` and
-    ``logits`` of the last position, and ``hidden`` [B, P, L+1, d] with trace.
+    ``logits`` of the last position, ``exit`` [B] (each sequence's exit
+    layer; L without exits) and ``hidden`` [B, P, L+1, d] with trace.
+
+    ``exit_tau`` (thresholds tau_1..tau_{L-1}, scalar broadcasts): River-LLM's
+    sequence-level exit in the prefill (River-LLM explainer, section 6.1: in
+    the prefill all tokens leave at the same layer; section 5.2: the exit fires
+    when the minimum state transition similarity over the tokens exceeds tau).
+    Reading: per sequence, over its prompt's tokens; after layer l < L a
+    sequence still on the backbone exits iff the smallest similarity of its
+    tokens is > tau_l, and its later layers run on the exit copies for every
+    one of its tokens.  None: full depth for every sequence.
     """
     sh = model.shape
     L, H, Hkv, hd = sh.n_layers, sh.n_heads, sh.n_kv_heads, sh.head_dim
@@ -418,44 +428,62 @@ def prefill(model: OracleModel, cache: KVCache, prompts, trace: bool = False):
     pos0 = cache.lens[:B].copy()
     if np.any(pos0 + P > cache.max_seq):
         raise ValueError("cache full")
+    tau = None
+    if exit_tau is not None:
+        tau = np.broadcast_to(np.asarray(exit_tau, dtype=np.float64), (max(L - 1, 0),))
     cos, sin = model.rope(int(pos0.max()) + P)
     h = model.tok_emb[prompts].copy()                 # [B, P, d]
     hidden = [h.copy()] if trace else None
+    exited = np.zeros(B, dtype=bool)
+    e = np.full(B, L, dtype=np.int32)
     group = H // Hkv
     scale = 1.0 / np.sqrt(hd)
     for l in range(1, L + 1):
-        x = rmsnorm(h, model.w(l, "attn_norm"), sh.rms_eps)
-        q = bf16_round(lin(x, model.w(l, "wq"))).reshape(B, P, H, hd)
-        k = bf16_round(lin(x, model.w(l, "wk"))).reshape(B, P, Hkv, hd)
-        v = bf16_round(lin(x, model.w(l, "wv"))).reshape(B, P, Hkv, hd)
-        o = np.empty((B, P, H, hd))
-        for b in range(B):
-            ap = pos0[b] + np.arange(P)
-            c, s = cos[ap][:, None, :], sin[ap][:, None, :]
-            qr = apply_rope(q[b], c, s)
-            kr = apply_rope(k[b], c, s)
-            for t in range(P):
-                cache.store(l, b, int(ap[t]), kr[t], v[b, t])
-            n = int(pos0[b]) + P
-            Kb, Vb = cache.keys(l, b, n)
-            for i in range(H):
-                j = i // group
-                sc = (qr[:, i] @ Kb[j].T) * scale           # [P, n]
-                mask = np.arange(n)[None, :] > ap[:, None]  # causal
-                sc = np.where(mask, -np.inf, sc)
-                pi = np.exp(sc - sc.max(axis=1, keepdims=True))
-                pi /= pi.sum(axis=1, keepdims=True)
-                o[b, :, i] = pi @ Vb[j]
-        o = bf16_round(o.reshape(B, P, H * hd))
-        h = h + lin(o, model.w(l, "wo"))
-        x = rmsnorm(h, model.w(l, "ffn_norm"), sh.rms_eps)
-        a = bf16_round(silu(lin(x, model.w(l, "w_gate"))) * lin(x, model.w(l, "w_up")))
-        h = h + lin(a, model.w(l, "w_down"))
+        h_in = h.copy() if tau is not None else None
+        for use_exit in (False, True):
+            rows = np.nonzero(exited == use_exit)[0]
+            if len(rows) == 0:
+                continue
+            W = model.w_exit if use_exit else model.w
+            hr = h[rows]
+            n = len(rows)
+            x = rmsnorm(hr, model.w(l, "attn_norm"), sh.rms_eps)
+            q = bf16_round(lin(x, W(l, "wq"))).reshape(n, P, H, hd)
+            k = bf16_round(lin(x, W(l, "wk"))).reshape(n, P, Hkv, hd)
+            v = bf16_round(lin(x, W(l, "wv"))).reshape(n, P, Hkv, hd)
+            o = np.empty((n, P, H, hd))
+            for i, b in enumerate(rows):
+                ap = pos0[b] + np.arange(P)
+                c, s_ = cos[ap][:, None, :], sin[ap][:, None, :]
+                qr = apply_rope(q[i], c, s_)
+                kr = apply_rope(k[i], c, s_)
+                for t in range(P):
+                    cache.store(l, b, int(ap[t]), kr[t], v[i, t])
+                nk = int(pos0[b]) + P
+                Kb, Vb = cache.keys(l, b, nk)
+                for hh in range(H):
+                    j = hh // group
+                    sc = (qr[:, hh] @ Kb[j].T) * scale           # [P, nk]
+                    mask = np.arange(nk)[None, :] > ap[:, None]  # causal
+                    sc = np.where(mask, -np.inf, sc)
+                    pi = np.exp(sc - sc.max(axis=1, keepdims=True))
+                    pi /= pi.sum(axis=1, keepdims=True)
+                    o[i, :, hh] = pi @ Vb[j]
+            o = bf16_round(o.reshape(n, P, H * hd))
+            hr = hr + lin(o, W(l, "wo"))
+            x = rmsnorm(hr, model.w(l, "ffn_norm"), sh.rms_eps)
+            a = bf16_round(silu(lin(x, W(l, "w_gate"))) * lin(x, W(l, "w_up")))
+            h[rows] = hr + lin(a, W(l, "w_down"))
+        if tau is not None and l < L:
+            for b in np.nonzero(~exited)[0]:
+                if state_transition_similarity(h_in[b], h[b]).min() > tau[l - 1]:
+                    exited[b] = True
+                    e[b] = l
         if trace:
             hidden.append(h.copy())
     tok, gap, logits = final_head(model, h[:, -1])
     cache.lens[:B] += P
-    info = {"gap": gap, "logits": logits, "h_last": h[:, -1].copy()}
+    info = {"gap": gap, "logits": logits, "h_last": h[:, -1].copy(), "exit": e}
     if trace:
         info["hidden"] = np.stack(hidden, axis=2)
     return tok, info
