@@ -137,6 +137,13 @@ typedef struct ee_model_config {
                           check_every <= 1, exit copies (not EE_EXIT_NONE) and max_batch
                           <= 8 (else EE_ERR_UNSUPPORTED).  The prefill's token stays greedy. */
   uint32_t sample_seed;
+  int32_t prefill_exit; /* 0: the prefill runs every layer on the backbone.  1: River-LLM's
+                           sequence-level exit in the prefill (River-LLM explainer, sections 6.1
+                           and 5.2): the prefill runs layer by layer over all positions, and after
+                           layer l < L a sequence leaves when the smallest state transition
+                           similarity of its prompt's tokens exceeds the model's threshold tau_l;
+                           its later layers run on the exit copies for every token (and write
+                           those K/V slots).  Needs EE_CRIT_STS and exit copies. */
 } ee_model_config;
 
 /* Device pointers of one layer.  Shapes: attn_norm, ffn_norm [d]; wq [H*hd, d];
@@ -219,17 +226,21 @@ ee_status ee_kv_cache_occupancy(const ee_kv_cache *c, uint8_t *counts_host);
 ee_status ee_kv_cache_destroy(ee_kv_cache *c);
 
 /* Prefill: runs sequences 0..batch-1 over P prompt tokens each (host [batch][P]
- * int32, row-major) at full depth with the backbone weights (no exit heads),
- * writing KV slots at positions len_b .. len_b+P-1, then returns the greedy token
- * after the last position in out_tokens_host [batch].  That token is also kept
- * on the device as the next decode input.  last_logits_host: optional host
- * [batch][V] float32 LM-head logits of the last position (NULL: not copied).
+ * int32, row-major) with the backbone weights (no exit heads; with prefill_exit,
+ * River-LLM's sequence-level exit as described at ee_model_config), writing KV
+ * slots at positions len_b .. len_b+P-1, then returns the greedy token after the
+ * last position in out_tokens_host [batch].  That token is also kept on the
+ * device as the next decode input.  last_logits_host: optional host [batch][V]
+ * float32 LM-head logits of the last position (NULL: not copied).
+ * exit_layers_host: optional host [batch], each sequence's prefill exit layer
+ * (L: no exit; always L without prefill_exit).
  * hip_stream: a hipStream_t or NULL (the library's own stream); the call
  * returns after the work has finished.
- * Errors: INVALID_ARG (token out of [0, V), batch out of range), CACHE_FULL. */
+ * Errors: INVALID_ARG (token out of [0, V), batch out of range), CACHE_FULL,
+ * OUT_OF_MEMORY (prefill_exit: per-position buffers of P * batch rows). */
 ee_status ee_prefill(ee_model *m, ee_kv_cache *c, int32_t batch, const int32_t *tokens_host,
                      int32_t P, void *hip_stream, int32_t *out_tokens_host,
-                     float *last_logits_host);
+                     float *last_logits_host, int32_t *exit_layers_host);
 
 /* One decode step for sequences 0..batch-1.
  * in_tokens_host: [batch] input tokens, or NULL to use each sequence's last

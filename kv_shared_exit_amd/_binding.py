@@ -52,7 +52,8 @@ class ModelConfig(C.Structure):
                 ("vocab", C.c_int32), ("group_size", C.c_int32), ("rms_eps", C.c_float),
                 ("rope_theta", C.c_float), ("exit_mode", C.c_int32), ("max_batch", C.c_int32),
                 ("max_positions", C.c_int32), ("criterion", C.c_int32), ("check_every", C.c_int32),
-                ("exit_rule", C.c_int32), ("temperature", C.c_float), ("sample_seed", C.c_uint32)]
+                ("exit_rule", C.c_int32), ("temperature", C.c_float), ("sample_seed", C.c_uint32),
+                ("prefill_exit", C.c_int32)]
 
 
 class LayerWeights(C.Structure):
@@ -93,7 +94,7 @@ def load() -> C.CDLL:
         "ee_kv_cache_read": [P, I32, I32, I32, I32, P, P],
         "ee_kv_cache_occupancy": [P, P],
         "ee_kv_cache_destroy": [P],
-        "ee_prefill": [P, P, I32, P, I32, P, P, P],
+        "ee_prefill": [P, P, I32, P, I32, P, P, P, P],
         "ee_decode_step": [P, P, I32, P, P, P, P, P, P, P],
         "ee_exit_weights_read": [P, I32, I32, I32, I32, P, P],
         "ee_profile_enable": [P, I32],

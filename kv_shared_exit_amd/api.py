@@ -44,7 +44,7 @@ class Model:
     def __init__(self, shape, dev_weights: dict, gamma=None, exit_mode: int = B.EE_EXIT_INT4,
                  max_batch: int = 8, max_positions: int = 4096, criterion: int = B.EE_CRIT_HEAD,
                  check_every: int = 1, exit_rule: int = B.EE_RULE_SEQUENCE, temperature: float = 0.0,
-                 sample_seed: int = 0):
+                 sample_seed: int = 0, prefill_exit: bool = False):
         self.lib = B.load()
         self.shape = shape
         self.w = dev_weights
@@ -52,7 +52,7 @@ class Model:
         cfg = B.ModelConfig(L, shape.d_model, shape.n_heads, shape.n_kv_heads, shape.head_dim,
                             shape.d_ff, shape.vocab, shape.group, shape.rms_eps, shape.rope_theta,
                             exit_mode, max_batch, max_positions, criterion, check_every, exit_rule,
-                            float(temperature), int(sample_seed))
+                            float(temperature), int(sample_seed), int(bool(prefill_exit)))
         layers = (B.LayerWeights * L)()
         for i, lw in enumerate(dev_weights["layers"]):
             for name in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down"):
@@ -156,15 +156,19 @@ def _stream_ptr(stream):
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def prefill(model: Model, cache: KVCache, prompts, stream=None, logits: bool = False):
-    """Prefill; returns the first tokens, or (tokens, last-position logits) with ``logits``."""
+def prefill(model: Model, cache: KVCache, prompts, stream=None, logits: bool = False, exits: bool = False):
+    """Prefill; returns the first tokens, plus the last position's logits with
+    ``logits`` and each sequence's prefill exit layer with ``exits`` (in that
+    order, as a tuple when either is asked for)."""
     prompts = np.ascontiguousarray(prompts, dtype=np.int32)
     batch, P = prompts.shape
     out = np.empty(batch, np.int32)
     lg = np.empty((batch, model.shape.vocab), np.float32) if logits else None
+    ex = np.empty(batch, np.int32) if exits else None
     B.check(model.lib.ee_prefill(model.h, cache.h, batch, B._ptr(prompts), P,
-                                 _stream_ptr(stream), B._ptr(out), B._ptr(lg)))
-    return (out, lg) if logits else out
+                                 _stream_ptr(stream), B._ptr(out), B._ptr(lg), B._ptr(ex)))
+    res = (out,) + ((lg,) if logits else ()) + ((ex,) if exits else ())
+    return res if len(res) > 1 else out
 
 
 def decode_step(model: Model, cache: KVCache, batch: int, tokens=None, forced=None, gamma=None,

@@ -211,6 +211,10 @@ void validate_config(const ee_model_config& c) {
   need(c.check_every >= 0, "check_every must be >= 0");
   need(c.exit_rule == EE_RULE_SEQUENCE || c.exit_rule == EE_RULE_BATCH_MIN, "bad exit_rule");
   need(std::isfinite(c.temperature) && c.temperature >= 0.0f, "temperature must be finite and >= 0");
+  need(c.prefill_exit == 0 || c.prefill_exit == 1, "bad prefill_exit");
+  if (c.prefill_exit)
+    need(c.criterion == EE_CRIT_STS && c.exit_mode != EE_EXIT_NONE,
+         "the prefill's sequence-level exit uses the state transition similarity and exit copies");
   if (c.temperature > 0.0f) {
     need(c.exit_mode != EE_EXIT_NONE && c.criterion == EE_CRIT_HEAD && c.check_every <= 1,
          "sampled decoding drafts from the exit head evaluated after every layer");
@@ -289,10 +293,24 @@ struct Debug {
   bool hidden = false, logits = false;
 };
 
+// One position of a prefill run layer by layer (River-LLM's sequence-level
+// exit, which needs every prompt token's similarity at a layer before the
+// next layer): this call runs layers l0..l1 for the position with its own
+// residual h and normalised input xn ([B][d] each); with sts set, the
+// similarity of each sequence's token at layer l1 (< L) goes there.
+struct PosRun {
+  float* h;
+  uint16_t* xn;
+  float* sts;
+  int l0, l1;
+  bool init;  // embed the position's token first (layer 1)
+};
+
 // Enqueues one position of all B sequences: layers 1..L, exit heads when
 // heads is set, and the final head when final is set (else the lengths advance).
 void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final,
-                      const int32_t* prompt, int P, int t, const Debug& dbg, hipStream_t s) {
+                      const int32_t* prompt, int P, int t, const Debug& dbg, hipStream_t s,
+                      const PosRun* pr = nullptr) {
   const ee_model_config& cf = m->cfg;
   const int L = cf.n_layers, d = cf.d_model, F = cf.d_ff, H = cf.n_heads, Hkv = cf.n_kv_heads;
   const int hd = cf.head_dim, qd = H * hd, kvd = Hkv * hd, nqkv = qd + 2 * kvd;
@@ -317,10 +335,14 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
   };
 
   const size_t pstride = (size_t)kMaxBatch * d;  // elements between partial-sum ranges
-  launch_init(st, prompt, P, t, B, L, m->tok_emb, d, cf.vocab, m->h, m->p_rec,
-              (const uint16_t*)m->lw[0].attn_norm, cf.rms_eps, m->xn, s);
+  float* hh = pr ? pr->h : m->h;        // residual [b][d]
+  uint16_t* xn = pr ? pr->xn : m->xn;   // the next projection's normalised input [b][d]
+  const int l_first = pr ? pr->l0 : 1, l_last = pr ? pr->l1 : L;
+  if (!pr || pr->init)
+    launch_init(st, prompt, P, t, B, L, m->tok_emb, d, cf.vocab, hh, m->p_rec,
+                (const uint16_t*)m->lw[0].attn_norm, cf.rms_eps, xn, s);
   if (dbg.hidden)
-    HIPCHK(hipMemcpy2DAsync(m->dbg_hidden, (size_t)(L + 1) * d * 4, m->h, (size_t)d * 4,
+    HIPCHK(hipMemcpy2DAsync(m->dbg_hidden, (size_t)(L + 1) * d * 4, hh, (size_t)d * 4,
                             (size_t)d * 4, B, hipMemcpyDeviceToDevice, s));
   // row lists: backbone rows run the bf16 weights, exited rows the int4 copy;
   // with unquantised exit copies every row runs the bf16 weights.
@@ -353,7 +375,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
     wa.cnt_i4 = &st->n_ex;
   };
 
-  for (int l = 1; l <= L; ++l) {
+  for (int l = l_first; l <= l_last; ++l) {
     const ee_layer_weights& w = m->lw[l - 1];
     const LayerQ* q = (int4 && l >= 2) ? &m->lq[l - 1] : nullptr;
     const size_t kvoff = (size_t)(l - 1) * c->Bmax * Hkv * c->S * hd;
@@ -377,7 +399,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       }
       a.list_bf = list_bf;
       a.cnt_bf = cnt_bf;
-      a.x = m->xn;  // bf16(rmsnorm(h) * attn_norm)
+      a.x = xn;  // bf16(rmsnorm(h) * attn_norm)
       a.x_stride = d;
       // epilogue: RoPE on q and k, k and v into this position's shared cache slot
       a.cosT = m->d_cos;
@@ -393,7 +415,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       a.hd_log2 = __builtin_ctz(hd);
       a.S = c->S;
       if (wide) {
-        WideArgs wa = wide_args(nqkv, d, m->ww[l - 1].qkv, m->xn, d, m->wide_y, nqkv);
+        WideArgs wa = wide_args(nqkv, d, m->ww[l - 1].qkv, xn, d, m->wide_y, nqkv);
         if (q) wide_i4(wa, q->qkv);
         launch_wide_proj(wa, s);
         launch_wide_qkv(m->wide_y, wa.nr, wa.y_cstride, nqkv, st->all, &st->n_all, B, a, s);
@@ -448,8 +470,9 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       }
       // with the similarity criterion the layer's input stays in h (the
       // residual after attention goes to h2) until the layer's end
-      float* h_mid = heads && sts_crit && l < L && l % every == 0 ? m->h2 : m->h;
-      launch_finish(h_mid, m->h, m->parts, nkc, pstride, B, d, (const uint16_t*)w.ffn_norm, cf.rms_eps, m->xn,
+      const bool sts_pre = pr && pr->sts && l < L;  // the prefill's similarity at this layer
+      float* h_mid = (heads && sts_crit && l < L && l % every == 0) || sts_pre ? m->h2 : hh;
+      launch_finish(h_mid, hh, m->parts, nkc, pstride, B, d, (const uint16_t*)w.ffn_norm, cf.rms_eps, xn,
                     nullptr, nullptr, nullptr, s);
     }
     {
@@ -468,12 +491,12 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       }
       a.list_bf = list_bf;
       a.cnt_bf = cnt_bf;
-      a.x = m->xn;  // bf16(rmsnorm(h) * ffn_norm)
+      a.x = xn;  // bf16(rmsnorm(h) * ffn_norm)
       a.x_stride = d;
       a.y = m->act;
       a.y_stride = F;
       if (wide) {  // gate rows 0..F-1, up rows F..2F-1
-        WideArgs wa = wide_args(2 * F, d, m->ww[l - 1].gu, m->xn, d, m->wide_y, 2 * F);
+        WideArgs wa = wide_args(2 * F, d, m->ww[l - 1].gu, xn, d, m->wide_y, 2 * F);
         if (q) {
           wide_i4(wa, q->gate);
           wa.q4[1] = q->up.codes;
@@ -518,11 +541,11 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       // the next projection's input: the next layer's attention norm, or the
       // final norm before the LM head; bf16(h) for this layer's exit head
       const void* g_next = l < L ? m->lw[l].attn_norm : (const void*)m->final_norm;
-      if (sts_here)  // h = h2 + partials; sts = cos(layer input in h, new h)
-        launch_finish(m->h, m->h2, m->parts, nkc, pstride, B, d, (const uint16_t*)g_next, cf.rms_eps, m->xn,
-                      nullptr, m->h, m->sts, s);
+      if (sts_here || (pr && pr->sts && l < L))  // h = h2 + partials; sts = cos(layer input in h, new h)
+        launch_finish(hh, m->h2, m->parts, nkc, pstride, B, d, (const uint16_t*)g_next, cf.rms_eps, xn,
+                      nullptr, hh, sts_here ? m->sts : pr->sts, s);
       else
-        launch_finish(m->h, m->h, m->parts, nkc, pstride, B, d, (const uint16_t*)g_next, cf.rms_eps, m->xn,
+        launch_finish(hh, hh, m->parts, nkc, pstride, B, d, (const uint16_t*)g_next, cf.rms_eps, xn,
                       head_here ? m->hb : nullptr, nullptr, nullptr, s);
     }
     const bool bmin = cf.exit_rule == EE_RULE_BATCH_MIN;
@@ -578,10 +601,10 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
         }
       }
       launch_decide(DECIDE_HEAD, bmin, st, m->head_part, nv, m->d_gamma, l, L, B, m->p_rec, nullptr, s);
-      if (sampled) launch_sample_draft(st, m->part_s, nv, l, B, m->z, m->xn + (size_t)kMaxBatch * d, d, s);
+      if (sampled) launch_sample_draft(st, m->part_s, nv, l, B, m->z, xn + (size_t)kMaxBatch * d, d, s);
     }
     if (dbg.hidden)
-      HIPCHK(hipMemcpy2DAsync(m->dbg_hidden + (size_t)l * d, (size_t)(L + 1) * d * 4, m->h,
+      HIPCHK(hipMemcpy2DAsync(m->dbg_hidden + (size_t)l * d, (size_t)(L + 1) * d * 4, hh,
                               (size_t)d * 4, (size_t)d * 4, B, hipMemcpyDeviceToDevice, s));
   }
   if (final) {
@@ -591,7 +614,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
     set_seg1(a, m->lm_head, cf.vocab);
     a.list_bf = st->all;
     a.cnt_bf = &st->n_all;
-    a.x = m->xn;  // bf16(rmsnorm(h) * final_norm)
+    a.x = xn;  // bf16(rmsnorm(h) * final_norm)
     a.x_stride = d;
     a.part = m->head_part;
     a.logits = dbg.logits ? m->dbg_logits : nullptr;
@@ -609,7 +632,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       set_seg1(r, m->lm_head, cf.vocab);
       r.list_bf = st->rej;  // pairs (b, 64 + b): the final input and the exit layer's z
       r.cnt_bf = &st->n_rej;
-      r.x = m->xn;
+      r.x = xn;
       r.x_stride = d;
       r.part = m->head_part;
       sampled_args(r);
@@ -1042,7 +1065,8 @@ ee_status ee_kv_cache_destroy(ee_kv_cache* c) {
 }
 
 ee_status ee_prefill(ee_model* m, ee_kv_cache* c, int32_t batch, const int32_t* tokens_host, int32_t P,
-                     void* hip_stream, int32_t* out_tokens_host, float* last_logits_host) {
+                     void* hip_stream, int32_t* out_tokens_host, float* last_logits_host,
+                     int32_t* exit_layers_host) {
   return guard([&] {
     check_model(m);
     if (!c || c->m != m) fail(EE_ERR_INVALID_ARG, "cache does not belong to the model");
@@ -1073,8 +1097,45 @@ ee_status ee_prefill(ee_model* m, ee_kv_cache* c, int32_t batch, const int32_t* 
       Debug last;
       last.logits = last_logits_host != nullptr;
       if (last.logits && !m->dbg_logits) m->dbg_logits = m->alloc<float>((size_t)kMaxBatch * m->cfg.vocab);
-      for (int t = 0; t < P; ++t)
-        enqueue_position(m, c, batch, false, t == P - 1, m->d_prompt, P, t, t == P - 1 ? last : dbg, s);
+      const int L = m->cfg.n_layers;
+      if (m->cfg.prefill_exit && L > 1) {
+        // River-LLM's sequence-level exit: layer by layer over every position,
+        // each position with its own residual and normalised input; after a
+        // layer, a sequence leaves when the smallest similarity of its tokens
+        // exceeds the layer's threshold, and its later layers run on the copies
+        const size_t rows = (size_t)P * batch;
+        float* hP = nullptr;
+        uint16_t* xP = nullptr;
+        float* sP = nullptr;
+        HIPCHK(hipMalloc(&hP, rows * m->cfg.d_model * 4));
+        HIPCHK(hipMalloc(&xP, rows * m->cfg.d_model * 2));
+        HIPCHK(hipMalloc(&sP, (rows + kMaxBatch) * 4));
+        float* smin = sP + rows;
+        if (m->gamma.size())
+          HIPCHK(hipMemcpyAsync(m->d_gamma, m->gamma.data(), m->gamma.size() * 4, hipMemcpyHostToDevice, s));
+        for (int l = 1; l <= L; ++l) {
+          for (int t = 0; t < P; ++t) {
+            const size_t off = (size_t)t * batch * m->cfg.d_model;
+            PosRun pr{hP + off, xP + off, l < L ? sP + (size_t)t * batch : nullptr, l, l, l == 1};
+            const bool fin = l == L && t == P - 1;
+            enqueue_position(m, c, batch, false, fin, m->d_prompt, P, t, fin ? last : dbg, s, &pr);
+          }
+          if (l < L) {
+            launch_advance(c->lens, batch, s, -P);  // the next layer starts at the first position again
+            launch_sts_min(sP, P, batch, smin, s);
+            launch_decide(DECIDE_STS, false, m->st, nullptr, 0, m->d_gamma, l, L, batch, nullptr, smin, s);
+          }
+        }
+        HIPCHK(hipGetLastError());
+        HIPCHK(hipStreamSynchronize(s));
+        (void)hipFree(hP);
+        (void)hipFree(xP);
+        (void)hipFree(sP);
+      } else {
+        for (int t = 0; t < P; ++t)
+          enqueue_position(m, c, batch, false, t == P - 1, m->d_prompt, P, t, t == P - 1 ? last : dbg, s);
+      }
+      HIPCHK(hipMemcpyAsync(m->h_out + kMaxBatch, m->st->e, batch * 4, hipMemcpyDeviceToHost, s));
       HIPCHK(hipMemcpyAsync(m->h_out, m->st->out_tok, batch * 4, hipMemcpyDeviceToHost, s));
       if (last.logits)
         HIPCHK(hipMemcpyAsync(last_logits_host, m->dbg_logits, (size_t)batch * m->cfg.vocab * 4,
@@ -1082,6 +1143,7 @@ ee_status ee_prefill(ee_model* m, ee_kv_cache* c, int32_t batch, const int32_t* 
       HIPCHK(hipStreamSynchronize(s));
       m->ev_used = 0;
       std::memcpy(out_tokens_host, m->h_out, batch * 4);
+      if (exit_layers_host) std::memcpy(exit_layers_host, m->h_out + kMaxBatch, batch * 4);
       for (int b = 0; b < batch; ++b) c->hlens[b] += P;
     });
   });

@@ -202,7 +202,10 @@ void launch_sample_final(StepState* st, const float* part_s, int nwg, int B, int
                          float itau, uint32_t seed, hipStream_t s);
 void launch_resample_final(StepState* st, const float* part_s, int nwg, int B, int V, int32_t* lens,
                            hipStream_t s);
-void launch_advance(int32_t* lens, int B, hipStream_t s);
+void launch_advance(int32_t* lens, int B, hipStream_t s, int delta = 1);
+// out[b] = min over t < P of sts[t * B + b]: each sequence's smallest
+// similarity over its prompt's tokens (the prefill's sequence-level exit).
+void launch_sts_min(const float* sts, int P, int B, float* out, hipStream_t s);
 void launch_quantize(const uint16_t* w, int N, int K, int G, int row0, uint32_t* codes,
                      uint16_t* scales, hipStream_t s);
 void launch_unpack(const uint32_t* codes, const uint16_t* scales, int K, int G, int row0, int nrows,

@@ -514,12 +514,27 @@ void launch_final(StepState* st, const float* part, int nwg, int B, int V, int32
   hipLaunchKernelGGL(final_kernel, dim3(B), dim3(64), 0, s, st, part, nwg, B, V, lens, advance);
 }
 
-__global__ void advance_kernel(int32_t* lens, int B) {
-  if ((int)threadIdx.x < B) lens[threadIdx.x] += 1;
+__global__ void advance_kernel(int32_t* lens, int B, int delta) {
+  if ((int)threadIdx.x < B) lens[threadIdx.x] += delta;
 }
 
-void launch_advance(int32_t* lens, int B, hipStream_t s) {
-  hipLaunchKernelGGL(advance_kernel, dim3(1), dim3(64), 0, s, lens, B);
+void launch_advance(int32_t* lens, int B, hipStream_t s, int delta) {
+  hipLaunchKernelGGL(advance_kernel, dim3(1), dim3(64), 0, s, lens, B, delta);
+}
+
+// out[b] = min over positions t < P of sts[t * B + b] (one wave per sequence).
+__global__ void sts_min_kernel(const float* sts, int P, int B, float* out) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  float m = INFINITY;
+  for (int t = lane; t < P; t += 64) m = fminf(m, sts[(size_t)t * B + b]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) m = fminf(m, __shfl_xor(m, o));
+  if (lane == 0) out[b] = m;
+}
+
+void launch_sts_min(const float* sts, int P, int B, float* out, hipStream_t s) {
+  if (!sts || !out || P < 1 || B < 1 || B > kMaxBatch) throw std::logic_error("sts_min: bad arguments");
+  hipLaunchKernelGGL(sts_min_kernel, dim3(B), dim3(64), 0, s, sts, P, B, out);
 }
 
 }  // namespace ee

@@ -409,3 +409,99 @@ def test_sampled_low_temperature_equals_greedy(gpu):
         if not np.array_equal(tg, tc):
             break
     assert checked >= 4
+
+
+# ---------------------------------------------------------------------------
+# River-LLM's sequence-level exit in the prefill
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name,batch,P", [("odd", 3, 9), ("hd64", 4, 40), ("tiny", 2, 70)])
+def test_prefill_sequence_exit_against_oracle(gpu, name, batch, P):
+    """The prefill runs layer by layer; after layer l a sequence leaves when the
+    smallest similarity of its prompt's tokens exceeds tau_l, and its later
+    layers run on the int4 copies for every token.  Thresholds are placed
+    between the sequences' token minima of the oracle's full-depth prefill
+    (each at least 1e-3 away from every minimum), at a different layer per
+    sequence where possible; exit layers equal the oracle's, and the last
+    position's logits, the token and every K/V slot match it."""
+    from kv_shared_exit_amd import api, _binding as Bd
+    from parity import maxrel, TOL
+    from oracle import model as om
+    from oracle.numerics import from_bf16_bits
+    sh = SHAPES[name]
+    L = sh.n_layers
+    w = synth.make_weights(sh, 13)
+    prompts = np.random.default_rng(31).integers(0, sh.vocab, (batch, P)).astype(np.int32)
+    orc = om.OracleModel(sh, w)
+    oc = om.KVCache(sh, batch, P + 1)
+    _, full = om.prefill(orc, oc, prompts, trace=True)
+    hid = full["hidden"]                      # [B, P, L+1, d]
+    mins = np.stack([om.state_transition_similarity(hid[:, :, l - 1], hid[:, :, l]).min(axis=1)
+                     for l in range(1, L)], axis=1)   # [B, L-1]
+    tau = np.full(L - 1, 2.0)
+    for l in range(1, L):                     # the first layer whose minima split the batch
+        v = np.sort(mins[:, l - 1])
+        gaps = np.diff(v)
+        if len(gaps) and gaps.max() > 2e-3:
+            k = int(np.argmax(gaps))
+            tau[l - 1] = 0.5 * (v[k] + v[k + 1])
+            break
+    assert np.all(np.abs(mins - tau[None, :]) > 1e-3)
+    oc = om.KVCache(sh, batch, P + 1)
+    to, info = om.prefill(orc, oc, prompts, exit_tau=tau)
+    assert len(set(info["exit"].tolist())) >= 2, info["exit"]
+    dev = api.upload_weights(w)
+    m = api.Model(sh, dev, gamma=tau, max_batch=batch, max_positions=P + 1, criterion=Bd.EE_CRIT_STS,
+                  prefill_exit=True)
+    c = api.KVCache(m, batch, P + 1, track=True)
+    try:
+        tg, lg, eg = api.prefill(m, c, prompts, logits=True, exits=True)
+        np.testing.assert_array_equal(eg, info["exit"])
+        for b in range(batch):
+            assert maxrel(lg[b], info["logits"][b]) <= TOL
+            band = max(1e-2, 2 * float(np.abs(lg[b].astype(np.float64) - info["logits"][b]).max()))
+            if info["gap"][b] > band:
+                assert tg[b] == to[b]
+            for l in range(1, L + 1):
+                k, v = c.read(l, b, 0, P)
+                kr = oc.K[l - 1, b, :, :P].transpose(1, 0, 2)
+                vr = oc.V[l - 1, b, :, :P].transpose(1, 0, 2)
+                assert maxrel(from_bf16_bits(k), kr) <= TOL and maxrel(from_bf16_bits(v), vr) <= TOL, (b, l)
+        assert np.all(c.occupancy()[:, :batch, :P] == 1)
+        assert list(c.lengths()[:batch]) == [P] * batch
+        # decoding continues from the prefill's cache and token
+        t1, e1 = api.decode_step(m, c, batch)
+        assert np.all((e1 >= 1) & (e1 <= L))
+    finally:
+        c.close()
+        m.close()
+
+
+def test_prefill_exit_off_and_unreachable_thresholds_equal_full_depth(gpu):
+    """prefill_exit with thresholds a similarity cannot exceed runs every layer on
+    the backbone: the layer-by-layer prefill equals the position-by-position one
+    (tokens, exit layers, logits within rounding, K/V)."""
+    from kv_shared_exit_amd import api, _binding as Bd
+    from parity import maxrel, TOL
+    from oracle.numerics import from_bf16_bits
+    sh = SHAPES["odd"]
+    w = synth.make_weights(sh, 14)
+    dev = api.upload_weights(w)
+    prompts = np.random.default_rng(2).integers(0, sh.vocab, (3, 12)).astype(np.int32)
+    out = []
+    for pe in (False, True):
+        m = api.Model(sh, dev, gamma=1.0, max_batch=3, max_positions=13, criterion=Bd.EE_CRIT_STS, prefill_exit=pe)
+        c = api.KVCache(m, 3, 13)
+        try:
+            t, lg, e = api.prefill(m, c, prompts, logits=True, exits=True)
+            kv = [c.read(l, b, 0, 12) for l in (1, sh.n_layers) for b in range(3)]
+            out.append((t, lg, e, kv))
+        finally:
+            c.close()
+            m.close()
+    (t0, l0, e0, kv0), (t1, l1, e1, kv1) = out
+    assert np.all(e0 == sh.n_layers) and np.all(e1 == sh.n_layers)
+    np.testing.assert_array_equal(t0, t1)
+    for b in range(3):
+        assert maxrel(l1[b], l0[b]) <= 1e-5
+    for (k0, v0), (k1, v1) in zip(kv0, kv1):
+        assert maxrel(from_bf16_bits(k1), from_bf16_bits(k0)) <= 1e-2
