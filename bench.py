@@ -121,12 +121,18 @@ def cpu_baseline(wl, weights, exit_layer, ctx, criterion="head", every=1):
 
 def prefill(api, model, cache, prompts, stream, t0, chunk=512):
     """Prefill in chunks of positions (the library appends each chunk after the
-    cached positions), logging progress on long prompts."""
+    cached positions), logging progress on long prompts; with the prefill's
+    sequence-level exit the whole prompt is one call (the decision takes the
+    minimum over all of its tokens).  Returns the exit layers of the last call."""
     P = prompts.shape[1]
+    if model.cfg.prefill_exit:
+        chunk = P
+    ex = None
     for p0 in range(0, P, chunk):
-        api.prefill(model, cache, prompts[:, p0:p0 + chunk], stream=stream)
+        _, ex = api.prefill(model, cache, prompts[:, p0:p0 + chunk], stream=stream, exits=True)
         if P > chunk:
             log(f"prefill positions {min(p0 + chunk, P)}/{P} ({time.time() - t0:.0f}s)")
+    return ex
 
 
 def baselines(api, wl, weights, dev, stream, exits, W, K2, ms_main, criterion=0, thresholds=None, every=1,
@@ -186,6 +192,8 @@ def main():
     ap.add_argument("--temperature", type=float, default=0.0,
                     help="sampled decoding with AdaDecode's verification at this temperature (secondary "
                          "line; 0: greedy)")
+    ap.add_argument("--prefill-exit", action="store_true",
+                    help="River-LLM's sequence-level exit in the prefill (with --criterion sts)")
     ap.add_argument("--no-baselines", action="store_true",
                     help="skip the full-depth and bf16-exit-copy comparison runs")
     ap.add_argument("--copy-probe", action="store_true",
@@ -217,6 +225,9 @@ def main():
         if thresholds is None:
             print(f"no similarity thresholds for {wl.name} (synth/calibration/{wl.name}_sts.json)", file=sys.stderr)
             sys.exit(2)
+    if args.prefill_exit and not sts:
+        print("--prefill-exit needs --criterion sts (the prefill's exit uses the token similarities)", file=sys.stderr)
+        sys.exit(2)
     alpha = synth.load_alpha(wl)
     # a calibrated workload without calibrated exit-head scales (the 34B shape:
     # its float64 oracle does not fit host memory) runs the exit layers of its
@@ -234,13 +245,18 @@ def main():
     every = max(1, args.check_every)
     rule = Bd.EE_RULE_BATCH_MIN if args.exit_rule == "batch-min" else Bd.EE_RULE_SEQUENCE
     model = api.Model(sh, dev, gamma=thresholds, max_batch=B, max_positions=S, criterion=crit, check_every=every,
-                      exit_rule=rule, temperature=args.temperature, sample_seed=wl.seed_prompts)
+                      exit_rule=rule, temperature=args.temperature, sample_seed=wl.seed_prompts,
+                      prefill_exit=args.prefill_exit)
     cache = api.KVCache(model, B, S)
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
     log(f"model ready ({time.time() - t0:.0f}s)")
     prompts = synth.make_prompts(wl)
-    prefill(api, model, cache, prompts, stream, t0)
+    torch.cuda.synchronize()
+    tp0 = time.perf_counter()
+    pexits = prefill(api, model, cache, prompts, stream, t0)
+    torch.cuda.synchronize()
+    prefill_s = time.perf_counter() - tp0
     log(f"prefill {B}x{P} done ({time.time() - t0:.0f}s)")
 
     exits, toks = [], []
@@ -377,6 +393,8 @@ def main():
                  "exit_hist": hist.tolist(),
                  "head_launches_per_step": round(head_launches / K, 2)},
         "cpu_baseline": None,
+        "prefill": {"seconds": round(prefill_s, 3), "positions": P, "batch": B,
+                    "exit_layers": None if pexits is None else [int(x) for x in pexits]},
     }
     if wl.name != "8b":
         out["metric"] = out["metric"].replace("(8B shape, b=8)", f"({wl.name} shape, b={B})")
@@ -401,6 +419,8 @@ def main():
     if rule == Bd.EE_RULE_BATCH_MIN:
         out["metric"] += ", batch-minimum exits"
         out["config"]["workload"] += ", batch-minimum exit rule"
+    if args.prefill_exit:
+        out["config"]["workload"] += ", sequence-level exit in the prefill (minimum token similarity)"
     if args.temperature > 0:
         out["metric"] += f", sampled (temperature {args.temperature}, verified drafts)"
         out["config"]["workload"] += (f", sampled decoding at temperature {args.temperature} with AdaDecode's "
