@@ -519,12 +519,24 @@ struct MmaRing {
   static constexpr int D = BF ? (P == 2 ? 1 : 2) : (P == 2 ? 1 : NG == 4 ? 2 : 4);
 };
 
-// Waves sharing a 16-row tile (splitting its 128-column blocks): enough that
-// the tiles of a column range occupy its waves, at most one block per wave.
+// Waves sharing a 16-row tile (splitting its 128-column blocks), a power of
+// two up to the block count: the split with the fewest block steps per wave
+// over the whole pass (rounds of the range's waves x blocks per wave), and of
+// those the fewest rounds (each round waits out a memory latency and a
+// cross-wave reduction).
 __host__ __device__ inline int mma_wpt(int nfull, int ntiles, int nwaves) {
-  int w = 1;
-  while (w < kWaves && 2 * w <= nfull && (long long)ntiles * w < nwaves) w *= 2;
-  return w;
+  int best = 1;
+  long long best_cost = -1, best_rounds = 0;
+  for (int w = 1; w <= kWaves && w <= nfull; w *= 2) {
+    const long long rounds = ((long long)ntiles * w + nwaves - 1) / nwaves;
+    const long long cost = rounds * ((nfull + w - 1) / w);
+    if (best_cost < 0 || cost < best_cost || (cost == best_cost && rounds < best_rounds)) {
+      best = w;
+      best_cost = cost;
+      best_rounds = rounds;
+    }
+  }
+  return best;
 }
 
 // MFMA pass over 16-row tiles for one weight format: BF true reads the bf16
