@@ -280,11 +280,12 @@ void set_seg1(ProjArgs& a, const void* w, int N) {
 
 // Attention work split: one wave per run of `tpw` 64-position tiles of a
 // (sequence, kv head); tpw grows with the context so that the launch keeps
-// about 2048 waves (and its partials stay a few percent of the K/V bytes).
+// about kAttnWaves waves (and its partials stay a few percent of the K/V bytes).
+constexpr long long kAttnWaves = 2048;
 void attn_split(int S, int B, int Hkv, int* tpw, int* nch) {
   const int tiles = (S + 63) / 64;
   int t = 1;
-  while (t < tiles && (long long)B * Hkv * ((tiles + t - 1) / t) > 2048) t *= 2;
+  while (t < tiles && (long long)B * Hkv * ((tiles + t - 1) / t) > kAttnWaves) t *= 2;
   *tpw = t;
   *nch = (tiles + t - 1) / t;
 }
