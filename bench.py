@@ -37,12 +37,12 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 # scaled by what the same counter reads for a 1 GiB device copy.  Valid only
 # for the kernel sources it was measured on (their sha256); otherwise null.
 TRAFFIC = {
-    "lse": {"fetch_kib": 513411.2708, "write_kib": 62.6, "fetch_scale": 1.9999342, "write_scale": 0.9999998,
+    "lse": {"fetch_kib": 513409.2500, "write_kib": 62.6, "fetch_scale": 1.9999337, "write_scale": 0.9999999,
             "sources": ("ee_proj.hip", "ee_device.h", "ee_internal.h", "ee_epi.h"),
-            "sources_sha256": "3f6229e5409dd6858b5e0cfaa7572dc8fef849afa1db2f2f06ea32710193d6d7"},
-    "wide": {"fetch_kib": 519640.3333, "write_kib": 512.0, "fetch_scale": 1.9999323, "write_scale": 0.9999999,
+            "sources_sha256": "103c9d3e5ac06464f52a5b324eb5ff39f008cdf3e86936110df8cf98c02a6173"},
+    "wide": {"fetch_kib": 519711.0833, "write_kib": 512.0, "fetch_scale": 1.9999313, "write_scale": 1.0000000,
              "sources": ("ee_wide.hip", "ee_device.h", "ee_internal.h", "ee_epi.h"),
-             "sources_sha256": "0c9d53adb7eb2fcd9cbd8ab52e174fb9c3a6bff1017896d510f7017188834da3"},
+             "sources_sha256": "2979e14089340b485f6aa67f125d7a8e18c593fdac40b4614bdc7469e75f8e81"},
 }
 # the workloads whose shape (128256 x 4096) the counters were taken at
 TRAFFIC_SHAPE = (128256, 4096)
