@@ -7,6 +7,13 @@
 //                                over a V x d bf16 matrix and `rows` staged rows
 //   ee_probe wide V d rows reps  the same GEMV for 9..64 rows on matrix cores
 //                                (wide_vocab_kernel<EPI_LSE> over the tiled copy)
+//   ee_probe proj EPI N K nbf ni4 g reps
+//                                a decoder projection (EPI: swiglu = gate/up
+//                                with its epilogue, part = O or down with
+//                                float32 partials) of N output rows over K
+//                                inputs, nbf rows on the bf16 weights and ni4
+//                                on the int4 G128 copy, on a grid of g
+//                                workgroups
 //   ee_probe copy MiB            one copy kernel reading and writing MiB each
 //
 // Prints the mean launch time (HIP events on the launch stream).
@@ -37,7 +44,9 @@ __global__ void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ d
 }
 
 static int usage() {
-  std::fprintf(stderr, "usage: ee_probe lse V d rows reps | ee_probe wide V d rows reps | ee_probe copy MiB\n");
+  std::fprintf(stderr,
+               "usage: ee_probe lse V d rows reps | ee_probe wide V d rows reps | "
+               "ee_probe proj swiglu|part N K nbf ni4 g reps | ee_probe copy MiB\n");
   return 2;
 }
 
@@ -65,6 +74,81 @@ int main(int argc, char** argv) {
     float ms = 0;
     CK(hipEventElapsedTime(&ms, e0, e1));
     std::printf("copy %zu MiB: %.2f us, %.1f GB/s (read + write)\n", mib, 1e3 * ms, 2.0 * n * 16 / (ms * 1e6));
+    return 0;
+  }
+  if (!std::strcmp(argv[1], "proj")) {
+    if (argc < 9) return usage();
+    const bool swiglu = !std::strcmp(argv[2], "swiglu");
+    if (!swiglu && std::strcmp(argv[2], "part")) return usage();
+    const int N = std::atoi(argv[3]), K = std::atoi(argv[4]), nbf = std::atoi(argv[5]), ni4 = std::atoi(argv[6]);
+    const int g = std::atoi(argv[7]), reps = std::atoi(argv[8]);
+    constexpr int G = 128;
+    if (N < 16 || N % 16 || K < G || K % G || nbf < 0 || ni4 < 0 || nbf + ni4 < 1 || nbf + ni4 > 8 || g < 1 ||
+        g > kNwgMax || reps < 1)
+      return usage();
+    if (swiglu && !proj_fits(K, nbf + ni4)) return usage();
+    const int P = swiglu ? 2 : 1;
+    uint16_t *W, *x, *sc;
+    uint32_t* codes;
+    void* y;
+    int32_t* lists;
+    const size_t wn = (size_t)N * K, cn = (size_t)N * K / 8, sn = (size_t)N * (K / G);
+    CK(hipMalloc(&W, P * wn * 2));
+    CK(hipMalloc(&codes, P * cn * 4));
+    CK(hipMalloc(&sc, P * sn * 2));
+    CK(hipMalloc(&x, (size_t)kMaxBatch * K * 2));
+    const size_t yn = swiglu ? (size_t)kMaxBatch * N * 2 : (size_t)8 * kMaxBatch * N * 4;
+    CK(hipMalloc(&y, yn));
+    CK(hipMalloc(&lists, 4 * kMaxBatch * 4));
+    CK(hipMemsetAsync(W, 0x3c, P * wn * 2, s));  // bf16 ~0.0115
+    CK(hipMemsetAsync(codes, 0x99, P * cn * 4, s));
+    CK(hipMemsetAsync(sc, 0x3c, P * sn * 2, s));
+    CK(hipMemsetAsync(x, 0x3c, (size_t)kMaxBatch * K * 2, s));
+    // rows 0..nbf-1 on bf16, nbf..nbf+ni4-1 on int4: lists then counts
+    std::vector<int32_t> hl(4 * kMaxBatch, 0);
+    for (int i = 0; i < nbf; ++i) hl[i] = i;
+    for (int i = 0; i < ni4; ++i) hl[kMaxBatch + i] = nbf + i;
+    hl[2 * kMaxBatch] = nbf;
+    hl[3 * kMaxBatch] = ni4;
+    CK(hipMemcpyAsync(lists, hl.data(), hl.size() * 4, hipMemcpyHostToDevice, s));
+    ProjArgs a{};
+    a.N = N;
+    a.K = K;
+    a.G = G;
+    a.nseg = 1;
+    a.wb[0] = W;
+    a.seg_end[0] = a.seg_end[1] = a.seg_end[2] = N;
+    a.q4 = codes;
+    a.s4 = sc;
+    if (swiglu) {
+      a.wb2 = W + wn;
+      a.q4b = codes + cn;
+      a.s4b = sc + sn;
+    }
+    a.x = x;
+    a.x_stride = K;
+    a.list_bf = lists;
+    a.list_i4 = lists + kMaxBatch;
+    a.cnt_bf = lists + 2 * kMaxBatch;
+    a.cnt_i4 = lists + 3 * kMaxBatch;
+    a.y = y;
+    a.y_stride = N;
+    a.y_cstride = kMaxBatch * N;
+    const int epi = swiglu ? EPI_SWIGLU : EPI_PART;
+    int nkc = 1;
+    auto launch = [&] { nkc = launch_proj(epi, a, g, nbf + ni4, s); };
+    launch();  // warm-up
+    CK(hipStreamSynchronize(s));
+    CK(hipEventRecord(e0, s));
+    for (int r = 0; r < reps; ++r) launch();
+    CK(hipEventRecord(e1, s));
+    CK(hipEventSynchronize(e1));
+    float ms = 0;
+    CK(hipEventElapsedTime(&ms, e0, e1));
+    const double us = 1e3 * ms / reps;
+    const double bytes = (nbf ? 2.0 * P * wn : 0.0) + (ni4 ? P * (cn * 4.0 + sn * 2.0) : 0.0);
+    std::printf("proj %s N=%d K=%d bf=%d i4=%d g=%d ranges=%d: %.2f us per launch, %.1f GB/s algorithmic\n", argv[2],
+                N, K, nbf, ni4, g, nkc, us, bytes / us / 1e3);
     return 0;
   }
   const bool wide = !std::strcmp(argv[1], "wide");
