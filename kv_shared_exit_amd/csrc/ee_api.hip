@@ -46,6 +46,19 @@ T* dalloc(size_t n) {
   return (T*)p;
 }
 
+// Device memory held for the length of one call, freed on every exit path
+// (hipFree waits for the work queued on it).
+template <typename T>
+struct CallBuffer {
+  T* p = nullptr;
+  explicit CallBuffer(size_t n) : p(dalloc<T>(n)) {}
+  ~CallBuffer() {
+    if (p) (void)hipFree(p);
+  }
+  CallBuffer(const CallBuffer&) = delete;
+  CallBuffer& operator=(const CallBuffer&) = delete;
+};
+
 struct Q4 {
   uint32_t* codes = nullptr;
   uint16_t* scales = nullptr;
@@ -1105,12 +1118,11 @@ ee_status ee_prefill(ee_model* m, ee_kv_cache* c, int32_t batch, const int32_t* 
         // layer, a sequence leaves when the smallest similarity of its tokens
         // exceeds the layer's threshold, and its later layers run on the copies
         const size_t rows = (size_t)P * batch;
-        float* hP = nullptr;
-        uint16_t* xP = nullptr;
-        float* sP = nullptr;
-        HIPCHK(hipMalloc(&hP, rows * m->cfg.d_model * 4));
-        HIPCHK(hipMalloc(&xP, rows * m->cfg.d_model * 2));
-        HIPCHK(hipMalloc(&sP, (rows + kMaxBatch) * 4));
+        CallBuffer<float> hbuf(rows * m->cfg.d_model), sbuf(rows + kMaxBatch);
+        CallBuffer<uint16_t> xbuf(rows * m->cfg.d_model);
+        float* hP = hbuf.p;
+        uint16_t* xP = xbuf.p;
+        float* sP = sbuf.p;
         float* smin = sP + rows;
         if (m->gamma.size())
           HIPCHK(hipMemcpyAsync(m->d_gamma, m->gamma.data(), m->gamma.size() * 4, hipMemcpyHostToDevice, s));
@@ -1129,9 +1141,6 @@ ee_status ee_prefill(ee_model* m, ee_kv_cache* c, int32_t batch, const int32_t* 
         }
         HIPCHK(hipGetLastError());
         HIPCHK(hipStreamSynchronize(s));
-        (void)hipFree(hP);
-        (void)hipFree(xP);
-        (void)hipFree(sP);
       } else {
         for (int t = 0; t < P; ++t)
           enqueue_position(m, c, batch, false, t == P - 1, m->d_prompt, P, t, t == P - 1 ? last : dbg, s);
@@ -1253,22 +1262,12 @@ ee_status ee_exit_weights_read(const ee_model* m, int32_t layer, int32_t which, 
     const int K = src->K, G = cf.group_size;
     ee_model* mm = const_cast<ee_model*>(m);
     with_sticky(mm, [&] {
-      int8_t* tmp = dalloc<int8_t>((size_t)nrows * K);
-      uint16_t* stmp = nullptr;
-      hipError_t e0 = hipMalloc((void**)&stmp, (size_t)nrows * (K / G) * 2);
-      if (e0 != hipSuccess) {
-        (void)hipFree(tmp);
-        HIPCHK(e0);
-      }
-      launch_unpack(src->codes, src->scales, K, G, off + row0, nrows, tmp, stmp, mm->own);
-      hipError_t e1 = hipStreamSynchronize(mm->own);
-      hipError_t e2 = hipMemcpy(codes_host, tmp, (size_t)nrows * K, hipMemcpyDeviceToHost);
-      hipError_t e3 = hipMemcpy(scales_host, stmp, (size_t)nrows * (K / G) * 2, hipMemcpyDeviceToHost);
-      (void)hipFree(tmp);
-      (void)hipFree(stmp);
-      HIPCHK(e1);
-      HIPCHK(e2);
-      HIPCHK(e3);
+      CallBuffer<int8_t> tmp((size_t)nrows * K);
+      CallBuffer<uint16_t> stmp((size_t)nrows * (K / G));
+      launch_unpack(src->codes, src->scales, K, G, off + row0, nrows, tmp.p, stmp.p, mm->own);
+      HIPCHK(hipStreamSynchronize(mm->own));
+      HIPCHK(hipMemcpy(codes_host, tmp.p, (size_t)nrows * K, hipMemcpyDeviceToHost));
+      HIPCHK(hipMemcpy(scales_host, stmp.p, (size_t)nrows * (K / G) * 2, hipMemcpyDeviceToHost));
     });
   });
 }
