@@ -336,20 +336,11 @@ void launch_attention(const AttnArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Exit decision and active-sequence compaction.
 // ---------------------------------------------------------------------------
-constexpr int kHeadThreads = 512;              // decide / final: one wave per row
+constexpr int kHeadThreads = 512;              // decide: eight waves
 constexpr int kHeadWaves = kHeadThreads / 64;
-constexpr int kPartPerLane = kNwgMax / 64;    // partials a lane merges (nwg <= kNwgMax)
-
-// Loads the (max, sum exp) partials k = lane + 64j of list position i, all
-// requested before any is used (absent ones: (-inf, 0), which merge as no-ops).
-__device__ __forceinline__ void load_lse_parts(const float* part, int nwg, int i, int lane,
-                                               float2 (&v)[kPartPerLane]) {
-#pragma unroll
-  for (int j = 0; j < kPartPerLane; ++j) {
-    const int k = lane + 64 * j;
-    v[j] = k < nwg ? *(const float2*)(part + ((size_t)k * kMaxBatch + i) * 4) : make_float2(-INFINITY, 0.0f);
-  }
-}
+constexpr int kPartPerLane = kNwgMax / 64;    // partials a lane of final merges (nwg <= kNwgMax)
+constexpr int kPartPerWave = kNwgMax / kHeadWaves;  // partials one wave of decide merges per position
+static_assert(kMaxBatch == 64 && kPartPerWave == 64, "decide: the lane split assumes 64 positions and 64 partials per wave");
 
 // MODE DECIDE_STS: the value of a row is its state transition similarity
 // sts[b] instead of the exit head's p; DECIDE_FORCED: no value, only forced
@@ -364,55 +355,87 @@ __global__ __launch_bounds__(kHeadThreads) void decide_kernel(StepState* st, con
   constexpr bool STS = MODE == DECIDE_STS;
   __shared__ int sx[kMaxBatch];
   __shared__ float pv[kMaxBatch];
+  __shared__ float2 red[kHeadWaves][kMaxBatch];
   __shared__ int sn;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  // the first row of each wave is requested before the row count is known
-  // (list positions below kMaxBatch are always in bounds); the wave's other
-  // rows (batches above 8) are requested together once the count is known
-  constexpr int kRowsPerWave = kMaxBatch / kHeadWaves;
-  float2 v[kRowsPerWave][kPartPerLane];
-  if constexpr (MODE == DECIDE_HEAD) load_lse_parts(part, nwg, w, lane, v[0]);
+  // DECIDE_HEAD, the (max, sum exp) partials of every list position into
+  // red[wave][position] (merged over the waves below).  All loads are
+  // requested before the row count is known (positions below the batch, or
+  // below 8, are always in bounds; absent partials merge as no-ops).
+  if constexpr (MODE == DECIDE_HEAD) {
+    if (B <= kHeadWaves) {
+      // wave w takes position w, its lanes the partials k = lane + 64j
+      float2 v[kPartPerLane];
+#pragma unroll
+      for (int j = 0; j < kPartPerLane; ++j) {
+        const int k = lane + 64 * j;
+        v[j] = k < nwg ? *(const float2*)(part + ((size_t)k * kMaxBatch + w) * 4) : make_float2(-INFINITY, 0.0f);
+      }
+#pragma unroll
+      for (int j = 1; j < kPartPerLane; ++j) lse_merge(v[0].x, v[0].y, v[j].x, v[j].y);
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const float m2 = __shfl_xor(v[0].x, o), s2 = __shfl_xor(v[0].y, o);
+        lse_merge(v[0].x, v[0].y, m2, s2);
+      }
+      if (lane < kHeadWaves) red[lane][w] = lane == 0 ? v[0] : make_float2(-INFINITY, 0.0f);
+    } else {
+      // wave w takes the partials k = w + 8t (t < 64) of every position.
+      // With Bp the batch rounded up to a power of two, lane (kk, i) =
+      // (lane / Bp, lane % Bp) takes position i and t = kk + (64 / Bp) j for
+      // j < Bp, so the lanes of one load read adjacent positions of a few
+      // workgroups' partials (contiguous runs, not a line per lane); each lane
+      // merges its Bp values as a tree, then the 64 / Bp lanes of a position
+      // combine theirs.
+      const int lg = 32 - __builtin_clz(B - 1);  // log2(Bp), uniform
+      const int bp = 1 << lg;
+      const int pos = lane & (bp - 1), kk = lane >> lg;
+      float2 v[kPartPerWave];
+#pragma unroll
+      for (int j = 0; j < kPartPerWave; ++j) {
+        const int k = w + kHeadWaves * (kk + (64 >> lg) * j);
+        v[j] = (j < bp && k < nwg) ? *(const float2*)(part + ((size_t)k * kMaxBatch + pos) * 4)
+                                   : make_float2(-INFINITY, 0.0f);
+      }
+#pragma unroll
+      for (int h = kPartPerWave / 2; h >= 1; h >>= 1) {
+        if (2 * h <= bp) {  // uniform: the levels of a tree over bp values
+#pragma unroll
+          for (int j = 0; j < h; ++j) lse_merge(v[j].x, v[j].y, v[j + h].x, v[j + h].y);
+        }
+      }
+      for (int o = bp; o < 64; o <<= 1) {
+        const float m2 = __shfl_xor(v[0].x, o), s2 = __shfl_xor(v[0].y, o);
+        lse_merge(v[0].x, v[0].y, m2, s2);
+      }
+      if (kk == 0) red[w][pos] = v[0];
+    }
+  }
   if ((int)threadIdx.x < B) sx[threadIdx.x] = st->exited[threadIdx.x];
   if (threadIdx.x == 0) sn = min(max(st->n_act, 0), B);
   __syncthreads();
   const int n = sn;
-  if constexpr (MODE == DECIDE_HEAD) {
-    if (n > kHeadWaves) {
-#pragma unroll
-      for (int r = 1; r < kRowsPerWave; ++r) load_lse_parts(part, nwg, min(w + r * kHeadWaves, n - 1), lane, v[r]);
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r) {
-    const int i = w + r * kHeadWaves;
-    if (i >= n) break;  // uniform over the wave
+  // one thread per list position (n <= kMaxBatch < kHeadThreads)
+  const int i = threadIdx.x;
+  if (i < n) {
     const int b = st->act[i];
     float p = 0.0f;
-    if constexpr (MODE == DECIDE_FORCED) {
-      p = 0.0f;
-    } else if constexpr (STS) {
+    if constexpr (STS) {
       p = sts[b];
-    } else {
-      float m = -INFINITY, s = 0.0f;
+    } else if constexpr (MODE == DECIDE_HEAD) {
+      float m = -INFINITY, sum = 0.0f;
 #pragma unroll
-      for (int j = 0; j < kPartPerLane; ++j) lse_merge(m, s, v[r][j].x, v[r][j].y);
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float m2 = __shfl_xor(m, o), s2 = __shfl_xor(s, o);
-        lse_merge(m, s, m2, s2);
-      }
-      p = 1.0f / s;
+      for (int ww = 0; ww < kHeadWaves; ++ww) lse_merge(m, sum, red[ww][i].x, red[ww][i].y);
+      p = 1.0f / sum;
     }
-    if (lane == 0) {
-      const int f = st->forced[b];
-      const bool own = MODE != DECIDE_FORCED && !batch_min && p > gamma[layer - 1];
-      const bool ex = f > 0 ? (layer == f) : own;
-      if (p_rec && MODE != DECIDE_FORCED) p_rec[(layer - 1) * kMaxBatch + b] = p;
-      pv[i] = p;
-      if (ex) {
-        sx[b] = 1;
-        st->e[b] = layer;
-      }
+    const int f = st->forced[b];
+    const bool own = MODE != DECIDE_FORCED && !batch_min && p > gamma[layer - 1];
+    const bool ex = f > 0 ? (layer == f) : own;
+    if (p_rec && MODE != DECIDE_FORCED) p_rec[(layer - 1) * kMaxBatch + b] = p;
+    pv[i] = p;
+    if (ex) {
+      sx[b] = 1;
+      st->e[b] = layer;
     }
   }
   if (MODE != DECIDE_FORCED && batch_min) {
@@ -459,6 +482,7 @@ __global__ __launch_bounds__(kHeadThreads) void decide_kernel(StepState* st, con
 void launch_decide(int mode, bool batch_min, StepState* st, const float* part, int nwg, const float* gamma,
                    int layer, int L, int B, float* p_rec, const float* sts, hipStream_t s) {
   const int bm = batch_min ? 1 : 0;
+  if (B < 1 || B > kMaxBatch) throw std::logic_error("decide: batch out of range");
   switch (mode) {
     case DECIDE_STS:
       if (!sts) throw std::logic_error("decide: no similarities");
