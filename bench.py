@@ -202,7 +202,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU: the early-exit decode step is data-parallel "
-              "(every sequence is independent) and this build runs on one MI355X only; "
+              "(every sequence is independent) and the library runs on one MI355X; "
               f"--gpus {args.gpus} is not supported.", file=sys.stderr)
         sys.exit(2)
 

@@ -64,7 +64,7 @@ typedef int32_t ee_status;
 #define EE_ERR_CACHE_FULL (-4)    /* a sequence would grow beyond the cache's max_seq */
 #define EE_ERR_SHAPE (-5)         /* the model shape is not supported by the kernels */
 #define EE_ERR_NOT_WRITTEN (-6)   /* a KV slot read back was never written (occupancy on) */
-#define EE_ERR_UNSUPPORTED (-7)   /* a feature not available in this build */
+#define EE_ERR_UNSUPPORTED (-7)   /* a feature the library does not implement */
 
 #define EE_EXIT_INT4 0 /* exit copies are the int4 group-quantised layers */
 #define EE_EXIT_BF16 1 /* exit copies are the backbone layers themselves (test mode) */
