@@ -56,7 +56,10 @@ dimension; RoPE rotates pairs (i, i + hd/2) by pos * theta^(-2i/hd) with a
 cos/sin table computed in float64 and rounded to float32; silu(g) = g/(1+e^-g).
 
 Pins (``tests/test_oracle_*.py``): attention, RMSNorm, SiLU, RoPE and softmax
-against torch CPU library routines and closed forms; gamma > 1 equals a plain
+against torch CPU library routines and closed forms; the exit head against
+closed forms (identity and permutation heads over a diagonal E, inputs placed
+off the bf16 grid so that each of its two roundings shows, T = 0 giving 1/V,
+no dependence on the final norm's gain, E and not the input embedding); gamma > 1 equals a plain
 decoder written from torch library calls; gamma <= 0 equals a plain decoder
 whose layers 2..L are the dequantised copies; unquantised exit copies equal
 full depth for any schedule; every KV slot is written exactly once; a sequence

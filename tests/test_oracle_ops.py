@@ -95,3 +95,125 @@ def test_exit_head_matches_torch():
     z = torch.from_numpy(bf16_round((hb @ T.T).numpy()))
     ref = torch.softmax(z @ E.T, dim=-1).max(dim=-1).values.numpy()
     np.testing.assert_allclose(p, ref, rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# The exit head pinned by closed forms (AdaDecode explainer, section 2.1: the
+# head's logits are h^(l) T^(l) E^T with E the LM-head matrix and no norm in
+# between; section 2.2: its top-1 probability is what gamma is compared with).
+# Each case builds weights for which the logits are known exactly, with
+# - tok_emb (E_in) unlike lm_head (E): a head that used E_in fails;
+# - h far from unit RMS and a final-norm gain of 3: a head that applied the
+#   final RMSNorm (or its gain) fails;
+# - values placed off the bf16 grid where a rounding matters: a head that
+#   dropped either rounding (of h, or of z = T h) fails.
+# ---------------------------------------------------------------------------
+def _head_model(d, V, T, E, gain=3.0):
+    from synth import ModelShape
+    sh = ModelShape(2, d, 1, 1, 32, 32, V, 32)
+
+    def bits(a):
+        return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+    rng = np.random.default_rng(11)
+    w = {"tok_emb": bits(rng.standard_normal((V, d))), "lm_head": bits(E),
+         "final_norm": bits(np.full(d, gain)), "layers": [{"head_T": bits(T)}, {}]}
+    return om.OracleModel(sh, w)
+
+
+def _p_closed(logits):
+    """max softmax by fsum over exp(l - max): the textbook definition."""
+    m = max(logits)
+    return 1.0 / math.fsum(math.exp(v - m) for v in logits)
+
+
+def _diag_E(d, V, c):
+    E = np.zeros((V, d))
+    E[np.arange(d), np.arange(d)] = c
+    return E
+
+
+def test_exit_head_identity_head_closed_form():
+    """T = I, E = c [I; 0], h on the bf16 grid: logits are c h_v for v < d and 0 beyond."""
+    d, V, c = 32, 80, 2.0
+    h = (np.arange(d) - 11.0) * 0.25          # on the bf16 grid, RMS ~ 2.9
+    m = _head_model(d, V, np.eye(d), _diag_E(d, V, c))
+    p, logits = om.exit_head(m, 1, h[None])
+    want = np.concatenate([c * h, np.zeros(V - d)])
+    np.testing.assert_array_equal(logits[0], want)
+    assert abs(p[0] - _p_closed(want.tolist())) <= 1e-15
+
+
+def test_exit_head_orientation_of_T():
+    """T a permutation (T[j, pi(j)] = 1): z_j = h_pi(j), so logit v is c h_pi(v) (z_j = sum_i T[j, i] h_i)."""
+    d, V, c = 32, 48, 1.0
+    pi = np.random.default_rng(4).permutation(d)
+    T = np.zeros((d, d))
+    T[np.arange(d), pi] = 1.0
+    h = np.arange(d, dtype=np.float64) * 0.5
+    m = _head_model(d, V, T, _diag_E(d, V, c))
+    _, logits = om.exit_head(m, 1, h[None])
+    np.testing.assert_array_equal(logits[0, :d], c * h[pi])
+    # the transposed map would put h_v at pi(v): differs for a non-involution
+    assert not np.array_equal(logits[0, :d], c * h[np.argsort(pi)])
+
+
+def test_exit_head_rounds_its_input_to_bf16():
+    """z_j = bf16(h_j) + h_{j+32} for j < 32 with h_j = m_j 2^-7 + 2^-9 (m_j in
+    [128, 255]) and h_{j+32} = 2^-8: rounding h first gives bf16(h_j) = m_j 2^-7
+    (a quarter unit rounds down), and the sum m_j 2^-7 + 2^-8 is the midpoint
+    between two bf16 values, which rounds to the even one (torch's cast of the
+    exact value).  Without the first rounding the sum lies above the midpoint
+    and always rounds up, so the logits of even m_j differ."""
+    d, V, c = 64, 100, 8.0
+    mv = 128 + (np.arange(32) * 37) % 128
+    h = np.concatenate([mv * 2.0 ** -7 + 2.0 ** -9, np.full(32, 2.0 ** -8)])
+    T = np.eye(d)
+    T[np.arange(32), np.arange(32) + 32] = 1.0
+    m = _head_model(d, V, T, _diag_E(d, V, c))
+    p, logits = om.exit_head(m, 1, h[None])
+    zs = torch.from_numpy((mv * 2.0 ** -7 + 2.0 ** -8).astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(zs[mv % 2 == 0], mv[mv % 2 == 0] * 2.0 ** -7)   # ties went to even
+    z = np.concatenate([zs, np.full(32, 2.0 ** -8)])
+    want = np.concatenate([c * z, np.zeros(V - d)])
+    np.testing.assert_array_equal(logits[0], want)
+    assert abs(p[0] - _p_closed(want.tolist())) <= 1e-15
+
+
+def test_exit_head_rounds_z_to_bf16():
+    """T = 1.5 I and h_v = m_v 2^-7 with odd m_v in [129, 255]: 1.5 m_v needs 9
+    significant bits, so z_v = bf16(1.5 h_v) (nearest, ties to even, from
+    torch's float32 -> bfloat16 cast of the exact value) differs from 1.5 h_v."""
+    d, V, c = 64, 90, 2.0
+    mv = 129 + 2 * (np.arange(d) % 64)
+    h = mv * 2.0 ** -7
+    m = _head_model(d, V, 1.5 * np.eye(d), _diag_E(d, V, c))
+    p, logits = om.exit_head(m, 1, h[None])
+    z = torch.from_numpy((1.5 * h).astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert np.all(z != 1.5 * h)
+    want = np.concatenate([c * z, np.zeros(V - d)])
+    np.testing.assert_array_equal(logits[0], want)
+    assert abs(p[0] - _p_closed(want.tolist())) <= 1e-15
+
+
+def test_exit_head_zero_T_gives_uniform():
+    """T = 0: every logit is 0 and p = 1 / V exactly."""
+    d, V = 32, 1000
+    rng = np.random.default_rng(5)
+    m = _head_model(d, V, np.zeros((d, d)), rng.standard_normal((V, d)))
+    p, logits = om.exit_head(m, 1, rng.standard_normal((3, d)))
+    assert np.all(logits == 0)
+    np.testing.assert_array_equal(p, np.full(3, 1.0 / V))
+
+
+def test_exit_head_ignores_final_norm_gain():
+    """The head has no final RMSNorm: changing the final-norm gain leaves p and the logits unchanged."""
+    d, V = 32, 200
+    rng = np.random.default_rng(6)
+    T = rng.standard_normal((d, d)) * 0.2
+    E = rng.standard_normal((V, d))
+    h = rng.standard_normal((2, d)) * 7
+    p1, l1 = om.exit_head(_head_model(d, V, T, E, gain=1.0), 1, h)
+    p2, l2 = om.exit_head(_head_model(d, V, T, E, gain=0.25), 1, h)
+    np.testing.assert_array_equal(l1, l2)
+    np.testing.assert_array_equal(p1, p2)
