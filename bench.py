@@ -92,31 +92,82 @@ def step_bytes(sh, exits, ctx, B, head_bytes=True, every=1):
     return tot, heads
 
 
-def cpu_baseline(wl, weights, exit_layer, ctx, criterion="head", every=1):
-    """The oracle's decode speed: one decode step of one sequence at the workload's shape,
-    with a synthetic (seeded) KV context of ``ctx`` positions and a forced exit layer."""
-    from threadpoolctl import threadpool_info
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, weights, exits, ctx, criterion="head", every=1, budget_s=30.0):
+    """The oracle's decode speed on the host: decode steps of the workload's
+    whole batch at its shape, over a synthetic (seeded) KV context of ``ctx``
+    positions per sequence, with the exit layers the GPU's first timed step
+    took (forced; the criterion is still evaluated).  BLAS threads are set to
+    every core of the process's affinity set.  As many steps as fit in about
+    ``budget_s`` seconds (at least one) are timed."""
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import model as om
     sh = wl.shape
+    B = len(exits)
+    cores = len(os.sched_getaffinity(0))
     orc = om.OracleModel(sh, weights, cache_f64=False)
-    for l in range(exit_layer + 1, sh.n_layers + 1):
+    for l in range(int(np.min(exits)) + 1, sh.n_layers + 1):
         for name in om.LINEAR:
             orc.quantized(l, name)            # model setup, like the GPU's ee_create_model
-    cache = om.KVCache(sh, 1, ctx + 2)
+    cache = om.KVCache(sh, B, ctx + 64)
     rng = np.random.default_rng(4242)
     kv = rng.standard_normal(cache.K[:, :, :, :ctx].shape, dtype=np.float32)
-    cache.K[:, :, :, :ctx] = kv.astype(np.float32)
-    cache.V[:, :, :, :ctx] = kv[:, :, :, ::-1].astype(np.float32)
-    cache.lens[0] = ctx
-    t0 = time.perf_counter()
-    om.decode_step(orc, cache, [1], gamma=wl.gamma, forced=[exit_layer], criterion=criterion, check_every=every)
-    dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": round(1.0 / dt, 5), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"1 decode step of 1 sequence, {sh.n_layers}-layer d{sh.d_model} shape, "
-                       f"synthetic {ctx}-position KV context, forced exit after layer {exit_layer}, "
+    cache.K[:, :, :, :ctx] = kv
+    cache.V[:, :, :, :ctx] = kv[:, :, :, ::-1]
+    del kv
+    cache.lens[:B] = ctx
+    toks = np.arange(1, B + 1)
+    n, dt = 0, 0.0
+    with threadpool_limits(limits=cores, user_api="blas"):
+        info = threadpool_info()
+        while n == 0 or (dt / n) * (n + 1) <= budget_s and n < 8:
+            t0 = time.perf_counter()
+            toks, _, _ = om.decode_step(orc, cache, toks, gamma=wl.gamma, forced=exits, criterion=criterion,
+                                        check_every=every)
+            dt += time.perf_counter() - t0
+            n += 1
+    blas = [f"{p.get('internal_api')} {p.get('version')} ({p.get('num_threads')} threads)"
+            for p in info if p.get("user_api") == "blas"]
+    return {"value": round(B * n / dt, 5), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{n} decode step(s) of the batch of {B}, {sh.n_layers}-layer d{sh.d_model} shape, "
+                       f"synthetic {ctx}-position KV context per sequence, exit layers of the GPU's first timed "
+                       f"step forced {[int(x) for x in exits]}, "
                        f"{'similarity' if criterion == 'sts' else 'exit-head'} criterion evaluated; "
-                       f"{dt:.1f} s, float64 numpy")}
+                       f"{dt:.1f} s, float64 numpy"
+                       + (f" (8 steps would exceed the ~{budget_s:.0f} s sample)" if n < 8 else "")),
+            "cpu_model": _cpu_model(), "blas": blas, "affinity_cores": cores}
+
+
+def hbm_copy_ceiling(reps=10):
+    """Device-to-device copy of 1 GiB (torch's copy kernel), timed with events on
+    the current stream: read + written bytes over the mean time, the streaming
+    ceiling a bandwidth-bound kernel is measured against."""
+    import torch
+    x = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    y.copy_(x)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    gbs = 2 * x.numel() * 4 / (ms * 1e-3) / 1e9
+    del x, y
+    return {"kind": "1 GiB device copy (read + write)", "GBps": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "ms": round(ms, 4)}
 
 
 def prefill(api, model, cache, prompts, stream, t0, chunk=512):
@@ -274,9 +325,12 @@ def main():
     tok_in0 = last.copy()
     # timed region: the production path (each step replays its captured graph)
     torch.cuda.synchronize()
+    step_ms = []
     t_start = time.perf_counter()
     for s in range(K):
-        t, e = step(W + s)
+        ts = time.perf_counter()
+        t, e = step(W + s)     # returns after the step's outputs are on the host
+        step_ms.append(1e3 * (time.perf_counter() - ts))
         toks.append(t.copy())
         exits.append(e.copy())
     torch.cuda.synchronize()
@@ -371,6 +425,9 @@ def main():
         "steps": K,
         "warmup": W,
         "ms_per_step": round(1e3 * t_el / K, 4),
+        "step_ms": {"median": round(float(np.median(step_ms)), 4),
+                    "p99": round(float(np.percentile(step_ms, 99)), 4),
+                    "min": round(float(np.min(step_ms)), 4), "max": round(float(np.max(step_ms)), 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -435,15 +492,14 @@ def main():
         out["roofline"] = {"bound": "hbm", "kernel": "whole decode step (no exit-head GEMV under this criterion)",
                            "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(step_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    out["hbm_copy_ceiling"] = hbm_copy_ceiling()
     if not args.no_baselines:
         out["speedup"] = baselines(api, wl, weights, dev, stream, exits, W, min(K, 40), 1e3 * t_el / K,
                                    criterion=crit, thresholds=thresholds, every=every, rule=rule)
         log(f"baselines done ({time.time() - t0:.0f}s)")
     del dev
     if not args.no_cpu_baseline:
-        ex = int(round(mean_exit))
-        out["cpu_baseline"] = cpu_baseline(wl, weights, min(max(ex, 1), sh.n_layers), P,
-                                           criterion=args.criterion, every=every)
+        out["cpu_baseline"] = cpu_baseline(wl, weights, exits[0], P, criterion=args.criterion, every=every)
         log(f"cpu baseline done ({time.time() - t0:.0f}s)")
     print(json.dumps(out), flush=True)
 

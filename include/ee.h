@@ -173,7 +173,12 @@ typedef struct ee_step_debug {
   float *gap;    /* [batch]: top-1 minus top-2 final logit (+inf when V == 1) */
 } ee_step_debug;
 
-/* Creates a model.  cfg, w: host structs describing borrowed device weights.
+/* Creates a model: the backbone plus its exit layers ("River-LLM 深度解析",
+ * section 4.2: each exit layer is a 4-bit copy of the original layer, about 75%
+ * smaller; section 8.1: the copy is made by quantising the original layer's
+ * weights with a max/7 scale, rounded and clamped to [-8, 7]), and the exit
+ * heads T_l of the AdaDecode explainer, section 2.1.
+ * cfg, w: host structs describing borrowed device weights.
  * gamma: host [n_layers - 1] per-layer thresholds (gamma_l, or tau_l with
  * EE_CRIT_STS), or NULL for 0.75 everywhere.
  * Builds the int4 exit copies of layers 2..L on the device (synchronously).
@@ -182,15 +187,22 @@ typedef struct ee_step_debug {
 ee_status ee_create_model(const ee_model_config *cfg, const ee_weights *w,
                           const float *gamma, ee_model **out);
 
-/* Destroys a model (NULL is allowed).  Caches created from it must be destroyed first. */
+/* Destroys a model (NULL is allowed) and everything it owns (int4 copies,
+ * workspaces, captured graphs).  Caches created from it must be destroyed
+ * first (else INVALID_ARG, nothing is freed). */
 ee_status ee_destroy_model(ee_model *m);
 
-/* Device bytes a KV cache of max_batch sequences and max_seq positions needs:
- * K and V, each [L][max_batch][Hkv][max_seq][hd] bf16, plus the per-sequence lengths. */
+/* The shared KV cache ("River-LLM 深度解析", section 4.3: the backbone and the
+ * exit layers read and write one cache, so an exited token still leaves K/V for
+ * every layer; section 8.2: get/update/store of one (layer, position) slot).
+ * Device bytes a KV cache of max_batch sequences and max_seq positions needs:
+ * K and V, each [L][max_batch][Hkv][max_seq][hd] bf16, plus the per-sequence
+ * lengths and last output tokens (512 bytes). */
 ee_status ee_kv_cache_bytes(const ee_model *m, int32_t max_batch, int32_t max_seq,
                             size_t *bytes);
 
-/* Creates an empty cache (all lengths 0).  dev_buf: caller-owned device buffer of
+/* Creates an empty shared cache (all lengths 0; "River-LLM 深度解析", section
+ * 4.3).  dev_buf: caller-owned device buffer of
  * at least ee_kv_cache_bytes bytes (kept alive until destroy), or NULL to let the
  * library allocate.  max_batch <= model max_batch, max_seq <= max_positions.
  * flags: EE_KV_TRACK_OCCUPANCY keeps a u8 write counter per slot. */
@@ -199,33 +211,46 @@ ee_status ee_kv_cache_create(ee_model *m, int32_t max_batch, int32_t max_seq,
                              ee_kv_cache **out);
 
 /* Sets the length of sequence seq (or of all sequences when seq == -1) to 0 and
- * clears its occupancy counters. */
+ * clears its occupancy counters and its kept output token. */
 ee_status ee_kv_cache_reset(ee_kv_cache *c, int32_t seq);
 
 /* Discards the last n positions of sequence seq (all sequences when seq == -1):
  * the length drops by n and, with occupancy tracking, the dropped slots' write
- * counters are cleared, so the positions can be written again.  This is the
+ * counters are cleared, so the positions can be written again.  With n > 0 the
+ * sequence's kept output token is dropped too (it followed the last dropped
+ * position): the next ee_decode_step must pass its input token.  This is the
  * rollback of a rejected token ("大语言模型解码加速：自适应层并行机制解析",
  * section 3.1: on a failed verification the KV entries after the last valid
  * token are discarded).  INVALID_ARG if n < 0 or n exceeds a length. */
 ee_status ee_kv_cache_rollback(ee_kv_cache *c, int32_t seq, int32_t n);
 
-/* Copies the max_batch sequence lengths to lens_host. */
+/* Copies the max_batch sequence lengths (positions written per sequence) to
+ * lens_host [max_batch] int32.  Host-side only: no device work. */
 ee_status ee_kv_cache_lengths(const ee_kv_cache *c, int32_t *lens_host);
 
 /* Copies K and V of positions [pos0, pos0+n) of one (1-based) layer and sequence
- * to host buffers, each [n][Hkv][hd] bf16 (uint16 bit patterns).  With occupancy
- * tracking, returns NOT_WRITTEN if any slot in the range was never written. */
+ * to host buffers, each [n][Hkv][hd] bf16 (uint16 bit patterns).  This is the
+ * cache's "get" ("River-LLM 深度解析", section 8.2: get returns nothing for a
+ * (layer, position) never stored): with occupancy tracking, NOT_WRITTEN if any
+ * slot in the range was never written (nothing is copied).  INVALID_ARG for a
+ * layer, sequence or range outside the cache. */
 ee_status ee_kv_cache_read(const ee_kv_cache *c, int32_t layer, int32_t seq, int32_t pos0,
                            int32_t n, void *k_host, void *v_host);
 
-/* Copies the occupancy counters [L][max_batch][max_seq] (u8) to the host.
+/* Copies the occupancy counters [L][max_batch][max_seq] (u8) to the host: the
+ * number of stores into each slot ("River-LLM 深度解析", section 8.2: one store
+ * per layer and position, whichever copy ran it).
  * UNSUPPORTED if the cache was created without EE_KV_TRACK_OCCUPANCY. */
 ee_status ee_kv_cache_occupancy(const ee_kv_cache *c, uint8_t *counts_host);
 
+/* Destroys a cache (NULL is allowed) after the work queued on the model's
+ * stream has finished; frees the library-owned buffer, never dev_buf, and
+ * releases the decode-step graphs captured for it. */
 ee_status ee_kv_cache_destroy(ee_kv_cache *c);
 
-/* Prefill: runs sequences 0..batch-1 over P prompt tokens each (host [batch][P]
+/* Prefill, the first of the two phases of generation ("River-LLM 深度解析",
+ * section 6.1: the prompt is processed as a whole, then tokens are generated
+ * one at a time).  Runs sequences 0..batch-1 over P prompt tokens each (host [batch][P]
  * int32, row-major) with the backbone weights (no exit heads; with prefill_exit,
  * River-LLM's sequence-level exit as described at ee_model_config), writing KV
  * slots at positions len_b .. len_b+P-1, then returns the greedy token after the
@@ -242,9 +267,16 @@ ee_status ee_prefill(ee_model *m, ee_kv_cache *c, int32_t batch, const int32_t *
                      int32_t P, void *hip_stream, int32_t *out_tokens_host,
                      float *last_logits_host, int32_t *exit_layers_host);
 
-/* One decode step for sequences 0..batch-1.
+/* One decode step, the second phase ("River-LLM 深度解析", section 6.1: each
+ * generated token decides its exit by itself), for sequences 0..batch-1: the
+ * per-layer exit decision of the AdaDecode explainer, sections 2.1-2.2 (or the
+ * criterion the model was created with) and the exit layers of "River-LLM
+ * 深度解析", sections 4.1-4.3, as described at the top of this file.
  * in_tokens_host: [batch] input tokens, or NULL to use each sequence's last
- *   output token kept on the device (from ee_prefill or the previous step).
+ *   output token, which this cache keeps on the device (from the last ee_prefill
+ *   or ee_decode_step on this cache that included the sequence).  NULL is
+ *   INVALID_ARG while some sequence b < batch has no kept token: none produced
+ *   on this cache yet, or reset or rolled back since.
  * forced_exit_host: [batch] or NULL; 0 lets the criterion decide, 1..L forces
  *   the exit layer (the criterion still runs; its decision is overridden).
  * gamma_host: [L-1] thresholds for this step (gamma_l or tau_l), or NULL for

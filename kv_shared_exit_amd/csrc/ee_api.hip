@@ -157,9 +157,11 @@ struct ee_kv_cache {
   ee_model* m = nullptr;
   int Bmax = 0, S = 0;
   uint16_t *K = nullptr, *V = nullptr;
-  int32_t* lens = nullptr;  // device
+  int32_t* lens = nullptr;      // device [Bmax]
+  int32_t* next_tok = nullptr;  // device [Bmax]: each sequence's last output token, its next input
   uint8_t* occ = nullptr;
   std::vector<int32_t> hlens;
+  std::vector<uint8_t> next_ok;  // whether next_tok[b] is the token after the sequence's last position
   void* owned = nullptr;
 };
 
@@ -924,7 +926,7 @@ ee_status ee_kv_cache_bytes(const ee_model* m, int32_t max_batch, int32_t max_se
     if (max_seq < 1 || max_seq > m->cfg.max_positions) fail(EE_ERR_INVALID_ARG, "max_seq out of range");
     const size_t kv = (size_t)m->cfg.n_layers * max_batch * m->cfg.n_kv_heads * max_seq *
                       m->cfg.head_dim * 2;
-    *bytes = 2 * kv + 256;
+    *bytes = 2 * kv + 512;
   });
 }
 
@@ -949,11 +951,12 @@ ee_status ee_kv_cache_create(ee_model* m, int32_t max_batch, int32_t max_seq, vo
           base = dalloc<char>(need);
           c->owned = base;
         }
-        const size_t kv = (need - 256) / 2;
+        const size_t kv = (need - 512) / 2;
         c->K = (uint16_t*)base;
         c->V = (uint16_t*)(base + kv);
         c->lens = (int32_t*)(base + 2 * kv);
-        HIPCHK(hipMemsetAsync(c->lens, 0, 256, m->own));
+        c->next_tok = (int32_t*)(base + 2 * kv + 256);
+        HIPCHK(hipMemsetAsync(c->lens, 0, 512, m->own));
         if (flags & EE_KV_TRACK_OCCUPANCY) {
           const size_t n = (size_t)m->cfg.n_layers * max_batch * max_seq;
           c->occ = dalloc<uint8_t>(n);
@@ -961,6 +964,7 @@ ee_status ee_kv_cache_create(ee_model* m, int32_t max_batch, int32_t max_seq, vo
         }
         HIPCHK(hipStreamSynchronize(m->own));
         c->hlens.assign(max_batch, 0);
+        c->next_ok.assign(max_batch, 0);
       } catch (...) {
         if (c->owned) (void)hipFree(c->owned);
         if (c->occ) (void)hipFree(c->occ);
@@ -981,7 +985,10 @@ ee_status ee_kv_cache_reset(ee_kv_cache* c, int32_t seq) {
     ee_model* m = c->m;
     with_sticky(m, [&] {
       const int lo = seq < 0 ? 0 : seq, hi = seq < 0 ? c->Bmax : seq + 1;
-      for (int b = lo; b < hi; ++b) c->hlens[b] = 0;
+      for (int b = lo; b < hi; ++b) {
+        c->hlens[b] = 0;
+        c->next_ok[b] = 0;
+      }
       HIPCHK(hipMemcpyAsync(c->lens, c->hlens.data(), c->Bmax * 4, hipMemcpyHostToDevice, m->own));
       if (c->occ)
         for (int l = 0; l < m->cfg.n_layers; ++l)
@@ -1006,6 +1013,7 @@ ee_status ee_kv_cache_rollback(ee_kv_cache* c, int32_t seq, int32_t n) {
     with_sticky(m, [&] {
       for (int b = lo; b < hi; ++b) {
         c->hlens[b] -= n;
+        c->next_ok[b] = 0;  // the token after the new last position is not kept
         if (c->occ)
           for (int l = 0; l < m->cfg.n_layers; ++l)
             HIPCHK(hipMemsetAsync(c->occ + ((size_t)l * c->Bmax + b) * c->S + c->hlens[b], 0, n, m->own));
@@ -1145,6 +1153,7 @@ ee_status ee_prefill(ee_model* m, ee_kv_cache* c, int32_t batch, const int32_t* 
         for (int t = 0; t < P; ++t)
           enqueue_position(m, c, batch, false, t == P - 1, m->d_prompt, P, t, t == P - 1 ? last : dbg, s);
       }
+      HIPCHK(hipMemcpyAsync(c->next_tok, m->st->out_tok, batch * 4, hipMemcpyDeviceToDevice, s));
       HIPCHK(hipMemcpyAsync(m->h_out + kMaxBatch, m->st->e, batch * 4, hipMemcpyDeviceToHost, s));
       HIPCHK(hipMemcpyAsync(m->h_out, m->st->out_tok, batch * 4, hipMemcpyDeviceToHost, s));
       if (last.logits)
@@ -1154,7 +1163,10 @@ ee_status ee_prefill(ee_model* m, ee_kv_cache* c, int32_t batch, const int32_t* 
       m->ev_used = 0;
       std::memcpy(out_tokens_host, m->h_out, batch * 4);
       if (exit_layers_host) std::memcpy(exit_layers_host, m->h_out + kMaxBatch, batch * 4);
-      for (int b = 0; b < batch; ++b) c->hlens[b] += P;
+      for (int b = 0; b < batch; ++b) {
+        c->hlens[b] += P;
+        c->next_ok[b] = 1;
+      }
     });
   });
 }
@@ -1180,6 +1192,12 @@ ee_status ee_decode_step(ee_model* m, ee_kv_cache* c, int32_t batch, const int32
     if (gamma_host)
       for (int l = 0; l < L - 1; ++l)
         if (!std::isfinite(gamma_host[l])) fail(EE_ERR_INVALID_ARG, "gamma must be finite");
+    if (!in_tokens_host)
+      for (int b = 0; b < batch; ++b)
+        if (!c->next_ok[b])
+          fail(EE_ERR_INVALID_ARG, "sequence " + std::to_string(b) +
+                                       " has no kept output token (none produced yet, or reset or rolled "
+                                       "back since): pass in_tokens");
     for (int b = 0; b < batch; ++b)
       if (c->hlens[b] + 1 > c->S) fail(EE_ERR_CACHE_FULL, "sequence " + std::to_string(b) + " is full");
     with_sticky(m, [&] {
@@ -1200,6 +1218,8 @@ ee_status ee_decode_step(ee_model* m, ee_kv_cache* c, int32_t batch, const int32
       for (int l = 0; l < L - 1; ++l) m->h_gamma[l] = gamma_host ? gamma_host[l] : m->gamma[l];
       if (in_tokens_host)
         HIPCHK(hipMemcpyAsync(m->st->tok, m->h_in, batch * 4, hipMemcpyHostToDevice, s));
+      else  // this cache's last outputs (the model's step state is shared by its caches)
+        HIPCHK(hipMemcpyAsync(m->st->tok, c->next_tok, batch * 4, hipMemcpyDeviceToDevice, s));
       HIPCHK(hipMemcpyAsync(m->st->forced, m->h_in + kMaxBatch, batch * 4, hipMemcpyHostToDevice, s));
       if (L > 1)
         HIPCHK(hipMemcpyAsync(m->d_gamma, m->h_gamma, (L - 1) * 4, hipMemcpyHostToDevice, s));
@@ -1208,6 +1228,7 @@ ee_status ee_decode_step(ee_model* m, ee_kv_cache* c, int32_t batch, const int32
       } else {
         replay_step(m, c, batch, s);
       }
+      HIPCHK(hipMemcpyAsync(c->next_tok, m->st->out_tok, batch * 4, hipMemcpyDeviceToDevice, s));
       HIPCHK(hipMemcpyAsync(m->h_out, m->st->out_tok, batch * 4, hipMemcpyDeviceToHost, s));
       HIPCHK(hipMemcpyAsync(m->h_out + kMaxBatch, m->st->e, batch * 4, hipMemcpyDeviceToHost, s));
       HIPCHK(hipMemcpyAsync(m->h_gap, m->st->gap, batch * 4, hipMemcpyDeviceToHost, s));
@@ -1230,7 +1251,10 @@ ee_status ee_decode_step(ee_model* m, ee_kv_cache* c, int32_t batch, const int32
       if (dbg && dbg->p_top1)
         for (int b = 0; b < batch; ++b)
           for (int l = 0; l < L - 1; ++l) dbg->p_top1[(size_t)b * (L - 1) + l] = prec[(size_t)l * kMaxBatch + b];
-      for (int b = 0; b < batch; ++b) c->hlens[b] += 1;
+      for (int b = 0; b < batch; ++b) {
+        c->hlens[b] += 1;
+        c->next_ok[b] = 1;
+      }
     });
   });
 }

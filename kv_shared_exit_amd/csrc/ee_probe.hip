@@ -7,13 +7,13 @@
 //                                over a V x d bf16 matrix and `rows` staged rows
 //   ee_probe wide V d rows reps  the same GEMV for 9..64 rows on matrix cores
 //                                (wide_vocab_kernel<EPI_LSE> over the tiled copy)
-//   ee_probe proj EPI N K nbf ni4 g reps
+//   ee_probe proj EPI N K nbf ni4 reps
 //                                a decoder projection (EPI: swiglu = gate/up
-//                                with its epilogue, part = O or down with
-//                                float32 partials) of N output rows over K
-//                                inputs, nbf rows on the bf16 weights and ni4
-//                                on the int4 G128 copy, on a grid of g
-//                                workgroups
+//                                with its epilogue, part = O, down or a
+//                                QKV-sized map with float32 partials) of N
+//                                output rows over K inputs, nbf rows on the
+//                                bf16 weights and ni4 on the int4 G128 copy,
+//                                on the decode step's grid (512 workgroups)
 //   ee_probe copy MiB            one copy kernel reading and writing MiB each
 //
 // Prints the mean launch time (HIP events on the launch stream).
@@ -46,7 +46,7 @@ __global__ void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ d
 static int usage() {
   std::fprintf(stderr,
                "usage: ee_probe lse V d rows reps | ee_probe wide V d rows reps | "
-               "ee_probe proj swiglu|part N K nbf ni4 g reps | ee_probe copy MiB\n");
+               "ee_probe proj swiglu|part N K nbf ni4 reps | ee_probe copy MiB\n");
   return 2;
 }
 
@@ -77,14 +77,14 @@ int main(int argc, char** argv) {
     return 0;
   }
   if (!std::strcmp(argv[1], "proj")) {
-    if (argc < 9) return usage();
+    if (argc < 8) return usage();
     const bool swiglu = !std::strcmp(argv[2], "swiglu");
     if (!swiglu && std::strcmp(argv[2], "part")) return usage();
     const int N = std::atoi(argv[3]), K = std::atoi(argv[4]), nbf = std::atoi(argv[5]), ni4 = std::atoi(argv[6]);
-    const int g = std::atoi(argv[7]), reps = std::atoi(argv[8]);
+    const int g = 512, reps = std::atoi(argv[7]);  // the decode step's projection grid
     constexpr int G = 128;
     if (N < 16 || N % 16 || K < G || K % G || nbf < 0 || ni4 < 0 || nbf + ni4 < 1 || nbf + ni4 > 8 || g < 1 ||
-        g > kNwgMax || reps < 1)
+        reps < 1)
       return usage();
     if (swiglu && !proj_fits(K, nbf + ni4)) return usage();
     const int P = swiglu ? 2 : 1;

@@ -89,6 +89,65 @@ def test_error_paths_leave_state_unchanged(api):
         m.close()
 
 
+def test_kept_tokens_are_per_cache_and_dropped_by_rollback(api):
+    """A step without input tokens feeds each sequence the last output token of
+    the same cache: two caches on one model keep their own, equal to passing
+    those tokens explicitly on fresh caches.  After a rollback or a reset the
+    kept token no longer follows the sequence's last position, so a step
+    without tokens is refused (state unchanged) until tokens are passed again."""
+    from kv_shared_exit_amd import _binding as B
+    sh = ODD
+    w, m = _model(api, sh, alpha=np.full(sh.n_layers - 1, 3000.0), max_batch=2, max_positions=12)
+    pa = np.array([[5, 6, 7], [8, 9, 10]], np.int32)
+    pb = np.array([[100, 200, 300], [400, 500, 600]], np.int32)
+    ca, cb = api.KVCache(m, 2, 12), api.KVCache(m, 2, 12)
+    fresh = api.KVCache(m, 2, 12)
+    try:
+        with pytest.raises(B.EEError) as e:
+            api.decode_step(m, fresh, 2)          # nothing produced on this cache yet
+        assert e.value.status == B.EE_ERR_INVALID_ARG
+        ta0, tb0 = api.prefill(m, ca, pa), api.prefill(m, cb, pb)
+        ta1, ea1 = api.decode_step(m, ca, 2)
+        tb1, eb1 = api.decode_step(m, cb, 2)
+        ta2, ea2 = api.decode_step(m, ca, 2)
+        # the same steps with explicit tokens on fresh caches
+        ra, rb = api.KVCache(m, 2, 12), api.KVCache(m, 2, 12)
+        try:
+            api.prefill(m, ra, pa)
+            api.prefill(m, rb, pb)
+            t, e_ = api.decode_step(m, ra, 2, tokens=ta0)
+            np.testing.assert_array_equal(t, ta1)
+            np.testing.assert_array_equal(e_, ea1)
+            t, e_ = api.decode_step(m, rb, 2, tokens=tb0)
+            np.testing.assert_array_equal(t, tb1)
+            np.testing.assert_array_equal(e_, eb1)
+            t, e_ = api.decode_step(m, ra, 2, tokens=ta1)
+            np.testing.assert_array_equal(t, ta2)
+            np.testing.assert_array_equal(e_, ea2)
+        finally:
+            ra.close()
+            rb.close()
+        ca.rollback(-1, 1)
+        assert list(ca.lengths()) == [4, 4]
+        with pytest.raises(B.EEError) as e:
+            api.decode_step(m, ca, 2)
+        assert e.value.status == B.EE_ERR_INVALID_ARG
+        assert list(ca.lengths()) == [4, 4]
+        t, _ = api.decode_step(m, ca, 2, tokens=ta1)  # the rolled-back step again
+        np.testing.assert_array_equal(t, ta2)
+        api.decode_step(m, ca, 2)                     # kept again
+        assert list(ca.lengths()) == [6, 6]
+        cb.reset(0)
+        with pytest.raises(B.EEError) as e:
+            api.decode_step(m, cb, 2)
+        assert e.value.status == B.EE_ERR_INVALID_ARG
+    finally:
+        fresh.close()
+        ca.close()
+        cb.close()
+        m.close()
+
+
 def test_cache_without_tracking_has_no_occupancy(api):
     from kv_shared_exit_amd import _binding as B
     w, m = _model(api, ODD, max_batch=1, max_positions=4)
