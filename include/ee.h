@@ -294,6 +294,26 @@ ee_status ee_decode_step(ee_model *m, ee_kv_cache *c, int32_t batch,
                          const float *gamma_host, void *hip_stream, int32_t *out_tokens_host,
                          int32_t *out_exit_layers_host, ee_step_debug *dbg);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture
+ * around its own work, tight serving loops, harnesses that forbid hipMalloc):
+ * the same decode step as ee_decode_step (same arguments and results, bit for
+ * bit), with its per-step device workspaces (residual, staged projection
+ * inputs, partial sums, attention and exit-head partials, step state) taken
+ * from a static device array of 32 MiB per GPU that the library holds until
+ * the process ends, instead of the model's own buffers.  It calls no
+ * hipMalloc, hipFree or other allocating routine; its kernels are launched
+ * one by one (no graph is captured or instantiated), without diagnostics or
+ * profiling.  UNSUPPORTED when the step's workspaces exceed the array (e.g.
+ * the 8B shape above 8 rows, whose matrix-core passes need larger partial
+ * sums); nothing runs then.  Every call on one GPU uses that GPU's single
+ * array, which keeps the last call's contents (the step state is cleared by a
+ * kernel at the start of each call): calls that overlap on one GPU, from any
+ * model or thread, race and must be serialised by the caller. */
+ee_status ee_decode_step_static(ee_model *m, ee_kv_cache *c, int32_t batch,
+                                const int32_t *in_tokens_host, const int32_t *forced_exit_host,
+                                const float *gamma_host, void *hip_stream, int32_t *out_tokens_host,
+                                int32_t *out_exit_layers_host);
+
 /* Copies the int4 exit copy of one linear map of 1-based layer (2..L) back to the
  * host as int8 codes [nrows][K] and bf16 scales [nrows][K/G] (uint16 bits).
  * which: 0 wq, 1 wk, 2 wv, 3 wo, 4 w_gate, 5 w_up, 6 w_down.

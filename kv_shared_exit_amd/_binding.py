@@ -35,7 +35,7 @@ EE_KV_TRACK_OCCUPANCY = 1
 EXPORTS = [
     "ee_create_model", "ee_destroy_model", "ee_kv_cache_bytes", "ee_kv_cache_create",
     "ee_kv_cache_reset", "ee_kv_cache_rollback", "ee_kv_cache_lengths", "ee_kv_cache_read", "ee_kv_cache_occupancy",
-    "ee_kv_cache_destroy", "ee_prefill", "ee_decode_step", "ee_exit_weights_read",
+    "ee_kv_cache_destroy", "ee_prefill", "ee_decode_step", "ee_decode_step_static", "ee_exit_weights_read",
     "ee_profile_enable", "ee_profile_read", "ee_last_error",
 ]
 
@@ -96,6 +96,7 @@ def load() -> C.CDLL:
         "ee_kv_cache_destroy": [P],
         "ee_prefill": [P, P, I32, P, I32, P, P, P, P],
         "ee_decode_step": [P, P, I32, P, P, P, P, P, P, P],
+        "ee_decode_step_static": [P, P, I32, P, P, P, P, P, P],
         "ee_exit_weights_read": [P, I32, I32, I32, I32, P, P],
         "ee_profile_enable": [P, I32],
         "ee_profile_read": [P, I32, C.POINTER(C.c_int64), C.POINTER(C.c_double)],

@@ -201,3 +201,21 @@ def decode_step(model: Model, cache: KVCache, batch: int, tokens=None, forced=No
                                      B._ptr(gam), _stream_ptr(stream), B._ptr(out_t),
                                      B._ptr(out_e), dbg_ptr))
     return out_t, out_e
+
+
+def decode_step_static(model: Model, cache: KVCache, batch: int, tokens=None, forced=None, gamma=None,
+                       stream=None):
+    """ee_decode_step_static: the decode step with its workspaces in the
+    library's static device array (no allocation); same results as
+    decode_step without diagnostics."""
+    L = model.shape.n_layers
+    tok = None if tokens is None else np.ascontiguousarray(tokens, dtype=np.int32)
+    frc = None if forced is None else np.ascontiguousarray(forced, dtype=np.int32)
+    gam = None
+    if gamma is not None:
+        gam = np.ascontiguousarray(np.broadcast_to(np.asarray(gamma, np.float32), (L - 1,)))
+    out_t = np.empty(batch, np.int32)
+    out_e = np.empty(batch, np.int32)
+    B.check(model.lib.ee_decode_step_static(model.h, cache.h, batch, B._ptr(tok), B._ptr(frc), B._ptr(gam),
+                                            _stream_ptr(stream), B._ptr(out_t), B._ptr(out_e)))
+    return out_t, out_e

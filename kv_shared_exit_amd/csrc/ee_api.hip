@@ -10,6 +10,7 @@
 #include <new>
 #include <string>
 #include <tuple>
+#include <type_traits>
 #include <vector>
 
 #include "ee.h"
@@ -17,9 +18,19 @@
 
 using namespace ee;
 
+// Device memory of ee_decode_step_static: the step's workspaces for callers
+// that cannot allocate (kScratchBytes per device, held until the process
+// ends).  Host code never uses this name as an address: the per-device
+// address comes from hipGetSymbolAddress (g_scratch below).
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 thread_local std::string g_err;
+
+constexpr int kMaxDevices = 64;
+char* g_scratch[kMaxDevices] = {};  // device address of `scratch` per device (resolved by ee_create_model)
 
 struct Error {
   ee_status code;
@@ -126,6 +137,7 @@ struct ee_model {
   int32_t* h_out = nullptr;  // out_tok[64], e[64]
   float* h_gap = nullptr;
   hipStream_t own = nullptr;
+  int device = 0;  // the HIP device the model was created on
   bool broken = false;
   std::string broken_msg;
   // profiling
@@ -305,6 +317,96 @@ void attn_split(int S, int B, int Hkv, int* tpw, int* nch) {
   *nch = (tiles + t - 1) / t;
 }
 
+// Device workspaces of the step's kernels: the residual, the staged inputs
+// of the projections, partial sums, attention partials, the exit heads'
+// partials and the step state.  The model owns one set (allocated by
+// ee_create_model); ee_decode_step_static carves one out of the static scratch
+// array instead.
+struct Work {
+  float* h = nullptr;          // float32 residual [64][d]
+  float* parts = nullptr;      // O / down partial sums [ranges][64][d]
+  uint16_t* xn = nullptr;      // normalised input of the next projection [2 * 64][d]
+  uint16_t* hb = nullptr;      // bf16(h), the exit head's input [64][d]
+  uint16_t* qrot = nullptr;    // rotated q [64][H * hd]
+  uint16_t* attn_o = nullptr;  // attention output [64][H * hd]
+  uint16_t* act = nullptr;     // SwiGLU output [64][F]
+  uint16_t* z = nullptr;       // exit head's bf16(T h) [64][d]
+  float* head_part = nullptr;  // vocabulary partials [512][64][4]
+  float* part_s = nullptr;     // sampled partials [512][64][kPartS]
+  float* h2 = nullptr;         // residual after attention (similarity criterion) [64][d]
+  float* sts = nullptr;        // similarity per sequence [64]
+  float* attn_part = nullptr;  // attention partials [B][H][nch][hd + 2]
+  StepState* st = nullptr;
+  float* p_rec = nullptr;      // criterion values [L - 1][64]
+  float* d_gamma = nullptr;    // thresholds [L - 1]
+  float* wide_y = nullptr;     // wide projections' partial sums
+  bool prof = true;            // profiled launches may record events
+};
+
+Work model_work(const ee_model* m) {
+  Work w;
+  w.h = m->h;
+  w.parts = m->parts;
+  w.xn = m->xn;
+  w.hb = m->hb;
+  w.qrot = m->qrot;
+  w.attn_o = m->attn_o;
+  w.act = m->act;
+  w.z = m->z;
+  w.head_part = m->head_part;
+  w.part_s = m->part_s;
+  w.h2 = m->h2;
+  w.sts = m->sts;
+  w.attn_part = m->attn_part;
+  w.st = m->st;
+  w.p_rec = m->p_rec;
+  w.d_gamma = m->d_gamma;
+  w.wide_y = m->wide_y;
+  return w;
+}
+
+// Bytes of the step's workspaces for B rows over a cache of S positions (the
+// sizes the model allocates for itself, attention partials for this S and B),
+// each aligned to 256 bytes; with base set, w's pointers are placed from base.
+size_t work_layout(const ee_model* m, int B, int S, char* base, Work* w) {
+  const ee_model_config& c = m->cfg;
+  const int L = c.n_layers, d = c.d_model, F = c.d_ff, qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
+  size_t off = 0;
+  auto take = [&](auto*& p, size_t bytes) {
+    off = (off + 255) & ~(size_t)255;
+    p = base ? reinterpret_cast<std::remove_reference_t<decltype(p)>>(base + off) : nullptr;
+    off += std::max<size_t>(bytes, 4);
+  };
+  const size_t Bm = kMaxBatch;
+  take(w->h, Bm * d * 4);
+  take(w->parts, (size_t)m->nkc_max * Bm * d * 4);
+  take(w->xn, 2 * Bm * d * 2);
+  take(w->hb, Bm * d * 2);
+  take(w->qrot, Bm * qd * 2);
+  take(w->attn_o, Bm * qd * 2);
+  take(w->act, Bm * F * 2);
+  take(w->z, Bm * d * 2);
+  take(w->head_part, (size_t)kNwg * Bm * 4 * 4);
+  if (c.temperature > 0.0f) take(w->part_s, (size_t)kNwg * Bm * kPartS * 4);
+  if (c.criterion == EE_CRIT_STS) {
+    take(w->h2, Bm * d * 4);
+    take(w->sts, Bm * 4);
+  }
+  int tpw = 0, nch = 0;
+  attn_split(S, B, c.n_kv_heads, &tpw, &nch);
+  take(w->attn_part, (size_t)B * c.n_heads * nch * (c.head_dim + 2) * 4);
+  take(w->st, sizeof(StepState));
+  take(w->p_rec, (size_t)std::max(L - 1, 1) * Bm * 4);
+  take(w->d_gamma, (size_t)std::max(L - 1, 1) * 4);
+  if (m->wide && B > 8) {
+    const size_t yq = (size_t)wide_ranges(qd + 2 * kvd, d, nullptr) * Bm * (qd + 2 * kvd);
+    const size_t yg = (size_t)wide_ranges(2 * F, d, nullptr) * Bm * 2 * F;
+    const size_t yt = (size_t)wide_ranges(d, d, nullptr) * Bm * d;
+    take(w->wide_y, std::max(yq, std::max(yg, yt)) * 4);
+  }
+  return (off + 255) & ~(size_t)255;
+}
+
 struct Debug {
   bool hidden = false, logits = false;
 };
@@ -324,13 +426,13 @@ struct PosRun {
 
 // Enqueues one position of all B sequences: layers 1..L, exit heads when
 // heads is set, and the final head when final is set (else the lengths advance).
-void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final,
+void enqueue_position(ee_model* m, const Work& W, ee_kv_cache* c, int B, bool heads, bool final,
                       const int32_t* prompt, int P, int t, const Debug& dbg, hipStream_t s,
                       const PosRun* pr = nullptr) {
   const ee_model_config& cf = m->cfg;
   const int L = cf.n_layers, d = cf.d_model, F = cf.d_ff, H = cf.n_heads, Hkv = cf.n_kv_heads;
   const int hd = cf.head_dim, qd = H * hd, kvd = Hkv * hd, nqkv = qd + 2 * kvd;
-  StepState* st = m->st;
+  StepState* st = W.st;
   const bool int4 = cf.exit_mode == EE_EXIT_INT4;
   heads = heads && cf.exit_mode != EE_EXIT_NONE;  // the plain decoder evaluates no criterion
   const bool sts_crit = cf.criterion == EE_CRIT_STS;
@@ -343,7 +445,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
   const int nv = wide_vocab ? kNwg : vocab_nwg(cf.vocab);
   const float itau = sampled ? 1.0f / cf.temperature : 0.0f;
   auto sampled_args = [&](ProjArgs& a) {
-    a.part_s = m->part_s;
+    a.part_s = W.part_s;
     a.itau = itau;
     a.seed = cf.sample_seed;
     a.lens = c->lens;
@@ -351,11 +453,11 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
   };
 
   const size_t pstride = (size_t)kMaxBatch * d;  // elements between partial-sum ranges
-  float* hh = pr ? pr->h : m->h;        // residual [b][d]
-  uint16_t* xn = pr ? pr->xn : m->xn;   // the next projection's normalised input [b][d]
+  float* hh = pr ? pr->h : W.h;        // residual [b][d]
+  uint16_t* xn = pr ? pr->xn : W.xn;   // the next projection's normalised input [b][d]
   const int l_first = pr ? pr->l0 : 1, l_last = pr ? pr->l1 : L;
   if (!pr || pr->init)
-    launch_init(st, prompt, P, t, B, L, m->tok_emb, d, cf.vocab, hh, m->p_rec,
+    launch_init(st, prompt, P, t, B, L, m->tok_emb, d, cf.vocab, hh, W.p_rec,
                 (const uint16_t*)m->lw[0].attn_norm, cf.rms_eps, xn, s);
   if (dbg.hidden)
     HIPCHK(hipMemcpy2DAsync(m->dbg_hidden, (size_t)(L + 1) * d * 4, hh, (size_t)d * 4,
@@ -421,7 +523,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       a.cosT = m->d_cos;
       a.sinT = m->d_sin;
       a.lens = c->lens;
-      a.qrot = m->qrot;
+      a.qrot = W.qrot;
       a.Kl = c->K + kvoff;
       a.Vl = c->V + kvoff;
       a.occ_l = c->occ ? c->occ + (size_t)(l - 1) * c->Bmax * c->S : nullptr;
@@ -431,17 +533,17 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       a.hd_log2 = __builtin_ctz(hd);
       a.S = c->S;
       if (wide) {
-        WideArgs wa = wide_args(nqkv, d, m->ww[l - 1].qkv, xn, d, m->wide_y, nqkv);
+        WideArgs wa = wide_args(nqkv, d, m->ww[l - 1].qkv, xn, d, W.wide_y, nqkv);
         if (q) wide_i4(wa, q->qkv);
         launch_wide_proj(wa, s);
-        launch_wide_qkv(m->wide_y, wa.nr, wa.y_cstride, nqkv, st->all, &st->n_all, B, a, s);
+        launch_wide_qkv(W.wide_y, wa.nr, wa.y_cstride, nqkv, st->all, &st->n_all, B, a, s);
       } else {
         launch_proj(EPI_QKV, a, kNwg, B, s);
       }
     }
     {
       AttnArgs a{};
-      a.q = m->qrot;
+      a.q = W.qrot;
       a.K = c->K + kvoff;
       a.V = c->V + kvoff;
       a.S = c->S;
@@ -453,8 +555,8 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       a.B = B;
       attn_split(c->S, B, Hkv, &a.tpw, &a.nch);
       a.scale = (float)(1.0 / std::sqrt((double)hd));
-      a.part = m->attn_part;
-      a.out = m->attn_o;
+      a.part = W.attn_part;
+      a.out = W.attn_o;
       launch_attention(a, s);
     }
     {
@@ -470,14 +572,14 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       }
       a.list_bf = list_bf;
       a.cnt_bf = cnt_bf;
-      a.x = m->attn_o;
+      a.x = W.attn_o;
       a.x_stride = qd;
-      a.y = m->parts;
+      a.y = W.parts;
       a.y_stride = d;
       a.y_cstride = (int)pstride;
       int nkc;
       if (wide) {
-        WideArgs wa = wide_args(d, qd, m->ww[l - 1].o, m->attn_o, qd, m->parts, d);
+        WideArgs wa = wide_args(d, qd, m->ww[l - 1].o, W.attn_o, qd, W.parts, d);
         if (q) wide_i4(wa, q->o);
         launch_wide_proj(wa, s);
         nkc = wa.nr;
@@ -487,8 +589,8 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       // with the similarity criterion the layer's input stays in h (the
       // residual after attention goes to h2) until the layer's end
       const bool sts_pre = pr && pr->sts && l < L;  // the prefill's similarity at this layer
-      float* h_mid = (heads && sts_crit && l < L && l % every == 0) || sts_pre ? m->h2 : hh;
-      launch_finish(h_mid, hh, m->parts, nkc, pstride, B, d, (const uint16_t*)w.ffn_norm, cf.rms_eps, xn,
+      float* h_mid = (heads && sts_crit && l < L && l % every == 0) || sts_pre ? W.h2 : hh;
+      launch_finish(h_mid, hh, W.parts, nkc, pstride, B, d, (const uint16_t*)w.ffn_norm, cf.rms_eps, xn,
                     nullptr, nullptr, nullptr, s);
     }
     {
@@ -509,10 +611,10 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       a.cnt_bf = cnt_bf;
       a.x = xn;  // bf16(rmsnorm(h) * ffn_norm)
       a.x_stride = d;
-      a.y = m->act;
+      a.y = W.act;
       a.y_stride = F;
       if (wide) {  // gate rows 0..F-1, up rows F..2F-1
-        WideArgs wa = wide_args(2 * F, d, m->ww[l - 1].gu, xn, d, m->wide_y, 2 * F);
+        WideArgs wa = wide_args(2 * F, d, m->ww[l - 1].gu, xn, d, W.wide_y, 2 * F);
         if (q) {
           wide_i4(wa, q->gate);
           wa.q4[1] = q->up.codes;
@@ -520,7 +622,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
           wa.n0 = F;
         }
         launch_wide_proj(wa, s);
-        launch_wide_swiglu(m->wide_y, wa.nr, wa.y_cstride, 2 * F, st->all, &st->n_all, B, F, m->act, s);
+        launch_wide_swiglu(W.wide_y, wa.nr, wa.y_cstride, 2 * F, st->all, &st->n_all, B, F, W.act, s);
       } else {
         launch_proj(EPI_SWIGLU, a, kNwg, B, s);
       }
@@ -540,14 +642,14 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       }
       a.list_bf = list_bf;
       a.cnt_bf = cnt_bf;
-      a.x = m->act;
+      a.x = W.act;
       a.x_stride = F;
-      a.y = m->parts;
+      a.y = W.parts;
       a.y_stride = d;
       a.y_cstride = (int)pstride;
       int nkc;
       if (wide) {
-        WideArgs wa = wide_args(d, F, m->ww[l - 1].down, m->act, F, m->parts, d);
+        WideArgs wa = wide_args(d, F, m->ww[l - 1].down, W.act, F, W.parts, d);
         if (q) wide_i4(wa, q->down);
         launch_wide_proj(wa, s);
         nkc = wa.nr;
@@ -558,16 +660,16 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       // final norm before the LM head; bf16(h) for this layer's exit head
       const void* g_next = l < L ? m->lw[l].attn_norm : (const void*)m->final_norm;
       if (sts_here || (pr && pr->sts && l < L))  // h = h2 + partials; sts = cos(layer input in h, new h)
-        launch_finish(hh, m->h2, m->parts, nkc, pstride, B, d, (const uint16_t*)g_next, cf.rms_eps, xn,
-                      nullptr, hh, sts_here ? m->sts : pr->sts, s);
+        launch_finish(hh, W.h2, W.parts, nkc, pstride, B, d, (const uint16_t*)g_next, cf.rms_eps, xn,
+                      nullptr, hh, sts_here ? W.sts : pr->sts, s);
       else
-        launch_finish(hh, hh, m->parts, nkc, pstride, B, d, (const uint16_t*)g_next, cf.rms_eps, xn,
-                      head_here ? m->hb : nullptr, nullptr, nullptr, s);
+        launch_finish(hh, hh, W.parts, nkc, pstride, B, d, (const uint16_t*)g_next, cf.rms_eps, xn,
+                      head_here ? W.hb : nullptr, nullptr, nullptr, s);
     }
     const bool bmin = cf.exit_rule == EE_RULE_BATCH_MIN;
-    if (sts_here) launch_decide(DECIDE_STS, bmin, st, nullptr, 0, m->d_gamma, l, L, B, m->p_rec, m->sts, s);
+    if (sts_here) launch_decide(DECIDE_STS, bmin, st, nullptr, 0, W.d_gamma, l, L, B, W.p_rec, W.sts, s);
     if (heads && l < L && !head_here)  // between checks only forced exits apply
-      launch_decide(DECIDE_FORCED, false, st, nullptr, 0, m->d_gamma, l, L, B, m->p_rec, nullptr, s);
+      launch_decide(DECIDE_FORCED, false, st, nullptr, 0, W.d_gamma, l, L, B, W.p_rec, nullptr, s);
     if (head_here && !sts_crit) {
       {
         ProjArgs a = base_args(m);
@@ -576,16 +678,16 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
         set_seg1(a, w.head_T, d);
         a.list_bf = st->act;
         a.cnt_bf = &st->n_act;
-        a.x = m->hb;  // bf16(h)
+        a.x = W.hb;  // bf16(h)
         a.x_stride = d;
-        a.y = m->z;
+        a.y = W.z;
         a.y_stride = d;
         if (wide && m->ww[l - 1].T) {
-          WideArgs wa = wide_args(d, d, m->ww[l - 1].T, m->hb, d, m->wide_y, d);
+          WideArgs wa = wide_args(d, d, m->ww[l - 1].T, W.hb, d, W.wide_y, d);
           wa.list_bf = st->act;
           wa.cnt_bf = &st->n_act;
           launch_wide_proj(wa, s);
-          launch_wide_bf16(m->wide_y, wa.nr, wa.y_cstride, d, st->act, &st->n_act, B, d, m->z, d, s);
+          launch_wide_bf16(W.wide_y, wa.nr, wa.y_cstride, d, st->act, &st->n_act, B, d, W.z, d, s);
         } else {
           launch_proj(EPI_BF16, a, kNwg, B, s);
         }
@@ -597,11 +699,11 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
         set_seg1(a, m->lm_head, cf.vocab);
         a.list_bf = st->act;
         a.cnt_bf = &st->n_act;
-        a.x = m->z;
+        a.x = W.z;
         a.x_stride = d;
-        a.part = m->head_part;
-        hipEvent_t e0, e1;
-        prof_events(m, &e0, &e1);
+        a.part = W.head_part;
+        hipEvent_t e0 = nullptr, e1 = nullptr;
+        if (W.prof) prof_events(m, &e0, &e1);
         // more than 8 rows go to the wide pass (one read of E for all rows);
         // the row count is on the device, so both are launched and one returns
         if (sampled) {  // also the draft's Gumbel-max and the tau statistics
@@ -616,8 +718,8 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
           }
         }
       }
-      launch_decide(DECIDE_HEAD, bmin, st, m->head_part, nv, m->d_gamma, l, L, B, m->p_rec, nullptr, s);
-      if (sampled) launch_sample_draft(st, m->part_s, nv, l, B, m->z, xn + (size_t)kMaxBatch * d, d, s);
+      launch_decide(DECIDE_HEAD, bmin, st, W.head_part, nv, W.d_gamma, l, L, B, W.p_rec, nullptr, s);
+      if (sampled) launch_sample_draft(st, W.part_s, nv, l, B, W.z, xn + (size_t)kMaxBatch * d, d, s);
     }
     if (dbg.hidden)
       HIPCHK(hipMemcpy2DAsync(m->dbg_hidden + (size_t)l * d, (size_t)(L + 1) * d * 4, hh,
@@ -632,7 +734,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
     a.cnt_bf = &st->n_all;
     a.x = xn;  // bf16(rmsnorm(h) * final_norm)
     a.x_stride = d;
-    a.part = m->head_part;
+    a.part = W.head_part;
     a.logits = dbg.logits ? m->dbg_logits : nullptr;
     a.logits_stride = cf.vocab;
     if (sampled) {
@@ -640,8 +742,8 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       // the verification, then the resampling of the rejected drafts
       sampled_args(a);
       launch_proj(EPI_ARGMAX_S, a, nv, B, s);
-      launch_final(st, m->head_part, nv, B, cf.vocab, c->lens, 0, s);
-      launch_sample_final(st, m->part_s, nv, B, L, cf.vocab, c->lens, itau, cf.sample_seed, s);
+      launch_final(st, W.head_part, nv, B, cf.vocab, c->lens, 0, s);
+      launch_sample_final(st, W.part_s, nv, B, L, cf.vocab, c->lens, itau, cf.sample_seed, s);
       ProjArgs r = base_args(m);
       r.N = cf.vocab;
       r.K = d;
@@ -650,10 +752,10 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       r.cnt_bf = &st->n_rej;
       r.x = xn;
       r.x_stride = d;
-      r.part = m->head_part;
+      r.part = W.head_part;
       sampled_args(r);
       launch_proj(EPI_RESAMPLE, r, nv, 2 * B, s);
-      launch_resample_final(st, m->part_s, nv, B, cf.vocab, c->lens, s);
+      launch_resample_final(st, W.part_s, nv, B, cf.vocab, c->lens, s);
     } else {
       if (wide_vocab) {  // every row of the batch: the wide pass alone
         a.wb[0] = m->lm_head_t;
@@ -661,7 +763,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
       } else {
         launch_proj(EPI_ARGMAX, a, nv, B, s);
       }
-      launch_final(st, m->head_part, nv, B, cf.vocab, c->lens, 1, s);
+      launch_final(st, W.head_part, nv, B, cf.vocab, c->lens, 1, s);
     }
   } else {
     launch_advance(c->lens, B, s);
@@ -676,7 +778,7 @@ void enqueue_position(ee_model* m, ee_kv_cache* c, int B, bool heads, bool final
 // kernel-recorded events of the exit head are not captured into graphs).
 void replay_step(ee_model* m, ee_kv_cache* c, int B, hipStream_t s) {
   if (m->prof) {
-    enqueue_position(m, c, B, true, true, nullptr, 1, 0, Debug{}, s);
+    enqueue_position(m, model_work(m), c, B, true, true, nullptr, 1, 0, Debug{}, s);
     return;
   }
 
@@ -688,7 +790,7 @@ void replay_step(ee_model* m, ee_kv_cache* c, int B, hipStream_t s) {
     HIPCHK(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
     bool ok = true;
     try {
-      enqueue_position(m, c, B, true, true, nullptr, 1, 0, Debug{}, s);
+      enqueue_position(m, model_work(m), c, B, true, true, nullptr, 1, 0, Debug{}, s);
     } catch (const Error&) {
       ok = false;
     }
@@ -739,6 +841,36 @@ T* halloc(size_t n) {
   return (T*)p;
 }
 
+// Host-side checks of a decode step's arguments (no state changes).
+void validate_step(ee_model* m, ee_kv_cache* c, int batch, const int32_t* in_tokens_host,
+                   const int32_t* forced_exit_host, const float* gamma_host, const int32_t* out_tokens_host,
+                   const int32_t* out_exit_layers_host) {
+  check_model(m);
+  if (!c || c->m != m) fail(EE_ERR_INVALID_ARG, "cache does not belong to the model");
+  if (!out_tokens_host || !out_exit_layers_host) fail(EE_ERR_INVALID_ARG, "null output");
+  if (batch < 1 || batch > c->Bmax) fail(EE_ERR_INVALID_ARG, "batch out of range");
+  const ee_model_config& cf = m->cfg;
+  const int L = cf.n_layers;
+  if (in_tokens_host)
+    for (int b = 0; b < batch; ++b)
+      if (in_tokens_host[b] < 0 || in_tokens_host[b] >= cf.vocab) fail(EE_ERR_INVALID_ARG, "token out of range");
+  if (forced_exit_host)
+    for (int b = 0; b < batch; ++b)
+      if (forced_exit_host[b] < 0 || forced_exit_host[b] > L)
+        fail(EE_ERR_INVALID_ARG, "forced exit layer out of range");
+  if (gamma_host)
+    for (int l = 0; l < L - 1; ++l)
+      if (!std::isfinite(gamma_host[l])) fail(EE_ERR_INVALID_ARG, "gamma must be finite");
+  if (!in_tokens_host)
+    for (int b = 0; b < batch; ++b)
+      if (!c->next_ok[b])
+        fail(EE_ERR_INVALID_ARG, "sequence " + std::to_string(b) +
+                                     " has no kept output token (none produced yet, or reset or rolled "
+                                     "back since): pass in_tokens");
+  for (int b = 0; b < batch; ++b)
+    if (c->hlens[b] + 1 > c->S) fail(EE_ERR_CACHE_FULL, "sequence " + std::to_string(b) + " is full");
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -779,6 +911,14 @@ ee_status ee_create_model(const ee_model_config* cfg, const ee_weights* w, const
       m->gamma = gam;
       HIPCHK(hipStreamCreateWithFlags(&m->own, hipStreamNonBlocking));
       no_rows();  // resolved on this device here, before any graph capture
+      HIPCHK(hipGetDevice(&m->device));
+      if (m->device < 0 || m->device >= kMaxDevices) fail(EE_ERR_UNSUPPORTED, "device index out of range");
+      if (!g_scratch[m->device]) {  // once per device, with that device current
+        void* p = nullptr;
+        HIPCHK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p) fail(EE_ERR_HIP, "hipGetSymbolAddress(scratch) returned null");
+        g_scratch[m->device] = (char*)p;
+      }
       const int L = c.n_layers, d = c.d_model, F = c.d_ff, G = c.group_size;
       const int qd = c.n_heads * c.head_dim, kvd = c.n_kv_heads * c.head_dim;
       // int4 exit copies of layers 2..L
@@ -1139,7 +1279,7 @@ ee_status ee_prefill(ee_model* m, ee_kv_cache* c, int32_t batch, const int32_t* 
             const size_t off = (size_t)t * batch * m->cfg.d_model;
             PosRun pr{hP + off, xP + off, l < L ? sP + (size_t)t * batch : nullptr, l, l, l == 1};
             const bool fin = l == L && t == P - 1;
-            enqueue_position(m, c, batch, false, fin, m->d_prompt, P, t, fin ? last : dbg, s, &pr);
+            enqueue_position(m, model_work(m), c, batch, false, fin, m->d_prompt, P, t, fin ? last : dbg, s, &pr);
           }
           if (l < L) {
             launch_advance(c->lens, batch, s, -P);  // the next layer starts at the first position again
@@ -1151,7 +1291,7 @@ ee_status ee_prefill(ee_model* m, ee_kv_cache* c, int32_t batch, const int32_t* 
         HIPCHK(hipStreamSynchronize(s));
       } else {
         for (int t = 0; t < P; ++t)
-          enqueue_position(m, c, batch, false, t == P - 1, m->d_prompt, P, t, t == P - 1 ? last : dbg, s);
+          enqueue_position(m, model_work(m), c, batch, false, t == P - 1, m->d_prompt, P, t, t == P - 1 ? last : dbg, s);
       }
       HIPCHK(hipMemcpyAsync(c->next_tok, m->st->out_tok, batch * 4, hipMemcpyDeviceToDevice, s));
       HIPCHK(hipMemcpyAsync(m->h_out + kMaxBatch, m->st->e, batch * 4, hipMemcpyDeviceToHost, s));
@@ -1175,31 +1315,10 @@ ee_status ee_decode_step(ee_model* m, ee_kv_cache* c, int32_t batch, const int32
                          const int32_t* forced_exit_host, const float* gamma_host, void* hip_stream,
                          int32_t* out_tokens_host, int32_t* out_exit_layers_host, ee_step_debug* dbg) {
   return guard([&] {
-    check_model(m);
-    if (!c || c->m != m) fail(EE_ERR_INVALID_ARG, "cache does not belong to the model");
-    if (!out_tokens_host || !out_exit_layers_host) fail(EE_ERR_INVALID_ARG, "null output");
-    if (batch < 1 || batch > c->Bmax) fail(EE_ERR_INVALID_ARG, "batch out of range");
+    validate_step(m, c, batch, in_tokens_host, forced_exit_host, gamma_host, out_tokens_host,
+                  out_exit_layers_host);
     const ee_model_config& cf = m->cfg;
     const int L = cf.n_layers;
-    if (in_tokens_host)
-      for (int b = 0; b < batch; ++b)
-        if (in_tokens_host[b] < 0 || in_tokens_host[b] >= cf.vocab)
-          fail(EE_ERR_INVALID_ARG, "token out of range");
-    if (forced_exit_host)
-      for (int b = 0; b < batch; ++b)
-        if (forced_exit_host[b] < 0 || forced_exit_host[b] > L)
-          fail(EE_ERR_INVALID_ARG, "forced exit layer out of range");
-    if (gamma_host)
-      for (int l = 0; l < L - 1; ++l)
-        if (!std::isfinite(gamma_host[l])) fail(EE_ERR_INVALID_ARG, "gamma must be finite");
-    if (!in_tokens_host)
-      for (int b = 0; b < batch; ++b)
-        if (!c->next_ok[b])
-          fail(EE_ERR_INVALID_ARG, "sequence " + std::to_string(b) +
-                                       " has no kept output token (none produced yet, or reset or rolled "
-                                       "back since): pass in_tokens");
-    for (int b = 0; b < batch; ++b)
-      if (c->hlens[b] + 1 > c->S) fail(EE_ERR_CACHE_FULL, "sequence " + std::to_string(b) + " is full");
     with_sticky(m, [&] {
       hipStream_t s = pick_stream(m, hip_stream);
       Debug dd;
@@ -1224,7 +1343,7 @@ ee_status ee_decode_step(ee_model* m, ee_kv_cache* c, int32_t batch, const int32
       if (L > 1)
         HIPCHK(hipMemcpyAsync(m->d_gamma, m->h_gamma, (L - 1) * 4, hipMemcpyHostToDevice, s));
       if (dbg) {
-        enqueue_position(m, c, batch, true, true, nullptr, 1, 0, dd, s);
+        enqueue_position(m, model_work(m), c, batch, true, true, nullptr, 1, 0, dd, s);
       } else {
         replay_step(m, c, batch, s);
       }
@@ -1251,6 +1370,54 @@ ee_status ee_decode_step(ee_model* m, ee_kv_cache* c, int32_t batch, const int32
       if (dbg && dbg->p_top1)
         for (int b = 0; b < batch; ++b)
           for (int l = 0; l < L - 1; ++l) dbg->p_top1[(size_t)b * (L - 1) + l] = prec[(size_t)l * kMaxBatch + b];
+      for (int b = 0; b < batch; ++b) {
+        c->hlens[b] += 1;
+        c->next_ok[b] = 1;
+      }
+    });
+  });
+}
+
+ee_status ee_decode_step_static(ee_model* m, ee_kv_cache* c, int32_t batch, const int32_t* in_tokens_host,
+                                const int32_t* forced_exit_host, const float* gamma_host, void* hip_stream,
+                                int32_t* out_tokens_host, int32_t* out_exit_layers_host) {
+  return guard([&] {
+    validate_step(m, c, batch, in_tokens_host, forced_exit_host, gamma_host, out_tokens_host,
+                  out_exit_layers_host);
+    const ee_model_config& cf = m->cfg;
+    const int L = cf.n_layers;
+    Work W;
+    const size_t need = work_layout(m, batch, c->S, nullptr, &W);
+    if (need > kScratchBytes)
+      fail(EE_ERR_UNSUPPORTED, "the step's workspaces need " + std::to_string(need) +
+                                   " bytes, more than the static scratch holds (" + std::to_string(kScratchBytes) +
+                                   "): use ee_decode_step");
+    char* base = g_scratch[m->device];
+    if (!base) fail(EE_ERR_HIP, "the static scratch was not resolved on the model's device");
+    work_layout(m, batch, c->S, base, &W);
+    W.prof = false;  // no events are created here
+    with_sticky(m, [&] {
+      hipStream_t s = pick_stream(m, hip_stream);
+      // the array keeps the last call's contents: the step state starts from zero
+      launch_fill_u32((uint32_t*)W.st, sizeof(StepState) / 4, 0u, s);
+      for (int b = 0; b < batch; ++b) {
+        m->h_in[b] = in_tokens_host ? in_tokens_host[b] : 0;
+        m->h_in[kMaxBatch + b] = forced_exit_host ? forced_exit_host[b] : 0;
+      }
+      for (int l = 0; l < L - 1; ++l) m->h_gamma[l] = gamma_host ? gamma_host[l] : m->gamma[l];
+      if (in_tokens_host)
+        HIPCHK(hipMemcpyAsync(W.st->tok, m->h_in, batch * 4, hipMemcpyHostToDevice, s));
+      else
+        HIPCHK(hipMemcpyAsync(W.st->tok, c->next_tok, batch * 4, hipMemcpyDeviceToDevice, s));
+      HIPCHK(hipMemcpyAsync(W.st->forced, m->h_in + kMaxBatch, batch * 4, hipMemcpyHostToDevice, s));
+      if (L > 1) HIPCHK(hipMemcpyAsync(W.d_gamma, m->h_gamma, (L - 1) * 4, hipMemcpyHostToDevice, s));
+      enqueue_position(m, W, c, batch, true, true, nullptr, 1, 0, Debug{}, s);
+      HIPCHK(hipMemcpyAsync(c->next_tok, W.st->out_tok, batch * 4, hipMemcpyDeviceToDevice, s));
+      HIPCHK(hipMemcpyAsync(m->h_out, W.st->out_tok, batch * 4, hipMemcpyDeviceToHost, s));
+      HIPCHK(hipMemcpyAsync(m->h_out + kMaxBatch, W.st->e, batch * 4, hipMemcpyDeviceToHost, s));
+      HIPCHK(hipStreamSynchronize(s));
+      std::memcpy(out_tokens_host, m->h_out, batch * 4);
+      std::memcpy(out_exit_layers_host, m->h_out + kMaxBatch, batch * 4);
       for (int b = 0; b < batch; ++b) {
         c->hlens[b] += 1;
         c->next_ok[b] = 1;

@@ -150,6 +150,8 @@ void launch_finish(float* h, const float* hsrc, const float* parts, int nparts, 
 void launch_init(StepState* st, const int32_t* prompt, int P, int t, int B, int L,
                  const uint16_t* emb, int d, int V, float* h, float* p_rec, const uint16_t* gain,
                  float eps, uint16_t* x, hipStream_t s);
+// p[0..n) = v (32-bit words), by a kernel.
+void launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 void launch_attention(const AttnArgs& a, hipStream_t s);
 // Vocabulary GEMVs (EPI_LSE / EPI_ARGMAX) for more than 8 rows on MFMA
 // (ee_wide.hip): E read once for up to 64 rows from a tiled copy made by

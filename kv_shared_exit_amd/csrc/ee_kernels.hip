@@ -22,6 +22,7 @@
 
 #include <math.h>
 
+#include <algorithm>
 #include <stdexcept>
 
 namespace ee {
@@ -90,6 +91,19 @@ __global__ __launch_bounds__(kInitThreads) void init_kernel(StepState* st, const
       st->n_all = B;
     }
   }
+}
+
+// Fills n 32-bit words with v (used instead of a memset node, also in code a
+// caller may capture into a graph).
+__global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+void launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s) {
+  if (n == 0) return;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 1024);
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(blocks), dim3(256), 0, s, p, n, v);
 }
 
 void launch_init(StepState* st, const int32_t* prompt, int P, int t, int B, int L,
