@@ -170,6 +170,21 @@ def hbm_copy_ceiling(reps=10):
             "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "ms": round(ms, 4)}
 
 
+def prefill_flops(sh, B, P, chunk):
+    """Algorithmic flops of the prefill of B sequences of P positions given in
+    calls of `chunk` positions: every projection over every position (2 flops
+    per weight per position), causal attention (scores and the weighted sum,
+    4 hd flops per (query, visible key) per q head) and the LM head of each
+    call's last position."""
+    L, d, V, hd, H = sh.n_layers, sh.d_model, sh.vocab, sh.head_dim, sh.n_heads
+    proj = 2 * B * P * sh.params_per_layer() * L
+    ctx = np.arange(1, P + 1, dtype=np.float64).sum()      # visible keys summed over the positions
+    attn = 4 * hd * H * ctx * B * L
+    calls = (P + chunk - 1) // chunk
+    head = 2 * B * V * d * calls
+    return proj + attn + head
+
+
 def prefill(api, model, cache, prompts, stream, t0, chunk=512):
     """Prefill in chunks of positions (the library appends each chunk after the
     cached positions), logging progress on long prompts; with the prefill's
@@ -308,7 +323,8 @@ def main():
     pexits = prefill(api, model, cache, prompts, stream, t0)
     torch.cuda.synchronize()
     prefill_s = time.perf_counter() - tp0
-    log(f"prefill {B}x{P} done ({time.time() - t0:.0f}s)")
+    pf_flops = prefill_flops(sh, B, P, P if args.prefill_exit else 512)
+    log(f"prefill {B}x{P} done in {prefill_s:.3f}s ({time.time() - t0:.0f}s)")
 
     exits, toks = [], []
 
@@ -451,6 +467,11 @@ def main():
                  "head_launches_per_step": round(head_launches / K, 2)},
         "cpu_baseline": None,
         "prefill": {"seconds": round(prefill_s, 3), "positions": P, "batch": B,
+                    "positions_per_s": round(B * P / prefill_s, 1),
+                    "chunk": P if args.prefill_exit else min(P, 512),
+                    "mfma": {"dtype": "bf16", "achieved": round(pf_flops / prefill_s / 1e12, 1),
+                             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(pf_flops / prefill_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)},
                     "exit_layers": None if pexits is None else [int(x) for x in pexits]},
     }
     if wl.name != "8b":

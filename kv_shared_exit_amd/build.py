@@ -8,7 +8,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libee.so")
 SOURCES = [os.path.join(PKG, "csrc", n) for n in ("ee_api.hip", "ee_kernels.hip", "ee_proj.hip",
-                                                      "ee_wide.hip", "ee_sample.hip")]
+                                                      "ee_wide.hip", "ee_sample.hip", "ee_prefill.hip")]
 # single-kernel launcher for hardware-counter runs (not part of the library)
 PROBE = os.path.join(PKG, "ee_probe")
 PROBE_SOURCES = [os.path.join(PKG, "csrc", n) for n in ("ee_probe.hip", "ee_proj.hip", "ee_wide.hip")]

@@ -411,24 +411,10 @@ struct Debug {
   bool hidden = false, logits = false;
 };
 
-// One position of a prefill run layer by layer (River-LLM's sequence-level
-// exit, which needs every prompt token's similarity at a layer before the
-// next layer): this call runs layers l0..l1 for the position with its own
-// residual h and normalised input xn ([B][d] each); with sts set, the
-// similarity of each sequence's token at layer l1 (< L) goes there.
-struct PosRun {
-  float* h;
-  uint16_t* xn;
-  float* sts;
-  int l0, l1;
-  bool init;  // embed the position's token first (layer 1)
-};
-
-// Enqueues one position of all B sequences: layers 1..L, exit heads when
+// Enqueues one decode step of all B sequences: layers 1..L, exit heads when
 // heads is set, and the final head when final is set (else the lengths advance).
 void enqueue_position(ee_model* m, const Work& W, ee_kv_cache* c, int B, bool heads, bool final,
-                      const int32_t* prompt, int P, int t, const Debug& dbg, hipStream_t s,
-                      const PosRun* pr = nullptr) {
+                      const int32_t* prompt, int P, int t, const Debug& dbg, hipStream_t s) {
   const ee_model_config& cf = m->cfg;
   const int L = cf.n_layers, d = cf.d_model, F = cf.d_ff, H = cf.n_heads, Hkv = cf.n_kv_heads;
   const int hd = cf.head_dim, qd = H * hd, kvd = Hkv * hd, nqkv = qd + 2 * kvd;
@@ -453,12 +439,10 @@ void enqueue_position(ee_model* m, const Work& W, ee_kv_cache* c, int B, bool he
   };
 
   const size_t pstride = (size_t)kMaxBatch * d;  // elements between partial-sum ranges
-  float* hh = pr ? pr->h : W.h;        // residual [b][d]
-  uint16_t* xn = pr ? pr->xn : W.xn;   // the next projection's normalised input [b][d]
-  const int l_first = pr ? pr->l0 : 1, l_last = pr ? pr->l1 : L;
-  if (!pr || pr->init)
-    launch_init(st, prompt, P, t, B, L, m->tok_emb, d, cf.vocab, hh, W.p_rec,
-                (const uint16_t*)m->lw[0].attn_norm, cf.rms_eps, xn, s);
+  float* hh = W.h;        // residual [b][d]
+  uint16_t* xn = W.xn;    // the next projection's normalised input [b][d]
+  launch_init(st, prompt, P, t, B, L, m->tok_emb, d, cf.vocab, hh, W.p_rec,
+              (const uint16_t*)m->lw[0].attn_norm, cf.rms_eps, xn, s);
   if (dbg.hidden)
     HIPCHK(hipMemcpy2DAsync(m->dbg_hidden, (size_t)(L + 1) * d * 4, hh, (size_t)d * 4,
                             (size_t)d * 4, B, hipMemcpyDeviceToDevice, s));
@@ -493,7 +477,7 @@ void enqueue_position(ee_model* m, const Work& W, ee_kv_cache* c, int B, bool he
     wa.cnt_i4 = &st->n_ex;
   };
 
-  for (int l = l_first; l <= l_last; ++l) {
+  for (int l = 1; l <= L; ++l) {
     const ee_layer_weights& w = m->lw[l - 1];
     const LayerQ* q = (int4 && l >= 2) ? &m->lq[l - 1] : nullptr;
     const size_t kvoff = (size_t)(l - 1) * c->Bmax * Hkv * c->S * hd;
@@ -588,8 +572,7 @@ void enqueue_position(ee_model* m, const Work& W, ee_kv_cache* c, int B, bool he
       }
       // with the similarity criterion the layer's input stays in h (the
       // residual after attention goes to h2) until the layer's end
-      const bool sts_pre = pr && pr->sts && l < L;  // the prefill's similarity at this layer
-      float* h_mid = (heads && sts_crit && l < L && l % every == 0) || sts_pre ? W.h2 : hh;
+      float* h_mid = heads && sts_crit && l < L && l % every == 0 ? W.h2 : hh;
       launch_finish(h_mid, hh, W.parts, nkc, pstride, B, d, (const uint16_t*)w.ffn_norm, cf.rms_eps, xn,
                     nullptr, nullptr, nullptr, s);
     }
@@ -659,9 +642,9 @@ void enqueue_position(ee_model* m, const Work& W, ee_kv_cache* c, int B, bool he
       // the next projection's input: the next layer's attention norm, or the
       // final norm before the LM head; bf16(h) for this layer's exit head
       const void* g_next = l < L ? m->lw[l].attn_norm : (const void*)m->final_norm;
-      if (sts_here || (pr && pr->sts && l < L))  // h = h2 + partials; sts = cos(layer input in h, new h)
+      if (sts_here)  // h = h2 + partials; sts = cos(layer input in h, new h)
         launch_finish(hh, W.h2, W.parts, nkc, pstride, B, d, (const uint16_t*)g_next, cf.rms_eps, xn,
-                      nullptr, hh, sts_here ? W.sts : pr->sts, s);
+                      nullptr, hh, W.sts, s);
       else
         launch_finish(hh, hh, W.parts, nkc, pstride, B, d, (const uint16_t*)g_next, cf.rms_eps, xn,
                       head_here ? W.hb : nullptr, nullptr, nullptr, s);
@@ -839,6 +822,158 @@ T* halloc(size_t n) {
     fail(EE_ERR_OUT_OF_MEMORY, "pinned host allocation failed");
   }
   return (T*)p;
+}
+
+// The prefill of P positions of sequences 0..B-1 ("River-LLM 深度解析", section
+// 6.1), layer by layer over all B * P positions at once: every projection is
+// one matrix-core GEMM over the rows of the sequences on the backbone (bf16
+// weights) and one over the rows of the exited sequences (int4 copies; only
+// with the sequence-level exit), RoPE writes each position's k and v into its
+// shared slot, causal attention reads the slots.  With prefill_exit, after
+// layer l < L a sequence leaves when the smallest state transition similarity
+// of its prompt's tokens exceeds tau_l (River-LLM, sections 6.1 and 5.2).
+// Rows are position-major (t * B + b).  The greedy token of each sequence's
+// last position, and its logits when asked, go to the step state / debug
+// buffer; the lengths advance by P.  Per-call buffers of B * P rows.
+void run_prefill(ee_model* m, ee_kv_cache* c, int B, int P, bool want_logits, hipStream_t s) {
+  const ee_model_config& cf = m->cfg;
+  const int L = cf.n_layers, d = cf.d_model, F = cf.d_ff, H = cf.n_heads, Hkv = cf.n_kv_heads;
+  const int hd = cf.head_dim, qd = H * hd, kvd = Hkv * hd, nqkv = qd + 2 * kvd, G = cf.group_size;
+  const bool int4 = cf.exit_mode == EE_EXIT_INT4;
+  const bool pexit = cf.prefill_exit && L > 1;
+  const bool w4 = pexit && int4;  // exited sequences run the int4 copies
+  const int R = P * B;
+  const int ngr_max = std::max(d, std::max(qd, F)) / G;
+  CallBuffer<float> hA((size_t)R * d), hB((size_t)R * d), aux(pexit ? (size_t)R + kMaxBatch : 1),
+      xs(w4 ? (size_t)R * ngr_max : 1);
+  CallBuffer<uint16_t> xn((size_t)R * d), qkv((size_t)R * nqkv), qrot((size_t)R * qd), ao((size_t)R * qd),
+      act((size_t)R * F);
+  StepState* st = m->st;
+  launch_prefill_embed(st, m->d_prompt, P, B, L, m->tok_emb, d, cf.vocab, hA.p,
+                       (const uint16_t*)m->lw[0].attn_norm, cf.rms_eps, xn.p, s);
+  const int32_t* list_bf = int4 ? st->act : st->all;
+  const int32_t* cnt_bf = int4 ? &st->n_act : &st->n_all;
+  float *h_in = hA.p, *h_out = hB.p;
+  auto gemm = [&](int epi, const GemmArgs& g0, const Q4* qa, const Q4* qb, const uint16_t* x, int K) {
+    GemmArgs g = g0;
+    g.K = K;
+    g.G = G;
+    g.x = x;
+    g.ldx = K;
+    g.P = P;
+    g.Bt = B;
+    g.list = list_bf;
+    g.cnt = cnt_bf;
+    launch_gemm(epi, false, g, R, s);
+    if (qa) {  // the exited sequences' rows on the int4 copy
+      launch_group_sums(x, K, K, G, xs.p, ngr_max, st->ex, &st->n_ex, P, B, s);
+      g.q4 = qa->codes;
+      g.s4 = qa->scales;
+      if (qb) {
+        g.q4b = qb->codes;
+        g.s4b = qb->scales;
+      }
+      g.xs = xs.p;
+      g.ldxs = ngr_max;
+      g.list = st->ex;
+      g.cnt = &st->n_ex;
+      launch_gemm(epi, true, g, R, s);
+    }
+  };
+  for (int l = 1; l <= L; ++l) {
+    const ee_layer_weights& w = m->lw[l - 1];
+    const LayerQ* q = (w4 && l >= 2) ? &m->lq[l - 1] : nullptr;
+    const size_t kvoff = (size_t)(l - 1) * c->Bmax * Hkv * c->S * hd;
+    uint16_t* Kl = c->K + kvoff;
+    uint16_t* Vl = c->V + kvoff;
+    {  // QKV into bf16(W x), then RoPE and the shared-slot K/V write
+      GemmArgs g{};
+      g.N = nqkv;
+      g.nseg = 3;
+      g.wb[0] = (const uint16_t*)w.wq;
+      g.wb[1] = (const uint16_t*)w.wk;
+      g.wb[2] = (const uint16_t*)w.wv;
+      g.seg_end[0] = qd;
+      g.seg_end[1] = qd + kvd;
+      g.seg_end[2] = nqkv;
+      g.ob = qkv.p;
+      g.ldo = nqkv;
+      gemm(GEPI_BF16, g, q ? &q->qkv : nullptr, nullptr, xn.p, d);
+      launch_rope_kv(qkv.p, P, B, H, Hkv, hd, m->d_cos, m->d_sin, c->lens, qrot.p, Kl, Vl,
+                     c->occ ? c->occ + (size_t)(l - 1) * c->Bmax * c->S : nullptr, c->S, s);
+    }
+    launch_prefill_attention(qrot.p, Kl, Vl, c->S, P, B, H, Hkv, hd, c->lens, ao.p, s);
+    {  // h_out = h_in + W_o o, then the FFN's RMSNorm
+      GemmArgs g{};
+      g.N = d;
+      g.nseg = 1;
+      g.wb[0] = (const uint16_t*)w.wo;
+      g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = d;
+      g.of = h_out;
+      g.src = h_in;
+      g.ldf = d;
+      gemm(GEPI_RESID, g, q ? &q->o : nullptr, nullptr, ao.p, qd);
+      launch_finish(h_out, h_out, nullptr, 0, 0, R, d, (const uint16_t*)w.ffn_norm, cf.rms_eps, xn.p, nullptr,
+                    nullptr, nullptr, s);
+    }
+    {  // gate and up with SwiGLU
+      GemmArgs g{};
+      g.N = F;
+      g.nseg = 1;
+      g.wb[0] = (const uint16_t*)w.w_gate;
+      g.wb2 = (const uint16_t*)w.w_up;
+      g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = F;
+      g.ob = act.p;
+      g.ldo = F;
+      gemm(GEPI_SWIGLU, g, q ? &q->gate : nullptr, q ? &q->up : nullptr, xn.p, d);
+    }
+    {  // h_out += W_d a, then the next norm (and the layer's similarity with the exit)
+      GemmArgs g{};
+      g.N = d;
+      g.nseg = 1;
+      g.wb[0] = (const uint16_t*)w.w_down;
+      g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = d;
+      g.of = h_out;
+      g.src = h_out;
+      g.ldf = d;
+      gemm(GEPI_RESID, g, q ? &q->down : nullptr, nullptr, act.p, F);
+      const uint16_t* g_next = (const uint16_t*)(l < L ? m->lw[l].attn_norm : (const void*)m->final_norm);
+      if (pexit && l < L) {
+        float* sts = aux.p;
+        float* smin = aux.p + R;
+        launch_finish(h_out, h_out, nullptr, 0, 0, R, d, g_next, cf.rms_eps, xn.p, nullptr, h_in, sts, s);
+        launch_sts_min(sts, P, B, smin, s);
+        launch_decide(DECIDE_STS, false, st, nullptr, 0, m->d_gamma, l, L, B, nullptr, smin, s);
+      } else {
+        launch_finish(h_out, h_out, nullptr, 0, 0, R, d, g_next, cf.rms_eps, xn.p, nullptr, nullptr, nullptr, s);
+      }
+    }
+    std::swap(h_in, h_out);
+  }
+  // the final head on each sequence's last position (rows (P - 1) * B + b)
+  ProjArgs a = base_args(m);
+  a.N = cf.vocab;
+  a.K = d;
+  set_seg1(a, m->lm_head, cf.vocab);
+  a.list_bf = st->all;
+  a.cnt_bf = &st->n_all;
+  a.x = xn.p + (size_t)(P - 1) * B * d;
+  a.x_stride = d;
+  a.part = m->head_part;
+  a.logits = want_logits ? m->dbg_logits : nullptr;
+  a.logits_stride = cf.vocab;
+  const bool wide_vocab = m->lm_head_t && B > 8;
+  const int nv = wide_vocab ? kNwg : vocab_nwg(cf.vocab);
+  if (wide_vocab) {
+    a.wb[0] = m->lm_head_t;
+    launch_wide_vocab(EPI_ARGMAX, a, nv, s);
+  } else {
+    launch_proj(EPI_ARGMAX, a, nv, B, s);
+  }
+  launch_final(st, m->head_part, nv, B, cf.vocab, c->lens, 1, s);
+  if (P > 1) launch_advance(c->lens, B, s, P - 1);
+  // the per-call buffers are freed when this returns: finish the work first
+  HIPCHK(hipStreamSynchronize(s));
 }
 
 // Host-side checks of a decode step's arguments (no state changes).
@@ -1255,48 +1390,16 @@ ee_status ee_prefill(ee_model* m, ee_kv_cache* c, int32_t batch, const int32_t* 
       HIPCHK(hipMemcpyAsync(m->d_prompt, tokens_host, n * 4, hipMemcpyHostToDevice, s));
       for (int b = 0; b < batch; ++b) m->h_in[kMaxBatch + b] = 0;
       HIPCHK(hipMemcpyAsync(m->st->forced, m->h_in + kMaxBatch, batch * 4, hipMemcpyHostToDevice, s));
-      Debug dbg;
-      Debug last;
-      last.logits = last_logits_host != nullptr;
-      if (last.logits && !m->dbg_logits) m->dbg_logits = m->alloc<float>((size_t)kMaxBatch * m->cfg.vocab);
-      const int L = m->cfg.n_layers;
-      if (m->cfg.prefill_exit && L > 1) {
-        // River-LLM's sequence-level exit: layer by layer over every position,
-        // each position with its own residual and normalised input; after a
-        // layer, a sequence leaves when the smallest similarity of its tokens
-        // exceeds the layer's threshold, and its later layers run on the copies
-        const size_t rows = (size_t)P * batch;
-        CallBuffer<float> hbuf(rows * m->cfg.d_model), sbuf(rows + kMaxBatch);
-        CallBuffer<uint16_t> xbuf(rows * m->cfg.d_model);
-        float* hP = hbuf.p;
-        uint16_t* xP = xbuf.p;
-        float* sP = sbuf.p;
-        float* smin = sP + rows;
-        if (m->gamma.size())
-          HIPCHK(hipMemcpyAsync(m->d_gamma, m->gamma.data(), m->gamma.size() * 4, hipMemcpyHostToDevice, s));
-        for (int l = 1; l <= L; ++l) {
-          for (int t = 0; t < P; ++t) {
-            const size_t off = (size_t)t * batch * m->cfg.d_model;
-            PosRun pr{hP + off, xP + off, l < L ? sP + (size_t)t * batch : nullptr, l, l, l == 1};
-            const bool fin = l == L && t == P - 1;
-            enqueue_position(m, model_work(m), c, batch, false, fin, m->d_prompt, P, t, fin ? last : dbg, s, &pr);
-          }
-          if (l < L) {
-            launch_advance(c->lens, batch, s, -P);  // the next layer starts at the first position again
-            launch_sts_min(sP, P, batch, smin, s);
-            launch_decide(DECIDE_STS, false, m->st, nullptr, 0, m->d_gamma, l, L, batch, nullptr, smin, s);
-          }
-        }
-        HIPCHK(hipGetLastError());
-        HIPCHK(hipStreamSynchronize(s));
-      } else {
-        for (int t = 0; t < P; ++t)
-          enqueue_position(m, model_work(m), c, batch, false, t == P - 1, m->d_prompt, P, t, t == P - 1 ? last : dbg, s);
-      }
+      const bool want_logits = last_logits_host != nullptr;
+      if (want_logits && !m->dbg_logits) m->dbg_logits = m->alloc<float>((size_t)kMaxBatch * m->cfg.vocab);
+      if (m->cfg.prefill_exit && m->gamma.size())
+        HIPCHK(hipMemcpyAsync(m->d_gamma, m->gamma.data(), m->gamma.size() * 4, hipMemcpyHostToDevice, s));
+      run_prefill(m, c, batch, P, want_logits, s);
+      HIPCHK(hipGetLastError());
       HIPCHK(hipMemcpyAsync(c->next_tok, m->st->out_tok, batch * 4, hipMemcpyDeviceToDevice, s));
       HIPCHK(hipMemcpyAsync(m->h_out + kMaxBatch, m->st->e, batch * 4, hipMemcpyDeviceToHost, s));
       HIPCHK(hipMemcpyAsync(m->h_out, m->st->out_tok, batch * 4, hipMemcpyDeviceToHost, s));
-      if (last.logits)
+      if (want_logits)
         HIPCHK(hipMemcpyAsync(last_logits_host, m->dbg_logits, (size_t)batch * m->cfg.vocab * 4,
                               hipMemcpyDeviceToHost, s));
       HIPCHK(hipStreamSynchronize(s));

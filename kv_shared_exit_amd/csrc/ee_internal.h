@@ -124,6 +124,48 @@ struct AttnArgs {
   uint16_t* out;       // [b][H*hd]
 };
 
+// A prefill projection on matrix cores (ee_prefill.hip): for the sequences
+// list[0..*cnt), rows r = t * n + i (n = *cnt) are position t of sequence
+// list[i], physical row t * Bt + list[i] of x and of the outputs.
+// out = x W^T over K columns, W [N][K] bf16 in up to 3 row segments (QKV),
+// or the int4 copy (q4/s4, rows 0..N); SwiGLU: gate = wb[0] / q4, up = wb2 /
+// q4b, N = F.  int4 needs the per-row group sums of x (xs [row][ldxs]).
+enum GemmEpi { GEPI_BF16 = 0, GEPI_RESID = 1, GEPI_SWIGLU = 2 };
+struct GemmArgs {
+  int N, K, G;
+  int nseg;
+  int seg_end[3];
+  const uint16_t* wb[3];
+  const uint16_t* wb2;
+  const uint32_t* q4; const uint16_t* s4;
+  const uint32_t* q4b; const uint16_t* s4b;
+  const uint16_t* x; int ldx;
+  const float* xs; int ldxs;
+  const int32_t* list; const int32_t* cnt;
+  int P, Bt;
+  uint16_t* ob; int ldo;                 // GEPI_BF16 / GEPI_SWIGLU: bf16 out [row][ldo]
+  float* of; const float* src; int ldf;  // GEPI_RESID: of = src + x W^T (float32; src may be of)
+};
+// Launches a prefill projection over at most max_rows rows (grid bound; the
+// device-side count decides which tiles run).
+void launch_gemm(int epi, bool w4, const GemmArgs& a, int max_rows, hipStream_t s);
+// xs[row][g] = sum of x[row][g G .. (g + 1) G) for the rows of the listed sequences.
+void launch_group_sums(const uint16_t* x, int ldx, int K, int G, float* xs, int ldxs, const int32_t* list,
+                       const int32_t* cnt, int P, int Bt, hipStream_t s);
+// RoPE of q and k of every prompt row (row t * B + b: position lens[b] + t),
+// q into qrot [row][H * hd], k and v into the layer's cache slots.
+void launch_rope_kv(const uint16_t* qkv, int P, int B, int H, int Hkv, int hd, const float* cosT,
+                    const float* sinT, const int32_t* lens, uint16_t* qrot, uint16_t* Kl, uint16_t* Vl,
+                    uint8_t* occ_l, int S, hipStream_t s);
+// Causal attention of every prompt row over the layer's cache (positions
+// 0..lens[b] + t), out [row][H * hd] bf16.
+void launch_prefill_attention(const uint16_t* q, const uint16_t* K, const uint16_t* V, int S, int P, int B, int H,
+                              int Hkv, int hd, const int32_t* lens, uint16_t* out, hipStream_t s);
+// Embedding rows of every prompt row into h, the first layer's RMSNorm into
+// x, and the step state's row lists reset.
+void launch_prefill_embed(StepState* st, const int32_t* prompt, int P, int B, int L, const uint16_t* emb, int d,
+                          int V, float* h, const uint16_t* gain, float eps, uint16_t* x, hipStream_t s);
+
 // launchers (ee_kernels.hip)
 // Whether min(8, batch) input rows of width K fit the projection's LDS stage.
 bool proj_fits(int K, int batch);

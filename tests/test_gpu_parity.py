@@ -478,8 +478,8 @@ def test_prefill_sequence_exit_against_oracle(gpu, name, batch, P):
 
 def test_prefill_exit_off_and_unreachable_thresholds_equal_full_depth(gpu):
     """prefill_exit with thresholds a similarity cannot exceed runs every layer on
-    the backbone: the layer-by-layer prefill equals the position-by-position one
-    (tokens, exit layers, logits within rounding, K/V)."""
+    the backbone: it equals the prefill without the exit (tokens, exit layers,
+    logits within rounding, K/V)."""
     from kv_shared_exit_amd import api, _binding as Bd
     from parity import maxrel, TOL
     from oracle.numerics import from_bf16_bits
@@ -505,3 +505,51 @@ def test_prefill_exit_off_and_unreachable_thresholds_equal_full_depth(gpu):
         assert maxrel(l1[b], l0[b]) <= 1e-5
     for (k0, v0), (k1, v1) in zip(kv0, kv1):
         assert maxrel(from_bf16_bits(k1), from_bf16_bits(k0)) <= 1e-2
+
+
+@pytest.mark.parametrize("name,batch,chunks", [("odd", 3, (20, 1, 24)), ("hd64", 2, (33, 31)),
+                                               ("gqa4", 4, (64, 70))])
+def test_prefill_in_chunks_against_oracle(gpu, name, batch, chunks):
+    """The prefill's matrix-core path over several calls: each call appends its
+    positions after the cached ones, so its queries attend to the earlier
+    calls' K/V slots as well as to its own.  Against the oracle's prefill of
+    the whole prompt: every K/V slot of every layer, the last position's
+    logits and the token."""
+    from kv_shared_exit_amd import api
+    from parity import maxrel, TOL, GAP_BAND
+    from oracle import model as om
+    from oracle.numerics import from_bf16_bits
+    sh = SHAPES[name]
+    P = sum(chunks)
+    w = synth.make_weights(sh, 15)
+    prompts = np.random.default_rng(41).integers(0, sh.vocab, (batch, P)).astype(np.int32)
+    dev = api.upload_weights(w)
+    m = api.Model(sh, dev, gamma=2.0, max_batch=batch, max_positions=P + 1)
+    c = api.KVCache(m, batch, P + 1, track=True)
+    try:
+        p0 = 0
+        for n in chunks:
+            tg, lg = api.prefill(m, c, prompts[:, p0:p0 + n], logits=True)
+            p0 += n
+        assert list(c.lengths()) == [P] * batch
+        occ = c.occupancy()
+        assert np.all(occ[:, :batch, :P] == 1) and np.all(occ[:, :batch, P:] == 0)
+        kv = {(l, b): c.read(l, b, 0, P) for l in range(1, sh.n_layers + 1) for b in range(batch)}
+    finally:
+        c.close()
+        m.close()
+    orc = om.OracleModel(sh, w)
+    oc = om.KVCache(sh, batch, P + 1)
+    to, info = om.prefill(orc, oc, prompts)
+    for b in range(batch):
+        e = maxrel(lg[b], info["logits"][b])
+        assert e <= TOL, f"{name} b={b} logits maxrel {e:.3g}"
+        band = max(GAP_BAND, 2 * float(np.abs(lg[b].astype(np.float64) - info["logits"][b]).max()))
+        if info["gap"][b] > band:
+            assert tg[b] == to[b], f"{name} b={b} token"
+        for l in range(1, sh.n_layers + 1):
+            k, v = kv[(l, b)]
+            kr = oc.K[l - 1, b, :, :P].transpose(1, 0, 2)
+            vr = oc.V[l - 1, b, :, :P].transpose(1, 0, 2)
+            ek, ev = maxrel(from_bf16_bits(k), kr), maxrel(from_bf16_bits(v), vr)
+            assert ek <= TOL and ev <= TOL, f"{name} KV layer {l} seq {b}: {ek:.3g} {ev:.3g}"
