@@ -134,8 +134,10 @@ typedef struct ee_model_config {
                           (sample_seed, 0) and counter (v / 4, sequence, position, stream)
                           (streams: 1 draft, 2 final, 3 resample, 4 acceptance uniform, word
                           0 of block 0); u = ((x >> 41) + 0.5) / 2^23.  Needs EE_CRIT_HEAD,
-                          check_every <= 1, exit copies (not EE_EXIT_NONE) and max_batch
-                          <= 8 (else EE_ERR_UNSUPPORTED).  The prefill's token stays greedy. */
+                          check_every <= 1 and exit copies (not EE_EXIT_NONE), else
+                          INVALID_ARG.  Above 8 rows the sampled vocabulary passes take
+                          the rows 8 at a time (E is read once per 8 rows).  The
+                          prefill's token stays greedy. */
   uint32_t sample_seed;
   int32_t prefill_exit; /* 0: the prefill runs every layer on the backbone.  1: River-LLM's
                            sequence-level exit in the prefill (River-LLM explainer, sections 6.1

@@ -11,7 +11,8 @@ SOURCES = [os.path.join(PKG, "csrc", n) for n in ("ee_api.hip", "ee_kernels.hip"
                                                       "ee_wide.hip", "ee_sample.hip", "ee_prefill.hip")]
 # single-kernel launcher for hardware-counter runs (not part of the library)
 PROBE = os.path.join(PKG, "ee_probe")
-PROBE_SOURCES = [os.path.join(PKG, "csrc", n) for n in ("ee_probe.hip", "ee_proj.hip", "ee_wide.hip")]
+PROBE_SOURCES = [os.path.join(PKG, "csrc", n) for n in ("ee_probe.hip", "ee_proj.hip", "ee_wide.hip",
+                                                          "ee_kernels.hip", "ee_prefill.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -242,11 +242,9 @@ void validate_config(const ee_model_config& c) {
   if (c.prefill_exit)
     need(c.criterion == EE_CRIT_STS && c.exit_mode != EE_EXIT_NONE,
          "the prefill's sequence-level exit uses the state transition similarity and exit copies");
-  if (c.temperature > 0.0f) {
+  if (c.temperature > 0.0f)
     need(c.exit_mode != EE_EXIT_NONE && c.criterion == EE_CRIT_HEAD && c.check_every <= 1,
          "sampled decoding drafts from the exit head evaluated after every layer");
-    if (c.max_batch > 8) fail(EE_ERR_UNSUPPORTED, "sampled decoding supports max_batch <= 8");
-  }
   need(std::isfinite(c.rms_eps) && c.rms_eps > 0 && std::isfinite(c.rope_theta) && c.rope_theta > 0,
        "rms_eps and rope_theta must be positive");
   shape(c.group_size == 32 || c.group_size == 64 || c.group_size == 128, "group_size must be 32, 64 or 128");

@@ -50,7 +50,7 @@ struct StepState {
   float draft_logit[kMaxBatch];
   float draft_lse[kMaxBatch];
   float lse_f[kMaxBatch];
-  int32_t rej[kMaxBatch];
+  int32_t rej[2 * kMaxBatch];
   int32_t n_rej, pad2;
 };
 

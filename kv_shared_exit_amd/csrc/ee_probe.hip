@@ -15,6 +15,14 @@
 //                                bf16 weights and ni4 on the int4 G128 copy,
 //                                on the decode step's grid (512 workgroups)
 //   ee_probe copy MiB            one copy kernel reading and writing MiB each
+//   ee_probe read MiB reps       a read-only stream of MiB (each thread sums its
+//                                16-byte loads): the streaming-read ceiling
+//   ee_probe attn B S ctx reps   decode attention (attn_kernel + combine) of B
+//                                sequences at the 8B heads (32 q / 8 kv of 128)
+//                                over ctx + 1 cached positions, cache capacity S
+//   ee_probe gemm EPI M N K reps the prefill GEMM (EPI: bf16, resid or swiglu) of
+//                                M token rows (8 sequences of M / 8 positions)
+//                                with N x K bf16 weights (swiglu: gate and up)
 //
 // Prints the mean launch time (HIP events on the launch stream).
 #include <hip/hip_runtime.h>
@@ -26,6 +34,7 @@
 #include <vector>
 
 #include "ee_internal.h"
+#include "ee_device.h"
 
 using namespace ee;
 
@@ -43,10 +52,29 @@ __global__ void copy_kernel(const uint4* __restrict__ src, uint4* __restrict__ d
     dst[i] = src[i];
 }
 
+// Reads n 16-byte words (4 loads in flight per thread) and writes one word per thread.
+__global__ __launch_bounds__(256) void read_kernel(const uint4* __restrict__ src, uint32_t* __restrict__ out,
+                                                   size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  uint32_t acc = 0;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const uint4 a = ld_stream(src + i), b = ld_stream(src + i + stride);
+    const uint4 c = ld_stream(src + i + 2 * stride), d = ld_stream(src + i + 3 * stride);
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < n; i += stride) {
+    const uint4 a = ld_stream(src + i);
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
 static int usage() {
   std::fprintf(stderr,
                "usage: ee_probe lse V d rows reps | ee_probe wide V d rows reps | "
-               "ee_probe proj swiglu|part N K nbf ni4 reps | ee_probe copy MiB\n");
+               "ee_probe proj swiglu|part N K nbf ni4 reps | ee_probe copy MiB | ee_probe read MiB reps | "
+               "ee_probe attn B S ctx reps | ee_probe gemm bf16|resid|swiglu M N K reps\n");
   return 2;
 }
 
@@ -74,6 +102,125 @@ int main(int argc, char** argv) {
     float ms = 0;
     CK(hipEventElapsedTime(&ms, e0, e1));
     std::printf("copy %zu MiB: %.2f us, %.1f GB/s (read + write)\n", mib, 1e3 * ms, 2.0 * n * 16 / (ms * 1e6));
+    return 0;
+  }
+  auto timed = [&](auto&& launch, int reps) {
+    launch();  // warm-up
+    CK(hipStreamSynchronize(s));
+    CK(hipEventRecord(e0, s));
+    for (int r = 0; r < reps; ++r) launch();
+    CK(hipEventRecord(e1, s));
+    CK(hipEventSynchronize(e1));
+    float ms = 0;
+    CK(hipEventElapsedTime(&ms, e0, e1));
+    return 1e3 * ms / reps;  // us per launch
+  };
+  if (!std::strcmp(argv[1], "read")) {
+    if (argc < 4) return usage();
+    const size_t mib = std::strtoull(argv[2], nullptr, 10);
+    const int reps = std::atoi(argv[3]);
+    if (mib == 0 || mib > 16384 || reps < 1) return usage();
+    const size_t n = mib << 16;
+    uint4* src;
+    uint32_t* out;
+    CK(hipMalloc(&src, n * 16));
+    CK(hipMalloc(&out, (size_t)4096 * 256 * 4));
+    CK(hipMemsetAsync(src, 1, n * 16, s));
+    const double us = timed([&] { hipLaunchKernelGGL(read_kernel, dim3(4096), dim3(256), 0, s, src, out, n); }, reps);
+    std::printf("read %zu MiB: %.2f us, %.1f GB/s\n", mib, us, n * 16.0 / us / 1e3);
+    return 0;
+  }
+  if (!std::strcmp(argv[1], "attn")) {
+    if (argc < 6) return usage();
+    const int B = std::atoi(argv[2]), S = std::atoi(argv[3]), ctx = std::atoi(argv[4]), reps = std::atoi(argv[5]);
+    const int H = 32, Hkv = 8, hd = 128;
+    if (B < 1 || B > kMaxBatch || S < 2 || ctx < 0 || ctx >= S || reps < 1) return usage();
+    // the decode step's split: runs of tiles so that about 2048 waves are launched
+    const int tiles = (S + 63) / 64;
+    int tpw = 1;
+    while (tpw < tiles && (long long)B * Hkv * ((tiles + tpw - 1) / tpw) > 2048) tpw *= 2;
+    const int nch = (tiles + tpw - 1) / tpw;
+    uint16_t *q, *K, *V, *out;
+    float* part;
+    int32_t* lens;
+    const size_t kvn = (size_t)B * Hkv * S * hd;
+    CK(hipMalloc(&q, (size_t)B * H * hd * 2));
+    CK(hipMalloc(&K, kvn * 2));
+    CK(hipMalloc(&V, kvn * 2));
+    CK(hipMalloc(&out, (size_t)B * H * hd * 2));
+    CK(hipMalloc(&part, (size_t)B * H * nch * (hd + 2) * 4));
+    CK(hipMalloc(&lens, kMaxBatch * 4));
+    CK(hipMemsetAsync(q, 0x3c, (size_t)B * H * hd * 2, s));
+    CK(hipMemsetAsync(K, 0x3c, kvn * 2, s));
+    CK(hipMemsetAsync(V, 0x3c, kvn * 2, s));
+    std::vector<int32_t> hl(kMaxBatch, ctx);
+    CK(hipMemcpyAsync(lens, hl.data(), hl.size() * 4, hipMemcpyHostToDevice, s));
+    AttnArgs a{};
+    a.q = q;
+    a.K = K;
+    a.V = V;
+    a.S = S;
+    a.Bmax = B;
+    a.lens = lens;
+    a.H = H;
+    a.Hkv = Hkv;
+    a.hd = hd;
+    a.B = B;
+    a.tpw = tpw;
+    a.nch = nch;
+    a.scale = 0.08838834764831845f;
+    a.part = part;
+    a.out = out;
+    const double us = timed([&] { launch_attention(a, s); }, reps);
+    const double bytes = (double)B * (ctx + 1) * Hkv * hd * 2 * 2;
+    std::printf("attn B=%d S=%d ctx=%d tiles/wave=%d partials=%d: %.2f us (attention + combine), %.1f GB/s algorithmic\n",
+                B, S, ctx, tpw, nch, us, bytes / us / 1e3);
+    return 0;
+  }
+  if (!std::strcmp(argv[1], "gemm")) {
+    if (argc < 7) return usage();
+    const int epi = !std::strcmp(argv[2], "bf16") ? GEPI_BF16 : !std::strcmp(argv[2], "resid") ? GEPI_RESID
+                    : !std::strcmp(argv[2], "swiglu") ? GEPI_SWIGLU : -1;
+    const int M = std::atoi(argv[3]), N = std::atoi(argv[4]), K = std::atoi(argv[5]), reps = std::atoi(argv[6]);
+    if (epi < 0 || M < 8 || M % 8 || N < 32 || N % 32 || K < 32 || K % 32 || reps < 1) return usage();
+    const int nmat = epi == GEPI_SWIGLU ? 2 : 1;
+    uint16_t *W, *x, *ob;
+    float* of;
+    int32_t* lists;
+    CK(hipMalloc(&W, (size_t)nmat * N * K * 2));
+    CK(hipMalloc(&x, (size_t)M * K * 2));
+    CK(hipMalloc(&ob, (size_t)M * N * 2));
+    CK(hipMalloc(&of, (size_t)M * N * 4));
+    CK(hipMalloc(&lists, 2 * kMaxBatch * 4));
+    CK(hipMemsetAsync(W, 0x3c, (size_t)nmat * N * K * 2, s));
+    CK(hipMemsetAsync(x, 0x3c, (size_t)M * K * 2, s));
+    CK(hipMemsetAsync(of, 0, (size_t)M * N * 4, s));
+    std::vector<int32_t> hl(2 * kMaxBatch, 0);
+    for (int i = 0; i < 8; ++i) hl[i] = i;
+    hl[kMaxBatch] = 8;
+    CK(hipMemcpyAsync(lists, hl.data(), hl.size() * 4, hipMemcpyHostToDevice, s));
+    GemmArgs g{};
+    g.N = N;
+    g.K = K;
+    g.G = 128;
+    g.nseg = 1;
+    g.wb[0] = W;
+    g.seg_end[0] = g.seg_end[1] = g.seg_end[2] = N;
+    g.wb2 = W + (size_t)N * K;
+    g.x = x;
+    g.ldx = K;
+    g.list = lists;
+    g.cnt = lists + kMaxBatch;
+    g.P = M / 8;
+    g.Bt = 8;
+    g.ob = ob;
+    g.ldo = N;
+    g.of = of;
+    g.src = of;
+    g.ldf = N;
+    const double us = timed([&] { launch_gemm(epi, false, g, M, s); }, reps);
+    const double flops = 2.0 * M * (double)N * K * nmat;
+    std::printf("gemm %s M=%d N=%d K=%d: %.2f us, %.1f TFLOP/s\n", argv[2], M, N, K, us, flops / us / 1e6);
     return 0;
   }
   if (!std::strcmp(argv[1], "proj")) {

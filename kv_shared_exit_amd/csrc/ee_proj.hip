@@ -632,7 +632,10 @@ __device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int 
         const uint16_t* sb = p == 0 ? a.s4 : a.s4b;
         const int code = here ? c.code : nx.code;
         const int scale = here ? c.scale : nx.scale;
-        ra[p][i][0] = ld_stream(real ? (const void*)(cb + code + kk * 16) : (const void*)idle);
+        // cached load: a block's codes are half of a 128-byte line per row, the
+        // other half being the next block; a streaming load fetched the line
+        // twice (measured 1.37x the algorithmic bytes for gate/up, 1.035x cached)
+        ra[p][i][0] = *(const uint4*)(real ? (const void*)(cb + code + kk * 16) : (const void*)idle);
 #pragma unroll
         for (int g = 0; g < NG; ++g) sc[p][i][g] = *(const uint2*)(real ? sb + scale + (kk * NG + g) * 16 : idle);
       }
@@ -880,7 +883,8 @@ __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a)
     const int32_t* lip = a.list_i4;
     asm volatile("" ::"s"(lbp), "s"(lip));
   }
-  const int n_bf = min(max(*a.cnt_bf, 0), kMaxBatch);
+  // (the resampling pass's list holds row pairs: up to 2 * kMaxBatch entries)
+  const int n_bf = min(max(*a.cnt_bf, 0), EPI == EPI_RESAMPLE ? 2 * kMaxBatch : kMaxBatch);
   const int n_i4 = min(max(*a.cnt_i4, 0), kMaxBatch);
   if constexpr (EPI == EPI_LSE || EPI == EPI_ARGMAX) {
     if (n_bf > a.max_rows) return;  // the wide (MFMA) vocabulary pass has these rows

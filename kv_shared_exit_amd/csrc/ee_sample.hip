@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void sample_final_kernel(StepState* st, c
 __global__ __launch_bounds__(kThreads) void resample_final_kernel(StepState* st, const float* part_s, int nwg,
                                                                   int B, int V, int32_t* lens) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int n = min(max(st->n_rej, 0), kMaxBatch);
+  const int n = min(max(st->n_rej, 0), 2 * kMaxBatch);
   for (int i = 2 * w; i < n; i += 2 * kWavesS) {
     const int b = st->rej[i];
     float bv[kPer];
@@ -199,7 +199,7 @@ void launch_sample_draft(StepState* st, const float* part_s, int nwg, int layer,
 
 void launch_sample_final(StepState* st, const float* part_s, int nwg, int B, int L, int V, const int32_t* lens,
                          float itau, uint32_t seed, hipStream_t s) {
-  if (nwg < 1 || nwg > kNwgMax || B < 1 || B > kMaxBatch / 2 || !part_s || !(itau > 0.0f))
+  if (nwg < 1 || nwg > kNwgMax || B < 1 || B > kMaxBatch || !part_s || !(itau > 0.0f))
     throw std::logic_error("sample_final: bad arguments");
   hipLaunchKernelGGL(sample_final_kernel, dim3(1), dim3(kThreads), 0, s, st, part_s, nwg, B, L, V, lens, itau,
                      seed);

@@ -378,6 +378,24 @@ def test_sampled_decoding_rejections_are_resampled(gpu):
     assert res.sample_outcomes.count("rejected") >= 3, res.sample_outcomes
 
 
+@pytest.mark.parametrize("batch,alpha", [(12, 7.0), (40, 3000.0)], ids=["b12", "b40-rejections"])
+def test_sampled_decoding_above_8_rows(gpu, batch, alpha):
+    """Sampled decoding on batches above 8 rows (a model with the matrix-core
+    passes): the sampled vocabulary passes take the rows 8 at a time.  At 40
+    rows with one-hot-like exit heads most drafts are rejected, so the
+    resampling pass's list holds more than 32 row pairs."""
+    from parity import run_parity
+    sh = SHAPES["hd64"]   # widths of 256 multiples: the matrix-core passes run the other projections
+    w = synth.make_weights(sh, 9, alpha=np.full(sh.n_layers - 1, alpha))
+    L = sh.n_layers
+    forced = (lambda s: np.array([1 + (b + s) % L for b in range(batch)], np.int32)) if alpha < 100 else None
+    res = run_parity(sh, w, batch, 5, 3, 0.75, forced_fn=forced, label=f"sampled-b{batch}",
+                     temperature=1.0, seed=77)
+    assert res.compared_tokens >= batch
+    if alpha > 100:
+        assert res.sample_outcomes.count("rejected") >= 33, res.sample_outcomes.count("rejected")
+
+
 def test_sampled_low_temperature_equals_greedy(gpu):
     """tau -> 0: the verified draw is the greedy token (the draft is the exit
     head's argmax, accepted iff it is the final argmax, else the residual's
