@@ -37,12 +37,12 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 # scaled by what the same counter reads for a 1 GiB device copy.  Valid only
 # for the kernel sources it was measured on (their sha256); otherwise null.
 TRAFFIC = {
-    "lse": {"fetch_kib": 513409.2500, "write_kib": 62.6, "fetch_scale": 1.9999337, "write_scale": 0.9999999,
+    "lse": {"fetch_kib": 513413.3333, "write_kib": 62.6, "fetch_scale": 1.9999352, "write_scale": 1.0000000,
             "sources": ("ee_proj.hip", "ee_device.h", "ee_internal.h", "ee_epi.h"),
-            "sources_sha256": "103c9d3e5ac06464f52a5b324eb5ff39f008cdf3e86936110df8cf98c02a6173"},
-    "wide": {"fetch_kib": 519711.0833, "write_kib": 512.0, "fetch_scale": 1.9999313, "write_scale": 1.0000000,
+            "sources_sha256": "b10cab1bd33863035e8afbf9f526afdca686684595f01d2f91f12654a1de3556"},
+    "wide": {"fetch_kib": 519594.8750, "write_kib": 512.0, "fetch_scale": 1.9999352, "write_scale": 1.0000000,
              "sources": ("ee_wide.hip", "ee_device.h", "ee_internal.h", "ee_epi.h"),
-             "sources_sha256": "2979e14089340b485f6aa67f125d7a8e18c593fdac40b4614bdc7469e75f8e81"},
+             "sources_sha256": "51f0f9f18e06bbd59398ff466e70f2526021d17933a8f77c426121a635eae46d"},
 }
 # the workloads whose shape (128256 x 4096) the counters were taken at
 TRAFFIC_SHAPE = (128256, 4096)
@@ -148,26 +148,38 @@ def cpu_baseline(wl, weights, exits, ctx, criterion="head", every=1, budget_s=30
             "cpu_model": _cpu_model(), "blas": blas, "affinity_cores": cores}
 
 
-def hbm_copy_ceiling(reps=10):
-    """Device-to-device copy of 1 GiB (torch's copy kernel), timed with events on
-    the current stream: read + written bytes over the mean time, the streaming
-    ceiling a bandwidth-bound kernel is measured against."""
+def hbm_ceiling():
+    """Measured streaming ceilings of this GPU, for the roofline fractions:
+    a read-only stream of 4 GiB (the library's 16-byte non-temporal loads,
+    kv_shared_exit_amd/ee_probe read, 20 launches, run as a child process) and
+    torch's 1 GiB device-to-device copy (read + write, 10 launches timed with
+    events on the current stream)."""
+    import subprocess
     import torch
+    out = {}
+    probe = os.path.join(ROOT, "kv_shared_exit_amd", "ee_probe")
+    if os.path.exists(probe):
+        r = subprocess.run([probe, "read", "4096", "20"], capture_output=True, text=True, timeout=120)
+        if r.returncode == 0 and "GB/s" in r.stdout:
+            gbs = float(r.stdout.strip().split(",")[-1].split()[0])
+            out["read"] = {"kind": "4 GiB read stream (ee_probe read, 20 launches)", "GBps": gbs,
+                           "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
     x = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     y = torch.empty_like(x)
     y.copy_(x)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
-    for _ in range(reps):
+    for _ in range(10):
         y.copy_(x)
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    ms = e0.elapsed_time(e1) / 10
     gbs = 2 * x.numel() * 4 / (ms * 1e-3) / 1e9
     del x, y
-    return {"kind": "1 GiB device copy (read + write)", "GBps": round(gbs, 1),
-            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4), "ms": round(ms, 4)}
+    out["copy"] = {"kind": "1 GiB device copy, torch (read + write)", "GBps": round(gbs, 1),
+                   "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
 
 
 def prefill_flops(sh, B, P, chunk):
@@ -513,7 +525,7 @@ def main():
         out["roofline"] = {"bound": "hbm", "kernel": "whole decode step (no exit-head GEMV under this criterion)",
                            "achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(step_gbs / HBM_PEAK_GBS, 4), "traffic": None}
-    out["hbm_copy_ceiling"] = hbm_copy_ceiling()
+    out["hbm_ceiling"] = hbm_ceiling()
     if not args.no_baselines:
         out["speedup"] = baselines(api, wl, weights, dev, stream, exits, W, min(K, 40), 1e3 * t_el / K,
                                    criterion=crit, thresholds=thresholds, every=every, rule=rule)
