@@ -539,6 +539,11 @@ void enqueue_position(ee_model* m, const Work& W, ee_kv_cache* c, int B, bool he
       a.scale = (float)(1.0 / std::sqrt((double)hd));
       a.part = W.attn_part;
       a.out = W.attn_o;
+      // one workgroup per (sequence, kv head), merged in LDS, once there are
+      // enough pairs to give every CU one (measured at 64 x 8 pairs: 173
+      // against 178 us with the split runs and their combine; at 8 x 8 pairs
+      // the split runs are faster: 14 against 18 us)
+      a.fused = (long long)B * Hkv >= 256;
       launch_attention(a, s);
     }
     {

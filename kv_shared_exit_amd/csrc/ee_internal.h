@@ -82,6 +82,11 @@ struct ProjArgs {
   int H, Hkv, hd, S;
   int hd_log2;                                    // log2(hd)
   int nwg_r;                                      // workgroups per column range (set by launch_proj)
+  // (set by launch_proj) bf16 workgroups per range when both formats have
+  // rows, and the int4 pass's waves per 16-row tile [both formats * 2 + last
+  // range]: computed once on the host instead of by every wave
+  int nbf_mix;
+  int wpt4[4];
   int max_rows;                                   // EPI_LSE / EPI_ARGMAX: do nothing above this many rows
                                                   // (the wide pass has them); 0 = no limit
   // sampled epilogues: 1 / temperature, the generator's seed, partials by
@@ -122,6 +127,7 @@ struct AttnArgs {
   float scale;
   float* part;         // [B][H][nch][hd + 2]
   uint16_t* out;       // [b][H*hd]
+  int fused;           // one workgroup per (sequence, kv head), merged in LDS (no partials)
 };
 
 // A prefill projection on matrix cores (ee_prefill.hip): for the sequences

@@ -323,9 +323,181 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const AttnArgs a) {
   if (tid < hd) a.out[((size_t)b * a.H + h) * hd + tid] = (uint16_t)f2bf(O / L);
 }
 
+// Fused variant: one workgroup of kAttnFusedWaves waves per (sequence, kv head).
+// The waves take the context's 64-position tiles in turn (wave w: tiles w,
+// w + kAttnFusedWaves, ...), each keeping its own online softmax exactly as
+// attn_kernel does for a run; the waves' (m, l, o) then meet in LDS and are
+// merged in wave order, as the combine kernel merges partials, and the bf16
+// output is written directly: no partial buffer, no second launch.  Inside
+// the tile loop a wave only synchronises with itself (its probabilities go
+// through its own LDS slice), so waves with fewer tiles never wait at a
+// barrier the others reach more often.
+constexpr int kAttnFusedWaves = 8;
+
+template <int HD, int GQ>
+__global__ __launch_bounds__(64 * kAttnFusedWaves) void attn_fused_kernel(const AttnArgs a) {
+  constexpr int KK = HD / 32;
+  constexpr int CPR = HD / 8;
+  constexpr int RPI = 64 / CPR;
+  constexpr int NVL = 64 / RPI;
+  __shared__ float pbw[kAttnFusedWaves][64][GQ];
+  __shared__ float crw[kAttnFusedWaves][GQ];
+  __shared__ float pm[kAttnFusedWaves][GQ], pl[kAttnFusedWaves][GQ];
+  __shared__ float po[kAttnFusedWaves][GQ][HD];
+
+  const int j = blockIdx.x, b = blockIdx.y;
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int g = a.H / a.Hkv;
+  const int hh = lane & 15;
+  const int qc = lane >> 4;
+  const int smax = a.S - 1;
+  const size_t base = ((size_t)b * a.Hkv + j) * a.S;
+  const uint16_t* Kb = a.K + base * HD;
+  const uint16_t* Vb = a.V + base * HD;
+  const int vr = lane / CPR, vc = lane - vr * CPR;
+  float (*pb)[GQ] = pbw[wave];
+  float* cr = crw[wave];
+
+  uint4 kv[4][KK];
+  uint4 vv[NVL];
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+      const int row = min(t0 + pt * 16 + (lane & 15), smax);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) kv[pt][kk] = ld_stream(Kb + (size_t)row * HD + qc * 8 + 32 * kk);
+    }
+#pragma unroll
+    for (int i = 0; i < NVL; ++i) {
+      const int row = min(t0 + vr + i * RPI, smax);
+      vv[i] = ld_stream(Vb + (size_t)row * HD + vc * 8);
+    }
+  };
+  uint4 qv[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    qv[kk] = make_uint4(0, 0, 0, 0);
+    if (hh < g) qv[kk] = *(const uint4*)(a.q + ((size_t)b * a.H + j * g + hh) * HD + qc * 8 + 32 * kk);
+  }
+  const int ctx = a.lens[b] + 1;
+
+  float m = -INFINITY, l = 0.0f;
+  float o[GQ][8];
+#pragma unroll
+  for (int i = 0; i < GQ; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[i][e] = 0.0f;
+
+  for (int t0 = wave * 64; t0 < ctx; t0 += 64 * kAttnFusedWaves) {
+    load_tile(t0);
+    const int nval = min(64, ctx - t0);
+    float sc[4][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+      f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv[pt][kk]),
+                                                      __builtin_bit_cast(bf16x8_t, qv[kk]), acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = pt * 16 + qc * 4 + r;
+        sc[pt][r] = p < nval ? acc[r] * a.scale : -INFINITY;
+        mt = fmaxf(mt, sc[pt][r]);
+      }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float mn = fmaxf(m, mt);
+    const float corr = __expf(m - mn);
+    float ls = 0.0f;
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = __expf(sc[pt][r] - mn);
+        ls += p;
+        if (hh < GQ) pb[pt * 16 + qc * 4 + r][hh] = p;
+      }
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+    l = l * corr + ls;
+    m = mn;
+    if (lane < GQ) cr[lane] = corr;
+    // this wave's LDS slice: its stores complete before its loads (LDS
+    // operations of a wave are performed in order); the barrier keeps the
+    // compiler from moving them across
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < GQ; ++i) {
+      const float f = cr[i];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[i][e] *= f;
+    }
+#pragma unroll
+    for (int ii = 0; ii < NVL; ++ii) {
+      const int t = vr + ii * RPI;
+      if (t < nval) {
+        const uint4 v4 = vv[ii];
+        const float ve[8] = {bf2f(v4.x & 0xffffu), bf2f(v4.x >> 16), bf2f(v4.y & 0xffffu), bf2f(v4.y >> 16),
+                             bf2f(v4.z & 0xffffu), bf2f(v4.z >> 16), bf2f(v4.w & 0xffffu), bf2f(v4.w >> 16)};
+#pragma unroll
+        for (int i = 0; i < GQ; ++i) {
+          const float p = pb[t][i];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[i][e] = fmaf(p, ve[e], o[i][e]);
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+#pragma unroll
+  for (int sft = CPR; sft < 64; sft <<= 1)
+#pragma unroll
+    for (int i = 0; i < GQ; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[i][e] += __shfl_xor(o[i][e], sft);
+  // this wave's partial into LDS (a wave without tiles: m = -inf, l = 0)
+  if (vr == 0) {
+#pragma unroll
+    for (int i = 0; i < GQ; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) po[wave][i][vc * 8 + e] = o[i][e];
+  }
+  if (lane < GQ) {
+    pm[wave][lane] = m;
+    pl[wave][lane] = l;
+  }
+  __syncthreads();
+  // merge in wave order: weights exp(m_w - max m), empty partials skipped
+  for (int idx = threadIdx.x; idx < g * HD; idx += 64 * kAttnFusedWaves) {
+    const int i = idx / HD, dd = idx - i * HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kAttnFusedWaves; ++w) M = fmaxf(M, pm[w][i]);
+    float L = 0.0f, O = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kAttnFusedWaves; ++w) {
+      const float f = __expf(pm[w][i] - M);  // 0 for an empty partial
+      L = fmaf(pl[w][i], f, L);
+      O = f > 0.0f ? fmaf(po[w][i][dd], f, O) : O;
+    }
+    a.out[((size_t)b * a.H + j * g + i) * HD + dd] = (uint16_t)f2bf(O / L);
+  }
+}
+
 template <int HD, int GQ>
 static void launch_attn_t(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((attn_kernel<HD, GQ>), dim3(a.nch, a.Hkv, a.B), dim3(64), 0, s, a);
+  if (a.fused)
+    hipLaunchKernelGGL((attn_fused_kernel<HD, GQ>), dim3(a.Hkv, a.B), dim3(64 * kAttnFusedWaves), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_kernel<HD, GQ>), dim3(a.nch, a.Hkv, a.B), dim3(64), 0, s, a);
 }
 
 template <int HD>
@@ -344,7 +516,7 @@ void launch_attention(const AttnArgs& a, hipStream_t s) {
     case 64: launch_attn_hd<64>(a, s); break;
     default: launch_attn_hd<128>(a, s); break;
   }
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(a.H, a.B), dim3(128), 0, s, a);
+  if (!a.fused) hipLaunchKernelGGL(attn_combine_kernel, dim3(a.H, a.B), dim3(128), 0, s, a);
 }
 
 // ---------------------------------------------------------------------------

@@ -24,9 +24,9 @@
 //     that split its columns, each lane unpacks one dword of codes (8 weights)
 //     into the A operand in registers (nibble | 0x4300 is the bf16 value
 //     136 + q), the inputs are the B operand (batch rows padded to 16 with
-//     zeros), and a second MFMA with A = 136 everywhere yields 136 * sum(x) per
-//     step, which is removed before each group of G inputs is scaled by its
-//     bf16 scale.
+//     zeros); the input stage sums every staged row over each scale group,
+//     and 136 times that sum is removed before each group of G products is
+//     scaled by its bf16 scale.
 #include "ee_internal.h"
 #include "ee_device.h"
 #include "ee_epi.h"
@@ -114,13 +114,42 @@ constexpr int kItems = kXLdsElems / 8 / kProjThreads;
 // different banks.
 __device__ __forceinline__ int xstride(int K) { return K + 8; }
 
-// The first chunk's ids were put in LDS at kernel start (read with scalar
-// loads, before anything is stored); later chunks read the list here.
+// A chunk's sequence ids into LDS (padded with the chunk's last id).  The
+// first chunk's are read through the scalar cache (a uniform address) and
+// written after the pass has issued its first weight loads: vector loads of
+// them queued behind the weight loads the other waves of the CU had already
+// issued (measured: ~3.4 us of an 11 us int4 pass went to wave 0 waiting for
+// its ids before requesting its own weights).  Later chunks read the list
+// with vector loads.  stage_x's first barrier publishes the ids.  Every list
+// holds at least 8 entries (launch_proj points an absent one at kNoRows).
+using cint = const int32_t __attribute__((address_space(4)));
 __device__ __forceinline__ void stage_rows(const int32_t* list, int c0, int nb, int* seq) {
-  if (c0 > 0 && threadIdx.x < 8) seq[threadIdx.x] = list[c0 + min((int)threadIdx.x, nb - 1)];
+  if (c0 == 0) {
+    if (threadIdx.x < 8) {
+      const cint* lp = (const cint*)list;
+      const int e = min((int)threadIdx.x, nb - 1);
+      int v = lp[0];
+#pragma unroll
+      for (int k = 1; k < 8; ++k) {
+        const int w = lp[k];
+        v = e == k ? w : v;
+      }
+      seq[threadIdx.x] = v;
+    }
+  } else if (threadIdx.x < 8) {
+    seq[threadIdx.x] = list[c0 + min((int)threadIdx.x, nb - 1)];
+  }
 }
 
-__device__ __forceinline__ void stage_x(const ProjArgs& a, const Work& w, int nb, const int* seq, uint16_t* xs) {
+// With PPG > 0 (the int4 pass: PPG = G / 8 items per scale group) the stage
+// also writes gs[b * (K / G) + g] = the float32 sum of row b over scale group g
+// of the range: the 136 * sum(x) each group's codes carry (see the int4 pass)
+// is then taken from here instead of being computed by every wave.  The items
+// of a group sit in PPG consecutive threads (aligned: K is a multiple of G),
+// summed by a butterfly over those lanes.
+template <int PPG = 0>
+__device__ __forceinline__ void stage_x(const ProjArgs& a, const Work& w, int nb, const int* seq, uint16_t* xs,
+                                        float* gs = nullptr) {
   __syncthreads();  // seq is in LDS
   const int k8 = w.K >> 3;
   const int n = nb * k8;  // items; item i = (row b, column group kk) goes to xs[b * xstride(K) + kk*8]
@@ -144,6 +173,19 @@ __device__ __forceinline__ void stage_x(const ProjArgs& a, const Work& w, int nb
 #pragma unroll
   for (int j = 0; j < kItems; ++j) {
     const int i = tid + j * kProjThreads;
+    if constexpr (PPG > 0) {
+      // a group lies wholly below n or wholly above it (n and i are aligned
+      // to PPG), so every lane of a group takes part in its butterfly
+      if (j * kProjThreads < n) {
+        float t = 0.0f;
+        const uint32_t e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) t += bf2f(e[c] & 0xffffu) + bf2f(e[c] >> 16);
+#pragma unroll
+        for (int off = 1; off < PPG; off <<= 1) t += __shfl_xor(t, off);
+        if (i < n && (i & (PPG - 1)) == 0) gs[i / PPG] = t;
+      }
+    }
     if (i < n) {
       const int b = row_of(i);
       *(uint4*)&xs[b * xstride(w.K) + (i - b * k8) * 8] = v[j];
@@ -211,7 +253,6 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, const Work& wk, int
   float lmt = -INFINITY, lst = 0.0f, pb = -INFINITY, pl = -INFINITY;
   int pi = 0x7fffffff;
 
-  stage_rows(list, c0, nb, seq);
   // request the first tile's first weights before the inputs are staged
   const int nfull = K >> 9;                  // full 512-element steps (every lane active)
   const int kt = nfull * 512 + lane * 8;     // this lane's element in the ragged tail
@@ -231,6 +272,7 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, const Work& wk, int
 #pragma unroll
     for (int r = 0; r < RP; ++r) cur[r] = ld_stream(w[r]);
   }
+  stage_rows(list, c0, nb, seq);
   stage_x(a, wk, nb, seq, xs);
   __syncthreads();
 
@@ -487,28 +529,15 @@ __device__ __forceinline__ uint32_t pick(const uint4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
 
-// tot += (sl * s_row) * (C - C136) for the 4 rows of this lane (sv: their 4
-// scales; sl is 1, or 0 for a slot without work)
-__device__ __forceinline__ void i4_group_scale(const uint2& sv, float sl, const f32x4_t& cg, const f32x4_t& c136,
+// tot += (sl * s_row) * (C - corr) for the 4 rows of this lane (sv: their 4
+// scales; corr = 136 * the group's input sum; sl is 1, or 0 for a slot
+// without work)
+__device__ __forceinline__ void i4_group_scale(const uint2& sv, float sl, const f32x4_t& cg, float corr,
                                                f32x4_t& tot) {
-  tot[0] = fmaf(sl * bf2f(sv.x & 0xffffu), cg[0] - c136[0], tot[0]);
-  tot[1] = fmaf(sl * bf2f(sv.x >> 16), cg[1] - c136[1], tot[1]);
-  tot[2] = fmaf(sl * bf2f(sv.y & 0xffffu), cg[2] - c136[2], tot[2]);
-  tot[3] = fmaf(sl * bf2f(sv.y >> 16), cg[3] - c136[3], tot[3]);
-}
-
-__device__ __forceinline__ bf16x8_t k136_operand() {
-  const uint4 k136 = make_uint4(0x43084308u, 0x43084308u, 0x43084308u, 0x43084308u);  // bf16 136.0
-  return __builtin_bit_cast(bf16x8_t, k136);
-}
-
-template <int P>
-__device__ __forceinline__ void i4_step(const uint32_t (&word)[P], const uint4& bv, f32x4_t (&cg)[P],
-                                        f32x4_t& c136) {
-  const bf16x8_t b8 = __builtin_bit_cast(bf16x8_t, bv);
-  c136 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k136_operand(), b8, c136, 0, 0, 0);
-#pragma unroll
-  for (int p = 0; p < P; ++p) cg[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack8(word[p]), b8, cg[p], 0, 0, 0);
+  tot[0] = fmaf(sl * bf2f(sv.x & 0xffffu), cg[0] - corr, tot[0]);
+  tot[1] = fmaf(sl * bf2f(sv.x >> 16), cg[1] - corr, tot[1]);
+  tot[2] = fmaf(sl * bf2f(sv.y & 0xffffu), cg[2] - corr, tot[2]);
+  tot[3] = fmaf(sl * bf2f(sv.y >> 16), cg[3] - corr, tot[3]);
 }
 
 // Ring depth (blocks of 128 columns in flight per wave): bf16 blocks are 64
@@ -516,7 +545,7 @@ __device__ __forceinline__ void i4_step(const uint32_t (&word)[P], const uint4& 
 // the scales; within 128 VGPRs.
 template <bool BF, int P, int NG>
 struct MmaRing {
-  static constexpr int D = BF ? (P == 2 ? 1 : 2) : (P == 2 ? 1 : NG == 4 ? 2 : 4);
+  static constexpr int D = BF ? (P == 2 ? 1 : 2) : (P == 2 ? (NG == 1 ? 2 : 1) : NG == 4 ? 2 : 4);
 };
 
 // Waves sharing a 16-row tile (splitting its 128-column blocks), a power of
@@ -544,8 +573,8 @@ __host__ __device__ inline int mma_wpt(int nfull, int ntiles, int nwaves) {
 // 8q..8q+7 of each 32-column step); BF false unpacks int4 codes (see above).
 // The inputs are the B operand (batch rows padded to 16 with zeros).
 template <int EPI, int NG, bool BF>
-__device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int nb, const int32_t* list, int c0,
-                                         int* seq, uint16_t* xs, float* red) {
+__device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int wpt, int nb, const int32_t* list,
+                                         int c0, int* seq, uint16_t* xs, float* red, float* gs) {
   constexpr int P = Ep<EPI>::P;
   constexpr int D = MmaRing<BF, P, NG>::D;
   constexpr int SL = BF ? 4 : 1;  // 16-byte loads per block and matrix
@@ -563,7 +592,7 @@ __device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int 
   const int gk0 = wk.k0 / G;            // first group of this range
   const int nfull = K >> 7;
   const int ntail = (K & 127) >> 5;     // MFMA steps in the tail
-  const int wpt = mma_wpt(nfull, ntiles, wk.nwg * kWaves);
+  // (wpt = mma_wpt(nfull, ntiles, wk.nwg * kWaves), computed by launch_proj)
   const int lw = __builtin_ctz(wpt);
   const int tpi = kWaves >> lw;         // tiles per workgroup iteration
   const int ws = wave & (wpt - 1);      // this wave's K slice of its tile
@@ -574,6 +603,7 @@ __device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int 
   const bool bok = m < nb;
   const bool tail_here = ws == wpt - 1 && ntail > 0;
   const uint16_t* xrow = xs + (bok ? m : 0) * xstride(K);
+  const float* gsr = gs + (bok ? m : 0) * (K / G);  // int4: this column's group sums
 
   // weight row of MFMA A row mm of tile tt (the QKV epilogue pairs RoPE rows)
   // (bf16 rows past N read row N-1; int4 rows are padded to a multiple of 16)
@@ -641,13 +671,13 @@ __device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int 
       }
     }
   };
-  stage_rows(list, c0, nb, seq);
   TileAt at_cur = tile_at(0);
   if (nfull > 0) {
 #pragma unroll
     for (int i = 0; i < D; ++i) issue(at_cur, at_cur, true, i, i);
   }
-  stage_x(a, wk, nb, seq, xs);
+  stage_rows(list, c0, nb, seq);
+  stage_x<BF ? 0 : G / 8>(a, wk, nb, seq, xs, gs);
   __syncthreads();
 
   float lm = -INFINITY, ls = 0.0f;            // EPI_LSE: running (max, sum exp) of column m
@@ -684,26 +714,22 @@ __device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int 
           }
         } else {
           constexpr int MPG = 4 / NG;  // MFMA steps per scale group
-          // one matrix at a time (fewer live operands); the 136 * sum(x)
-          // correction of each group is computed with the first
-          f32x4_t c136g[NG];
+          // the group's 136 * sum(x) for this lane's batch column (0 for a
+          // padding column, whose inputs are zero)
+          float corr[NG];
+#pragma unroll
+          for (int g = 0; g < NG; ++g) corr[g] = bok ? 136.0f * gsr[u * NG + g] : 0.0f;
 #pragma unroll
           for (int p = 0; p < P; ++p) {
             f32x4_t cg = {0.0f, 0.0f, 0.0f, 0.0f};
-            f32x4_t c136 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
               uint4 bv = *(const uint4*)(xrow + u * 128 + 32 * st + 8 * q);
               if (!bok) bv = make_uint4(0, 0, 0, 0);
-              const bf16x8_t b8 = __builtin_bit_cast(bf16x8_t, bv);
-              if (p == 0) c136 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k136_operand(), b8, c136, 0, 0, 0);
-              cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack8(pick(ra[p][i][0], st)), b8, cg, 0, 0, 0);
+              cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack8(pick(ra[p][i][0], st)),
+                                                           __builtin_bit_cast(bf16x8_t, bv), cg, 0, 0, 0);
               if (st % MPG == MPG - 1) {
-                if (p == 0) {
-                  c136g[st / MPG] = c136;
-                  c136 = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-                }
-                i4_group_scale(sc[p][i][st / MPG], sl, cg, c136g[st / MPG], tot[p]);
+                i4_group_scale(sc[p][i][st / MPG], sl, cg, corr[st / MPG], tot[p]);
                 cg = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
               }
             }
@@ -716,6 +742,9 @@ __device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int 
       }
     }
     if (tail_here && t < ntiles) {  // K mod 128: steps of 32 columns, last wave of the tile
+      f32x4_t cgt[P];
+#pragma unroll
+      for (int p = 0; p < P; ++p) cgt[p] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       for (int st = 0; st < ntail; ++st) {
         const int ka = nfull * 128 + 32 * st;
         uint4 bv = *(const uint4*)(xrow + ka + 8 * q);
@@ -730,18 +759,24 @@ __device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int 
             tot[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), b8, tot[p], 0, 0, 0);
           }
         } else {
-          f32x4_t c136 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k136_operand(), b8, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f},
-                                                                 0, 0, 0);
+          // the tail holds whole scale groups (K is a multiple of G): the
+          // group's products accumulate over its steps and are scaled at its
+          // last step
 #pragma unroll
           for (int p = 0; p < P; ++p) {
             const uint32_t* cb = p == 0 ? a.q4 : a.q4b;
-            const uint16_t* sb = p == 0 ? a.s4 : a.s4b;
             const uint32_t word = cb[(size_t)arow(t, m) * ldc + ((wk.k0 + ka) >> 3) + q];
-            const f32x4_t cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack8(word), b8,
-                                                                       f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-            // scaled per 32-column step (every step lies in one group)
-            const uint2 sv = *(const uint2*)(sb + ((size_t)(r0 >> 4) * ngr + gk0 + ka / G) * 16 + (r0 & 15));
-            i4_group_scale(sv, 1.0f, cg, c136, tot[p]);
+            cgt[p] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(unpack8(word), b8, cgt[p], 0, 0, 0);
+          }
+          if ((st + 1) % (G / 32) == 0) {
+            const float corr = bok ? 136.0f * gsr[ka / G] : 0.0f;
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+              const uint16_t* sb = p == 0 ? a.s4 : a.s4b;
+              const uint2 sv = *(const uint2*)(sb + ((size_t)(r0 >> 4) * ngr + gk0 + ka / G) * 16 + (r0 & 15));
+              i4_group_scale(sv, 1.0f, cgt[p], corr, tot[p]);
+              cgt[p] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+            }
           }
         }
       }
@@ -765,12 +800,22 @@ __device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int 
         rw[3] = tot[p][3];
         __syncthreads();
         if (fin) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float s = 0.0f;
-            for (int ww = 0; ww < wpt; ++ww) s += red[((wave * wpt + ww) * 64 + lane) * 4 + i];
-            vals[p][i] = s;
+          // slices in order (wpt is an even power of two here), two reads
+          // in flight
+          float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+          const float* rs = red + ((wave * wpt) * 64 + lane) * 4;
+          for (int ww = 0; ww < wpt; ww += 2) {
+            const float4 u = *(const float4*)(rs + ww * 256);
+            const float4 v = *(const float4*)(rs + (ww + 1) * 256);
+            s0 = (s0 + u.x) + v.x;
+            s1 = (s1 + u.y) + v.y;
+            s2 = (s2 + u.z) + v.z;
+            s3 = (s3 + u.w) + v.w;
           }
+          vals[p][0] = s0;
+          vals[p][1] = s1;
+          vals[p][2] = s2;
+          vals[p][3] = s3;
         }
         __syncthreads();
       }
@@ -863,6 +908,9 @@ __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a)
   __shared__ __attribute__((aligned(16))) uint16_t xs[kXLdsElems + 8 * 8];
   __shared__ __attribute__((aligned(16))) float red[kWaves * 64 * 4];
   __shared__ int seqc[8];  // sequence ids of the staged rows of a later chunk
+  // int4 pass: sums of the staged rows over each scale group of the range
+  constexpr bool kI4 = EPI == EPI_PART || EPI == EPI_SWIGLU || EPI == EPI_QKV;
+  __shared__ float gsum[kI4 ? kXLdsElems / (128 / NG) : 1];
   Work wk;
   wk.nwg = a.nwg_r;
   wk.chunk = 0;
@@ -870,37 +918,18 @@ __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a)
   wk.wg = blockIdx.x - wk.chunk * wk.nwg;
   wk.k0 = wk.chunk * a.kc;
   wk.K = min(a.kc, a.K - wk.k0);
-  // Row counts and the first 8 ids of both lists, read before anything is
-  // stored (no chain of dependent loads before the first weights are
-  // requested); the staging relies on the padding below.  launch_proj points an absent list or count at kNoRows, so nothing here
-  // branches on a pointer (a branch per pointer serialised the loads: one
-  // memory latency each).  The list pointers are pinned to the first argument
-  // loads; lanes 0..7 of wave 0 read the first 8 ids of both lists and store
-  // them, a chunk's ids padded with its last id.
+  // Row counts, read through the scalar cache (uniform addresses) before
+  // anything else; launch_proj points an absent list or count at kNoRows, so
+  // nothing here branches on a pointer.  Each pass stages its own ids.
   __shared__ int seq0[2][8];
-  {
-    const int32_t* lbp = a.list_bf;
-    const int32_t* lip = a.list_i4;
-    asm volatile("" ::"s"(lbp), "s"(lip));
-  }
   // (the resampling pass's list holds row pairs: up to 2 * kMaxBatch entries)
-  const int n_bf = min(max(*a.cnt_bf, 0), EPI == EPI_RESAMPLE ? 2 * kMaxBatch : kMaxBatch);
-  const int n_i4 = min(max(*a.cnt_i4, 0), kMaxBatch);
+  const int n_bf = min(max(*(const cint*)a.cnt_bf, 0), EPI == EPI_RESAMPLE ? 2 * kMaxBatch : kMaxBatch);
+  const int n_i4 = min(max(*(const cint*)a.cnt_i4, 0), kMaxBatch);
   if constexpr (EPI == EPI_LSE || EPI == EPI_ARGMAX) {
     if (n_bf > a.max_rows) return;  // the wide (MFMA) vocabulary pass has these rows
   }
   if constexpr (EPI == EPI_RESAMPLE) {
     if (n_bf == 0) return;  // nothing rejected
-  }
-  if (threadIdx.x < 64) {
-    const int e = threadIdx.x & 7;
-    const int lb = a.list_bf[e], li = a.list_i4[e];
-    const int pb = __shfl(lb, max(min(n_bf, 8) - 1, 0));
-    const int pi = __shfl(li, max(min(n_i4, 8) - 1, 0));
-    if (threadIdx.x < 8) {
-      seq0[0][e] = e < n_bf ? lb : pb;
-      seq0[1][e] = e < n_i4 ? li : pi;
-    }
   }
   // When both weight formats have rows, the workgroups of each column range
   // split between them (the int4 share above its share of the bytes, since
@@ -909,15 +938,11 @@ __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a)
   // projection kind: QKV and O (at most 2 ranges) 176, the FFN (gate/up,
   // down) 128.
   int fmt_lo = 0, fmt_hi = 1;
+  int wsel = wk.chunk == a.nkc - 1 ? 1 : 0;  // int4 wave split: last range or not
   if constexpr (EPI == EPI_PART || EPI == EPI_QKV || EPI == EPI_SWIGLU) {
     if (n_bf > 0 && n_i4 > 0 && wk.nwg >= 2) {
-      const int share = (EPI == EPI_SWIGLU || a.nkc > 2) ? kBfShareFfn : kBfShare;
-      int nbf = min(wk.nwg - 1, max(1, (wk.nwg * share) >> 8));
-      // the bf16 waves take whole rounds of tiles: keep the rounds this share
-      // gives and hand the workgroups they do not need to the int4 rows
-      const int tb = (a.N + Ep<EPI>::R - 1) / Ep<EPI>::R;
-      const int rounds = (tb + nbf * kWaves - 1) / (nbf * kWaves);
-      nbf = min(nbf, max(1, (tb + rounds * kWaves - 1) / (rounds * kWaves)));
+      const int nbf = a.nbf_mix;
+      wsel += 2;
       if (wk.wg < nbf) {
         fmt_hi = 0;
         wk.nwg = nbf;
@@ -928,7 +953,8 @@ __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a)
       }
     }
   }
-  bool first = true;  // the first pass needs no barrier: its staging waits for seq0
+  const int wpt = a.wpt4[wsel];
+  bool first = true;  // the first pass needs no barrier: nothing in LDS is in use yet
   for (int fmt = fmt_lo; fmt <= fmt_hi; ++fmt) {
     if constexpr (Ep<EPI>::VOCAB || EPI == EPI_BF16) {
       if (fmt == 1) break;  // these run on backbone rows only
@@ -943,7 +969,7 @@ __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a)
       int* seq = c0 == 0 ? seq0[fmt] : seqc;
       if (fmt == 0) {
         if constexpr (kBf16Mfma) {
-          mma_pass<EPI, NG, true>(a, wk, nb, list, c0, seq, xs, red);
+          mma_pass<EPI, NG, true>(a, wk, wpt, nb, list, c0, seq, xs, red, gsum);
         } else {
           if (nb == 1)
             bf16_pass<EPI, 1>(a, wk, nb, list, c0, seq, xs, red);
@@ -956,7 +982,7 @@ __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a)
         }
       } else {
         if constexpr (EPI == EPI_PART || EPI == EPI_SWIGLU || EPI == EPI_QKV)
-          mma_pass<EPI, NG, false>(a, wk, nb, list, c0, seq, xs, red);
+          mma_pass<EPI, NG, false>(a, wk, wpt, nb, list, c0, seq, xs, red, gsum);
       }
     }
   }
@@ -1027,6 +1053,31 @@ int launch_proj(int epi, const ProjArgs& a0, int nwg, int batch, hipStream_t s, 
     throw std::logic_error("projection input too wide for the stage");
   }
   a.nwg_r = g / a.nkc;
+  // the workgroup split between the formats and the int4 wave split, as the
+  // device would derive them: bf16 share of each range (of 256: measured per
+  // projection kind), trimmed so the bf16 waves keep the whole rounds of
+  // tiles the share gives them; int4 waves per tile by mma_wpt
+  a.nbf_mix = 0;
+  for (int i = 0; i < 4; ++i) a.wpt4[i] = 1;
+  if (epi == EPI_PART || epi == EPI_SWIGLU || epi == EPI_QKV) {
+    const int nw = a.nwg_r;
+    if (nw >= 2) {
+      const int R = epi == EPI_SWIGLU ? 1 : 2;  // bf16 rows per wave tile
+      const int share = (epi == EPI_SWIGLU || a.nkc > 2) ? kBfShareFfn : kBfShare;
+      int nbf = std::min(nw - 1, std::max(1, (nw * share) >> 8));
+      const int tb = (a.N + R - 1) / R;
+      const int rounds = (tb + nbf * kWaves - 1) / (nbf * kWaves);
+      nbf = std::min(nbf, std::max(1, (tb + rounds * kWaves - 1) / (rounds * kWaves)));
+      a.nbf_mix = nbf;
+    }
+    const int ntiles = (a.N + 15) >> 4;
+    for (int mixed = 0; mixed < 2; ++mixed)
+      for (int last = 0; last < 2; ++last) {
+        const int kr = last ? a.K - (a.nkc - 1) * a.kc : a.kc;
+        const int nwr = mixed ? std::max(1, nw - a.nbf_mix) : nw;
+        a.wpt4[mixed * 2 + last] = mma_wpt(kr >> 7, ntiles, nwr * kWaves);
+      }
+  }
   if (epi == EPI_QKV && (a.hd < 32 || (a.hd & (a.hd - 1)) || (1 << a.hd_log2) != a.hd))
     throw std::logic_error("QKV epilogue needs a power-of-two head_dim >= 32 and its log2");
   switch (epi) {

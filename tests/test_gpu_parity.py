@@ -297,6 +297,21 @@ def test_wide_batch_vocabulary_pass(gpu, label, sh, batch):
     assert res.compared_tokens >= batch * 2
 
 
+def test_attention_one_workgroup_per_sequence_and_kv_head(gpu):
+    """32 sequences x 8 kv heads (256 pairs): decode attention runs one
+    workgroup per (sequence, kv head), whose 8 waves take the 9 tiles of each
+    521..523-position context in turn (wave 0 two, the last tile ragged), and
+    merges the waves' partial softmax states in LDS; half the rows exit after
+    layer 1, so layer 2 runs both weight formats."""
+    from parity import run_parity
+    sh = SHAPES["hd64"]
+    w = synth.make_weights(sh, 9)
+    B = 32
+    forced = np.where(np.arange(B) % 2 == 0, 1, 0).astype(np.int32)
+    res = run_parity(sh, w, B, 520, 3, 2.0, forced_fn=lambda s: forced, label="fused-attn-b32")
+    assert res.compared_tokens >= B * 2
+
+
 # ---------------------------------------------------------------------------
 # The batch-minimum exit rule
 # ---------------------------------------------------------------------------
