@@ -83,9 +83,11 @@ struct ProjArgs {
   int hd_log2;                                    // log2(hd)
   int nwg_r;                                      // workgroups per column range (set by launch_proj)
   // (set by launch_proj) bf16 workgroups per range when both formats have
-  // rows, and the int4 pass's waves per 16-row tile [both formats * 2 + last
+  // rows, workgroups per range that work when only int4 rows are present,
+  // and the int4 pass's waves per 16-row tile [both formats * 2 + last
   // range]: computed once on the host instead of by every wave
   int nbf_mix;
+  int nwg_i4;
   int wpt4[4];
   int max_rows;                                   // EPI_LSE / EPI_ARGMAX: do nothing above this many rows
                                                   // (the wide pass has them); 0 = no limit
