@@ -431,12 +431,19 @@ __global__ __launch_bounds__(kProjThreads, 4) void wide_proj_kernel(const WideAr
     const uint32_t* cp = a.q4[seg] + (size_t)(ts * 16 + (lane & 15)) * (a.K >> 3) + (k0 >> 3) + (lane >> 4) * 4;
     const uint16_t* sp = a.s4[seg] + ((size_t)ts * ngr + k0 / G) * 16 + 4 * (lane >> 4);
     const int nbk = kw >> 7;  // 128-column blocks of the range
-    uint4 rc[2];
-    uint2 rs[2][NG];
+    // codes of two chunks (RD = 4 blocks) in flight at group size 128: slots
+    // 0-1 hold the even chunks' blocks, 2-3 the odd chunks' (the chunk loop is
+    // unrolled by two so every slot index is fixed); smaller groups keep one
+    // chunk (their scales take the registers).  Cached loads: a block's codes
+    // are half of a 128-byte line per row, the other half being the next
+    // block.
+    constexpr int RD = NG == 1 ? 4 : 2;
+    uint4 rc[RD];
+    uint2 rs[RD][NG];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < RD; ++i) {
       const int u = min(i, nbk - 1);
-      rc[i] = ld_stream(cp + u * 16);
+      rc[i] = *(const uint4*)(cp + u * 16);
 #pragma unroll
       for (int g = 0; g < NG; ++g) rs[i][g] = *(const uint2*)(sp + (u * NG + g) * 16);
     }
@@ -447,19 +454,21 @@ __global__ __launch_bounds__(kProjThreads, 4) void wide_proj_kernel(const WideAr
     f32x4_t cg[4];
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) cg[bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int c = 0; c < nch; ++c) {
+    // one 256-column chunk: its two blocks from ring slots sl, sl + 1, which
+    // are then refilled with the blocks RD / 2 chunks ahead
+    auto do_chunk = [&](const int c, const int sl) {
       const uint16_t* xb = xs + (c & 1) * kWideBuf + (lane & 15) * kWideStride + (lane >> 4) * 8;
       const float* xsr = &xsum[c & 1][lane & 15][0];
 #pragma unroll
       for (int ub = 0; ub < 2; ++ub) {
-        const uint4 cw = rc[ub];
+        const uint4 cw = rc[sl + ub];
         uint2 sv[NG];
 #pragma unroll
-        for (int g = 0; g < NG; ++g) sv[g] = rs[ub][g];
-        const int un = min(c * 2 + ub + 2, nbk - 1);  // past the end: reload (unused)
-        rc[ub] = ld_stream(cp + un * 16);
+        for (int g = 0; g < NG; ++g) sv[g] = rs[sl + ub][g];
+        const int un = min(c * 2 + ub + RD, nbk - 1);  // past the end: reload (unused)
+        rc[sl + ub] = *(const uint4*)(cp + un * 16);
 #pragma unroll
-        for (int g = 0; g < NG; ++g) rs[ub][g] = *(const uint2*)(sp + (un * NG + g) * 16);
+        for (int g = 0; g < NG; ++g) rs[sl + ub][g] = *(const uint2*)(sp + (un * NG + g) * 16);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const bf16x8_t aop = unpack8(pick(cw, j));
@@ -490,6 +499,14 @@ __global__ __launch_bounds__(kProjThreads, 4) void wide_proj_kernel(const WideAr
       if (c + 1 < nch) EE_STAGE_STORE((c + 1) & 1);
       __syncthreads();
       EE_STAGE_LOAD(min(c + 2, nch - 1));
+    };
+    if constexpr (RD == 4) {
+      for (int c = 0; c < nch; c += 2) {
+        do_chunk(c, 0);
+        if (c + 1 < nch) do_chunk(c + 1, 2);  // uniform
+      }
+    } else {
+      for (int c = 0; c < nch; ++c) do_chunk(c, 0);
     }
   }
 #undef EE_STAGE_LOAD
