@@ -542,8 +542,23 @@ __global__ __launch_bounds__(kHeadThreads) void decide_kernel(StepState* st, con
   __shared__ int sx[kMaxBatch];
   __shared__ float pv[kMaxBatch];
   __shared__ float2 red[kHeadWaves][kMaxBatch];
-  __shared__ int sn;
+  __shared__ int sact[kMaxBatch], sfrc[kMaxBatch];
+  __shared__ float ssts[kMaxBatch];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  // the step state of every row (lists, forced layers, exit flags, the
+  // similarities), the row count and the threshold, requested before the
+  // partials so that nothing after the merge waits for memory (every array
+  // holds kMaxBatch entries)
+  int act_t = 0, frc_t = 0, exi_t = 0;
+  float sts_t = 0.0f;
+  if ((int)threadIdx.x < kMaxBatch) {
+    act_t = st->act[threadIdx.x];
+    frc_t = st->forced[threadIdx.x];
+    exi_t = st->exited[threadIdx.x];
+    if constexpr (STS) sts_t = sts[threadIdx.x];
+  }
+  const int n_act = st->n_act;
+  const float gam = MODE != DECIDE_FORCED ? gamma[layer - 1] : 0.0f;
   // DECIDE_HEAD, the (max, sum exp) partials of every list position into
   // red[wave][position] (merged over the waves below).  All loads are
   // requested before the row count is known (positions below the batch, or
@@ -597,25 +612,29 @@ __global__ __launch_bounds__(kHeadThreads) void decide_kernel(StepState* st, con
       if (kk == 0) red[w][pos] = v[0];
     }
   }
-  if ((int)threadIdx.x < B) sx[threadIdx.x] = st->exited[threadIdx.x];
-  if (threadIdx.x == 0) sn = min(max(st->n_act, 0), B);
+  if ((int)threadIdx.x < kMaxBatch) {
+    sx[threadIdx.x] = exi_t;
+    sact[threadIdx.x] = act_t;
+    sfrc[threadIdx.x] = frc_t;
+    if constexpr (STS) ssts[threadIdx.x] = sts_t;
+  }
   __syncthreads();
-  const int n = sn;
+  const int n = min(max(n_act, 0), B);
   // one thread per list position (n <= kMaxBatch < kHeadThreads)
   const int i = threadIdx.x;
   if (i < n) {
-    const int b = st->act[i];
+    const int b = sact[i];
     float p = 0.0f;
     if constexpr (STS) {
-      p = sts[b];
+      p = ssts[b];
     } else if constexpr (MODE == DECIDE_HEAD) {
       float m = -INFINITY, sum = 0.0f;
 #pragma unroll
       for (int ww = 0; ww < kHeadWaves; ++ww) lse_merge(m, sum, red[ww][i].x, red[ww][i].y);
       p = 1.0f / sum;
     }
-    const int f = st->forced[b];
-    const bool own = MODE != DECIDE_FORCED && !batch_min && p > gamma[layer - 1];
+    const int f = sfrc[b];
+    const bool own = MODE != DECIDE_FORCED && !batch_min && p > gam;
     const bool ex = f > 0 ? (layer == f) : own;
     if (p_rec && MODE != DECIDE_FORCED) p_rec[(layer - 1) * kMaxBatch + b] = p;
     pv[i] = p;
@@ -630,14 +649,14 @@ __global__ __launch_bounds__(kHeadThreads) void decide_kernel(StepState* st, con
       float mn = INFINITY;
       bool any = false;
       for (int i = 0; i < n; ++i)
-        if (st->forced[st->act[i]] == 0) {
+        if (sfrc[sact[i]] == 0) {
           mn = fminf(mn, pv[i]);
           any = true;
         }
-      if (any && mn > gamma[layer - 1])
+      if (any && mn > gam)
         for (int i = 0; i < n; ++i) {
-          const int b = st->act[i];
-          if (st->forced[b] == 0) {
+          const int b = sact[i];
+          if (sfrc[b] == 0) {
             sx[b] = 1;
             st->e[b] = layer;
           }
