@@ -37,12 +37,12 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 # scaled by what the same counter reads for a 1 GiB device copy.  Valid only
 # for the kernel sources it was measured on (their sha256); otherwise null.
 TRAFFIC = {
-    "lse": {"fetch_kib": 513396.0208, "write_kib": 62.6, "fetch_scale": 1.9999330, "write_scale": 0.9999998,
+    "lse": {"fetch_kib": 513396.0625, "write_kib": 62.6, "fetch_scale": 1.9999340, "write_scale": 0.9999999,
             "sources": ("ee_proj.hip", "ee_device.h", "ee_internal.h", "ee_epi.h"),
             "sources_sha256": "8254a30322e114e4e64b8044ee5e090b551ca582a2fbe7d0e5958ebf5878f686"},
-    "wide": {"fetch_kib": 519681.3958, "write_kib": 512.0, "fetch_scale": 1.9999330, "write_scale": 0.9999998,
+    "wide": {"fetch_kib": 519726.1562, "write_kib": 512.0, "fetch_scale": 1.9999340, "write_scale": 0.9999999,
              "sources": ("ee_wide.hip", "ee_device.h", "ee_internal.h", "ee_epi.h"),
-             "sources_sha256": "86d5395160992fff22b3e67b270990b4a531b35e1f53d0ef5a22e83e2be6ef5e"},
+             "sources_sha256": "688c73a7235055158949647e8ac19ee8d79f59e74b726ca0684686edd548102e"},
 }
 # the workloads whose shape (128256 x 4096) the counters were taken at
 TRAFFIC_SHAPE = (128256, 4096)
@@ -151,19 +151,23 @@ def cpu_baseline(wl, weights, exits, ctx, criterion="head", every=1, budget_s=30
 def hbm_ceiling():
     """Measured streaming ceilings of this GPU, for the roofline fractions:
     a read-only stream of 4 GiB (the library's 16-byte non-temporal loads,
-    kv_shared_exit_amd/ee_probe read, 20 launches, run as a child process) and
-    torch's 1 GiB device-to-device copy (read + write, 10 launches timed with
-    events on the current stream)."""
+    kv_shared_exit_amd/ee_probe read, 20 launches, run as a child process;
+    the grid sweeps the buffer in strided rounds), the same bytes read with
+    one contiguous region per workgroup (ee_probe readc), and torch's 1 GiB
+    device-to-device copy (read + write, 10 launches timed with events on the
+    current stream)."""
     import subprocess
     import torch
     out = {}
     probe = os.path.join(ROOT, "kv_shared_exit_amd", "ee_probe")
     if os.path.exists(probe):
-        r = subprocess.run([probe, "read", "4096", "20"], capture_output=True, text=True, timeout=120)
-        if r.returncode == 0 and "GB/s" in r.stdout:
-            gbs = float(r.stdout.strip().split(",")[-1].split()[0])
-            out["read"] = {"kind": "4 GiB read stream (ee_probe read, 20 launches)", "GBps": gbs,
-                           "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        for key, mode, kind in (("read", "read", "4 GiB read stream, strided rounds (ee_probe read, 20 launches)"),
+                                ("read_regions", "readc",
+                                 "4 GiB read, one contiguous region per workgroup (ee_probe readc, 20 launches)")):
+            r = subprocess.run([probe, mode, "4096", "20"], capture_output=True, text=True, timeout=120)
+            if r.returncode == 0 and "GB/s" in r.stdout:
+                gbs = float(r.stdout.strip().split(",")[-1].split()[0])
+                out[key] = {"kind": kind, "GBps": gbs, "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
     x = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     y = torch.empty_like(x)
     y.copy_(x)

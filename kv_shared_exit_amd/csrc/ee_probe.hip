@@ -17,6 +17,8 @@
 //   ee_probe copy MiB            one copy kernel reading and writing MiB each
 //   ee_probe read MiB reps       a read-only stream of MiB (each thread sums its
 //                                16-byte loads): the streaming-read ceiling
+//   ee_probe readc MiB reps      the same bytes read with one contiguous region
+//                                per workgroup (512 workgroups)
 //   ee_probe attn B S ctx reps   decode attention (attn_kernel + combine) of B
 //                                sequences at the 8B heads (32 q / 8 kv of 128)
 //                                over ctx + 1 cached positions, cache capacity S
@@ -70,10 +72,27 @@ __global__ __launch_bounds__(256) void read_kernel(const uint4* __restrict__ src
   out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+// Each workgroup reads one contiguous region of n / gridDim.x words, 4 loads
+// in flight per thread, and writes one word per thread.
+__global__ __launch_bounds__(256) void read_region_kernel(const uint4* __restrict__ src, uint32_t* __restrict__ out,
+                                                          size_t n) {
+  const size_t per = n / gridDim.x;
+  const uint4* base = src + (size_t)blockIdx.x * per;
+  uint32_t acc = 0;
+  size_t i = threadIdx.x;
+  for (; i + 3 * blockDim.x < per; i += 4 * blockDim.x) {
+    const uint4 a = ld_stream(base + i), b = ld_stream(base + i + blockDim.x);
+    const uint4 c = ld_stream(base + i + 2 * blockDim.x), d = ld_stream(base + i + 3 * blockDim.x);
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < per; i += blockDim.x) acc ^= ld_stream(base + i).x;
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
 static int usage() {
   std::fprintf(stderr,
                "usage: ee_probe lse V d rows reps | ee_probe wide V d rows reps | "
-               "ee_probe proj swiglu|part N K nbf ni4 reps | ee_probe copy MiB | ee_probe read MiB reps | "
+               "ee_probe proj swiglu|part N K nbf ni4 reps | ee_probe copy MiB | ee_probe read|readc MiB reps | "
                "ee_probe attn B S ctx reps | ee_probe gemm bf16|resid|swiglu M N K reps\n");
   return 2;
 }
@@ -115,7 +134,8 @@ int main(int argc, char** argv) {
     CK(hipEventElapsedTime(&ms, e0, e1));
     return 1e3 * ms / reps;  // us per launch
   };
-  if (!std::strcmp(argv[1], "read")) {
+  const bool region = !std::strcmp(argv[1], "readc");
+  if (!std::strcmp(argv[1], "read") || region) {
     if (argc < 4) return usage();
     const size_t mib = std::strtoull(argv[2], nullptr, 10);
     const int reps = std::atoi(argv[3]);
@@ -126,8 +146,15 @@ int main(int argc, char** argv) {
     CK(hipMalloc(&src, n * 16));
     CK(hipMalloc(&out, (size_t)4096 * 256 * 4));
     CK(hipMemsetAsync(src, 1, n * 16, s));
-    const double us = timed([&] { hipLaunchKernelGGL(read_kernel, dim3(4096), dim3(256), 0, s, src, out, n); }, reps);
-    std::printf("read %zu MiB: %.2f us, %.1f GB/s\n", mib, us, n * 16.0 / us / 1e3);
+    const double us = timed(
+        [&] {
+          if (region)
+            hipLaunchKernelGGL(read_region_kernel, dim3(512), dim3(256), 0, s, src, out, n);
+          else
+            hipLaunchKernelGGL(read_kernel, dim3(4096), dim3(256), 0, s, src, out, n);
+        },
+        reps);
+    std::printf("%s %zu MiB: %.2f us, %.1f GB/s\n", region ? "readc" : "read", mib, us, n * 16.0 / us / 1e3);
     return 0;
   }
   if (!std::strcmp(argv[1], "attn")) {
