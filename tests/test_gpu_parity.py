@@ -82,6 +82,20 @@ def test_forced_exit_schedule(gpu, name):
                      label=f"{name}-forced")
 
 
+@pytest.mark.parametrize("name,batch", [("odd", 5), ("mid", 8)])
+def test_every_row_exited_after_layer_one(gpu, name, batch):
+    """Every sequence exits after layer 1, so layers 2..L run only exited rows:
+    the projections take the smaller grid of that case (widths with int4 tails
+    and ragged 16-row tiles in "odd", a 5120-column input in "mid")."""
+    from parity import run_parity
+    sh = SHAPES[name]
+    w = synth.make_weights(sh, 13)
+    res = run_parity(sh, w, batch, 5, 3, 0.75, forced_fn=lambda s: np.ones(batch, np.int32),
+                     label=f"{name}-all-exited")
+    for e in res.exits:
+        assert (e == 1).all(), e
+
+
 @pytest.mark.parametrize("name", ["odd", "mid"])
 def test_unquantised_exit_copies(gpu, name):
     from parity import run_parity
