@@ -33,6 +33,28 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// Lane exchange within a row of 16 lanes through the DPP modifier (no LDS
+// round trip): C is the DPP control (0xB1 quad_perm [1,0,3,2], 0x4E quad_perm
+// [2,3,0,1], 0x141 row_half_mirror, 0x140 row_mirror).
+template <int C>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), C, 0xF, 0xF, false));
+}
+
+// Sum over each aligned group of N adjacent lanes (N = 1, 2, 4, 8 or 16),
+// left in every lane of the group: exchanges with lane ^ 1 and lane ^ 2, then
+// with the mirrored lane of the 8- and the 16-lane half (after the quads hold
+// their sums, the mirrored lane holds the other quad's, or the other half's).
+template <int N>
+__device__ __forceinline__ float group_sum_dpp(float v) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "group of 1..16 lanes");
+  if constexpr (N >= 2) v += dpp_f<0xB1>(v);
+  if constexpr (N >= 4) v += dpp_f<0x4E>(v);
+  if constexpr (N >= 8) v += dpp_f<0x141>(v);
+  if constexpr (N >= 16) v += dpp_f<0x140>(v);
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // Cross-lane "transpose-reduce": V partial sums per lane, summed over the 64
 // lanes of the wave.  Each halving stage keeps half of the values and trades

@@ -34,6 +34,7 @@
 
 #include <algorithm>
 #include <stdexcept>
+#include <type_traits>
 
 namespace ee {
 
@@ -41,7 +42,7 @@ namespace {
 
 constexpr int kWideRows = 64;             // batch rows of one pass (MFMA B columns)
 constexpr int kWideCols = 256;            // input columns staged per chunk
-constexpr int kWideStride = kWideCols + 8;  // LDS row stride (16 bytes of padding)
+constexpr int kWideStride = kWideCols + 16;  // LDS row stride: 32 bytes of padding (no bank conflicts in the operand reads)
 constexpr int kWideBuf = kWideRows * kWideStride;
 constexpr int kWideWaves = kProjThreads / 64;
 constexpr int kWideTiles = 1;             // 16-row tiles per wave
@@ -64,16 +65,17 @@ __device__ __forceinline__ uint32_t pick(const uint4& v, int j) {
   return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
 }
 
-// Sum of one staged 16-byte piece (8 bf16 inputs) over the PPG pieces of its
-// scale group (adjacent lanes of the row's 32), stored by the group's first lane
+// Sum of one staged 16-byte piece (8 bf16 inputs: four dot products with
+// (1, 1)) over the PPG pieces of its scale group (adjacent lanes of the row's
+// 32, summed through DPP), stored by the group's first lane
 template <int PPG>
 __device__ __forceinline__ void wide_group_sum(const uint4& v, float* row_sums, int tid) {
-  float t = 0.0f;
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) t += bf2f(w[i] & 0xffffu) + bf2f(w[i] >> 16);
-#pragma unroll
-  for (int off = 1; off < PPG; off <<= 1) t += __shfl_xor(t, off);
+  constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 (1, 1)
+  float t = dot2(v.x, kOnes, 0.0f);
+  t = dot2(v.y, kOnes, t);
+  t = dot2(v.z, kOnes, t);
+  t = dot2(v.w, kOnes, t);
+  t = group_sum_dpp<PPG>(t);
   if ((tid & (PPG - 1)) == 0) row_sums[(tid & 31) / PPG] = t;
 }
 
@@ -369,159 +371,181 @@ __global__ __launch_bounds__(kProjThreads, 4) void wide_proj_kernel(const WideAr
   const uint16_t* sx[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) sx[j] = a.x + (size_t)list[min(srow + 16 * j, n - 1)] * a.x_stride + k0 + scol;
-  uint4 s0, s1, s2, s3;
-#define EE_STAGE_LOAD(c)                \
-  do {                                  \
-    const int co_ = (c) * kWideCols;    \
-    s0 = *(const uint4*)(sx[0] + co_);  \
-    s1 = *(const uint4*)(sx[1] + co_);  \
-    s2 = *(const uint4*)(sx[2] + co_);  \
-    s3 = *(const uint4*)(sx[3] + co_);  \
+  uint4 s0, s1{}, s2{}, s3{};
+  // (used inside the loop body below: only the NBS blocks of rows are staged)
+#define EE_STAGE_LOAD(c)                            \
+  do {                                              \
+    const int co_ = (c) * kWideCols;                \
+    s0 = *(const uint4*)(sx[0] + co_);              \
+    if (NBS > 1) s1 = *(const uint4*)(sx[1] + co_); \
+    if (NBS > 2) s2 = *(const uint4*)(sx[2] + co_); \
+    if (NBS > 3) s3 = *(const uint4*)(sx[3] + co_); \
   } while (0)
-#define EE_STAGE_STORE(buf)                                           \
-  do {                                                                \
-    uint16_t* d_ = xs + (buf) * kWideBuf + srow * kWideStride + scol; \
-    *(uint4*)(d_) = s0;                                               \
-    *(uint4*)(d_ + 16 * kWideStride) = s1;                            \
-    *(uint4*)(d_ + 32 * kWideStride) = s2;                            \
-    *(uint4*)(d_ + 48 * kWideStride) = s3;                            \
-    if (i4) {                                                         \
-      wide_group_sum<PPG>(s0, xsum[buf][srow], tid);                  \
-      wide_group_sum<PPG>(s1, xsum[buf][srow + 16], tid);             \
-      wide_group_sum<PPG>(s2, xsum[buf][srow + 32], tid);             \
-      wide_group_sum<PPG>(s3, xsum[buf][srow + 48], tid);             \
-    }                                                                 \
+#define EE_STAGE_STORE(buf)                                                   \
+  do {                                                                        \
+    uint16_t* d_ = xs + (buf) * kWideBuf + srow * kWideStride + scol;         \
+    *(uint4*)(d_) = s0;                                                       \
+    if (NBS > 1) *(uint4*)(d_ + 16 * kWideStride) = s1;                       \
+    if (NBS > 2) *(uint4*)(d_ + 32 * kWideStride) = s2;                       \
+    if (NBS > 3) *(uint4*)(d_ + 48 * kWideStride) = s3;                       \
+    if (i4) {                                                                 \
+      wide_group_sum<PPG>(s0, xsum[buf][srow], tid);                          \
+      if (NBS > 1) wide_group_sum<PPG>(s1, xsum[buf][srow + 16], tid);        \
+      if (NBS > 2) wide_group_sum<PPG>(s2, xsum[buf][srow + 32], tid);        \
+      if (NBS > 3) wide_group_sum<PPG>(s3, xsum[buf][srow + 48], tid);        \
+    }                                                                         \
   } while (0)
 
-  f32x4_t acc[4];
+  // At group size 128 the batch blocks (16 rows each) are a template constant
+  // of the loop body, so each MFMA and its LDS operand are issued without a
+  // branch and the compiler keeps several operand reads in flight (NBB = 0:
+  // the count read at run time, for the smaller groups, whose scales leave no
+  // registers for it).
+  auto run = [&](auto nbb_c) {
+    constexpr int NBS = decltype(nbb_c)::value ? decltype(nbb_c)::value : 4;  // blocks staged
+    const int NBB = decltype(nbb_c)::value ? decltype(nbb_c)::value : nbb;
+    f32x4_t acc[4];
 #pragma unroll
-  for (int bb = 0; bb < 4; ++bb) acc[bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int bb = 0; bb < 4; ++bb) acc[bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  if (!i4) {
-    const int nks = a.K >> 5;
-    const int st0 = k0 >> 5, ns = kw >> 5;  // first step of the range, steps in it
-    const uint16_t* at = a.wt + ((size_t)tc * nks * 64 + lane) * 8;
-    uint4 ra[8];
+    if (!i4) {
+      const int nks = a.K >> 5;
+      const int st0 = k0 >> 5, ns = kw >> 5;  // first step of the range, steps in it
+      const uint16_t* at = a.wt + ((size_t)tc * nks * 64 + lane) * 8;
+      uint4 ra[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ra[i] = ld_stream(at + (size_t)(st0 + min(i, ns - 1)) * 512);
-    EE_STAGE_LOAD(0);
-    EE_STAGE_STORE(0);
-    EE_STAGE_LOAD(min(1, nch - 1));
-    __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-      const uint16_t* xb = xs + (c & 1) * kWideBuf + (lane & 15) * kWideStride + (lane >> 4) * 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bf16x8_t aop = as_bf16x8(ra[i]);
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb)
-          if (bb < nbb)
-            acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                aop, as_bf16x8(*(const uint4*)(xb + bb * 16 * kWideStride + i * 32)), acc[bb], 0, 0, 0);
-        ra[i] = ld_stream(at + (size_t)(st0 + min(c * 8 + i + 8, ns - 1)) * 512);  // past the end: reload (unused)
-      }
-      if (c + 1 < nch) EE_STAGE_STORE((c + 1) & 1);
+      for (int i = 0; i < 8; ++i) ra[i] = ld_stream(at + (size_t)(st0 + min(i, ns - 1)) * 512);
+      EE_STAGE_LOAD(0);
+      EE_STAGE_STORE(0);
+      EE_STAGE_LOAD(min(1, nch - 1));
       __syncthreads();
-      EE_STAGE_LOAD(min(c + 2, nch - 1));
-    }
-  } else {
-    const int seg = tc * 16 >= a.n0 ? 1 : 0;
-    const int ts = tc - (seg ? a.n0 >> 4 : 0);  // tile within its segment
-    const int ngr = a.K / G;
-    const uint32_t* cp = a.q4[seg] + (size_t)(ts * 16 + (lane & 15)) * (a.K >> 3) + (k0 >> 3) + (lane >> 4) * 4;
-    const uint16_t* sp = a.s4[seg] + ((size_t)ts * ngr + k0 / G) * 16 + 4 * (lane >> 4);
-    const int nbk = kw >> 7;  // 128-column blocks of the range
-    // codes of two chunks (RD = 4 blocks) in flight at group size 128: slots
-    // 0-1 hold the even chunks' blocks, 2-3 the odd chunks' (the chunk loop is
-    // unrolled by two so every slot index is fixed); smaller groups keep one
-    // chunk (their scales take the registers).  Cached loads: a block's codes
-    // are half of a 128-byte line per row, the other half being the next
-    // block.
-    constexpr int RD = NG == 1 ? 4 : 2;
-    uint4 rc[RD];
-    uint2 rs[RD][NG];
+      for (int c = 0; c < nch; ++c) {
+        const uint16_t* xb = xs + (c & 1) * kWideBuf + (lane & 15) * kWideStride + (lane >> 4) * 8;
 #pragma unroll
-    for (int i = 0; i < RD; ++i) {
-      const int u = min(i, nbk - 1);
-      rc[i] = *(const uint4*)(cp + u * 16);
-#pragma unroll
-      for (int g = 0; g < NG; ++g) rs[i][g] = *(const uint2*)(sp + (u * NG + g) * 16);
-    }
-    EE_STAGE_LOAD(0);
-    EE_STAGE_STORE(0);
-    EE_STAGE_LOAD(min(1, nch - 1));
-    __syncthreads();
-    f32x4_t cg[4];
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) cg[bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    // one 256-column chunk: its two blocks from ring slots sl, sl + 1, which
-    // are then refilled with the blocks RD / 2 chunks ahead
-    auto do_chunk = [&](const int c, const int sl) {
-      const uint16_t* xb = xs + (c & 1) * kWideBuf + (lane & 15) * kWideStride + (lane >> 4) * 8;
-      const float* xsr = &xsum[c & 1][lane & 15][0];
-#pragma unroll
-      for (int ub = 0; ub < 2; ++ub) {
-        const uint4 cw = rc[sl + ub];
-        uint2 sv[NG];
-#pragma unroll
-        for (int g = 0; g < NG; ++g) sv[g] = rs[sl + ub][g];
-        const int un = min(c * 2 + ub + RD, nbk - 1);  // past the end: reload (unused)
-        rc[sl + ub] = *(const uint4*)(cp + un * 16);
-#pragma unroll
-        for (int g = 0; g < NG; ++g) rs[sl + ub][g] = *(const uint2*)(sp + (un * NG + g) * 16);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16x8_t aop = unpack8(pick(cw, j));
+        for (int i = 0; i < 8; ++i) {
+          const bf16x8_t aop = as_bf16x8(ra[i]);
 #pragma unroll
           for (int bb = 0; bb < 4; ++bb)
-            if (bb < nbb)
-              cg[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  aop, as_bf16x8(*(const uint4*)(xb + bb * 16 * kWideStride + (ub * 4 + j) * 32)), cg[bb], 0, 0, 0);
-          if ((j + 1) % SPG == 0) {  // end of a scale group
-            const int gi = j / SPG;
-            const uint2 sc = sv[gi];
-            const float q0 = bf2f(sc.x & 0xffffu), q1 = bf2f(sc.x >> 16);
-            const float q2 = bf2f(sc.y & 0xffffu), q3 = bf2f(sc.y >> 16);
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {
-              if (bb < nbb) {
-                const float corr = 136.0f * xsr[bb * 16 * 2 * NG + ub * NG + gi];
-                acc[bb][0] = fmaf(q0, cg[bb][0] - corr, acc[bb][0]);
-                acc[bb][1] = fmaf(q1, cg[bb][1] - corr, acc[bb][1]);
-                acc[bb][2] = fmaf(q2, cg[bb][2] - corr, acc[bb][2]);
-                acc[bb][3] = fmaf(q3, cg[bb][3] - corr, acc[bb][3]);
-              }
-              cg[bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-            }
-          }
+            if (bb < NBB)
+              acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  aop, as_bf16x8(*(const uint4*)(xb + bb * 16 * kWideStride + i * 32)), acc[bb], 0, 0, 0);
+          ra[i] = ld_stream(at + (size_t)(st0 + min(c * 8 + i + 8, ns - 1)) * 512);  // past the end: reload (unused)
+          __builtin_amdgcn_sched_barrier(0);
         }
-      }
-      if (c + 1 < nch) EE_STAGE_STORE((c + 1) & 1);
-      __syncthreads();
-      EE_STAGE_LOAD(min(c + 2, nch - 1));
-    };
-    if constexpr (RD == 4) {
-      for (int c = 0; c < nch; c += 2) {
-        do_chunk(c, 0);
-        if (c + 1 < nch) do_chunk(c + 1, 2);  // uniform
+        if (c + 1 < nch) EE_STAGE_STORE((c + 1) & 1);
+        __syncthreads();
+        EE_STAGE_LOAD(min(c + 2, nch - 1));
       }
     } else {
-      for (int c = 0; c < nch; ++c) do_chunk(c, 0);
+      const int seg = tc * 16 >= a.n0 ? 1 : 0;
+      const int ts = tc - (seg ? a.n0 >> 4 : 0);  // tile within its segment
+      const int ngr = a.K / G;
+      const uint32_t* cp = a.q4[seg] + (size_t)(ts * 16 + (lane & 15)) * (a.K >> 3) + (k0 >> 3) + (lane >> 4) * 4;
+      const uint16_t* sp = a.s4[seg] + ((size_t)ts * ngr + k0 / G) * 16 + 4 * (lane >> 4);
+      const int nbk = kw >> 7;  // 128-column blocks of the range
+      // codes of two chunks (RD = 4 blocks) in flight at group size 128: slots
+      // 0-1 hold the even chunks' blocks, 2-3 the odd chunks' (the chunk loop is
+      // unrolled by two so every slot index is fixed); smaller groups keep one
+      // chunk (their scales take the registers).  Cached loads: a block's codes
+      // are half of a 128-byte line per row, the other half being the next
+      // block.
+      constexpr int RD = NG == 1 ? 4 : 2;
+      uint4 rc[RD];
+      uint2 rs[RD][NG];
+#pragma unroll
+      for (int i = 0; i < RD; ++i) {
+        const int u = min(i, nbk - 1);
+        rc[i] = *(const uint4*)(cp + u * 16);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) rs[i][g] = *(const uint2*)(sp + (u * NG + g) * 16);
+      }
+      EE_STAGE_LOAD(0);
+      EE_STAGE_STORE(0);
+      EE_STAGE_LOAD(min(1, nch - 1));
+      __syncthreads();
+      f32x4_t cg[4];
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) cg[bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      // one 256-column chunk: its two blocks from ring slots sl, sl + 1, which
+      // are then refilled with the blocks RD / 2 chunks ahead
+      auto do_chunk = [&](const int c, const int sl) {
+        const uint16_t* xb = xs + (c & 1) * kWideBuf + (lane & 15) * kWideStride + (lane >> 4) * 8;
+        const float* xsr = &xsum[c & 1][lane & 15][0];
+#pragma unroll
+        for (int ub = 0; ub < 2; ++ub) {
+          const uint4 cw = rc[sl + ub];
+          uint2 sv[NG];
+#pragma unroll
+          for (int g = 0; g < NG; ++g) sv[g] = rs[sl + ub][g];
+          const int un = min(c * 2 + ub + RD, nbk - 1);  // past the end: reload (unused)
+          rc[sl + ub] = *(const uint4*)(cp + un * 16);
+#pragma unroll
+          for (int g = 0; g < NG; ++g) rs[sl + ub][g] = *(const uint2*)(sp + (un * NG + g) * 16);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bf16x8_t aop = unpack8(pick(cw, j));
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb)
+              if (bb < NBB)
+                cg[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    aop, as_bf16x8(*(const uint4*)(xb + bb * 16 * kWideStride + (ub * 4 + j) * 32)), cg[bb], 0, 0, 0);
+            if ((j + 1) % SPG == 0) {  // end of a scale group
+              const int gi = j / SPG;
+              const uint2 sc = sv[gi];
+              const float q0 = bf2f(sc.x & 0xffffu), q1 = bf2f(sc.x >> 16);
+              const float q2 = bf2f(sc.y & 0xffffu), q3 = bf2f(sc.y >> 16);
+#pragma unroll
+              for (int bb = 0; bb < 4; ++bb) {
+                if (bb < NBB) {
+                  const float corr = 136.0f * xsr[bb * 16 * 2 * NG + ub * NG + gi];
+                  acc[bb][0] = fmaf(q0, cg[bb][0] - corr, acc[bb][0]);
+                  acc[bb][1] = fmaf(q1, cg[bb][1] - corr, acc[bb][1]);
+                  acc[bb][2] = fmaf(q2, cg[bb][2] - corr, acc[bb][2]);
+                  acc[bb][3] = fmaf(q3, cg[bb][3] - corr, acc[bb][3]);
+                }
+                cg[bb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+              }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        if (c + 1 < nch) EE_STAGE_STORE((c + 1) & 1);
+        __syncthreads();
+        EE_STAGE_LOAD(min(c + 2, nch - 1));
+      };
+      if constexpr (RD == 4) {
+        for (int c = 0; c < nch; c += 2) {
+          do_chunk(c, 0);
+          if (c + 1 < nch) do_chunk(c + 1, 2);  // uniform
+        }
+      } else {
+        for (int c = 0; c < nch; ++c) do_chunk(c, 0);
+      }
     }
-  }
 #undef EE_STAGE_LOAD
 #undef EE_STAGE_STORE
 
-  // lane l holds rows 16 tile + 4 (l / 16) .. +3 of batch column l % 16 of block bb
-  if (tile < ntiles) {
+    // lane l holds rows 16 tile + 4 (l / 16) .. +3 of batch column l % 16 of block bb
+    if (tile < ntiles) {
 #pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      const int col = bb * 16 + (lane & 15);
-      if (bb < nbb && col < n) {
-        float* dst = a.y + (size_t)r * a.y_cstride + (size_t)list[col] * a.y_stride + tile * 16 + 4 * (lane >> 4);
-        *(float4*)dst = make_float4(acc[bb][0], acc[bb][1], acc[bb][2], acc[bb][3]);
+      for (int bb = 0; bb < 4; ++bb) {
+        const int col = bb * 16 + (lane & 15);
+        if (bb < NBB && col < n) {
+          float* dst = a.y + (size_t)r * a.y_cstride + (size_t)list[col] * a.y_stride + tile * 16 + 4 * (lane >> 4);
+          *(float4*)dst = make_float4(acc[bb][0], acc[bb][1], acc[bb][2], acc[bb][3]);
+        }
       }
     }
+  };
+  if constexpr (NG == 1) {
+    switch (nbb) {
+      case 1: run(std::integral_constant<int, 1>{}); break;
+      case 2: run(std::integral_constant<int, 2>{}); break;
+      case 3: run(std::integral_constant<int, 3>{}); break;
+      default: run(std::integral_constant<int, 4>{}); break;
+    }
+  } else {
+    run(std::integral_constant<int, 0>{});
   }
 }
 

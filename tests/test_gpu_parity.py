@@ -293,6 +293,10 @@ def test_largest_batch(gpu):
     ("wide-b64", ModelShape(2, 256, 4, 2, 64, 384, 700, 32, rope_theta=10000.0), 64),
     # group 128, head_dim 128, one batch block plus one row
     ("wide-g128", ModelShape(3, 512, 4, 2, 128, 768, 500, 128, rope_theta=500000.0), 17),
+    # group 128 with 3 and 4 batch blocks (the loop bodies specialised for
+    # them), the rows of a layer split between the two formats
+    ("wide-g128-b40", ModelShape(3, 512, 4, 2, 128, 768, 500, 128, rope_theta=500000.0), 40),
+    ("wide-g128-b64", ModelShape(3, 512, 4, 2, 128, 768, 500, 128, rope_theta=500000.0), 64),
 ])
 def test_wide_batch_vocabulary_pass(gpu, label, sh, batch):
     """Batches of more than 8 rows: the projections run on the matrix-core pass
