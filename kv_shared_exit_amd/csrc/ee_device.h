@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <math.h>
 
+#include <type_traits>
+
 namespace ee {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -31,6 +33,57 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// The value held by lane ^ M (M = 1, 2, 4, 8, 16 or 32) without an LDS round
+// trip: within a row of 16 lanes through the DPP modifier (quad permutes for 1
+// and 2; for 4, a shift left by 4 into the lanes whose bit 2 is clear and a
+// shift right into the others, chosen by the bank mask; a rotation by 8 for
+// 8), across rows with the gfx950 permlane swaps (each returns the lower half
+// of the pair duplicated and the upper half duplicated: the partner is the
+// other half).  Every lane of the wave must be active.
+template <int M>
+__device__ __forceinline__ int xor_lane(int v, int lane) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "lane offset");
+  if constexpr (M == 1) {
+    return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);
+  } else if constexpr (M == 2) {
+    return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);
+  } else if constexpr (M == 4) {
+    const int t = __builtin_amdgcn_update_dpp(v, v, 0x104, 0xF, 0x5, false);
+    return __builtin_amdgcn_update_dpp(t, v, 0x114, 0xF, 0xA, false);
+  } else if constexpr (M == 8) {
+    return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false);
+  } else if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)((lane & 16) ? r[0] : r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)((lane & 32) ? r[0] : r[1]);
+  }
+}
+
+template <int M>
+__device__ __forceinline__ float xor_lane(float v, int lane) {
+  return __int_as_float(xor_lane<M>(__float_as_int(v), lane));
+}
+
+// f(std::integral_constant<int, M>) for M = FROM, 2 FROM, ..., up to 32
+template <int FROM, typename F>
+__device__ __forceinline__ void each_offset_up(F&& f) {
+  if constexpr (FROM <= 32) {
+    f(std::integral_constant<int, FROM>{});
+    each_offset_up<2 * FROM>(f);
+  }
+}
+
+// f(std::integral_constant<int, M>) for M = 32, 16, ..., down to TO
+template <int TO, int M = 32, typename F>
+__device__ __forceinline__ void each_offset_down(F&& f) {
+  if constexpr (M >= TO) {
+    f(std::integral_constant<int, M>{});
+    each_offset_down<TO, M / 2>(f);
+  }
 }
 
 // Lane exchange within a row of 16 lanes through the DPP modifier (no LDS
@@ -72,11 +125,11 @@ struct XRed {
       for (int i = 0; i < half; ++i) {
         const float keep = hi ? v[half + i] : v[i];
         const float send = hi ? v[i] : v[half + i];
-        v[i] = keep + __shfl_xor(send, 1 << S);
+        v[i] = keep + xor_lane<(1 << S)>(send, lane);
       }
       XRed<V, S + 1>::run(v, lane);
     } else if constexpr (S < 6) {
-      v[0] += __shfl_xor(v[0], 1 << S);
+      v[0] += xor_lane<(1 << S)>(v[0], lane);
       XRed<V, S + 1>::run(v, lane);
     }
   }

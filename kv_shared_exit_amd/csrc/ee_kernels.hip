@@ -56,8 +56,7 @@ __global__ __launch_bounds__(kInitThreads) void init_kernel(StepState* st, const
   }
   __shared__ float wsum[kInitThreads / 64];
   __shared__ float rs;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+  each_offset_down<1>([&](auto mc) { ss += xor_lane<decltype(mc)::value>(ss, tid & 63); });
   if ((tid & 63) == 0) wsum[tid >> 6] = ss;
   __syncthreads();
   if (tid == 0) {
@@ -214,8 +213,8 @@ __global__ __launch_bounds__(64) void attn_kernel(const AttnArgs a) {
         mt = fmaxf(mt, sc[pt][r]);
       }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = fmaxf(mt, xor_lane<16>(mt, lane));
+    mt = fmaxf(mt, xor_lane<32>(mt, lane));
     const float mn = fmaxf(m, mt);
     const float corr = __expf(m - mn);   // 0 on the first tile (m = -inf)
     float ls = 0.0f;
@@ -227,8 +226,8 @@ __global__ __launch_bounds__(64) void attn_kernel(const AttnArgs a) {
         ls += p;
         if (hh < GQ) pb[pt * 16 + qc * 4 + r][hh] = p;
       }
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
+    ls += xor_lane<16>(ls, lane);
+    ls += xor_lane<32>(ls, lane);
     l = l * corr + ls;
     m = mn;
     if (lane < GQ) cr[lane] = corr;
@@ -257,12 +256,12 @@ __global__ __launch_bounds__(64) void attn_kernel(const AttnArgs a) {
     __syncthreads();
   }
   // sum over the row groups of a V load (lanes with equal vc)
-#pragma unroll
-  for (int sft = CPR; sft < 64; sft <<= 1)
+  each_offset_up<CPR>([&](auto mc) {
 #pragma unroll
     for (int i = 0; i < GQ; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[i][e] += __shfl_xor(o[i][e], sft);
+      for (int e = 0; e < 8; ++e) o[i][e] += xor_lane<decltype(mc)::value>(o[i][e], lane);
+  });
   if (vr == 0) {
 #pragma unroll
     for (int i = 0; i < GQ; ++i) {
@@ -408,8 +407,8 @@ __global__ __launch_bounds__(64 * kAttnFusedWaves) void attn_fused_kernel(const 
         mt = fmaxf(mt, sc[pt][r]);
       }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = fmaxf(mt, xor_lane<16>(mt, lane));
+    mt = fmaxf(mt, xor_lane<32>(mt, lane));
     const float mn = fmaxf(m, mt);
     const float corr = __expf(m - mn);
     float ls = 0.0f;
@@ -421,8 +420,8 @@ __global__ __launch_bounds__(64 * kAttnFusedWaves) void attn_fused_kernel(const 
         ls += p;
         if (hh < GQ) pb[pt * 16 + qc * 4 + r][hh] = p;
       }
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
+    ls += xor_lane<16>(ls, lane);
+    ls += xor_lane<32>(ls, lane);
     l = l * corr + ls;
     m = mn;
     if (lane < GQ) cr[lane] = corr;
@@ -457,12 +456,12 @@ __global__ __launch_bounds__(64 * kAttnFusedWaves) void attn_fused_kernel(const 
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-#pragma unroll
-  for (int sft = CPR; sft < 64; sft <<= 1)
+  each_offset_up<CPR>([&](auto mc) {
 #pragma unroll
     for (int i = 0; i < GQ; ++i)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[i][e] += __shfl_xor(o[i][e], sft);
+      for (int e = 0; e < 8; ++e) o[i][e] += xor_lane<decltype(mc)::value>(o[i][e], lane);
+  });
   // this wave's partial into LDS (a wave without tiles: m = -inf, l = 0)
   if (vr == 0) {
 #pragma unroll
@@ -574,11 +573,10 @@ __global__ __launch_bounds__(kHeadThreads) void decide_kernel(StepState* st, con
       }
 #pragma unroll
       for (int j = 1; j < kPartPerLane; ++j) lse_merge(v[0].x, v[0].y, v[j].x, v[j].y);
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float m2 = __shfl_xor(v[0].x, o), s2 = __shfl_xor(v[0].y, o);
-        lse_merge(v[0].x, v[0].y, m2, s2);
-      }
+      each_offset_up<1>([&](auto mc) {
+        constexpr int M = decltype(mc)::value;
+        lse_merge(v[0].x, v[0].y, xor_lane<M>(v[0].x, lane), xor_lane<M>(v[0].y, lane));
+      });
       if (lane < kHeadWaves) red[lane][w] = lane == 0 ? v[0] : make_float2(-INFINITY, 0.0f);
     } else {
       // wave w takes the partials k = w + 8t (t < 64) of every position.
@@ -721,11 +719,10 @@ __global__ __launch_bounds__(64) void final_kernel(StepState* st, const float* p
     Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
 #pragma unroll
     for (int j = 0; j < kPartPerLane; ++j) top2_merge(t, Top2{v[j].x, __float_as_int(v[j].y), v[j].z});
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      Top2 u{__shfl_xor(t.v1, o), __shfl_xor(t.i1, o), __shfl_xor(t.v2, o)};
-      top2_merge(t, u);
-    }
+    each_offset_up<1>([&](auto mc) {
+      constexpr int M = decltype(mc)::value;
+      top2_merge(t, Top2{xor_lane<M>(t.v1, lane), xor_lane<M>(t.i1, lane), xor_lane<M>(t.v2, lane)});
+    });
     if (lane == 0) {
       const int tok = (t.i1 >= 0 && t.i1 < V) ? t.i1 : 0;  // no finite logit: token 0
       st->out_tok[b] = tok;
@@ -756,8 +753,7 @@ __global__ void sts_min_kernel(const float* sts, int P, int B, float* out) {
   const int b = blockIdx.x, lane = threadIdx.x;
   float m = INFINITY;
   for (int t = lane; t < P; t += 64) m = fminf(m, sts[(size_t)t * B + b]);
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) m = fminf(m, __shfl_xor(m, o));
+  each_offset_up<1>([&](auto mc) { m = fminf(m, xor_lane<decltype(mc)::value>(m, lane)); });
   if (lane == 0) out[b] = m;
 }
 

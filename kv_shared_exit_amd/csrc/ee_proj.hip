@@ -177,12 +177,12 @@ __device__ __forceinline__ void stage_x(const ProjArgs& a, const Work& w, int nb
       // a group lies wholly below n or wholly above it (n and i are aligned
       // to PPG), so every lane of a group takes part in its butterfly
       if (j * kProjThreads < n) {
-        float t = 0.0f;
-        const uint32_t e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) t += bf2f(e[c] & 0xffffu) + bf2f(e[c] >> 16);
-#pragma unroll
-        for (int off = 1; off < PPG; off <<= 1) t += __shfl_xor(t, off);
+        constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 (1, 1)
+        float t = dot2(v[j].x, kOnes, 0.0f);
+        t = dot2(v[j].y, kOnes, t);
+        t = dot2(v[j].z, kOnes, t);
+        t = dot2(v[j].w, kOnes, t);
+        t = group_sum_dpp<PPG>(t);
         if (i < n && (i & (PPG - 1)) == 0) gs[i / PPG] = t;
       }
     }
@@ -318,10 +318,10 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, const Work& wk, int
     const float v = acc[0];
     const int n = EPI == EPI_QKV ? qkv_row<R / 2>(a, t, rr) : n0 + (rr % R);
     if constexpr (EPI == EPI_QKV) {
-      const float u = __shfl_xor(v, 1);  // the RoPE partner row sits in the partner lane
+      const float u = xor_lane<1>(v, lane);  // the RoPE partner row sits in the partner lane
       if (lane_ok) qkv_out(a, seq[bsel], n, v, u);
     } else if constexpr (EPI == EPI_SWIGLU) {
-      const float u = __shfl_xor(v, 1);  // the up row sits in the partner lane
+      const float u = xor_lane<1>(v, lane);  // the up row sits in the partner lane
       if (lane_ok && (lane & 1) == 0 && n < N)
         ((uint16_t*)a.y)[(size_t)seq[bsel] * a.y_stride + n] = (uint16_t)f2bf(silu_mul(v, u));
     } else if constexpr (EPI == EPI_LSE) {
@@ -366,7 +366,7 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, const Work& wk, int
     } else if constexpr (EPI == EPI_RESAMPLE) {
       // rows come in pairs (final input of sequence b, its exit layer's z at
       // row 64 + b): the pair's two values sit in lanes l and l ^ (V / 2)
-      const float u = __shfl_xor(v, V / 2);
+      const float u = xor_lane<V / 2>(v, lane);
       if (lane_ok && (bsel & 1) == 0 && n < N) {
         const int sq = seq[bsel];
         const float r = __expf(v * a.itau - a.st->lse_f[sq]) - __expf(u * a.itau - a.st->draft_lse[sq]);
@@ -827,7 +827,7 @@ __device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int 
       // lane (q, m) holds rows arow(tf, 4q + i); the RoPE partners sit in lane ^ 32
       float u[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = __shfl_xor(vals[0][i], 32);
+      for (int i = 0; i < 4; ++i) u[i] = xor_lane<32>(vals[0][i], lane);
       if (!bok) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) qkv_out(a, seq[m], arow(tf, 4 * q + i), vals[0][i], u[i]);
@@ -1211,14 +1211,14 @@ __global__ __launch_bounds__(kFinThreads) void finish_kernel(float* h, const flo
   constexpr int kW = kFinThreads / 64;
   __shared__ float wsum[3][kW];
   __shared__ float rs;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    ss += __shfl_xor(ss, o);
+  each_offset_down<1>([&](auto mc) {
+    constexpr int M = decltype(mc)::value;
+    ss += xor_lane<M>(ss, tid & 63);
     if constexpr (STS) {
-      si += __shfl_xor(si, o);
-      sd += __shfl_xor(sd, o);
+      si += xor_lane<M>(si, tid & 63);
+      sd += xor_lane<M>(sd, tid & 63);
     }
-  }
+  });
   if ((tid & 63) == 0) {
     wsum[0][tid >> 6] = ss;
     wsum[1][tid >> 6] = si;

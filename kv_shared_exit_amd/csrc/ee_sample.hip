@@ -61,18 +61,17 @@ __device__ Merged merge_parts(const float* part_s, int nwg, int b, int lane) {
     }
     r.logit = fmaxf(r.logit, l5[j]);
   }
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float m2 = __shfl_xor(r.m, o), s2 = __shfl_xor(r.s, o);
-    lse_merge(r.m, r.s, m2, s2);
-    const float b2 = __shfl_xor(r.best, o);
-    const int i2 = __shfl_xor(r.idx, o);
+  each_offset_up<1>([&](auto mc) {
+    constexpr int M = decltype(mc)::value;
+    lse_merge(r.m, r.s, xor_lane<M>(r.m, lane), xor_lane<M>(r.s, lane));
+    const float b2 = xor_lane<M>(r.best, lane);
+    const int i2 = xor_lane<M>(r.idx, lane);
     if (b2 > r.best || (b2 == r.best && i2 < r.idx)) {
       r.best = b2;
       r.idx = i2;
     }
-    r.logit = fmaxf(r.logit, __shfl_xor(r.logit, o));
-  }
+    r.logit = fmaxf(r.logit, xor_lane<M>(r.logit, lane));
+  });
   return r;
 }
 
@@ -168,15 +167,15 @@ __global__ __launch_bounds__(kThreads) void resample_final_kernel(StepState* st,
         best = bv[j];
         idx = bi[j];
       }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float b2 = __shfl_xor(best, o);
-      const int i2 = __shfl_xor(idx, o);
+    each_offset_up<1>([&](auto mc) {
+      constexpr int M = decltype(mc)::value;
+      const float b2 = xor_lane<M>(best, lane);
+      const int i2 = xor_lane<M>(idx, lane);
       if (b2 > best || (b2 == best && i2 < idx)) {
         best = b2;
         idx = i2;
       }
-    }
+    });
     if (lane == 0) {
       const int tok = (idx >= 0 && idx < V) ? idx : 0;  // an empty residual cannot be drawn from: token 0
       st->out_tok[b] = tok;

@@ -255,16 +255,15 @@ __global__ __launch_bounds__(kProjThreads, 4) void wide_vocab_kernel(const ProjA
   // merge the four lanes of each column, then the waves (fixed order)
 #pragma unroll
   for (int bb = 0; bb < 4; ++bb) {
-#pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
+    each_offset_up<16>([&](auto mc) {
+      constexpr int M = decltype(mc)::value;
       if constexpr (EPI == EPI_LSE) {
-        const float m2 = __shfl_xor(lm[bb], off), s2 = __shfl_xor(ls[bb], off);
-        lse_merge(lm[bb], ls[bb], m2, s2);
+        lse_merge(lm[bb], ls[bb], xor_lane<M>(lm[bb], lane), xor_lane<M>(ls[bb], lane));
       } else {
-        const Top2 o{__shfl_xor(tp[bb].v1, off), __shfl_xor(tp[bb].i1, off), __shfl_xor(tp[bb].v2, off)};
-        top2_merge(tp[bb], o);
+        top2_merge(tp[bb], Top2{xor_lane<M>(tp[bb].v1, lane), xor_lane<M>(tp[bb].i1, lane),
+                                xor_lane<M>(tp[bb].v2, lane)});
       }
-    }
+    });
     if (lane < 16) {
       float* rw = red + (wave * kWideRows + bb * 16 + lane) * 4;
       if constexpr (EPI == EPI_LSE) {
