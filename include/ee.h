@@ -305,9 +305,10 @@ ee_status ee_decode_step(ee_model *m, ee_kv_cache *c, int32_t batch,
  * the process ends, instead of the model's own buffers.  It calls no
  * hipMalloc, hipFree or other allocating routine; its kernels are launched
  * one by one (no graph is captured or instantiated), without diagnostics or
- * profiling.  UNSUPPORTED when the step's workspaces exceed the array (e.g.
- * the 8B shape above 8 rows, whose matrix-core passes need larger partial
- * sums); nothing runs then.  Every call on one GPU uses that GPU's single
+ * profiling.  UNSUPPORTED when the step's workspaces exceed the array (they
+ * grow with the model widths: e.g. a feed-forward width of 49152 above 8
+ * rows, whose partial sums need more; the 8B shape fits at any batch);
+ * nothing runs then.  Every call on one GPU uses that GPU's single
  * array, which keeps the last call's contents (the step state is cleared by a
  * kernel at the start of each call): calls that overlap on one GPU, from any
  * model or thread, race and must be serialised by the caller. */

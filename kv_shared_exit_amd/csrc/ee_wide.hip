@@ -333,10 +333,15 @@ void launch_wide_vocab(int epi, const ProjArgs& a0, int nwg, hipStream_t s, hipE
 //   * The ranges are summed by the epilogue kernels below (or by the finish
 //     kernel for O and down), in range order.
 // ---------------------------------------------------------------------------
+// Column ranges: the most (up to 8) that keep one format's workgroups within
+// 256, so a launch with both formats fits the 512 resident workgroups in one
+// round (measured at 64 rows, 8B widths: gate/up 1 range 42 us against 54 us
+// for 3 with bf16 rows only, 59 against 63 us with 32 rows of each; QKV 4
+// ranges 13 against 16 us).
 int wide_ranges(int N, int K, int* kr) {
   const int nrb = (N + 127) / 128;
   const int steps = K / kWideCols;
-  int nr = std::max(1, std::min(std::min(8, steps), (512 + nrb - 1) / nrb));
+  int nr = std::max(1, std::min(std::min(8, steps), 256 / nrb));
   const int w = (steps + nr - 1) / nr;
   if (kr) *kr = w * kWideCols;
   return (steps + w - 1) / w;

@@ -85,29 +85,43 @@ def test_static_step_equals_decode_step(api, name):
 
 
 def test_static_step_refuses_workspaces_beyond_the_array(api):
-    """At the 8B widths (d 4096, F 14336) a batch of 16 runs the matrix-core
-    passes, whose partial sums need more than the 32 MiB array: refused with
-    UNSUPPORTED before anything runs (lengths unchanged); a batch of 8 on the
-    same model fits and equals ee_decode_step."""
+    """With a feed-forward width of 49152 (d 4096) a batch of 16 runs the
+    matrix-core passes, whose gate/up partial sums (64 rows x 98304 outputs in
+    float32) and the down projection's partial sums need more than the 32 MiB
+    array: refused with UNSUPPORTED before anything runs (lengths unchanged);
+    a batch of 8 on the same model fits and equals ee_decode_step.  At the 8B
+    widths (F 14336) a batch of 16 fits and equals ee_decode_step."""
     from kv_shared_exit_amd import _binding as Bd
-    sh = ModelShape(1, 4096, 32, 8, 128, 14336, 1000, 128, rope_theta=500000.0)
-    w = synth.make_weights(sh, 22)
-    dev = api.upload_weights(w)
-    m = api.Model(sh, dev, gamma=2.0, max_batch=16, max_positions=8)
-    ref, sta = api.KVCache(m, 16, 8), api.KVCache(m, 16, 8)
-    try:
-        prompts = np.random.default_rng(5).integers(0, sh.vocab, (16, 3)).astype(np.int32)
-        t0 = api.prefill(m, ref, prompts)
-        api.prefill(m, sta, prompts)
-        with pytest.raises(Bd.EEError) as e:
-            api.decode_step_static(m, sta, 16, tokens=t0)
-        assert e.value.status == Bd.EE_ERR_UNSUPPORTED
-        assert list(sta.lengths()) == [3] * 16
-        tr, er = api.decode_step(m, ref, 8, tokens=t0[:8])
-        ts, es = api.decode_step_static(m, sta, 8, tokens=t0[:8])
-        np.testing.assert_array_equal(ts, tr)
-        np.testing.assert_array_equal(es, er)
-    finally:
-        ref.close()
-        sta.close()
-        m.close()
+
+    def run(sh, seed, refuse):
+        w = synth.make_weights(sh, seed)
+        dev = api.upload_weights(w)
+        del w
+        m = api.Model(sh, dev, gamma=2.0, max_batch=16, max_positions=8)
+        ref, sta = api.KVCache(m, 16, 8), api.KVCache(m, 16, 8)
+        try:
+            prompts = np.random.default_rng(seed).integers(0, sh.vocab, (16, 3)).astype(np.int32)
+            t0 = api.prefill(m, ref, prompts)
+            api.prefill(m, sta, prompts)
+            if refuse:
+                with pytest.raises(Bd.EEError) as e:
+                    api.decode_step_static(m, sta, 16, tokens=t0)
+                assert e.value.status == Bd.EE_ERR_UNSUPPORTED
+                assert list(sta.lengths()) == [3] * 16
+            else:
+                tr, er = api.decode_step(m, ref, 16, tokens=t0)
+                ts, es = api.decode_step_static(m, sta, 16, tokens=t0)
+                np.testing.assert_array_equal(ts, tr)
+                np.testing.assert_array_equal(es, er)
+                t0 = tr
+            tr, er = api.decode_step(m, ref, 8, tokens=t0[:8])
+            ts, es = api.decode_step_static(m, sta, 8, tokens=t0[:8])
+            np.testing.assert_array_equal(ts, tr)
+            np.testing.assert_array_equal(es, er)
+        finally:
+            ref.close()
+            sta.close()
+            m.close()
+
+    run(ModelShape(1, 4096, 32, 8, 128, 49152, 1000, 128, rope_theta=500000.0), 23, True)
+    run(ModelShape(1, 4096, 32, 8, 128, 14336, 1000, 128, rope_theta=500000.0), 22, False)
