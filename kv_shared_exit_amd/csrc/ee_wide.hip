@@ -404,9 +404,10 @@ __global__ __launch_bounds__(kProjThreads, 4) void wide_proj_kernel(const WideAr
   // of the loop body, so each MFMA and its LDS operand are issued without a
   // branch and the compiler keeps several operand reads in flight (NBB = 0:
   // the count read at run time, for the smaller groups, whose scales leave no
-  // registers for it).
-  auto run = [&](auto nbb_c) {
+  // registers for it).  RB: 32-column steps of bf16 weights in flight per wave.
+  auto run = [&](auto nbb_c, auto rb_c) {
     constexpr int NBS = decltype(nbb_c)::value ? decltype(nbb_c)::value : 4;  // blocks staged
+    constexpr int RB = decltype(rb_c)::value;
     const int NBB = decltype(nbb_c)::value ? decltype(nbb_c)::value : nbb;
     f32x4_t acc[4];
 #pragma unroll
@@ -416,9 +417,9 @@ __global__ __launch_bounds__(kProjThreads, 4) void wide_proj_kernel(const WideAr
       const int nks = a.K >> 5;
       const int st0 = k0 >> 5, ns = kw >> 5;  // first step of the range, steps in it
       const uint16_t* at = a.wt + ((size_t)tc * nks * 64 + lane) * 8;
-      uint4 ra[8];
+      uint4 ra[RB];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ra[i] = ld_stream(at + (size_t)(st0 + min(i, ns - 1)) * 512);
+      for (int i = 0; i < RB; ++i) ra[i] = ld_stream(at + (size_t)(st0 + min(i, ns - 1)) * 512);
       EE_STAGE_LOAD(0);
       EE_STAGE_STORE(0);
       EE_STAGE_LOAD(min(1, nch - 1));
@@ -427,20 +428,20 @@ __global__ __launch_bounds__(kProjThreads, 4) void wide_proj_kernel(const WideAr
         const uint16_t* xb = xs + (c & 1) * kWideBuf + (lane & 15) * kWideStride + (lane >> 4) * 8;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const bf16x8_t aop = as_bf16x8(ra[i]);
+          const bf16x8_t aop = as_bf16x8(ra[i % RB]);  // step c * 8 + i (RB divides 8)
 #pragma unroll
           for (int bb = 0; bb < 4; ++bb)
             if (bb < NBB)
               acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                   aop, as_bf16x8(*(const uint4*)(xb + bb * 16 * kWideStride + i * 32)), acc[bb], 0, 0, 0);
-          ra[i] = ld_stream(at + (size_t)(st0 + min(c * 8 + i + 8, ns - 1)) * 512);  // past the end: reload (unused)
+          ra[i % RB] = ld_stream(at + (size_t)(st0 + min(c * 8 + i + RB, ns - 1)) * 512);  // past the end: reload (unused)
           __builtin_amdgcn_sched_barrier(0);
         }
         if (c + 1 < nch) EE_STAGE_STORE((c + 1) & 1);
         __syncthreads();
         EE_STAGE_LOAD(min(c + 2, nch - 1));
       }
-    } else {
+    } else if constexpr (RB == 4) {
       const int seg = tc * 16 >= a.n0 ? 1 : 0;
       const int ts = tc - (seg ? a.n0 >> 4 : 0);  // tile within its segment
       const int ngr = a.K / G;
@@ -541,15 +542,28 @@ __global__ __launch_bounds__(kProjThreads, 4) void wide_proj_kernel(const WideAr
       }
     }
   };
+  // bf16 weights: 4 steps (4 KB) in flight per wave, 2 when the launch has
+  // more int4 rows than bf16 rows.  The int4 workgroups that share a CU with
+  // bf16 workgroups wait for their loads behind the bf16 stream's; a shallower
+  // bf16 ring shortens that queue.  Measured at the 8B widths, 64 rows (gate/up,
+  // bf16 / int4 rows): 8 steps 42.4 / 58.9 / 73.1 us (64/0, 32/32, 8/56), 4
+  // steps 40.4 / 53.6 / 67.6, 2 steps 49.6 / 56.8 / 56.8.
+  const bool shallow = !i4 && *a.cnt_i4 > n;
+  auto go = [&](auto nbb_c) {
+    if (shallow)
+      run(nbb_c, std::integral_constant<int, 2>{});
+    else
+      run(nbb_c, std::integral_constant<int, 4>{});
+  };
   if constexpr (NG == 1) {
     switch (nbb) {
-      case 1: run(std::integral_constant<int, 1>{}); break;
-      case 2: run(std::integral_constant<int, 2>{}); break;
-      case 3: run(std::integral_constant<int, 3>{}); break;
-      default: run(std::integral_constant<int, 4>{}); break;
+      case 1: go(std::integral_constant<int, 1>{}); break;
+      case 2: go(std::integral_constant<int, 2>{}); break;
+      case 3: go(std::integral_constant<int, 3>{}); break;
+      default: go(std::integral_constant<int, 4>{}); break;
     }
   } else {
-    run(std::integral_constant<int, 0>{});
+    go(std::integral_constant<int, 0>{});
   }
 }
 
