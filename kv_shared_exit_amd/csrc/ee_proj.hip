@@ -275,6 +275,8 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, const Work& wk, int
   stage_rows(list, c0, nb, seq);
   stage_x(a, wk, nb, seq, xs);
   __syncthreads();
+  // QKV: the position of this lane's sequence (seq is padded to 8 ids)
+  const int pos = EPI == EPI_QKV ? a.lens[seq[bsel]] : 0;
 
   for (; t < ntiles; t += nwc) {
     const int n0 = t * R;
@@ -285,6 +287,8 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, const Work& wk, int
         for (int r = 0; r < RP; ++r) cur[r] = ld_stream(w[r]);
       }
     }
+    QkvPre pre{};
+    if constexpr (EPI == EPI_QKV) pre = qkv_pre(a, seq[bsel], qkv_row<R / 2>(a, t, rr), pos);
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.0f;
@@ -319,7 +323,7 @@ __device__ __forceinline__ void bf16_pass(const ProjArgs& a, const Work& wk, int
     const int n = EPI == EPI_QKV ? qkv_row<R / 2>(a, t, rr) : n0 + (rr % R);
     if constexpr (EPI == EPI_QKV) {
       const float u = xor_lane<1>(v, lane);  // the RoPE partner row sits in the partner lane
-      if (lane_ok) qkv_out(a, seq[bsel], n, v, u);
+      if (lane_ok) qkv_out(a, seq[bsel], n, v, u, pos, pre);
     } else if constexpr (EPI == EPI_SWIGLU) {
       const float u = xor_lane<1>(v, lane);  // the up row sits in the partner lane
       if (lane_ok && (lane & 1) == 0 && n < N)
@@ -679,6 +683,8 @@ __device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int 
   stage_rows(list, c0, nb, seq);
   stage_x<BF ? 0 : G / 8>(a, wk, nb, seq, xs, gs);
   __syncthreads();
+  // QKV: the position of this column's sequence, read while the tiles run
+  const int pos = EPI == EPI_QKV ? a.lens[seq[bok ? m : 0]] : 0;
 
   float lm = -INFINITY, ls = 0.0f;            // EPI_LSE: running (max, sum exp) of column m
   Top2 tp{-INFINITY, 0x7fffffff, -INFINITY};  // EPI_ARGMAX
@@ -830,7 +836,10 @@ __device__ __forceinline__ void mma_pass(const ProjArgs& a, const Work& wk, int 
       for (int i = 0; i < 4; ++i) u[i] = xor_lane<32>(vals[0][i], lane);
       if (!bok) continue;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) qkv_out(a, seq[m], arow(tf, 4 * q + i), vals[0][i], u[i]);
+      for (int i = 0; i < 4; ++i) {
+        const int n = arow(tf, 4 * q + i);
+        qkv_out(a, seq[m], n, vals[0][i], u[i], pos, qkv_pre(a, seq[m], n, pos));
+      }
       continue;
     }
     if (!bok) continue;
