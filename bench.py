@@ -37,12 +37,12 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 # scaled by what the same counter reads for a 1 GiB device copy.  Valid only
 # for the kernel sources it was measured on (their sha256); otherwise null.
 TRAFFIC = {
-    "lse": {"fetch_kib": 513396.0625, "write_kib": 62.6, "fetch_scale": 1.9999340, "write_scale": 0.9999999,
+    "lse": {"fetch_kib": 513399.1354, "write_kib": 62.6, "fetch_scale": 1.9999328, "write_scale": 0.9999999,
             "sources": ("ee_proj.hip", "ee_device.h", "ee_internal.h", "ee_epi.h"),
-            "sources_sha256": "8254a30322e114e4e64b8044ee5e090b551ca582a2fbe7d0e5958ebf5878f686"},
-    "wide": {"fetch_kib": 519726.1562, "write_kib": 512.0, "fetch_scale": 1.9999340, "write_scale": 0.9999999,
+            "sources_sha256": "ef909b8fcfd272fa68436a476a0329a717c0ba0f099c30f857bfd424bfef4cfb"},
+    "wide": {"fetch_kib": 519662.4375, "write_kib": 512.0, "fetch_scale": 1.9999328, "write_scale": 0.9999999,
              "sources": ("ee_wide.hip", "ee_device.h", "ee_internal.h", "ee_epi.h"),
-             "sources_sha256": "688c73a7235055158949647e8ac19ee8d79f59e74b726ca0684686edd548102e"},
+             "sources_sha256": "44f8711175bd2e8bc23940dbbea332bf2844248f308b0a0b119814c6fdf0d2d8"},
 }
 # the workloads whose shape (128256 x 4096) the counters were taken at
 TRAFFIC_SHAPE = (128256, 4096)

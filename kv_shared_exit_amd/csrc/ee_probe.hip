@@ -14,14 +14,24 @@
 //                                output rows over K inputs, nbf rows on the
 //                                bf16 weights and ni4 on the int4 G128 copy,
 //                                on the decode step's grid (512 workgroups)
+//   ee_probe wproj N K nbf ni4 reps
+//                                a decoder projection for more than 8 rows on
+//                                matrix cores (wide_proj_kernel: N output rows
+//                                over K inputs, nbf rows on the tiled bf16
+//                                weights and ni4 on the int4 G128 copy, float32
+//                                partial sums over the column ranges the decode
+//                                step uses; gate/up: N = 2 F with the up rows
+//                                from F on)
 //   ee_probe copy MiB            one copy kernel reading and writing MiB each
 //   ee_probe read MiB reps       a read-only stream of MiB (each thread sums its
 //                                16-byte loads): the streaming-read ceiling
 //   ee_probe readc MiB reps      the same bytes read with one contiguous region
 //                                per workgroup (512 workgroups)
-//   ee_probe attn B S ctx reps   decode attention (attn_kernel + combine) of B
-//                                sequences at the 8B heads (32 q / 8 kv of 128)
-//                                over ctx + 1 cached positions, cache capacity S
+//   ee_probe attn B S ctx reps   decode attention of B sequences at the 8B heads
+//                                (32 q / 8 kv of 128) over ctx + 1 cached
+//                                positions, cache capacity S: attn_kernel +
+//                                combine, or from 256 (sequence, kv head) pairs
+//                                attn_fused_kernel, as the decode step launches
 //   ee_probe gemm EPI M N K reps the prefill GEMM (EPI: bf16, resid or swiglu) of
 //                                M token rows (8 sequences of M / 8 positions)
 //                                with N x K bf16 weights (swiglu: gate and up)
@@ -92,7 +102,8 @@ __global__ __launch_bounds__(256) void read_region_kernel(const uint4* __restric
 static int usage() {
   std::fprintf(stderr,
                "usage: ee_probe lse V d rows reps | ee_probe wide V d rows reps | "
-               "ee_probe proj swiglu|part N K nbf ni4 reps | ee_probe copy MiB | ee_probe read|readc MiB reps | "
+               "ee_probe proj swiglu|part N K nbf ni4 reps | ee_probe wproj N K nbf ni4 reps | ee_probe copy MiB | "
+               "ee_probe read|readc MiB reps | "
                "ee_probe attn B S ctx reps | ee_probe gemm bf16|resid|swiglu M N K reps\n");
   return 2;
 }
@@ -198,6 +209,7 @@ int main(int argc, char** argv) {
     a.scale = 0.08838834764831845f;
     a.part = part;
     a.out = out;
+    a.fused = (long long)B * Hkv >= 256;  // as the decode step: one workgroup per (sequence, kv head)
     const double us = timed([&] { launch_attention(a, s); }, reps);
     const double bytes = (double)B * (ctx + 1) * Hkv * hd * 2 * 2;
     std::printf("attn B=%d S=%d ctx=%d tiles/wave=%d partials=%d: %.2f us (attention + combine), %.1f GB/s algorithmic\n",
@@ -323,6 +335,78 @@ int main(int argc, char** argv) {
     const double bytes = (nbf ? 2.0 * P * wn : 0.0) + (ni4 ? P * (cn * 4.0 + sn * 2.0) : 0.0);
     std::printf("proj %s N=%d K=%d bf=%d i4=%d g=%d ranges=%d: %.2f us per launch, %.1f GB/s algorithmic\n", argv[2],
                 N, K, nbf, ni4, g, nkc, us, bytes / us / 1e3);
+    return 0;
+  }
+  if (!std::strcmp(argv[1], "wproj")) {
+    if (argc < 7) return usage();
+    const int N = std::atoi(argv[2]), K = std::atoi(argv[3]), nbf = std::atoi(argv[4]), ni4 = std::atoi(argv[5]);
+    const int reps = std::atoi(argv[6]);
+    constexpr int G = 128;
+    if (N < 128 || N % 128 || K < 256 || K % 256 || nbf < 0 || ni4 < 0 || nbf + ni4 < 1 || nbf + ni4 > kMaxBatch ||
+        reps < 1)
+      return usage();
+    const int n0 = N % 256 == 0 ? N / 2 : N;  // second int4 segment from N / 2 (gate/up), if even
+    const size_t wn = (size_t)N * K;
+    uint16_t *W, *Wt, *x, *sc;
+    uint32_t* codes;
+    float* y;
+    int32_t* lists;
+    int kr = 0;
+    const int nr = wide_ranges(N, K, &kr);
+    CK(hipMalloc(&W, wn * 2));
+    CK(hipMalloc(&Wt, wn * 2));
+    CK(hipMalloc(&codes, wn / 2));
+    CK(hipMalloc(&sc, wn / G * 2));
+    CK(hipMalloc(&x, (size_t)kMaxBatch * K * 2));
+    CK(hipMalloc(&y, (size_t)nr * kMaxBatch * N * 4));
+    CK(hipMalloc(&lists, 4 * kMaxBatch * 4));
+    CK(hipMemsetAsync(W, 0x3c, wn * 2, s));  // bf16 ~0.0115
+    CK(hipMemsetAsync(codes, 0x99, wn / 2, s));
+    CK(hipMemsetAsync(sc, 0x3c, wn / G * 2, s));
+    CK(hipMemsetAsync(x, 0x3c, (size_t)kMaxBatch * K * 2, s));
+    launch_tile_rows(W, N, K, Wt, s);
+    std::vector<int32_t> hl(4 * kMaxBatch, 0);
+    for (int i = 0; i < nbf; ++i) hl[i] = i;
+    for (int i = 0; i < ni4; ++i) hl[kMaxBatch + i] = nbf + i;
+    hl[2 * kMaxBatch] = nbf;
+    hl[3 * kMaxBatch] = ni4;
+    CK(hipMemcpyAsync(lists, hl.data(), hl.size() * 4, hipMemcpyHostToDevice, s));
+    WideArgs a{};
+    a.N = N;
+    a.K = K;
+    a.nr = nr;
+    a.kr = kr;
+    a.wt = Wt;
+    a.q4[0] = codes;
+    a.s4[0] = sc;
+    a.n0 = n0;
+    if (n0 < N) {
+      a.q4[1] = codes + (size_t)n0 * K / 8;
+      a.s4[1] = sc + (size_t)n0 * (K / G);
+    }
+    a.G = G;
+    a.x = x;
+    a.x_stride = K;
+    a.list_bf = lists;
+    a.list_i4 = lists + kMaxBatch;
+    a.cnt_bf = lists + 2 * kMaxBatch;
+    a.cnt_i4 = lists + 3 * kMaxBatch;
+    a.y = y;
+    a.y_stride = N;
+    a.y_cstride = (size_t)kMaxBatch * N;
+    launch_wide_proj(a, s);  // warm-up
+    CK(hipStreamSynchronize(s));
+    CK(hipEventRecord(e0, s));
+    for (int r = 0; r < reps; ++r) launch_wide_proj(a, s);
+    CK(hipEventRecord(e1, s));
+    CK(hipEventSynchronize(e1));
+    float ms = 0;
+    CK(hipEventElapsedTime(&ms, e0, e1));
+    const double us = 1e3 * ms / reps;
+    const double bytes = (nbf ? 2.0 * wn : 0.0) + (ni4 ? wn / 2.0 + wn / G * 2.0 : 0.0);
+    const double flops = 2.0 * wn * (nbf + ni4);
+    std::printf("wproj N=%d K=%d bf=%d i4=%d ranges=%d: %.2f us per launch, %.1f GB/s algorithmic, %.1f TFLOP/s\n", N,
+                K, nbf, ni4, nr, us, bytes / us / 1e3, flops / us / 1e6);
     return 0;
   }
   const bool wide = !std::strcmp(argv[1], "wide");
