@@ -42,7 +42,7 @@ TRAFFIC = {
             "sources_sha256": "ef909b8fcfd272fa68436a476a0329a717c0ba0f099c30f857bfd424bfef4cfb"},
     "wide": {"fetch_kib": 519662.4375, "write_kib": 512.0, "fetch_scale": 1.9999328, "write_scale": 0.9999999,
              "sources": ("ee_wide.hip", "ee_device.h", "ee_internal.h", "ee_epi.h"),
-             "sources_sha256": "44f8711175bd2e8bc23940dbbea332bf2844248f308b0a0b119814c6fdf0d2d8"},
+             "sources_sha256": "3610417a96ce9f14081999d2e945ac5ce21349e1447243406df548a8dac57b45"},
 }
 # the workloads whose shape (128256 x 4096) the counters were taken at
 TRAFFIC_SHAPE = (128256, 4096)

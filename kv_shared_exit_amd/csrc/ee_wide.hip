@@ -324,7 +324,8 @@ void launch_wide_vocab(int epi, const ProjArgs& a0, int nwg, hipStream_t s, hipE
 //   * A workgroup owns 128 rows (a 16-row tile per wave) and one column range;
 //     the input rows of the range are staged in LDS 256 columns at a time,
 //     double-buffered (as in the vocabulary pass).
-//   * bf16 rows read the tiled copy (8 steps of 1 KB in flight per wave).
+//   * bf16 rows read the tiled copy (4 or 2 steps of 1 KB in flight per wave,
+//     see the end of the kernel).
 //   * int4 rows: a lane unpacks a dword of codes (8 weights) into the A
 //     operand (nibble | 0x4300 is the bf16 value 136 + q); the 136 * sum(x)
 //     of each scale group is computed once per staged row when the inputs are
