@@ -599,16 +599,18 @@ void enqueue_position(ee_model* m, const Work& W, ee_kv_cache* c, int B, bool he
       a.x_stride = d;
       a.y = W.act;
       a.y_stride = F;
-      if (wide) {  // gate rows 0..F-1, up rows F..2F-1
+      if (wide) {  // gate and up rows paired 8 by 8 per tile (launch_tile_pair_rows)
         WideArgs wa = wide_args(2 * F, d, m->ww[l - 1].gu, xn, d, W.wide_y, 2 * F);
+        wa.pair = F;
         if (q) {
           wide_i4(wa, q->gate);
           wa.q4[1] = q->up.codes;
           wa.s4[1] = q->up.scales;
           wa.n0 = F;
         }
+        if (wa.nr == 1) wa.act = W.act;  // SwiGLU in the pass itself
         launch_wide_proj(wa, s);
-        launch_wide_swiglu(W.wide_y, wa.nr, wa.y_cstride, 2 * F, st->all, &st->n_all, B, F, W.act, s);
+        if (!wa.act) launch_wide_swiglu(W.wide_y, wa.nr, wa.y_cstride, 2 * F, st->all, &st->n_all, B, F, W.act, s);
       } else {
         launch_proj(EPI_SWIGLU, a, kNwg, B, s);
       }
@@ -1112,8 +1114,7 @@ ee_status ee_create_model(const ee_model_config* cfg, const ee_weights* w, const
           t.o = m->alloc<uint16_t>((size_t)d * qd);
           launch_tile_rows((const uint16_t*)lw.wo, d, qd, t.o, m->own);
           t.gu = m->alloc<uint16_t>((size_t)2 * F * d);
-          launch_tile_rows((const uint16_t*)lw.w_gate, F, d, t.gu, m->own);
-          launch_tile_rows((const uint16_t*)lw.w_up, F, d, t.gu + (size_t)F * d, m->own);
+          launch_tile_pair_rows((const uint16_t*)lw.w_gate, (const uint16_t*)lw.w_up, F, d, t.gu, m->own);
           t.down = m->alloc<uint16_t>((size_t)d * F);
           launch_tile_rows((const uint16_t*)lw.w_down, d, F, t.down, m->own);
           if (l < L && lw.head_T) {

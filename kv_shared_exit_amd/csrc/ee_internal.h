@@ -116,6 +116,12 @@ struct WideArgs {
   const int32_t* list_bf; const int32_t* cnt_bf;  // rows run with bf16 weights
   const int32_t* list_i4; const int32_t* cnt_i4;  // rows run with int4 weights (may be null)
   float* y; size_t y_cstride; int y_stride;       // y[r * y_cstride + seq * y_stride + n]
+  // gate/up (pair = F): tile t holds gate rows 8t..8t+7 then up rows 8t..8t+7
+  // (launch_tile_pair_rows; int4: q4/s4[0] gate, [1] up); with one column
+  // range and act set, the pass applies SwiGLU itself and writes bf16
+  // act[seq][F] (no partial sums); otherwise y holds the pairs in tile order
+  int pair;
+  uint16_t* act;
 };
 
 struct AttnArgs {
@@ -217,6 +223,8 @@ void launch_wide_vocab(int epi, const ProjArgs& a, int nwg, hipStream_t s, hipEv
 // contiguous.  Segments of a multi-part matrix (QKV, gate/up) are tiled one
 // after the other (each a multiple of 16 rows): dst is the segment's first row.
 void launch_tile_rows(const uint16_t* W, int N, int K, uint16_t* dst, hipStream_t s);
+// gate/up [F][K] each into F / 8 tiles of 8 gate rows and the same 8 up rows
+void launch_tile_pair_rows(const uint16_t* gate, const uint16_t* up, int F, int K, uint16_t* dst, hipStream_t s);
 // Column ranges of a wide projection (N rows, K columns): count and width.
 int wide_ranges(int N, int K, int* kr);
 // Partial sums of a wide projection over a.nr ranges (set a.nr, a.kr with
@@ -224,7 +232,8 @@ int wide_ranges(int N, int K, int* kr);
 void launch_wide_proj(WideArgs a, hipStream_t s);
 // Epilogues of a wide projection over the rows of list/cnt: the sum of the
 // ranges, then RoPE and the shared-slot K/V write (QKV, ProjArgs as for
-// EPI_QKV), SwiGLU of rows n and F + n into out [seq][F], or bf16 into out.
+// EPI_QKV), SwiGLU of the gate/up pairs (the tile order of a WideArgs pair) into
+// out [seq][F], or bf16 into out.
 void launch_wide_qkv(const float* y, int nr, size_t cstride, int ystride, const int32_t* list,
                      const int32_t* cnt, int B, const ProjArgs& qa, hipStream_t s);
 void launch_wide_swiglu(const float* y, int nr, size_t cstride, int ystride, const int32_t* list,

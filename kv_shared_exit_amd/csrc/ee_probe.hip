@@ -14,14 +14,16 @@
 //                                output rows over K inputs, nbf rows on the
 //                                bf16 weights and ni4 on the int4 G128 copy,
 //                                on the decode step's grid (512 workgroups)
-//   ee_probe wproj N K nbf ni4 reps
+//   ee_probe wproj N K nbf ni4 reps [pair]
 //                                a decoder projection for more than 8 rows on
 //                                matrix cores (wide_proj_kernel: N output rows
 //                                over K inputs, nbf rows on the tiled bf16
 //                                weights and ni4 on the int4 G128 copy, float32
 //                                partial sums over the column ranges the decode
-//                                step uses; gate/up: N = 2 F with the up rows
-//                                from F on)
+//                                step uses); pair 1: gate/up as the decode step
+//                                runs it (N = 2 F, gate and up rows paired per
+//                                tile, SwiGLU applied by the pass when it has
+//                                one column range)
 //   ee_probe copy MiB            one copy kernel reading and writing MiB each
 //   ee_probe read MiB reps       a read-only stream of MiB (each thread sums its
 //                                16-byte loads): the streaming-read ceiling
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(256) void read_region_kernel(const uint4* __restric
 static int usage() {
   std::fprintf(stderr,
                "usage: ee_probe lse V d rows reps | ee_probe wide V d rows reps | "
-               "ee_probe proj swiglu|part N K nbf ni4 reps | ee_probe wproj N K nbf ni4 reps | ee_probe copy MiB | "
+               "ee_probe proj swiglu|part N K nbf ni4 reps | ee_probe wproj N K nbf ni4 reps [pair] | ee_probe copy MiB | "
                "ee_probe read|readc MiB reps | "
                "ee_probe attn B S ctx reps | ee_probe gemm bf16|resid|swiglu M N K reps\n");
   return 2;
@@ -341,6 +343,7 @@ int main(int argc, char** argv) {
     if (argc < 7) return usage();
     const int N = std::atoi(argv[2]), K = std::atoi(argv[3]), nbf = std::atoi(argv[4]), ni4 = std::atoi(argv[5]);
     const int reps = std::atoi(argv[6]);
+    const bool pair = argc > 7 && std::atoi(argv[7]) != 0;
     constexpr int G = 128;
     if (N < 128 || N % 128 || K < 256 || K % 256 || nbf < 0 || ni4 < 0 || nbf + ni4 < 1 || nbf + ni4 > kMaxBatch ||
         reps < 1)
@@ -360,11 +363,17 @@ int main(int argc, char** argv) {
     CK(hipMalloc(&x, (size_t)kMaxBatch * K * 2));
     CK(hipMalloc(&y, (size_t)nr * kMaxBatch * N * 4));
     CK(hipMalloc(&lists, 4 * kMaxBatch * 4));
+    uint16_t* act = nullptr;
+    CK(hipMalloc(&act, (size_t)kMaxBatch * N / 2 * 2));
     CK(hipMemsetAsync(W, 0x3c, wn * 2, s));  // bf16 ~0.0115
     CK(hipMemsetAsync(codes, 0x99, wn / 2, s));
     CK(hipMemsetAsync(sc, 0x3c, wn / G * 2, s));
     CK(hipMemsetAsync(x, 0x3c, (size_t)kMaxBatch * K * 2, s));
-    launch_tile_rows(W, N, K, Wt, s);
+    if (pair && (N % 256 || n0 * 2 != N)) return usage();
+    if (pair)
+      launch_tile_pair_rows(W, W + (size_t)n0 * K, n0, K, Wt, s);
+    else
+      launch_tile_rows(W, N, K, Wt, s);
     std::vector<int32_t> hl(4 * kMaxBatch, 0);
     for (int i = 0; i < nbf; ++i) hl[i] = i;
     for (int i = 0; i < ni4; ++i) hl[kMaxBatch + i] = nbf + i;
@@ -394,6 +403,10 @@ int main(int argc, char** argv) {
     a.y = y;
     a.y_stride = N;
     a.y_cstride = (size_t)kMaxBatch * N;
+    if (pair) {
+      a.pair = n0;
+      if (nr == 1) a.act = act;
+    }
     launch_wide_proj(a, s);  // warm-up
     CK(hipStreamSynchronize(s));
     CK(hipEventRecord(e0, s));
@@ -405,8 +418,9 @@ int main(int argc, char** argv) {
     const double us = 1e3 * ms / reps;
     const double bytes = (nbf ? 2.0 * wn : 0.0) + (ni4 ? wn / 2.0 + wn / G * 2.0 : 0.0);
     const double flops = 2.0 * wn * (nbf + ni4);
-    std::printf("wproj N=%d K=%d bf=%d i4=%d ranges=%d: %.2f us per launch, %.1f GB/s algorithmic, %.1f TFLOP/s\n", N,
-                K, nbf, ni4, nr, us, bytes / us / 1e3, flops / us / 1e6);
+    std::printf("wproj N=%d K=%d bf=%d i4=%d ranges=%d%s: %.2f us per launch, %.1f GB/s algorithmic, %.1f TFLOP/s\n",
+                N, K, nbf, ni4, nr, pair ? (a.act ? " pair+swiglu" : " pair") : "", us, bytes / us / 1e3,
+                flops / us / 1e6);
     return 0;
   }
   const bool wide = !std::strcmp(argv[1], "wide");

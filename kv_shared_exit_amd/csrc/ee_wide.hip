@@ -111,6 +111,33 @@ void launch_tile_rows(const uint16_t* W, int N, int K, uint16_t* dst, hipStream_
                      N, K, dst, pieces);
 }
 
+// The gate/up pair order: tile t holds gate rows 8t..8t+7 (tile rows 0-7) and
+// up rows 8t..8t+7 (tile rows 8-15), each tile in the order above, so the
+// gate and up values of an output end up in lanes l and l ^ 32 of the MFMA
+// result.
+__global__ void tile_pair_rows_kernel(const uint16_t* __restrict__ gate, const uint16_t* __restrict__ up, int K,
+                                      uint16_t* __restrict__ Wt, size_t pieces) {
+  const size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= pieces) return;
+  const int nks = K / 32;
+  const int lane = (int)(g & 63);
+  const size_t blk = g >> 6;
+  const int t = (int)(blk / nks);
+  const int k = (int)(blk - (size_t)t * nks);
+  const int r = lane & 15;
+  const uint16_t* src = (r < 8 ? gate : up) + (size_t)(t * 8 + (r & 7)) * K + k * 32 + (lane >> 4) * 8;
+  *(uint4*)(Wt + g * 8) = *(const uint4*)src;
+}
+
+void launch_tile_pair_rows(const uint16_t* gate, const uint16_t* up, int F, int K, uint16_t* dst, hipStream_t s) {
+  if (!wide_vocab_supported(K) || F < 8 || F % 8 || !gate || !up || !dst)
+    throw std::logic_error("tiled gate/up copy: unsupported shape");
+  const size_t pieces = (size_t)2 * F * K / 8;
+  const int threads = 256;
+  hipLaunchKernelGGL(tile_pair_rows_kernel, dim3((unsigned)((pieces + threads - 1) / threads)), dim3(threads), 0, s,
+                     gate, up, K, dst, pieces);
+}
+
 void launch_tile_vocab(const uint16_t* E, int V, int d, uint16_t* Et, hipStream_t s) {
   launch_tile_rows(E, V, d, Et, s);
 }
@@ -443,11 +470,24 @@ __global__ __launch_bounds__(kProjThreads, 4) void wide_proj_kernel(const WideAr
         EE_STAGE_LOAD(min(c + 2, nch - 1));
       }
     } else if constexpr (RB == 4) {
-      const int seg = tc * 16 >= a.n0 ? 1 : 0;
-      const int ts = tc - (seg ? a.n0 >> 4 : 0);  // tile within its segment
       const int ngr = a.K / G;
-      const uint32_t* cp = a.q4[seg] + (size_t)(ts * 16 + (lane & 15)) * (a.K >> 3) + (k0 >> 3) + (lane >> 4) * 4;
-      const uint16_t* sp = a.s4[seg] + ((size_t)ts * ngr + k0 / G) * 16 + 4 * (lane >> 4);
+      // this lane's code row (A operand row lane % 16) and the four rows of
+      // its scales (result rows 4 (lane / 16) ..): segment and row in it
+      int cseg, crow, sseg, srw;
+      if (a.pair) {  // gate rows 8 tc .. (tile rows 0-7), then the same up rows
+        cseg = (lane & 15) >= 8;
+        crow = tc * 8 + (lane & 7);
+        sseg = (lane >> 4) >= 2;
+        srw = tc * 8 + 4 * ((lane >> 4) & 1);
+      } else {
+        cseg = sseg = tc * 16 >= a.n0 ? 1 : 0;
+        const int ts = tc - (cseg ? a.n0 >> 4 : 0);  // tile within its segment
+        crow = ts * 16 + (lane & 15);
+        srw = ts * 16 + 4 * (lane >> 4);
+      }
+      const uint32_t* cp = a.q4[cseg] + (size_t)crow * (a.K >> 3) + (k0 >> 3) + (lane >> 4) * 4;
+      // scales: [16-row tile of the segment][group][row of the tile]
+      const uint16_t* sp = a.s4[sseg] + ((size_t)(srw >> 4) * ngr + k0 / G) * 16 + (srw & 15);
       const int nbk = kw >> 7;  // 128-column blocks of the range
       // codes of two chunks (RD = 4 blocks) in flight at group size 128: slots
       // 0-1 hold the even chunks' blocks, 2-3 the odd chunks' (the chunk loop is
@@ -532,7 +572,20 @@ __global__ __launch_bounds__(kProjThreads, 4) void wide_proj_kernel(const WideAr
 #undef EE_STAGE_STORE
 
     // lane l holds rows 16 tile + 4 (l / 16) .. +3 of batch column l % 16 of block bb
-    if (tile < ntiles) {
+    if (a.act) {  // gate/up in one range: SwiGLU of the pair in lanes l, l ^ 32 (uniform)
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        float u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = xor_lane<32>(acc[bb][i], lane);
+        const int col = bb * 16 + (lane & 15);
+        if (tile < ntiles && bb < NBB && col < n && lane < 32) {
+          const uint32_t o0 = f2bf(silu_mul(acc[bb][0], u[0])) | (f2bf(silu_mul(acc[bb][1], u[1])) << 16);
+          const uint32_t o1 = f2bf(silu_mul(acc[bb][2], u[2])) | (f2bf(silu_mul(acc[bb][3], u[3])) << 16);
+          *(uint2*)(a.act + (size_t)list[col] * a.pair + tile * 8 + 4 * (lane >> 4)) = make_uint2(o0, o1);
+        }
+      }
+    } else if (tile < ntiles) {
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
         const int col = bb * 16 + (lane & 15);
@@ -572,11 +625,13 @@ void launch_wide_proj(WideArgs a, hipStream_t s) {
   if (!a.cnt_bf || !a.list_bf) a.cnt_bf = a.list_bf = no_rows();
   const bool i4 = a.q4[0] != nullptr;
   if (!i4 || !a.cnt_i4 || !a.list_i4) a.cnt_i4 = a.list_i4 = no_rows();
-  if (!wide_vocab_supported(a.K) || a.N < 16 || a.N % 16 || !a.wt || !a.x || !a.y || a.nr < 1 ||
+  if (!wide_vocab_supported(a.K) || a.N < 16 || a.N % 16 || !a.wt || !a.x || (!a.y && !a.act) || a.nr < 1 ||
       a.kr % kWideCols || (long long)a.nr * a.kr < a.K || (long long)(a.nr - 1) * a.kr >= a.K)
     throw std::logic_error("wide projection: unsupported arguments");
+  if ((a.pair && (a.pair % 16 || (long long)2 * a.pair != a.N)) || (a.act && (!a.pair || a.nr != 1)))
+    throw std::logic_error("wide projection: unsupported gate/up pairing");
   if (i4 && (a.n0 % 16 || a.n0 <= 0 || !a.s4[0] || (a.n0 < a.N && (!a.q4[1] || !a.s4[1])) ||
-             (a.G != 32 && a.G != 64 && a.G != 128)))
+             (a.pair && a.n0 != a.pair) || (a.G != 32 && a.G != 64 && a.G != 128)))
     throw std::logic_error("wide projection: unsupported int4 arguments");
   a.nrb = (a.N + 127) / 128;
   a.g_bf = a.nrb * a.nr;
@@ -629,8 +684,8 @@ __global__ void wide_swiglu_kernel(const float* y, int nr, size_t cs, int ys, co
   const int nn = blockIdx.x * kEpiThreads + threadIdx.x;
   if (nn >= F) return;
   const int seq = list[p];
-  const float* yr = y + (size_t)seq * ys;
-  out[(size_t)seq * F + nn] = (uint16_t)f2bf(silu_mul(wide_sum(yr + nn, nr, cs), wide_sum(yr + F + nn, nr, cs)));
+  const float* yr = y + (size_t)seq * ys + (nn >> 3) * 16 + (nn & 7);  // the pair order: gate, then up 8 later
+  out[(size_t)seq * F + nn] = (uint16_t)f2bf(silu_mul(wide_sum(yr, nr, cs), wide_sum(yr + 8, nr, cs)));
 }
 
 __global__ void wide_bf16_kernel(const float* y, int nr, size_t cs, int ys, const int32_t* list, const int32_t* cnt,
