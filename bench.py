@@ -37,10 +37,10 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 # scaled by what the same counter reads for a 1 GiB device copy.  Valid only
 # for the kernel sources it was measured on (their sha256); otherwise null.
 TRAFFIC = {
-    "lse": {"fetch_kib": 513399.1354, "write_kib": 62.6, "fetch_scale": 1.9999325, "write_scale": 1.0000000,
+    "lse": {"fetch_kib": 513397.5729, "write_kib": 62.6, "fetch_scale": 1.9999318, "write_scale": 1.0000000,
             "sources": ("ee_proj.hip", "ee_device.h", "ee_internal.h", "ee_epi.h"),
-            "sources_sha256": "50f487483857a49608a018b2b6f4921db5b297aae7c2df73216505d67c4cfc37"},
-    "wide": {"fetch_kib": 519400.2917, "write_kib": 512.0, "fetch_scale": 1.9999325, "write_scale": 1.0000000,
+            "sources_sha256": "b0236efe775bbfab808e9feca1683d68e4f8a2bc6b04d6ba999ff7fb40788407"},
+    "wide": {"fetch_kib": 519706.4062, "write_kib": 512.0, "fetch_scale": 1.9999318, "write_scale": 1.0000000,
              "sources": ("ee_wide.hip", "ee_device.h", "ee_internal.h", "ee_epi.h"),
              "sources_sha256": "63cb356ff00dd1f43437088a16c51a62445e9b40f8f1d68c189b5af16d2df2f1"},
 }

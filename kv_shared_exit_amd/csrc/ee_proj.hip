@@ -1132,13 +1132,13 @@ int launch_proj(int epi, const ProjArgs& a0, int nwg, int batch, hipStream_t s, 
 // ---------------------------------------------------------------------------
 constexpr int kFinThreads = 256;
 constexpr int kFinVec = 4;    // float4 per thread per row chunk
-constexpr int kFinParts = 8;  // column ranges summed with all loads in flight
+constexpr int kFinParts = 8;  // column ranges summed with all loads in flight (at most)
 
 // A workgroup owns a row.  Rows up to kFinThreads * kFinVec * 4 columns are
 // held in registers between the sum of squares and the normalisation; wider
 // rows are processed in chunks and re-read (this workgroup wrote them).  Every
 // load of a chunk (residual, partial sums, gains) is issued before any is used.
-template <bool STS>
+template <bool STS, int NP>
 __global__ __launch_bounds__(kFinThreads) void finish_kernel(float* h, const float* hsrc, const float* parts,
                                                              int nparts, size_t cstride, int d, const uint16_t* gain,
                                                              float eps, uint16_t* x, uint16_t* hb, const float* hin,
@@ -1162,7 +1162,7 @@ __global__ __launch_bounds__(kFinThreads) void finish_kernel(float* h, const flo
   const size_t pcs = nparts > 0 ? cstride : 0;
   const int plast = max(nparts - 1, 0);
   for (int c0 = 0; c0 < d4; c0 += per) {
-    float4 pv[kFinParts][kFinVec];
+    float4 pv[NP][kFinVec];
     float4 vi[kFinVec];
 #pragma unroll
     for (int j = 0; j < kFinVec; ++j) {
@@ -1171,12 +1171,12 @@ __global__ __launch_bounds__(kFinThreads) void finish_kernel(float* h, const flo
       if constexpr (STS) vi[j] = *(const float4*)(hi + 4 * i);
       g[j] = *(const uint2*)(gain + 4 * i);
 #pragma unroll
-      for (int c = 0; c < kFinParts; ++c) pv[c][j] = *(const float4*)(pbase + min(c, plast) * pcs + 4 * i);
+      for (int c = 0; c < NP; ++c) pv[c][j] = *(const float4*)(pbase + min(c, plast) * pcs + 4 * i);
     }
 #pragma unroll
     for (int j = 0; j < kFinVec; ++j) {
 #pragma unroll
-      for (int c = 0; c < kFinParts; ++c) {
+      for (int c = 0; c < NP; ++c) {
         if (c < nparts) {
           v[j].x += pv[c][j].x;
           v[j].y += pv[c][j].y;
@@ -1184,7 +1184,7 @@ __global__ __launch_bounds__(kFinThreads) void finish_kernel(float* h, const flo
           v[j].w += pv[c][j].w;
         }
       }
-      for (int c = kFinParts; c < nparts; ++c) {  // more ranges than kFinParts (very wide inputs)
+      for (int c = NP; c < nparts; ++c) {  // more ranges than NP (very wide inputs)
         const int i = min(c0 + tid + j * kFinThreads, d4 - 1);
         const float4 p = *(const float4*)(parts + c * cstride + (size_t)b * d + 4 * i);
         v[j].x += p.x;
@@ -1280,12 +1280,25 @@ void launch_finish(float* h, const float* hsrc, const float* parts, int nparts, 
                    hipStream_t s) {
   if (!h || !hsrc || !gain || !x || (nparts > 0 && !parts) || d % 4 || (!hin != !sts))
     throw std::logic_error("finish: bad arguments");
-  if (sts)
-    hipLaunchKernelGGL(finish_kernel<true>, dim3(B), dim3(kFinThreads), 0, s, h, hsrc, parts, nparts, cstride, d,
-                       gain, eps, x, hb, hin, sts);
+  // the ranges summed with all loads in flight: the fewest of 1, 2, 4, 8 that
+  // cover nparts (a load per range and element, so no more than needed)
+  auto go = [&](auto np) {
+    constexpr int NP = decltype(np)::value;
+    if (sts)
+      hipLaunchKernelGGL((finish_kernel<true, NP>), dim3(B), dim3(kFinThreads), 0, s, h, hsrc, parts, nparts,
+                         cstride, d, gain, eps, x, hb, hin, sts);
+    else
+      hipLaunchKernelGGL((finish_kernel<false, NP>), dim3(B), dim3(kFinThreads), 0, s, h, hsrc, parts, nparts,
+                         cstride, d, gain, eps, x, hb, hin, sts);
+  };
+  if (nparts <= 1)
+    go(std::integral_constant<int, 1>{});
+  else if (nparts <= 2)
+    go(std::integral_constant<int, 2>{});
+  else if (nparts <= 4)
+    go(std::integral_constant<int, 4>{});
   else
-    hipLaunchKernelGGL(finish_kernel<false>, dim3(B), dim3(kFinThreads), 0, s, h, hsrc, parts, nparts, cstride, d,
-                       gain, eps, x, hb, hin, sts);
+    go(std::integral_constant<int, kFinParts>{});
 }
 
 // ---------------------------------------------------------------------------
