@@ -414,9 +414,8 @@ def main():
     # measured HBM traffic per launch, averaged like the algorithmic bytes (a
     # launch without rows reads nothing)
     traffic = None
-    # a launch with more than 8 rows on the backbone (batches above 8) runs the
-    # wide pass, else the 8-row pass: each launch with work takes its kernel's
-    # measured bytes
+    # batches above 8 run every exit head on the wide pass, batches up to 8 on
+    # the 8-row pass: each launch with work takes its kernel's measured bytes
     def measured(kind):
         tr = TRAFFIC[kind]
         if kernel_sources_sha256(tr["sources"]) != tr["sources_sha256"]:
@@ -428,7 +427,7 @@ def main():
             for l in range(every, sh.n_layers, every):
                 a_rows = int((exits[s_] >= l).sum())
                 if a_rows:
-                    t_ = measured("wide" if B > 8 and a_rows > 8 else "lse")
+                    t_ = measured("wide" if B > 8 else "lse")
                     tot = None if t_ is None or tot is None else tot + t_
         traffic = None if tot is None else round(tot / n_launch)
 
@@ -443,8 +442,7 @@ def main():
     if args.temperature > 0:
         head_kernel = "exit-head vocabulary GEMV with the draft's draw (proj_kernel<6, 1>)"
     elif B > 8:
-        head_kernel = ("exit-head vocabulary GEMV: wide_vocab_kernel<3> above 8 rows on the backbone, "
-                       "proj_kernel<3, 1> otherwise (one launch each, the other returns at once)")
+        head_kernel = "exit-head vocabulary GEMV (wide_vocab_kernel<3>, any number of rows on the backbone)"
     else:
         head_kernel = "exit-head vocabulary GEMV (proj_kernel<3, 1>)"
     hist = np.bincount(exits.reshape(-1), minlength=sh.n_layers + 1)[1:]

@@ -692,18 +692,17 @@ void enqueue_position(ee_model* m, const Work& W, ee_kv_cache* c, int B, bool he
         a.part = W.head_part;
         hipEvent_t e0 = nullptr, e1 = nullptr;
         if (W.prof) prof_events(m, &e0, &e1);
-        // more than 8 rows go to the wide pass (one read of E for all rows);
-        // the row count is on the device, so both are launched and one returns
+        // steps of more than 8 rows use the wide pass for every count of rows
+        // on the backbone (one read of E for all of them; with few rows it
+        // costs about what the 8-row pass does, and one launch replaces two)
         if (sampled) {  // also the draft's Gumbel-max and the tau statistics
           sampled_args(a);
           launch_proj(EPI_LSE_S, a, nv, B, s, e0, e1);
+        } else if (wide_vocab) {
+          a.wb[0] = m->lm_head_t;
+          launch_wide_vocab(EPI_LSE, a, nv, s, e0, e1);
         } else {
-          if (wide_vocab) a.max_rows = 8;
-          launch_proj(EPI_LSE, a, nv, B, s, e0, wide_vocab ? nullptr : e1);
-          if (wide_vocab) {
-            a.wb[0] = m->lm_head_t;
-            launch_wide_vocab(EPI_LSE, a, nv, s, e1);
-          }
+          launch_proj(EPI_LSE, a, nv, B, s, e0, e1);
         }
       }
       launch_decide(DECIDE_HEAD, bmin, st, W.head_part, nv, W.d_gamma, l, L, B, W.p_rec, nullptr, s);

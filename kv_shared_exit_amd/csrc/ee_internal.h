@@ -89,8 +89,6 @@ struct ProjArgs {
   int nbf_mix;
   int nwg_i4;
   int wpt4[4];
-  int max_rows;                                   // EPI_LSE / EPI_ARGMAX: do nothing above this many rows
-                                                  // (the wide pass has them); 0 = no limit
   // sampled epilogues: 1 / temperature, the generator's seed, partials by
   // sequence [nwg][kMaxBatch][kPartS], and the step state
   float itau;
@@ -209,15 +207,16 @@ void launch_init(StepState* st, const int32_t* prompt, int P, int t, int B, int 
 // p[0..n) = v (32-bit words), by a kernel.
 void launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 void launch_attention(const AttnArgs& a, hipStream_t s);
-// Vocabulary GEMVs (EPI_LSE / EPI_ARGMAX) for more than 8 rows on MFMA
-// (ee_wide.hip): E read once for up to 64 rows from a tiled copy made by
-// launch_tile_vocab (wide_vocab_elems(V, d) bf16).  The kernel does nothing
-// when the device-side row count is 8 or less.  Writes nwg partials per row
-// like launch_proj; with ev_end set, the launch records its end into it.
+// Vocabulary GEMVs (EPI_LSE / EPI_ARGMAX) on MFMA for steps of more than 8
+// rows (ee_wide.hip): E read once for up to 64 rows from a tiled copy made by
+// launch_tile_vocab (wide_vocab_elems(V, d) bf16), whatever the device-side
+// row count (nothing is done when it is 0).  Writes nwg partials per row like
+// launch_proj; with events set, the launch records its start and end.
 bool wide_vocab_supported(int d);
 size_t wide_vocab_elems(int V, int d);
 void launch_tile_vocab(const uint16_t* E, int V, int d, uint16_t* Et, hipStream_t s);
-void launch_wide_vocab(int epi, const ProjArgs& a, int nwg, hipStream_t s, hipEvent_t ev_end = nullptr);
+void launch_wide_vocab(int epi, const ProjArgs& a, int nwg, hipStream_t s, hipEvent_t ev_start = nullptr,
+                       hipEvent_t ev_end = nullptr);
 // The tiled order of a bf16 matrix [N][K] (K a multiple of 256; rows padded to
 // 16 with zeros): the 1 KB A operand of each 16-row tile and 32-column step
 // contiguous.  Segments of a multi-part matrix (QKV, gate/up) are tiled one

@@ -934,9 +934,6 @@ __global__ __launch_bounds__(kProjThreads, 4) void proj_kernel(const ProjArgs a)
   // (the resampling pass's list holds row pairs: up to 2 * kMaxBatch entries)
   const int n_bf = min(max(*(const cint*)a.cnt_bf, 0), EPI == EPI_RESAMPLE ? 2 * kMaxBatch : kMaxBatch);
   const int n_i4 = min(max(*(const cint*)a.cnt_i4, 0), kMaxBatch);
-  if constexpr (EPI == EPI_LSE || EPI == EPI_ARGMAX) {
-    if (n_bf > a.max_rows) return;  // the wide (MFMA) vocabulary pass has these rows
-  }
   if constexpr (EPI == EPI_RESAMPLE) {
     if (n_bf == 0) return;  // nothing rejected
   }
@@ -1066,7 +1063,6 @@ int launch_proj(int epi, const ProjArgs& a0, int nwg, int batch, hipStream_t s, 
   ProjArgs a = a0;
   if (!a.cnt_bf || !a.list_bf) a.cnt_bf = a.list_bf = no_rows();
   if (!a.cnt_i4 || !a.list_i4) a.cnt_i4 = a.list_i4 = no_rows();
-  if (a.max_rows <= 0) a.max_rows = kMaxBatch;
   // the vocabulary epilogues write one partial per workgroup (kNwgMax of them)
   int g = std::max(1, std::min(nwg, kNwgMax));
   a.nkc = 1;

@@ -142,14 +142,16 @@ void launch_tile_vocab(const uint16_t* E, int V, int d, uint16_t* Et, hipStream_
   launch_tile_rows(E, V, d, Et, s);
 }
 
-// a.wb[0]: the tiled E; a.N = V; a.K = d; rows: list_bf / cnt_bf (runs only
-// when the count exceeds 8: the vector-ALU pass takes smaller counts).
+// a.wb[0]: the tiled E; a.N = V; a.K = d; rows: list_bf / cnt_bf, any count
+// from 1 to 64 (the four 16-row batch blocks are computed whatever the count:
+// the pass is bound by reading E, so a launch with few rows costs about what
+// one with 64 does, and no second launch is needed for small counts).
 template <int EPI>
 __global__ __launch_bounds__(kProjThreads, 4) void wide_vocab_kernel(const ProjArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[2 * kWideBuf];
   __shared__ float red[kWideWaves * kWideRows * 4];
   const int n = min(max(*a.cnt_bf, 0), kWideRows);
-  if (n <= 8) return;  // the vector-ALU pass has these rows
+  if (n == 0) return;  // no row on the backbone
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -327,7 +329,8 @@ __global__ __launch_bounds__(kProjThreads, 4) void wide_vocab_kernel(const ProjA
   }
 }
 
-void launch_wide_vocab(int epi, const ProjArgs& a0, int nwg, hipStream_t s, hipEvent_t ev_end) {
+void launch_wide_vocab(int epi, const ProjArgs& a0, int nwg, hipStream_t s, hipEvent_t ev_start,
+                       hipEvent_t ev_end) {
   ProjArgs a = a0;
   if (!a.cnt_bf || !a.list_bf) a.cnt_bf = a.list_bf = no_rows();
   if (!wide_vocab_supported(a.K) || a.N < 1 || !a.wb[0] || !a.part)
@@ -335,8 +338,8 @@ void launch_wide_vocab(int epi, const ProjArgs& a0, int nwg, hipStream_t s, hipE
   if (epi != EPI_LSE && epi != EPI_ARGMAX) throw std::logic_error("wide vocabulary pass: epilogue");
   const int g = std::max(1, std::min(nwg, kNwgMax));
   auto kern = epi == EPI_LSE ? wide_vocab_kernel<EPI_LSE> : wide_vocab_kernel<EPI_ARGMAX>;
-  if (ev_end)
-    hipExtLaunchKernelGGL(kern, dim3(g), dim3(kProjThreads), 0, s, nullptr, ev_end, 0, a);
+  if (ev_start || ev_end)
+    hipExtLaunchKernelGGL(kern, dim3(g), dim3(kProjThreads), 0, s, ev_start, ev_end, 0, a);
   else
     hipLaunchKernelGGL(kern, dim3(g), dim3(kProjThreads), 0, s, a);
 }

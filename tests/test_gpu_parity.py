@@ -302,9 +302,10 @@ def test_wide_batch_vocabulary_pass(gpu, label, sh, batch):
     """Batches of more than 8 rows: the projections run on the matrix-core pass
     (both weight formats, column ranges summed by the epilogues) when the widths
     are multiples of 256; the exit head's vocabulary pass and the LM head run on
-    the matrix-core pass over the tiled copy of E whenever more than 8 rows are
-    on the backbone (the final LM head always, since every row takes it), and on
-    the vector-ALU pass otherwise; exits are spread so that layers see both."""
+    the matrix-core pass over the tiled copy of E for any number of rows on the
+    backbone; exits are spread so that some layers have more than 8 rows on the
+    backbone and some fewer (the pass computes four 16-row batch blocks and
+    keeps only the listed rows)."""
     from parity import run_parity
     wl = Workload(label, sh, 1, 6, 4, 0.75, "calibrated", max(1.2, sh.n_layers / 2), index=9)
     cal = calibrate(wl, verbose=False)
