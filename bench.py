@@ -37,12 +37,12 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix-core peak
 # scaled by what the same counter reads for a 1 GiB device copy.  Valid only
 # for the kernel sources it was measured on (their sha256); otherwise null.
 TRAFFIC = {
-    "lse": {"fetch_kib": 513397.5729, "write_kib": 62.6, "fetch_scale": 1.9999318, "write_scale": 1.0000000,
+    "lse": {"fetch_kib": 513397.5625, "write_kib": 62.6, "fetch_scale": 1.9999340, "write_scale": 0.9999999,
             "sources": ("ee_proj.hip", "ee_device.h", "ee_internal.h", "ee_epi.h"),
-            "sources_sha256": "b0236efe775bbfab808e9feca1683d68e4f8a2bc6b04d6ba999ff7fb40788407"},
-    "wide": {"fetch_kib": 519706.4062, "write_kib": 512.0, "fetch_scale": 1.9999318, "write_scale": 1.0000000,
+            "sources_sha256": "fe5be4b424ad6cf612d99f8526939fe985394c9b6213d38a11de3a7175df8765"},
+    "wide": {"fetch_kib": 519396.8646, "write_kib": 512.0, "fetch_scale": 1.9999340, "write_scale": 0.9999999,
              "sources": ("ee_wide.hip", "ee_device.h", "ee_internal.h", "ee_epi.h"),
-             "sources_sha256": "63cb356ff00dd1f43437088a16c51a62445e9b40f8f1d68c189b5af16d2df2f1"},
+             "sources_sha256": "7f1965e47fe4553aa1fb250da079086f9590f5461f192770007625948b5a22f0"},
 }
 # the workloads whose shape (128256 x 4096) the counters were taken at
 TRAFFIC_SHAPE = (128256, 4096)

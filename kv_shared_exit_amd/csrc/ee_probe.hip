@@ -3,10 +3,14 @@
 // process, and a plain device copy of known size that calibrates the byte
 // counters.
 //
-//   ee_probe lse V d rows reps   exit-head vocabulary GEMV (proj_kernel<EPI_LSE>)
+//   ee_probe lse V d rows reps [grid]
+//                                exit-head vocabulary GEMV (proj_kernel<EPI_LSE>)
 //                                over a V x d bf16 matrix and `rows` staged rows
-//   ee_probe wide V d rows reps  the same GEMV for 9..64 rows on matrix cores
-//                                (wide_vocab_kernel<EPI_LSE> over the tiled copy)
+//   ee_probe wide V d rows reps [grid]
+//                                the same GEMV on matrix cores as steps of more
+//                                than 8 rows run it (wide_vocab_kernel<EPI_LSE>
+//                                over the tiled copy, 1..64 rows); grid: the
+//                                workgroups (default: the decode step's)
 //   ee_probe proj EPI N K nbf ni4 reps
 //                                a decoder projection (EPI: swiglu = gate/up
 //                                with its epilogue, part = O, down or a
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(256) void read_region_kernel(const uint4* __restric
 
 static int usage() {
   std::fprintf(stderr,
-               "usage: ee_probe lse V d rows reps | ee_probe wide V d rows reps | "
+               "usage: ee_probe lse|wide V d rows reps [grid] | "
                "ee_probe proj swiglu|part N K nbf ni4 reps | ee_probe wproj N K nbf ni4 reps [pair] | ee_probe copy MiB | "
                "ee_probe read|readc MiB reps | "
                "ee_probe attn B S ctx reps | ee_probe gemm bf16|resid|swiglu M N K reps\n");
@@ -429,7 +433,7 @@ int main(int argc, char** argv) {
     const int V = std::atoi(argv[2]), d = std::atoi(argv[3]), rows = std::atoi(argv[4]), reps = std::atoi(argv[5]);
     if (V < 1 || d < 32 || d % 32 || rows < 1 || reps < 1) return usage();
     if (!wide && (rows > 8 || !proj_fits(d, rows))) return usage();
-    if (wide && (rows <= 8 || rows > kMaxBatch || !wide_vocab_supported(d))) return usage();
+    if (wide && (rows > kMaxBatch || !wide_vocab_supported(d))) return usage();
     uint16_t *E, *x;
     float* part;
     int32_t* lists;
@@ -465,10 +469,13 @@ int main(int argc, char** argv) {
     // workgroups that keep the full grid's rounds of 2-row wave tiles
     const int tiles = (V + 1) / 2, waves = kProjThreads / 64;
     const int rounds = (tiles + kNwgMax * waves - 1) / (kNwgMax * waves);
-    const int nv = std::max(1, std::min(kNwgMax, (tiles + rounds * waves - 1) / (rounds * waves)));
+    int nv = std::max(1, std::min(kNwgMax, (tiles + rounds * waves - 1) / (rounds * waves)));
+    if (wide) nv = kNwgMax;  // as the decode step launches it
+    if (argc > 6) nv = std::atoi(argv[6]);  // or the grid given
+    if (nv < 1 || nv > kNwgMax) return usage();
     auto launch = [&] {
       if (wide)
-        launch_wide_vocab(EPI_LSE, a, kNwgMax, s);
+        launch_wide_vocab(EPI_LSE, a, nv, s);
       else
         launch_proj(EPI_LSE, a, nv, rows, s);
     };
