@@ -316,6 +316,23 @@ def test_wide_batch_vocabulary_pass(gpu, label, sh, batch):
     assert res.compared_tokens >= batch * 2
 
 
+def test_wide_vocabulary_pass_with_few_rows_on_the_backbone(gpu):
+    """A step of 12 rows (the matrix-core passes) where 9 rows are forced out
+    after layer 1: the exit head of layer 2 has 3 rows on the backbone and runs
+    on the wide vocabulary pass, which serves every exit head of a step above
+    8 rows; its p values (compared at every evaluated head) and the exits
+    match the oracle."""
+    from parity import run_parity
+    sh = ModelShape(3, 512, 4, 2, 128, 768, 500, 128, rope_theta=500000.0)
+    w = synth.make_weights(sh, 9)
+    B = 12
+    forced = np.where(np.arange(B) < 9, 1, 0).astype(np.int32)
+    res = run_parity(sh, w, B, 6, 3, 2.0, forced_fn=lambda s: forced, label="wide-few-rows")
+    assert res.compared_tokens >= B * 2
+    exits = np.concatenate(res.exits)
+    assert (exits == 1).sum() >= 9 and (exits == 3).sum() >= 3
+
+
 def test_attention_one_workgroup_per_sequence_and_kv_head(gpu):
     """32 sequences x 8 kv heads (256 pairs): decode attention runs one
     workgroup per (sequence, kv head), whose 8 waves take the 9 tiles of each
